@@ -1,0 +1,369 @@
+"""Checks that pin the fp64 oracle to facts outside itself.
+
+Each ``pin_*`` function raises ``AssertionError`` when the oracle disagrees
+with a closed form, a library routine, a brute-force search, or an
+invariance of the method.  ``test_oracle_pins.py`` runs them on the real
+oracle and, to show they have teeth, on copies of it with one plausible
+mistake planted (a dropped scale, a wrong divisor, a reversed tie-break, a
+transposed operand, a missing rebase, ...).
+
+The pages print no worked numerical example, so no value here is quoted from
+them; every expected value is derived by hand in the docstring next to it,
+or comes from an independent routine (torch's scaled_dot_product_attention
+and avg_pool1d, itertools.combinations).
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+import torch
+
+import oracle.vsa_oracle as O
+
+RNG_SEED = 20261203
+
+
+def _rng(extra=0):
+    return np.random.default_rng(RNG_SEED + extra)
+
+
+def _sdpa(q, k, v):
+    """Textbook softmax(q k^T / sqrt(D)) v via torch's fp64 CPU routine."""
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x)) for x in (q, k, v))
+    return torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).numpy()
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+
+def pin_block_sizes():
+    assert O.block_sizes(256) == [64] * 4
+    assert O.block_sizes(13 * 64 + 40) == [64] * 13 + [40]
+    assert O.block_sizes(1) == [1]
+    assert O.block_sizes(64) == [64]
+    try:
+        O.block_sizes(0)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("zero-length sequence must be rejected")
+
+
+def pin_pool_partial_block():
+    """Block 0 full with rows 0..63 (mean 31.5); block 1 partial with rows
+    valued 1, 2, 3 (mean 2).  A divisor of 64 for the partial block would give
+    6/64 instead of 2."""
+    d = 4
+    x = np.zeros((128, d))
+    x[:64] = np.arange(64)[:, None]
+    x[64:67] = np.array([1.0, 2.0, 3.0])[:, None]
+    x[67:] = 1e9  # padding rows must never be read
+    m = O.pool(x, [64, 3])
+    assert np.array_equal(m[0], np.full(d, 31.5)), m[0]
+    assert np.array_equal(m[1], np.full(d, 2.0)), m[1]
+
+
+def pin_two_token_closed_form():
+    """One partial block of 2 tokens, D = 64 (scale 1/8).
+
+    q0 = (8 ln 3, 0, ...), k0 = e0, k1 = 0 -> logits ln 3 and 0 -> weights 3/4
+    and 1/4, so out_s[0] = 0.75 v0 + 0.25 v1.  q1 = 0 -> weights 1/2, 1/2.
+    With a single block the coarse softmax has one key: out_c = Vc[0] =
+    (v0 + v1) / 2, and routing must pick block 0.  Gate 0.5 per token:
+    out = 0.5 out_c + out_s.
+    """
+    D = 64
+    q = np.zeros((1, 1, 2, D)); k = np.zeros((1, 1, 2, D)); v = np.zeros((1, 1, 2, D))
+    q[0, 0, 0, 0] = 8.0 * math.log(3.0)
+    k[0, 0, 0, 0] = 1.0
+    v[0, 0, 0, 1] = 4.0
+    v[0, 0, 1, 2] = 8.0
+    gate = np.full((1, 1, 2), 0.5)
+    r = O.vsa_forward(q, k, v, topk=3, gate=gate)
+    want_s0 = np.zeros(D); want_s0[1] = 3.0; want_s0[2] = 2.0
+    want_s1 = np.zeros(D); want_s1[1] = 2.0; want_s1[2] = 4.0
+    want_c = np.zeros(D); want_c[1] = 2.0; want_c[2] = 4.0
+    assert np.allclose(r["out_s"][0, 0, 0], want_s0, atol=1e-14, rtol=0)
+    assert np.allclose(r["out_s"][0, 0, 1], want_s1, atol=1e-14, rtol=0)
+    assert np.allclose(r["out_c"][0, 0, 0], want_c, atol=1e-14, rtol=0)
+    assert r["q2k_idx"].tolist() == [[[[0]]]] and r["q2k_num"].tolist() == [[[1]]]
+    assert np.allclose(r["out"][0, 0, 0], 0.5 * want_c + want_s0, atol=1e-14, rtol=0)
+    assert np.allclose(r["out"][0, 0, 1], 0.5 * want_c + want_s1, atol=1e-14, rtol=0)
+
+
+def _two_block_case(D=128):
+    """Q: one full block, every row (a, 0, ...), a = sqrt(D) ln 3.  K block 0
+    rows e0, K block 1 zero.  V block 0 rows all 1.0 in column 5, V block 1
+    rows all 1.0 in column 9.  Coarse dots: a and 0 -> coarse weights 3/4 and
+    1/4 -> out_c = 0.75 e5 + 0.25 e9.  Fine logits: ln 3 for the 64 tokens of
+    block 0, 0 for the 64 of block 1 -> the same 3/4 : 1/4 split."""
+    a = math.sqrt(D) * math.log(3.0)
+    q = np.zeros((1, 1, 64, D)); q[..., 0] = a
+    k = np.zeros((1, 1, 128, D)); k[0, 0, :64, 0] = 1.0
+    v = np.zeros((1, 1, 128, D)); v[0, 0, :64, 5] = 1.0; v[0, 0, 64:, 9] = 1.0
+    return q, k, v
+
+
+def pin_coarse_and_routing_closed_form():
+    q, k, v = _two_block_case()
+    want = np.zeros(128); want[5] = 0.75; want[9] = 0.25
+    r = O.vsa_forward(q, k, v, topk=2)
+    assert np.allclose(r["out_c"][0, 0, 0], want, atol=1e-14, rtol=0)
+    assert np.allclose(r["out_s"][0, 0], want[None, :], atol=1e-14, rtol=0)
+    assert np.allclose(r["out"][0, 0], 2 * want[None, :], atol=1e-14, rtol=0)
+    assert r["q2k_idx"][0, 0, 0].tolist() == [0, 1]
+    r1 = O.vsa_forward(q, k, v, topk=1)
+    assert r1["q2k_idx"][0, 0, 0].tolist() == [0]  # block 0 has the larger score
+    e5 = np.zeros(128); e5[5] = 1.0
+    assert np.allclose(r1["out_s"][0, 0], e5[None, :], atol=1e-14, rtol=0)
+    assert np.allclose(r1["out_c"][0, 0, 0], want, atol=1e-14, rtol=0)  # coarse stays dense
+
+
+def pin_combine_closed_form():
+    """out_c row (1, 2), out_s rows (10, 20), (30, 40); gate (0.5, 2):
+    out = (10.5, 21), (32, 44).  Ungated adds: (11, 22), (31, 42).  A full
+    [n, D] gate equal to (0.5, 3) per column on row 0 gives (10.5, 26)."""
+    oc = np.array([1.0, 2.0])
+    os_ = np.array([[10.0, 20.0], [30.0, 40.0]])
+    assert np.array_equal(O.combine(oc, os_, np.array([0.5, 2.0])),
+                          np.array([[10.5, 21.0], [32.0, 44.0]]))
+    assert np.array_equal(O.combine(oc, os_, None), np.array([[11.0, 22.0], [31.0, 42.0]]))
+    assert np.array_equal(O.combine(oc, os_[:1], np.array([[0.5, 3.0]])),
+                          np.array([[10.5, 26.0]]))
+
+
+# ---------------------------------------------------------------------------
+# routing: brute force and tie rule
+# ---------------------------------------------------------------------------
+
+def pin_topk_bruteforce():
+    """For distinct scores the selected set is the unique k-subset with the
+    largest score sum; checked against every subset."""
+    rng = _rng(1)
+    for n, k in [(4, 2), (6, 3), (8, 3), (9, 5), (7, 1), (5, 5)]:
+        for _ in range(20):
+            row = rng.standard_normal(n)
+            best = max(itertools.combinations(range(n), k), key=lambda c: row[list(c)].sum())
+            sel, gap = O.select_topk(row, k)
+            assert sel == sorted(best), (row, k, sel, best)
+            s = np.sort(row)[::-1]
+            want_gap = s[k - 1] - s[k] if k < n else math.inf
+            assert gap == want_gap
+
+
+def pin_topk_ties_and_order():
+    """Equal scores go to the lower block index; output is ascending; topk is
+    clamped to the number of blocks; topk < 1 is an error."""
+    assert O.select_topk(np.array([1.0, 3.0, 3.0, 2.0]), 2)[0] == [1, 2]
+    assert O.select_topk(np.array([5.0, 5.0, 1.0]), 1)[0] == [0]
+    assert O.select_topk(np.array([1.0, 2.0, 2.0, 2.0]), 2)[0] == [1, 2]
+    assert O.select_topk(np.array([0.0, 9.0, 1.0, 8.0]), 2)[0] == [1, 3]
+    assert O.select_topk(np.array([4.0, 1.0, 3.0]), 3)[0] == [0, 1, 2]
+    assert O.select_topk(np.array([4.0, 1.0, 3.0]), 10)[0] == [0, 1, 2]
+    assert O.select_topk(np.array([2.0, 2.0]), 1)[1] == 0.0
+    try:
+        O.select_topk(np.array([1.0]), 0)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("topk < 1 must be rejected")
+
+
+def pin_selection_property(seed=3):
+    """On a random batch every row's selected minimum >= unselected maximum."""
+    rng = _rng(seed)
+    q = rng.standard_normal((2, 2, 64 * 9 - 13, 64))
+    k = rng.standard_normal((2, 2, 64 * 7 - 5, 64))
+    v = rng.standard_normal(k.shape)
+    r = O.vsa_forward(q, k, v, topk=3, blocks=[])
+    for b, h, i in itertools.product(range(2), range(2), range(9)):
+        qc = O.pool(q[b, h], O.block_sizes(q.shape[2]))
+        kc = O.pool(k[b, h], O.block_sizes(k.shape[2]))
+        dots = qc @ kc.T  # (check only: the ranking quantity)
+        sel = r["q2k_idx"][b, h, i]
+        uns = np.setdiff1d(np.arange(7), sel)
+        assert dots[i, sel].min() >= dots[i, uns].max()
+        assert list(sel) == sorted(sel)
+
+
+# ---------------------------------------------------------------------------
+# reduction to dense attention (library routine)
+# ---------------------------------------------------------------------------
+
+def pin_dense_equivalence(seed=4):
+    """topk = all blocks: out_s is textbook attention over the whole sequence,
+    including a ragged tail and Sq != Skv; out_c is textbook attention over
+    pooled tensors, the pooling done by torch's avg_pool1d (full blocks)."""
+    rng = _rng(seed)
+    for (B, H, Sq, Skv, D) in [(2, 3, 256, 256, 64), (1, 2, 200, 333, 128), (1, 1, 64, 64, 128)]:
+        q = rng.standard_normal((B, H, Sq, D))
+        k = rng.standard_normal((B, H, Skv, D))
+        v = rng.standard_normal((B, H, Skv, D))
+        r = O.vsa_forward(q, k, v, topk=10 ** 6)
+        assert np.allclose(r["out_s"], _sdpa(q, k, v), atol=1e-12, rtol=0)
+        if Sq % 64 == 0 and Skv % 64 == 0:
+            def ap(x):
+                t = torch.from_numpy(x).reshape(B * H, x.shape[2], D).transpose(1, 2)
+                return torch.nn.functional.avg_pool1d(t, 64).transpose(1, 2).reshape(
+                    B, H, -1, D).numpy()
+            assert np.allclose(r["out_c"], _sdpa(ap(q), ap(k), ap(v)), atol=1e-12, rtol=0)
+
+
+def pin_single_block(seed=5):
+    """S <= 64: one block, routing {0}, out_c = Vc[0] exactly (softmax over a
+    single key is 1), out_s = dense attention over <= 64 tokens."""
+    rng = _rng(seed)
+    for S in (64, 37, 1):
+        q = rng.standard_normal((1, 2, S, 64))
+        k = rng.standard_normal((1, 2, S, 64))
+        v = rng.standard_normal((1, 2, S, 64))
+        r = O.vsa_forward(q, k, v, topk=4)
+        assert r["q2k_idx"].reshape(-1).tolist() == [0, 0]
+        assert np.allclose(r["out_c"][:, :, 0], v.mean(axis=2), atol=1e-15, rtol=0)
+        assert np.allclose(r["out_s"], _sdpa(q, k, v), atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------------------
+# invariances
+# ---------------------------------------------------------------------------
+
+def _rand_dense(seed, B=1, H=2, nq=6, nkv=7, D=64, tail=0):
+    rng = _rng(seed)
+    q = rng.standard_normal((B, H, 64 * nq - tail, D))
+    k = rng.standard_normal((B, H, 64 * nkv, D))
+    v = rng.standard_normal((B, H, 64 * nkv, D))
+    g = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, H, 64 * nq - tail))))
+    return q, k, v, g
+
+
+def pin_permute_within_kv_block(seed=6):
+    q, k, v, g = _rand_dense(seed)
+    r0 = O.vsa_forward(q, k, v, 3, g)
+    perm = np.concatenate([64 * j + _rng(seed + 100 + j).permutation(64) for j in range(7)])
+    r1 = O.vsa_forward(q, k[:, :, perm], v[:, :, perm], 3, g)
+    assert np.array_equal(r0["q2k_idx"], r1["q2k_idx"])
+    assert np.allclose(r0["out"], r1["out"], atol=1e-12, rtol=0)
+
+
+def pin_permute_kv_blocks(seed=7):
+    q, k, v, g = _rand_dense(seed)
+    bperm = _rng(seed + 1).permutation(7)  # new block j holds old block bperm[j]
+    tok = np.concatenate([64 * bperm[j] + np.arange(64) for j in range(7)])
+    r0 = O.vsa_forward(q, k, v, 3, g)
+    r1 = O.vsa_forward(q, k[:, :, tok], v[:, :, tok], 3, g)
+    inv = np.argsort(bperm)  # old block o is now at inv[o]
+    mapped = np.sort(inv[r0["q2k_idx"]], axis=-1)
+    assert np.array_equal(mapped, r1["q2k_idx"])
+    assert np.allclose(r0["out"], r1["out"], atol=1e-12, rtol=0)
+
+
+def pin_linear_in_v(seed=8):
+    q, k, v, g = _rand_dense(seed, tail=17)
+    v2 = _rng(seed + 1).standard_normal(v.shape)
+    a = O.vsa_forward(q, k, v, 2, g)
+    b = O.vsa_forward(q, k, v2, 2, g)
+    c = O.vsa_forward(q, k, v + 2.0 * v2, 2, g)
+    assert np.allclose(c["out"], a["out"] + 2.0 * b["out"], atol=1e-12, rtol=0)
+    assert np.allclose(c["out_c"], a["out_c"] + 2.0 * b["out_c"], atol=1e-12, rtol=0)
+
+
+def pin_gate_special_values(seed=9):
+    q, k, v, g = _rand_dense(seed, tail=30)
+    un = O.vsa_forward(q, k, v, 3, None)
+    one = O.vsa_forward(q, k, v, 3, np.ones_like(g))
+    zero = O.vsa_forward(q, k, v, 3, np.zeros_like(g))
+    assert np.array_equal(un["out"], one["out"])
+    assert np.array_equal(zero["out"], zero["out_s"])
+    per_tok = O.vsa_forward(q, k, v, 3, g)
+    full = O.vsa_forward(q, k, v, 3, np.repeat(g[..., None], q.shape[-1], axis=-1))
+    assert np.array_equal(per_tok["out"], full["out"])
+
+
+# ---------------------------------------------------------------------------
+# varlen: packed equals per-sequence
+# ---------------------------------------------------------------------------
+
+def _pack(seqs, key, H, D, lens):
+    n = [-(-s // 64) for s in lens]
+    out = np.zeros((H, 64 * sum(n)) + ((D,) if key != "gate" else ()))
+    o = 0
+    for s, x in enumerate(seqs):
+        out[:, o:o + lens[s]] = x[key]
+        o += 64 * n[s]
+    return out
+
+
+def pin_varlen_matches_per_sequence(seed=10):
+    rng = _rng(seed)
+    H, D = 3, 64
+    lens_q = [5 * 64, 9 * 64, 13 * 64 + 40, 64, 1]
+    lens_kv = [6 * 64, 9 * 64, 14 * 64 - 7, 64, 130]
+    topk = [2, 3, 4, 1, 5]
+    seqs = []
+    for sq, skv in zip(lens_q, lens_kv):
+        seqs.append(dict(q=rng.standard_normal((H, sq, D)), k=rng.standard_normal((H, skv, D)),
+                         v=rng.standard_normal((H, skv, D)),
+                         gate=1 / (1 + np.exp(-rng.standard_normal((H, sq))))))
+    qp, kp, vp = (_pack(seqs, x, H, D, lens_q if x == "q" else lens_kv) for x in "qkv")
+    gp = _pack(seqs, "gate", H, D, lens_q)
+    r = O.vsa_forward_varlen(qp, kp, vp, lens_q, lens_kv, topk, gp)
+    oq = nq_acc = nkv_acc = 0
+    for s, x in enumerate(seqs):
+        ref = O.vsa_forward(x["q"][None], x["k"][None], x["v"][None], topk[s], x["gate"][None])
+        nq = -(-lens_q[s] // 64)
+        nkv = -(-lens_kv[s] // 64)
+        kk = min(topk[s], nkv)
+        sl = slice(oq, oq + lens_q[s])
+        assert np.array_equal(r["out"][:, sl], ref["out"][0]), s
+        assert np.array_equal(r["out_c"][:, nq_acc:nq_acc + nq], ref["out_c"][0]), s
+        got = r["q2k_idx"][:, nq_acc:nq_acc + nq]
+        assert np.array_equal(got[..., :kk], ref["q2k_idx"][0] + nkv_acc), s
+        assert (got[..., kk:] == -1).all()
+        assert (r["q2k_num"][:, nq_acc:nq_acc + nq] == kk).all()
+        pad = slice(oq + lens_q[s], oq + 64 * nq)
+        assert (r["out"][:, pad] == 0).all() and (r["out_s"][:, pad] == 0).all()
+        oq += 64 * nq
+        nq_acc += nq
+        nkv_acc += nkv
+
+
+def pin_single_sequence_varlen_equals_dense(seed=11):
+    q, k, v, g = _rand_dense(seed, B=1, H=2, nq=5, nkv=5, tail=0)
+    d = O.vsa_forward(q, k, v, 2, g)
+    r = O.vsa_forward_varlen(q[0], k[0], v[0], [q.shape[2]], [k.shape[2]], [2], g[0])
+    assert np.array_equal(r["out"], d["out"][0])
+    assert np.array_equal(r["q2k_idx"], d["q2k_idx"][0])
+
+
+# ---------------------------------------------------------------------------
+# magnitude sanity (statistics of N(0,1) inputs)
+# ---------------------------------------------------------------------------
+
+def pin_magnitudes(seed=12):
+    """With N(0,1) inputs and D = 128 the fine logits are ~N(0,1); the output
+    of attention over n tokens then has variance E[e^{2s}] / (n E[e^s]^2) =
+    e / n, n = 64 k.  Pooled tensors have variance 1/64 per entry, so the
+    coarse logits are ~0 and out_c averages nKV pooled values: variance 1/S."""
+    rng = _rng(seed)
+    H, nb, D, topk = 4, 24, 128, 6
+    S = 64 * nb
+    q, k, v = (rng.standard_normal((1, H, S, D)) for _ in range(3))
+    r = O.vsa_forward(q, k, v, topk, blocks=[(0, h, i) for h in range(H) for i in range(0, nb, 4)])
+    os_ = r["out_s"][np.isfinite(r["out_s"])]
+    rms_s = math.sqrt(np.mean(os_ ** 2))
+    assert abs(rms_s / math.sqrt(math.e / (64 * topk)) - 1) < 0.15, rms_s
+    rms_c = math.sqrt(np.mean(r["out_c"] ** 2))
+    assert abs(rms_c * math.sqrt(S) - 1) < 0.15, rms_c
+
+
+ALL_PINS = [
+    pin_block_sizes, pin_pool_partial_block, pin_two_token_closed_form,
+    pin_coarse_and_routing_closed_form, pin_combine_closed_form, pin_topk_bruteforce,
+    pin_topk_ties_and_order, pin_selection_property, pin_dense_equivalence,
+    pin_single_block, pin_permute_within_kv_block, pin_permute_kv_blocks,
+    pin_linear_in_v, pin_gate_special_values, pin_varlen_matches_per_sequence,
+    pin_single_sequence_varlen_equals_dense, pin_magnitudes,
+]

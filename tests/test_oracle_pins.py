@@ -1,0 +1,141 @@
+"""The oracle against its pins, and the pins against planted oracle mistakes.
+
+The mistakes are planted in the oracle, on the CPU (never in GPU code): each
+variant below is a plausible slip in writing the method down, and at least one
+pin must reject it.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.vsa_oracle as O
+from tests import oracle_pins as P
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes
+# ---------------------------------------------------------------------------
+
+def _sparse_no_scale(q_rows, k, v, kv_sizes, idx, block=64):
+    keys = np.concatenate([k[block * j: block * j + kv_sizes[j]] for j in idx])
+    vals = np.concatenate([v[block * j: block * j + kv_sizes[j]] for j in idx])
+    s = q_rows @ keys.T
+    w = np.exp(s - s.max(axis=1, keepdims=True))
+    return (w / w.sum(axis=1, keepdims=True)) @ vals
+
+
+def _pool_div64(x, sizes, block=64):
+    return np.stack([x[block * i: block * i + n].sum(axis=0) / block for i, n in enumerate(sizes)])
+
+
+def _pool_reads_padding(x, sizes, block=64):
+    return np.stack([x[block * i: block * i + block].mean(axis=0) for i, _ in enumerate(sizes)])
+
+
+def _coarse_no_scale(qc, kc, vc):
+    dots = qc @ kc.T
+    w = np.exp(dots - dots.max(axis=1, keepdims=True))
+    return dots, (w / w.sum(axis=1, keepdims=True)) @ vc
+
+
+def _coarse_transposed(qc, kc, vc):
+    # probabilities transposed before the value product (raises on non-square)
+    dots = qc @ kc.T
+    lg = dots / math.sqrt(qc.shape[1])
+    w = np.exp(lg - lg.max(axis=1, keepdims=True))
+    return dots, (w / w.sum(axis=1, keepdims=True)).T @ vc
+
+
+def _coarse_softmax_wrong_axis(qc, kc, vc):
+    dots = qc @ kc.T
+    lg = dots / math.sqrt(qc.shape[1])
+    w = np.exp(lg - lg.max(axis=0, keepdims=True))
+    return dots, (w / w.sum(axis=0, keepdims=True)) @ vc
+
+
+def _topk_high_index_ties(row, topk):
+    n = row.shape[0]
+    kk = min(topk, n)
+    order = np.lexsort((-np.arange(n), -row))
+    gap = float(row[order[kk - 1]] - row[order[kk]]) if kk < n else math.inf
+    return sorted(int(j) for j in order[:kk]), gap
+
+
+def _topk_unsorted(row, topk):
+    n = row.shape[0]
+    kk = min(topk, n)
+    order = np.lexsort((np.arange(n), -row))
+    gap = float(row[order[kk - 1]] - row[order[kk]]) if kk < n else math.inf
+    return [int(j) for j in order[:kk]], gap
+
+
+def _topk_smallest(row, topk):
+    return _orig_select(-row, topk)
+
+
+def _combine_gate_on_sparse(out_c_row, out_s_rows, gate_rows):
+    if gate_rows is None:
+        return out_c_row[None, :] + out_s_rows
+    g = gate_rows[:, None] if gate_rows.ndim == 1 else gate_rows
+    return out_c_row[None, :] + g * out_s_rows
+
+
+def _combine_drops_coarse(out_c_row, out_s_rows, gate_rows):
+    return out_s_rows + 0.0 * out_c_row[None, :]
+
+
+_orig_select = O.select_topk
+_orig_varlen = O.vsa_forward_varlen
+
+
+def _varlen_no_rebase(*a, **kw):
+    r = _orig_varlen(*a, **kw)
+    cu_kv = O.varlen_metadata(a[3], a[4])[3]
+    idx = r["q2k_idx"].copy()
+    for s in range(len(cu_kv) - 1):
+        rows = r["seq_of_block"] == s
+        sub = idx[:, rows]
+        sub[sub >= 0] -= cu_kv[s]
+        idx[:, rows] = sub
+    r["q2k_idx"] = idx
+    return r
+
+
+MISTAKES = {
+    "sparse_scale_dropped": ("sparse_block", _sparse_no_scale),
+    "pool_divides_by_64": ("pool", _pool_div64),
+    "pool_reads_padding": ("pool", _pool_reads_padding),
+    "coarse_scale_dropped": ("coarse", _coarse_no_scale),
+    "coarse_transposed_operand": ("coarse", _coarse_transposed),
+    "coarse_softmax_wrong_axis": ("coarse", _coarse_softmax_wrong_axis),
+    "topk_ties_to_higher_index": ("select_topk", _topk_high_index_ties),
+    "topk_not_ascending": ("select_topk", _topk_unsorted),
+    "topk_picks_smallest": ("select_topk", _topk_smallest),
+    "combine_gate_on_sparse": ("combine", _combine_gate_on_sparse),
+    "combine_drops_coarse": ("combine", _combine_drops_coarse),
+    "varlen_indices_not_rebased": ("vsa_forward_varlen", _varlen_no_rebase),
+}
+
+
+def _some_pin_fails():
+    failed = []
+    for pin in P.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            failed.append(pin.__name__)
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(MISTAKES))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, bad = MISTAKES[name]
+    monkeypatch.setattr(O, attr, bad)
+    failed = _some_pin_fails()
+    assert failed, f"no pin rejects the planted mistake {name}"
