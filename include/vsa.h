@@ -1,0 +1,271 @@
+/*
+ * vsa.h - C ABI of libvsa, the forward pass of video sparse attention (VSA)
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The method (taken from the FastVideo pages listed per entry point):
+ *   1. Q, K and V are cut into 64-token blocks;
+ *   2. a coarse branch pools every block to its mean and runs softmax
+ *      attention of the pooled queries over the pooled keys/values, giving one
+ *      coarse output row per query block (out_c, kept at block resolution);
+ *   3. for every query block the top-k KV blocks by coarse score are selected
+ *      (q2k_idx, q2k_num);
+ *   4. a block-sparse attention runs each query block over only its selected
+ *      KV blocks (out_s);
+ *   5. out = out_c * gate + out_s, out_c broadcast over the block's tokens
+ *      (out_c + out_s without a gate);
+ *   6. several sequences of different lengths can be packed, block-aligned,
+ *      into one tensor and handled in one launch per stage.
+ *
+ * Conventions shared by every entry point:
+ *   - bf16 tensors are passed as uint16_t storage (vsa_bf16), device memory;
+ *   - every device pointer must be 16-byte aligned unless stated otherwise;
+ *   - the caller owns every buffer; the library allocates no device memory
+ *     and keeps no state between calls except a per-thread error message;
+ *   - every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *     null stream) and performs no host-device synchronisation;
+ *   - all arguments are validated on the host before anything is launched; a
+ *     negative return value is an error code (VSA_ERR_*), nothing has been
+ *     launched in that case, and vsa_last_error() describes it;
+ *   - block_size must be 64 and head_dim 64 or 128.
+ *
+ * Layouts:
+ *   DENSE   q [B, H, Sq, D], k/v [B, H, Skv, D], out [B, H, Sq, D], each batch
+ *           item one sequence; block i of a sequence holds tokens
+ *           [64 i, min(64 i + 64, S)).
+ *   PACKED  block-padded packing of num_seqs sequences: q [H, 64*Nq, D],
+ *           k/v [H, 64*Nkv, D] with Nq/Nkv the total block counts; sequence s
+ *           owns global query blocks [cu_blocks_q[s], cu_blocks_q[s+1]) and KV
+ *           blocks [cu_blocks_kv[s], cu_blocks_kv[s+1]); global block g starts
+ *           at slot 64 g and its first block_sizes_*[g] slots are valid tokens
+ *           (the rest is padding, never read).
+ *   Block-resolution tensors: out_c is float32 [B, H, nQ, D] (DENSE) or
+ *   [H, Nq, D] (PACKED); q2k_num is int32 [B, H, nQ] or [H, Nq]; q2k_idx is
+ *   int32 [B, H, nQ, kk] with kk = min(topk, nKV) and per-sequence KV block
+ *   numbers (DENSE), or [H, Nq, max_topk] with GLOBAL KV block numbers and -1
+ *   after the first q2k_num entries (PACKED).  Selected indices are stored in
+ *   ascending order.
+ */
+#ifndef VSA_H
+#define VSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t vsa_bf16; /* bfloat16 bit pattern */
+typedef void *vsa_stream;  /* hipStream_t */
+
+#define VSA_BLOCK 64
+
+/* status codes */
+#define VSA_OK 0
+#define VSA_ERR_NULL (-1)        /* a required pointer is NULL */
+#define VSA_ERR_UNSUPPORTED (-2) /* block_size != 64, head_dim not 64/128, or a size over a limit */
+#define VSA_ERR_TOPK (-3)        /* topk < 1 */
+#define VSA_ERR_SHAPE (-4)       /* empty batch, zero-length sequence, inconsistent block counts */
+#define VSA_ERR_GATE (-5)        /* bad gate mode or strides */
+#define VSA_ERR_WORKSPACE (-6)   /* workspace missing or too small */
+#define VSA_ERR_ALIGN (-7)       /* pointer or stride not aligned as required */
+#define VSA_ERR_ALIAS (-8)       /* out overlaps an input */
+#define VSA_ERR_HIP (-9)         /* a HIP runtime call or kernel launch failed */
+
+/* layouts */
+#define VSA_LAYOUT_DENSE 0
+#define VSA_LAYOUT_PACKED 1
+
+/* gate modes: none; one value per (token, head) broadcast over D; full */
+#define VSA_GATE_NONE 0
+#define VSA_GATE_TOKEN 1
+#define VSA_GATE_FULL 2
+
+/*
+ * A problem description shared by the stage entry points.  For DENSE fill
+ * batch, seqlen_q, seqlen_kv and topk; the PACKED fields are ignored.  For
+ * PACKED fill the num_seqs..topk_per_seq block (device arrays as produced by
+ * vsa_build_metadata and copied to the device); batch/seqlen/topk are
+ * ignored.  The kernels never read outside the arrays whose lengths are given
+ * here, whatever values the device arrays hold: block sizes are clamped to
+ * [1, 64], per-sequence top-k to [1, min(max_topk, KV blocks)], and indices
+ * outside a query block's own sequence are skipped.
+ */
+typedef struct vsa_problem {
+    int32_t layout;     /* VSA_LAYOUT_DENSE or VSA_LAYOUT_PACKED */
+    int32_t heads;      /* H >= 1 */
+    int32_t head_dim;   /* D: 64 or 128 */
+    int32_t block_size; /* must be 64 */
+    /* DENSE */
+    int32_t batch;     /* B >= 1 */
+    int32_t seqlen_q;  /* Sq >= 1 */
+    int32_t seqlen_kv; /* Skv >= 1 */
+    int32_t topk;      /* >= 1, clamped to ceil(Skv/64) */
+    /* PACKED */
+    int32_t num_seqs;        /* >= 1 */
+    int32_t total_q_blocks;  /* Nq = cu_blocks_q[num_seqs] */
+    int32_t total_kv_blocks; /* Nkv = cu_blocks_kv[num_seqs] */
+    int32_t max_q_blocks;    /* max over sequences of query blocks */
+    int32_t max_kv_blocks;   /* max over sequences of KV blocks */
+    int32_t max_topk;        /* row length of q2k_idx, >= every per-sequence top-k */
+    const int32_t *cu_blocks_q;    /* device, [num_seqs + 1] */
+    const int32_t *cu_blocks_kv;   /* device, [num_seqs + 1] */
+    const int32_t *block_sizes_q;  /* device, [Nq], 1..64 */
+    const int32_t *block_sizes_kv; /* device, [Nkv], 1..64 */
+    const int32_t *topk_per_seq;   /* device, [num_seqs] */
+} vsa_problem;
+
+/* Sizes reported by vsa_build_metadata. */
+typedef struct vsa_meta_sizes {
+    int32_t num_seqs;
+    int32_t total_q_blocks;
+    int32_t total_kv_blocks;
+    int32_t max_q_blocks;
+    int32_t max_kv_blocks;
+    int32_t max_topk; /* max over sequences of min(topk, KV blocks) */
+    int64_t q_slots;  /* 64 * total_q_blocks: rows per head of packed q/out */
+    int64_t kv_slots; /* 64 * total_kv_blocks */
+} vsa_meta_sizes;
+
+/*
+ * vsa_build_metadata - host-side block metadata for PACKED sequences.
+ * ("[kernel] Add varlen support for block-sparse attention", Summary / How it
+ * works: block-aligned packing with 64 slots per block and rebasing of
+ * q2k_idx to global block offsets; "[kernel] Extract VSA utility functions
+ * into fastvideo_kernel": build_vsa_metadata, variable block sizes.)
+ *
+ * seqlens_q/seqlens_kv/topk are host arrays of num_seqs entries
+ * (seqlens_kv NULL means equal to seqlens_q).  `sizes` is always filled.
+ * The five output arrays are host arrays the caller allocates from `sizes`
+ * (pass all NULL to size them first): cu_blocks_q/kv [num_seqs + 1],
+ * block_sizes_q [total_q_blocks], block_sizes_kv [total_kv_blocks],
+ * topk_clamped [num_seqs] = min(topk[s], KV blocks of s).
+ * Errors: VSA_ERR_NULL (seqlens_q, topk or sizes NULL; some but not all
+ * outputs NULL), VSA_ERR_SHAPE (num_seqs < 1, a length < 1, totals beyond
+ * 2^31 slots), VSA_ERR_TOPK (a topk < 1).  No device memory is touched.
+ */
+int vsa_build_metadata(int32_t num_seqs, const int32_t *seqlens_q, const int32_t *seqlens_kv,
+                       const int32_t *topk, vsa_meta_sizes *sizes, int32_t *cu_blocks_q,
+                       int32_t *cu_blocks_kv, int32_t *block_sizes_q, int32_t *block_sizes_kv,
+                       int32_t *topk_clamped);
+
+/*
+ * vsa_workspace_size - bytes of device workspace the problem needs
+ * (vsa_coarse_topk, vsa_forward, vsa_forward_varlen).  It holds only
+ * block-resolution data: pooled Q/K/V in float64 plus, for the two forward
+ * calls, the float32 coarse output and the routing indices when the caller
+ * does not ask for them; it never scales with S*D (no full-sequence
+ * temporary, "[perf] avoid full-sequence materialization in VSA coarse/sparse
+ * combine", Change).  Returns 0 when the problem is invalid.
+ */
+size_t vsa_workspace_size(const vsa_problem *problem);
+
+/*
+ * vsa_coarse_topk - pool + coarse attention + top-k routing (steps 1-3).
+ * ("[perf] avoid full-sequence materialization in VSA coarse/sparse
+ * combine", Problem / Change / Correctness; "[chore] release fastvideo-kernel
+ * 0.3.0", Block-sparse / VSA attention improvements.)
+ *
+ * Reads q, k, v (bf16, layout per problem).  Writes out_c (float32,
+ * block-resolution), q2k_idx and q2k_num (int32, layouts above).  The pooled
+ * means and the coarse scores are computed in float64 and ties between equal
+ * scores go to the lower KV block.  workspace must hold
+ * vsa_workspace_size(problem) bytes (256-byte aligned).
+ * Limits: at most 4096 KV blocks per sequence (VSA_ERR_UNSUPPORTED).
+ */
+int vsa_coarse_topk(const vsa_problem *problem, const vsa_bf16 *q, const vsa_bf16 *k,
+                    const vsa_bf16 *v, float *out_c, int32_t *q2k_idx, int32_t *q2k_num,
+                    void *workspace, size_t workspace_bytes, vsa_stream stream);
+
+/*
+ * vsa_sparse_attn_from_indices - block-sparse attention of every query block
+ * over the KV blocks listed for it (step 4).  ("[chore] release
+ * fastvideo-kernel 0.3.0", Block-sparse / VSA attention improvements:
+ * block_sparse_attn_from_indices(q, k, v, q2k_idx, q2k_num,
+ * variable_block_sizes); PACKED is block_sparse_attn_varlen.)
+ *
+ * q2k_idx/q2k_num as written by vsa_coarse_topk (or any caller-made list in
+ * the same layout; row length min(topk, nKV) for DENSE, max_topk for
+ * PACKED).  Writes out (bf16, query layout): softmax over the valid tokens of
+ * the listed blocks, bf16 matrix products with float32 accumulation and
+ * float32 softmax.  In PACKED layout padding slots of out are written with 0.
+ * A query block whose list holds no valid block gets 0.  out must not overlap
+ * q, k or v (VSA_ERR_ALIAS).
+ */
+int vsa_sparse_attn_from_indices(const vsa_problem *problem, const vsa_bf16 *q,
+                                 const vsa_bf16 *k, const vsa_bf16 *v, const int32_t *q2k_idx,
+                                 const int32_t *q2k_num, vsa_bf16 *out, vsa_stream stream);
+
+/*
+ * vsa_combine - in place out = bf16(fma(out_c, gate, out)) (step 5), or
+ * bf16(out_c + out) for VSA_GATE_NONE; float32 arithmetic, one rounding;
+ * out_c is broadcast over the tokens of its block and never expanded.
+ * ("[perf] avoid full-sequence materialization in VSA coarse/sparse
+ * combine", Problem, Change and the follow-up comment on strict shapes and
+ * the gate passed as a transposed view.)
+ *
+ * gate_mode VSA_GATE_TOKEN: gate[b*s0 + h*s1 + t*s2] for DENSE and
+ * gate[h*s1 + slot*s2] for PACKED; VSA_GATE_FULL: the same plus d (stride 1);
+ * gate_strides = {s0, s1, s2} in elements, or NULL for the contiguous
+ * [B, H, Sq(, D)] / [H, slots(, D)] layout.  A transposed [B, S, H(, D)]
+ * view is accepted without a copy.  FULL requires the three strides to be
+ * multiples of 8 (VSA_ERR_ALIGN); strides must be >= 0 (VSA_ERR_GATE).
+ * Padding slots of PACKED out are left untouched.
+ */
+int vsa_combine(const vsa_problem *problem, const float *out_c, const vsa_bf16 *gate,
+                int32_t gate_mode, const int64_t *gate_strides, vsa_bf16 *out,
+                vsa_stream stream);
+
+/*
+ * vsa_forward - the whole DENSE forward: vsa_coarse_topk, then
+ * vsa_sparse_attn_from_indices into out, then vsa_combine in place.
+ * ("FastVideo Kernel" README, Usage: video_sparse_attn(q, k, v, block_sizes,
+ * block_sizes, topk); "[perf] avoid full-sequence materialization ...",
+ * Problem.)
+ *
+ * q [B,H,Sq,D], k/v [B,H,Skv,D], out [B,H,Sq,D], bf16.  gate as in
+ * vsa_combine (gate_strides may be NULL).  q2k_idx, q2k_num and out_c are
+ * optional outputs (NULL: kept in the workspace).  workspace must hold
+ * vsa_workspace_size() bytes for the matching DENSE problem.
+ */
+int vsa_forward(const vsa_bf16 *q, const vsa_bf16 *k, const vsa_bf16 *v, const vsa_bf16 *gate,
+                int32_t gate_mode, const int64_t *gate_strides, vsa_bf16 *out, int32_t *q2k_idx,
+                int32_t *q2k_num, float *out_c, int32_t batch, int32_t heads, int32_t seqlen_q,
+                int32_t seqlen_kv, int32_t head_dim, int32_t block_size, int32_t topk,
+                void *workspace, size_t workspace_bytes, vsa_stream stream);
+
+/*
+ * vsa_forward_varlen - the whole PACKED forward in one launch per stage over
+ * all sequences ("[kernel] Add varlen support for block-sparse attention",
+ * Summary / How it works; "[chore] release fastvideo-kernel 0.3.0",
+ * varlen block-sparse attention with Q/KV length mismatch).
+ *
+ * q [H, 64*Nq, D], k/v [H, 64*Nkv, D], out [H, 64*Nq, D] (padding slots of out
+ * are written with 0).  The device metadata arrays and sizes are those of
+ * vsa_build_metadata (topk_per_seq = its topk_clamped).  q2k_idx holds global
+ * KV block numbers.  Optional outputs and workspace as for vsa_forward.
+ */
+int vsa_forward_varlen(const vsa_bf16 *q, const vsa_bf16 *k, const vsa_bf16 *v,
+                       const vsa_bf16 *gate, int32_t gate_mode, const int64_t *gate_strides,
+                       vsa_bf16 *out, int32_t *q2k_idx, int32_t *q2k_num, float *out_c,
+                       const int32_t *cu_blocks_q, const int32_t *cu_blocks_kv,
+                       const int32_t *block_sizes_q, const int32_t *block_sizes_kv,
+                       const int32_t *topk_per_seq, int32_t num_seqs, int32_t total_q_blocks,
+                       int32_t total_kv_blocks, int32_t max_q_blocks, int32_t max_kv_blocks,
+                       int32_t max_topk, int32_t heads, int32_t head_dim, int32_t block_size,
+                       void *workspace, size_t workspace_bytes, vsa_stream stream);
+
+/* Text for a status code (static storage). */
+const char *vsa_status_string(int status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char *vsa_last_error(void);
+
+/* Library version string. */
+const char *vsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSA_H */

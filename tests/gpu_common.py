@@ -1,0 +1,99 @@
+"""Shared pieces of the GPU parity tests: running the HIP path through the C ABI
+on seeded workloads and running the oracle on the same inputs."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+import video_sparse_attention_amd as vsa
+from tests.numerics import f64
+
+DEV = "cuda:0"
+
+
+def note(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_dense_stages(inp, dev=DEV, idx_override=None):
+    """Stage calls on a dense workload: returns dict with out, out_s, out_c,
+    q2k_idx, q2k_num (CPU tensors).  With ``idx_override`` (numpy idx, num) the
+    sparse stage runs on those indices instead of the GPU's own."""
+    B, H, Sq, Skv, D = inp.shape
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    gate = None if inp.gate is None else inp.gate.to(dev)
+    prob = vsa.dense_problem(B, H, Sq, Skv, D, inp.topk)
+    cs, isz, ns = vsa.block_shapes(prob)
+    out_c = torch.empty(cs, dtype=torch.float32, device=dev)
+    idx = torch.empty(isz, dtype=torch.int32, device=dev)
+    num = torch.empty(ns, dtype=torch.int32, device=dev)
+    ws = vsa.alloc_workspace(prob, dev)
+    vsa.vsa_coarse_topk(prob, q, k, v, out_c, idx, num, ws)
+    if idx_override is not None:
+        sidx = torch.from_numpy(np.ascontiguousarray(idx_override[0])).to(dev)
+        snum = torch.from_numpy(np.ascontiguousarray(idx_override[1])).to(dev)
+    else:
+        sidx, snum = idx, num
+    out = torch.empty_like(q)
+    vsa.vsa_sparse_attn_from_indices(prob, q, k, v, sidx, snum, out)
+    out_s = out.clone()
+    vsa.vsa_combine(prob, out_c, gate, out)
+    torch.cuda.synchronize()
+    return dict(out=out.cpu(), out_s=out_s.cpu(), out_c=out_c.cpu(), q2k_idx=idx.cpu(),
+                q2k_num=num.cpu())
+
+
+def run_varlen_stages(inp, dev=DEV, idx_override=None):
+    meta = vsa.vsa_build_metadata(inp.seqlens_q, inp.seqlens_kv, inp.topk, device=dev)
+    H, D = inp.heads, inp.head_dim
+    prob = meta.problem(H, D)
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    gate = None if inp.gate is None else inp.gate.to(dev)
+    cs, isz, ns = vsa.block_shapes(prob)
+    out_c = torch.empty(cs, dtype=torch.float32, device=dev)
+    idx = torch.empty(isz, dtype=torch.int32, device=dev)
+    num = torch.empty(ns, dtype=torch.int32, device=dev)
+    ws = vsa.alloc_workspace(prob, dev)
+    vsa.vsa_coarse_topk(prob, q, k, v, out_c, idx, num, ws)
+    if idx_override is not None:
+        sidx = torch.from_numpy(np.ascontiguousarray(idx_override[0])).to(dev)
+        snum = torch.from_numpy(np.ascontiguousarray(idx_override[1])).to(dev)
+    else:
+        sidx, snum = idx, num
+    out = torch.full_like(q, float("nan"))  # padding slots must come back as 0
+    vsa.vsa_sparse_attn_from_indices(prob, q, k, v, sidx, snum, out)
+    out_s = out.clone()
+    vsa.vsa_combine(prob, out_c, gate, out)
+    torch.cuda.synchronize()
+    return dict(out=out.cpu(), out_s=out_s.cpu(), out_c=out_c.cpu(), q2k_idx=idx.cpu(),
+                q2k_num=num.cpu(), meta=meta)
+
+
+def oracle_dense(inp, blocks=None):
+    g = None if inp.gate is None else f64(inp.gate)
+    return oracle.vsa_forward(f64(inp.q), f64(inp.k), f64(inp.v), inp.topk, g, blocks=blocks)
+
+
+def oracle_varlen(inp, blocks=None):
+    g = None if inp.gate is None else f64(inp.gate)
+    return oracle.vsa_forward_varlen(f64(inp.q), f64(inp.k), f64(inp.v), inp.seqlens_q,
+                                     inp.seqlens_kv, inp.topk, g, blocks=blocks)
+
+
+def assert_tie_free(ref):
+    ok, min_gap, nbad = oracle.tie_free(ref["gap"], float(np.max(ref["max_abs_dot"])))
+    note(f"  routing margin: min gap {min_gap:.3e}, rows at/below threshold {nbad}")
+    assert ok, f"inputs are not tie-free ({nbad} rows), index parity is not meaningful"
+
+
+def assert_indices_equal(gpu_idx, gpu_num, ref):
+    gi = gpu_idx.numpy()
+    gn = gpu_num.numpy()
+    assert np.array_equal(gn, ref["q2k_num"]), "q2k_num differs"
+    assert np.array_equal(gi, ref["q2k_idx"]), \
+        f"q2k_idx differs in {int((gi != ref['q2k_idx']).any(axis=-1).sum())} rows"

@@ -1,0 +1,246 @@
+"""CPU tests of libvsa's host side: exported symbols, metadata, workspace sizing
+and every validation error.  No kernel is launched: every call here fails
+validation before any HIP call (fake device addresses are never touched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from video_sparse_attention_amd import _abi
+from video_sparse_attention_amd._abi import VsaMetaSizes, VsaProblem
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vsa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _abi.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vsa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("vsa_build_metadata", "vsa_workspace_size", "vsa_forward", "vsa_forward_varlen",
+              "vsa_coarse_topk", "vsa_sparse_attn_from_indices", "vsa_combine",
+              "vsa_status_string", "vsa_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _abi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (vsa_\w+)", out))
+    assert set(declared_functions()) <= exported
+    assert set(_abi.SIGNATURES) == set(declared_functions())
+
+
+def test_status_strings(lib):
+    for code in range(-9, 1):
+        s = lib.vsa_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.vsa_status_string(-99).decode() == "unknown status"
+    assert b"gfx950" in lib.vsa_version()
+
+
+# ---------------------------------------------------------------------------
+# metadata
+# ---------------------------------------------------------------------------
+
+def _meta(lib, sq, skv, topk):
+    n = len(sq)
+    arr = lambda xs: (ctypes.c_int32 * max(len(xs), 1))(*xs)
+    sizes = VsaMetaSizes()
+    rc = lib.vsa_build_metadata(n, arr(sq), None if skv is None else arr(skv), arr(topk),
+                                ctypes.byref(sizes), None, None, None, None, None)
+    if rc:
+        return rc, sizes, None
+    bufs = [(ctypes.c_int32 * (n + 1))(), (ctypes.c_int32 * (n + 1))(),
+            (ctypes.c_int32 * sizes.total_q_blocks)(), (ctypes.c_int32 * sizes.total_kv_blocks)(),
+            (ctypes.c_int32 * n)()]
+    rc = lib.vsa_build_metadata(n, arr(sq), None if skv is None else arr(skv), arr(topk),
+                                ctypes.byref(sizes), *bufs)
+    return rc, sizes, [list(b) for b in bufs]
+
+
+@pytest.mark.parametrize("sq,skv,topk", [
+    ([320, 576, 872], None, [2, 3, 4]),
+    ([64 * n for n in range(32, 145, 16)], [64 * (n + 8) for n in range(32, 145, 16)],
+     [8, 12, 15, 18, 21, 24, 28, 31]),
+    ([1, 65, 130], [200, 1, 64], [5, 1, 1]),
+])
+def test_metadata_matches_oracle(lib, sq, skv, topk):
+    rc, sizes, (cu_q, cu_kv, bs_q, bs_kv, tk) = _meta(lib, sq, skv, topk)
+    assert rc == 0
+    skv_ = sq if skv is None else skv
+    qsz, ksz, ocu_q, ocu_kv = oracle.varlen_metadata(sq, skv_)
+    assert cu_q == list(ocu_q) and cu_kv == list(ocu_kv)
+    assert bs_q == [n for x in qsz for n in x] and bs_kv == [n for x in ksz for n in x]
+    assert tk == [min(t, len(k)) for t, k in zip(topk, ksz)]
+    assert sizes.total_q_blocks == ocu_q[-1] and sizes.total_kv_blocks == ocu_kv[-1]
+    assert sizes.max_q_blocks == max(len(x) for x in qsz)
+    assert sizes.max_kv_blocks == max(len(x) for x in ksz)
+    assert sizes.max_topk == max(tk)
+    assert sizes.q_slots == 64 * ocu_q[-1] and sizes.kv_slots == 64 * ocu_kv[-1]
+
+
+def test_metadata_errors(lib):
+    assert _meta(lib, [], None, [])[0] == _abi.VSA_ERR_SHAPE            # empty batch
+    assert _meta(lib, [64, 0], None, [1, 1])[0] == _abi.VSA_ERR_SHAPE   # zero-length sequence
+    assert _meta(lib, [64], [0], [1])[0] == _abi.VSA_ERR_SHAPE
+    assert _meta(lib, [64, 64], None, [1, 0])[0] == _abi.VSA_ERR_TOPK   # topk < 1
+    sizes = VsaMetaSizes()
+    one = (ctypes.c_int32 * 1)(64)
+    assert lib.vsa_build_metadata(1, None, None, one, ctypes.byref(sizes),
+                                  None, None, None, None, None) == _abi.VSA_ERR_NULL
+    assert lib.vsa_build_metadata(1, one, None, one, None, None, None, None, None, None) == _abi.VSA_ERR_NULL
+    buf = (ctypes.c_int32 * 2)()
+    assert lib.vsa_build_metadata(1, one, None, one, ctypes.byref(sizes), buf, None, None, None,
+                                  None) == _abi.VSA_ERR_NULL  # some outputs but not all
+    assert lib.vsa_build_metadata(1, (ctypes.c_int32 * 1)(2 ** 31 - 1), None, one, ctypes.byref(sizes),
+                                  None, None, None, None, None) == _abi.VSA_ERR_SHAPE
+
+
+# ---------------------------------------------------------------------------
+# workspace
+# ---------------------------------------------------------------------------
+
+def dense(B=1, H=2, Sq=1000, Skv=1000, D=128, topk=3, bs=64):
+    return VsaProblem(layout=0, heads=H, head_dim=D, block_size=bs, batch=B, seqlen_q=Sq,
+                      seqlen_kv=Skv, topk=topk)
+
+
+FAKE = 0x7f0000000000  # 256-aligned, never dereferenced
+
+
+def packed(num_seqs=2, nq=5, nkv=6, mq=3, mkv=4, mk=2, H=2, D=64, ptrs=True):
+    p = [FAKE + 4096 * i for i in range(5)] if ptrs else [None] * 5
+    return VsaProblem(layout=1, heads=H, head_dim=D, block_size=64, num_seqs=num_seqs,
+                      total_q_blocks=nq, total_kv_blocks=nkv, max_q_blocks=mq, max_kv_blocks=mkv,
+                      max_topk=mk, cu_blocks_q=p[0], cu_blocks_kv=p[1], block_sizes_q=p[2],
+                      block_sizes_kv=p[3], topk_per_seq=p[4])
+
+
+def test_workspace_is_block_resolution(lib):
+    """The workspace never holds a full-sequence tensor: it is a fixed fraction of
+    one [B,H,S,D] bf16 tensor, from block-resolution float64 pooled Q/K/V, the
+    float32 coarse output and the routing indices."""
+    sizes = []
+    for S in (64 * 10, 64 * 100, 64 * 242):
+        p = dense(B=1, H=56, Sq=S, Skv=S, D=128, topk=49)
+        ws = lib.vsa_workspace_size(ctypes.byref(p))
+        full = 56 * S * 128 * 2
+        assert 0 < ws < 0.3 * full
+        sizes.append(ws)
+    p = packed()
+    assert lib.vsa_workspace_size(ctypes.byref(p)) > 0
+    assert lib.vsa_workspace_size(ctypes.byref(dense(bs=32))) == 0
+
+
+# ---------------------------------------------------------------------------
+# validation errors of the compute entry points (no launch happens)
+# ---------------------------------------------------------------------------
+
+A = ctypes.c_void_p(FAKE)
+B_ = ctypes.c_void_p(FAKE + (1 << 32))
+C_ = ctypes.c_void_p(FAKE + (2 << 32))
+O_ = ctypes.c_void_p(FAKE + (3 << 32))
+W_ = ctypes.c_void_p(FAKE + (4 << 32))
+G_ = ctypes.c_void_p(FAKE + (5 << 32))
+
+
+def coarse(lib, p, q=A, k=B_, v=C_, oc=O_, idx=G_, num=G_, ws=W_, wsb=1 << 40):
+    return lib.vsa_coarse_topk(ctypes.byref(p), q, k, v, oc, idx, num, ws, wsb, None)
+
+
+def sparse(lib, p, q=A, k=B_, v=C_, idx=G_, num=G_, out=O_):
+    return lib.vsa_sparse_attn_from_indices(ctypes.byref(p), q, k, v, idx, num, out, None)
+
+
+def comb(lib, p, oc=C_, gate=G_, mode=1, st=None, out=O_):
+    return lib.vsa_combine(ctypes.byref(p), oc, gate, mode, st, out, None)
+
+
+def fwd(lib, q=A, k=B_, v=C_, gate=None, mode=0, st=None, out=O_, B=1, H=2, Sq=1000, Skv=1000,
+        D=128, bs=64, topk=3, ws=W_, wsb=1 << 40):
+    return lib.vsa_forward(q, k, v, gate, mode, st, out, None, None, None, B, H, Sq, Skv, D, bs,
+                           topk, ws, wsb, None)
+
+
+E = _abi
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda L: coarse(L, dense(), q=None), E.VSA_ERR_NULL),
+    (lambda L: coarse(L, dense(), oc=None), E.VSA_ERR_NULL),
+    (lambda L: coarse(L, dense(), ws=None), E.VSA_ERR_WORKSPACE),
+    (lambda L: coarse(L, dense(), wsb=100), E.VSA_ERR_WORKSPACE),
+    (lambda L: coarse(L, dense(), ws=ctypes.c_void_p(FAKE + 64)), E.VSA_ERR_ALIGN),
+    (lambda L: coarse(L, dense(), k=ctypes.c_void_p(FAKE + 2)), E.VSA_ERR_ALIGN),
+    (lambda L: coarse(L, dense(bs=128)), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: coarse(L, dense(D=96)), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: coarse(L, dense(topk=0)), E.VSA_ERR_TOPK),
+    (lambda L: coarse(L, dense(B=0)), E.VSA_ERR_SHAPE),
+    (lambda L: coarse(L, dense(H=0)), E.VSA_ERR_SHAPE),
+    (lambda L: coarse(L, dense(Sq=0)), E.VSA_ERR_SHAPE),
+    (lambda L: coarse(L, dense(Skv=0)), E.VSA_ERR_SHAPE),
+    (lambda L: coarse(L, dense(Skv=64 * 4097)), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: coarse(L, packed(num_seqs=0)), E.VSA_ERR_SHAPE),
+    (lambda L: coarse(L, packed(ptrs=False)), E.VSA_ERR_NULL),
+    (lambda L: coarse(L, packed(nq=1, num_seqs=2)), E.VSA_ERR_SHAPE),
+    (lambda L: coarse(L, packed(mq=9)), E.VSA_ERR_SHAPE),
+    (lambda L: coarse(L, packed(mk=0)), E.VSA_ERR_TOPK),
+    (lambda L: sparse(L, dense(), idx=None), E.VSA_ERR_NULL),
+    (lambda L: sparse(L, dense(), out=ctypes.c_void_p(FAKE + 1000 * 128)), E.VSA_ERR_ALIAS),
+    (lambda L: sparse(L, dense(), out=ctypes.c_void_p(FAKE + (1 << 32) + 4096)), E.VSA_ERR_ALIAS),
+    (lambda L: sparse(L, dense(), out=ctypes.c_void_p(FAKE + (3 << 32) + 8)), E.VSA_ERR_ALIGN),
+    (lambda L: comb(L, dense(), mode=3), E.VSA_ERR_GATE),
+    (lambda L: comb(L, dense(), gate=None), E.VSA_ERR_NULL),
+    (lambda L: comb(L, dense(), st=(ctypes.c_int64 * 3)(-1, 1, 1)), E.VSA_ERR_GATE),
+    (lambda L: comb(L, dense(), st=(ctypes.c_int64 * 3)(2000, 0, 1)), E.VSA_ERR_GATE),
+    (lambda L: comb(L, dense(), mode=2, st=(ctypes.c_int64 * 3)(8, 8, 12)), E.VSA_ERR_ALIGN),
+    (lambda L: comb(L, dense(), gate=ctypes.c_void_p(FAKE + (5 << 32) + 1)), E.VSA_ERR_ALIGN),
+    (lambda L: comb(L, dense(), gate=ctypes.c_void_p(FAKE + (3 << 32) + 64)), E.VSA_ERR_ALIAS),
+    (lambda L: comb(L, dense(), oc=None), E.VSA_ERR_NULL),
+    (lambda L: fwd(L, out=A), E.VSA_ERR_ALIAS),
+    (lambda L: fwd(L, wsb=10), E.VSA_ERR_WORKSPACE),
+    (lambda L: fwd(L, mode=1, gate=None), E.VSA_ERR_NULL),
+    (lambda L: fwd(L, B=0), E.VSA_ERR_SHAPE),
+    (lambda L: fwd(L, topk=-1), E.VSA_ERR_TOPK),
+    (lambda L: fwd(L, bs=32), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: L.vsa_forward_varlen(A, B_, C_, None, 0, None, O_, None, None, None,
+                                    None, G_, G_, G_, G_, 1, 1, 1, 1, 1, 1, 2, 64, 64, W_,
+                                    1 << 40, None), E.VSA_ERR_NULL),
+    (lambda L: L.vsa_forward_varlen(A, B_, C_, None, 0, None, O_, None, None, None,
+                                    G_, G_, G_, G_, G_, 0, 1, 1, 1, 1, 1, 2, 64, 64, W_,
+                                    1 << 40, None), E.VSA_ERR_SHAPE),
+])
+def test_validation_errors(lib, call, code):
+    rc = call(lib)
+    assert rc == code, (rc, lib.vsa_last_error())
+    assert lib.vsa_last_error()
+
+
+def test_layout_maps_on_cpu(tmp_path):
+    """Compile and run the host-only check of the attention kernel's index maps
+    (bijections, bounds, MFMA k-slot relabelling, LDS bank model, XCD remap)."""
+    exe = tmp_path / "layout_check"
+    src = os.path.join(ROOT, "tests", "cpp", "layout_check.hip")
+    inc = [f"-I{os.path.join(ROOT, 'video_sparse_attention_amd', 'csrc')}",
+           f"-I{os.path.join(ROOT, 'include')}"]
+    subprocess.run(["hipcc", "-O1", "-std=c++17", *inc, src, "-o", str(exe)], check=True,
+                   capture_output=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "layout checks passed" in r.stdout

@@ -1,0 +1,30 @@
+"""Video sparse attention (VSA) forward for AMD Instinct MI355X (gfx950).
+
+The computation lives in ``lib/libvsa.so`` (hand-written HIP kernels behind
+the C ABI of ``include/vsa.h``); this package is its thin PyTorch binding.
+Every entry point loads the library on first use and raises ``ImportError``
+if it has not been built (there is no fallback path).
+"""
+from ._abi import VsaError, load as load_library  # noqa: F401
+
+from .binding import (  # noqa: E402,F401
+    BLOCK,
+    VarlenMeta,
+    alloc_workspace,
+    block_shapes,
+    dense_problem,
+    token_shapes,
+    vsa_build_metadata,
+    vsa_coarse_topk,
+    vsa_combine,
+    vsa_forward,
+    vsa_forward_varlen,
+    vsa_sparse_attn_from_indices,
+    vsa_workspace_size,
+)
+
+__all__ = [
+    "BLOCK", "VarlenMeta", "VsaError", "alloc_workspace", "block_shapes", "dense_problem",
+    "token_shapes", "vsa_build_metadata", "vsa_coarse_topk", "vsa_combine", "vsa_forward",
+    "vsa_forward_varlen", "vsa_sparse_attn_from_indices", "vsa_workspace_size",
+]

@@ -1,0 +1,299 @@
+"""Thin PyTorch binding over libvsa: argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI
+(``include/vsa.h``); this module checks tensor shapes, dtypes and devices,
+takes device memory from PyTorch (outputs, workspace), passes raw pointers
+and the current HIP stream, and turns error codes into ``VsaError``.  The
+function names are those of the C entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import _abi
+from ._abi import (VSA_GATE_FULL, VSA_GATE_NONE, VSA_GATE_TOKEN, VSA_LAYOUT_DENSE,
+                   VSA_LAYOUT_PACKED, VsaError, VsaMetaSizes, VsaProblem)
+
+BLOCK = 64
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None, contiguous=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.requires_grad:
+        raise RuntimeError(f"{name} requires grad: the VSA forward here has no backward")
+
+
+def _gate_args(gate: Optional[torch.Tensor], token_shape, full_shape):
+    """(mode, strides array or None) for a gate tensor, strict on shape."""
+    if gate is None:
+        return VSA_GATE_NONE, None
+    _need(gate, "gate", torch.bfloat16, contiguous=False)
+    shp = tuple(gate.shape)
+    if shp == tuple(token_shape):
+        mode = VSA_GATE_TOKEN
+        st = list(gate.stride())
+    elif shp == tuple(full_shape):
+        if gate.stride(-1) != 1:
+            raise ValueError("a full gate needs unit stride over head_dim")
+        mode = VSA_GATE_FULL
+        st = list(gate.stride()[:-1])
+    else:
+        raise ValueError(f"gate has shape {shp}, expected {tuple(token_shape)} or {tuple(full_shape)}")
+    if len(st) == 2:  # packed: [H, slots(, D)] -> (unused, head, slot)
+        st = [0] + st
+    return mode, (ctypes.c_int64 * 3)(*st)
+
+
+# ---------------------------------------------------------------------------
+# metadata and problems
+# ---------------------------------------------------------------------------
+
+@dataclass
+class VarlenMeta:
+    sizes: VsaMetaSizes
+    seqlens_q: List[int]
+    seqlens_kv: List[int]
+    cu_blocks_q: torch.Tensor      # host int32 [num_seqs + 1]
+    cu_blocks_kv: torch.Tensor
+    block_sizes_q: torch.Tensor    # host int32 [Nq]
+    block_sizes_kv: torch.Tensor
+    topk: torch.Tensor             # host int32 [num_seqs], clamped
+    device_arrays: Optional[dict] = None
+
+    def to(self, device) -> "VarlenMeta":
+        names = ("cu_blocks_q", "cu_blocks_kv", "block_sizes_q", "block_sizes_kv", "topk")
+        self.device_arrays = {n: getattr(self, n).to(device) for n in names}
+        return self
+
+    def problem(self, heads: int, head_dim: int) -> VsaProblem:
+        if self.device_arrays is None:
+            raise RuntimeError("call .to(device) before building a packed problem")
+        d = self.device_arrays
+        s = self.sizes
+        return VsaProblem(
+            layout=VSA_LAYOUT_PACKED, heads=heads, head_dim=head_dim, block_size=BLOCK,
+            num_seqs=s.num_seqs, total_q_blocks=s.total_q_blocks,
+            total_kv_blocks=s.total_kv_blocks, max_q_blocks=s.max_q_blocks,
+            max_kv_blocks=s.max_kv_blocks, max_topk=s.max_topk,
+            cu_blocks_q=d["cu_blocks_q"].data_ptr(), cu_blocks_kv=d["cu_blocks_kv"].data_ptr(),
+            block_sizes_q=d["block_sizes_q"].data_ptr(),
+            block_sizes_kv=d["block_sizes_kv"].data_ptr(), topk_per_seq=d["topk"].data_ptr())
+
+
+def vsa_build_metadata(seqlens_q: Sequence[int], seqlens_kv: Optional[Sequence[int]] = None,
+                       topk: Sequence[int] = (), device=None) -> VarlenMeta:
+    """Host block metadata for packed sequences (vsa_build_metadata)."""
+    lib = _abi.load()
+    n = len(seqlens_q)
+    sq = (ctypes.c_int32 * max(n, 1))(*seqlens_q)
+    skv = None if seqlens_kv is None else (ctypes.c_int32 * max(n, 1))(*seqlens_kv)
+    if len(topk) != n:
+        raise ValueError("topk needs one entry per sequence")
+    tk = (ctypes.c_int32 * max(n, 1))(*topk)
+    sizes = VsaMetaSizes()
+    _abi.check(lib.vsa_build_metadata(n, sq, skv, tk, ctypes.byref(sizes),
+                                      None, None, None, None, None), "vsa_build_metadata")
+    cu_q = torch.zeros(n + 1, dtype=torch.int32)
+    cu_kv = torch.zeros(n + 1, dtype=torch.int32)
+    bs_q = torch.zeros(sizes.total_q_blocks, dtype=torch.int32)
+    bs_kv = torch.zeros(sizes.total_kv_blocks, dtype=torch.int32)
+    tkc = torch.zeros(n, dtype=torch.int32)
+    _abi.check(lib.vsa_build_metadata(n, sq, skv, tk, ctypes.byref(sizes), _ptr(cu_q), _ptr(cu_kv),
+                                      _ptr(bs_q), _ptr(bs_kv), _ptr(tkc)), "vsa_build_metadata")
+    meta = VarlenMeta(sizes, list(seqlens_q), list(seqlens_q if seqlens_kv is None else seqlens_kv),
+                      cu_q, cu_kv, bs_q, bs_kv, tkc)
+    return meta.to(device) if device is not None else meta
+
+
+def dense_problem(batch: int, heads: int, seqlen_q: int, seqlen_kv: int, head_dim: int,
+                  topk: int) -> VsaProblem:
+    return VsaProblem(layout=VSA_LAYOUT_DENSE, heads=heads, head_dim=head_dim, block_size=BLOCK,
+                      batch=batch, seqlen_q=seqlen_q, seqlen_kv=seqlen_kv, topk=topk)
+
+
+def vsa_workspace_size(problem: VsaProblem) -> int:
+    return int(_abi.load().vsa_workspace_size(ctypes.byref(problem)))
+
+
+def alloc_workspace(problem: VsaProblem, device) -> torch.Tensor:
+    n = vsa_workspace_size(problem)
+    if n == 0:
+        raise VsaError(_abi.VSA_ERR_SHAPE, (_abi.load().vsa_last_error() or b"").decode(),
+                       "vsa_workspace_size")
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + n]
+
+
+def block_shapes(problem: VsaProblem):
+    """(out_c shape, q2k_idx shape, q2k_num shape) of a problem."""
+    if problem.layout == VSA_LAYOUT_DENSE:
+        nq = -(-problem.seqlen_q // BLOCK)
+        nkv = -(-problem.seqlen_kv // BLOCK)
+        kk = min(problem.topk, nkv)
+        b, h, d = problem.batch, problem.heads, problem.head_dim
+        return (b, h, nq, d), (b, h, nq, kk), (b, h, nq)
+    h, nq, d = problem.heads, problem.total_q_blocks, problem.head_dim
+    return (h, nq, d), (h, nq, problem.max_topk), (h, nq)
+
+
+def token_shapes(problem: VsaProblem):
+    """(q/out shape, k/v shape) of a problem."""
+    h, d = problem.heads, problem.head_dim
+    if problem.layout == VSA_LAYOUT_DENSE:
+        b = problem.batch
+        return (b, h, problem.seqlen_q, d), (b, h, problem.seqlen_kv, d)
+    return (h, BLOCK * problem.total_q_blocks, d), (h, BLOCK * problem.total_kv_blocks, d)
+
+
+# ---------------------------------------------------------------------------
+# stage entry points
+# ---------------------------------------------------------------------------
+
+def _check_qkv(problem, q, k, v):
+    qs, ks = token_shapes(problem)
+    _need(q, "q", torch.bfloat16, qs)
+    _need(k, "k", torch.bfloat16, ks)
+    _need(v, "v", torch.bfloat16, ks)
+
+
+def vsa_coarse_topk(problem: VsaProblem, q, k, v, out_c, q2k_idx, q2k_num, workspace) -> None:
+    _check_qkv(problem, q, k, v)
+    cs, isz, ns = block_shapes(problem)
+    _need(out_c, "out_c", torch.float32, cs)
+    _need(q2k_idx, "q2k_idx", torch.int32, isz)
+    _need(q2k_num, "q2k_num", torch.int32, ns)
+    _need(workspace, "workspace", torch.uint8)
+    _abi.check(_abi.load().vsa_coarse_topk(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(out_c), _ptr(q2k_idx),
+        _ptr(q2k_num), _ptr(workspace), workspace.numel(), _stream(q.device)), "vsa_coarse_topk")
+
+
+def vsa_sparse_attn_from_indices(problem: VsaProblem, q, k, v, q2k_idx, q2k_num, out) -> None:
+    _check_qkv(problem, q, k, v)
+    _, isz, ns = block_shapes(problem)
+    if tuple(q2k_idx.shape[:-1]) != tuple(isz[:-1]):
+        raise ValueError(f"q2k_idx has shape {tuple(q2k_idx.shape)}, expected {isz[:-1]} + (k,)")
+    if problem.layout == VSA_LAYOUT_DENSE and q2k_idx.shape[-1] != isz[-1]:
+        raise ValueError(f"q2k_idx rows must hold min(topk, nKV) = {isz[-1]} entries")
+    _need(q2k_idx, "q2k_idx", torch.int32)
+    _need(q2k_num, "q2k_num", torch.int32, ns)
+    _need(out, "out", torch.bfloat16, token_shapes(problem)[0])
+    _abi.check(_abi.load().vsa_sparse_attn_from_indices(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(q2k_idx), _ptr(q2k_num), _ptr(out),
+        _stream(q.device)), "vsa_sparse_attn_from_indices")
+
+
+def _gate_shapes(problem):
+    qs = token_shapes(problem)[0]
+    return qs[:-1], qs
+
+
+def vsa_combine(problem: VsaProblem, out_c, gate, out) -> None:
+    cs, _, _ = block_shapes(problem)
+    _need(out_c, "out_c", torch.float32, cs)
+    _need(out, "out", torch.bfloat16, token_shapes(problem)[0])
+    mode, st = _gate_args(gate, *_gate_shapes(problem))
+    _abi.check(_abi.load().vsa_combine(
+        ctypes.byref(problem), _ptr(out_c), _ptr(gate), mode, st, _ptr(out),
+        _stream(out.device)), "vsa_combine")
+
+
+# ---------------------------------------------------------------------------
+# whole forward
+# ---------------------------------------------------------------------------
+
+def vsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int,
+                gate: Optional[torch.Tensor] = None, *, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, return_aux: bool = False):
+    """VSA forward on dense ``[B, H, S, D]`` bf16 tensors (vsa_forward).
+
+    ``gate``: None, ``[B, H, Sq]`` or ``[B, H, Sq, D]`` bf16 (any strides, e.g. a
+    transposed ``[B, S, H]`` view).  With ``return_aux`` also returns
+    ``(out_c, q2k_idx, q2k_num)``.
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, S, D]")
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2] if k.dim() == 4 else -1
+    problem = dense_problem(B, H, Sq, Skv, D, topk)
+    _check_qkv(problem, q, k, v)
+    mode, st = _gate_args(gate, (B, H, Sq), (B, H, Sq, D))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, q.shape)
+    if workspace is None:
+        workspace = alloc_workspace(problem, q.device)
+    aux = None
+    if return_aux:
+        cs, isz, ns = block_shapes(problem)
+        aux = (torch.empty(cs, dtype=torch.float32, device=q.device),
+               torch.empty(isz, dtype=torch.int32, device=q.device),
+               torch.empty(ns, dtype=torch.int32, device=q.device))
+    oc, idx, num = aux if aux else (None, None, None)
+    _abi.check(_abi.load().vsa_forward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), mode, st, _ptr(out), _ptr(idx), _ptr(num),
+        _ptr(oc), B, H, Sq, Skv, D, BLOCK, topk, _ptr(workspace), workspace.numel(),
+        _stream(q.device)), "vsa_forward")
+    return (out, *aux) if return_aux else out
+
+
+def vsa_forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, meta: VarlenMeta,
+                       gate: Optional[torch.Tensor] = None, *, out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, return_aux: bool = False):
+    """VSA forward over block-padded packed sequences (vsa_forward_varlen).
+
+    ``q`` is ``[H, 64*Nq, D]``, ``k``/``v`` ``[H, 64*Nkv, D]``; ``meta`` from
+    ``vsa_build_metadata(..., device=q.device)``.  ``gate``: None,
+    ``[H, 64*Nq]`` or ``[H, 64*Nq, D]``.
+    """
+    if q.dim() != 3:
+        raise ValueError("packed q must be [H, slots, D]")
+    H, _, D = q.shape
+    if meta.device_arrays is None:
+        meta.to(q.device)
+    problem = meta.problem(H, D)
+    _check_qkv(problem, q, k, v)
+    mode, st = _gate_args(gate, *_gate_shapes(problem))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, q.shape)
+    if workspace is None:
+        workspace = alloc_workspace(problem, q.device)
+    aux = None
+    if return_aux:
+        cs, isz, ns = block_shapes(problem)
+        aux = (torch.empty(cs, dtype=torch.float32, device=q.device),
+               torch.empty(isz, dtype=torch.int32, device=q.device),
+               torch.empty(ns, dtype=torch.int32, device=q.device))
+    oc, idx, num = aux if aux else (None, None, None)
+    d = meta.device_arrays
+    s = meta.sizes
+    _abi.check(_abi.load().vsa_forward_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), mode, st, _ptr(out), _ptr(idx), _ptr(num), _ptr(oc),
+        _ptr(d["cu_blocks_q"]), _ptr(d["cu_blocks_kv"]), _ptr(d["block_sizes_q"]),
+        _ptr(d["block_sizes_kv"]), _ptr(d["topk"]), s.num_seqs, s.total_q_blocks,
+        s.total_kv_blocks, s.max_q_blocks, s.max_kv_blocks, s.max_topk, H, D, BLOCK,
+        _ptr(workspace), workspace.numel(), _stream(q.device)), "vsa_forward_varlen")
+    return (out, *aux) if return_aux else out

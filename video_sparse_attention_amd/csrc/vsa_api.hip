@@ -1,0 +1,424 @@
+// Host side of libvsa: argument validation, block metadata, workspace
+// partitioning and the launch sequence of every C entry point declared in
+// vsa.h.  Nothing here allocates device memory or synchronises the stream.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+#include "vsa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return VSA_OK;
+}
+
+constexpr int64_t kGridYZMax = 65535;
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Validate a problem and build its kernel-side view.
+int make_problem(const vsa_problem* pr, vsa::DevProblem* P) {
+    if (!pr) return fail(VSA_ERR_NULL, "problem is NULL");
+    if (pr->block_size != VSA_BLOCK)
+        return fail(VSA_ERR_UNSUPPORTED, "block_size %d unsupported (only 64)", pr->block_size);
+    if (pr->head_dim != 64 && pr->head_dim != 128)
+        return fail(VSA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", pr->head_dim);
+    if (pr->heads < 1) return fail(VSA_ERR_SHAPE, "heads must be >= 1 (got %d)", pr->heads);
+    if (pr->heads > kGridYZMax) return fail(VSA_ERR_UNSUPPORTED, "heads > %lld", (long long)kGridYZMax);
+    *P = vsa::DevProblem{};
+    P->H = pr->heads;
+    P->D = pr->head_dim;
+    if (pr->layout == VSA_LAYOUT_DENSE) {
+        if (pr->batch < 1) return fail(VSA_ERR_SHAPE, "empty batch (batch=%d)", pr->batch);
+        if (3LL * pr->batch > kGridYZMax) return fail(VSA_ERR_UNSUPPORTED, "batch too large");
+        if (pr->seqlen_q < 1 || pr->seqlen_kv < 1)
+            return fail(VSA_ERR_SHAPE, "zero-length sequence (Sq=%d, Skv=%d)", pr->seqlen_q, pr->seqlen_kv);
+        if (pr->topk < 1) return fail(VSA_ERR_TOPK, "topk must be >= 1 (got %d)", pr->topk);
+        P->packed = 0;
+        P->nseq = pr->batch;
+        P->Sq = pr->seqlen_q;
+        P->Skv = pr->seqlen_kv;
+        P->nQ = (pr->seqlen_q + VSA_BLOCK - 1) / VSA_BLOCK;
+        P->nKV = (pr->seqlen_kv + VSA_BLOCK - 1) / VSA_BLOCK;
+        if (P->nKV > vsa::kMaxKvBlocks)
+            return fail(VSA_ERR_UNSUPPORTED, "%d KV blocks per sequence exceeds %d", P->nKV, vsa::kMaxKvBlocks);
+        P->kk = std::min(pr->topk, P->nKV);
+        P->idx_row = P->kk;
+        if ((int64_t)P->nQ * P->H * P->nseq > 0x7fffffffLL)
+            return fail(VSA_ERR_UNSUPPORTED, "too many query blocks in one launch");
+    } else if (pr->layout == VSA_LAYOUT_PACKED) {
+        if (pr->num_seqs < 1) return fail(VSA_ERR_SHAPE, "empty batch (num_seqs=%d)", pr->num_seqs);
+        if (pr->num_seqs > kGridYZMax) return fail(VSA_ERR_UNSUPPORTED, "num_seqs > %lld", (long long)kGridYZMax);
+        if (!pr->cu_blocks_q || !pr->cu_blocks_kv || !pr->block_sizes_q || !pr->block_sizes_kv ||
+            !pr->topk_per_seq)
+            return fail(VSA_ERR_NULL, "packed metadata array is NULL");
+        if (pr->total_q_blocks < pr->num_seqs || pr->total_kv_blocks < pr->num_seqs)
+            return fail(VSA_ERR_SHAPE, "every sequence needs at least one block (Nq=%d, Nkv=%d, seqs=%d)",
+                        pr->total_q_blocks, pr->total_kv_blocks, pr->num_seqs);
+        if (pr->max_q_blocks < 1 || pr->max_q_blocks > pr->total_q_blocks || pr->max_kv_blocks < 1 ||
+            pr->max_kv_blocks > pr->total_kv_blocks)
+            return fail(VSA_ERR_SHAPE, "max block counts inconsistent with totals");
+        if (pr->max_kv_blocks > vsa::kMaxKvBlocks)
+            return fail(VSA_ERR_UNSUPPORTED, "%d KV blocks per sequence exceeds %d", pr->max_kv_blocks,
+                        vsa::kMaxKvBlocks);
+        if (pr->max_topk < 1) return fail(VSA_ERR_TOPK, "max_topk must be >= 1 (got %d)", pr->max_topk);
+        if ((int64_t)pr->total_q_blocks * pr->heads > 0x7fffffffLL)
+            return fail(VSA_ERR_UNSUPPORTED, "too many query blocks in one launch");
+        P->packed = 1;
+        P->nseq = pr->num_seqs;
+        P->cu_q = pr->cu_blocks_q;
+        P->cu_kv = pr->cu_blocks_kv;
+        P->bs_q = pr->block_sizes_q;
+        P->bs_kv = pr->block_sizes_kv;
+        P->topk_s = pr->topk_per_seq;
+        P->total_q = pr->total_q_blocks;
+        P->total_kv = pr->total_kv_blocks;
+        P->max_q = pr->max_q_blocks;
+        P->max_kv = pr->max_kv_blocks;
+        P->max_topk = pr->max_topk;
+        P->idx_row = pr->max_topk;
+    } else {
+        return fail(VSA_ERR_UNSUPPORTED, "unknown layout %d", pr->layout);
+    }
+    return VSA_OK;
+}
+
+// element counts of the token-resolution tensors
+int64_t q_elems(const vsa::DevProblem& P) {
+    return P.packed ? (int64_t)P.H * P.total_q * VSA_BLOCK * P.D : (int64_t)P.nseq * P.H * P.Sq * P.D;
+}
+int64_t kv_elems(const vsa::DevProblem& P) {
+    return P.packed ? (int64_t)P.H * P.total_kv * VSA_BLOCK * P.D : (int64_t)P.nseq * P.H * P.Skv * P.D;
+}
+int64_t qblocks(const vsa::DevProblem& P) {
+    return P.packed ? (int64_t)P.H * P.total_q : (int64_t)P.nseq * P.H * P.nQ;
+}
+int64_t kvblocks(const vsa::DevProblem& P) {
+    return P.packed ? (int64_t)P.H * P.total_kv : (int64_t)P.nseq * P.H * P.nKV;
+}
+
+struct Workspace {
+    double *qc, *kc, *vc;
+    float* out_c;
+    int *idx, *num;
+    size_t pooled_bytes, total_bytes;
+};
+
+Workspace plan_workspace(const vsa::DevProblem& P, void* base) {
+    Workspace w{};
+    char* p = (char*)base;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char* r = p ? p + off : nullptr;
+        off += round_up(bytes);
+        return r;
+    };
+    w.qc = (double*)take(sizeof(double) * qblocks(P) * P.D);
+    w.kc = (double*)take(sizeof(double) * kvblocks(P) * P.D);
+    w.vc = (double*)take(sizeof(double) * kvblocks(P) * P.D);
+    w.pooled_bytes = off;
+    w.out_c = (float*)take(sizeof(float) * qblocks(P) * P.D);
+    w.idx = (int*)take(sizeof(int) * qblocks(P) * P.idx_row);
+    w.num = (int*)take(sizeof(int) * qblocks(P));
+    w.total_bytes = off;
+    return w;
+}
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+int check_qkv(const vsa::DevProblem& P, const void* q, const void* k, const void* v) {
+    if (!q || !k || !v) return fail(VSA_ERR_NULL, "q, k or v is NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(VSA_ERR_ALIGN, "q, k and v must be 16-byte aligned");
+    return VSA_OK;
+}
+
+int check_out_alias(const vsa::DevProblem& P, const void* out, const void* q, const void* k, const void* v) {
+    const int64_t qb = 2 * q_elems(P), kb = 2 * kv_elems(P);
+    if (overlaps(out, qb, q, qb) || overlaps(out, qb, k, kb) || overlaps(out, qb, v, kb))
+        return fail(VSA_ERR_ALIAS, "out overlaps q, k or v");
+    return VSA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return VSA_OK;
+    return fail(VSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int gate_strides(const vsa::DevProblem& P, const uint16_t* gate, int mode, const int64_t* gs,
+                 int64_t out[3]) {
+    out[0] = out[1] = out[2] = 0;
+    if (mode == VSA_GATE_NONE) return VSA_OK;
+    if (mode != VSA_GATE_TOKEN && mode != VSA_GATE_FULL) return fail(VSA_ERR_GATE, "unknown gate mode %d", mode);
+    if (!gate) return fail(VSA_ERR_NULL, "gate is NULL with gate_mode %d", mode);
+    const int64_t dmul = mode == VSA_GATE_FULL ? P.D : 1;
+    if (gs) {
+        for (int i = 0; i < 3; ++i) {
+            if (gs[i] < 0) return fail(VSA_ERR_GATE, "negative gate stride");
+            out[i] = gs[i];
+        }
+        if (!P.packed && P.Sq > 1 && out[2] == 0) return fail(VSA_ERR_GATE, "gate token stride is 0");
+        if (P.H > 1 && out[1] == 0) return fail(VSA_ERR_GATE, "gate head stride is 0");
+    } else if (!P.packed) {
+        out[2] = dmul;
+        out[1] = (int64_t)P.Sq * dmul;
+        out[0] = (int64_t)P.H * P.Sq * dmul;
+    } else {
+        out[2] = dmul;
+        out[1] = (int64_t)P.total_q * VSA_BLOCK * dmul;
+        out[0] = 0;
+    }
+    if (mode == VSA_GATE_FULL) {
+        if (!aligned16(gate)) return fail(VSA_ERR_ALIGN, "full gate must be 16-byte aligned");
+        for (int i = 0; i < 3; ++i)
+            if (out[i] % 8) return fail(VSA_ERR_ALIGN, "full gate strides must be multiples of 8 elements");
+    } else if (((uintptr_t)gate & 1u) != 0) {
+        return fail(VSA_ERR_ALIGN, "gate must be 2-byte aligned");
+    }
+    return VSA_OK;
+}
+
+int run_coarse(const vsa::DevProblem& P, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+               float* out_c, int* idx, int* num, const Workspace& w, hipStream_t st) {
+    int rc = hip_status(vsa::launch_pool(P, q, k, v, w.qc, w.kc, w.vc, st), "pool launch");
+    if (rc) return rc;
+    return hip_status(vsa::launch_coarse_topk(P, w.qc, w.kc, w.vc, out_c, idx, num, st), "coarse/top-k launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vsa_status_string(int status) {
+    switch (status) {
+        case VSA_OK: return "ok";
+        case VSA_ERR_NULL: return "NULL pointer";
+        case VSA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case VSA_ERR_TOPK: return "invalid topk";
+        case VSA_ERR_SHAPE: return "invalid shape";
+        case VSA_ERR_GATE: return "invalid gate";
+        case VSA_ERR_WORKSPACE: return "workspace missing or too small";
+        case VSA_ERR_ALIGN: return "misaligned pointer or stride";
+        case VSA_ERR_ALIAS: return "output overlaps an input";
+        case VSA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* vsa_last_error(void) { return g_err.c_str(); }
+
+const char* vsa_version(void) { return "libvsa 0.1.0 gfx950"; }
+
+int vsa_build_metadata(int32_t num_seqs, const int32_t* seqlens_q, const int32_t* seqlens_kv,
+                       const int32_t* topk, vsa_meta_sizes* sizes, int32_t* cu_blocks_q,
+                       int32_t* cu_blocks_kv, int32_t* block_sizes_q, int32_t* block_sizes_kv,
+                       int32_t* topk_clamped) {
+    if (!sizes) return fail(VSA_ERR_NULL, "sizes is NULL");
+    *sizes = vsa_meta_sizes{};
+    if (num_seqs < 1) return fail(VSA_ERR_SHAPE, "empty batch (num_seqs=%d)", num_seqs);
+    if (!seqlens_q || !topk) return fail(VSA_ERR_NULL, "seqlens_q or topk is NULL");
+    const int nout = !!cu_blocks_q + !!cu_blocks_kv + !!block_sizes_q + !!block_sizes_kv + !!topk_clamped;
+    if (nout != 0 && nout != 5) return fail(VSA_ERR_NULL, "pass all five output arrays or none");
+    if (!seqlens_kv) seqlens_kv = seqlens_q;
+    int64_t tq = 0, tkv = 0;
+    int32_t mq = 0, mkv = 0, mk = 0;
+    for (int s = 0; s < num_seqs; ++s) {
+        if (seqlens_q[s] < 1 || seqlens_kv[s] < 1)
+            return fail(VSA_ERR_SHAPE, "sequence %d has zero length (q=%d, kv=%d)", s, seqlens_q[s], seqlens_kv[s]);
+        if (topk[s] < 1) return fail(VSA_ERR_TOPK, "sequence %d: topk must be >= 1 (got %d)", s, topk[s]);
+        const int32_t nq = (seqlens_q[s] + VSA_BLOCK - 1) / VSA_BLOCK;
+        const int32_t nkv = (seqlens_kv[s] + VSA_BLOCK - 1) / VSA_BLOCK;
+        tq += nq;
+        tkv += nkv;
+        mq = std::max(mq, nq);
+        mkv = std::max(mkv, nkv);
+        mk = std::max(mk, std::min(topk[s], nkv));
+    }
+    if (tq * VSA_BLOCK > 0x7fffffffLL || tkv * VSA_BLOCK > 0x7fffffffLL)
+        return fail(VSA_ERR_SHAPE, "packed length exceeds 2^31 slots");
+    sizes->num_seqs = num_seqs;
+    sizes->total_q_blocks = (int32_t)tq;
+    sizes->total_kv_blocks = (int32_t)tkv;
+    sizes->max_q_blocks = mq;
+    sizes->max_kv_blocks = mkv;
+    sizes->max_topk = mk;
+    sizes->q_slots = tq * VSA_BLOCK;
+    sizes->kv_slots = tkv * VSA_BLOCK;
+    if (nout == 0) return ok();
+    int32_t oq = 0, okv = 0;
+    for (int s = 0; s < num_seqs; ++s) {
+        const int32_t nq = (seqlens_q[s] + VSA_BLOCK - 1) / VSA_BLOCK;
+        const int32_t nkv = (seqlens_kv[s] + VSA_BLOCK - 1) / VSA_BLOCK;
+        cu_blocks_q[s] = oq;
+        cu_blocks_kv[s] = okv;
+        for (int i = 0; i < nq; ++i) block_sizes_q[oq + i] = std::min(VSA_BLOCK, seqlens_q[s] - VSA_BLOCK * i);
+        for (int j = 0; j < nkv; ++j) block_sizes_kv[okv + j] = std::min(VSA_BLOCK, seqlens_kv[s] - VSA_BLOCK * j);
+        topk_clamped[s] = std::min(topk[s], nkv);
+        oq += nq;
+        okv += nkv;
+    }
+    cu_blocks_q[num_seqs] = oq;
+    cu_blocks_kv[num_seqs] = okv;
+    return ok();
+}
+
+size_t vsa_workspace_size(const vsa_problem* problem) {
+    vsa::DevProblem P;
+    if (make_problem(problem, &P) != VSA_OK) return 0;
+    return plan_workspace(P, nullptr).total_bytes;
+}
+
+int vsa_coarse_topk(const vsa_problem* problem, const vsa_bf16* q, const vsa_bf16* k, const vsa_bf16* v,
+                    float* out_c, int32_t* q2k_idx, int32_t* q2k_num, void* workspace,
+                    size_t workspace_bytes, vsa_stream stream) {
+    vsa::DevProblem P;
+    int rc = make_problem(problem, &P);
+    if (rc) return rc;
+    if ((rc = check_qkv(P, q, k, v))) return rc;
+    if (!out_c || !q2k_idx || !q2k_num) return fail(VSA_ERR_NULL, "out_c, q2k_idx or q2k_num is NULL");
+    if (!aligned16(out_c)) return fail(VSA_ERR_ALIGN, "out_c must be 16-byte aligned");
+    if (((uintptr_t)q2k_idx & 3u) || ((uintptr_t)q2k_num & 3u)) return fail(VSA_ERR_ALIGN, "index arrays must be 4-byte aligned");
+    if (!workspace) return fail(VSA_ERR_WORKSPACE, "workspace is NULL");
+    if ((uintptr_t)workspace % kAlign) return fail(VSA_ERR_ALIGN, "workspace must be 256-byte aligned");
+    const Workspace w = plan_workspace(P, workspace);
+    if (workspace_bytes < w.pooled_bytes)
+        return fail(VSA_ERR_WORKSPACE, "workspace holds %zu bytes, needs %zu", workspace_bytes, w.pooled_bytes);
+    rc = run_coarse(P, q, k, v, out_c, q2k_idx, q2k_num, w, (hipStream_t)stream);
+    return rc ? rc : ok();
+}
+
+int vsa_sparse_attn_from_indices(const vsa_problem* problem, const vsa_bf16* q, const vsa_bf16* k,
+                                 const vsa_bf16* v, const int32_t* q2k_idx, const int32_t* q2k_num,
+                                 vsa_bf16* out, vsa_stream stream) {
+    vsa::DevProblem P;
+    int rc = make_problem(problem, &P);
+    if (rc) return rc;
+    if ((rc = check_qkv(P, q, k, v))) return rc;
+    if (!q2k_idx || !q2k_num || !out) return fail(VSA_ERR_NULL, "q2k_idx, q2k_num or out is NULL");
+    if (!aligned16(out)) return fail(VSA_ERR_ALIGN, "out must be 16-byte aligned");
+    if ((rc = check_out_alias(P, out, q, k, v))) return rc;
+    rc = hip_status(vsa::launch_sparse_attn(P, q, k, v, q2k_idx, q2k_num, out, (hipStream_t)stream),
+                    "sparse attention launch");
+    return rc ? rc : ok();
+}
+
+int vsa_combine(const vsa_problem* problem, const float* out_c, const vsa_bf16* gate, int32_t gate_mode,
+                const int64_t* gate_strides_in, vsa_bf16* out, vsa_stream stream) {
+    vsa::DevProblem P;
+    int rc = make_problem(problem, &P);
+    if (rc) return rc;
+    if (!out_c || !out) return fail(VSA_ERR_NULL, "out_c or out is NULL");
+    if (!aligned16(out_c) || !aligned16(out)) return fail(VSA_ERR_ALIGN, "out_c and out must be 16-byte aligned");
+    int64_t gs[3];
+    if ((rc = gate_strides(P, gate, gate_mode, gate_strides_in, gs))) return rc;
+    if (gate_mode != VSA_GATE_NONE) {
+        const int64_t ob = 2 * q_elems(P);
+        if (overlaps(out, ob, gate, 2)) return fail(VSA_ERR_ALIAS, "gate overlaps out");
+    }
+    rc = hip_status(vsa::launch_combine(P, out_c, gate, gate_mode, gs[0], gs[1], gs[2], out, (hipStream_t)stream),
+                    "combine launch");
+    return rc ? rc : ok();
+}
+
+static int forward_common(const vsa_problem* pr, const vsa_bf16* q, const vsa_bf16* k, const vsa_bf16* v,
+                          const vsa_bf16* gate, int32_t gate_mode, const int64_t* gate_strides_in,
+                          vsa_bf16* out, int32_t* q2k_idx, int32_t* q2k_num, float* out_c,
+                          void* workspace, size_t workspace_bytes, vsa_stream stream) {
+    vsa::DevProblem P;
+    int rc = make_problem(pr, &P);
+    if (rc) return rc;
+    if ((rc = check_qkv(P, q, k, v))) return rc;
+    if (!out) return fail(VSA_ERR_NULL, "out is NULL");
+    if (!aligned16(out)) return fail(VSA_ERR_ALIGN, "out must be 16-byte aligned");
+    if ((rc = check_out_alias(P, out, q, k, v))) return rc;
+    int64_t gs[3];
+    if ((rc = gate_strides(P, gate, gate_mode, gate_strides_in, gs))) return rc;
+    if (out_c && !aligned16(out_c)) return fail(VSA_ERR_ALIGN, "out_c must be 16-byte aligned");
+    if ((q2k_idx && ((uintptr_t)q2k_idx & 3u)) || (q2k_num && ((uintptr_t)q2k_num & 3u)))
+        return fail(VSA_ERR_ALIGN, "index arrays must be 4-byte aligned");
+    if (!workspace) return fail(VSA_ERR_WORKSPACE, "workspace is NULL");
+    if ((uintptr_t)workspace % kAlign) return fail(VSA_ERR_ALIGN, "workspace must be 256-byte aligned");
+    const Workspace w = plan_workspace(P, workspace);
+    if (workspace_bytes < w.total_bytes)
+        return fail(VSA_ERR_WORKSPACE, "workspace holds %zu bytes, needs %zu", workspace_bytes, w.total_bytes);
+    float* oc = out_c ? out_c : w.out_c;
+    int* idx = q2k_idx ? q2k_idx : w.idx;
+    int* num = q2k_num ? q2k_num : w.num;
+    hipStream_t st = (hipStream_t)stream;
+    if ((rc = run_coarse(P, q, k, v, oc, idx, num, w, st))) return rc;
+    if ((rc = hip_status(vsa::launch_sparse_attn(P, q, k, v, idx, num, out, st), "sparse attention launch")))
+        return rc;
+    if ((rc = hip_status(vsa::launch_combine(P, oc, gate, gate_mode, gs[0], gs[1], gs[2], out, st),
+                         "combine launch")))
+        return rc;
+    return ok();
+}
+
+int vsa_forward(const vsa_bf16* q, const vsa_bf16* k, const vsa_bf16* v, const vsa_bf16* gate,
+                int32_t gate_mode, const int64_t* gate_strides, vsa_bf16* out, int32_t* q2k_idx,
+                int32_t* q2k_num, float* out_c, int32_t batch, int32_t heads, int32_t seqlen_q,
+                int32_t seqlen_kv, int32_t head_dim, int32_t block_size, int32_t topk, void* workspace,
+                size_t workspace_bytes, vsa_stream stream) {
+    vsa_problem pr{};
+    pr.layout = VSA_LAYOUT_DENSE;
+    pr.heads = heads;
+    pr.head_dim = head_dim;
+    pr.block_size = block_size;
+    pr.batch = batch;
+    pr.seqlen_q = seqlen_q;
+    pr.seqlen_kv = seqlen_kv;
+    pr.topk = topk;
+    return forward_common(&pr, q, k, v, gate, gate_mode, gate_strides, out, q2k_idx, q2k_num, out_c, workspace,
+                          workspace_bytes, stream);
+}
+
+int vsa_forward_varlen(const vsa_bf16* q, const vsa_bf16* k, const vsa_bf16* v, const vsa_bf16* gate,
+                       int32_t gate_mode, const int64_t* gate_strides, vsa_bf16* out, int32_t* q2k_idx,
+                       int32_t* q2k_num, float* out_c, const int32_t* cu_blocks_q, const int32_t* cu_blocks_kv,
+                       const int32_t* block_sizes_q, const int32_t* block_sizes_kv,
+                       const int32_t* topk_per_seq, int32_t num_seqs, int32_t total_q_blocks,
+                       int32_t total_kv_blocks, int32_t max_q_blocks, int32_t max_kv_blocks, int32_t max_topk,
+                       int32_t heads, int32_t head_dim, int32_t block_size, void* workspace,
+                       size_t workspace_bytes, vsa_stream stream) {
+    vsa_problem pr{};
+    pr.layout = VSA_LAYOUT_PACKED;
+    pr.heads = heads;
+    pr.head_dim = head_dim;
+    pr.block_size = block_size;
+    pr.num_seqs = num_seqs;
+    pr.total_q_blocks = total_q_blocks;
+    pr.total_kv_blocks = total_kv_blocks;
+    pr.max_q_blocks = max_q_blocks;
+    pr.max_kv_blocks = max_kv_blocks;
+    pr.max_topk = max_topk;
+    pr.cu_blocks_q = cu_blocks_q;
+    pr.cu_blocks_kv = cu_blocks_kv;
+    pr.block_sizes_q = block_sizes_q;
+    pr.block_sizes_kv = block_sizes_kv;
+    pr.topk_per_seq = topk_per_seq;
+    return forward_common(&pr, q, k, v, gate, gate_mode, gate_strides, out, q2k_idx, q2k_num, out_c, workspace,
+                          workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Internal definitions shared by the libvsa kernels and the host entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_layout.hpp"
+#include "vsa.h"
+
+namespace vsa {
+
+constexpr int kBlock = 64;
+
+// Kernel-side view of a problem (passed by value to every kernel).
+struct DevProblem {
+    int packed;  // 0 dense [B,H,S,D], 1 block-padded packed [H,slots,D]
+    int H, D;
+    int nseq;  // B (dense) or num_seqs (packed)
+    // dense
+    int Sq, Skv, nQ, nKV, kk;  // kk = min(topk, nKV)
+    // packed
+    const int* cu_q;
+    const int* cu_kv;
+    const int* bs_q;
+    const int* bs_kv;
+    const int* topk_s;
+    int total_q, total_kv, max_q, max_kv, max_topk;
+    int idx_row;  // row length of q2k_idx: kk (dense) or max_topk (packed)
+};
+
+// One sequence on one head: where its blocks live.
+struct SeqView {
+    int nq, nkv, k;       // query blocks, KV blocks, top-k (clamped)
+    int qblk0, kvblk0;    // first global block index (packed) or 0 (dense)
+    int64_t qblk_base;    // index of block 0 in block-resolution q arrays
+    int64_t kvblk_base;   // index of block 0 in block-resolution kv arrays
+    int64_t qrow_base;    // row (token slot) of block 0 in q/out
+    int64_t kvrow_base;   // row of block 0 in k/v
+    int idx_rebase;       // added to local KV block numbers when stored
+};
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+__device__ __forceinline__ SeqView seq_view(const DevProblem& P, int s, int h) {
+    SeqView v;
+    if (!P.packed) {
+        v.nq = P.nQ;
+        v.nkv = P.nKV;
+        v.k = P.kk;
+        v.qblk0 = 0;
+        v.kvblk0 = 0;
+        const int64_t sh = (int64_t)s * P.H + h;
+        v.qblk_base = sh * P.nQ;
+        v.kvblk_base = sh * P.nKV;
+        v.qrow_base = sh * P.Sq;
+        v.kvrow_base = sh * P.Skv;
+        v.idx_rebase = 0;
+    } else {
+        int q0 = clampi(P.cu_q[s], 0, P.total_q);
+        int q1 = clampi(P.cu_q[s + 1], q0, P.total_q);
+        int k0 = clampi(P.cu_kv[s], 0, P.total_kv);
+        int k1 = clampi(P.cu_kv[s + 1], k0, P.total_kv);
+        v.nq = min(q1 - q0, P.max_q);
+        v.nkv = min(k1 - k0, P.max_kv);
+        v.k = clampi(P.topk_s[s], 1, min(P.max_topk, max(v.nkv, 1)));
+        v.qblk0 = q0;
+        v.kvblk0 = k0;
+        v.qblk_base = (int64_t)h * P.total_q + q0;
+        v.kvblk_base = (int64_t)h * P.total_kv + k0;
+        v.qrow_base = ((int64_t)h * P.total_q + q0) * kBlock;
+        v.kvrow_base = ((int64_t)h * P.total_kv + k0) * kBlock;
+        v.idx_rebase = k0;
+    }
+    return v;
+}
+
+// Valid tokens of local query / KV block i of sequence view v.
+__device__ __forceinline__ int q_block_size(const DevProblem& P, const SeqView& v, int i) {
+    if (!P.packed) return min(kBlock, P.Sq - kBlock * i);
+    return clampi(P.bs_q[v.qblk0 + i], 1, kBlock);
+}
+__device__ __forceinline__ int kv_block_size(const DevProblem& P, const SeqView& v, int j) {
+    if (!P.packed) return min(kBlock, P.Skv - kBlock * j);
+    return clampi(P.bs_kv[v.kvblk0 + j], 1, kBlock);
+}
+
+// Sequence owning global query block g (packed): largest s with cu_q[s] <= g.
+__device__ __forceinline__ int seq_of_qblock(const DevProblem& P, int g) {
+    int lo = 0, hi = P.nseq - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (P.cu_q[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// ---------------------------------------------------------------------------
+// launchers (one per kernel family; each returns hipError_t of the launch)
+// ---------------------------------------------------------------------------
+hipError_t launch_pool(const DevProblem& P, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       double* qc, double* kc, double* vc, hipStream_t st);
+hipError_t launch_coarse_topk(const DevProblem& P, const double* qc, const double* kc,
+                              const double* vc, float* out_c, int* idx, int* num, hipStream_t st);
+hipError_t launch_sparse_attn(const DevProblem& P, const uint16_t* q, const uint16_t* k,
+                              const uint16_t* v, const int* idx, const int* num, uint16_t* out,
+                              hipStream_t st);
+hipError_t launch_combine(const DevProblem& P, const float* out_c, const uint16_t* gate, int mode,
+                          int64_t gs0, int64_t gs1, int64_t gs2, uint16_t* out, hipStream_t st);
+
+// Rows per workgroup of the coarse kernel for a given KV block bound (0 = unsupported).
+int coarse_rows_per_group(int max_kv_blocks, int D);
+constexpr int kMaxKvBlocks = 4096;
+
+}  // namespace vsa
