@@ -43,7 +43,23 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=10.0,
                     help="wall-time budget of the oracle sample (whole heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy kernel (reference for the HBM "
+                         "byte counters) three times and exit")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain elementwise copy of known size: 1 GiB read, 1 GiB written per launch."""
+    import torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read_per_launch": 4 * n,
+                      "copy_calibration_bytes_written_per_launch": 4 * n}), flush=True)
 
 
 def kernel_hash(path=SPARSE_SRC) -> str:
@@ -108,6 +124,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the forward "
               "is not sharded across GPUs in this build.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
 

@@ -1,6 +1,11 @@
-// CPU check of the index maps used by the block-sparse attention kernel:
-// bijections, bounds, the MFMA k-slot relabelling, and an LDS bank model of
-// the V^T staging writes and operand reads.  Runs on the host only.
+// CPU check of the index maps used by the block-sparse attention kernel.
+// It simulates, on the host, the direct global->LDS copies of one K and one V
+// block into their swizzled tiles and every MFMA operand fetch from them
+// (ds_read_b128 for K, ds_read_b64_tr_b16 for V, the latter with the lane
+// rule of the hardware: within a 16-lane group, lane i receives element i & 3
+// of the 8-byte chunks addressed by lanes (i >> 2) + 4 r, r = 0..3), and
+// checks that every lane gets exactly the K / V elements the MFMA layout
+// needs.  Also: bounds, bijections, an LDS bank model, the XCD remap.
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -10,17 +15,19 @@
 #include "attn_layout.hpp"
 
 static int failures = 0;
-#define CHECK(cond, ...)                    \
-    do {                                    \
-        if (!(cond)) {                      \
-            printf("FAIL: " __VA_ARGS__);   \
-            printf("\n");                   \
-            ++failures;                     \
-        }                                   \
+#define CHECK(cond, ...)                  \
+    do {                                  \
+        if (!(cond)) {                    \
+            if (failures < 20) {          \
+                printf("FAIL: " __VA_ARGS__); \
+                printf("\n");             \
+            }                             \
+            ++failures;                   \
+        }                                 \
     } while (0)
 
-// Max number of distinct addresses (4-byte words) falling in one bank, over
-// the lanes serviced together.
+// Max number of distinct 4-byte words falling in one bank over the lanes
+// serviced together.
 static int bank_ways(const std::vector<int>& byte_addr, const std::vector<int>& bytes, int banks) {
     std::vector<std::set<int>> words(banks);
     for (size_t i = 0; i < byte_addr.size(); ++i)
@@ -33,80 +40,132 @@ static int bank_ways(const std::vector<int>& byte_addr, const std::vector<int>& 
     return worst;
 }
 
+// value stored for element (token t, dim d) of a block: unique and recognisable
+static int val(int t, int d) { return t * 1000 + d; }
+
+template <int D, bool IS_V>
+static std::vector<int> fill_tile(int valid) {
+    constexpr int CH = D / 8;
+    std::vector<int> tile(64 * D, -1);
+    std::vector<int> hits(64 * CH, 0);
+    for (int wave = 0; wave < 2; ++wave)
+        for (int n = 0; n < CH / 2; ++n)
+            for (int lane = 0; lane < 64; ++lane) {
+                const int p = vsa::load_chunk_pos(n, wave, lane);
+                CHECK(p >= 0 && p < 64 * CH, "chunk position %d out of range", p);
+                hits[p]++;
+                const int row = p / CH;
+                const int sw = IS_V ? vsa::v_swz<CH>(row) : vsa::k_swz<CH>(row);
+                const int c = (p % CH) ^ sw;
+                CHECK(c >= 0 && c < CH, "logical chunk %d out of range", c);
+                const int src_row = row < valid ? row : valid - 1;
+                // lane's 16 bytes land at byte 16*lane of the wave's 1 KiB segment
+                const int lds_elem = (2 * n + wave) * 64 * 8 + 8 * lane;
+                CHECK(lds_elem == 8 * p, "segment placement");
+                for (int e = 0; e < 8; ++e) tile[lds_elem + e] = val(src_row, 8 * c + e);
+            }
+    for (int p = 0; p < 64 * CH; ++p) CHECK(hits[p] == 1, "chunk %d written %d times", p, hits[p]);
+    return tile;
+}
+
 template <int D>
 static void check_d() {
     constexpr int CH = D / 8;
-    // tok_pos: bijection within each 16-token group, and the k-slot relabelling
-    std::set<int> seen;
-    for (int t = 0; t < 64; ++t) {
-        const int p = vsa::tok_pos(t);
-        CHECK(p >= 0 && p < 64 && p / 16 == t / 16, "tok_pos(%d)=%d", t, p);
-        seen.insert(p);
-    }
-    CHECK(seen.size() == 64, "tok_pos not a bijection");
-    for (int s4 = 0; s4 < 4; ++s4)
-        for (int hh = 0; hh < 2; ++hh)
-            for (int jj = 0; jj < 2; ++jj)
-                for (int ii = 0; ii < 4; ++ii)
-                    CHECK(vsa::tok_pos(16 * s4 + 8 * jj + 4 * hh + ii) == 16 * s4 + 8 * hh + 4 * jj + ii,
-                          "k-slot relabelling s4=%d hh=%d jj=%d ii=%d", s4, hh, jj, ii);
-    // vt_off: bijection onto [0, D*64)
-    std::vector<int> hit(D * 64, 0);
-    for (int d = 0; d < D; ++d)
-        for (int p = 0; p < 64; ++p) {
-            const int o = vsa::vt_off(d, p);
-            CHECK(o >= 0 && o < D * 64, "vt_off(%d,%d)=%d out of range", d, p, o);
-            if (o >= 0 && o < D * 64) hit[o]++;
+    constexpr int KS = D / 16, DT = D / 32;
+    // swizzles are permutations of a row's chunks
+    for (int row = 0; row < 64; ++row) {
+        std::set<int> a, b;
+        for (int c = 0; c < CH; ++c) {
+            a.insert(vsa::tile_off<CH>(row, c, vsa::k_swz<CH>(row)));
+            b.insert(vsa::tile_off<CH>(row, c, vsa::v_swz<CH>(row)));
         }
-    for (int o = 0; o < D * 64; ++o) CHECK(hit[o] == 1, "vt_off hits %d %d times", o, hit[o]);
-    // staging units cover every (g4, c) once
-    std::vector<int> cov(16 * CH, 0);
-    for (int u = 0; u < 16 * CH; ++u) {
-        int g4, c;
-        vsa::stage_unit<CH>(u, &g4, &c);
-        CHECK(g4 >= 0 && g4 < 16 && c >= 0 && c < CH, "unit %d -> (%d,%d)", u, g4, c);
-        cov[g4 * CH + c]++;
+        CHECK((int)a.size() == CH && (int)b.size() == CH, "swizzle of row %d not a permutation", row);
+        CHECK(*a.rbegin() < 64 * D && *b.rbegin() < 64 * D, "tile offset out of range");
     }
-    for (int x = 0; x < 16 * CH; ++x) CHECK(cov[x] == 1, "unit coverage %d = %d", x, cov[x]);
-
-    // bank model, 32 banks x 4 bytes: ds_write_b64 serviced 16 lanes at a time
-    int worst_w = 0;
-    for (int wave_instr = 0; wave_instr < 16 * CH / 64; ++wave_instr)
-        for (int e = 0; e < 8; ++e)
-            for (int quarter = 0; quarter < 4; ++quarter) {
-                std::vector<int> a, b;
-                for (int l = 16 * quarter; l < 16 * quarter + 16; ++l) {
-                    int g4, c;
-                    vsa::stage_unit<CH>(64 * wave_instr + l, &g4, &c);
-                    a.push_back(2 * vsa::vt_off(8 * c + e, vsa::tok_pos(4 * g4)));
-                    b.push_back(8);
+    for (int valid : {64, 37, 1}) {
+        const std::vector<int> kt = fill_tile<D, false>(valid);
+        const std::vector<int> vt = fill_tile<D, true>(valid);
+        // K operand of S^T = K Q^T: lane l gets K[32 mt + l%32][16 ks + 8 hh + 0..7]
+        for (int mt = 0; mt < 2; ++mt)
+            for (int ks = 0; ks < KS; ++ks)
+                for (int l = 0; l < 64; ++l) {
+                    const int row = 32 * mt + (l & 31), hh = l >> 5;
+                    const int off = vsa::tile_off<CH>(row, 2 * ks + hh, vsa::k_swz<CH>(row));
+                    const int r = row < valid ? row : valid - 1;
+                    for (int e = 0; e < 8; ++e)
+                        CHECK(kt[off + e] == val(r, 16 * ks + 8 * hh + e), "K operand mt%d ks%d lane%d e%d", mt, ks, l, e);
                 }
-                const int w = bank_ways(a, b, 32);
-                worst_w = w > worst_w ? w : worst_w;
-            }
-    // ds_read_b128 of the V^T operand serviced 8 lanes at a time
-    int worst_r = 0;
-    for (int dt = 0; dt < D / 32; ++dt)
-        for (int s4 = 0; s4 < 4; ++s4)
-            for (int oct = 0; oct < 8; ++oct) {
-                std::vector<int> a, b;
-                for (int l = 8 * oct; l < 8 * oct + 8; ++l) {
-                    const int d = 32 * dt + (l & 31), hh = l >> 5;
-                    a.push_back(2 * vsa::vt_off(d, 16 * s4 + 8 * hh));
-                    b.push_back(16);
+        // V^T operand of O^T = V^T P^T via two transpose reads per k-step:
+        // lane l needs V[16 s4 + 8 jj + 4 hh + r][32 dt + l%32] in slot 4 jj + r
+        for (int dt = 0; dt < DT; ++dt)
+            for (int s4 = 0; s4 < 4; ++s4)
+                for (int jj = 0; jj < 2; ++jj) {
+                    int addr[64];
+                    for (int l = 0; l < 64; ++l) {
+                        const int g16 = l >> 4, L16 = l & 15, hh = l >> 5;
+                        const int tok = 16 * s4 + 8 * jj + 4 * hh + vsa::tr_token(L16);
+                        const int d = 32 * dt + 16 * (g16 & 1) + 4 * vsa::tr_dquad(L16);
+                        addr[l] = vsa::tile_off<CH>(tok, d >> 3, vsa::v_swz<CH>(tok)) + (d & 7);
+                        CHECK(addr[l] >= 0 && addr[l] + 3 < 64 * D, "tr address out of range");
+                    }
+                    for (int l = 0; l < 64; ++l) {
+                        const int grp = l & ~15, i = l & 15, hh = l >> 5;
+                        for (int r = 0; r < 4; ++r) {
+                            const int src = grp + (i >> 2) + 4 * r;
+                            const int got = vt[addr[src] + (i & 3)];
+                            const int tok = 16 * s4 + 8 * jj + 4 * hh + r;
+                            const int t = tok < valid ? tok : valid - 1;
+                            CHECK(got == val(t, 32 * dt + (l & 31)), "V operand dt%d s4%d jj%d lane%d r%d", dt, s4, jj, l, r);
+                        }
+                    }
                 }
-                const int w = bank_ways(a, b, 32);
-                worst_r = w > worst_r ? w : worst_r;
+    }
+    // LDS bank model: K reads (b128) and V transpose reads (b64), for 32 and
+    // 64 banks of 4 bytes (passes of 128 and 256 bytes)
+    int worst[2][2] = {{0, 0}, {0, 0}};
+    for (int m = 0; m < 2; ++m) {
+        const int banks = m == 0 ? 32 : 64;
+        for (int mt = 0; mt < 2; ++mt)
+            for (int ks = 0; ks < KS; ++ks) {
+                const int lpp = banks * 4 / 16;
+                for (int p0 = 0; p0 < 64; p0 += lpp) {
+                    std::vector<int> a, b;
+                    for (int l = p0; l < p0 + lpp; ++l) {
+                        const int row = 32 * mt + (l & 31);
+                        a.push_back(2 * vsa::tile_off<CH>(row, 2 * ks + (l >> 5), vsa::k_swz<CH>(row)));
+                        b.push_back(16);
+                    }
+                    const int w = bank_ways(a, b, banks);
+                    worst[0][m] = w > worst[0][m] ? w : worst[0][m];
+                }
             }
-    printf("D=%d: worst bank ways (32x4B model): staging write %d, operand read %d\n", D, worst_w, worst_r);
-    CHECK(worst_w == 1, "staging writes conflict (%d-way)", worst_w);
-    CHECK(worst_r == 1, "operand reads conflict (%d-way)", worst_r);
+        for (int dt = 0; dt < DT; ++dt)
+            for (int s4 = 0; s4 < 4; ++s4)
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int lpp = banks * 4 / 8;
+                    for (int p0 = 0; p0 < 64; p0 += lpp) {
+                        std::vector<int> a, b;
+                        for (int l = p0; l < p0 + lpp; ++l) {
+                            const int g16 = l >> 4, L16 = l & 15, hh = l >> 5;
+                            const int tok = 16 * s4 + 8 * jj + 4 * hh + vsa::tr_token(L16);
+                            const int d = 32 * dt + 16 * (g16 & 1) + 4 * vsa::tr_dquad(L16);
+                            a.push_back(2 * (vsa::tile_off<CH>(tok, d >> 3, vsa::v_swz<CH>(tok)) + (d & 7)));
+                            b.push_back(8);
+                        }
+                        const int w = bank_ways(a, b, banks);
+                        worst[1][m] = w > worst[1][m] ? w : worst[1][m];
+                    }
+                }
+    }
+    printf("D=%d: worst bank ways K read %d/%d, V read %d/%d (32/64 banks)\n", D, worst[0][0], worst[0][1],
+           worst[1][0], worst[1][1]);
+    CHECK(worst[0][0] == 1 && worst[1][0] == 1, "bank conflicts in the 32-bank model");
+    if (D == 128) CHECK(worst[0][1] == 1 && worst[1][1] == 1, "bank conflicts in the 64-bank model");
 }
 
 int main() {
     check_d<128>();
     check_d<64>();
-    // xcd_remap is a bijection of [0, N)
     const int Ns[] = {1, 2, 7, 8, 9, 15, 16, 17, 63, 64, 65, 242, 1000, 13552, 16896, 100003};
     for (int N : Ns) {
         std::vector<char> hit(N, 0);

@@ -68,6 +68,8 @@ def test_deterministic():
     (1, 2, 448, 640, 128, 4, "transposed"), # gate given as a transposed [B,S,H] view
     (3, 1, 200, 70, 64, 1, None),           # top-1, partial KV tail block
     (1, 1, 64 * 40 + 3, 64 * 40 + 3, 128, 8, "token"),  # many blocks + 3-token tail
+    (1, 1, 128, 64 * 300, 128, 20, None),    # 300 KV blocks: 16 keys per lane in the top-k
+    (1, 1, 200, 64 * 1100 - 5, 64, 7, None), # 1100 KV blocks: 64 keys per lane, 4 rows per group
 ])
 def test_dense_edge_cases(B, H, Sq, Skv, D, topk, gate):
     inp = synth.dense_inputs(B, H, Sq, D, topk, seed=2000 + Sq + Skv + D + topk,

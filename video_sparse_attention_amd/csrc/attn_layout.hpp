@@ -1,45 +1,53 @@
 // Index maps of the block-sparse attention kernel, usable on host and
-// device so that their coverage and bank behaviour can be checked on a CPU.
+// device so that their coverage and LDS bank behaviour can be checked on a
+// CPU.
+//
+// A KV block lives in LDS as two row-major tiles, K[64][D] and V[64][D]
+// (bf16), written 16 bytes per lane by direct global->LDS loads.  Lane l of
+// a wave's load instruction always lands at LDS byte base + 16 l, so the
+// layout is chosen by which global 16-byte chunk each lane fetches: the
+// chunks of every row are XOR-permuted by a function of the row so that the
+// MFMA operand reads hit distinct banks.
 #pragma once
 
 #include <hip/hip_runtime.h>
 
 namespace vsa {
 
-// LDS position of KV token t inside its 16-token group.  The MFMA k-slot
-// 8*hh + 4*jj + ii of the O^T = V^T P^T product stands for token
-// 16*s + 8*jj + 4*hh + ii, which is where the S^T accumulator of lane half hh
-// holds it; storing token t at this position makes each lane's 8 k-slots one
-// contiguous 16-byte group.
-__host__ __device__ inline int tok_pos(int t) {
-    return (t & ~15) | (((t >> 2) & 1) << 3) | (((t >> 3) & 1) << 2) | (t & 3);
-}
-
-// Element offset of V^T[d][pos] in LDS: rows of 64 tokens (128 bytes), the
-// eight 16-byte groups of a row XOR-swizzled by (d ^ d/8) mod 8 so that
-// (a) eight consecutive rows read at one group hit eight different groups
-// and (b) rows 8 apart written at one group do too.
-__host__ __device__ inline int vt_off(int d, int pos) {
-    const int swz = (d ^ (d >> 3)) & 7;
-    return d * 64 + 8 * ((pos >> 3) ^ swz) + (pos & 7);
-}
-
-// Staging unit u (0 .. 16*CH-1) -> 4-token group g4 and 16-byte chunk c.
-// Within a 16-lane quarter-wave the eight chunks pair with two token groups
-// whose LDS positions differ by 4 elements, so a quarter-wave's ds_write_b64
-// covers 16 distinct 8-byte bank pairs.
+// XOR applied to the 16-byte chunk index of K row `row` (CH chunks per row).
+// The S^T = K Q^T A operand reads one chunk of 32 consecutive rows per
+// instruction (ds_read_b128); rows 0..15 of a pass then fall on 16
+// different chunk columns.
 template <int CH>
-__host__ __device__ inline void stage_unit(int u, int* g4, int* c) {
-    const int ul = u & 63, uw = u >> 6;
-    const int clo = ul & 7, gl = 2 * ((ul >> 3) & 1) + ((ul >> 4) & 1), b5 = ul >> 5;
-    if (CH == 16) {
-        *c = clo + 8 * b5;
-        *g4 = 4 * uw + gl;
-    } else {
-        *c = clo;
-        *g4 = 4 * (2 * uw + b5) + gl;
-    }
+__host__ __device__ inline int k_swz(int row) {
+    return CH == 16 ? (row & 15) : ((row ^ (row >> 3)) & 7);
 }
+
+// XOR applied to the chunk index of V row `row`.  The O^T = V^T P^T A
+// operand is read with ds_read_b64_tr_b16: each 16-lane group fetches a
+// 4-token x 16-d sub-block; rows 4a..4a+3 are spread over four disjoint
+// chunk pairs (and four disjoint chunk quads for the 32 lanes of a pass).
+template <int CH>
+__host__ __device__ inline int v_swz(int row) {
+    return (4 * (row & 3) + 2 * ((row >> 1) & 1)) & (CH - 1);
+}
+
+// Element offset of logical chunk c of row `row` in a [64][8*CH] tile.
+template <int CH>
+__host__ __device__ inline int tile_off(int row, int c, int swz) {
+    return row * CH * 8 + 8 * (c ^ swz);
+}
+
+// Direct-load instruction n of wave w (2 waves, 64 lanes) fills LDS chunk
+// p = (2 n + w) * 64 + lane; that physical chunk holds logical chunk
+// (p % CH) ^ swz(p / CH) of row p / CH.
+__host__ __device__ inline int load_chunk_pos(int n, int wave, int lane) { return (2 * n + wave) * 64 + lane; }
+
+// Source lane of ds_read_b64_tr_b16 inside its 16-lane group: lane L reads
+// the 8 bytes holding d = d0 + 4 (L & 3) .. +3 of token base + (L >> 2); after
+// the transpose lane i holds d = d0 + i of tokens base .. base + 3.
+__host__ __device__ inline int tr_token(int L) { return L >> 2; }
+__host__ __device__ inline int tr_dquad(int L) { return L & 3; }
 
 // Workgroups are handed to the 8 XCDs round-robin by linear id.  Re-number
 // them so that each XCD walks a contiguous range of logical work items (the

@@ -9,14 +9,16 @@
 //   1. the R pooled query rows are staged in LDS;
 //   2. raw float64 dot products Qc[i] . Kc[j] for every KV block j of the
 //      sequence land in LDS (thread j reads Kc[j] once and serves R rows);
-//   3. one wave per row selects the top-k exactly: the k-th largest score is
-//      found bit by bit on order-preserving 64-bit keys (64 rounds of a
-//      wave-wide count), ties at the threshold go to the lowest indices, and
-//      the indices are emitted in ascending order with ballot prefix counts;
+//   3. one wave per row selects the top-k exactly: the row's order-preserving
+//      64-bit keys sit in registers (up to 64 per lane), the k-th largest is
+//      found bit by bit (64 rounds of a wave-wide ballot count), ties at the
+//      threshold go to the lowest indices, and the indices are emitted in
+//      ascending order with ballot prefix counts;
 //   4. the same wave turns the row into softmax weights exp((s - max)/sqrt(D))
 //      and their sum, in float64;
 //   5. out_c[i][d] = sum_j w[i][j] Vc[j][d] / sum_j w[i][j], rounded once to
-//      float32.
+//      float32; each thread loads a Vc value once and applies it to all R
+//      rows.
 // Scores, softmax and the coarse product stay in float64 so that the
 // selected set matches a float64 reference on any input whose k-th and
 // (k+1)-th scores are not within a few ulps of each other.
@@ -52,13 +54,13 @@ __device__ __forceinline__ double wave_sum(double x) {
     return x;
 }
 
-template <int D, int R>
+template <int D, int R, int KPL>
 __global__ __launch_bounds__(kCoarseThreads) void coarse_topk_kernel(
     DevProblem P, const double* __restrict__ qc, const double* __restrict__ kc,
     const double* __restrict__ vc, float* __restrict__ out_c, int* __restrict__ idx_out,
     int* __restrict__ num_out, int kv_cap, double scale) {
     extern __shared__ double lds[];
-    double* qrow = lds;              // [R][D]
+    double* qrow = lds;              // [R][D]; reused for the final reduction
     double* sc = lds + R * D;        // [R][kv_cap]
     __shared__ double lsum[R];
 
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_topk_kernel(
     const int i0 = blockIdx.x * R;
     if (i0 >= sv.nq) return;
     const int nr = min(R, sv.nq - i0);
-    const int nkv = min(sv.nkv, kv_cap);
+    const int nkv = min(min(sv.nkv, kv_cap), 64 * KPL);
     const int tid = threadIdx.x;
 
     // 1. pooled query rows
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_topk_kernel(
     }
     __syncthreads();
 
-    // 2. raw scores
+    // 2. raw scores: thread j reads Kc[j] once and serves all R rows
     for (int j = tid; j < nkv; j += kCoarseThreads) {
         double acc[R];
 #pragma unroll
@@ -89,8 +91,9 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_topk_kernel(
             const double2 kv = kr[d2];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                acc[r] = fma(qrow[r * D + 2 * d2], kv.x, acc[r]);
-                acc[r] = fma(qrow[r * D + 2 * d2 + 1], kv.y, acc[r]);
+                const double2 qv = *reinterpret_cast<const double2*>(&qrow[r * D + 2 * d2]);
+                acc[r] = fma(qv.x, kv.x, acc[r]);
+                acc[r] = fma(qv.y, kv.y, acc[r]);
             }
         }
 #pragma unroll
@@ -98,7 +101,8 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_topk_kernel(
     }
     __syncthreads();
 
-    // 3 + 4. per row: exact top-k, then softmax weights
+    // 3 + 4. per row (one wave): exact top-k on keys held in registers, then
+    // softmax weights written back in place
     const int wave = tid / 64;
     const int lane = tid % 64;
     for (int r = wave; r < nr; r += kCoarseWaves) {
@@ -107,31 +111,35 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_topk_kernel(
         const int64_t qb = sv.qblk_base + i0 + r;
         int* orow = idx_out + qb * P.idx_row;
 
-        // k-th largest key, found bit by bit
+        uint64_t key[KPL];  // 0 marks "no block": below the key of any double
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+            const int j = 64 * e + lane;
+            key[e] = j < nkv ? order_key(row[j]) : 0ull;
+        }
+        // largest T with #{key >= T} >= k, i.e. the k-th largest key
         uint64_t T = 0;
         for (int bit = 63; bit >= 0; --bit) {
             const uint64_t cand = T | (1ull << bit);
             int cnt = 0;
-            for (int j0 = 0; j0 < nkv; j0 += 64) {
-                const int j = j0 + lane;
-                const bool ge = j < nkv && order_key(row[j]) >= cand;
-                cnt += __popcll(__ballot(ge));
-            }
+#pragma unroll
+            for (int e = 0; e < KPL; ++e)
+                if (64 * e < nkv) cnt += __popcll(__ballot(key[e] >= cand));
             if (cnt >= k) T = cand;
         }
         int n_gt = 0;
-        for (int j0 = 0; j0 < nkv; j0 += 64) {
-            const int j = j0 + lane;
-            n_gt += __popcll(__ballot(j < nkv && order_key(row[j]) > T));
-        }
+#pragma unroll
+        for (int e = 0; e < KPL; ++e)
+            if (64 * e < nkv) n_gt += __popcll(__ballot(key[e] > T));
         const int need_eq = k - n_gt;
         int n_sel = 0, n_eq = 0;
-        for (int j0 = 0; j0 < nkv; j0 += 64) {
-            const int j = j0 + lane;
-            const uint64_t key = j < nkv ? order_key(row[j]) : 0ull;
-            const bool eq = j < nkv && key == T;
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+            if (64 * e >= nkv) break;
+            const int j = 64 * e + lane;
+            const bool eq = key[e] == T;
             const uint64_t eq_mask = __ballot(eq);
-            const bool sel = j < nkv && (key > T || (eq && n_eq + prefix_popc(eq_mask) < need_eq));
+            const bool sel = key[e] > T || (eq && n_eq + prefix_popc(eq_mask) < need_eq);
             const uint64_t sel_mask = __ballot(sel);
             if (sel) orow[n_sel + prefix_popc(sel_mask)] = j + sv.idx_rebase;
             n_sel += __popcll(sel_mask);
@@ -140,7 +148,6 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_topk_kernel(
         for (int t = n_sel + lane; t < P.idx_row; t += 64) orow[t] = -1;
         if (lane == 0) num_out[qb] = n_sel;
 
-        // softmax weights in place
         double m = -INFINITY;
         for (int j = lane; j < nkv; j += 64) m = fmax(m, row[j]);
         m = wave_max(m);
@@ -155,15 +162,34 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_topk_kernel(
     }
     __syncthreads();
 
-    // 5. coarse output
-    constexpr int RS = kCoarseThreads / D;  // row groups
+    // 5. coarse output: thread (d, part) sums over every PARTS-th KV block for
+    // all rows at once, each Vc value loaded once; parts are added via LDS
+    constexpr int PARTS = kCoarseThreads / D;
     const int d = tid % D;
-    for (int r = tid / D; r < nr; r += RS) {
-        const double* w = sc + r * kv_cap;
-        double acc = 0.0;
-        for (int j = 0; j < nkv; ++j) acc = fma(w[j], vc[(sv.kvblk_base + j) * D + d], acc);
-        out_c[(sv.qblk_base + i0 + r) * D + d] = (float)(acc / lsum[r]);
+    const int part = tid / D;
+    double acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0;
+#pragma unroll 4
+    for (int j = part; j < nkv; j += PARTS) {
+        const double vv = vc[(sv.kvblk_base + j) * D + d];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = fma(sc[r * kv_cap + j], vv, acc[r]);
     }
+    for (int p = 1; p < PARTS; ++p) {
+        if (part == p)
+#pragma unroll
+            for (int r = 0; r < R; ++r) qrow[r * D + d] = acc[r];
+        __syncthreads();
+        if (part == 0)
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] += qrow[r * D + d];
+        __syncthreads();
+    }
+    if (part == 0)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (r < nr) out_c[(sv.qblk_base + i0 + r) * D + d] = (float)(acc[r] / lsum[r]);
 }
 
 template <int D>
@@ -171,16 +197,25 @@ size_t coarse_lds_bytes(int R, int kv_cap) {
     return (size_t)8 * R * (D + kv_cap);
 }
 
-template <int D, int R>
-hipError_t launch_r(const DevProblem& P, const double* qc, const double* kc, const double* vc,
-                    float* out_c, int* idx, int* num, hipStream_t st) {
+template <int D, int R, int KPL>
+hipError_t launch_rk(const DevProblem& P, const double* qc, const double* kc, const double* vc,
+                     float* out_c, int* idx, int* num, hipStream_t st) {
     const int max_nq = P.packed ? P.max_q : P.nQ;
     const int kv_cap = P.packed ? P.max_kv : P.nKV;
     dim3 grid((max_nq + R - 1) / R, P.H, P.nseq);
     const size_t lds = coarse_lds_bytes<D>(R, kv_cap);
-    hipLaunchKernelGGL((coarse_topk_kernel<D, R>), grid, dim3(kCoarseThreads), lds, st, P, qc, kc,
-                       vc, out_c, idx, num, kv_cap, 1.0 / sqrt((double)D));
+    hipLaunchKernelGGL((coarse_topk_kernel<D, R, KPL>), grid, dim3(kCoarseThreads), lds, st, P, qc,
+                       kc, vc, out_c, idx, num, kv_cap, 1.0 / sqrt((double)D));
     return hipGetLastError();
+}
+
+template <int D, int R>
+hipError_t launch_r(const DevProblem& P, const double* qc, const double* kc, const double* vc,
+                    float* out_c, int* idx, int* num, hipStream_t st) {
+    const int kv_cap = P.packed ? P.max_kv : P.nKV;
+    if (kv_cap <= 4 * 64) return launch_rk<D, R, 4>(P, qc, kc, vc, out_c, idx, num, st);
+    if (kv_cap <= 16 * 64) return launch_rk<D, R, 16>(P, qc, kc, vc, out_c, idx, num, st);
+    return launch_rk<D, R, 64>(P, qc, kc, vc, out_c, idx, num, st);
 }
 
 template <int D>

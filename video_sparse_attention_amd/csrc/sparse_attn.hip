@@ -6,25 +6,26 @@
 //
 // Work decomposition (gfx950, 64-wide waves, bf16 MFMA 32x32x16):
 //   * one workgroup = 2 waves = one 64-token query block of one head; wave w
-//     owns query rows 32w .. 32w+31;
+//     owns query rows 32w .. 32w+31 and keeps its Q fragment in registers;
 //   * scores are computed transposed, S^T = K Q^T, so the accumulator layout
 //     of v_mfma_f32_32x32x16_bf16 gives every lane ONE query column and 32
-//     of its KV tokens: the running max / sum of the online softmax stay in
-//     the lane (one cross-lane step with lane ^ 32 per KV block);
-//   * the output is accumulated transposed as well, O^T = V^T P^T, so the
-//     bf16 probabilities feed the B operand straight from the S^T
-//     accumulator registers (k-slots are relabelled consistently on both
-//     operands) and the per-query rescale by exp(m_old - m_new) is in-lane;
-//   * K (A operand of S^T: row = KV token, k = d) is loaded from global
-//     memory straight into MFMA registers, 16 bytes per lane;
-//   * V must be contracted over tokens, so it is staged once per KV block
-//     into LDS transposed, V^T[d][token], with the tokens of each 16-token
-//     group permuted so that a lane's 8 k-slots are one 16-byte ds_read and
-//     the 16-byte groups XOR-swizzled by the row so that the transposing
-//     ds_write_b64 and the ds_read_b128 stay free of bank conflicts;
-//   * Q stays in registers for the whole block list; float32 accumulation and
-//     softmax (exp2 with log2(e)/sqrt(D) folded into one FMA); one bf16
-//     rounding per output element.
+//     of its KV tokens: the running max and sum of the online softmax stay
+//     in the lane (one exchange with lane ^ 32 per KV block);
+//   * the output is accumulated transposed too, O^T = V^T P^T: the bf16
+//     probabilities feed the B operand straight from the S^T accumulator
+//     registers (the k-slots of both operands are relabelled the same way)
+//     and the rescale by exp(m_old - m_new) is in-lane;
+//   * each selected KV block is copied global -> LDS by direct loads
+//     (global_load_lds_dwordx4, no register staging) into row-major K and V
+//     tiles with XOR-swizzled 16-byte chunks; K operands come from
+//     ds_read_b128, the transposed V operands from ds_read_b64_tr_b16;
+//   * software pipeline per KV block t: wait K_t, S = K_t Q^T, release the K
+//     tile and start loading K_{t+1}; softmax; wait V_t, O += V_t^T P^T,
+//     release the V tile and start loading V_{t+1} - so each load overlaps
+//     half an iteration of this workgroup plus the work of the other
+//     workgroups on the CU;
+//   * float32 accumulation and softmax (exp2 with log2(e)/sqrt(D) folded
+//     into one FMA); one bf16 rounding per output element.
 #include "attn_layout.hpp"
 #include "vsa_internal.hpp"
 
@@ -32,23 +33,92 @@ namespace vsa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kAttnThreads = 128;
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
-
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
-
-__device__ __forceinline__ uint32_t word(const uint4& u, int w) {
-    return w == 0 ? u.x : (w == 1 ? u.y : (w == 2 ? u.z : u.w));
-}
 
 __device__ __forceinline__ uint32_t bf16pair(float a, float b) {
     const __bf16 x = (__bf16)a, y = (__bf16)b;
     return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (loads complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier that first waits for this wave's own LDS reads, so that
+// no wave can start overwriting a tile while another's read is in flight.
+__device__ __forceinline__ void wg_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// A pointer every lane holds the same value of, moved to scalar registers.
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const T*)(((uint64_t)hi << 32) | lo);
+}
+
+// Scalar load of base[i] (base and i wave-uniform), waited for inside the
+// same asm block.  A scalar load is counted by lgkmcnt, so reading the block
+// list never waits for the direct-to-LDS loads in flight (vmcnt).
+__device__ __forceinline__ int sload_i32(const int* base, int i) {
+    int v;
+    asm volatile("s_load_dword %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
+                 : "=s"(v)
+                 : "s"(base), "s"(i * 4)
+                 : "memory");
+    return v;
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's bytes land at LDS byte lds_base + 16 l.  Written as inline
+// assembly (no output register) so that the compiler does not add its own
+// conservative waits for the LDS write before every LDS read; the kernel
+// orders these copies with explicit vmcnt waits and barriers.
+// M0 (the LDS base of the copy) is saved and restored inside the block.
+__device__ __forceinline__ void dma_16B(const uint16_t* gptr, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gptr), "s"(lds_base)
+        : "memory");
+}
+
+// Copy KV block rows [0, 64) of `src` (rows past `valid` repeat row valid-1,
+// so every address stays inside the tensor and every LDS value is finite)
+// into a swizzled tile: CH/2 copies per wave.
+template <int D, bool IS_V>
+__device__ __forceinline__ void load_tile(uint16_t* tile, const uint16_t* __restrict__ src,
+                                          int64_t row0, int valid, int wave, int lane) {
+    constexpr int CH = D / 8;
+#pragma unroll
+    for (int n = 0; n < CH / 2; ++n) {
+        const int p = load_chunk_pos(n, wave, lane);
+        const int row = p / CH;
+        const int sw = IS_V ? v_swz<CH>(row) : k_swz<CH>(row);
+        const int c = (p % CH) ^ sw;
+        const int r = min(row, valid - 1);
+        dma_16B(src + (row0 + r) * D + 8 * c,
+                __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(tile + (2 * n + wave) * 64 * 8)));
+    }
 }
 
 template <int D>
@@ -56,12 +126,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     DevProblem P, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int* __restrict__ idx, const int* __restrict__ num,
     uint16_t* __restrict__ out, float c_log2) {
-    constexpr int KS = D / 16;        // MFMA k-steps over d for S^T
-    constexpr int DT = D / 32;        // 32-row d tiles of O^T
-    constexpr int CH = D / 8;         // 16-byte chunks per token row
-    constexpr int UNITS = 16 * CH;    // (4-token group, chunk) staging units
-    constexpr int UPT = UNITS / kAttnThreads;
-    __shared__ __attribute__((aligned(16))) uint16_t vt[D * kBlock];
+    constexpr int KS = D / 16;      // MFMA k-steps over d for S^T
+    constexpr int DT = D / 32;      // 32-row d tiles of O^T
+    constexpr int CH = D / 8;       // 16-byte chunks per token row
+    constexpr int LOADS = CH / 2;   // direct-load instructions per wave per tile
+    __shared__ __attribute__((aligned(1024))) uint16_t k_tile[kBlock * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_tile[kBlock * D];
 
     // ---- which query block -------------------------------------------------
     int s, h, i;
@@ -102,6 +172,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
         if (qr < qsize) u = *reinterpret_cast<const uint4*>(q + (qrow0 + qr) * D + 16 * ks + 8 * hh);
         qf[ks] = as_bf16x8(u);
     }
+    // Q is in registers before the first direct-to-LDS copy is issued, so the
+    // copies in flight are the only vector-memory operations the pipeline's
+    // vmcnt waits count.
+    __builtin_amdgcn_s_waitcnt(0);
 
     f32x16 o[DT];
 #pragma unroll
@@ -112,125 +186,137 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     float l = 0.f;        // this lane's share of the running sum
 
     const int64_t qb = sv.qblk_base + i;
-    const int n = clampi(num[qb], 0, P.idx_row);
-    const int* list = idx + qb * P.idx_row;
+    const int n = __builtin_amdgcn_readfirstlane(clampi(num[qb], 0, P.idx_row));
+    const int* list = uniform_ptr(idx + qb * P.idx_row);
+    const int* bs_kv = P.packed ? uniform_ptr(P.bs_kv + sv.kvblk0) : nullptr;
+    const int rebase = __builtin_amdgcn_readfirstlane(sv.idx_rebase);
+    const int nkv = __builtin_amdgcn_readfirstlane(sv.nkv);
 
-    for (int t = 0; t < n; ++t) {
-        const int j = list[t] - sv.idx_rebase;
-        if (j < 0 || j >= sv.nkv) continue;
-        const int kvsize = kv_block_size(P, sv, j);
-        const int64_t kvrow0 = sv.kvrow_base + (int64_t)kBlock * j;
-
-        // K operand: A of S^T, row = KV token 32 mt + l32, k-slots = d
-        bf16x8 kf[2][KS];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const int r = 32 * mt + l32;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                uint4 u = make_uint4(0, 0, 0, 0);
-                if (r < kvsize) u = *reinterpret_cast<const uint4*>(k + (kvrow0 + r) * D + 16 * ks + 8 * hh);
-                kf[mt][ks] = as_bf16x8(u);
-            }
+    // next valid entry of the list at or after position t (-1: none)
+    auto next_valid = [&](int& t) -> int {
+        for (; t < n; ++t) {
+            const int j = sload_i32(list, t) - rebase;
+            if (j >= 0 && j < nkv) return j;
         }
+        return -1;
+    };
+    // valid tokens of local KV block j
+    auto kv_size = [&](int j) -> int {
+        return P.packed ? clampi(sload_i32(bs_kv, j), 1, kBlock) : min(kBlock, P.Skv - kBlock * j);
+    };
 
-        // V block -> registers (4 tokens x 8 d per unit)
-        uint4 vr[UPT][4];
-        int ug4[UPT], uc[UPT];
-#pragma unroll
-        for (int r = 0; r < UPT; ++r) {
-            const int u = tid + kAttnThreads * r;
-            int c, g4;
-            stage_unit<CH>(u, &g4, &c);
-            ug4[r] = g4;
-            uc[r] = c;
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int tok = 4 * g4 + ii;
-                uint4 w = make_uint4(0, 0, 0, 0);
-                if (tok < kvsize) w = *reinterpret_cast<const uint4*>(v + (kvrow0 + tok) * D + 8 * c);
-                vr[r][ii] = w;
-            }
-        }
+    // per-lane read positions inside the tiles
+    // V^T operand via transpose reads: 16-lane group g16 covers d0 .. d0+15
+    const int g16 = lane >> 4, L16 = lane & 15;
+    const int tr_r = tr_token(L16), tr_a = tr_dquad(L16);
+    const int tr_d = 16 * (g16 & 1) + 4 * tr_a;  // + 32 dt
 
-        __syncthreads();  // every wave is done reading the previous V^T
-#pragma unroll
-        for (int r = 0; r < UPT; ++r) {
-            const int pos = tok_pos(4 * ug4[r]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int d = 8 * uc[r] + e;
-                uint2 w2;
-                if ((e & 1) == 0) {
-                    w2.x = pack_lo(word(vr[r][0], e >> 1), word(vr[r][1], e >> 1));
-                    w2.y = pack_lo(word(vr[r][2], e >> 1), word(vr[r][3], e >> 1));
-                } else {
-                    w2.x = pack_hi(word(vr[r][0], e >> 1), word(vr[r][1], e >> 1));
-                    w2.y = pack_hi(word(vr[r][2], e >> 1), word(vr[r][3], e >> 1));
-                }
-                *reinterpret_cast<uint2*>(&vt[vt_off(d, pos)]) = w2;
-            }
-        }
-        __syncthreads();
+    // Pipeline.  Each pass issues the loads of block `jn` (if any) and computes
+    // block `j` (if any); the first pass only issues.  One call site per tile
+    // keeps a single direct-load instruction per tile in the loop.
+    int t = 0;
+    int j = -1, kvsize = 0;
+    int jn = next_valid(t);
+    int kvsize_n = jn >= 0 ? kv_size(jn) : 0;
+    bool first = true;
+    while (j >= 0 || first) {
+        const bool cur = j >= 0;
+        const bool more = jn >= 0;
+        const int64_t r0n = more ? sv.kvrow_base + (int64_t)kBlock * jn : 0;
 
-        // S^T = K Q^T : two 32x32 tiles over the block's 64 tokens
+        // ---- S^T = K Q^T ----------------------------------------------------
         f32x16 sacc[2];
+        if (cur) {
+            wait_vmcnt<LOADS>();  // this wave's part of K_t is in LDS (V_t may be in flight)
+            wg_barrier();         // ... and the other wave's part
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+            for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
+                for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
+                const int row = 32 * mt + l32;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mt][ks], qf[ks], sacc[mt], 0, 0, 0);
+                for (int ks = 0; ks < KS; ++ks) {
+                    const uint4 a = *reinterpret_cast<const uint4*>(
+                        k_tile + tile_off<CH>(row, 2 * ks + hh, k_swz<CH>(row)));
+                    sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[ks], sacc[mt], 0, 0, 0);
+                }
+            }
+            wg_barrier();  // both waves are done with the K tile
         }
+        if (more) load_tile<D, false>(k_tile, k, r0n, kvsize_n, wave, lane);
 
-        // online softmax; accumulator e of tile mt is token 32 mt + 8 (e/4) + 4 hh + e%4
-        float bm = -INFINITY;
+        if (cur) {
+            // ---- online softmax; acc e of tile mt is token 32 mt + 8 (e/4) + 4 hh + e%4
+            float bm = -INFINITY;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int tok = 32 * mt + 8 * (e >> 2) + 4 * hh + (e & 3);
-                if (tok >= kvsize) sacc[mt][e] = -INFINITY;
-                bm = fmaxf(bm, sacc[mt][e]);
-            }
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float m_new = fmaxf(m, bm);
-        const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c_log2);
-        m = m_new;
-        const float mc = m_new * c_log2;
-        float ps = 0.f;
+                for (int e = 0; e < 16; ++e) {
+                    const int tok = 32 * mt + 8 * (e >> 2) + 4 * hh + (e & 3);
+                    if (tok >= kvsize) sacc[mt][e] = -INFINITY;
+                    bm = fmaxf(bm, sacc[mt][e]);
+                }
+            bm = fmaxf(bm, __shfl_xor(bm, 32));
+            const float m_new = fmaxf(m, bm);
+            const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c_log2);
+            m = m_new;
+            const float mc = m_new * c_log2;
+            float ps = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][e], c_log2, -mc));
-                sacc[mt][e] = p;
-                ps += p;
-            }
-        l = fmaf(l, alpha, ps);
+                for (int e = 0; e < 16; ++e) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][e], c_log2, -mc));
+                    sacc[mt][e] = p;
+                    ps += p;
+                }
+            l = fmaf(l, alpha, ps);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+                for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
 
-        // O^T += V^T P^T over 4 k-steps of 16 tokens
+            // ---- O^T += V^T P^T over 4 k-steps of 16 tokens -----------------
+            if (more) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();  // V_t landed (K_{t+1} may be in flight)
+            wg_barrier();
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-            const f32x16& sa = sacc[s4 >> 1];
-            const int base = 8 * (s4 & 1);
-            uint4 pw;
-            pw.x = bf16pair(sa[base + 0], sa[base + 1]);
-            pw.y = bf16pair(sa[base + 2], sa[base + 3]);
-            pw.z = bf16pair(sa[base + 4], sa[base + 5]);
-            pw.w = bf16pair(sa[base + 6], sa[base + 7]);
-            const bf16x8 pb = as_bf16x8(pw);
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const f32x16& sa = sacc[s4 >> 1];
+                const int base = 8 * (s4 & 1);
+                uint4 pw;
+                pw.x = bf16pair(sa[base + 0], sa[base + 1]);
+                pw.y = bf16pair(sa[base + 2], sa[base + 3]);
+                pw.z = bf16pair(sa[base + 4], sa[base + 5]);
+                pw.w = bf16pair(sa[base + 6], sa[base + 7]);
+                const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const int d = 32 * dt + l32;
-                const uint4 va = *reinterpret_cast<const uint4*>(&vt[vt_off(d, 16 * s4 + 8 * hh)]);
-                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), pb, o[dt], 0, 0, 0);
+                for (int dt = 0; dt < DT; ++dt) {
+                    const int d = 32 * dt + tr_d;
+                    s16x4 half[2];
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) {
+                        const int tok = 16 * s4 + 8 * jj + 4 * hh + tr_r;
+                        const int off = tile_off<CH>(tok, d >> 3, v_swz<CH>(tok)) + (d & 7);
+                        half[jj] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)v_tile + off));
+                    }
+                    const uint2 h0 = __builtin_bit_cast(uint2, half[0]);
+                    const uint2 h1 = __builtin_bit_cast(uint2, half[1]);
+                    const uint4 va = make_uint4(h0.x, h0.y, h1.x, h1.y);
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), pb, o[dt], 0, 0, 0);
+                }
             }
+            wg_barrier();  // both waves are done with the V tile
+        }
+        if (more) load_tile<D, true>(v_tile, v, r0n, kvsize_n, wave, lane);
+
+        first = false;
+        j = jn;
+        kvsize = kvsize_n;
+        if (more) {
+            ++t;
+            jn = next_valid(t);
+            kvsize_n = jn >= 0 ? kv_size(jn) : 0;
         }
     }
 
