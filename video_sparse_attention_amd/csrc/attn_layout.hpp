@@ -16,17 +16,21 @@ namespace vsa {
 
 // XOR applied to the 16-byte chunk index of K row `row` (CH chunks per row).
 // The S^T = K Q^T A operand reads one chunk of 32 consecutive rows per
-// instruction (ds_read_b128); rows 0..15 of a pass then fall on 16
-// different chunk columns.
+// instruction (ds_read_b128, serviced 8 lanes at a time); rows 0..7 of a
+// pass fall on 8 different 16-byte bank groups.  The swizzle depends only on
+// row bits that stay fixed across a lane's copy instructions (rows 8n + r0
+// for D = 128, 16n + r0 for D = 64), so a lane's source offset inside a
+// block advances by a constant 2048 bytes per instruction.
 template <int CH>
 __host__ __device__ inline int k_swz(int row) {
-    return CH == 16 ? (row & 15) : ((row ^ (row >> 3)) & 7);
+    return CH == 16 ? (row & 7) : ((row & 7) ^ ((row >> 3) & 1));
 }
 
 // XOR applied to the chunk index of V row `row`.  The O^T = V^T P^T A
 // operand is read with ds_read_b64_tr_b16: each 16-lane group fetches a
 // 4-token x 16-d sub-block; rows 4a..4a+3 are spread over four disjoint
 // chunk pairs (and four disjoint chunk quads for the 32 lanes of a pass).
+// Depends on row & 3 only.
 template <int CH>
 __host__ __device__ inline int v_swz(int row) {
     return (4 * (row & 3) + 2 * ((row >> 1) & 1)) & (CH - 1);
@@ -42,6 +46,17 @@ __host__ __device__ inline int tile_off(int row, int c, int swz) {
 // p = (2 n + w) * 64 + lane; that physical chunk holds logical chunk
 // (p % CH) ^ swz(p / CH) of row p / CH.
 __host__ __device__ inline int load_chunk_pos(int n, int wave, int lane) { return (2 * n + wave) * 64 + lane; }
+
+// Byte offset, inside a full 64-row block of the source tensor, of the chunk
+// that instruction 0 of (wave, lane) copies; instruction n copies the one
+// 2048 * n bytes further (rows are 8 * CH * 2 bytes).
+template <int CH, bool IS_V>
+__host__ __device__ inline int lane_src_offset(int wave, int lane) {
+    const int p = load_chunk_pos(0, wave, lane);
+    const int row = p / CH;
+    const int sw = IS_V ? v_swz<CH>(row) : k_swz<CH>(row);
+    return row * CH * 16 + 16 * ((p % CH) ^ sw);
+}
 
 // Source lane of ds_read_b64_tr_b16 inside its 16-lane group: lane L reads
 // the 8 bytes holding d = d0 + 4 (L & 3) .. +3 of token base + (L >> 2); after

@@ -25,7 +25,9 @@
 //     half an iteration of this workgroup plus the work of the other
 //     workgroups on the CU;
 //   * float32 accumulation and softmax (exp2 with log2(e)/sqrt(D) folded
-//     into one FMA); one bf16 rounding per output element.
+//     into one FMA); the running max moves lazily (only when a block raises
+//     it by more than 2^8), so most blocks skip the rescale of the output;
+//     one bf16 rounding per output element.
 #include "attn_layout.hpp"
 #include "vsa_internal.hpp"
 
@@ -44,9 +46,13 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t bf16pair(float a, float b) {
-    const __bf16 x = (__bf16)a, y = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight
@@ -71,53 +77,55 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
     return (const T*)(((uint64_t)hi << 32) | lo);
 }
 
-// Scalar load of base[i] (base and i wave-uniform), waited for inside the
-// same asm block.  A scalar load is counted by lgkmcnt, so reading the block
-// list never waits for the direct-to-LDS loads in flight (vmcnt).
-__device__ __forceinline__ int sload_i32(const int* base, int i) {
-    int v;
-    asm volatile("s_load_dword %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
-                 : "=s"(v)
-                 : "s"(base), "s"(i * 4)
-                 : "memory");
-    return v;
-}
+// Read-only, wave-uniform data (the block list, block sizes) is read through
+// the constant address space so the compiler uses scalar loads, which are
+// counted by lgkmcnt and never wait for the direct-to-LDS copies in flight.
+typedef const __attribute__((address_space(4))) int const_int;
 
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
-// lane l's bytes land at LDS byte lds_base + 16 l.  Written as inline
-// assembly (no output register) so that the compiler does not add its own
-// conservative waits for the LDS write before every LDS read; the kernel
-// orders these copies with explicit vmcnt waits and barriers.
-// M0 (the LDS base of the copy) is saved and restored inside the block.
-__device__ __forceinline__ void dma_16B(const uint16_t* gptr, uint32_t lds_base) {
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4,
+// scalar base + per-lane 32-bit offset): lane l's bytes land at LDS byte
+// lds_base + 16 l.  Written as inline assembly (it has no output register)
+// so that the compiler does not add its own conservative waits for the LDS
+// write before every LDS read; the kernel orders these copies with explicit
+// vmcnt waits and barriers.  M0 (the LDS base of the copy) is saved and
+// restored inside the block.
+__device__ __forceinline__ void dma_16B(const void* sbase, uint32_t voff, uint32_t lds_base) {
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
+        "s_mov_b32 m0, %3\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "v"(gptr), "s"(lds_base)
+        : "v"(voff), "s"(sbase), "s"(lds_base)
         : "memory");
 }
 
-// Copy KV block rows [0, 64) of `src` (rows past `valid` repeat row valid-1,
-// so every address stays inside the tensor and every LDS value is finite)
-// into a swizzled tile: CH/2 copies per wave.
+// Copy one 64-row KV block starting at `block` into a swizzled tile.  Full
+// blocks: every lane's source offset is lane_off + 2048 n.  Partial blocks
+// (valid < 64): rows past valid - 1 repeat that row, so every address stays
+// inside the tensor and every LDS value is finite.
 template <int D, bool IS_V>
-__device__ __forceinline__ void load_tile(uint16_t* tile, const uint16_t* __restrict__ src,
-                                          int64_t row0, int valid, int wave, int lane) {
+__device__ __forceinline__ void load_tile(uint16_t* tile, const uint16_t* block, int valid, int wave,
+                                          int lane, uint32_t lane_off) {
     constexpr int CH = D / 8;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)tile) + 1024u * wave;
+    const char* base = (const char*)uniform_ptr(block);
+    if (valid == kBlock) {
 #pragma unroll
-    for (int n = 0; n < CH / 2; ++n) {
-        const int p = load_chunk_pos(n, wave, lane);
-        const int row = p / CH;
-        const int sw = IS_V ? v_swz<CH>(row) : k_swz<CH>(row);
-        const int c = (p % CH) ^ sw;
-        const int r = min(row, valid - 1);
-        dma_16B(src + (row0 + r) * D + 8 * c,
-                __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(tile + (2 * n + wave) * 64 * 8)));
+        for (int n = 0; n < CH / 2; ++n)
+            dma_16B(base + 2048 * n, lane_off, __builtin_amdgcn_readfirstlane(lds0 + 2048u * n));
+    } else {
+#pragma unroll
+        for (int n = 0; n < CH / 2; ++n) {
+            const int p = load_chunk_pos(n, wave, lane);
+            const int row = p / CH;
+            const int sw = IS_V ? v_swz<CH>(row) : k_swz<CH>(row);
+            const int c = (p % CH) ^ sw;
+            const int r = min(row, valid - 1);
+            dma_16B(base, (uint32_t)(r * CH * 16 + 16 * c), __builtin_amdgcn_readfirstlane(lds0 + 2048u * n));
+        }
     }
 }
 
@@ -130,6 +138,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     constexpr int DT = D / 32;      // 32-row d tiles of O^T
     constexpr int CH = D / 8;       // 16-byte chunks per token row
     constexpr int LOADS = CH / 2;   // direct-load instructions per wave per tile
+    // The running max is only moved when a block's max exceeds it by more than
+    // kLazy (in log2 units): probabilities then stay <= 2^kLazy, far from any
+    // float32/bf16 range limit, and most blocks skip the rescale entirely.
+    constexpr float kLazy = 8.0f;
     __shared__ __attribute__((aligned(1024))) uint16_t k_tile[kBlock * D];
     __shared__ __attribute__((aligned(1024))) uint16_t v_tile[kBlock * D];
 
@@ -172,48 +184,51 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
         if (qr < qsize) u = *reinterpret_cast<const uint4*>(q + (qrow0 + qr) * D + 16 * ks + 8 * hh);
         qf[ks] = as_bf16x8(u);
     }
-    // Q is in registers before the first direct-to-LDS copy is issued, so the
-    // copies in flight are the only vector-memory operations the pipeline's
-    // vmcnt waits count.
-    __builtin_amdgcn_s_waitcnt(0);
 
     f32x16 o[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
-    float m = -INFINITY;  // running max of raw scores for this lane's query
+    float m = -INFINITY;  // running (lazy) max of raw scores for this lane's query
     float l = 0.f;        // this lane's share of the running sum
 
     const int64_t qb = sv.qblk_base + i;
     const int n = __builtin_amdgcn_readfirstlane(clampi(num[qb], 0, P.idx_row));
-    const int* list = uniform_ptr(idx + qb * P.idx_row);
-    const int* bs_kv = P.packed ? uniform_ptr(P.bs_kv + sv.kvblk0) : nullptr;
+    const_int* list = (const_int*)uniform_ptr(idx + qb * P.idx_row);
+    const_int* bs_kv = (const_int*)(P.packed ? uniform_ptr(P.bs_kv + sv.kvblk0) : nullptr);
     const int rebase = __builtin_amdgcn_readfirstlane(sv.idx_rebase);
     const int nkv = __builtin_amdgcn_readfirstlane(sv.nkv);
+    const float lazy_raw = kLazy / c_log2;  // kLazy in raw-score units
+
+    // Q is in registers before the first direct-to-LDS copy is issued, so the
+    // copies in flight are the only vector-memory operations the pipeline's
+    // vmcnt waits count.
+    __builtin_amdgcn_s_waitcnt(0);
 
     // next valid entry of the list at or after position t (-1: none)
     auto next_valid = [&](int& t) -> int {
         for (; t < n; ++t) {
-            const int j = sload_i32(list, t) - rebase;
+            const int j = list[t] - rebase;
             if (j >= 0 && j < nkv) return j;
         }
         return -1;
     };
     // valid tokens of local KV block j
     auto kv_size = [&](int j) -> int {
-        return P.packed ? clampi(sload_i32(bs_kv, j), 1, kBlock) : min(kBlock, P.Skv - kBlock * j);
+        return P.packed ? clampi(bs_kv[j], 1, kBlock) : min(kBlock, P.Skv - kBlock * j);
     };
 
-    // per-lane read positions inside the tiles
+    // per-lane positions inside the tiles
+    const uint32_t koff = (uint32_t)lane_src_offset<CH, false>(wave, lane);
+    const uint32_t voff = (uint32_t)lane_src_offset<CH, true>(wave, lane);
     // V^T operand via transpose reads: 16-lane group g16 covers d0 .. d0+15
     const int g16 = lane >> 4, L16 = lane & 15;
     const int tr_r = tr_token(L16), tr_a = tr_dquad(L16);
     const int tr_d = 16 * (g16 & 1) + 4 * tr_a;  // + 32 dt
 
     // Pipeline.  Each pass issues the loads of block `jn` (if any) and computes
-    // block `j` (if any); the first pass only issues.  One call site per tile
-    // keeps a single direct-load instruction per tile in the loop.
+    // block `j` (if any); the first pass only issues.
     int t = 0;
     int j = -1, kvsize = 0;
     int jn = next_valid(t);
@@ -243,24 +258,36 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
             }
             wg_barrier();  // both waves are done with the K tile
         }
-        if (more) load_tile<D, false>(k_tile, k, r0n, kvsize_n, wave, lane);
+        if (more) load_tile<D, false>(k_tile, k + r0n * D, kvsize_n, wave, lane, koff);
 
         if (cur) {
             // ---- online softmax; acc e of tile mt is token 32 mt + 8 (e/4) + 4 hh + e%4
+            if (kvsize < kBlock) {
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int tok = 32 * mt + 8 * (e >> 2) + 4 * hh + (e & 3);
+                        if (tok >= kvsize) sacc[mt][e] = -INFINITY;
+                    }
+            }
             float bm = -INFINITY;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int tok = 32 * mt + 8 * (e >> 2) + 4 * hh + (e & 3);
-                    if (tok >= kvsize) sacc[mt][e] = -INFINITY;
-                    bm = fmaxf(bm, sacc[mt][e]);
-                }
+                for (int e = 0; e < 16; ++e) bm = fmaxf(bm, sacc[mt][e]);
             bm = fmaxf(bm, __shfl_xor(bm, 32));
-            const float m_new = fmaxf(m, bm);
-            const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c_log2);
-            m = m_new;
-            const float mc = m_new * c_log2;
+            if (__ballot(bm > m + lazy_raw)) {  // some query's max moved: rescale
+                const float m_new = fmaxf(m, bm);
+                const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c_log2);
+                m = m_new;
+                l *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+            }
+            const float mc = m * c_log2;
             float ps = 0.f;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
@@ -270,11 +297,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
                     sacc[mt][e] = p;
                     ps += p;
                 }
-            l = fmaf(l, alpha, ps);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+            l += ps;
 
             // ---- O^T += V^T P^T over 4 k-steps of 16 tokens -----------------
             if (more) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();  // V_t landed (K_{t+1} may be in flight)
@@ -308,7 +331,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
             }
             wg_barrier();  // both waves are done with the V tile
         }
-        if (more) load_tile<D, true>(v_tile, v, r0n, kvsize_n, wave, lane);
+        if (more) load_tile<D, true>(v_tile, v + r0n * D, kvsize_n, wave, lane, voff);
 
         first = false;
         j = jn;
