@@ -59,8 +59,8 @@ static std::vector<int> fill_tile(int valid) {
                 const int sw = IS_V ? vsa::v_swz<CH>(row) : vsa::k_swz<CH>(row);
                 const int c = (p % CH) ^ sw;
                 CHECK(c >= 0 && c < CH, "logical chunk %d out of range", c);
-                // full blocks use the fixed per-lane offset + 2048 n
-                const int fast = vsa::lane_src_offset<CH, IS_V>(wave, lane) + 2048 * n;
+                // full blocks use the fixed per-lane offset of n & 1 + 4096 (n >> 1)
+                const int fast = vsa::lane_src_offset<CH, IS_V>(wave, lane, n & 1) + 4096 * (n >> 1);
                 CHECK(fast == row * ROWB + 16 * c, "fast-path offset D%d n%d w%d l%d", D, n, wave, lane);
                 CHECK(fast >= 0 && fast + 16 <= 64 * ROWB, "fast-path offset out of the block");
                 const int src_row = row < valid ? row : valid - 1;
@@ -167,6 +167,7 @@ static void check_d() {
     printf("D=%d: worst bank ways K read %d/%d, V read %d/%d (32/64 banks)\n", D, worst[0][0], worst[0][1],
            worst[1][0], worst[1][1]);
     CHECK(worst[0][0] == 1 && worst[1][0] == 1, "bank conflicts in the 32-bank model");
+    if (D == 128) CHECK(worst[0][1] == 1 && worst[1][1] == 1, "bank conflicts in the 64-bank model");
 }
 
 int main() {

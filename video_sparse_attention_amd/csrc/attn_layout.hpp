@@ -16,14 +16,14 @@ namespace vsa {
 
 // XOR applied to the 16-byte chunk index of K row `row` (CH chunks per row).
 // The S^T = K Q^T A operand reads one chunk of 32 consecutive rows per
-// instruction (ds_read_b128, serviced 8 lanes at a time); rows 0..7 of a
-// pass fall on 8 different 16-byte bank groups.  The swizzle depends only on
-// row bits that stay fixed across a lane's copy instructions (rows 8n + r0
-// for D = 128, 16n + r0 for D = 64), so a lane's source offset inside a
-// block advances by a constant 2048 bytes per instruction.
+// instruction (ds_read_b128); with 64 banks a pass serves 16 lanes = 16
+// consecutive rows, which then fall on 16 different chunk columns.  Copy
+// instruction n of a lane covers row 8n + r0 (D = 128) or 16n + r0 (D = 64),
+// so the swizzle seen by a lane only depends on n through bit 3 of the row
+// (D = 128): its source offset is lane_off[n & 1] + 2048 n.
 template <int CH>
 __host__ __device__ inline int k_swz(int row) {
-    return CH == 16 ? (row & 7) : ((row & 7) ^ ((row >> 3) & 1));
+    return CH == 16 ? (row & 15) : ((row & 7) ^ ((row >> 3) & 1));
 }
 
 // XOR applied to the chunk index of V row `row`.  The O^T = V^T P^T A
@@ -48,11 +48,11 @@ __host__ __device__ inline int tile_off(int row, int c, int swz) {
 __host__ __device__ inline int load_chunk_pos(int n, int wave, int lane) { return (2 * n + wave) * 64 + lane; }
 
 // Byte offset, inside a full 64-row block of the source tensor, of the chunk
-// that instruction 0 of (wave, lane) copies; instruction n copies the one
-// 2048 * n bytes further (rows are 8 * CH * 2 bytes).
+// that copy instruction n (n = 0 or 1) of (wave, lane) fetches; instruction
+// n + 2m fetches the one 4096 m bytes further (rows are 16 * CH bytes).
 template <int CH, bool IS_V>
-__host__ __device__ inline int lane_src_offset(int wave, int lane) {
-    const int p = load_chunk_pos(0, wave, lane);
+__host__ __device__ inline int lane_src_offset(int wave, int lane, int n) {
+    const int p = load_chunk_pos(n, wave, lane);
     const int row = p / CH;
     const int sw = IS_V ? v_swz<CH>(row) : k_swz<CH>(row);
     return row * CH * 16 + 16 * ((p % CH) ^ sw);

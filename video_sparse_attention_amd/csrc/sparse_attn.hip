@@ -103,19 +103,20 @@ __device__ __forceinline__ void dma_16B(const void* sbase, uint32_t voff, uint32
 }
 
 // Copy one 64-row KV block starting at `block` into a swizzled tile.  Full
-// blocks: every lane's source offset is lane_off + 2048 n.  Partial blocks
+// blocks: a lane's source offset is lane_off[n & 1] + 2048 n.  Partial blocks
 // (valid < 64): rows past valid - 1 repeat that row, so every address stays
 // inside the tensor and every LDS value is finite.
 template <int D, bool IS_V>
 __device__ __forceinline__ void load_tile(uint16_t* tile, const uint16_t* block, int valid, int wave,
-                                          int lane, uint32_t lane_off) {
+                                          int lane, uint32_t lane_off0, uint32_t lane_off1) {
     constexpr int CH = D / 8;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)tile) + 1024u * wave;
     const char* base = (const char*)uniform_ptr(block);
     if (valid == kBlock) {
 #pragma unroll
         for (int n = 0; n < CH / 2; ++n)
-            dma_16B(base + 2048 * n, lane_off, __builtin_amdgcn_readfirstlane(lds0 + 2048u * n));
+            dma_16B(base + 4096 * (n >> 1), (n & 1) ? lane_off1 : lane_off0,
+                    __builtin_amdgcn_readfirstlane(lds0 + 2048u * n));
     } else {
 #pragma unroll
         for (int n = 0; n < CH / 2; ++n) {
@@ -220,8 +221,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     };
 
     // per-lane positions inside the tiles
-    const uint32_t koff = (uint32_t)lane_src_offset<CH, false>(wave, lane);
-    const uint32_t voff = (uint32_t)lane_src_offset<CH, true>(wave, lane);
+    const uint32_t koff0 = (uint32_t)lane_src_offset<CH, false>(wave, lane, 0);
+    const uint32_t koff1 = (uint32_t)lane_src_offset<CH, false>(wave, lane, 1);
+    const uint32_t voff0 = (uint32_t)lane_src_offset<CH, true>(wave, lane, 0);
+    const uint32_t voff1 = (uint32_t)lane_src_offset<CH, true>(wave, lane, 1);
     // V^T operand via transpose reads: 16-lane group g16 covers d0 .. d0+15
     const int g16 = lane >> 4, L16 = lane & 15;
     const int tr_r = tr_token(L16), tr_a = tr_dquad(L16);
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
             }
             wg_barrier();  // both waves are done with the K tile
         }
-        if (more) load_tile<D, false>(k_tile, k + r0n * D, kvsize_n, wave, lane, koff);
+        if (more) load_tile<D, false>(k_tile, k + r0n * D, kvsize_n, wave, lane, koff0, koff1);
 
         if (cur) {
             // ---- online softmax; acc e of tile mt is token 32 mt + 8 (e/4) + 4 hh + e%4
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
             }
             wg_barrier();  // both waves are done with the V tile
         }
-        if (more) load_tile<D, true>(v_tile, v + r0n * D, kvsize_n, wave, lane, voff);
+        if (more) load_tile<D, true>(v_tile, v + r0n * D, kvsize_n, wave, lane, voff0, voff1);
 
         first = false;
         j = jn;
