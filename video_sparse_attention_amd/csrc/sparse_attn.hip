@@ -19,6 +19,8 @@
 //     (global_load_lds_dwordx4, no register staging) into row-major K and V
 //     tiles with XOR-swizzled 16-byte chunks; K operands come from
 //     ds_read_b128, the transposed V operands from ds_read_b64_tr_b16;
+//   * the block list is walked from a rotated start (see kSweep) so that
+//     concurrently running workgroups share KV blocks in L2;
 //   * software pipeline per KV block t: wait K_t, S = K_t Q^T, release the K
 //     tile and start loading K_{t+1}; softmax; wait V_t, O += V_t^T P^T,
 //     release the V tile and start loading V_{t+1} - so each load overlaps
@@ -40,6 +42,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kAttnThreads = 128;
+// Workgroups resident on one XCD at a time (32 CUs x 4 workgroups).  Query
+// block i starts its walk over its block list at entry (i mod kSweep) * n /
+// kSweep and wraps around, so the workgroups running together on an XCD read
+// nearby entries of their (ascending) lists at the same time and share them
+// in L2, instead of all starting at the front while earlier ones are deep
+// into theirs.  Only the order of the online-softmax updates changes.
+constexpr int kSweep = 128;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -207,10 +216,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     // vmcnt waits count.
     __builtin_amdgcn_s_waitcnt(0);
 
-    // next valid entry of the list at or after position t (-1: none)
+    // the walk visits list positions (t0 + t) mod n for t = 0 .. n-1
+    const int t0 = n > 0 ? ((i % kSweep) * n) / kSweep : 0;
+    // next valid entry at or after walk step t (-1: none)
     auto next_valid = [&](int& t) -> int {
         for (; t < n; ++t) {
-            const int j = list[t] - rebase;
+            int pos = t0 + t;
+            if (pos >= n) pos -= n;
+            const int j = list[pos] - rebase;
             if (j >= 0 && j < nkv) return j;
         }
         return -1;
