@@ -11,14 +11,14 @@
 //      sequence land in LDS (thread j reads Kc[j] once and serves R rows);
 //   3. one wave per row selects the top-k exactly: the row's order-preserving
 //      64-bit keys sit in registers (up to 64 per lane), the k-th largest is
-//      found bit by bit (64 rounds of a wave-wide ballot count), ties at the
+//      found bit by bit with wave-wide ballot counts (32 rounds on the high
+//      halves, 32 more on the low halves only when needed), ties at the
 //      threshold go to the lowest indices, and the indices are emitted in
 //      ascending order with ballot prefix counts;
 //   4. the same wave turns the row into softmax weights exp((s - max)/sqrt(D))
 //      and their sum, in float64;
 //   5. out_c[i][d] = sum_j w[i][j] Vc[j][d] / sum_j w[i][j], rounded once to
-//      float32; each thread loads a Vc value once and applies it to all R
-//      rows.
+//      float32; each thread owns 4 d of 2 rows.
 // Scores, softmax and the coarse product stay in float64 so that the
 // selected set matches a float64 reference on any input whose k-th and
 // (k+1)-th scores are not within a few ulps of each other.
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_topk_kernel(
     const double* __restrict__ vc, float* __restrict__ out_c, int* __restrict__ idx_out,
     int* __restrict__ num_out, int kv_cap, double scale) {
     extern __shared__ double lds[];
-    double* qrow = lds;              // [R][D]; reused for the final reduction
+    double* qrow = lds;              // [R][D]
     double* sc = lds + R * D;        // [R][kv_cap]
     __shared__ double lsum[R];
 
@@ -117,16 +117,42 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_topk_kernel(
             const int j = 64 * e + lane;
             key[e] = j < nkv ? order_key(row[j]) : 0ull;
         }
-        // largest T with #{key >= T} >= k, i.e. the k-th largest key
-        uint64_t T = 0;
-        for (int bit = 63; bit >= 0; --bit) {
-            const uint64_t cand = T | (1ull << bit);
+        // T = the k-th largest key.  First the k-th largest of the high 32 bits
+        // (Th) by bitwise bisection on 32-bit compares; the low 32 bits only
+        // need a second bisection when the candidates sharing Th are more than
+        // the number still to be chosen.
+        uint32_t Th = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = Th | (1u << bit);
             int cnt = 0;
 #pragma unroll
             for (int e = 0; e < KPL; ++e)
-                if (64 * e < nkv) cnt += __popcll(__ballot(key[e] >= cand));
-            if (cnt >= k) T = cand;
+                if (64 * e < nkv) cnt += __popcll(__ballot((uint32_t)(key[e] >> 32) >= cand));
+            if (cnt >= k) Th = cand;
         }
+        int gt_hi = 0, eq_hi = 0;
+#pragma unroll
+        for (int e = 0; e < KPL; ++e)
+            if (64 * e < nkv) {
+                const uint32_t hi = (uint32_t)(key[e] >> 32);
+                gt_hi += __popcll(__ballot(hi > Th));
+                eq_hi += __popcll(__ballot(hi == Th));
+            }
+        const int need_hi = k - gt_hi;  // >= 1 and <= eq_hi
+        uint32_t Tl = 0;
+        if (eq_hi != need_hi) {
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t cand = Tl | (1u << bit);
+                int cnt = 0;
+#pragma unroll
+                for (int e = 0; e < KPL; ++e)
+                    if (64 * e < nkv)
+                        cnt += __popcll(__ballot((uint32_t)(key[e] >> 32) == Th && (uint32_t)key[e] >= cand));
+                if (cnt >= need_hi) Tl = cand;
+            }
+        }
+        // (when every candidate is chosen, T = Th:0 selects all of them below)
+        const uint64_t T = ((uint64_t)Th << 32) | Tl;
         int n_gt = 0;
 #pragma unroll
         for (int e = 0; e < KPL; ++e)
@@ -162,34 +188,39 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_topk_kernel(
     }
     __syncthreads();
 
-    // 5. coarse output: thread (d, part) sums over every PARTS-th KV block for
-    // all rows at once, each Vc value loaded once; parts are added via LDS
-    constexpr int PARTS = kCoarseThreads / D;
-    const int d = tid % D;
-    const int part = tid / D;
-    double acc[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.0;
+    // 5. coarse output: thread (quad, pair) owns d = 4 quad .. +3 of rows
+    // 2 pair, 2 pair + 1 (and further pairs when R > 2 * groups): per KV block
+    // two 16-byte loads of Vc and two LDS reads of weights feed 8 FMAs.
+    constexpr int QUADS = D / 4;
+    constexpr int PAIRS = kCoarseThreads / QUADS;  // row pairs handled at once
+    const int quad = tid % QUADS;
+    const int pair = tid / QUADS;
+    for (int r0 = 2 * pair; r0 < nr; r0 += 2 * PAIRS) {
+        const bool two = r0 + 1 < nr;
+        const double* w0 = sc + r0 * kv_cap;
+        const double* w1 = sc + (two ? r0 + 1 : r0) * kv_cap;
+        double a0[4] = {0.0, 0.0, 0.0, 0.0}, a1[4] = {0.0, 0.0, 0.0, 0.0};
+        const double2* vcol = reinterpret_cast<const double2*>(vc + sv.kvblk_base * D + 4 * quad);
 #pragma unroll 4
-    for (int j = part; j < nkv; j += PARTS) {
-        const double vv = vc[(sv.kvblk_base + j) * D + d];
-#pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = fma(sc[r * kv_cap + j], vv, acc[r]);
+        for (int j = 0; j < nkv; ++j) {
+            const double2 x = vcol[j * (D / 2)];
+            const double2 y = vcol[j * (D / 2) + 1];
+            const double p0 = w0[j], p1 = w1[j];
+            a0[0] = fma(p0, x.x, a0[0]); a0[1] = fma(p0, x.y, a0[1]);
+            a0[2] = fma(p0, y.x, a0[2]); a0[3] = fma(p0, y.y, a0[3]);
+            a1[0] = fma(p1, x.x, a1[0]); a1[1] = fma(p1, x.y, a1[1]);
+            a1[2] = fma(p1, y.x, a1[2]); a1[3] = fma(p1, y.y, a1[3]);
+        }
+        float* o0 = out_c + (sv.qblk_base + i0 + r0) * D + 4 * quad;
+        const double l0 = lsum[r0];
+        *reinterpret_cast<float4*>(o0) =
+            make_float4((float)(a0[0] / l0), (float)(a0[1] / l0), (float)(a0[2] / l0), (float)(a0[3] / l0));
+        if (two) {
+            const double l1 = lsum[r0 + 1];
+            *reinterpret_cast<float4*>(o0 + D) =
+                make_float4((float)(a1[0] / l1), (float)(a1[1] / l1), (float)(a1[2] / l1), (float)(a1[3] / l1));
+        }
     }
-    for (int p = 1; p < PARTS; ++p) {
-        if (part == p)
-#pragma unroll
-            for (int r = 0; r < R; ++r) qrow[r * D + d] = acc[r];
-        __syncthreads();
-        if (part == 0)
-#pragma unroll
-            for (int r = 0; r < R; ++r) acc[r] += qrow[r * D + d];
-        __syncthreads();
-    }
-    if (part == 0)
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            if (r < nr) out_c[(sv.qblk_base + i0 + r) * D + d] = (float)(acc[r] / lsum[r]);
 }
 
 template <int D>

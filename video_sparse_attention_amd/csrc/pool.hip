@@ -2,19 +2,22 @@
 // block means; "[perf] avoid full-sequence materialization in VSA
 // coarse/sparse combine", Problem and Notes).
 //
-// One workgroup of 256 threads pools one 64-token block of one head of one
-// tensor.  Thread (g, c) reads the 16-byte chunk c (8 consecutive d) of
-// tokens g, g + G, ... and accumulates them in float64; the G partial sums of
-// each d are then added through LDS.  Sums of at most 64 bf16 values in
-// float64 are exact for any realistic data, so the result does not depend on
-// the order of the additions; the mean is an IEEE division by the block's
-// valid-token count.  HBM-bound: every input byte is read once.
+// HBM-bound streaming kernel.  Thread (block, c) owns the 16-byte chunk c
+// (8 consecutive d) of one 64-token block and walks the block's valid tokens
+// with independent 16-byte loads (8 in flight per thread), accumulating the
+// 8 sums in float64 registers: no LDS and no cross-thread reduction.  The
+// CH = D/8 threads of a block read each token row as one contiguous
+// 16*CH-byte segment, so every load instruction of a wave is fully
+// coalesced.  Sums of at most 64 bf16 values in float64 are exact for any
+// realistic data, so the result does not depend on the order of the
+// additions; the mean is an IEEE division by the block's valid-token count.
 #include "vsa_internal.hpp"
 
 namespace vsa {
 namespace {
 
 constexpr int kPoolThreads = 256;
+constexpr int kUnroll = 8;
 
 __device__ __forceinline__ double bf16_lo(uint32_t w) { return (double)__uint_as_float(w << 16); }
 __device__ __forceinline__ double bf16_hi(uint32_t w) { return (double)__uint_as_float(w & 0xffff0000u); }
@@ -26,18 +29,14 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(DevProblem P, const 
                                                             double* __restrict__ qc,
                                                             double* __restrict__ kc,
                                                             double* __restrict__ vc) {
-    constexpr int CH = D / 8;                // 16-byte chunks per row
-    constexpr int G = kPoolThreads / CH;     // token groups
-    constexpr int TPG = kBlock / G;          // tokens per group
-    __shared__ double part[G][D];
-
-    const int which = blockIdx.z % 3;  // 0 q, 1 k, 2 v
-    const int b = blockIdx.z / 3;      // batch item (dense) or 0 (packed)
+    constexpr int CH = D / 8;                  // threads per block
+    constexpr int BPG = kPoolThreads / CH;     // blocks per workgroup
+    const int which = blockIdx.z % 3;          // 0 q, 1 k, 2 v
+    const int b = blockIdx.z / 3;              // batch item (dense) or 0 (packed)
     const int h = blockIdx.y;
-    const int blk = blockIdx.x;
+    const int blk = blockIdx.x * BPG + threadIdx.x / CH;
+    const int c = threadIdx.x % CH;
 
-    const uint16_t* src;
-    double* dst;
     int64_t row0, out_row;
     int size;
     if (!P.packed) {
@@ -55,54 +54,44 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(DevProblem P, const 
         row0 = ((int64_t)h * nb + blk) * kBlock;
         out_row = (int64_t)h * nb + blk;
     }
-    src = which == 0 ? q : (which == 1 ? k : v);
-    dst = which == 0 ? qc : (which == 1 ? kc : vc);
+    const uint16_t* src = (which == 0 ? q : (which == 1 ? k : v)) + row0 * D + 8 * c;
+    double* dst = which == 0 ? qc : (which == 1 ? kc : vc);
 
-    const int c = threadIdx.x % CH;
-    const int g = threadIdx.x / CH;
     double acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-    uint4 w[TPG];
+    for (int t0 = 0; t0 < size; t0 += kUnroll) {
+        uint4 w[kUnroll];
 #pragma unroll
-    for (int r = 0; r < TPG; ++r) {
-        const int t = g + G * r;
-        if (t < size)
-            w[r] = *reinterpret_cast<const uint4*>(src + (row0 + t) * D + 8 * c);
-        else
-            w[r] = make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < kUnroll; ++u) {
+            const int t = t0 + u;
+            w[u] = t < size ? *reinterpret_cast<const uint4*>(src + (int64_t)t * D) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            acc[0] += bf16_lo(w[u].x); acc[1] += bf16_hi(w[u].x);
+            acc[2] += bf16_lo(w[u].y); acc[3] += bf16_hi(w[u].y);
+            acc[4] += bf16_lo(w[u].z); acc[5] += bf16_hi(w[u].z);
+            acc[6] += bf16_lo(w[u].w); acc[7] += bf16_hi(w[u].w);
+        }
     }
+    const double cnt = (double)size;
+    double2* o = reinterpret_cast<double2*>(dst + out_row * D + 8 * c);
 #pragma unroll
-    for (int r = 0; r < TPG; ++r) {
-        acc[0] += bf16_lo(w[r].x); acc[1] += bf16_hi(w[r].x);
-        acc[2] += bf16_lo(w[r].y); acc[3] += bf16_hi(w[r].y);
-        acc[4] += bf16_lo(w[r].z); acc[5] += bf16_hi(w[r].z);
-        acc[6] += bf16_lo(w[r].w); acc[7] += bf16_hi(w[r].w);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) part[g][8 * c + e] = acc[e];
-    __syncthreads();
-    for (int d = threadIdx.x; d < D; d += kPoolThreads) {
-        double s = 0.0;
-#pragma unroll
-        for (int gg = 0; gg < G; ++gg) s += part[gg][d];
-        dst[out_row * D + d] = s / (double)size;
-    }
+    for (int e = 0; e < 4; ++e) o[e] = make_double2(acc[2 * e] / cnt, acc[2 * e + 1] / cnt);
 }
 
 }  // namespace
 
 hipError_t launch_pool(const DevProblem& P, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        double* qc, double* kc, double* vc, hipStream_t st) {
-    dim3 grid, block(kPoolThreads);
-    if (!P.packed)
-        grid = dim3(max(P.nQ, P.nKV), P.H, 3 * P.nseq);
-    else
-        grid = dim3(max(P.total_q, P.total_kv), P.H, 3);
+    const int bpg = kPoolThreads / (P.D / 8);
+    const int nb = P.packed ? max(P.total_q, P.total_kv) : max(P.nQ, P.nKV);
+    const dim3 grid((nb + bpg - 1) / bpg, P.H, P.packed ? 3 : 3 * P.nseq);
     if (P.D == 128)
-        hipLaunchKernelGGL(pool_kernel<128>, grid, block, 0, st, P, q, k, v, qc, kc, vc);
+        hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(kPoolThreads), 0, st, P, q, k, v, qc, kc, vc);
     else
-        hipLaunchKernelGGL(pool_kernel<64>, grid, block, 0, st, P, q, k, v, qc, kc, vc);
+        hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(kPoolThreads), 0, st, P, q, k, v, qc, kc, vc);
     return hipGetLastError();
 }
 
