@@ -122,7 +122,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the forward "
-              "is not sharded across GPUs in this build.", file=sys.stderr)
+              "is not sharded across GPUs.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
