@@ -64,6 +64,22 @@ __device__ __forceinline__ uint32_t bf16pair(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// max / sum of x over lanes l and l ^ 32 (v_permlane32_swap: the two halves
+// of the wave trade places, so the pair of results holds both halves)
+__device__ __forceinline__ float max_with_lane_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_lane_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// acc + the two bf16 values packed in w (one v_dot2 against (1, 1))
+__device__ __forceinline__ float sum_bf16_pair(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3F803F80u), acc,
+                                           false);
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight
 // (loads complete in issue order).
 template <int N>
@@ -111,21 +127,39 @@ __device__ __forceinline__ void dma_16B(const void* sbase, uint32_t voff, uint32
         : "memory");
 }
 
+// Two direct copies sharing one M0: the immediate offset of the second
+// (2048) is added to both its global and its LDS address, so with voff_b =
+// (wanted source offset) - 2048 it lands 2048 bytes after the first.
+__device__ __forceinline__ void dma_16B_pair(const void* sbase, uint32_t voff_a, uint32_t voff_b,
+                                             uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %4\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %3\n\t"
+        "global_load_lds_dwordx4 %2, %3 offset:2048\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff_a), "v"(voff_b), "s"(sbase), "s"(lds_base)
+        : "memory");
+}
+
 // Copy one 64-row KV block starting at `block` into a swizzled tile.  Full
-// blocks: a lane's source offset is lane_off[n & 1] + 2048 n.  Partial blocks
-// (valid < 64): rows past valid - 1 repeat that row, so every address stays
-// inside the tensor and every LDS value is finite.
+// blocks: instructions 2m and 2m + 1 of a lane fetch lane_off0 + 4096 m and
+// lane_off1 + 4096 m (passed as lane_off1_m2k = lane_off1 - 2048, see
+// dma_16B_pair) into LDS bytes lds0 + 4096 m and lds0 + 4096 m + 2048.
+// Partial blocks (valid < 64): rows past valid - 1 repeat that row, so every
+// address stays inside the tensor and every LDS value is finite.
 template <int D, bool IS_V>
-__device__ __forceinline__ void load_tile(uint16_t* tile, const uint16_t* block, int valid, int wave,
-                                          int lane, uint32_t lane_off0, uint32_t lane_off1) {
+__device__ __forceinline__ void load_tile(uint32_t lds0, const uint16_t* block, int valid, int wave,
+                                          int lane, uint32_t lane_off0, uint32_t lane_off1_m2k) {
     constexpr int CH = D / 8;
-    const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)tile) + 1024u * wave;
     const char* base = (const char*)uniform_ptr(block);
     if (valid == kBlock) {
 #pragma unroll
-        for (int n = 0; n < CH / 2; ++n)
-            dma_16B(base + 4096 * (n >> 1), (n & 1) ? lane_off1 : lane_off0,
-                    __builtin_amdgcn_readfirstlane(lds0 + 2048u * n));
+        for (int m = 0; m < CH / 4; ++m)
+            dma_16B_pair(base + 4096 * m, lane_off0, lane_off1_m2k, lds0 + 4096u * m);
     } else {
 #pragma unroll
         for (int n = 0; n < CH / 2; ++n) {
@@ -134,7 +168,7 @@ __device__ __forceinline__ void load_tile(uint16_t* tile, const uint16_t* block,
             const int sw = IS_V ? v_swz<CH>(row) : k_swz<CH>(row);
             const int c = (p % CH) ^ sw;
             const int r = min(row, valid - 1);
-            dma_16B(base, (uint32_t)(r * CH * 16 + 16 * c), __builtin_amdgcn_readfirstlane(lds0 + 2048u * n));
+            dma_16B(base, (uint32_t)(r * CH * 16 + 16 * c), lds0 + 2048u * n);
         }
     }
 }
@@ -218,12 +252,24 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
 
     // the walk visits list positions (t0 + t) mod n for t = 0 .. n-1
     const int t0 = n > 0 ? ((i % kSweep) * n) / kSweep : 0;
+    auto entry = [&](int t) -> int {
+        int pos = t0 + t;
+        if (pos >= n) pos -= n;
+        return list[pos];
+    };
+    // The entry of walk step pre_t is loaded one step ahead, so the scalar
+    // load's latency is hidden behind a whole block of work.
+    int pre_t = 0;
+    int pre = n > 0 ? entry(0) : 0;
     // next valid entry at or after walk step t (-1: none)
     auto next_valid = [&](int& t) -> int {
         for (; t < n; ++t) {
-            int pos = t0 + t;
-            if (pos >= n) pos -= n;
-            const int j = list[pos] - rebase;
+            const int raw = t == pre_t ? pre : entry(t);
+            if (t + 1 < n) {
+                pre = entry(t + 1);
+                pre_t = t + 1;
+            }
+            const int j = raw - rebase;
             if (j >= 0 && j < nkv) return j;
         }
         return -1;
@@ -235,9 +281,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
 
     // per-lane positions inside the tiles
     const uint32_t koff0 = (uint32_t)lane_src_offset<CH, false>(wave, lane, 0);
-    const uint32_t koff1 = (uint32_t)lane_src_offset<CH, false>(wave, lane, 1);
+    const uint32_t koff1 = (uint32_t)lane_src_offset<CH, false>(wave, lane, 1) - 2048u;
     const uint32_t voff0 = (uint32_t)lane_src_offset<CH, true>(wave, lane, 0);
-    const uint32_t voff1 = (uint32_t)lane_src_offset<CH, true>(wave, lane, 1);
+    const uint32_t voff1 = (uint32_t)lane_src_offset<CH, true>(wave, lane, 1) - 2048u;
+    // this wave's LDS byte base inside each tile
+    const uint32_t k_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)k_tile + 1024u * wave);
+    const uint32_t v_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)v_tile + 1024u * wave);
     // V^T operand via transpose reads: 16-lane group g16 covers d0 .. d0+15
     const int g16 = lane >> 4, L16 = lane & 15;
     const int tr_r = tr_token(L16), tr_a = tr_dquad(L16);
@@ -261,20 +310,23 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
             wait_vmcnt<LOADS>();  // this wave's part of K_t is in LDS (V_t may be in flight)
             wg_barrier();         // ... and the other wave's part
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
-                const int row = 32 * mt + l32;
+            // the two 32-token tiles alternate so that each MFMA has a whole
+            // MFMA of time for its K operand read
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    const int row = 32 * mt + l32;
                     const uint4 a = *reinterpret_cast<const uint4*>(
                         k_tile + tile_off<CH>(row, 2 * ks + hh, k_swz<CH>(row)));
                     sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[ks], sacc[mt], 0, 0, 0);
                 }
-            }
             wg_barrier();  // both waves are done with the K tile
         }
-        if (more) load_tile<D, false>(k_tile, k + r0n * D, kvsize_n, wave, lane, koff0, koff1);
+        if (more) load_tile<D, false>(k_lds, k + r0n * D, kvsize_n, wave, lane, koff0, koff1);
 
         if (cur) {
             // ---- online softmax; acc e of tile mt is token 32 mt + 8 (e/4) + 4 hh + e%4
@@ -292,7 +344,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) bm = fmaxf(bm, sacc[mt][e]);
-            bm = fmaxf(bm, __shfl_xor(bm, 32));
+            bm = max_with_lane_xor32(bm);
             if (__ballot(bm > m + lazy_raw)) {  // some query's max moved: rescale
                 const float m_new = fmaxf(m, bm);
                 const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c_log2);
@@ -304,30 +356,29 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
                     for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
             }
             const float mc = m * c_log2;
-            float ps = 0.f;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][e], c_log2, -mc));
-                    sacc[mt][e] = p;
-                    ps += p;
-                }
-            l += ps;
+                for (int e = 0; e < 16; ++e) sacc[mt][e] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][e], c_log2, -mc));
+            // bf16 probabilities, the B operand of O^T += V^T P^T; the row sum
+            // is taken over these rounded values (two per dot2 instruction)
+            uint32_t pw[4][4];
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    pw[s4][w] = bf16pair(sacc[s4 >> 1][8 * (s4 & 1) + 2 * w], sacc[s4 >> 1][8 * (s4 & 1) + 2 * w + 1]);
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) l = sum_bf16_pair(pw[s4][w], l);
 
             // ---- O^T += V^T P^T over 4 k-steps of 16 tokens -----------------
             if (more) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();  // V_t landed (K_{t+1} may be in flight)
             wg_barrier();
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) {
-                const f32x16& sa = sacc[s4 >> 1];
-                const int base = 8 * (s4 & 1);
-                uint4 pw;
-                pw.x = bf16pair(sa[base + 0], sa[base + 1]);
-                pw.y = bf16pair(sa[base + 2], sa[base + 3]);
-                pw.z = bf16pair(sa[base + 4], sa[base + 5]);
-                pw.w = bf16pair(sa[base + 6], sa[base + 7]);
-                const bf16x8 pb = as_bf16x8(pw);
+                const bf16x8 pb = as_bf16x8(make_uint4(pw[s4][0], pw[s4][1], pw[s4][2], pw[s4][3]));
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
                     const int d = 32 * dt + tr_d;
@@ -347,7 +398,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
             }
             wg_barrier();  // both waves are done with the V tile
         }
-        if (more) load_tile<D, true>(v_tile, v + r0n * D, kvsize_n, wave, lane, voff0, voff1);
+        if (more) load_tile<D, true>(v_lds, v + r0n * D, kvsize_n, wave, lane, voff0, voff1);
 
         first = false;
         j = jn;
@@ -360,7 +411,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     }
 
     // ---- normalise and store: lane holds O[qr][32 dt + 8 j + 4 hh + 0..3] ----
-    const float lt = l + __shfl_xor(l, 32);
+    const float lt = sum_with_lane_xor32(l);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (qr < qsize) {
         uint16_t* orow = out + (qrow0 + qr) * D;
