@@ -313,17 +313,30 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
-            // the two 32-token tiles alternate so that each MFMA has a whole
-            // MFMA of time for its K operand read
+            // K operands are read two k-steps ahead of their MFMAs (the two
+            // 32-token tiles alternate), so each read has four MFMAs of time
+            auto k_read = [&](int mt, int ks) -> uint4 {
+                const int row = 32 * mt + l32;
+                return *reinterpret_cast<const uint4*>(k_tile + tile_off<CH>(row, 2 * ks + hh, k_swz<CH>(row)));
+            };
+            uint4 ka[3][2];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    const int row = 32 * mt + l32;
-                    const uint4 a = *reinterpret_cast<const uint4*>(
-                        k_tile + tile_off<CH>(row, 2 * ks + hh, k_swz<CH>(row)));
-                    sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qf[ks], sacc[mt], 0, 0, 0);
+                for (int mt = 0; mt < 2; ++mt) ka[ks][mt] = k_read(mt, ks);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + 2 < KS) {
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) ka[(ks + 2) % 3][mt] = k_read(mt, ks + 2);
                 }
+                // keep the scheduler from sinking the reads next to their use
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+                    sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[ks % 3][mt]), qf[ks], sacc[mt], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             wg_barrier();  // both waves are done with the K tile
         }
         if (more) load_tile<D, false>(k_lds, k + r0n * D, kvsize_n, wave, lane, koff0, koff1);
