@@ -3,10 +3,13 @@
 
 One step is one pass of the whole forward over the large video-DiT workload
 (B=1, H=56, D=128, S=15488 = 242 blocks of 64, top-49, gated): pool + coarse
-attention + top-k routing, block-sparse attention, in-place combine, issued
-through the C ABI stage entry points exactly as vsa_forward issues them, on
-PyTorch's current HIP stream with inputs resident in HBM.  HIP events between
-the stages give each kernel's average duration over the timed steps.
+attention + top-k routing, then block-sparse attention with the combine fused
+into its epilogue, issued through the C ABI stage entry points exactly as
+vsa_forward issues them, on PyTorch's current HIP stream with inputs resident
+in HBM.  HIP events between the stages give each kernel's average duration
+over the timed steps.  Outside the timed steps the stand-alone combine kernel
+is timed with L2 and MALL flushed (its HBM rate) and the sparse kernel
+without the fused combine is timed for comparison.
 
 Prints one JSON line.  ``value`` is effective TFLOP/s of the whole step with
 the pages' benchmark convention 4*B*H*nQ*k*64*64*D (padded blocks counted as
@@ -175,16 +178,14 @@ def main():
         if ev: ev[0].record()
         vsa.vsa_coarse_topk(prob, q, k, v, out_c, idx, num, ws)
         if ev: ev[1].record()
-        vsa.vsa_sparse_attn_from_indices(prob, q, k, v, idx, num, out)
+        vsa.vsa_sparse_attn_combine(prob, q, k, v, idx, num, out_c, gate, out)
         if ev: ev[2].record()
-        vsa.vsa_combine(prob, out_c, gate, out)
-        if ev: ev[3].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -192,13 +193,36 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    st = {"coarse": 0.0, "sparse": 0.0, "combine": 0.0}
+    st = {"coarse": 0.0, "sparse": 0.0}
     for e in evs:
         st["coarse"] += e[0].elapsed_time(e[1])
         st["sparse"] += e[1].elapsed_time(e[2])
-        st["combine"] += e[2].elapsed_time(e[3])
     avg = {key: val / args.steps for key, val in st.items()}  # ms
     ms_per_step = wall * 1e3 / args.steps
+
+    # Outside the timed steps: the stand-alone combine kernel (the pages'
+    # separate combine) with L2 and MALL flushed before each launch by
+    # writing a 1 GiB buffer, and the sparse kernel without the fused combine.
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    comb_ms, unf_ms = [], []
+    for _ in range(5):
+        flush.fill_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        vsa.vsa_combine(prob, out_c, gate, out)
+        e1.record()
+        torch.cuda.synchronize()
+        comb_ms.append(e0.elapsed_time(e1))
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        vsa.vsa_sparse_attn_from_indices(prob, q, k, v, idx, num, out)
+        e1.record()
+        torch.cuda.synchronize()
+        unf_ms.append(e0.elapsed_time(e1))
+    del flush
+    comb = sorted(comb_ms)[len(comb_ms) // 2]
+    unf = sorted(unf_ms)[len(unf_ms) // 2]
 
     # algorithmic bytes: the combine reads and writes out once, reads the gate and out_c
     gate_bytes = 0 if gate is None else 2 * q_tokens
@@ -207,6 +231,7 @@ def main():
     coarse_bytes = 2 * (q.numel() + 2 * k.numel()) + 8 * D * (n_qblocks + 2 * (kv_tokens // 64))
     sparse_tf = flops / (avg["sparse"] * 1e-3) / 1e12
     traffic = measured_traffic(None)
+    kname = "sparse_attn_kernel<128, 1>" if gate is not None else "sparse_attn_kernel<128, 0>"
 
     res = {
         "metric": METRIC,
@@ -224,7 +249,7 @@ def main():
         "config": cfg,
         "roofline": {
             "bound": "mfma",
-            "kernel": "sparse_attn_kernel<128>",
+            "kernel": kname + " (block-sparse attention with the combine fused)",
             "achieved": round(sparse_tf, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
@@ -236,11 +261,12 @@ def main():
         "kernels": {
             "coarse_topk_stage_ms": round(avg["coarse"], 4),
             "coarse_topk_stage_GBps": round(coarse_bytes / (avg["coarse"] * 1e-3) / 1e9, 1),
-            "sparse_attn_ms": round(avg["sparse"], 4),
-            "sparse_attn_TFLOPs": round(sparse_tf, 2),
-            "combine_ms": round(avg["combine"], 4),
-            "combine_GBps": round(comb_bytes / (avg["combine"] * 1e-3) / 1e9, 1),
-            "combine_frac_hbm": round(comb_bytes / (avg["combine"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "sparse_attn_combine_ms": round(avg["sparse"], 4),
+            "sparse_attn_combine_TFLOPs": round(sparse_tf, 2),
+            "sparse_attn_unfused_ms": round(unf, 4),
+            "combine_standalone_cold_ms": round(comb, 4),
+            "combine_standalone_GBps": round(comb_bytes / (comb * 1e-3) / 1e9, 1),
+            "combine_standalone_frac_hbm": round(comb_bytes / (comb * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "combine_bytes": comb_bytes,
         },
         "cpu_baseline": None,

@@ -217,8 +217,28 @@ int vsa_combine(const vsa_problem *problem, const float *out_c, const vsa_bf16 *
                 vsa_stream stream);
 
 /*
+ * vsa_sparse_attn_combine - steps 4 and 5 in one kernel: the block-sparse
+ * attention of vsa_sparse_attn_from_indices whose epilogue adds the block's
+ * coarse row, out = bf16(fma(out_c, gate, O)) (bf16(out_c + O) for
+ * VSA_GATE_NONE), with O the float32 normalised attention output, so the
+ * sparse output is rounded once instead of twice and is never written to
+ * memory on its own.  ("[perf] avoid full-sequence materialization in VSA
+ * coarse/sparse combine", Change, and the review thread: the fused combine of
+ * another backend, which moves gated values towards the float32 result.)
+ *
+ * Arguments as for vsa_sparse_attn_from_indices plus out_c, gate,
+ * gate_mode and gate_strides as for vsa_combine (same checks and errors).
+ * Padding slots of PACKED out are written with 0.  out must not overlap q,
+ * k, v or gate.
+ */
+int vsa_sparse_attn_combine(const vsa_problem *problem, const vsa_bf16 *q, const vsa_bf16 *k,
+                            const vsa_bf16 *v, const int32_t *q2k_idx, const int32_t *q2k_num,
+                            const float *out_c, const vsa_bf16 *gate, int32_t gate_mode,
+                            const int64_t *gate_strides, vsa_bf16 *out, vsa_stream stream);
+
+/*
  * vsa_forward - the whole DENSE forward: vsa_coarse_topk, then
- * vsa_sparse_attn_from_indices into out, then vsa_combine in place.
+ * vsa_sparse_attn_combine into out.
  * ("FastVideo Kernel" README, Usage: video_sparse_attn(q, k, v, block_sizes,
  * block_sizes, topk); "[perf] avoid full-sequence materialization ...",
  * Problem.)

@@ -43,9 +43,11 @@ def run_dense_stages(inp, dev=DEV, idx_override=None):
     vsa.vsa_sparse_attn_from_indices(prob, q, k, v, sidx, snum, out)
     out_s = out.clone()
     vsa.vsa_combine(prob, out_c, gate, out)
+    out_f = torch.empty_like(q)
+    vsa.vsa_sparse_attn_combine(prob, q, k, v, sidx, snum, out_c, gate, out_f)
     torch.cuda.synchronize()
     return dict(out=out.cpu(), out_s=out_s.cpu(), out_c=out_c.cpu(), q2k_idx=idx.cpu(),
-                q2k_num=num.cpu())
+                q2k_num=num.cpu(), out_fused=out_f.cpu())
 
 
 def run_varlen_stages(inp, dev=DEV, idx_override=None):
@@ -69,9 +71,11 @@ def run_varlen_stages(inp, dev=DEV, idx_override=None):
     vsa.vsa_sparse_attn_from_indices(prob, q, k, v, sidx, snum, out)
     out_s = out.clone()
     vsa.vsa_combine(prob, out_c, gate, out)
+    out_f = torch.full_like(q, float("nan"))
+    vsa.vsa_sparse_attn_combine(prob, q, k, v, sidx, snum, out_c, gate, out_f)
     torch.cuda.synchronize()
     return dict(out=out.cpu(), out_s=out_s.cpu(), out_c=out_c.cpu(), q2k_idx=idx.cpu(),
-                q2k_num=num.cpu(), meta=meta)
+                q2k_num=num.cpu(), meta=meta, out_fused=out_f.cpu())
 
 
 def oracle_dense(inp, blocks=None):

@@ -43,6 +43,16 @@ def check_sparse(gpu: np.ndarray, ref: np.ndarray, what: str = "out_s"):
     return rel
 
 
+def check_fused(fused: np.ndarray, unfused: np.ndarray, out_s: np.ndarray, what: str = "fused"):
+    """The fused combine rounds once (bf16(fma(out_c, g, O))) where the stage
+    sequence rounds O to bf16 first: they may differ by the rounding of O
+    (half a bf16 ulp, 2^-9 |O|) plus one rounding of the result each."""
+    bound = 2.0 ** -8 * (np.abs(out_s) + np.abs(fused) + np.abs(unfused))
+    m = np.isfinite(unfused)
+    bad = np.abs(fused[m] - unfused[m]) > bound[m]
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond the double-rounding bound"
+
+
 def check_out_c(gpu: np.ndarray, ref: np.ndarray):
     bad = ~np.isclose(gpu, ref, rtol=OUT_C_RTOL, atol=OUT_C_ATOL)
     assert not bad.any(), f"out_c: {int(bad.sum())} elements off, worst rel " \

@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("vsa_build_metadata", "vsa_workspace_size", "vsa_forward", "vsa_forward_varlen",
-              "vsa_coarse_topk", "vsa_sparse_attn_from_indices", "vsa_combine",
+              "vsa_coarse_topk", "vsa_sparse_attn_from_indices", "vsa_sparse_attn_combine", "vsa_combine",
               "vsa_status_string", "vsa_last_error"):
         assert n in names
 
@@ -172,6 +172,10 @@ def comb(lib, p, oc=C_, gate=G_, mode=1, st=None, out=O_):
     return lib.vsa_combine(ctypes.byref(p), oc, gate, mode, st, out, None)
 
 
+def fused(lib, p, q=A, k=B_, v=C_, idx=G_, num=G_, oc=W_, gate=G_, mode=1, st=None, out=O_):
+    return lib.vsa_sparse_attn_combine(ctypes.byref(p), q, k, v, idx, num, oc, gate, mode, st, out, None)
+
+
 def fwd(lib, q=A, k=B_, v=C_, gate=None, mode=0, st=None, out=O_, B=1, H=2, Sq=1000, Skv=1000,
         D=128, bs=64, topk=3, ws=W_, wsb=1 << 40):
     return lib.vsa_forward(q, k, v, gate, mode, st, out, None, None, None, B, H, Sq, Skv, D, bs,
@@ -213,7 +217,16 @@ E = _abi
     (lambda L: comb(L, dense(), gate=ctypes.c_void_p(FAKE + (5 << 32) + 1)), E.VSA_ERR_ALIGN),
     (lambda L: comb(L, dense(), gate=ctypes.c_void_p(FAKE + (3 << 32) + 64)), E.VSA_ERR_ALIAS),
     (lambda L: comb(L, dense(), oc=None), E.VSA_ERR_NULL),
+    (lambda L: fused(L, dense(), oc=None), E.VSA_ERR_NULL),
+    (lambda L: fused(L, dense(), idx=None), E.VSA_ERR_NULL),
+    (lambda L: fused(L, dense(), mode=5), E.VSA_ERR_GATE),
+    (lambda L: fused(L, dense(), gate=None), E.VSA_ERR_NULL),
+    (lambda L: fused(L, dense(), out=B_), E.VSA_ERR_ALIAS),
+    (lambda L: fused(L, dense(), gate=ctypes.c_void_p(FAKE + (3 << 32) + 64)), E.VSA_ERR_ALIAS),
+    (lambda L: fused(L, dense(), oc=ctypes.c_void_p(FAKE + (4 << 32) + 4)), E.VSA_ERR_ALIGN),
+    (lambda L: fused(L, dense(), mode=2, st=(ctypes.c_int64 * 3)(8, 8, 12)), E.VSA_ERR_ALIGN),
     (lambda L: fwd(L, out=A), E.VSA_ERR_ALIAS),
+    (lambda L: fwd(L, mode=1, gate=ctypes.c_void_p(FAKE + (3 << 32) + 64)), E.VSA_ERR_ALIAS),
     (lambda L: fwd(L, wsb=10), E.VSA_ERR_WORKSPACE),
     (lambda L: fwd(L, mode=1, gate=None), E.VSA_ERR_NULL),
     (lambda L: fwd(L, B=0), E.VSA_ERR_SHAPE),

@@ -30,6 +30,8 @@ def test_large_video_dit_shape():
     N.check_out_c(N.f64(gpu["out_c"]), ref["out_c"])
     rel = N.check_sparse(N.f64(gpu["out_s"]), ref["out_s"])
     mx, mean = N.check_out(N.f64(gpu["out"]), ref["out"])
+    N.check_out(N.f64(gpu["out_fused"]), ref["out"], "out (fused combine)")
+    N.check_fused(N.f64(gpu["out_fused"]), N.f64(gpu["out"]), N.f64(gpu["out_s"]))
     G.note(f"  out max-abs {mx:.2e} mean-abs {mean:.2e}; sparse rel-rms {rel:.2e}")
 
 
@@ -48,6 +50,8 @@ def test_varlen_many_sequences():
     N.check_out_c(N.f64(gpu["out_c"]), ref["out_c"])
     N.check_sparse(N.f64(gpu["out_s"]), ref["out_s"])
     mx, mean = N.check_out(N.f64(gpu["out"]), ref["out"])
+    N.check_out(N.f64(gpu["out_fused"]), ref["out"], "out (fused combine)")
+    N.check_fused(N.f64(gpu["out_fused"]), N.f64(gpu["out"]), N.f64(gpu["out_s"]))
     G.note(f"  out max-abs {mx:.2e} mean-abs {mean:.2e}")
 
 

@@ -23,7 +23,10 @@ def _full_check_dense(inp, gpu=None, tag=""):
     N.check_out_c(N.f64(gpu["out_c"]), ref["out_c"])
     rel = N.check_sparse(N.f64(gpu["out_s"]), ref["out_s"])
     mx, mean = N.check_out(N.f64(gpu["out"]), ref["out"])
-    G.note(f"  out max-abs {mx:.2e} mean-abs {mean:.2e}; sparse rel-rms {rel:.2e}")
+    fmx, fmean = N.check_out(N.f64(gpu["out_fused"]), ref["out"], "out (fused combine)")
+    N.check_fused(N.f64(gpu["out_fused"]), N.f64(gpu["out"]), N.f64(gpu["out_s"]))
+    G.note(f"  out max-abs {mx:.2e} mean-abs {mean:.2e} (fused {fmx:.2e} / {fmean:.2e}); "
+           f"sparse rel-rms {rel:.2e}")
     return gpu, ref
 
 
@@ -39,14 +42,20 @@ def test_dense_equivalence():
     assert (gpu["q2k_idx"].numpy() == np.arange(nkv)).all()
 
 
-def test_forward_equals_stage_sequence():
-    """vsa_forward launches exactly the stage kernels: identical bits."""
-    inp = synth.workload("dense_equiv")
+@pytest.mark.parametrize("name", ["dense_equiv", "tiny", "gated"])
+def test_forward_equals_stage_sequence(name):
+    """vsa_forward launches exactly the stage kernels (coarse/top-k, then the
+    sparse attention with the fused combine): identical bits."""
+    if name == "gated":
+        inp = synth.dense_inputs(2, 3, 64 * 5 + 17, 128, 2, seed=43, gated=True)
+    else:
+        inp = synth.workload(name)
     gpu = G.run_dense_stages(inp)
     q, k, v = (t.to(G.DEV) for t in (inp.q, inp.k, inp.v))
-    out, oc, idx, num = vsa.vsa_forward(q, k, v, inp.topk, None, return_aux=True)
+    g = None if inp.gate is None else inp.gate.to(G.DEV)
+    out, oc, idx, num = vsa.vsa_forward(q, k, v, inp.topk, g, return_aux=True)
     torch.cuda.synchronize()
-    assert torch.equal(out.cpu(), gpu["out"])
+    assert torch.equal(out.cpu(), gpu["out_fused"])
     assert torch.equal(oc.cpu(), gpu["out_c"])
     assert torch.equal(idx.cpu(), gpu["q2k_idx"])
     assert torch.equal(num.cpu(), gpu["q2k_num"])
@@ -156,13 +165,16 @@ def test_varlen_small():
     N.check_out_c(N.f64(gpu["out_c"]), ref["out_c"])
     N.check_sparse(N.f64(gpu["out_s"]), ref["out_s"])
     N.check_out(N.f64(gpu["out"]), ref["out"])
+    N.check_out(N.f64(gpu["out_fused"]), ref["out"], "out (fused combine)")
+    N.check_fused(N.f64(gpu["out_fused"]), N.f64(gpu["out"]), N.f64(gpu["out_s"]))
     # padding slots hold 0
-    out = gpu["out"].float().numpy()
-    o = 0
-    for sq in inp.seqlens_q:
-        nb = -(-sq // 64)
-        assert (out[:, o + sq:o + 64 * nb] == 0).all()
-        o += 64 * nb
+    for key in ("out", "out_fused"):
+        out = gpu[key].float().numpy()
+        o = 0
+        for sq in inp.seqlens_q:
+            nb = -(-sq // 64)
+            assert (out[:, o + sq:o + 64 * nb] == 0).all(), key
+            o += 64 * nb
 
 
 @pytest.mark.parametrize("gated", [False, True])
@@ -182,6 +194,7 @@ def test_varlen_packed_equals_per_sequence(gated):
         nq, nkv = -(-lens_q[s] // 64), -(-lens_kv[s] // 64)
         kk = min(topk[s], nkv)
         assert torch.equal(packed["out"][:, oq:oq + lens_q[s]], one["out"][0]), s
+        assert torch.equal(packed["out_fused"][:, oq:oq + lens_q[s]], one["out_fused"][0]), s
         assert torch.equal(packed["out_c"][:, bq:bq + nq], one["out_c"][0]), s
         pi = packed["q2k_idx"][:, bq:bq + nq]
         assert torch.equal(pi[..., :kk], one["q2k_idx"][0] + bkv), s
@@ -201,6 +214,7 @@ def test_single_sequence_varlen_equals_dense():
                              pad(inp.gate[0], ()), [S], [S], [3])
     var = G.run_varlen_stages(vin)
     assert torch.equal(var["out"][:, :S], dense["out"][0])
+    assert torch.equal(var["out_fused"][:, :S], dense["out_fused"][0])
     assert torch.equal(var["q2k_idx"], dense["q2k_idx"][0])
 
 

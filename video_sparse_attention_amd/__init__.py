@@ -19,6 +19,7 @@ from .binding import (  # noqa: E402,F401
     vsa_combine,
     vsa_forward,
     vsa_forward_varlen,
+    vsa_sparse_attn_combine,
     vsa_sparse_attn_from_indices,
     vsa_workspace_size,
 )
@@ -26,5 +27,5 @@ from .binding import (  # noqa: E402,F401
 __all__ = [
     "BLOCK", "VarlenMeta", "VsaError", "alloc_workspace", "block_shapes", "dense_problem",
     "token_shapes", "vsa_build_metadata", "vsa_coarse_topk", "vsa_combine", "vsa_forward",
-    "vsa_forward_varlen", "vsa_sparse_attn_from_indices", "vsa_workspace_size",
+    "vsa_forward_varlen", "vsa_sparse_attn_combine", "vsa_sparse_attn_from_indices", "vsa_workspace_size",
 ]

@@ -205,6 +205,26 @@ def vsa_sparse_attn_from_indices(problem: VsaProblem, q, k, v, q2k_idx, q2k_num,
         _stream(q.device)), "vsa_sparse_attn_from_indices")
 
 
+def vsa_sparse_attn_combine(problem: VsaProblem, q, k, v, q2k_idx, q2k_num, out_c, gate, out) -> None:
+    """Block-sparse attention with the combine fused into its epilogue:
+    ``out = out_c[block] * gate + attention`` (``+`` without a gate), one
+    rounding to bf16."""
+    _check_qkv(problem, q, k, v)
+    cs, isz, ns = block_shapes(problem)
+    if tuple(q2k_idx.shape[:-1]) != tuple(isz[:-1]):
+        raise ValueError(f"q2k_idx has shape {tuple(q2k_idx.shape)}, expected {isz[:-1]} + (k,)")
+    if problem.layout == VSA_LAYOUT_DENSE and q2k_idx.shape[-1] != isz[-1]:
+        raise ValueError(f"q2k_idx rows must hold min(topk, nKV) = {isz[-1]} entries")
+    _need(q2k_idx, "q2k_idx", torch.int32)
+    _need(q2k_num, "q2k_num", torch.int32, ns)
+    _need(out_c, "out_c", torch.float32, cs)
+    _need(out, "out", torch.bfloat16, token_shapes(problem)[0])
+    mode, st = _gate_args(gate, *_gate_shapes(problem))
+    _abi.check(_abi.load().vsa_sparse_attn_combine(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(q2k_idx), _ptr(q2k_num), _ptr(out_c),
+        _ptr(gate), mode, st, _ptr(out), _stream(q.device)), "vsa_sparse_attn_combine")
+
+
 def _gate_shapes(problem):
     qs = token_shapes(problem)[0]
     return qs[:-1], qs

@@ -173,11 +173,23 @@ __device__ __forceinline__ void load_tile(uint32_t lds0, const uint16_t* block, 
     }
 }
 
-template <int D>
+// Epilogue of the kernel: write the sparse output itself, or fuse the
+// combine with the block's coarse row (no gate, a per-token gate, or a full
+// [.., D] gate).
+enum CombineMode { kSparseOnly = -1, kAddCoarse = 0, kTokenGate = 1, kFullGate = 2 };
+
+// Where the combine's inputs live (unused for kSparseOnly).
+struct CombineArgs {
+    const float* out_c;     // block-resolution coarse output
+    const uint16_t* gate;   // bf16 gate
+    int64_t gs0, gs1, gs2;  // gate element strides: batch, head, token
+};
+
+template <int D, int CMODE>
 __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     DevProblem P, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int* __restrict__ idx, const int* __restrict__ num,
-    uint16_t* __restrict__ out, float c_log2) {
+    uint16_t* __restrict__ out, float c_log2, CombineArgs C) {
     constexpr int KS = D / 16;      // MFMA k-steps over d for S^T
     constexpr int DT = D / 32;      // 32-row d tiles of O^T
     constexpr int CH = D / 8;       // 16-byte chunks per token row
@@ -426,7 +438,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     // ---- normalise and store: lane holds O[qr][32 dt + 8 j + 4 hh + 0..3] ----
     const float lt = sum_with_lane_xor32(l);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (qr < qsize) {
+    if (qr < qsize && CMODE == kSparseOnly) {
         uint16_t* orow = out + (qrow0 + qr) * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -436,6 +448,42 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
                 w2.x = bf16pair(o[dt][4 * jj + 0] * inv, o[dt][4 * jj + 1] * inv);
                 w2.y = bf16pair(o[dt][4 * jj + 2] * inv, o[dt][4 * jj + 3] * inv);
                 *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * jj + 4 * hh) = w2;
+            }
+    } else if (qr < qsize) {
+        // fused combine: out = out_c[block] * gate + O / l in float32 (FMA),
+        // one rounding to bf16
+        uint16_t* orow = out + (qrow0 + qr) * D;
+        const float* ocr = C.out_c + qb * D;
+        // token index of this row along the gate's token axis
+        const int64_t tok = (int64_t)kBlock * (P.packed ? sv.qblk0 + i : i) + qr;
+        const int64_t goff = (P.packed ? 0 : (int64_t)s * C.gs0) + (int64_t)h * C.gs1 + tok * C.gs2;
+        float g = 1.f;
+        if (CMODE == kTokenGate) g = __uint_as_float((uint32_t)C.gate[goff] << 16);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int d0 = 32 * dt + 8 * jj + 4 * hh;
+                const float4 c4 = *reinterpret_cast<const float4*>(ocr + d0);
+                float r[4];
+                const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+                if (CMODE == kFullGate) {
+                    const uint2 gw = *reinterpret_cast<const uint2*>(C.gate + goff + d0);
+                    const float gg[4] = {__uint_as_float(gw.x << 16), __uint_as_float(gw.x & 0xffff0000u),
+                                         __uint_as_float(gw.y << 16), __uint_as_float(gw.y & 0xffff0000u)};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) r[e] = __builtin_fmaf(cc[e], gg[e], o[dt][4 * jj + e] * inv);
+                } else if (CMODE == kTokenGate) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) r[e] = __builtin_fmaf(cc[e], g, o[dt][4 * jj + e] * inv);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) r[e] = cc[e] + o[dt][4 * jj + e] * inv;
+                }
+                uint2 w2;
+                w2.x = bf16pair(r[0], r[1]);
+                w2.y = bf16pair(r[2], r[3]);
+                *reinterpret_cast<uint2*>(orow + d0) = w2;
             }
     } else if (P.packed) {
         uint16_t* orow = out + (qrow0 + qr) * D;
@@ -447,21 +495,40 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     }
 }
 
+template <int CMODE>
+hipError_t launch_mode(const DevProblem& P, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       const int* idx, const int* num, uint16_t* out, const CombineArgs& C, hipStream_t st) {
+    const int64_t N = P.packed ? (int64_t)P.total_q * P.H : (int64_t)P.nQ * P.H * P.nseq;
+    if (N <= 0 || N > 0x7fffffff) return hipErrorInvalidValue;
+    const float c = (float)(1.4426950408889634 / sqrt((double)P.D));
+    if (P.D == 128)
+        hipLaunchKernelGGL((sparse_attn_kernel<128, CMODE>), dim3((unsigned)N), dim3(kAttnThreads), 0, st, P, q,
+                           k, v, idx, num, out, c, C);
+    else
+        hipLaunchKernelGGL((sparse_attn_kernel<64, CMODE>), dim3((unsigned)N), dim3(kAttnThreads), 0, st, P, q,
+                           k, v, idx, num, out, c, C);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_sparse_attn(const DevProblem& P, const uint16_t* q, const uint16_t* k,
                               const uint16_t* v, const int* idx, const int* num, uint16_t* out,
                               hipStream_t st) {
-    const int64_t N = P.packed ? (int64_t)P.total_q * P.H : (int64_t)P.nQ * P.H * P.nseq;
-    if (N <= 0 || N > 0x7fffffff) return hipErrorInvalidValue;
-    const float c = (float)(1.4426950408889634 / sqrt((double)P.D));
-    if (P.D == 128)
-        hipLaunchKernelGGL(sparse_attn_kernel<128>, dim3((unsigned)N), dim3(kAttnThreads), 0, st, P, q,
-                           k, v, idx, num, out, c);
-    else
-        hipLaunchKernelGGL(sparse_attn_kernel<64>, dim3((unsigned)N), dim3(kAttnThreads), 0, st, P, q,
-                           k, v, idx, num, out, c);
-    return hipGetLastError();
+    return launch_mode<kSparseOnly>(P, q, k, v, idx, num, out, CombineArgs{nullptr, nullptr, 0, 0, 0}, st);
+}
+
+hipError_t launch_sparse_attn_combine(const DevProblem& P, const uint16_t* q, const uint16_t* k,
+                                      const uint16_t* v, const int* idx, const int* num, const float* out_c,
+                                      const uint16_t* gate, int mode, int64_t gs0, int64_t gs1, int64_t gs2,
+                                      uint16_t* out, hipStream_t st) {
+    const CombineArgs C{out_c, gate, gs0, gs1, gs2};
+    switch (mode) {
+        case 0: return launch_mode<kAddCoarse>(P, q, k, v, idx, num, out, C, st);
+        case 1: return launch_mode<kTokenGate>(P, q, k, v, idx, num, out, C, st);
+        case 2: return launch_mode<kFullGate>(P, q, k, v, idx, num, out, C, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace vsa

@@ -323,6 +323,27 @@ int vsa_sparse_attn_from_indices(const vsa_problem* problem, const vsa_bf16* q, 
     return rc ? rc : ok();
 }
 
+int vsa_sparse_attn_combine(const vsa_problem* problem, const vsa_bf16* q, const vsa_bf16* k,
+                            const vsa_bf16* v, const int32_t* q2k_idx, const int32_t* q2k_num,
+                            const float* out_c, const vsa_bf16* gate, int32_t gate_mode,
+                            const int64_t* gate_strides_in, vsa_bf16* out, vsa_stream stream) {
+    vsa::DevProblem P;
+    int rc = make_problem(problem, &P);
+    if (rc) return rc;
+    if ((rc = check_qkv(P, q, k, v))) return rc;
+    if (!q2k_idx || !q2k_num || !out || !out_c) return fail(VSA_ERR_NULL, "q2k_idx, q2k_num, out_c or out is NULL");
+    if (!aligned16(out) || !aligned16(out_c)) return fail(VSA_ERR_ALIGN, "out_c and out must be 16-byte aligned");
+    if ((rc = check_out_alias(P, out, q, k, v))) return rc;
+    int64_t gs[3];
+    if ((rc = gate_strides(P, gate, gate_mode, gate_strides_in, gs))) return rc;
+    if (gate_mode != VSA_GATE_NONE && overlaps(out, 2 * q_elems(P), gate, 2))
+        return fail(VSA_ERR_ALIAS, "gate overlaps out");
+    rc = hip_status(vsa::launch_sparse_attn_combine(P, q, k, v, q2k_idx, q2k_num, out_c, gate, gate_mode, gs[0],
+                                                    gs[1], gs[2], out, (hipStream_t)stream),
+                    "fused sparse attention launch");
+    return rc ? rc : ok();
+}
+
 int vsa_combine(const vsa_problem* problem, const float* out_c, const vsa_bf16* gate, int32_t gate_mode,
                 const int64_t* gate_strides_in, vsa_bf16* out, vsa_stream stream) {
     vsa::DevProblem P;
@@ -354,6 +375,8 @@ static int forward_common(const vsa_problem* pr, const vsa_bf16* q, const vsa_bf
     if ((rc = check_out_alias(P, out, q, k, v))) return rc;
     int64_t gs[3];
     if ((rc = gate_strides(P, gate, gate_mode, gate_strides_in, gs))) return rc;
+    if (gate_mode != VSA_GATE_NONE && overlaps(out, 2 * q_elems(P), gate, 2))
+        return fail(VSA_ERR_ALIAS, "gate overlaps out");
     if (out_c && !aligned16(out_c)) return fail(VSA_ERR_ALIGN, "out_c must be 16-byte aligned");
     if ((q2k_idx && ((uintptr_t)q2k_idx & 3u)) || (q2k_num && ((uintptr_t)q2k_num & 3u)))
         return fail(VSA_ERR_ALIGN, "index arrays must be 4-byte aligned");
@@ -367,10 +390,9 @@ static int forward_common(const vsa_problem* pr, const vsa_bf16* q, const vsa_bf
     int* num = q2k_num ? q2k_num : w.num;
     hipStream_t st = (hipStream_t)stream;
     if ((rc = run_coarse(P, q, k, v, oc, idx, num, w, st))) return rc;
-    if ((rc = hip_status(vsa::launch_sparse_attn(P, q, k, v, idx, num, out, st), "sparse attention launch")))
-        return rc;
-    if ((rc = hip_status(vsa::launch_combine(P, oc, gate, gate_mode, gs[0], gs[1], gs[2], out, st),
-                         "combine launch")))
+    if ((rc = hip_status(vsa::launch_sparse_attn_combine(P, q, k, v, idx, num, oc, gate, gate_mode, gs[0], gs[1],
+                                                         gs[2], out, st),
+                         "fused sparse attention launch")))
         return rc;
     return ok();
 }

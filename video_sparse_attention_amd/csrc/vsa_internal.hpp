@@ -104,6 +104,10 @@ hipError_t launch_coarse_topk(const DevProblem& P, const double* qc, const doubl
 hipError_t launch_sparse_attn(const DevProblem& P, const uint16_t* q, const uint16_t* k,
                               const uint16_t* v, const int* idx, const int* num, uint16_t* out,
                               hipStream_t st);
+hipError_t launch_sparse_attn_combine(const DevProblem& P, const uint16_t* q, const uint16_t* k,
+                                      const uint16_t* v, const int* idx, const int* num, const float* out_c,
+                                      const uint16_t* gate, int mode, int64_t gs0, int64_t gs1, int64_t gs2,
+                                      uint16_t* out, hipStream_t st);
 hipError_t launch_combine(const DevProblem& P, const float* out_c, const uint16_t* gate, int mode,
                           int64_t gs0, int64_t gs1, int64_t gs2, uint16_t* out, hipStream_t st);
 
