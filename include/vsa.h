@@ -152,11 +152,13 @@ int vsa_build_metadata(int32_t num_seqs, const int32_t *seqlens_q, const int32_t
 /*
  * vsa_workspace_size - bytes of device workspace the problem needs
  * (vsa_coarse_topk, vsa_forward, vsa_forward_varlen).  It holds only
- * block-resolution data: pooled Q/K/V in float64 plus, for the two forward
+ * block-resolution data, no full-sequence temporary ("[perf] avoid
+ * full-sequence materialization in VSA coarse/sparse combine", Change):
+ * pooled Q/K/V in float64, the float64 block-level score matrix of a chunk of
+ * query blocks (the coarse stage runs chunk by chunk so that this matrix
+ * stays below max(32 MiB, 1/8 of the bytes of q)) and, for the two forward
  * calls, the float32 coarse output and the routing indices when the caller
- * does not ask for them; it never scales with S*D (no full-sequence
- * temporary, "[perf] avoid full-sequence materialization in VSA coarse/sparse
- * combine", Change).  Returns 0 when the problem is invalid.
+ * does not ask for them.  Returns 0 when the problem is invalid.
  */
 size_t vsa_workspace_size(const vsa_problem *problem);
 

@@ -133,15 +133,16 @@ def packed(num_seqs=2, nq=5, nkv=6, mq=3, mkv=4, mk=2, H=2, D=64, ptrs=True):
 
 
 def test_workspace_is_block_resolution(lib):
-    """The workspace never holds a full-sequence tensor: it is a fixed fraction of
-    one [B,H,S,D] bf16 tensor, from block-resolution float64 pooled Q/K/V, the
-    float32 coarse output and the routing indices."""
+    """The workspace never holds a full-sequence tensor: it is a bounded
+    fraction of one [B,H,S,D] bf16 tensor, from block-resolution float64 pooled
+    Q/K/V, the chunked block-level score matrix, the float32 coarse output and
+    the routing indices."""
     sizes = []
-    for S in (64 * 10, 64 * 100, 64 * 242):
+    for S in (64 * 10, 64 * 100, 64 * 242, 64 * 4096):
         p = dense(B=1, H=56, Sq=S, Skv=S, D=128, topk=49)
         ws = lib.vsa_workspace_size(ctypes.byref(p))
         full = 56 * S * 128 * 2
-        assert 0 < ws < 0.3 * full
+        assert 0 < ws < 0.4 * full, (S, ws / full)
         sizes.append(ws)
     p = packed()
     assert lib.vsa_workspace_size(ctypes.byref(p)) > 0

@@ -66,3 +66,24 @@ def test_large_sparse_on_oracle_indices():
     ref = G.oracle_dense(inp, blocks=blocks)
     gpu = G.run_dense_stages(inp, idx_override=(ref["q2k_idx"], ref["q2k_num"]))
     N.check_sparse(N.f64(gpu["out_s"]), ref["out_s"])
+
+
+def test_coarse_in_chunks():
+    """2100 x 2100 query/KV blocks on one head: the float64 score matrix (35 MB)
+    exceeds the coarse stage's workspace bound, so it runs in two chunks of
+    query blocks; every index row, every coarse row and sampled outputs are
+    compared with the oracle."""
+    S = 64 * 2100
+    inp = synth.dense_inputs(1, 1, S, 64, 7, seed=2100, gated=True)
+    nq = S // 64
+    rng = np.random.default_rng(7)
+    blocks = [(0, 0, int(i)) for i in rng.choice(nq, 16, replace=False)] + [(0, 0, 1996), (0, 0, 1997),
+                                                                             (0, 0, nq - 1)]
+    G.note(f"case chunked coarse: S={S} D=64 topk=7, {len(blocks)} sampled blocks")
+    gpu = G.run_dense_stages(inp)
+    ref = G.oracle_dense(inp, blocks=blocks)
+    G.assert_tie_free(ref)
+    G.assert_indices_equal(gpu["q2k_idx"], gpu["q2k_num"], ref)
+    N.check_out_c(N.f64(gpu["out_c"]), ref["out_c"])
+    N.check_sparse(N.f64(gpu["out_s"]), ref["out_s"])
+    N.check_out(N.f64(gpu["out_fused"]), ref["out"], "out (fused combine)")

@@ -4,32 +4,34 @@
 // selection.  "[chore] release fastvideo-kernel 0.3.0", Block-sparse / VSA
 // attention improvements: q2k_idx / q2k_num.)
 //
-// One workgroup (4 waves) handles R consecutive query blocks of one sequence
-// and head:
-//   1. the R pooled query rows are staged in LDS;
-//   2. raw float64 dot products Qc[i] . Kc[j] for every KV block j of the
-//      sequence land in LDS (thread j reads Kc[j] once and serves R rows);
-//   3. one wave per row selects the top-k exactly: the row's order-preserving
+// Three launches, all in float64 so that the selected set matches a float64
+// reference on any input whose k-th and (k+1)-th scores are not within a few
+// ulps of each other.  They run over chunks of C query blocks per sequence
+// (one chunk unless the score matrix would exceed its workspace bound):
+//   1. scores: for every sequence and head the block-level score matrix
+//      Qc Kc^T (raw dot products, no scale) of the chunk's query blocks is
+//      written to a workspace matrix with one row per query block; 64 x 64
+//      output tiles per workgroup, 16-wide d slices of Qc and Kc staged
+//      transposed in LDS, 4 x 4 outputs per thread;
+//   2. select: one wave per query block row.  The row's order-preserving
 //      64-bit keys sit in registers (up to 64 per lane), the k-th largest is
-//      found bit by bit with wave-wide ballot counts (32 rounds on the high
+//      found by bisection with wave-wide ballot counts (32 rounds on the high
 //      halves, 32 more on the low halves only when needed), ties at the
 //      threshold go to the lowest indices, and the indices are emitted in
-//      ascending order with ballot prefix counts;
-//   4. the same wave turns the row into softmax weights exp((s - max)/sqrt(D))
-//      and their sum, in float64;
-//   5. out_c[i][d] = sum_j w[i][j] Vc[j][d] / sum_j w[i][j], rounded once to
-//      float32; each thread owns 4 d of 2 rows.
-// Scores, softmax and the coarse product stay in float64 so that the
-// selected set matches a float64 reference on any input whose k-th and
-// (k+1)-th scores are not within a few ulps of each other.
+//      ascending order with ballot prefix counts.  The row is then replaced
+//      by its softmax weights exp((s - max) / sqrt(D)) and their sum is kept;
+//   3. output: out_c = W Vc / sum(W) per row, 64 rows x D columns per
+//      workgroup, 16-row slices of W and Vc staged in LDS, rounded once to
+//      float32.
 #include "vsa_internal.hpp"
 
 namespace vsa {
 namespace {
 
-constexpr int kCoarseThreads = 256;
-constexpr int kCoarseWaves = kCoarseThreads / 64;
-constexpr size_t kCoarseLdsBudget = 60 * 1024;
+constexpr int kThreads = 256;
+constexpr int kTile = 64;   // query rows (and KV columns) per workgroup tile
+constexpr int kSlice = 16;  // d (or KV) values per LDS slice
+constexpr int kPad = 2;     // keeps each transposed LDS row 16-byte aligned
 
 __device__ __forceinline__ uint64_t order_key(double s) {
     // -0.0 and +0.0 compare equal as doubles; fold them before the bit map.
@@ -37,10 +39,8 @@ __device__ __forceinline__ uint64_t order_key(double s) {
     return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
-__device__ __forceinline__ int lane_id() { return __lane_id(); }
-
 __device__ __forceinline__ int prefix_popc(uint64_t mask) {
-    const int l = lane_id();
+    const int l = __lane_id();
     const uint64_t below = l == 0 ? 0ull : (mask & ((~0ull) >> (64 - l)));
     return __popcll(below);
 }
@@ -54,234 +54,327 @@ __device__ __forceinline__ double wave_sum(double x) {
     return x;
 }
 
-template <int D, int R, int KPL>
-__global__ __launch_bounds__(kCoarseThreads) void coarse_topk_kernel(
-    DevProblem P, const double* __restrict__ qc, const double* __restrict__ kc,
-    const double* __restrict__ vc, float* __restrict__ out_c, int* __restrict__ idx_out,
-    int* __restrict__ num_out, int kv_cap, double scale) {
-    extern __shared__ double lds[];
-    double* qrow = lds;              // [R][D]
-    double* sc = lds + R * D;        // [R][kv_cap]
-    __shared__ double lsum[R];
-
-    const int s = blockIdx.z;
-    const int h = blockIdx.y;
+// ---------------------------------------------------------------------------
+// 1. block-level scores
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void coarse_scores_kernel(DevProblem P, const double* __restrict__ qc,
+                                                                 const double* __restrict__ kc,
+                                                                 double* __restrict__ sc, int ld,
+                                                                 int tiles_kv, int c0, int C) {
+    __shared__ __attribute__((aligned(16))) double qt[kSlice][kTile + kPad];  // [d][row]
+    __shared__ __attribute__((aligned(16))) double kt[kSlice][kTile + kPad];  // [d][col]
+    const int s = blockIdx.z, h = blockIdx.y;
     const SeqView sv = seq_view(P, s, h);
-    const int i0 = blockIdx.x * R;
-    if (i0 >= sv.nq) return;
-    const int nr = min(R, sv.nq - i0);
-    const int nkv = min(min(sv.nkv, kv_cap), 64 * KPL);
+    const int i0 = c0 + (blockIdx.x / tiles_kv) * kTile;  // local query block of tile row 0
+    const int j0 = (blockIdx.x % tiles_kv) * kTile;
+    const int iend = min(sv.nq, c0 + C);
+    if (i0 >= iend || j0 >= sv.nkv) return;
+    const int64_t srow0 = ((int64_t)s * P.H + h) * C - c0;  // scratch row of local block 0
     const int tid = threadIdx.x;
+    const int ty = tid / 16, tx = tid % 16;
+    // staging: thread t copies 4 consecutive d of row t / 4
+    const int sr = tid / 4, sd = 4 * (tid % 4);
+    const bool q_ok = i0 + sr < iend, k_ok = j0 + sr < sv.nkv;
+    const double* qrow = qc + (sv.qblk_base + i0 + (q_ok ? sr : 0)) * D + sd;
+    const double* krow = kc + (sv.kvblk_base + j0 + (k_ok ? sr : 0)) * D + sd;
 
-    // 1. pooled query rows
-    for (int e = tid; e < R * D; e += kCoarseThreads) {
-        const int r = e / D;
-        qrow[e] = r < nr ? qc[(sv.qblk_base + i0 + r) * D + (e % D)] : 0.0;
-    }
-    __syncthreads();
-
-    // 2. raw scores: thread j reads Kc[j] once and serves all R rows
-    for (int j = tid; j < nkv; j += kCoarseThreads) {
-        double acc[R];
+    double acc[4][4];
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = 0.0;
-        const double2* kr = reinterpret_cast<const double2*>(kc + (sv.kvblk_base + j) * D);
-#pragma unroll 4
-        for (int d2 = 0; d2 < D / 2; ++d2) {
-            const double2 kv = kr[d2];
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const double2 qv = *reinterpret_cast<const double2*>(&qrow[r * D + 2 * d2]);
-                acc[r] = fma(qv.x, kv.x, acc[r]);
-                acc[r] = fma(qv.y, kv.y, acc[r]);
-            }
+        for (int c = 0; c < 4; ++c) acc[r][c] = 0.0;
+    for (int d0 = 0; d0 < D; d0 += kSlice) {
+        double2 qa = make_double2(0.0, 0.0), qb = qa, ka = qa, kb = qa;
+        if (q_ok) {
+            qa = *reinterpret_cast<const double2*>(qrow + d0);
+            qb = *reinterpret_cast<const double2*>(qrow + d0 + 2);
         }
-#pragma unroll
-        for (int r = 0; r < R; ++r) sc[r * kv_cap + j] = acc[r];
-    }
-    __syncthreads();
-
-    // 3 + 4. per row (one wave): exact top-k on keys held in registers, then
-    // softmax weights written back in place
-    const int wave = tid / 64;
-    const int lane = tid % 64;
-    for (int r = wave; r < nr; r += kCoarseWaves) {
-        double* row = sc + r * kv_cap;
-        const int k = sv.k;
-        const int64_t qb = sv.qblk_base + i0 + r;
-        int* orow = idx_out + qb * P.idx_row;
-
-        uint64_t key[KPL];  // 0 marks "no block": below the key of any double
-#pragma unroll
-        for (int e = 0; e < KPL; ++e) {
-            const int j = 64 * e + lane;
-            key[e] = j < nkv ? order_key(row[j]) : 0ull;
+        if (k_ok) {
+            ka = *reinterpret_cast<const double2*>(krow + d0);
+            kb = *reinterpret_cast<const double2*>(krow + d0 + 2);
         }
-        // T = the k-th largest key.  First the k-th largest of the high 32 bits
-        // (Th) by bitwise bisection on 32-bit compares; the low 32 bits only
-        // need a second bisection when the candidates sharing Th are more than
-        // the number still to be chosen.
-        uint32_t Th = 0;
+        __syncthreads();  // previous slice fully consumed
+        qt[sd + 0][sr] = qa.x; qt[sd + 1][sr] = qa.y; qt[sd + 2][sr] = qb.x; qt[sd + 3][sr] = qb.y;
+        kt[sd + 0][sr] = ka.x; kt[sd + 1][sr] = ka.y; kt[sd + 2][sr] = kb.x; kt[sd + 3][sr] = kb.y;
+        __syncthreads();
+#pragma unroll
+        for (int d = 0; d < kSlice; ++d) {
+            const double2 q01 = *reinterpret_cast<const double2*>(&qt[d][4 * ty]);
+            const double2 q23 = *reinterpret_cast<const double2*>(&qt[d][4 * ty + 2]);
+            const double2 k01 = *reinterpret_cast<const double2*>(&kt[d][4 * tx]);
+            const double2 k23 = *reinterpret_cast<const double2*>(&kt[d][4 * tx + 2]);
+            const double qv[4] = {q01.x, q01.y, q23.x, q23.y};
+            const double kv[4] = {k01.x, k01.y, k23.x, k23.y};
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[r][c] = fma(qv[r], kv[c], acc[r][c]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 4 * ty + r;
+        if (i >= iend) continue;
+        double* out = sc + (srow0 + i) * ld + j0 + 4 * tx;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (j0 + 4 * tx + c < sv.nkv) out[c] = acc[r][c];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 2. exact top-k per row, then softmax weights in place
+// ---------------------------------------------------------------------------
+template <int KPL>
+__global__ __launch_bounds__(kThreads) void coarse_select_kernel(DevProblem P, double* __restrict__ sc, int ld,
+                                                                 double* __restrict__ lsum,
+                                                                 int* __restrict__ idx_out,
+                                                                 int* __restrict__ num_out, double scale,
+                                                                 int c0, int C) {
+    const int wave = threadIdx.x / 64;
+    const int lane = threadIdx.x % 64;
+    // scratch row = (s * H + h) * C + (i - c0)
+    const int64_t srow = (int64_t)blockIdx.x * (kThreads / 64) + wave;
+    if (srow >= (int64_t)P.nseq * P.H * C) return;
+    const int i = c0 + (int)(srow % C);
+    const int64_t sh = srow / C;
+    const int h = (int)(sh % P.H), s = (int)(sh / P.H);
+    const SeqView sv = seq_view(P, s, h);
+    if (i >= sv.nq) return;
+    const int64_t qb = sv.qblk_base + i;
+    double* row = sc + srow * ld;
+    int* orow = idx_out + qb * P.idx_row;
+    const int nkv = min(sv.nkv, 64 * KPL);
+    const int k = sv.k;
+
+    uint64_t key[KPL];  // 0 marks "no block": below the key of any double
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) {
+        const int j = 64 * e + lane;
+        key[e] = j < nkv ? order_key(row[j]) : 0ull;
+    }
+    // T = the k-th largest key.  First the k-th largest of the high 32 bits
+    // (Th) by bitwise bisection on 32-bit compares; the low 32 bits only need
+    // a second bisection when the candidates sharing Th are more than the
+    // number still to be chosen.
+    uint32_t Th = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = Th | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int e = 0; e < KPL; ++e)
+            if (64 * e < nkv) cnt += __popcll(__ballot((uint32_t)(key[e] >> 32) >= cand));
+        if (cnt >= k) Th = cand;
+    }
+    int gt_hi = 0, eq_hi = 0;
+#pragma unroll
+    for (int e = 0; e < KPL; ++e)
+        if (64 * e < nkv) {
+            const uint32_t hi = (uint32_t)(key[e] >> 32);
+            gt_hi += __popcll(__ballot(hi > Th));
+            eq_hi += __popcll(__ballot(hi == Th));
+        }
+    const int need_hi = k - gt_hi;  // >= 1 and <= eq_hi
+    uint32_t Tl = 0;
+    if (eq_hi != need_hi) {
         for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cand = Th | (1u << bit);
+            const uint32_t cand = Tl | (1u << bit);
             int cnt = 0;
 #pragma unroll
             for (int e = 0; e < KPL; ++e)
-                if (64 * e < nkv) cnt += __popcll(__ballot((uint32_t)(key[e] >> 32) >= cand));
-            if (cnt >= k) Th = cand;
+                if (64 * e < nkv)
+                    cnt += __popcll(__ballot((uint32_t)(key[e] >> 32) == Th && (uint32_t)key[e] >= cand));
+            if (cnt >= need_hi) Tl = cand;
         }
-        int gt_hi = 0, eq_hi = 0;
-#pragma unroll
-        for (int e = 0; e < KPL; ++e)
-            if (64 * e < nkv) {
-                const uint32_t hi = (uint32_t)(key[e] >> 32);
-                gt_hi += __popcll(__ballot(hi > Th));
-                eq_hi += __popcll(__ballot(hi == Th));
-            }
-        const int need_hi = k - gt_hi;  // >= 1 and <= eq_hi
-        uint32_t Tl = 0;
-        if (eq_hi != need_hi) {
-            for (int bit = 31; bit >= 0; --bit) {
-                const uint32_t cand = Tl | (1u << bit);
-                int cnt = 0;
-#pragma unroll
-                for (int e = 0; e < KPL; ++e)
-                    if (64 * e < nkv)
-                        cnt += __popcll(__ballot((uint32_t)(key[e] >> 32) == Th && (uint32_t)key[e] >= cand));
-                if (cnt >= need_hi) Tl = cand;
-            }
-        }
-        // (when every candidate is chosen, T = Th:0 selects all of them below)
-        const uint64_t T = ((uint64_t)Th << 32) | Tl;
-        int n_gt = 0;
-#pragma unroll
-        for (int e = 0; e < KPL; ++e)
-            if (64 * e < nkv) n_gt += __popcll(__ballot(key[e] > T));
-        const int need_eq = k - n_gt;
-        int n_sel = 0, n_eq = 0;
-#pragma unroll
-        for (int e = 0; e < KPL; ++e) {
-            if (64 * e >= nkv) break;
-            const int j = 64 * e + lane;
-            const bool eq = key[e] == T;
-            const uint64_t eq_mask = __ballot(eq);
-            const bool sel = key[e] > T || (eq && n_eq + prefix_popc(eq_mask) < need_eq);
-            const uint64_t sel_mask = __ballot(sel);
-            if (sel) orow[n_sel + prefix_popc(sel_mask)] = j + sv.idx_rebase;
-            n_sel += __popcll(sel_mask);
-            n_eq += __popcll(eq_mask);
-        }
-        for (int t = n_sel + lane; t < P.idx_row; t += 64) orow[t] = -1;
-        if (lane == 0) num_out[qb] = n_sel;
-
-        double m = -INFINITY;
-        for (int j = lane; j < nkv; j += 64) m = fmax(m, row[j]);
-        m = wave_max(m);
-        double l = 0.0;
-        for (int j = lane; j < nkv; j += 64) {
-            const double w = exp((row[j] - m) * scale);
-            row[j] = w;
-            l += w;
-        }
-        l = wave_sum(l);
-        if (lane == 0) lsum[r] = l;
     }
-    __syncthreads();
+    // (when every candidate is chosen, T = Th:0 selects all of them below)
+    const uint64_t T = ((uint64_t)Th << 32) | Tl;
+    int n_gt = 0;
+#pragma unroll
+    for (int e = 0; e < KPL; ++e)
+        if (64 * e < nkv) n_gt += __popcll(__ballot(key[e] > T));
+    const int need_eq = k - n_gt;
+    int n_sel = 0, n_eq = 0;
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) {
+        if (64 * e >= nkv) break;
+        const int j = 64 * e + lane;
+        const bool eq = key[e] == T;
+        const uint64_t eq_mask = __ballot(eq);
+        const bool sel = key[e] > T || (eq && n_eq + prefix_popc(eq_mask) < need_eq);
+        const uint64_t sel_mask = __ballot(sel);
+        if (sel) orow[n_sel + prefix_popc(sel_mask)] = j + sv.idx_rebase;
+        n_sel += __popcll(sel_mask);
+        n_eq += __popcll(eq_mask);
+    }
+    for (int t = n_sel + lane; t < P.idx_row; t += 64) orow[t] = -1;
+    if (lane == 0) num_out[qb] = n_sel;
 
-    // 5. coarse output: thread (quad, pair) owns d = 4 quad .. +3 of rows
-    // 2 pair, 2 pair + 1 (and further pairs when R > 2 * groups): per KV block
-    // two 16-byte loads of Vc and two LDS reads of weights feed 8 FMAs.
-    constexpr int QUADS = D / 4;
-    constexpr int PAIRS = kCoarseThreads / QUADS;  // row pairs handled at once
-    const int quad = tid % QUADS;
-    const int pair = tid / QUADS;
-    for (int r0 = 2 * pair; r0 < nr; r0 += 2 * PAIRS) {
-        const bool two = r0 + 1 < nr;
-        const double* w0 = sc + r0 * kv_cap;
-        const double* w1 = sc + (two ? r0 + 1 : r0) * kv_cap;
-        double a0[4] = {0.0, 0.0, 0.0, 0.0}, a1[4] = {0.0, 0.0, 0.0, 0.0};
-        const double2* vcol = reinterpret_cast<const double2*>(vc + sv.kvblk_base * D + 4 * quad);
+    // softmax weights in place and their sum
+    double m = -INFINITY;
+    for (int j = lane; j < nkv; j += 64) m = fmax(m, row[j]);
+    m = wave_max(m);
+    double l = 0.0;
+    for (int j = lane; j < nkv; j += 64) {
+        const double w = exp((row[j] - m) * scale);
+        row[j] = w;
+        l += w;
+    }
+    l = wave_sum(l);
+    if (lane == 0) lsum[qb] = l;
+}
+
+// ---------------------------------------------------------------------------
+// 3. out_c = W Vc / sum(W)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void coarse_out_kernel(DevProblem P, const double* __restrict__ sc, int ld,
+                                                              const double* __restrict__ lsum,
+                                                              const double* __restrict__ vc,
+                                                              float* __restrict__ out_c, int c0, int C) {
+    constexpr int CPT = D / 16;  // output columns per thread
+    __shared__ __attribute__((aligned(16))) double wt[kSlice][kTile + kPad];  // [kv][row]
+    __shared__ __attribute__((aligned(16))) double vs[kSlice][D];             // [kv][d]
+    const int s = blockIdx.z, h = blockIdx.y;
+    const SeqView sv = seq_view(P, s, h);
+    const int i0 = c0 + blockIdx.x * kTile;
+    const int iend = min(sv.nq, c0 + C);
+    if (i0 >= iend) return;
+    const int64_t srow0 = ((int64_t)s * P.H + h) * C - c0;  // scratch row of local block 0
+    const int nkv = sv.nkv;
+    const int tid = threadIdx.x;
+    const int ty = tid / 16, tx = tid % 16;
+    // staging of W: thread t copies 4 consecutive KV entries of row t / 4
+    const int sr = tid / 4, sj = 4 * (tid % 4);
+    const bool w_ok = i0 + sr < iend;
+    const double* wrow = sc + (srow0 + i0 + (w_ok ? sr : 0)) * ld;
+
+    double acc[4][CPT];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[r][c] = 0.0;
+    for (int j0 = 0; j0 < nkv; j0 += kSlice) {
+        double wv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = j0 + sj + e;
+            wv[e] = (w_ok && j < nkv) ? wrow[j] : 0.0;
+        }
+        // Vc slice: 16 rows of D values, one double2 per thread per pass
+        double2 vv[D / 32];
+#pragma unroll
+        for (int p = 0; p < D / 32; ++p) {
+            const int e = tid + kThreads * p;  // double2 index in the [16][D] slice
+            const int jr = e / (D / 2), dc = 2 * (e % (D / 2));
+            vv[p] = j0 + jr < nkv ? *reinterpret_cast<const double2*>(vc + (sv.kvblk_base + j0 + jr) * D + dc)
+                                  : make_double2(0.0, 0.0);
+        }
+        __syncthreads();  // previous slice fully consumed
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wt[sj + e][sr] = wv[e];
+#pragma unroll
+        for (int p = 0; p < D / 32; ++p) {
+            const int e = tid + kThreads * p;
+            *reinterpret_cast<double2*>(&vs[e / (D / 2)][2 * (e % (D / 2))]) = vv[p];
+        }
+        __syncthreads();
 #pragma unroll 4
-        for (int j = 0; j < nkv; ++j) {
-            const double2 x = vcol[j * (D / 2)];
-            const double2 y = vcol[j * (D / 2) + 1];
-            const double p0 = w0[j], p1 = w1[j];
-            a0[0] = fma(p0, x.x, a0[0]); a0[1] = fma(p0, x.y, a0[1]);
-            a0[2] = fma(p0, y.x, a0[2]); a0[3] = fma(p0, y.y, a0[3]);
-            a1[0] = fma(p1, x.x, a1[0]); a1[1] = fma(p1, x.y, a1[1]);
-            a1[2] = fma(p1, y.x, a1[2]); a1[3] = fma(p1, y.y, a1[3]);
+        for (int jj = 0; jj < kSlice; ++jj) {
+            const double2 w01 = *reinterpret_cast<const double2*>(&wt[jj][4 * ty]);
+            const double2 w23 = *reinterpret_cast<const double2*>(&wt[jj][4 * ty + 2]);
+            const double w[4] = {w01.x, w01.y, w23.x, w23.y};
+            double v[CPT];
+#pragma unroll
+            for (int c = 0; c < CPT; c += 2) {
+                const double2 t2 = *reinterpret_cast<const double2*>(&vs[jj][CPT * tx + c]);
+                v[c] = t2.x;
+                v[c + 1] = t2.y;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) acc[r][c] = fma(w[r], v[c], acc[r][c]);
         }
-        float* o0 = out_c + (sv.qblk_base + i0 + r0) * D + 4 * quad;
-        const double l0 = lsum[r0];
-        *reinterpret_cast<float4*>(o0) =
-            make_float4((float)(a0[0] / l0), (float)(a0[1] / l0), (float)(a0[2] / l0), (float)(a0[3] / l0));
-        if (two) {
-            const double l1 = lsum[r0 + 1];
-            *reinterpret_cast<float4*>(o0 + D) =
-                make_float4((float)(a1[0] / l1), (float)(a1[1] / l1), (float)(a1[2] / l1), (float)(a1[3] / l1));
-        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 4 * ty + r;
+        if (i >= iend) continue;
+        const int64_t qb = sv.qblk_base + i;
+        const double l = lsum[qb];
+        float* o = out_c + qb * D + CPT * tx;
+#pragma unroll
+        for (int c = 0; c < CPT; c += 4)
+            *reinterpret_cast<float4*>(o + c) = make_float4((float)(acc[r][c] / l), (float)(acc[r][c + 1] / l),
+                                                           (float)(acc[r][c + 2] / l), (float)(acc[r][c + 3] / l));
     }
 }
 
 template <int D>
-size_t coarse_lds_bytes(int R, int kv_cap) {
-    return (size_t)8 * R * (D + kv_cap);
-}
-
-template <int D, int R, int KPL>
-hipError_t launch_rk(const DevProblem& P, const double* qc, const double* kc, const double* vc,
-                     float* out_c, int* idx, int* num, hipStream_t st) {
+hipError_t launch_d(const DevProblem& P, const double* qc, const double* kc, const double* vc, float* out_c,
+                    int* idx, int* num, double* sc, double* lsum, int C, hipStream_t st) {
     const int max_nq = P.packed ? P.max_q : P.nQ;
-    const int kv_cap = P.packed ? P.max_kv : P.nKV;
-    dim3 grid((max_nq + R - 1) / R, P.H, P.nseq);
-    const size_t lds = coarse_lds_bytes<D>(R, kv_cap);
-    hipLaunchKernelGGL((coarse_topk_kernel<D, R, KPL>), grid, dim3(kCoarseThreads), lds, st, P, qc,
-                       kc, vc, out_c, idx, num, kv_cap, 1.0 / sqrt((double)D));
-    return hipGetLastError();
-}
-
-template <int D, int R>
-hipError_t launch_r(const DevProblem& P, const double* qc, const double* kc, const double* vc,
-                    float* out_c, int* idx, int* num, hipStream_t st) {
-    const int kv_cap = P.packed ? P.max_kv : P.nKV;
-    if (kv_cap <= 4 * 64) return launch_rk<D, R, 4>(P, qc, kc, vc, out_c, idx, num, st);
-    if (kv_cap <= 16 * 64) return launch_rk<D, R, 16>(P, qc, kc, vc, out_c, idx, num, st);
-    return launch_rk<D, R, 64>(P, qc, kc, vc, out_c, idx, num, st);
-}
-
-template <int D>
-hipError_t launch_d(const DevProblem& P, const double* qc, const double* kc, const double* vc,
-                    float* out_c, int* idx, int* num, hipStream_t st) {
-    const int kv_cap = P.packed ? P.max_kv : P.nKV;
-    const int R = coarse_rows_per_group(kv_cap, D);
-    switch (R) {
-        case 16: return launch_r<D, 16>(P, qc, kc, vc, out_c, idx, num, st);
-        case 8: return launch_r<D, 8>(P, qc, kc, vc, out_c, idx, num, st);
-        case 4: return launch_r<D, 4>(P, qc, kc, vc, out_c, idx, num, st);
-        case 2: return launch_r<D, 2>(P, qc, kc, vc, out_c, idx, num, st);
-        case 1: return launch_r<D, 1>(P, qc, kc, vc, out_c, idx, num, st);
-        default: return hipErrorInvalidValue;
+    const int ld = P.packed ? P.max_kv : P.nKV;
+    const int tq = (C + kTile - 1) / kTile, tk = (ld + kTile - 1) / kTile;
+    const int64_t rows = (int64_t)P.nseq * P.H * C;
+    const dim3 sgrid((unsigned)((rows + kThreads / 64 - 1) / (kThreads / 64)));
+    const double scale = 1.0 / sqrt((double)D);
+    for (int c0 = 0; c0 < max_nq; c0 += C) {
+        hipLaunchKernelGGL(coarse_scores_kernel<D>, dim3(tq * tk, P.H, P.nseq), dim3(kThreads), 0, st, P, qc, kc,
+                           sc, ld, tk, c0, C);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (ld <= 4 * 64)
+            hipLaunchKernelGGL(coarse_select_kernel<4>, sgrid, dim3(kThreads), 0, st, P, sc, ld, lsum, idx, num,
+                               scale, c0, C);
+        else if (ld <= 16 * 64)
+            hipLaunchKernelGGL(coarse_select_kernel<16>, sgrid, dim3(kThreads), 0, st, P, sc, ld, lsum, idx, num,
+                               scale, c0, C);
+        else
+            hipLaunchKernelGGL(coarse_select_kernel<64>, sgrid, dim3(kThreads), 0, st, P, sc, ld, lsum, idx, num,
+                               scale, c0, C);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(coarse_out_kernel<D>, dim3(tq, P.H, P.nseq), dim3(kThreads), 0, st, P, sc, ld, lsum, vc,
+                           out_c, c0, C);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
+    return hipSuccess;
+}
+
+// Query blocks per chunk: all of them unless the chunk's score matrix would
+// exceed max(32 MiB, 1/8 of the bytes of the bf16 query tensor).
+int chunk_rows(const DevProblem& P) {
+    const int max_nq = P.packed ? P.max_q : P.nQ;
+    const int64_t ld = P.packed ? P.max_kv : P.nKV;
+    const int64_t q_bytes = P.packed ? (int64_t)P.H * P.total_q * kBlock * P.D * 2
+                                     : (int64_t)P.nseq * P.H * P.Sq * P.D * 2;
+    const int64_t cap = q_bytes / 8 > ((int64_t)32 << 20) ? q_bytes / 8 : ((int64_t)32 << 20);
+    const int64_t per_row = (int64_t)P.nseq * P.H * ld * 8;
+    const int64_t c = cap / (per_row > 0 ? per_row : 1);
+    return (int)(c >= max_nq ? max_nq : (c < 1 ? 1 : c));
 }
 
 }  // namespace
 
-int coarse_rows_per_group(int max_kv_blocks, int D) {
-    if (max_kv_blocks < 1 || max_kv_blocks > kMaxKvBlocks) return 0;
-    const size_t per_row = (size_t)8 * (D + max_kv_blocks);
-    size_t r = kCoarseLdsBudget / per_row;
-    if (r >= 16) return 16;
-    if (r >= 8) return 8;
-    if (r >= 4) return 4;
-    if (r >= 2) return 2;
-    if (r >= 1) return 1;
-    return 0;
+size_t coarse_scratch_doubles(const DevProblem& P) {
+    const int64_t ld = P.packed ? P.max_kv : P.nKV;
+    const int64_t rows = P.packed ? (int64_t)P.H * P.total_q : (int64_t)P.nseq * P.H * P.nQ;
+    return (size_t)((int64_t)P.nseq * P.H * chunk_rows(P) * ld + rows);
 }
 
-hipError_t launch_coarse_topk(const DevProblem& P, const double* qc, const double* kc,
-                              const double* vc, float* out_c, int* idx, int* num, hipStream_t st) {
-    if (P.D == 128) return launch_d<128>(P, qc, kc, vc, out_c, idx, num, st);
-    return launch_d<64>(P, qc, kc, vc, out_c, idx, num, st);
+hipError_t launch_coarse_topk(const DevProblem& P, const double* qc, const double* kc, const double* vc,
+                              float* out_c, int* idx, int* num, double* scratch, hipStream_t st) {
+    const int kv_cap = P.packed ? P.max_kv : P.nKV;
+    if (kv_cap < 1 || kv_cap > kMaxKvBlocks) return hipErrorInvalidValue;
+    const int C = chunk_rows(P);
+    double* sc = scratch;
+    double* lsum = scratch + (int64_t)P.nseq * P.H * C * kv_cap;
+    if (P.D == 128) return launch_d<128>(P, qc, kc, vc, out_c, idx, num, sc, lsum, C, st);
+    return launch_d<64>(P, qc, kc, vc, out_c, idx, num, sc, lsum, C, st);
 }
 
 }  // namespace vsa

@@ -118,9 +118,10 @@ int64_t kvblocks(const vsa::DevProblem& P) {
 
 struct Workspace {
     double *qc, *kc, *vc;
+    double* coarse;  // block-level scores / weights and their row sums
     float* out_c;
     int *idx, *num;
-    size_t pooled_bytes, total_bytes;
+    size_t coarse_bytes, total_bytes;
 };
 
 Workspace plan_workspace(const vsa::DevProblem& P, void* base) {
@@ -135,7 +136,8 @@ Workspace plan_workspace(const vsa::DevProblem& P, void* base) {
     w.qc = (double*)take(sizeof(double) * qblocks(P) * P.D);
     w.kc = (double*)take(sizeof(double) * kvblocks(P) * P.D);
     w.vc = (double*)take(sizeof(double) * kvblocks(P) * P.D);
-    w.pooled_bytes = off;
+    w.coarse = (double*)take(sizeof(double) * vsa::coarse_scratch_doubles(P));
+    w.coarse_bytes = off;
     w.out_c = (float*)take(sizeof(float) * qblocks(P) * P.D);
     w.idx = (int*)take(sizeof(int) * qblocks(P) * P.idx_row);
     w.num = (int*)take(sizeof(int) * qblocks(P));
@@ -203,7 +205,8 @@ int run_coarse(const vsa::DevProblem& P, const uint16_t* q, const uint16_t* k, c
                float* out_c, int* idx, int* num, const Workspace& w, hipStream_t st) {
     int rc = hip_status(vsa::launch_pool(P, q, k, v, w.qc, w.kc, w.vc, st), "pool launch");
     if (rc) return rc;
-    return hip_status(vsa::launch_coarse_topk(P, w.qc, w.kc, w.vc, out_c, idx, num, st), "coarse/top-k launch");
+    return hip_status(vsa::launch_coarse_topk(P, w.qc, w.kc, w.vc, out_c, idx, num, w.coarse, st),
+                      "coarse/top-k launch");
 }
 
 }  // namespace
@@ -302,8 +305,8 @@ int vsa_coarse_topk(const vsa_problem* problem, const vsa_bf16* q, const vsa_bf1
     if (!workspace) return fail(VSA_ERR_WORKSPACE, "workspace is NULL");
     if ((uintptr_t)workspace % kAlign) return fail(VSA_ERR_ALIGN, "workspace must be 256-byte aligned");
     const Workspace w = plan_workspace(P, workspace);
-    if (workspace_bytes < w.pooled_bytes)
-        return fail(VSA_ERR_WORKSPACE, "workspace holds %zu bytes, needs %zu", workspace_bytes, w.pooled_bytes);
+    if (workspace_bytes < w.coarse_bytes)
+        return fail(VSA_ERR_WORKSPACE, "workspace holds %zu bytes, needs %zu", workspace_bytes, w.coarse_bytes);
     rc = run_coarse(P, q, k, v, out_c, q2k_idx, q2k_num, w, (hipStream_t)stream);
     return rc ? rc : ok();
 }

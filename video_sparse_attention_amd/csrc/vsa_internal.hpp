@@ -99,8 +99,11 @@ __device__ __forceinline__ int seq_of_qblock(const DevProblem& P, int g) {
 // ---------------------------------------------------------------------------
 hipError_t launch_pool(const DevProblem& P, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        double* qc, double* kc, double* vc, hipStream_t st);
+// scratch: coarse_scratch_doubles(P) doubles (block-level scores and row sums)
 hipError_t launch_coarse_topk(const DevProblem& P, const double* qc, const double* kc,
-                              const double* vc, float* out_c, int* idx, int* num, hipStream_t st);
+                              const double* vc, float* out_c, int* idx, int* num, double* scratch,
+                              hipStream_t st);
+size_t coarse_scratch_doubles(const DevProblem& P);
 hipError_t launch_sparse_attn(const DevProblem& P, const uint16_t* q, const uint16_t* k,
                               const uint16_t* v, const int* idx, const int* num, uint16_t* out,
                               hipStream_t st);
@@ -111,8 +114,6 @@ hipError_t launch_sparse_attn_combine(const DevProblem& P, const uint16_t* q, co
 hipError_t launch_combine(const DevProblem& P, const float* out_c, const uint16_t* gate, int mode,
                           int64_t gs0, int64_t gs1, int64_t gs2, uint16_t* out, hipStream_t st);
 
-// Rows per workgroup of the coarse kernel for a given KV block bound (0 = unsupported).
-int coarse_rows_per_group(int max_kv_blocks, int D);
 constexpr int kMaxKvBlocks = 4096;
 
 }  // namespace vsa
