@@ -84,8 +84,9 @@ __global__ __launch_bounds__(kThreads) void coarse_scores_kernel(DevProblem P, c
     for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[r][c] = 0.0;
-    for (int d0 = 0; d0 < D; d0 += kSlice) {
-        double2 qa = make_double2(0.0, 0.0), qb = qa, ka = qa, kb = qa;
+    // the next slice is loaded into registers while the current one is used
+    double2 qa = make_double2(0.0, 0.0), qb = qa, ka = qa, kb = qa;
+    auto fetch = [&](int d0) {
         if (q_ok) {
             qa = *reinterpret_cast<const double2*>(qrow + d0);
             qb = *reinterpret_cast<const double2*>(qrow + d0 + 2);
@@ -94,10 +95,14 @@ __global__ __launch_bounds__(kThreads) void coarse_scores_kernel(DevProblem P, c
             ka = *reinterpret_cast<const double2*>(krow + d0);
             kb = *reinterpret_cast<const double2*>(krow + d0 + 2);
         }
+    };
+    fetch(0);
+    for (int d0 = 0; d0 < D; d0 += kSlice) {
         __syncthreads();  // previous slice fully consumed
         qt[sd + 0][sr] = qa.x; qt[sd + 1][sr] = qa.y; qt[sd + 2][sr] = qb.x; qt[sd + 3][sr] = qb.y;
         kt[sd + 0][sr] = ka.x; kt[sd + 1][sr] = ka.y; kt[sd + 2][sr] = kb.x; kt[sd + 3][sr] = kb.y;
         __syncthreads();
+        if (d0 + kSlice < D) fetch(d0 + kSlice);
 #pragma unroll
         for (int d = 0; d < kSlice; ++d) {
             const double2 q01 = *reinterpret_cast<const double2*>(&qt[d][4 * ty]);
@@ -255,15 +260,15 @@ __global__ __launch_bounds__(kThreads) void coarse_out_kernel(DevProblem P, cons
     for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int c = 0; c < CPT; ++c) acc[r][c] = 0.0;
-    for (int j0 = 0; j0 < nkv; j0 += kSlice) {
-        double wv[4];
+    // the next slice is loaded into registers while the current one is used
+    double wv[4];
+    double2 vv[D / 32];  // Vc slice: 16 rows of D values, one double2 per thread per pass
+    auto fetch = [&](int j0) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int j = j0 + sj + e;
             wv[e] = (w_ok && j < nkv) ? wrow[j] : 0.0;
         }
-        // Vc slice: 16 rows of D values, one double2 per thread per pass
-        double2 vv[D / 32];
 #pragma unroll
         for (int p = 0; p < D / 32; ++p) {
             const int e = tid + kThreads * p;  // double2 index in the [16][D] slice
@@ -271,6 +276,9 @@ __global__ __launch_bounds__(kThreads) void coarse_out_kernel(DevProblem P, cons
             vv[p] = j0 + jr < nkv ? *reinterpret_cast<const double2*>(vc + (sv.kvblk_base + j0 + jr) * D + dc)
                                   : make_double2(0.0, 0.0);
         }
+    };
+    fetch(0);
+    for (int j0 = 0; j0 < nkv; j0 += kSlice) {
         __syncthreads();  // previous slice fully consumed
 #pragma unroll
         for (int e = 0; e < 4; ++e) wt[sj + e][sr] = wv[e];
@@ -280,6 +288,7 @@ __global__ __launch_bounds__(kThreads) void coarse_out_kernel(DevProblem P, cons
             *reinterpret_cast<double2*>(&vs[e / (D / 2)][2 * (e % (D / 2))]) = vv[p];
         }
         __syncthreads();
+        if (j0 + kSlice < nkv) fetch(j0 + kSlice);
 #pragma unroll 4
         for (int jj = 0; jj < kSlice; ++jj) {
             const double2 w01 = *reinterpret_cast<const double2*>(&wt[jj][4 * ty]);
