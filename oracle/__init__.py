@@ -11,4 +11,6 @@ from .vsa_oracle import (  # noqa: F401
     varlen_metadata,
     vsa_forward,
     vsa_forward_varlen,
+    forward_packed_blocks,
 )
+from . import tiles  # noqa: F401

@@ -263,10 +263,23 @@ def vsa_forward_varlen(q, k, v, seqlens_q: Sequence[int], seqlens_kv: Sequence[i
     (``[H, nQ_total, D]``), ``q2k_idx`` (``[H, nQ_total, max_k]`` int32, -1 past
     ``q2k_num``), ``q2k_num``, ``gap``, ``max_abs_dot`` (``[H, num_seqs]``).
     """
+    qsz, ksz, _, _ = varlen_metadata(seqlens_q, seqlens_kv)
+    return forward_packed_blocks(q, k, v, qsz, ksz, topk, gate, blocks)
+
+
+def forward_packed_blocks(q, k, v, qsz: Sequence[Sequence[int]], ksz: Sequence[Sequence[int]],
+                          topk: Sequence[int], gate=None,
+                          blocks: Optional[Sequence[Tuple[int, int]]] = None) -> Dict[str, np.ndarray]:
+    """The packed forward of ``vsa_forward_varlen`` for arbitrary per-block
+    valid-token counts: sequence ``s`` has query blocks of ``qsz[s]`` valid
+    tokens and KV blocks of ``ksz[s]`` valid tokens, each block at the start
+    of its own 64 slots (the layout the pages' ``variable_block_sizes``
+    describe; a partial block need not be the last one)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     H, _, D = q.shape
-    qsz, ksz, cu_q, cu_kv = varlen_metadata(seqlens_q, seqlens_kv)
-    ns = len(seqlens_q)
+    cu_q = np.concatenate([[0], np.cumsum([len(x) for x in qsz])]).astype(np.int64)
+    cu_kv = np.concatenate([[0], np.cumsum([len(x) for x in ksz])]).astype(np.int64)
+    ns = len(qsz)
     nq_tot = int(cu_q[-1])
     kk = [min(topk[s], len(ksz[s])) for s in range(ns)]
     max_k = max(kk)

@@ -20,6 +20,7 @@ import math
 import numpy as np
 import torch
 
+import oracle.tiles as TL
 import oracle.vsa_oracle as O
 
 RNG_SEED = 20261203
@@ -359,6 +360,100 @@ def pin_magnitudes(seed=12):
     assert abs(rms_c * math.sqrt(S) - 1) < 0.15, rms_c
 
 
+# ---------------------------------------------------------------------------
+# 3-D tile partition ("[kernel] Extract VSA utility functions into
+# fastvideo_kernel", Summary / Design decisions)
+# ---------------------------------------------------------------------------
+
+TILE_CASES = [((4, 4, 4), (4, 4, 4)), ((5, 6, 7), (4, 4, 4)), ((3, 9, 2), (4, 4, 4)),
+              ((8, 4, 12), (4, 4, 4)), ((6, 10, 5), (2, 4, 8)), ((1, 1, 130), (1, 1, 64)),
+              ((9, 1, 1), (8, 1, 1))]
+
+
+def pin_tile_partition_by_sorting():
+    """Tile order from an independent construction: tile number of every
+    token from its coordinates, then a stable sort by (tile, t, h, w); sizes by
+    counting; padded slot = 64 * tile + rank inside the tile."""
+    for (T, H, W), (tt, th, tw) in TILE_CASES:
+        m = TL.tile_partition(T, H, W, (tt, th, tw))
+        t, h, w = np.unravel_index(np.arange(T * H * W), (T, H, W))
+        n_h, n_w = -(-H // th), -(-W // tw)
+        tile_of = ((t // tt) * n_h + h // th) * n_w + w // tw
+        fwd = np.lexsort((w, h, t, tile_of))
+        assert np.array_equal(m["tile_partition_indices"], fwd), (T, H, W)
+        sizes = np.bincount(tile_of, minlength=-(-T // tt) * n_h * n_w)
+        assert np.array_equal(m["variable_block_sizes"], sizes)
+        first = np.concatenate([[0], np.cumsum(sizes)[:-1]])
+        tiles_in_order = tile_of[fwd]
+        rank = np.arange(len(fwd)) - first[tiles_in_order]
+        assert np.array_equal(m["non_pad_index"], 64 * tiles_in_order + rank)
+        assert np.array_equal(m["reverse_tile_partition_indices"][fwd], np.arange(len(fwd)))
+        assert sizes.sum() == T * H * W and sizes.max() <= tt * th * tw
+
+
+def pin_tile_closed_forms():
+    """Grids that are multiples of the tile: every tile is full; a 1 x 1 x N
+    grid with 1 x 1 x 64 tiles is the identity order with 64-token blocks."""
+    m = TL.tile_partition(8, 8, 12, (4, 4, 4))
+    assert (m["variable_block_sizes"] == 64).all() and len(m["variable_block_sizes"]) == 2 * 2 * 3
+    # first tile: t, h, w in 0..3, raster inside
+    want0 = [(t * 8 + h) * 12 + w for t in range(4) for h in range(4) for w in range(4)]
+    assert list(m["tile_partition_indices"][:64]) == want0
+    m = TL.tile_partition(1, 1, 200, (1, 1, 64))
+    assert np.array_equal(m["tile_partition_indices"], np.arange(200))
+    assert list(m["variable_block_sizes"]) == O.block_sizes(200)
+    assert np.array_equal(m["non_pad_index"], np.arange(200))
+
+
+def pin_tile_gather_scatter_roundtrip(seed=13):
+    rng = np.random.default_rng(seed)
+    for (T, H, W), tile in TILE_CASES[:5]:
+        x = rng.standard_normal((2, T * H * W, 3))
+        y = TL.tile_gather(x, (T, H, W), tile)
+        m = TL.tile_partition(T, H, W, tile)
+        pad = np.ones(y.shape[1], dtype=bool)
+        pad[m["non_pad_index"]] = False
+        assert (y[:, pad] == 0).all()
+        assert np.array_equal(TL.tile_scatter(y, (T, H, W), tile), x)
+
+
+def pin_video_forward_1d_equals_dense(seed=14):
+    """A 1 x 1 x S grid in 1 x 1 x 64 tiles is the dense forward on the raster
+    sequence (same blocks, same order)."""
+    rng = np.random.default_rng(seed)
+    S, D = 64 * 5 + 23, 16
+    q, k, v = (rng.standard_normal((2, 3, S, D)) for _ in range(3))
+    gate = rng.uniform(0, 1, (2, 3, S))
+    dense = O.vsa_forward(q, k, v, 3, gate)
+    vid = TL.vsa_forward_video(q, k, v, (1, 1, S), 3, gate, tile=(1, 1, 64))
+    assert np.allclose(vid["out_raster"], dense["out"], rtol=1e-12, atol=1e-13)
+    nq = len(O.block_sizes(S))
+    idx = vid["q2k_idx"].reshape(3, 2, nq, 3) - (np.arange(2) * nq)[None, :, None, None]
+    assert np.array_equal(idx.transpose(1, 0, 2, 3), dense["q2k_idx"])
+
+
+def pin_video_forward_tile_equivariance(seed=15):
+    """Permuting the tokens inside every tile of the input permutes the output
+    the same way and changes nothing else (the pool, the routing and the
+    softmax over a block do not see the order of its tokens)."""
+    rng = np.random.default_rng(seed)
+    grid, tile = (5, 6, 7), (4, 4, 4)
+    S, D = 5 * 6 * 7, 8
+    q, k, v = (rng.standard_normal((1, 2, S, D)) for _ in range(3))
+    m = TL.tile_partition(*grid, tile)
+    fwd, sizes = m["tile_partition_indices"], m["variable_block_sizes"]
+    perm = np.arange(S)  # raster index -> raster index it takes its token from
+    p0 = 0
+    for n in sizes:
+        members = fwd[p0:p0 + n]
+        perm[members] = members[rng.permutation(n)]
+        p0 += n
+    a = TL.vsa_forward_video(q, k, v, grid, 3, tile=tile)
+    b = TL.vsa_forward_video(q[:, :, perm], k[:, :, perm], v[:, :, perm], grid, 3, tile=tile)
+    assert np.array_equal(a["q2k_idx"], b["q2k_idx"])
+    assert np.allclose(a["out_raster"][:, :, perm], b["out_raster"], rtol=1e-11, atol=1e-12)
+
+
 ALL_PINS = [
     pin_block_sizes, pin_pool_partial_block, pin_two_token_closed_form,
     pin_coarse_and_routing_closed_form, pin_combine_closed_form, pin_topk_bruteforce,
@@ -366,4 +461,6 @@ ALL_PINS = [
     pin_single_block, pin_permute_within_kv_block, pin_permute_kv_blocks,
     pin_linear_in_v, pin_gate_special_values, pin_varlen_matches_per_sequence,
     pin_single_sequence_varlen_equals_dense, pin_magnitudes,
+    pin_tile_partition_by_sorting, pin_tile_closed_forms, pin_tile_gather_scatter_roundtrip,
+    pin_video_forward_1d_equals_dense, pin_video_forward_tile_equivariance,
 ]

@@ -9,6 +9,7 @@ import math
 import numpy as np
 import pytest
 
+import oracle.tiles as TL
 import oracle.vsa_oracle as O
 from tests import oracle_pins as P
 
@@ -107,6 +108,37 @@ def _varlen_no_rebase(*a, **kw):
     return r
 
 
+_tile_partition_ok = TL.tile_partition
+
+
+def _tiles_local_order_w_slowest(T, H, W, tile=(4, 4, 4)):
+    tt, th, tw = tile
+    m = _tile_partition_ok(T, H, W, tile)
+    fwd = []
+    for bt in range(-(-T // tt)):
+        for bh in range(-(-H // th)):
+            for bw in range(-(-W // tw)):
+                for lw in range(min(tw, W - bw * tw)):
+                    for lh in range(min(th, H - bh * th)):
+                        for lt in range(min(tt, T - bt * tt)):
+                            fwd.append(((bt * tt + lt) * H + (bh * th + lh)) * W + (bw * tw + lw))
+    m["tile_partition_indices"] = np.asarray(fwd)
+    m["reverse_tile_partition_indices"] = np.argsort(fwd)
+    return m
+
+
+def _tiles_unpadded(T, H, W, tile=(4, 4, 4)):
+    m = _tile_partition_ok(T, H, W, tile)
+    m["non_pad_index"] = np.arange(len(m["non_pad_index"]))
+    return m
+
+
+def _tiles_reverse_is_forward(T, H, W, tile=(4, 4, 4)):
+    m = _tile_partition_ok(T, H, W, tile)
+    m["reverse_tile_partition_indices"] = m["tile_partition_indices"].copy()
+    return m
+
+
 MISTAKES = {
     "sparse_scale_dropped": ("sparse_block", _sparse_no_scale),
     "pool_divides_by_64": ("pool", _pool_div64),
@@ -120,6 +152,9 @@ MISTAKES = {
     "combine_gate_on_sparse": ("combine", _combine_gate_on_sparse),
     "combine_drops_coarse": ("combine", _combine_drops_coarse),
     "varlen_indices_not_rebased": ("vsa_forward_varlen", _varlen_no_rebase),
+    "tiles_local_order_w_slowest": ("tiles.tile_partition", _tiles_local_order_w_slowest),
+    "tiles_not_padded": ("tiles.tile_partition", _tiles_unpadded),
+    "tiles_reverse_is_forward": ("tiles.tile_partition", _tiles_reverse_is_forward),
 }
 
 
@@ -136,6 +171,9 @@ def _some_pin_fails():
 @pytest.mark.parametrize("name", sorted(MISTAKES))
 def test_planted_mistake_is_caught(name, monkeypatch):
     attr, bad = MISTAKES[name]
-    monkeypatch.setattr(O, attr, bad)
+    mod = O
+    if attr.startswith("tiles."):
+        mod, attr = TL, attr.split(".", 1)[1]
+    monkeypatch.setattr(mod, attr, bad)
     failed = _some_pin_fails()
     assert failed, f"no pin rejects the planted mistake {name}"
