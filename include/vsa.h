@@ -277,6 +277,66 @@ int vsa_forward_varlen(const vsa_bf16 *q, const vsa_bf16 *k, const vsa_bf16 *v,
                        int32_t max_topk, int32_t heads, int32_t head_dim, int32_t block_size,
                        void *workspace, size_t workspace_bytes, vsa_stream stream);
 
+/*
+ * 3-D tile partition of video latents ("[kernel] Extract VSA utility
+ * functions into fastvideo_kernel", Summary, Design decisions and review
+ * thread: tile partition indices and their inverse, variable block sizes with
+ * the tile size a parameter, the non-pad index, one-call metadata).
+ *
+ * A latent is a T x H x W grid of tokens flattened in raster order (w
+ * fastest).  It is cut into tiles of tile_t x tile_h x tile_w tokens (at most
+ * 64; 4 x 4 x 4 is the usual choice), the last tile along an axis shorter when
+ * the extent is not a multiple; tiles are ordered in raster order of their
+ * tile coordinates and the tokens of a tile in raster order.  Each tile is
+ * one VSA block of the PACKED layout: 64 slots, its first tile-size slots
+ * valid.
+ */
+
+/*
+ * vsa_tile_partition - host index arrays of the partition.
+ * *num_tiles is always written.  Each output may be NULL:
+ *   tile_sizes [num_tiles]                      valid tokens of each tile
+ *   tile_partition_indices [T*H*W]              raster index of tiled position p
+ *   reverse_tile_partition_indices [T*H*W]      tiled position of raster index r
+ *   non_pad_index [T*H*W]                       slot 64*tile + rank of position p
+ * Errors: VSA_ERR_NULL (num_tiles NULL), VSA_ERR_SHAPE (an extent < 1, a tile
+ * of more than 64 tokens, more than 2^31 - 1 tokens or slots).
+ */
+int vsa_tile_partition(int32_t T, int32_t H, int32_t W, int32_t tile_t, int32_t tile_h, int32_t tile_w,
+                       int32_t *num_tiles, int32_t *tile_sizes, int64_t *tile_partition_indices,
+                       int64_t *reverse_tile_partition_indices, int64_t *non_pad_index);
+
+/*
+ * vsa_build_tile_metadata - the PACKED-layout metadata (same outputs and
+ * conventions as vsa_build_metadata) of num_videos videos of one grid packed
+ * one after another, queries and keys/values on the same tiles, top-k
+ * clamped to the tile count.  Errors as vsa_build_metadata and
+ * vsa_tile_partition; VSA_ERR_UNSUPPORTED beyond 4096 tiles per video.
+ */
+int vsa_build_tile_metadata(int32_t num_videos, int32_t T, int32_t H, int32_t W, int32_t tile_t,
+                            int32_t tile_h, int32_t tile_w, int32_t topk, vsa_meta_sizes *sizes,
+                            int32_t *cu_blocks_q, int32_t *cu_blocks_kv, int32_t *block_sizes_q,
+                            int32_t *block_sizes_kv, int32_t *topk_clamped);
+
+/*
+ * vsa_tile_gather - x [batch, heads, T*H*W, elems] (raster order, contiguous,
+ * bf16) -> y [heads, batch * 64 * num_tiles, elems] in tile order, video b at
+ * slots [b * 64 * num_tiles, (b + 1) * 64 * num_tiles), padding slots written
+ * with 0: the PACKED input of vsa_forward_varlen for the metadata of
+ * vsa_build_tile_metadata (elems = head_dim for q/k/v, 1 for a per-token
+ * gate, head_dim for a full gate).
+ * vsa_tile_scatter - the inverse, y -> x (padding slots are not read).
+ * Device pointers, asynchronous on stream.  elems a multiple of 8 needs
+ * 16-byte aligned tensors, otherwise 2-byte.  Errors: VSA_ERR_NULL,
+ * VSA_ERR_SHAPE, VSA_ERR_ALIGN, VSA_ERR_ALIAS (x and y overlap), VSA_ERR_HIP.
+ */
+int vsa_tile_gather(const vsa_bf16 *x, vsa_bf16 *y, int32_t batch, int32_t heads, int32_t T, int32_t H,
+                    int32_t W, int32_t tile_t, int32_t tile_h, int32_t tile_w, int32_t elems,
+                    vsa_stream stream);
+int vsa_tile_scatter(const vsa_bf16 *y, vsa_bf16 *x, int32_t batch, int32_t heads, int32_t T, int32_t H,
+                     int32_t W, int32_t tile_t, int32_t tile_h, int32_t tile_w, int32_t elems,
+                     vsa_stream stream);
+
 /* Text for a status code (static storage). */
 const char *vsa_status_string(int status);
 

@@ -258,3 +258,66 @@ def test_layout_maps_on_cpu(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "layout checks passed" in r.stdout
+
+
+# ---------------------------------------------------------------------------
+# 3-D tile partition (host side)
+# ---------------------------------------------------------------------------
+
+TILE_CASES = [((4, 4, 4), (4, 4, 4)), ((5, 6, 7), (4, 4, 4)), ((3, 9, 2), (4, 4, 4)),
+              ((8, 4, 12), (4, 4, 4)), ((6, 10, 5), (2, 4, 8)), ((1, 1, 130), (1, 1, 64)),
+              ((9, 1, 1), (8, 1, 1)), ((13, 17, 11), (4, 4, 4))]
+
+
+@pytest.mark.parametrize("grid,tile", TILE_CASES)
+def test_tile_partition_matches_oracle(lib, grid, tile):
+    import oracle.tiles as TL
+    import video_sparse_attention_amd as vsa
+    got = vsa.tile_partition(*grid, tile)
+    want = TL.tile_partition(*grid, tile)
+    for key in want:
+        assert np.array_equal(got[key].numpy(), want[key]), key
+
+
+@pytest.mark.parametrize("grid,tile", TILE_CASES[:4])
+def test_tile_metadata_is_packed_layout(lib, grid, tile):
+    import oracle.tiles as TL
+    import video_sparse_attention_amd as vsa
+    m = vsa.vsa_build_tile_metadata(3, grid, 7, tile)
+    sizes = TL.tile_partition(*grid, tile)["variable_block_sizes"]
+    n = len(sizes)
+    assert m.sizes.num_seqs == 3 and m.sizes.total_q_blocks == 3 * n == m.sizes.total_kv_blocks
+    assert m.cu_blocks_q.tolist() == [0, n, 2 * n, 3 * n] == m.cu_blocks_kv.tolist()
+    assert np.array_equal(m.block_sizes_q.numpy(), np.tile(sizes, 3))
+    assert np.array_equal(m.block_sizes_kv.numpy(), np.tile(sizes, 3))
+    assert m.topk.tolist() == [min(7, n)] * 3 and m.sizes.max_topk == min(7, n)
+
+
+def test_tile_errors(lib):
+    nt = ctypes.c_int32(0)
+    E = _abi
+    assert lib.vsa_tile_partition(4, 4, 4, 4, 4, 4, None, None, None, None, None) == E.VSA_ERR_NULL
+    assert lib.vsa_tile_partition(0, 4, 4, 4, 4, 4, ctypes.byref(nt), None, None, None, None) == E.VSA_ERR_SHAPE
+    assert lib.vsa_tile_partition(4, 4, 4, 8, 4, 4, ctypes.byref(nt), None, None, None, None) == E.VSA_ERR_SHAPE
+    assert lib.vsa_tile_partition(4, 4, 4, 4, 0, 4, ctypes.byref(nt), None, None, None, None) == E.VSA_ERR_SHAPE
+    sizes = _abi.VsaMetaSizes()
+    assert lib.vsa_build_tile_metadata(0, 4, 4, 4, 4, 4, 4, 1, ctypes.byref(sizes),
+                                       None, None, None, None, None) == E.VSA_ERR_SHAPE
+    assert lib.vsa_build_tile_metadata(1, 4, 4, 4, 4, 4, 4, 0, ctypes.byref(sizes),
+                                       None, None, None, None, None) == E.VSA_ERR_TOPK
+    assert lib.vsa_build_tile_metadata(1, 4, 4, 4, 4, 4, 4, 1, None,
+                                       None, None, None, None, None) == E.VSA_ERR_NULL
+    assert lib.vsa_build_tile_metadata(1, 64, 64, 68, 4, 4, 4, 1, ctypes.byref(sizes),
+                                       None, None, None, None, None) == E.VSA_ERR_UNSUPPORTED
+    # gather / scatter validation (fake device addresses are never touched)
+    g = lambda *a: lib.vsa_tile_gather(*a)
+    assert g(None, O_, 1, 2, 4, 4, 4, 4, 4, 4, 128, None) == E.VSA_ERR_NULL
+    assert g(A, ctypes.c_void_p(FAKE + 8), 1, 2, 4, 4, 4, 4, 4, 4, 128, None) in (E.VSA_ERR_ALIGN, E.VSA_ERR_ALIAS)
+    assert g(A, ctypes.c_void_p(FAKE + (3 << 32) + 8), 1, 2, 4, 4, 4, 4, 4, 4, 128, None) == E.VSA_ERR_ALIGN
+    assert g(A, ctypes.c_void_p(FAKE + 4096), 1, 2, 4, 4, 4, 4, 4, 4, 128, None) == E.VSA_ERR_ALIAS
+    assert g(A, O_, 0, 2, 4, 4, 4, 4, 4, 4, 128, None) == E.VSA_ERR_SHAPE
+    assert g(A, O_, 1, 2, 4, 4, 4, 4, 4, 4, 0, None) == E.VSA_ERR_SHAPE
+    assert g(A, O_, 1, 2, 4, 4, 4, 3, 5, 5, 128, None) == E.VSA_ERR_SHAPE
+    assert lib.vsa_tile_scatter(A, ctypes.c_void_p(FAKE + 2), 1, 2, 4, 4, 4, 4, 4, 4, 1, None) == E.VSA_ERR_ALIAS
+    assert lib.vsa_tile_scatter(A, ctypes.c_void_p(FAKE + (3 << 32) + 1), 1, 2, 4, 4, 4, 4, 4, 4, 1,
+                                None) == E.VSA_ERR_ALIGN

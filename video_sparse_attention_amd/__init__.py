@@ -14,7 +14,13 @@ from .binding import (  # noqa: E402,F401
     block_shapes,
     dense_problem,
     token_shapes,
+    DEFAULT_TILE,
+    tile_gather,
+    tile_partition,
+    tile_scatter,
     vsa_build_metadata,
+    vsa_build_tile_metadata,
+    vsa_forward_video,
     vsa_coarse_topk,
     vsa_combine,
     vsa_forward,
@@ -26,6 +32,7 @@ from .binding import (  # noqa: E402,F401
 
 __all__ = [
     "BLOCK", "VarlenMeta", "VsaError", "alloc_workspace", "block_shapes", "dense_problem",
-    "token_shapes", "vsa_build_metadata", "vsa_coarse_topk", "vsa_combine", "vsa_forward",
+    "token_shapes", "DEFAULT_TILE", "tile_gather", "tile_partition", "tile_scatter",
+    "vsa_build_tile_metadata", "vsa_forward_video", "vsa_build_metadata", "vsa_coarse_topk", "vsa_combine", "vsa_forward",
     "vsa_forward_varlen", "vsa_sparse_attn_combine", "vsa_sparse_attn_from_indices", "vsa_workspace_size",
 ]

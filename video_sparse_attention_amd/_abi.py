@@ -63,6 +63,11 @@ SIGNATURES = {
     "vsa_forward_varlen": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
                                  vp, vp, vp, vp, vp,
                                  i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]),
+    "vsa_tile_partition": (i32, [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
+    "vsa_build_tile_metadata": (i32, [i32, i32, i32, i32, i32, i32, i32, i32,
+                                      ctypes.POINTER(VsaMetaSizes), vp, vp, vp, vp, vp]),
+    "vsa_tile_gather": (i32, [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp]),
+    "vsa_tile_scatter": (i32, [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp]),
     "vsa_status_string": (ctypes.c_char_p, [i32]),
     "vsa_last_error": (ctypes.c_char_p, []),
     "vsa_version": (ctypes.c_char_p, []),

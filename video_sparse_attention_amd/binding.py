@@ -317,3 +317,120 @@ def vsa_forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, meta: 
         s.total_kv_blocks, s.max_q_blocks, s.max_kv_blocks, s.max_topk, H, D, BLOCK,
         _ptr(workspace), workspace.numel(), _stream(q.device)), "vsa_forward_varlen")
     return (out, *aux) if return_aux else out
+
+
+# ---------------------------------------------------------------------------
+# video latents: 3-D tile partition, gather / scatter, tiled forward
+# ---------------------------------------------------------------------------
+
+DEFAULT_TILE = (4, 4, 4)
+
+
+def tile_partition(T: int, H: int, W: int, tile=DEFAULT_TILE) -> dict:
+    """Host index arrays of the 3-D tile partition (vsa_tile_partition):
+    ``tile_partition_indices``, ``reverse_tile_partition_indices``,
+    ``variable_block_sizes`` and ``non_pad_index`` (CPU int64 tensors)."""
+    lib = _abi.load()
+    nt = ctypes.c_int32(0)
+    _abi.check(lib.vsa_tile_partition(T, H, W, *tile, ctypes.byref(nt), None, None, None, None),
+               "vsa_tile_partition")
+    S = T * H * W
+    sizes = torch.zeros(nt.value, dtype=torch.int32)
+    fwd = torch.zeros(S, dtype=torch.int64)
+    rev = torch.zeros(S, dtype=torch.int64)
+    nonpad = torch.zeros(S, dtype=torch.int64)
+    _abi.check(lib.vsa_tile_partition(T, H, W, *tile, ctypes.byref(nt), _ptr(sizes), _ptr(fwd), _ptr(rev),
+                                      _ptr(nonpad)), "vsa_tile_partition")
+    return dict(tile_partition_indices=fwd, reverse_tile_partition_indices=rev,
+                variable_block_sizes=sizes.to(torch.int64), non_pad_index=nonpad)
+
+
+def vsa_build_tile_metadata(num_videos: int, grid, topk: int, tile=DEFAULT_TILE, device=None) -> VarlenMeta:
+    """Packed-layout metadata of ``num_videos`` videos of one ``grid = (T, H,
+    W)``, one block per tile (vsa_build_tile_metadata)."""
+    lib = _abi.load()
+    T, H, W = grid
+    sizes = VsaMetaSizes()
+    _abi.check(lib.vsa_build_tile_metadata(num_videos, T, H, W, *tile, topk, ctypes.byref(sizes),
+                                           None, None, None, None, None), "vsa_build_tile_metadata")
+    n = num_videos
+    cu_q = torch.zeros(n + 1, dtype=torch.int32)
+    cu_kv = torch.zeros(n + 1, dtype=torch.int32)
+    bs_q = torch.zeros(sizes.total_q_blocks, dtype=torch.int32)
+    bs_kv = torch.zeros(sizes.total_kv_blocks, dtype=torch.int32)
+    tkc = torch.zeros(n, dtype=torch.int32)
+    _abi.check(lib.vsa_build_tile_metadata(num_videos, T, H, W, *tile, topk, ctypes.byref(sizes), _ptr(cu_q),
+                                           _ptr(cu_kv), _ptr(bs_q), _ptr(bs_kv), _ptr(tkc)),
+               "vsa_build_tile_metadata")
+    S = T * H * W
+    meta = VarlenMeta(sizes, [S] * n, [S] * n, cu_q, cu_kv, bs_q, bs_kv, tkc)
+    return meta.to(device) if device is not None else meta
+
+
+def _tile_count(grid, tile) -> int:
+    return -(-grid[0] // tile[0]) * -(-grid[1] // tile[1]) * -(-grid[2] // tile[2])
+
+
+def tile_gather(x: torch.Tensor, grid, tile=DEFAULT_TILE, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``x`` ``[B, heads, T*H*W(, E)]`` raster -> ``[heads, B * 64 * n_tiles(, E)]``
+    tile order with zero padding (vsa_tile_gather)."""
+    T, H, W = grid
+    squeeze = x.dim() == 3
+    if x.dim() not in (3, 4) or x.shape[2] != T * H * W:
+        raise ValueError(f"x must be [B, heads, {T * H * W}(, E)], got {tuple(x.shape)}")
+    _need(x, "x", torch.bfloat16)
+    B, Hh = x.shape[0], x.shape[1]
+    E = 1 if squeeze else x.shape[3]
+    slots = BLOCK * _tile_count(grid, tile)
+    shape = (Hh, B * slots) if squeeze else (Hh, B * slots, E)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, shape)
+    _abi.check(_abi.load().vsa_tile_gather(_ptr(x), _ptr(out), B, Hh, T, H, W, *tile, E, _stream(x.device)),
+               "vsa_tile_gather")
+    return out
+
+
+def tile_scatter(y: torch.Tensor, grid, batch: int, tile=DEFAULT_TILE,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Inverse of ``tile_gather``: ``[heads, B * 64 * n_tiles(, E)]`` ->
+    ``[B, heads, T*H*W(, E)]`` (vsa_tile_scatter)."""
+    T, H, W = grid
+    slots = BLOCK * _tile_count(grid, tile)
+    squeeze = y.dim() == 2
+    if y.dim() not in (2, 3) or y.shape[1] != batch * slots:
+        raise ValueError(f"y must be [heads, {batch * slots}(, E)], got {tuple(y.shape)}")
+    _need(y, "y", torch.bfloat16)
+    Hh = y.shape[0]
+    E = 1 if squeeze else y.shape[2]
+    shape = (batch, Hh, T * H * W) if squeeze else (batch, Hh, T * H * W, E)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=y.device)
+    _need(out, "out", torch.bfloat16, shape)
+    _abi.check(_abi.load().vsa_tile_scatter(_ptr(y), _ptr(out), batch, Hh, T, H, W, *tile, E, _stream(y.device)),
+               "vsa_tile_scatter")
+    return out
+
+
+def vsa_forward_video(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid, topk: int,
+                      gate: Optional[torch.Tensor] = None, tile=DEFAULT_TILE, *, return_aux: bool = False):
+    """VSA forward of ``B`` videos of one ``grid = (T, H, W)`` given in raster
+    order, ``q``/``k``/``v`` ``[B, heads, T*H*W, D]``: the tokens are gathered
+    into tile order, the forward runs with one block per tile
+    (vsa_forward_varlen with vsa_build_tile_metadata) and the output is
+    scattered back to raster order.  ``gate``: None, ``[B, heads, T*H*W]`` or
+    ``[B, heads, T*H*W, D]`` (contiguous).  With ``return_aux`` also returns
+    ``(out_c, q2k_idx, q2k_num)`` in the packed tile layout."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, heads, T*H*W, D]")
+    B, Hh, S, D = q.shape
+    for name, t in (("k", k), ("v", v)):
+        if tuple(t.shape) != tuple(q.shape):
+            raise ValueError(f"{name} must have the shape of q {tuple(q.shape)}, got {tuple(t.shape)}")
+    meta = vsa_build_tile_metadata(B, grid, topk, tile, device=q.device)
+    gq, gk, gv = (tile_gather(t, grid, tile) for t in (q, k, v))
+    gg = None if gate is None else tile_gather(gate, grid, tile)
+    res = vsa_forward_varlen(gq, gk, gv, meta, gg, return_aux=return_aux)
+    out_t = res[0] if return_aux else res
+    out = tile_scatter(out_t, grid, B, tile)
+    return (out, *res[1:]) if return_aux else out

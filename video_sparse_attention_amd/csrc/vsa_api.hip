@@ -209,6 +209,40 @@ int run_coarse(const vsa::DevProblem& P, const uint16_t* q, const uint16_t* k, c
                       "coarse/top-k launch");
 }
 
+int check_tiles(int32_t T, int32_t H, int32_t W, int32_t tt, int32_t th, int32_t tw, vsa::TileGrid* g) {
+    if (T < 1 || H < 1 || W < 1) return fail(VSA_ERR_SHAPE, "grid extents must be >= 1 (got %d x %d x %d)", T, H, W);
+    if (tt < 1 || th < 1 || tw < 1 || (int64_t)tt * th * tw > VSA_BLOCK)
+        return fail(VSA_ERR_SHAPE, "tile %d x %d x %d: extents must be >= 1 and the tile at most %d tokens", tt, th,
+                    tw, VSA_BLOCK);
+    if ((int64_t)T * H * W > 0x7fffffffLL) return fail(VSA_ERR_SHAPE, "grid exceeds 2^31 - 1 tokens");
+    *g = vsa::make_tile_grid(T, H, W, tt, th, tw);
+    if ((int64_t)g->ntiles * VSA_BLOCK > 0x7fffffffLL) return fail(VSA_ERR_SHAPE, "padded length exceeds 2^31 slots");
+    return VSA_OK;
+}
+
+int tile_copy(const vsa_bf16* src, vsa_bf16* dst, int32_t batch, int32_t heads, int32_t T, int32_t H, int32_t W,
+              int32_t tt, int32_t th, int32_t tw, int32_t elems, bool scatter, vsa_stream stream) {
+    vsa::TileGrid g;
+    int rc = check_tiles(T, H, W, tt, th, tw, &g);
+    if (rc) return rc;
+    if (batch < 1 || heads < 1 || elems < 1)
+        return fail(VSA_ERR_SHAPE, "batch, heads and elems must be >= 1 (got %d, %d, %d)", batch, heads, elems);
+    if ((int64_t)batch * g.ntiles * VSA_BLOCK > 0x7fffffffLL)
+        return fail(VSA_ERR_SHAPE, "packed length exceeds 2^31 slots");
+    if (!src || !dst) return fail(VSA_ERR_NULL, "source or destination is NULL");
+    const bool vec = elems % 8 == 0;
+    const uintptr_t mask = vec ? 15u : 1u;
+    if (((uintptr_t)src & mask) || ((uintptr_t)dst & mask))
+        return fail(VSA_ERR_ALIGN, "tensors must be %d-byte aligned", vec ? 16 : 2);
+    const int64_t raster_bytes = 2LL * batch * heads * ((int64_t)T * H * W) * elems;
+    const int64_t tiled_bytes = 2LL * batch * heads * ((int64_t)g.ntiles * VSA_BLOCK) * elems;
+    const int64_t sb = scatter ? tiled_bytes : raster_bytes, db = scatter ? raster_bytes : tiled_bytes;
+    if (overlaps(src, sb, dst, db)) return fail(VSA_ERR_ALIAS, "source and destination overlap");
+    rc = hip_status(vsa::launch_tile_copy(g, src, dst, batch, heads, elems, scatter, (hipStream_t)stream),
+                    scatter ? "tile scatter launch" : "tile gather launch");
+    return rc ? rc : ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -444,6 +478,78 @@ int vsa_forward_varlen(const vsa_bf16* q, const vsa_bf16* k, const vsa_bf16* v, 
     pr.topk_per_seq = topk_per_seq;
     return forward_common(&pr, q, k, v, gate, gate_mode, gate_strides, out, q2k_idx, q2k_num, out_c, workspace,
                           workspace_bytes, stream);
+}
+
+int vsa_tile_partition(int32_t T, int32_t H, int32_t W, int32_t tile_t, int32_t tile_h, int32_t tile_w,
+                       int32_t* num_tiles, int32_t* tile_sizes, int64_t* tile_partition_indices,
+                       int64_t* reverse_tile_partition_indices, int64_t* non_pad_index) {
+    if (!num_tiles) return fail(VSA_ERR_NULL, "num_tiles is NULL");
+    *num_tiles = 0;
+    vsa::TileGrid g;
+    int rc = check_tiles(T, H, W, tile_t, tile_h, tile_w, &g);
+    if (rc) return rc;
+    *num_tiles = g.ntiles;
+    int64_t p = 0;
+    for (int b = 0; b < g.ntiles; ++b) {
+        int et, eh, ew;
+        const int n = vsa::tile_extents(g, b, et, eh, ew);
+        if (tile_sizes) tile_sizes[b] = n;
+        for (int u = 0; u < n; ++u, ++p) {
+            const int64_t r = vsa::tile_token_raster(g, b, u, eh, ew);
+            if (tile_partition_indices) tile_partition_indices[p] = r;
+            if (reverse_tile_partition_indices) reverse_tile_partition_indices[r] = p;
+            if (non_pad_index) non_pad_index[p] = (int64_t)VSA_BLOCK * b + u;
+        }
+    }
+    return ok();
+}
+
+int vsa_build_tile_metadata(int32_t num_videos, int32_t T, int32_t H, int32_t W, int32_t tile_t, int32_t tile_h,
+                            int32_t tile_w, int32_t topk, vsa_meta_sizes* sizes, int32_t* cu_blocks_q,
+                            int32_t* cu_blocks_kv, int32_t* block_sizes_q, int32_t* block_sizes_kv,
+                            int32_t* topk_clamped) {
+    if (!sizes) return fail(VSA_ERR_NULL, "sizes is NULL");
+    *sizes = vsa_meta_sizes{};
+    vsa::TileGrid g;
+    int rc = check_tiles(T, H, W, tile_t, tile_h, tile_w, &g);
+    if (rc) return rc;
+    if (num_videos < 1) return fail(VSA_ERR_SHAPE, "empty batch (num_videos=%d)", num_videos);
+    if (topk < 1) return fail(VSA_ERR_TOPK, "topk must be >= 1 (got %d)", topk);
+    if (g.ntiles > vsa::kMaxKvBlocks)
+        return fail(VSA_ERR_UNSUPPORTED, "%d tiles per video exceeds %d", g.ntiles, vsa::kMaxKvBlocks);
+    const int nout = !!cu_blocks_q + !!cu_blocks_kv + !!block_sizes_q + !!block_sizes_kv + !!topk_clamped;
+    if (nout != 0 && nout != 5) return fail(VSA_ERR_NULL, "pass all five output arrays or none");
+    const int64_t total = (int64_t)num_videos * g.ntiles;
+    if (total * VSA_BLOCK > 0x7fffffffLL) return fail(VSA_ERR_SHAPE, "packed length exceeds 2^31 slots");
+    const int32_t kk = std::min(topk, g.ntiles);
+    sizes->num_seqs = num_videos;
+    sizes->total_q_blocks = (int32_t)total;
+    sizes->total_kv_blocks = (int32_t)total;
+    sizes->max_q_blocks = g.ntiles;
+    sizes->max_kv_blocks = g.ntiles;
+    sizes->max_topk = kk;
+    sizes->q_slots = total * VSA_BLOCK;
+    sizes->kv_slots = total * VSA_BLOCK;
+    if (nout == 0) return ok();
+    for (int s = 0; s <= num_videos; ++s) cu_blocks_q[s] = cu_blocks_kv[s] = s * g.ntiles;
+    for (int s = 0; s < num_videos; ++s) {
+        topk_clamped[s] = kk;
+        for (int b = 0; b < g.ntiles; ++b) {
+            int et, eh, ew;
+            block_sizes_q[s * g.ntiles + b] = block_sizes_kv[s * g.ntiles + b] = vsa::tile_extents(g, b, et, eh, ew);
+        }
+    }
+    return ok();
+}
+
+int vsa_tile_gather(const vsa_bf16* x, vsa_bf16* y, int32_t batch, int32_t heads, int32_t T, int32_t H,
+                    int32_t W, int32_t tile_t, int32_t tile_h, int32_t tile_w, int32_t elems, vsa_stream stream) {
+    return tile_copy(x, y, batch, heads, T, H, W, tile_t, tile_h, tile_w, elems, false, stream);
+}
+
+int vsa_tile_scatter(const vsa_bf16* y, vsa_bf16* x, int32_t batch, int32_t heads, int32_t T, int32_t H,
+                     int32_t W, int32_t tile_t, int32_t tile_h, int32_t tile_w, int32_t elems, vsa_stream stream) {
+    return tile_copy(y, x, batch, heads, T, H, W, tile_t, tile_h, tile_w, elems, true, stream);
 }
 
 }  // extern "C"

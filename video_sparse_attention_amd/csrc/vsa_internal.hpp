@@ -95,6 +95,46 @@ __device__ __forceinline__ int seq_of_qblock(const DevProblem& P, int g) {
 }
 
 // ---------------------------------------------------------------------------
+// 3-D tile partition of a T x H x W token grid (raster order, w fastest) into
+// tiles of tt x th x tw tokens: tiles in raster order of their tile
+// coordinates (edge tiles shorter), tokens in raster order inside a tile.
+// ("[kernel] Extract VSA utility functions into fastvideo_kernel", Summary.)
+// ---------------------------------------------------------------------------
+struct TileGrid {
+    int T, H, W;     // token grid
+    int tt, th, tw;  // tile extents
+    int nt, nh, nw;  // tiles along each axis
+    int ntiles;
+};
+
+__host__ __device__ inline TileGrid make_tile_grid(int T, int H, int W, int tt, int th, int tw) {
+    TileGrid g;
+    g.T = T; g.H = H; g.W = W;
+    g.tt = tt; g.th = th; g.tw = tw;
+    g.nt = (T + tt - 1) / tt;
+    g.nh = (H + th - 1) / th;
+    g.nw = (W + tw - 1) / tw;
+    g.ntiles = g.nt * g.nh * g.nw;
+    return g;
+}
+
+// Extents of tile b along t, h, w; returns its token count.
+__host__ __device__ inline int tile_extents(const TileGrid& g, int b, int& et, int& eh, int& ew) {
+    const int bt = b / (g.nh * g.nw), bh = (b / g.nw) % g.nh, bw = b % g.nw;
+    et = g.T - bt * g.tt < g.tt ? g.T - bt * g.tt : g.tt;
+    eh = g.H - bh * g.th < g.th ? g.H - bh * g.th : g.th;
+    ew = g.W - bw * g.tw < g.tw ? g.W - bw * g.tw : g.tw;
+    return et * eh * ew;
+}
+
+// Raster index of the u-th token (u < tile size) of tile b.
+__host__ __device__ inline int64_t tile_token_raster(const TileGrid& g, int b, int u, int eh, int ew) {
+    const int bt = b / (g.nh * g.nw), bh = (b / g.nw) % g.nh, bw = b % g.nw;
+    const int lt = u / (eh * ew), lh = (u / ew) % eh, lw = u % ew;
+    return ((int64_t)(bt * g.tt + lt) * g.H + (bh * g.th + lh)) * g.W + (bw * g.tw + lw);
+}
+
+// ---------------------------------------------------------------------------
 // launchers (one per kernel family; each returns hipError_t of the launch)
 // ---------------------------------------------------------------------------
 hipError_t launch_pool(const DevProblem& P, const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -111,6 +151,10 @@ hipError_t launch_sparse_attn_combine(const DevProblem& P, const uint16_t* q, co
                                       const uint16_t* v, const int* idx, const int* num, const float* out_c,
                                       const uint16_t* gate, int mode, int64_t gs0, int64_t gs1, int64_t gs2,
                                       uint16_t* out, hipStream_t st);
+// gather (scatter = false): x [B, Hh, T*H*W, elems] raster -> y [Hh, B * 64 *
+// ntiles, elems] tile order with zero padding; scatter: the inverse.
+hipError_t launch_tile_copy(const TileGrid& g, const uint16_t* src, uint16_t* dst, int B, int Hh, int elems,
+                            bool scatter, hipStream_t st);
 hipError_t launch_combine(const DevProblem& P, const float* out_c, const uint16_t* gate, int mode,
                           int64_t gs0, int64_t gs1, int64_t gs2, uint16_t* out, hipStream_t st);
 
