@@ -42,7 +42,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="large", choices=["large", "varlen_many"])
+    ap.add_argument("--workload", default="large", choices=["large", "varlen_many", "video"],
+                    help="large (the default line), varlen_many, or video: the large shape as an "
+                         "11 x 32 x 44 latent in 4 x 4 x 4 tiles, gathered from and scattered to "
+                         "raster order")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0,
                     help="wall-time budget of the oracle sample (whole heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -121,6 +124,84 @@ def cpu_baseline(inp, budget_s: float):
                       f"{t_total:.1f} s; rate scaled by the same effective-FLOP formula"}
 
 
+def video_bench(args, torch, synth, vsa):
+    """The large shape as a video latent (11 x 32 x 44 tokens, 4 x 4 x 4 tiles,
+    partial along t): one step = gather q, k, v and the gate into tile order,
+    coarse stage, sparse attention with the fused combine, scatter of the
+    output back to raster order."""
+    dev = torch.device("cuda:0")
+    grid, tile, H, D = (11, 32, 44), (4, 4, 4), 56, 128
+    S = grid[0] * grid[1] * grid[2]
+    n_tiles = -(-grid[0] // 4) * -(-grid[1] // 4) * -(-grid[2] // 4)
+    topk = -(-n_tiles // 5)
+    inp = synth.dense_inputs(1, H, S, D, topk, seed=1006, gated=True)
+    q, k, v, gate = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.gate))
+    meta = vsa.vsa_build_tile_metadata(1, grid, topk, tile, device=dev)
+    prob = meta.problem(H, D)
+    slots = 64 * n_tiles
+    gq, gk, gv = (torch.empty(H, slots, D, dtype=torch.bfloat16, device=dev) for _ in range(3))
+    gg = torch.empty(H, slots, dtype=torch.bfloat16, device=dev)
+    cs, isz, ns = vsa.block_shapes(prob)
+    out_c = torch.empty(cs, dtype=torch.float32, device=dev)
+    idx = torch.empty(isz, dtype=torch.int32, device=dev)
+    num = torch.empty(ns, dtype=torch.int32, device=dev)
+    out_t = torch.empty(H, slots, D, dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(q)
+    ws = vsa.alloc_workspace(prob, dev)
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        for src, dst in ((q, gq), (k, gk), (v, gv), (gate, gg)):
+            vsa.tile_gather(src, grid, tile, out=dst)
+        if ev: ev[1].record()
+        vsa.vsa_coarse_topk(prob, gq, gk, gv, out_c, idx, num, ws)
+        if ev: ev[2].record()
+        vsa.vsa_sparse_attn_combine(prob, gq, gk, gv, idx, num, out_c, gg, out_t)
+        if ev: ev[3].record()
+        vsa.tile_scatter(out_t, grid, 1, tile, out=out)
+        if ev: ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ("gather", "coarse", "sparse", "scatter")
+    avg = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, n in enumerate(names)}
+    ms_per_step = wall * 1e3 / args.steps
+    flops = 4.0 * H * n_tiles * topk * 64 * 64 * D
+    sparse_tf = flops / (avg["sparse"] * 1e-3) / 1e12
+    gather_bytes = 3 * (2 * H * S * D + 2 * H * slots * D) + 2 * H * S + 2 * H * slots
+    scatter_bytes = 2 * H * S * D * 2
+    res = {
+        "metric": METRIC,
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"video latent {grid[0]}x{grid[1]}x{grid[2]} = {S} tokens in 4x4x4 tiles "
+                               f"({n_tiles} tiles, partial along t), H={H} D={D}, top-{topk}, token gate; "
+                               "gather + forward + scatter",
+                   "heads": H, "head_dim": D, "grid": list(grid), "tile": list(tile), "topk": topk,
+                   "gate": "token"},
+        "roofline": {"bound": "mfma", "kernel": "sparse_attn_kernel<128, 1>", "achieved": round(sparse_tf, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(sparse_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "avg_launch_ms": round(avg["sparse"], 4), "flops_per_launch": flops},
+        "kernels": {"tile_gather_ms": round(avg["gather"], 4),
+                    "tile_gather_GBps": round(gather_bytes / (avg["gather"] * 1e-3) / 1e9, 1),
+                    "coarse_topk_stage_ms": round(avg["coarse"], 4),
+                    "sparse_attn_combine_ms": round(avg["sparse"], 4),
+                    "tile_scatter_ms": round(avg["scatter"], 4),
+                    "tile_scatter_GBps": round(scatter_bytes / (avg["scatter"] * 1e-3) / 1e9, 1)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -138,6 +219,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "video":
+        video_bench(args, torch, synth, vsa)
+        return
     inp = synth.workload(args.workload)
 
     if isinstance(inp, synth.DenseInputs):
