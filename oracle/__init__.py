@@ -14,3 +14,4 @@ from .vsa_oracle import (  # noqa: F401
     forward_packed_blocks,
 )
 from . import tiles  # noqa: F401
+from . import vsa_backward  # noqa: F401

@@ -21,6 +21,7 @@ import numpy as np
 import torch
 
 import oracle.tiles as TL
+import oracle.vsa_backward as BW
 import oracle.vsa_oracle as O
 
 RNG_SEED = 20261203
@@ -454,6 +455,65 @@ def pin_video_forward_tile_equivariance(seed=15):
     assert np.allclose(a["out_raster"][:, :, perm], b["out_raster"], rtol=1e-11, atol=1e-12)
 
 
+# ---------------------------------------------------------------------------
+# backward ("[kernel] Add varlen support for block-sparse attention", Test
+# plan: backward; "[chore] release fastvideo-kernel 0.3.0": forward and
+# backward of the block-sparse attention)
+# ---------------------------------------------------------------------------
+
+def _t64(x, grad=False):
+    return torch.tensor(np.asarray(x, dtype=np.float64), dtype=torch.float64, requires_grad=grad)
+
+
+def pin_backward_forward_matches_oracle(seed=16):
+    """The differentiable restatement computes the oracle's forward."""
+    rng = np.random.default_rng(seed)
+    B, H, S, D = 2, 2, 64 * 3 + 21, 8
+    q, k, v = (rng.standard_normal((B, H, S, D)) for _ in range(3))
+    for gate in (None, rng.uniform(0, 1, (B, H, S)), rng.uniform(0, 1, (B, H, S, D))):
+        ref = O.vsa_forward(q, k, v, 2, gate)
+        out, out_c, out_s = BW.forward_torch(_t64(q), _t64(k), _t64(v), None if gate is None else _t64(gate),
+                                             ref["q2k_idx"])
+        assert np.allclose(out.detach().numpy(), ref["out"], rtol=1e-12, atol=1e-13)
+        assert np.allclose(out_c.detach().numpy(), ref["out_c"], rtol=1e-12, atol=1e-13)
+        assert np.allclose(out_s.detach().numpy(), ref["out_s"], rtol=1e-12, atol=1e-13)
+
+
+def pin_backward_gradcheck(seed=17):
+    """Gradients of the restatement against finite differences (routing fixed)."""
+    rng = np.random.default_rng(seed)
+    B, H, S, D = 1, 1, 64 + 6, 3
+    q, k, v = (rng.standard_normal((B, H, S, D)) for _ in range(3))
+    gate = rng.uniform(0.2, 0.8, (B, H, S))
+    idx = O.vsa_forward(q, k, v, 1, gate)["q2k_idx"]
+    w = _t64(rng.standard_normal((B, H, S, D)))
+    f = lambda a, b_, c, g: (BW.forward_torch(a, b_, c, g, idx)[0] * w).sum()
+    assert torch.autograd.gradcheck(f, (_t64(q, True), _t64(k, True), _t64(v, True), _t64(gate, True)),
+                                    eps=1e-6, atol=1e-7, rtol=1e-5)
+
+
+def pin_backward_dense_equivalence(seed=18):
+    """top-k = every block: the sparse branch's gradients are those of
+    dense softmax attention (torch's scaled_dot_product_attention, float64)
+    and the coarse branch's those of dense attention on the block means."""
+    rng = np.random.default_rng(seed)
+    B, H, S, D = 1, 2, 64 * 3, 8
+    q, k, v = (rng.standard_normal((B, H, S, D)) for _ in range(3))
+    w = rng.standard_normal((B, H, S, D))
+    wc = rng.standard_normal((B, H, 3, D))
+    idx = O.vsa_forward(q, k, v, 3)["q2k_idx"]
+    tq, tk, tv = _t64(q, True), _t64(k, True), _t64(v, True)
+    _, out_c, out_s = BW.forward_torch(tq, tk, tv, None, idx)
+    ((out_s * _t64(w)).sum() + (out_c * _t64(wc)).sum()).backward()
+    rq, rk, rv = _t64(q, True), _t64(k, True), _t64(v, True)
+    ref_s = torch.nn.functional.scaled_dot_product_attention(rq, rk, rv)
+    pool = lambda x: torch.nn.functional.avg_pool1d(x.reshape(B * H, S, D).transpose(1, 2), 64).transpose(1, 2).reshape(B, H, 3, D)
+    ref_c = torch.nn.functional.scaled_dot_product_attention(pool(rq), pool(rk), pool(rv))
+    ((ref_s * _t64(w)).sum() + (ref_c * _t64(wc)).sum()).backward()
+    for a, b_ in ((tq, rq), (tk, rk), (tv, rv)):
+        assert np.allclose(a.grad.numpy(), b_.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
 ALL_PINS = [
     pin_block_sizes, pin_pool_partial_block, pin_two_token_closed_form,
     pin_coarse_and_routing_closed_form, pin_combine_closed_form, pin_topk_bruteforce,
@@ -463,4 +523,5 @@ ALL_PINS = [
     pin_single_sequence_varlen_equals_dense, pin_magnitudes,
     pin_tile_partition_by_sorting, pin_tile_closed_forms, pin_tile_gather_scatter_roundtrip,
     pin_video_forward_1d_equals_dense, pin_video_forward_tile_equivariance,
+    pin_backward_forward_matches_oracle, pin_backward_gradcheck, pin_backward_dense_equivalence,
 ]

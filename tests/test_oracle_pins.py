@@ -7,9 +7,11 @@ pin must reject it.
 import math
 
 import numpy as np
+import torch
 import pytest
 
 import oracle.tiles as TL
+import oracle.vsa_backward as BW
 import oracle.vsa_oracle as O
 from tests import oracle_pins as P
 
@@ -139,6 +141,23 @@ def _tiles_reverse_is_forward(T, H, W, tile=(4, 4, 4)):
     return m
 
 
+_forward_torch_ok = BW.forward_torch
+
+
+def _bw_gate_on_sparse(q, k, v, gate, idx, block=64):
+    out, out_c, out_s = _forward_torch_ok(q, k, v, None, idx, block)
+    if gate is None:
+        return out, out_c, out_s
+    g = gate[..., None] if gate.dim() == 3 else gate
+    blk = torch.arange(q.shape[2]) // block
+    return out_c[:, :, blk] + out_s * g, out_c, out_s
+
+
+def _bw_value_detached(q, k, v, gate, idx, block=64):
+    # gradient stops at v in the sparse branch (a slip in the restatement)
+    return _forward_torch_ok(q, k, v.detach(), gate, idx, block)
+
+
 MISTAKES = {
     "sparse_scale_dropped": ("sparse_block", _sparse_no_scale),
     "pool_divides_by_64": ("pool", _pool_div64),
@@ -155,6 +174,8 @@ MISTAKES = {
     "tiles_local_order_w_slowest": ("tiles.tile_partition", _tiles_local_order_w_slowest),
     "tiles_not_padded": ("tiles.tile_partition", _tiles_unpadded),
     "tiles_reverse_is_forward": ("tiles.tile_partition", _tiles_reverse_is_forward),
+    "backward_gate_on_sparse": ("backward.forward_torch", _bw_gate_on_sparse),
+    "backward_value_detached": ("backward.forward_torch", _bw_value_detached),
 }
 
 
@@ -163,7 +184,7 @@ def _some_pin_fails():
     for pin in P.ALL_PINS:
         try:
             pin()
-        except (AssertionError, ValueError, IndexError):
+        except (AssertionError, ValueError, IndexError, torch.autograd.gradcheck.GradcheckError):
             failed.append(pin.__name__)
     return failed
 
@@ -174,6 +195,8 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     mod = O
     if attr.startswith("tiles."):
         mod, attr = TL, attr.split(".", 1)[1]
+    elif attr.startswith("backward."):
+        mod, attr = BW, attr.split(".", 1)[1]
     monkeypatch.setattr(mod, attr, bad)
     failed = _some_pin_fails()
     assert failed, f"no pin rejects the planted mistake {name}"
