@@ -184,7 +184,7 @@ def _some_pin_fails():
     for pin in P.ALL_PINS:
         try:
             pin()
-        except (AssertionError, ValueError, IndexError, torch.autograd.gradcheck.GradcheckError):
+        except Exception:  # a pin that raises rejects the planted mistake
             failed.append(pin.__name__)
     return failed
 
