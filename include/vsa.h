@@ -278,6 +278,76 @@ int vsa_forward_varlen(const vsa_bf16 *q, const vsa_bf16 *k, const vsa_bf16 *v,
                        void *workspace, size_t workspace_bytes, vsa_stream stream);
 
 /*
+ * Training: the forward that keeps what the backward needs, and the backward.
+ * ("[kernel] Add varlen support for block-sparse attention", Test plan:
+ * backward correctness of the block-sparse attention against per-sequence
+ * references; "[chore] release fastvideo-kernel 0.3.0", Block-sparse / VSA
+ * attention improvements: block-sparse attention forward and backward.)
+ * The backward is the gradient of the forward with the routing (q2k_idx)
+ * held fixed: the top-k choice is piecewise constant and carries none.
+ */
+
+/*
+ * vsa_sparse_attn_combine_train - vsa_sparse_attn_combine that also writes
+ * out_s, the bf16 normalised block-sparse attention output on its own (query
+ * layout, padding slots of PACKED written with 0), and lse, float32, one per
+ * query row ([B, H, Sq] DENSE, [H, 64*Nq] PACKED, padding slots not written):
+ * log2 of the softmax denominator of the row in units where the row's
+ * probabilities are exp2(s * log2(e) / sqrt(D) - lse) for raw scores s = q.k
+ * (-inf for a row whose list holds no valid block).  Arguments, checks and
+ * errors as vsa_sparse_attn_combine; out_s and lse must not be NULL, out_s
+ * 16-byte aligned, lse 4-byte aligned, and neither may overlap an input or
+ * out (VSA_ERR_ALIAS).
+ */
+int vsa_sparse_attn_combine_train(const vsa_problem *problem, const vsa_bf16 *q, const vsa_bf16 *k,
+                                  const vsa_bf16 *v, const int32_t *q2k_idx, const int32_t *q2k_num,
+                                  const float *out_c, const vsa_bf16 *gate, int32_t gate_mode,
+                                  const int64_t *gate_strides, vsa_bf16 *out, vsa_bf16 *out_s, float *lse,
+                                  vsa_stream stream);
+
+/*
+ * vsa_backward_workspace_size - bytes of device workspace vsa_backward needs:
+ * float64 block means of Q, K, V and their gradients, the coarse output
+ * gradient, two float64 block-level matrices (query blocks x the most KV
+ * blocks of a sequence: the coarse softmax and its score gradient), 128 float32
+ * row statistics per query block and the inverse routing (KV blocks x the
+ * most query blocks of a sequence, int32).  Returns 0 when the problem is
+ * invalid.
+ */
+size_t vsa_backward_workspace_size(const vsa_problem *problem);
+
+/*
+ * vsa_backward - gradients of sum(out * dout) for the forward
+ * out = out_c * gate + out_s run with these q, k, v, gate and routing.
+ *
+ * Inputs: q, k, v (bf16, layouts above); q2k_idx / q2k_num as written by
+ * vsa_coarse_topk (each list strictly ascending); out_c (float32) from
+ * vsa_coarse_topk; gate, gate_mode, gate_strides as for vsa_combine; out_s
+ * and lse from vsa_sparse_attn_combine_train; dout (bf16, query layout; its
+ * padding slots are not read).
+ * Outputs (bf16, written in full, PACKED padding slots with 0): dq in the
+ * query layout, dk and dv in the KV layout, and for a gate dgate, contiguous
+ * in the query layout whatever gate_strides were: [B, H, Sq] / [H, 64*Nq]
+ * for VSA_GATE_TOKEN, the same with a trailing D for VSA_GATE_FULL (NULL and
+ * unused for VSA_GATE_NONE).
+ * Arithmetic: the coarse branch and the gradients through the block means
+ * in float64; the block-sparse part as bf16 matrix products with float32
+ * accumulation (probabilities recomputed from lse, rounded to bf16 as
+ * product operands); one rounding per output element.  No atomics: results
+ * are bit-for-bit repeatable.
+ * Errors as vsa_sparse_attn_combine, plus VSA_ERR_NULL (a required pointer
+ * NULL), VSA_ERR_ALIGN (tensors not 16-byte aligned, lse not 4-byte aligned,
+ * workspace not 256-byte aligned), VSA_ERR_ALIAS (an output overlapping an
+ * input or another output), VSA_ERR_WORKSPACE (fewer than
+ * vsa_backward_workspace_size bytes).
+ */
+int vsa_backward(const vsa_problem *problem, const vsa_bf16 *q, const vsa_bf16 *k, const vsa_bf16 *v,
+                 const int32_t *q2k_idx, const int32_t *q2k_num, const float *out_c, const vsa_bf16 *gate,
+                 int32_t gate_mode, const int64_t *gate_strides, const vsa_bf16 *out_s, const float *lse,
+                 const vsa_bf16 *dout, vsa_bf16 *dq, vsa_bf16 *dk, vsa_bf16 *dv, vsa_bf16 *dgate,
+                 void *workspace, size_t workspace_bytes, vsa_stream stream);
+
+/*
  * 3-D tile partition of video latents ("[kernel] Extract VSA utility
  * functions into fastvideo_kernel", Summary, Design decisions and review
  * thread: tile partition indices and their inverse, variable block sizes with

@@ -17,7 +17,11 @@ attention, sparse attention over the selected blocks, combine), and
 ``torch.autograd`` differentiates it.  The routing comes from
 ``vsa_oracle``.  Pins (``tests/oracle_pins.py``): this forward reproduces
 ``vsa_oracle.vsa_forward`` and its gradients pass
-``torch.autograd.gradcheck`` against finite differences.
+``torch.autograd.gradcheck`` against finite differences; with every block
+selected they are those of dense attention.  ``sparse_row_lse2`` (the
+per-row log-sum-exp a training forward keeps) is pinned to scipy's
+``logsumexp`` with every block selected and to the oracle's sparse output
+through the probabilities it defines.
 """
 from __future__ import annotations
 
@@ -71,6 +75,27 @@ def forward_torch(q, k, v, gate, idx, block: int = O.BLOCK):
     return torch.stack(out_rows), torch.stack(outc_rows), torch.stack(outs_rows)
 
 
+def sparse_row_lse2(q, k, idx, block: int = O.BLOCK) -> np.ndarray:
+    """Base-2 log of the softmax denominator of every query row of the sparse
+    branch: ``log2(sum_t exp(q . k_t / sqrt(D)))`` over the valid tokens of
+    the row's selected KV blocks, ``[B, H, Sq]`` from ``[B, H, S, D]`` inputs
+    and routing ``idx`` (``[B, H, nQ, kk]``).  A training forward keeps it so
+    that the backward can recompute the probabilities as ``exp2(q . k_t
+    log2(e) / sqrt(D) - lse)``."""
+    q, k = np.asarray(q, dtype=np.float64), np.asarray(k, dtype=np.float64)
+    B, H, Sq, D = q.shape
+    qs, ks = O.block_sizes(Sq, block), O.block_sizes(k.shape[2], block)
+    out = np.empty((B, H, Sq))
+    for b in range(B):
+        for h in range(H):
+            for i, n in enumerate(qs):
+                keys = np.concatenate([k[b, h, block * j: block * j + ks[j]] for j in idx[b, h, i]])
+                s = q[b, h, block * i: block * i + n] @ keys.T / math.sqrt(D)
+                m = s.max(axis=1, keepdims=True)
+                out[b, h, block * i: block * i + n] = (m[:, 0] + np.log(np.exp(s - m).sum(axis=1))) / math.log(2.0)
+    return out
+
+
 def vsa_backward(q, k, v, topk: int, gate, dout) -> Dict[str, np.ndarray]:
     """Gradients of ``sum(out * dout)`` with respect to q, k, v and the gate
     (float64 numpy in, float64 numpy out), plus the forward's routing and
@@ -85,5 +110,5 @@ def vsa_backward(q, k, v, topk: int, gate, dout) -> Dict[str, np.ndarray]:
                dgate=None if tg is None else tg.grad.numpy(),
                out=out.detach().numpy(), out_c=out_c.detach().numpy(), out_s=out_s.detach().numpy(),
                q2k_idx=fwd["q2k_idx"], q2k_num=fwd["q2k_num"], gap=fwd["gap"],
-               max_abs_dot=fwd["max_abs_dot"])
+               max_abs_dot=fwd["max_abs_dot"], lse=sparse_row_lse2(q, k, fwd["q2k_idx"]))
     return res

@@ -13,4 +13,6 @@ from .inputs import (  # noqa: F401
     varlen_inputs,
     workload,
     bf16_to_f64,
+    full_gate,
+    output_grad,
 )

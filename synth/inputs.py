@@ -130,6 +130,20 @@ def varlen_inputs(seqlens_q: List[int], seqlens_kv: Optional[List[int]], H: int,
                         name, per_seq)
 
 
+def output_grad(shape, seed: int) -> torch.Tensor:
+    """Seeded output gradient for backward workloads: N(0, 1) in float32 from
+    its own generator, rounded to bf16."""
+    gen = torch.Generator().manual_seed(seed)
+    return _bf16_randn(gen, shape)
+
+
+def full_gate(shape, seed: int) -> torch.Tensor:
+    """Seeded gate with one value per (token, head, d): sigmoid of N(0, 1)
+    logits, rounded to bf16 (the per-token gate's recipe, one more axis)."""
+    gen = torch.Generator().manual_seed(seed)
+    return _bf16_gate(gen, shape)
+
+
 # ---------------------------------------------------------------------------
 # Named workloads.  Seeds are 1000 + the workload's number.
 # ---------------------------------------------------------------------------

@@ -43,7 +43,7 @@ static int bank_ways(const std::vector<int>& byte_addr, const std::vector<int>& 
 // value stored for element (token t, dim d) of a block: unique and recognisable
 static int val(int t, int d) { return t * 1000 + d; }
 
-template <int D, bool IS_V>
+template <int D, int SW>
 static std::vector<int> fill_tile(int valid) {
     constexpr int CH = D / 8;
     constexpr int ROWB = CH * 16;  // bytes per source row
@@ -56,12 +56,12 @@ static std::vector<int> fill_tile(int valid) {
                 CHECK(p >= 0 && p < 64 * CH, "chunk position %d out of range", p);
                 hits[p]++;
                 const int row = p / CH;
-                const int sw = IS_V ? vsa::v_swz<CH>(row) : vsa::k_swz<CH>(row);
+                const int sw = vsa::tile_swz<CH, SW>(row);
                 const int c = (p % CH) ^ sw;
                 CHECK(c >= 0 && c < CH, "logical chunk %d out of range", c);
                 // full blocks use the fixed per-lane offset of n & 1 + 4096 (n >> 1)
-                const int fast = vsa::lane_src_offset<CH, IS_V>(wave, lane, n & 1) + 4096 * (n >> 1);
-                CHECK(fast == row * ROWB + 16 * c, "fast-path offset D%d n%d w%d l%d", D, n, wave, lane);
+                const int fast = vsa::lane_src_offset<CH, SW>(wave, lane, n & 1) + 4096 * (n >> 1);
+                CHECK(fast == row * ROWB + 16 * c, "fast-path offset D%d SW%d n%d w%d l%d", D, SW, n, wave, lane);
                 CHECK(fast >= 0 && fast + 16 <= 64 * ROWB, "fast-path offset out of the block");
                 const int src_row = row < valid ? row : valid - 1;
                 const int src_byte = valid == 64 ? fast : src_row * ROWB + 16 * c;
@@ -75,99 +75,137 @@ static std::vector<int> fill_tile(int valid) {
     return tile;
 }
 
-template <int D>
-static void check_d() {
+// Row operand (the A operand of S^T = K Q^T, or of S = Q K^T / dP = dO V^T in
+// the backward): lane l gets T[32 mt + l%32][16 ks + 8 hh + 0..7].
+template <int D, int SW>
+static void check_row_operand(const std::vector<int>& t, int valid) {
+    constexpr int CH = D / 8, KS = D / 16;
+    for (int mt = 0; mt < 2; ++mt)
+        for (int ks = 0; ks < KS; ++ks)
+            for (int l = 0; l < 64; ++l) {
+                const int row = 32 * mt + (l & 31), hh = l >> 5;
+                const int off = vsa::tile_off<CH>(row, 2 * ks + hh, vsa::tile_swz<CH, SW>(row));
+                const int r = row < valid ? row : valid - 1;
+                for (int e = 0; e < 8; ++e)
+                    CHECK(t[off + e] == val(r, 16 * ks + 8 * hh + e), "row operand SW%d mt%d ks%d lane%d e%d", SW, mt,
+                          ks, l, e);
+            }
+}
+
+// Transposed operand (V^T of O^T = V^T P^T; K^T, Q^T, dO^T in the backward)
+// via two transpose reads per k-step: lane l needs T[16 s4 + 8 jj + 4 hh +
+// r][32 dt + l%32] in slot 4 jj + r.
+template <int D, int SW>
+static void tr_addresses(int dt, int s4, int jj, int* addr) {
     constexpr int CH = D / 8;
-    constexpr int KS = D / 16, DT = D / 32;
-    // swizzles are permutations of a row's chunks
-    for (int row = 0; row < 64; ++row) {
-        std::set<int> a, b;
-        for (int c = 0; c < CH; ++c) {
-            a.insert(vsa::tile_off<CH>(row, c, vsa::k_swz<CH>(row)));
-            b.insert(vsa::tile_off<CH>(row, c, vsa::v_swz<CH>(row)));
-        }
-        CHECK((int)a.size() == CH && (int)b.size() == CH, "swizzle of row %d not a permutation", row);
-        CHECK(*a.rbegin() < 64 * D && *b.rbegin() < 64 * D, "tile offset out of range");
+    for (int l = 0; l < 64; ++l) {
+        const int g16 = l >> 4, L16 = l & 15, hh = l >> 5;
+        const int tok = 16 * s4 + 8 * jj + 4 * hh + vsa::tr_token(L16);
+        const int d = 32 * dt + 16 * (g16 & 1) + 4 * vsa::tr_dquad(L16);
+        addr[l] = vsa::tile_off<CH>(tok, d >> 3, vsa::tile_swz<CH, SW>(tok)) + (d & 7);
     }
-    for (int valid : {64, 37, 1}) {
-        const std::vector<int> kt = fill_tile<D, false>(valid);
-        const std::vector<int> vt = fill_tile<D, true>(valid);
-        // K operand of S^T = K Q^T: lane l gets K[32 mt + l%32][16 ks + 8 hh + 0..7]
-        for (int mt = 0; mt < 2; ++mt)
-            for (int ks = 0; ks < KS; ++ks)
+}
+template <int D, int SW>
+static void check_tr_operand(const std::vector<int>& t, int valid) {
+    constexpr int DT = D / 32;
+    for (int dt = 0; dt < DT; ++dt)
+        for (int s4 = 0; s4 < 4; ++s4)
+            for (int jj = 0; jj < 2; ++jj) {
+                int addr[64];
+                tr_addresses<D, SW>(dt, s4, jj, addr);
+                for (int l = 0; l < 64; ++l) CHECK(addr[l] >= 0 && addr[l] + 3 < 64 * D, "tr address out of range");
                 for (int l = 0; l < 64; ++l) {
-                    const int row = 32 * mt + (l & 31), hh = l >> 5;
-                    const int off = vsa::tile_off<CH>(row, 2 * ks + hh, vsa::k_swz<CH>(row));
-                    const int r = row < valid ? row : valid - 1;
-                    for (int e = 0; e < 8; ++e)
-                        CHECK(kt[off + e] == val(r, 16 * ks + 8 * hh + e), "K operand mt%d ks%d lane%d e%d", mt, ks, l, e);
-                }
-        // V^T operand of O^T = V^T P^T via two transpose reads per k-step:
-        // lane l needs V[16 s4 + 8 jj + 4 hh + r][32 dt + l%32] in slot 4 jj + r
-        for (int dt = 0; dt < DT; ++dt)
-            for (int s4 = 0; s4 < 4; ++s4)
-                for (int jj = 0; jj < 2; ++jj) {
-                    int addr[64];
-                    for (int l = 0; l < 64; ++l) {
-                        const int g16 = l >> 4, L16 = l & 15, hh = l >> 5;
-                        const int tok = 16 * s4 + 8 * jj + 4 * hh + vsa::tr_token(L16);
-                        const int d = 32 * dt + 16 * (g16 & 1) + 4 * vsa::tr_dquad(L16);
-                        addr[l] = vsa::tile_off<CH>(tok, d >> 3, vsa::v_swz<CH>(tok)) + (d & 7);
-                        CHECK(addr[l] >= 0 && addr[l] + 3 < 64 * D, "tr address out of range");
-                    }
-                    for (int l = 0; l < 64; ++l) {
-                        const int grp = l & ~15, i = l & 15, hh = l >> 5;
-                        for (int r = 0; r < 4; ++r) {
-                            const int src = grp + (i >> 2) + 4 * r;
-                            const int got = vt[addr[src] + (i & 3)];
-                            const int tok = 16 * s4 + 8 * jj + 4 * hh + r;
-                            const int t = tok < valid ? tok : valid - 1;
-                            CHECK(got == val(t, 32 * dt + (l & 31)), "V operand dt%d s4%d jj%d lane%d r%d", dt, s4, jj, l, r);
-                        }
+                    const int grp = l & ~15, i = l & 15, hh = l >> 5;
+                    for (int r = 0; r < 4; ++r) {
+                        const int src = grp + (i >> 2) + 4 * r;
+                        const int got = t[addr[src] + (i & 3)];
+                        const int tok = 16 * s4 + 8 * jj + 4 * hh + r;
+                        const int tt = tok < valid ? tok : valid - 1;
+                        CHECK(got == val(tt, 32 * dt + (l & 31)), "tr operand SW%d dt%d s4%d jj%d lane%d r%d", SW, dt,
+                              s4, jj, l, r);
                     }
                 }
-    }
-    // LDS bank model: K reads (b128) and V transpose reads (b64), for 32 and
-    // 64 banks of 4 bytes (passes of 128 and 256 bytes)
-    int worst[2][2] = {{0, 0}, {0, 0}};
-    for (int m = 0; m < 2; ++m) {
-        const int banks = m == 0 ? 32 : 64;
-        for (int mt = 0; mt < 2; ++mt)
-            for (int ks = 0; ks < KS; ++ks) {
-                const int lpp = banks * 4 / 16;
+            }
+}
+
+// LDS bank model: worst ways of the row reads (b128) and of the transpose
+// reads (b64) of a tile, with `banks` banks of 4 bytes (passes of 4 banks
+// bytes).
+template <int D, int SW>
+static int bank_row(int banks) {
+    constexpr int CH = D / 8, KS = D / 16;
+    int worst = 0;
+    for (int mt = 0; mt < 2; ++mt)
+        for (int ks = 0; ks < KS; ++ks) {
+            const int lpp = banks * 4 / 16;
+            for (int p0 = 0; p0 < 64; p0 += lpp) {
+                std::vector<int> a, b;
+                for (int l = p0; l < p0 + lpp; ++l) {
+                    const int row = 32 * mt + (l & 31);
+                    a.push_back(2 * vsa::tile_off<CH>(row, 2 * ks + (l >> 5), vsa::tile_swz<CH, SW>(row)));
+                    b.push_back(16);
+                }
+                const int w = bank_ways(a, b, banks);
+                worst = w > worst ? w : worst;
+            }
+        }
+    return worst;
+}
+template <int D, int SW>
+static int bank_tr(int banks) {
+    constexpr int DT = D / 32;
+    int worst = 0;
+    for (int dt = 0; dt < DT; ++dt)
+        for (int s4 = 0; s4 < 4; ++s4)
+            for (int jj = 0; jj < 2; ++jj) {
+                int addr[64];
+                tr_addresses<D, SW>(dt, s4, jj, addr);
+                const int lpp = banks * 4 / 8;
                 for (int p0 = 0; p0 < 64; p0 += lpp) {
                     std::vector<int> a, b;
                     for (int l = p0; l < p0 + lpp; ++l) {
-                        const int row = 32 * mt + (l & 31);
-                        a.push_back(2 * vsa::tile_off<CH>(row, 2 * ks + (l >> 5), vsa::k_swz<CH>(row)));
-                        b.push_back(16);
+                        a.push_back(2 * addr[l]);
+                        b.push_back(8);
                     }
                     const int w = bank_ways(a, b, banks);
-                    worst[0][m] = w > worst[0][m] ? w : worst[0][m];
+                    worst = w > worst ? w : worst;
                 }
             }
-        for (int dt = 0; dt < DT; ++dt)
-            for (int s4 = 0; s4 < 4; ++s4)
-                for (int jj = 0; jj < 2; ++jj) {
-                    const int lpp = banks * 4 / 8;
-                    for (int p0 = 0; p0 < 64; p0 += lpp) {
-                        std::vector<int> a, b;
-                        for (int l = p0; l < p0 + lpp; ++l) {
-                            const int g16 = l >> 4, L16 = l & 15, hh = l >> 5;
-                            const int tok = 16 * s4 + 8 * jj + 4 * hh + vsa::tr_token(L16);
-                            const int d = 32 * dt + 16 * (g16 & 1) + 4 * vsa::tr_dquad(L16);
-                            a.push_back(2 * (vsa::tile_off<CH>(tok, d >> 3, vsa::v_swz<CH>(tok)) + (d & 7)));
-                            b.push_back(8);
-                        }
-                        const int w = bank_ways(a, b, banks);
-                        worst[1][m] = w > worst[1][m] ? w : worst[1][m];
-                    }
-                }
+    return worst;
+}
+
+template <int D>
+static void check_d() {
+    constexpr int CH = D / 8;
+    // swizzles are permutations of a row's chunks
+    for (int row = 0; row < 64; ++row) {
+        std::set<int> a, b, c;
+        for (int x = 0; x < CH; ++x) {
+            a.insert(vsa::tile_off<CH>(row, x, vsa::k_swz<CH>(row)));
+            b.insert(vsa::tile_off<CH>(row, x, vsa::v_swz<CH>(row)));
+            c.insert(vsa::tile_off<CH>(row, x, vsa::dual_swz<CH>(row)));
+        }
+        CHECK((int)a.size() == CH && (int)b.size() == CH && (int)c.size() == CH,
+              "swizzle of row %d not a permutation", row);
+        CHECK(*a.rbegin() < 64 * D && *b.rbegin() < 64 * D && *c.rbegin() < 64 * D, "tile offset out of range");
     }
-    printf("D=%d: worst bank ways K read %d/%d, V read %d/%d (32/64 banks)\n", D, worst[0][0], worst[0][1],
-           worst[1][0], worst[1][1]);
-    CHECK(worst[0][0] == 1 && worst[1][0] == 1, "bank conflicts in the 32-bank model");
-    if (D == 128) CHECK(worst[0][1] == 1 && worst[1][1] == 1, "bank conflicts in the 64-bank model");
+    for (int valid : {64, 37, 1}) {
+        check_row_operand<D, vsa::kSwzRow>(fill_tile<D, vsa::kSwzRow>(valid), valid);
+        check_tr_operand<D, vsa::kSwzTr>(fill_tile<D, vsa::kSwzTr>(valid), valid);
+        const std::vector<int> dual = fill_tile<D, vsa::kSwzDual>(valid);
+        check_row_operand<D, vsa::kSwzDual>(dual, valid);
+        check_tr_operand<D, vsa::kSwzDual>(dual, valid);
+    }
+    for (int banks : {32, 64}) {
+        const int kr = bank_row<D, vsa::kSwzRow>(banks), vt = bank_tr<D, vsa::kSwzTr>(banks);
+        const int dr = bank_row<D, vsa::kSwzDual>(banks), dtr = bank_tr<D, vsa::kSwzDual>(banks);
+        printf("D=%d, %d banks: worst ways K rows %d, V transposed %d, dual rows %d, dual transposed %d\n", D, banks,
+               kr, vt, dr, dtr);
+        // the forward's K and V tiles are conflict-free with 32 banks (and with
+        // 64 for D = 128); the dual layout is made for gfx950's 64 banks
+        if (banks == 32 || D == 128) CHECK(kr == 1 && vt == 1, "bank conflicts (D=%d, %d banks)", D, banks);
+        if (banks == 64) CHECK(dr == 1 && dtr == 1, "dual layout bank conflicts (D=%d)", D);
+    }
 }
 
 int main() {

@@ -514,6 +514,39 @@ def pin_backward_dense_equivalence(seed=18):
         assert np.allclose(a.grad.numpy(), b_.grad.numpy(), rtol=1e-10, atol=1e-12)
 
 
+def pin_lse_dense_equivalence(seed=19):
+    """Every block selected: the row log-sum-exp is scipy's logsumexp of the
+    dense scaled scores, in base 2."""
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(seed)
+    B, H, S, D = 1, 2, 64 * 2 + 9, 16
+    q, k = rng.standard_normal((B, H, S, D)), rng.standard_normal((B, H, S, D))
+    idx = O.vsa_forward(q, k, k, 3)["q2k_idx"]
+    ref = logsumexp(np.einsum("bhsd,bhtd->bhst", q, k) / math.sqrt(D), axis=-1) / math.log(2.0)
+    assert np.allclose(BW.sparse_row_lse2(q, k, idx), ref, rtol=1e-13, atol=1e-12)
+
+
+def pin_lse_reproduces_sparse_output(seed=20):
+    """The probabilities exp2(s log2(e) / sqrt(D) - lse) over each row's
+    selected tokens give the oracle's sparse output (top-k 2 of 4 blocks,
+    ragged last block)."""
+    rng = np.random.default_rng(seed)
+    B, H, S, D = 1, 2, 64 * 3 + 30, 8
+    q, k, v = (rng.standard_normal((B, H, S, D)) for _ in range(3))
+    ref = O.vsa_forward(q, k, v, 2)
+    lse = BW.sparse_row_lse2(q, k, ref["q2k_idx"])
+    sizes = O.block_sizes(S)
+    for b in range(B):
+        for h in range(H):
+            for i, n in enumerate(sizes):
+                toks = np.concatenate([np.arange(64 * j, 64 * j + sizes[j]) for j in ref["q2k_idx"][b, h, i]])
+                rows = slice(64 * i, 64 * i + n)
+                s_ = q[b, h, rows] @ k[b, h, toks].T
+                p = np.exp2(s_ * (1.0 / math.log(2.0)) / math.sqrt(D) - lse[b, h, rows][:, None])
+                assert np.allclose(p.sum(axis=1), 1.0, rtol=1e-12)
+                assert np.allclose(p @ v[b, h, toks], ref["out_s"][b, h, rows], rtol=1e-11, atol=1e-12)
+
+
 ALL_PINS = [
     pin_block_sizes, pin_pool_partial_block, pin_two_token_closed_form,
     pin_coarse_and_routing_closed_form, pin_combine_closed_form, pin_topk_bruteforce,
@@ -524,4 +557,5 @@ ALL_PINS = [
     pin_tile_partition_by_sorting, pin_tile_closed_forms, pin_tile_gather_scatter_roundtrip,
     pin_video_forward_1d_equals_dense, pin_video_forward_tile_equivariance,
     pin_backward_forward_matches_oracle, pin_backward_gradcheck, pin_backward_dense_equivalence,
+    pin_lse_dense_equivalence, pin_lse_reproduces_sparse_output,
 ]

@@ -246,6 +246,83 @@ def test_validation_errors(lib, call, code):
     assert lib.vsa_last_error()
 
 
+# ---------------------------------------------------------------------------
+# training entry points: validation and workspace (no launch happens)
+# ---------------------------------------------------------------------------
+
+def _fk(n):
+    return ctypes.c_void_p(FAKE + (n << 32))
+
+
+# distinct fake buffers, 4 GiB apart: q, k, v, out_c, ws, gate/idx, out_s, lse, dout, dq, dk, dv, dgate
+OS_, LSE_, DO_, DQ_, DK_, DV_, DG_ = (_fk(n) for n in range(6, 13))
+
+
+def train_fwd(lib, p, q=A, k=B_, v=C_, idx=G_, num=G_, oc=W_, gate=None, mode=0, st=None, out=O_, out_s=OS_,
+              lse=LSE_):
+    return lib.vsa_sparse_attn_combine_train(ctypes.byref(p), q, k, v, idx, num, oc, gate, mode, st, out, out_s,
+                                             lse, None)
+
+
+def bwd(lib, p, q=A, k=B_, v=C_, idx=G_, num=G_, oc=O_, gate=None, mode=0, st=None, out_s=OS_, lse=LSE_, dout=DO_,
+        dq=DQ_, dk=DK_, dv=DV_, dgate=DG_, ws=W_, wsb=1 << 40):
+    return lib.vsa_backward(ctypes.byref(p), q, k, v, idx, num, oc, gate, mode, st, out_s, lse, dout, dq, dk, dv,
+                            dgate, ws, wsb, None)
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda L: train_fwd(L, dense(), out_s=None), E.VSA_ERR_NULL),
+    (lambda L: train_fwd(L, dense(), lse=None), E.VSA_ERR_NULL),
+    (lambda L: train_fwd(L, dense(), out_s=ctypes.c_void_p(FAKE + (6 << 32) + 8)), E.VSA_ERR_ALIGN),
+    (lambda L: train_fwd(L, dense(), lse=ctypes.c_void_p(FAKE + (7 << 32) + 2)), E.VSA_ERR_ALIGN),
+    (lambda L: train_fwd(L, dense(), out_s=O_), E.VSA_ERR_ALIAS),
+    (lambda L: train_fwd(L, dense(), out_s=A), E.VSA_ERR_ALIAS),
+    (lambda L: train_fwd(L, dense(), lse=ctypes.c_void_p(FAKE + (6 << 32) + 4096)), E.VSA_ERR_ALIAS),
+    (lambda L: train_fwd(L, dense(), mode=1, gate=ctypes.c_void_p(FAKE + (6 << 32) + 64)), E.VSA_ERR_ALIAS),
+    (lambda L: train_fwd(L, dense(), mode=4, gate=G_), E.VSA_ERR_GATE),
+    (lambda L: bwd(L, dense(), dout=None), E.VSA_ERR_NULL),
+    (lambda L: bwd(L, dense(), lse=None), E.VSA_ERR_NULL),
+    (lambda L: bwd(L, dense(), dk=None), E.VSA_ERR_NULL),
+    (lambda L: bwd(L, dense(), mode=1, gate=G_, dgate=None), E.VSA_ERR_NULL),
+    (lambda L: bwd(L, dense(), mode=2, gate=G_, dgate=ctypes.c_void_p(FAKE + (12 << 32) + 2)), E.VSA_ERR_ALIGN),
+    (lambda L: bwd(L, dense(), mode=1, gate=G_, dgate=ctypes.c_void_p(FAKE + (12 << 32) + 1)), E.VSA_ERR_ALIGN),
+    (lambda L: bwd(L, dense(), dq=ctypes.c_void_p(FAKE + (9 << 32) + 8)), E.VSA_ERR_ALIGN),
+    (lambda L: bwd(L, dense(), lse=ctypes.c_void_p(FAKE + (7 << 32) + 1)), E.VSA_ERR_ALIGN),
+    (lambda L: bwd(L, dense(), dq=A), E.VSA_ERR_ALIAS),
+    (lambda L: bwd(L, dense(), dk=DO_), E.VSA_ERR_ALIAS),
+    (lambda L: bwd(L, dense(), dv=ctypes.c_void_p(FAKE + (10 << 32) + 4096)), E.VSA_ERR_ALIAS),
+    (lambda L: bwd(L, dense(), dq=ctypes.c_void_p(FAKE + (7 << 32) + 64)), E.VSA_ERR_ALIAS),
+    (lambda L: bwd(L, dense(), mode=2, gate=G_, dgate=DQ_), E.VSA_ERR_ALIAS),
+    (lambda L: bwd(L, dense(), mode=1, gate=G_, dgate=ctypes.c_void_p(FAKE + (3 << 32) + 256)), E.VSA_ERR_ALIAS),
+    (lambda L: bwd(L, dense(), ws=None), E.VSA_ERR_WORKSPACE),
+    (lambda L: bwd(L, dense(), wsb=4096), E.VSA_ERR_WORKSPACE),
+    (lambda L: bwd(L, dense(), ws=ctypes.c_void_p(FAKE + (4 << 32) + 16)), E.VSA_ERR_ALIGN),
+    (lambda L: bwd(L, dense(D=80)), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: bwd(L, dense(topk=0)), E.VSA_ERR_TOPK),
+    (lambda L: bwd(L, packed(ptrs=False)), E.VSA_ERR_NULL),
+    (lambda L: bwd(L, dense(), mode=3, gate=G_), E.VSA_ERR_GATE),
+])
+def test_training_validation_errors(lib, call, code):
+    rc = call(lib)
+    assert rc == code, (rc, lib.vsa_last_error())
+    assert lib.vsa_last_error()
+
+
+def test_backward_workspace(lib):
+    """The backward workspace holds block-resolution float64 data, the
+    block-level coarse matrices and the inverse routing: a small fraction of
+    one bf16 [B,H,S,D] tensor for long sequences."""
+    for S in (64 * 10, 64 * 242, 64 * 1024):
+        p = dense(B=1, H=56, Sq=S, Skv=S, D=128, topk=32)
+        ws = lib.vsa_backward_workspace_size(ctypes.byref(p))
+        nb = S // 64
+        qb = 56 * nb
+        floor = 8 * qb * 128 * 7 + 2 * 8 * qb * nb + 4 * qb * 128 + 4 * qb * nb + 4 * qb
+        assert floor <= ws <= floor + 13 * 256, (S, ws, floor)
+    assert lib.vsa_backward_workspace_size(ctypes.byref(packed())) > 0
+    assert lib.vsa_backward_workspace_size(ctypes.byref(dense(bs=32))) == 0
+
+
 def test_layout_maps_on_cpu(tmp_path):
     """Compile and run the host-only check of the attention kernel's index maps
     (bijections, bounds, MFMA k-slot relabelling, LDS bank model, XCD remap)."""

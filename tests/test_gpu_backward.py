@@ -1,0 +1,196 @@
+"""GPU parity of the backward pass (vsa_sparse_attn_combine_train + vsa_backward,
+through the C ABI) against the fp64 oracle of ``oracle/vsa_backward.py`` on
+seeded inputs that span several blocks with ragged tails, every gate mode,
+Sq != Skv, single-block and single-token sequences, and packed sequences.
+
+Tolerances (gradients are compared relative to the reference's own scale,
+since their magnitude follows dout and the softmax sharpness): the sparse
+part rounds P and dS to bf16 as MFMA operands (relative 2^-9 each) and every
+output once to bf16 (2^-9); the errors of the sums over 64 * top-k tokens
+are unbiased, so the worst element stays within a few times 2^-9 of the
+largest gradient and the mean within a fraction of that of the mean one."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import video_sparse_attention_amd as vsa
+from oracle import vsa_backward as BW
+from tests import gpu_common as G
+from tests import numerics as N
+
+pytestmark = pytest.mark.gpu
+
+GRAD_MAX_REL = 2e-2   # max |gpu - ref| / max |ref|
+GRAD_MEAN_REL = 1e-2  # mean |gpu - ref| / mean |ref|
+LSE_ABS = 4e-3        # log2 units: the bf16 rounding of the summed probabilities
+
+
+def check_grad(gpu: np.ndarray, ref: np.ndarray, what: str):
+    assert np.isfinite(gpu).all(), f"{what}: non-finite values"
+    d = np.abs(gpu - ref)
+    scale_max, scale_mean = float(np.abs(ref).max()), float(np.abs(ref).mean())
+    mx, mean = float(d.max()) / max(scale_max, 1e-30), float(d.mean()) / max(scale_mean, 1e-30)
+    G.note(f"  {what}: max-err/max {mx:.2e}, mean-err/mean {mean:.2e} (|ref| max {scale_max:.2e})")
+    assert mx <= GRAD_MAX_REL, f"{what}: max error {mx:.3e} of the largest gradient > {GRAD_MAX_REL}"
+    assert mean <= GRAD_MEAN_REL, f"{what}: mean error {mean:.3e} of the mean gradient > {GRAD_MEAN_REL}"
+
+
+def run_dense_train(q, k, v, gate, dout, topk, dev=G.DEV):
+    """Coarse/top-k, the training forward, the plain fused forward and the
+    backward on dense [B, H, S, D] CPU bf16 tensors; returns CPU results."""
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    q, k, v, dout = (t.to(dev) for t in (q, k, v, dout))
+    gate = None if gate is None else gate.to(dev)
+    prob = vsa.dense_problem(B, H, Sq, Skv, D, topk)
+    cs, isz, ns = vsa.block_shapes(prob)
+    out_c = torch.empty(cs, dtype=torch.float32, device=dev)
+    idx = torch.empty(isz, dtype=torch.int32, device=dev)
+    num = torch.empty(ns, dtype=torch.int32, device=dev)
+    vsa.vsa_coarse_topk(prob, q, k, v, out_c, idx, num, vsa.alloc_workspace(prob, dev))
+    out = torch.empty_like(q)
+    out_s = torch.empty_like(q)
+    lse = torch.empty(vsa.lse_shape(prob), dtype=torch.float32, device=dev)
+    vsa.vsa_sparse_attn_combine_train(prob, q, k, v, idx, num, out_c, gate, out, out_s, lse)
+    out_plain = torch.empty_like(q)
+    vsa.vsa_sparse_attn_combine(prob, q, k, v, idx, num, out_c, gate, out_plain)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = None if gate is None else torch.empty(gate.shape, dtype=torch.bfloat16, device=dev)
+    vsa.vsa_backward(prob, q, k, v, idx, num, out_c, gate, out_s, lse, dout, dq, dk, dv, dg)
+    torch.cuda.synchronize()
+    cpu = lambda t: None if t is None else t.cpu()
+    return dict(out=cpu(out), out_plain=cpu(out_plain), out_s=cpu(out_s), lse=cpu(lse), q2k_idx=cpu(idx),
+                q2k_num=cpu(num), dq=cpu(dq), dk=cpu(dk), dv=cpu(dv), dgate=cpu(dg))
+
+
+def check_dense_case(q, k, v, gate, topk, seed, tag):
+    G.note(f"case {tag}: q {tuple(q.shape)} kv {tuple(k.shape)} topk={topk} "
+           f"gate={'none' if gate is None else tuple(gate.shape)}")
+    dout = synth.output_grad(q.shape, seed)
+    gpu = run_dense_train(q, k, v, gate, dout, topk)
+    ref = BW.vsa_backward(N.f64(q), N.f64(k), N.f64(v), topk, None if gate is None else N.f64(gate), N.f64(dout))
+    G.assert_tie_free(ref)
+    G.assert_indices_equal(gpu["q2k_idx"], gpu["q2k_num"], ref)
+    assert torch.equal(gpu["out"], gpu["out_plain"]), "training forward changed the output bits"
+    N.check_out(N.f64(gpu["out"]), ref["out"])
+    N.check_sparse(N.f64(gpu["out_s"]), ref["out_s"])
+    dl = float(np.abs(N.f64(gpu["lse"]) - ref["lse"]).max())
+    G.note(f"  lse max-abs {dl:.2e}")
+    assert dl <= LSE_ABS, f"lse: max-abs {dl:.3e} > {LSE_ABS}"
+    for name in ("dq", "dk", "dv"):
+        check_grad(N.f64(gpu[name]), ref[name], name)
+    if gate is not None:
+        check_grad(N.f64(gpu["dgate"]), ref["dgate"], "dgate")
+    return gpu, ref
+
+
+def test_backward_tiny():
+    inp = synth.workload("tiny")
+    check_dense_case(inp.q, inp.k, inp.v, None, inp.topk, 2001, "tiny")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_token_gate_ragged(D):
+    inp = synth.dense_inputs(1, 2, 64 * 5 + 17, D, 2, seed=2002 + D, gated=True)
+    check_dense_case(inp.q, inp.k, inp.v, inp.gate, 2, 2003 + D, f"token gate D={D}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_full_gate_sq_ne_skv(D):
+    inp = synth.dense_inputs(2, 2, 64 * 3 + 10, D, 3, seed=2010 + D, S_kv=64 * 5 + 33)
+    gate = synth.full_gate((2, 2, 64 * 3 + 10, D), 2011 + D)
+    check_dense_case(inp.q, inp.k, inp.v, gate, 3, 2012 + D, f"full gate Sq!=Skv D={D}")
+
+
+def test_backward_every_block_selected():
+    """top-k = every KV block: the sparse part is dense attention."""
+    inp = synth.dense_inputs(1, 3, 64 * 4, 128, 4, seed=2020)
+    gpu, _ = check_dense_case(inp.q, inp.k, inp.v, None, 4, 2021, "every block")
+    assert (gpu["q2k_num"].numpy() == 4).all()
+
+
+@pytest.mark.parametrize("Sq,Skv", [(1, 200), (70, 40), (64, 64), (130, 1)])
+def test_backward_degenerate_lengths(Sq, Skv):
+    """One-token queries, a single (partial) KV block, exact block multiples."""
+    inp = synth.dense_inputs(1, 2, Sq, 64, 2, seed=2030 + Sq, S_kv=Skv, gated=True)
+    check_dense_case(inp.q, inp.k, inp.v, inp.gate, 2, 2031 + Sq + Skv, f"Sq={Sq} Skv={Skv}")
+
+
+def test_backward_is_deterministic():
+    inp = synth.dense_inputs(1, 2, 64 * 6 + 3, 128, 3, seed=2040, gated=True)
+    dout = synth.output_grad(inp.q.shape, 2041)
+    a = run_dense_train(inp.q, inp.k, inp.v, inp.gate, dout, 3)
+    b = run_dense_train(inp.q, inp.k, inp.v, inp.gate, dout, 3)
+    for name in ("dq", "dk", "dv", "dgate", "out", "lse"):
+        assert torch.equal(a[name], b[name]), name
+
+
+def test_autograd_wrapper_matches_entry_points():
+    """video_sparse_attn under autograd calls the same kernels: bitwise the
+    gradients of the direct calls."""
+    inp = synth.dense_inputs(1, 2, 64 * 3 + 5, 64, 2, seed=2050, gated=True)
+    dout = synth.output_grad(inp.q.shape, 2051)
+    direct = run_dense_train(inp.q, inp.k, inp.v, inp.gate, dout, 2)
+    q, k, v, g = (t.to(G.DEV).requires_grad_(True) for t in (inp.q, inp.k, inp.v, inp.gate))
+    out = vsa.video_sparse_attn(q, k, v, 2, g)
+    out.backward(dout.to(G.DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach().cpu(), direct["out"])
+    for t, name in ((q, "dq"), (k, "dk"), (v, "dv"), (g, "dgate")):
+        assert torch.equal(t.grad.cpu(), direct[name]), name
+
+
+# ---------------------------------------------------------------------------
+# packed sequences: every sequence against its own dense oracle
+# ---------------------------------------------------------------------------
+
+def test_backward_varlen_matches_per_sequence():
+    seqlens_q = [64 * 2 + 7, 64 * 4, 30]
+    seqlens_kv = [64 * 3 + 50, 64 * 2 + 1, 64 * 5]
+    topk = [2, 1, 3]
+    H, D = 2, 128
+    inp = synth.varlen_inputs(seqlens_q, seqlens_kv, H, D, topk, seed=2060, gated=True)
+    G.note(f"case varlen: seqlens_q={seqlens_q} seqlens_kv={seqlens_kv} topk={topk}")
+    dev = G.DEV
+    meta = vsa.vsa_build_metadata(seqlens_q, seqlens_kv, topk, device=dev)
+    prob = meta.problem(H, D)
+    q, k, v, gate = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.gate))
+    dout_cpu = synth.output_grad(inp.q.shape, 2061)
+    dout = dout_cpu.to(dev)
+    cs, isz, ns = vsa.block_shapes(prob)
+    out_c = torch.empty(cs, dtype=torch.float32, device=dev)
+    idx = torch.empty(isz, dtype=torch.int32, device=dev)
+    num = torch.empty(ns, dtype=torch.int32, device=dev)
+    vsa.vsa_coarse_topk(prob, q, k, v, out_c, idx, num, vsa.alloc_workspace(prob, dev))
+    out = torch.full_like(q, float("nan"))
+    out_s = torch.full_like(q, float("nan"))
+    lse = torch.empty(vsa.lse_shape(prob), dtype=torch.float32, device=dev)
+    vsa.vsa_sparse_attn_combine_train(prob, q, k, v, idx, num, out_c, gate, out, out_s, lse)
+    nan = float("nan")
+    dq, dk, dv = (torch.full_like(t, nan) for t in (q, k, v))
+    dg = torch.full_like(gate, nan)
+    vsa.vsa_backward(prob, q, k, v, idx, num, out_c, gate, out_s, lse, dout, dq, dk, dv, dg)
+    torch.cuda.synchronize()
+    dq, dk, dv, dg, lse = (t.cpu() for t in (dq, dk, dv, dg, lse))
+    oq = okv = 0
+    for s, (sq, skv) in enumerate(zip(seqlens_q, seqlens_kv)):
+        per = inp.per_seq[s]
+        g64 = lambda t: N.f64(t)[None]
+        ref = BW.vsa_backward(g64(per["q"]), g64(per["k"]), g64(per["v"]), topk[s], g64(per["gate"]),
+                              N.f64(dout_cpu[:, oq:oq + sq])[None])
+        G.assert_tie_free(ref)
+        G.note(f"  sequence {s}")
+        check_grad(N.f64(dq[:, oq:oq + sq]), ref["dq"][0], "dq")
+        check_grad(N.f64(dk[:, okv:okv + skv]), ref["dk"][0], "dk")
+        check_grad(N.f64(dv[:, okv:okv + skv]), ref["dv"][0], "dv")
+        check_grad(N.f64(dg[:, oq:oq + sq]), ref["dgate"][0], "dgate")
+        dl = float(np.abs(N.f64(lse[:, oq:oq + sq]) - ref["lse"][0]).max())
+        assert dl <= LSE_ABS, f"lse of sequence {s}: {dl:.3e}"
+        nq, nkv = -(-sq // 64), -(-skv // 64)
+        # padding slots of every gradient are written with 0
+        assert (dq[:, oq + sq:oq + 64 * nq] == 0).all() and (dg[:, oq + sq:oq + 64 * nq] == 0).all()
+        assert (dk[:, okv + skv:okv + 64 * nkv] == 0).all() and (dv[:, okv + skv:okv + 64 * nkv] == 0).all()
+        oq += 64 * nq
+        okv += 64 * nkv

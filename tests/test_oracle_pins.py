@@ -142,6 +142,7 @@ def _tiles_reverse_is_forward(T, H, W, tile=(4, 4, 4)):
 
 
 _forward_torch_ok = BW.forward_torch
+_lse_ok = BW.sparse_row_lse2
 
 
 def _bw_gate_on_sparse(q, k, v, gate, idx, block=64):
@@ -156,6 +157,31 @@ def _bw_gate_on_sparse(q, k, v, gate, idx, block=64):
 def _bw_value_detached(q, k, v, gate, idx, block=64):
     # gradient stops at v in the sparse branch (a slip in the restatement)
     return _forward_torch_ok(q, k, v.detach(), gate, idx, block)
+
+
+def _lse_natural_log(q, k, idx, block=64):
+    # natural log instead of base 2
+    return _lse_ok(q, k, idx, block) * math.log(2.0)
+
+
+def _lse_unscaled(q, k, idx, block=64):
+    # scores without the 1 / sqrt(D) factor
+    return _lse_ok(np.asarray(q) * math.sqrt(np.asarray(q).shape[-1]), k, idx, block)
+
+
+def _lse_max_only(q, k, idx, block=64):
+    # the row max of the scaled scores taken for the log-sum-exp
+    q, k = np.asarray(q, dtype=np.float64), np.asarray(k, dtype=np.float64)
+    B, H, Sq, D = q.shape
+    qs, ks = O.block_sizes(Sq), O.block_sizes(k.shape[2])
+    out = np.empty((B, H, Sq))
+    for b in range(B):
+        for h in range(H):
+            for i, n in enumerate(qs):
+                keys = np.concatenate([k[b, h, 64 * j: 64 * j + ks[j]] for j in idx[b, h, i]])
+                s_ = q[b, h, 64 * i: 64 * i + n] @ keys.T / math.sqrt(D)
+                out[b, h, 64 * i: 64 * i + n] = s_.max(axis=1) / math.log(2.0)
+    return out
 
 
 MISTAKES = {
@@ -176,6 +202,9 @@ MISTAKES = {
     "tiles_reverse_is_forward": ("tiles.tile_partition", _tiles_reverse_is_forward),
     "backward_gate_on_sparse": ("backward.forward_torch", _bw_gate_on_sparse),
     "backward_value_detached": ("backward.forward_torch", _bw_value_detached),
+    "lse_natural_log": ("backward.sparse_row_lse2", _lse_natural_log),
+    "lse_unscaled": ("backward.sparse_row_lse2", _lse_unscaled),
+    "lse_max_only": ("backward.sparse_row_lse2", _lse_max_only),
 }
 
 

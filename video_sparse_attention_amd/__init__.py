@@ -1,4 +1,4 @@
-"""Video sparse attention (VSA) forward for AMD Instinct MI355X (gfx950).
+"""Video sparse attention (VSA) forward and backward for AMD Instinct MI355X (gfx950).
 
 The computation lives in ``lib/libvsa.so`` (hand-written HIP kernels behind
 the C ABI of ``include/vsa.h``); this package is its thin PyTorch binding.
@@ -28,6 +28,12 @@ from .binding import (  # noqa: E402,F401
     vsa_sparse_attn_combine,
     vsa_sparse_attn_from_indices,
     vsa_workspace_size,
+    alloc_backward_workspace,
+    lse_shape,
+    video_sparse_attn,
+    vsa_backward,
+    vsa_backward_workspace_size,
+    vsa_sparse_attn_combine_train,
 )
 
 __all__ = [
@@ -35,4 +41,6 @@ __all__ = [
     "token_shapes", "DEFAULT_TILE", "tile_gather", "tile_partition", "tile_scatter",
     "vsa_build_tile_metadata", "vsa_forward_video", "vsa_build_metadata", "vsa_coarse_topk", "vsa_combine", "vsa_forward",
     "vsa_forward_varlen", "vsa_sparse_attn_combine", "vsa_sparse_attn_from_indices", "vsa_workspace_size",
+    "alloc_backward_workspace", "lse_shape", "video_sparse_attn", "vsa_backward",
+    "vsa_backward_workspace_size", "vsa_sparse_attn_combine_train",
 ]

@@ -58,6 +58,10 @@ SIGNATURES = {
     "vsa_sparse_attn_from_indices": (i32, [P_PROBLEM, vp, vp, vp, vp, vp, vp, vp]),
     "vsa_sparse_attn_combine": (i32, [P_PROBLEM, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]),
     "vsa_combine": (i32, [P_PROBLEM, vp, vp, i32, vp, vp, vp]),
+    "vsa_sparse_attn_combine_train": (i32, [P_PROBLEM, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
+    "vsa_backward_workspace_size": (sz, [P_PROBLEM]),
+    "vsa_backward": (i32, [P_PROBLEM, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
+                           vp, vp, vp, vp, vp, sz, vp]),
     "vsa_forward": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
                           i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]),
     "vsa_forward_varlen": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,

@@ -29,7 +29,7 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need(t: torch.Tensor, name: str, dtype, shape=None, contiguous=True):
+def _need(t: torch.Tensor, name: str, dtype, shape=None, contiguous=True, grad_ok=False):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
@@ -40,8 +40,9 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None, contiguous=True):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if t.requires_grad:
-        raise RuntimeError(f"{name} requires grad: the VSA forward here has no backward")
+    if t.requires_grad and not grad_ok and torch.is_grad_enabled():
+        raise RuntimeError(f"{name} requires grad: this entry point records no gradient, "
+                           "use video_sparse_attn for training")
 
 
 def _gate_args(gate: Optional[torch.Tensor], token_shape, full_shape):
@@ -238,6 +239,135 @@ def vsa_combine(problem: VsaProblem, out_c, gate, out) -> None:
     _abi.check(_abi.load().vsa_combine(
         ctypes.byref(problem), _ptr(out_c), _ptr(gate), mode, st, _ptr(out),
         _stream(out.device)), "vsa_combine")
+
+
+# ---------------------------------------------------------------------------
+# training: forward that keeps out_s and lse, backward
+# ---------------------------------------------------------------------------
+
+def lse_shape(problem: VsaProblem):
+    return token_shapes(problem)[0][:-1]
+
+
+def vsa_sparse_attn_combine_train(problem: VsaProblem, q, k, v, q2k_idx, q2k_num, out_c, gate, out,
+                                  out_s, lse) -> None:
+    """vsa_sparse_attn_combine that also writes ``out_s`` (the bf16 sparse
+    attention output on its own) and ``lse`` (float32 per query row, log2 of
+    the softmax denominator in exp2 units of the scaled scores)."""
+    _check_qkv(problem, q, k, v)
+    cs, isz, ns = block_shapes(problem)
+    if tuple(q2k_idx.shape[:-1]) != tuple(isz[:-1]):
+        raise ValueError(f"q2k_idx has shape {tuple(q2k_idx.shape)}, expected {isz[:-1]} + (k,)")
+    _need(q2k_idx, "q2k_idx", torch.int32)
+    _need(q2k_num, "q2k_num", torch.int32, ns)
+    _need(out_c, "out_c", torch.float32, cs)
+    qs = token_shapes(problem)[0]
+    _need(out, "out", torch.bfloat16, qs)
+    _need(out_s, "out_s", torch.bfloat16, qs)
+    _need(lse, "lse", torch.float32, lse_shape(problem))
+    mode, st = _gate_args(gate, *_gate_shapes(problem))
+    _abi.check(_abi.load().vsa_sparse_attn_combine_train(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(q2k_idx), _ptr(q2k_num), _ptr(out_c),
+        _ptr(gate), mode, st, _ptr(out), _ptr(out_s), _ptr(lse), _stream(q.device)),
+        "vsa_sparse_attn_combine_train")
+
+
+def vsa_backward_workspace_size(problem: VsaProblem) -> int:
+    return int(_abi.load().vsa_backward_workspace_size(ctypes.byref(problem)))
+
+
+def alloc_backward_workspace(problem: VsaProblem, device) -> torch.Tensor:
+    n = vsa_backward_workspace_size(problem)
+    if n == 0:
+        raise VsaError(_abi.VSA_ERR_SHAPE, (_abi.load().vsa_last_error() or b"").decode(),
+                       "vsa_backward_workspace_size")
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + n]
+
+
+def vsa_backward(problem: VsaProblem, q, k, v, q2k_idx, q2k_num, out_c, gate, out_s, lse, dout,
+                 dq, dk, dv, dgate=None, workspace=None) -> None:
+    """Gradients of ``sum(out * dout)`` of the forward with these inputs and
+    routing (vsa_backward): writes ``dq``, ``dk``, ``dv`` and, with a gate,
+    ``dgate`` (contiguous, the gate's shape)."""
+    _check_qkv(problem, q, k, v)
+    cs, isz, ns = block_shapes(problem)
+    if tuple(q2k_idx.shape[:-1]) != tuple(isz[:-1]):
+        raise ValueError(f"q2k_idx has shape {tuple(q2k_idx.shape)}, expected {isz[:-1]} + (k,)")
+    _need(q2k_idx, "q2k_idx", torch.int32)
+    _need(q2k_num, "q2k_num", torch.int32, ns)
+    _need(out_c, "out_c", torch.float32, cs)
+    qs, ks = token_shapes(problem)
+    _need(out_s, "out_s", torch.bfloat16, qs)
+    _need(lse, "lse", torch.float32, lse_shape(problem))
+    _need(dout, "dout", torch.bfloat16, qs)
+    _need(dq, "dq", torch.bfloat16, qs)
+    _need(dk, "dk", torch.bfloat16, ks)
+    _need(dv, "dv", torch.bfloat16, ks)
+    mode, st = _gate_args(gate, *_gate_shapes(problem))
+    if mode != VSA_GATE_NONE:
+        _need(dgate, "dgate", torch.bfloat16, gate.shape)
+    if workspace is None:
+        workspace = alloc_backward_workspace(problem, q.device)
+    _need(workspace, "workspace", torch.uint8)
+    _abi.check(_abi.load().vsa_backward(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(q2k_idx), _ptr(q2k_num), _ptr(out_c),
+        _ptr(gate), mode, st, _ptr(out_s), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(dgate if mode != VSA_GATE_NONE else None), _ptr(workspace), workspace.numel(),
+        _stream(q.device)), "vsa_backward")
+
+
+class _VideoSparseAttn(torch.autograd.Function):
+    """Autograd wrapper: forward = vsa_coarse_topk + vsa_sparse_attn_combine_train,
+    backward = vsa_backward (the routing is held fixed)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, gate, topk):
+        B, H, Sq, D = q.shape
+        problem = dense_problem(B, H, Sq, k.shape[2], D, topk)
+        q, k, v = q.detach(), k.detach(), v.detach()
+        g = None if gate is None else gate.detach()
+        cs, isz, ns = block_shapes(problem)
+        dev = q.device
+        out_c = torch.empty(cs, dtype=torch.float32, device=dev)
+        idx = torch.empty(isz, dtype=torch.int32, device=dev)
+        num = torch.empty(ns, dtype=torch.int32, device=dev)
+        vsa_coarse_topk(problem, q, k, v, out_c, idx, num, alloc_workspace(problem, dev))
+        out = torch.empty_like(q)
+        out_s = torch.empty_like(q)
+        lse = torch.empty(lse_shape(problem), dtype=torch.float32, device=dev)
+        vsa_sparse_attn_combine_train(problem, q, k, v, idx, num, out_c, g, out, out_s, lse)
+        ctx.topk = topk
+        ctx.has_gate = g is not None
+        ctx.save_for_backward(q, k, v, *( [g] if g is not None else []), idx, num, out_c, out_s, lse)
+        ctx.mark_non_differentiable(idx, num)
+        return out, idx, num
+
+    @staticmethod
+    def backward(ctx, dout, _didx, _dnum):
+        saved = list(ctx.saved_tensors)
+        q, k, v = saved[:3]
+        g = saved[3] if ctx.has_gate else None
+        idx, num, out_c, out_s, lse = saved[4 if ctx.has_gate else 3:]
+        B, H, Sq, D = q.shape
+        problem = dense_problem(B, H, Sq, k.shape[2], D, ctx.topk)
+        dout = dout.contiguous()
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dg = None if g is None else torch.empty(g.shape, dtype=torch.bfloat16, device=q.device)
+        vsa_backward(problem, q, k, v, idx, num, out_c, g, out_s, lse, dout, dq, dk, dv, dg)
+        return dq, dk, dv, dg, None
+
+
+def video_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int,
+                      gate: Optional[torch.Tensor] = None, return_routing: bool = False):
+    """Differentiable VSA on dense ``[B, H, S, D]`` bf16 tensors: the forward of
+    ``vsa_forward`` and, through autograd, the gradients of q, k, v and the
+    gate (``[B, H, Sq]`` or ``[B, H, Sq, D]``) from vsa_backward."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, S, D]")
+    out, idx, num = _VideoSparseAttn.apply(q, k, v, gate, topk)
+    return (out, idx, num) if return_routing else out
 
 
 # ---------------------------------------------------------------------------

@@ -36,6 +36,28 @@ __host__ __device__ inline int v_swz(int row) {
     return (4 * (row & 3) + 2 * ((row >> 1) & 1)) & (CH - 1);
 }
 
+// XOR for a tile read both ways: by rows (ds_read_b128, as K above) and
+// transposed (ds_read_b64_tr_b16, as V above), which the backward kernels do
+// with K, Q and dO.  Row reads need distinct values over 16 consecutive rows
+// (D = 128) or over the 8 rows of one parity among 16 (D = 64, two rows per
+// 256 bytes); a transposed read of rows 4a..4a+3 needs the four (D = 128) or
+// the two same-parity (D = 64) rows in different groups of four chunks.
+// D = 128: 4 (row & 3) + ((row >> 2) & 3); D = 64: 4 ((row >> 1) & 1) +
+// ((row >> 2) & 3).  Depends on the row only through bits 0..3, and for D = 128
+// on copy instruction n only through n & 1 (as k_swz).
+template <int CH>
+__host__ __device__ inline int dual_swz(int row) {
+    return CH == 16 ? 4 * (row & 3) + ((row >> 2) & 3) : 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+}
+
+// Swizzle kinds of a tile: read by rows, transposed, or both.
+enum { kSwzRow = 0, kSwzTr = 1, kSwzDual = 2 };
+
+template <int CH, int SW>
+__host__ __device__ inline int tile_swz(int row) {
+    return SW == kSwzRow ? k_swz<CH>(row) : (SW == kSwzTr ? v_swz<CH>(row) : dual_swz<CH>(row));
+}
+
 // Element offset of logical chunk c of row `row` in a [64][8*CH] tile.
 template <int CH>
 __host__ __device__ inline int tile_off(int row, int c, int swz) {
@@ -50,11 +72,11 @@ __host__ __device__ inline int load_chunk_pos(int n, int wave, int lane) { retur
 // Byte offset, inside a full 64-row block of the source tensor, of the chunk
 // that copy instruction n (n = 0 or 1) of (wave, lane) fetches; instruction
 // n + 2m fetches the one 4096 m bytes further (rows are 16 * CH bytes).
-template <int CH, bool IS_V>
+template <int CH, int SW>
 __host__ __device__ inline int lane_src_offset(int wave, int lane, int n) {
     const int p = load_chunk_pos(n, wave, lane);
     const int row = p / CH;
-    const int sw = IS_V ? v_swz<CH>(row) : k_swz<CH>(row);
+    const int sw = tile_swz<CH, SW>(row);
     return row * CH * 16 + 16 * ((p % CH) ^ sw);
 }
 

@@ -1,0 +1,779 @@
+// Backward pass of the VSA forward: gradients of q, k, v and the gate for a
+// given output gradient, with the routing (q2k_idx) held fixed - the top-k
+// choice is piecewise constant in the inputs and carries no gradient.
+// ("[kernel] Add varlen support for block-sparse attention", Test plan:
+// backward of the block-sparse attention; "[chore] release fastvideo-kernel
+// 0.3.0", Block-sparse / VSA attention improvements: forward and backward.)
+//
+// With out = out_c[block] * g + O (O the block-sparse attention output, out_c
+// the coarse attention of the block means, g the gate or 1) the launches are:
+//   1. combine backward, per query block: the softmax-backward row term
+//      delta[t] = dout[t] . O[t], dOc[block] = sum_t dout[t] * g[t],
+//      dg[t] = dout[t] * out_c[block] (summed over d for a per-token gate), and
+//      the row statistics (log-sum-exp, delta) of the block in one 512-byte row;
+//   2. the block means again (the forward's pool kernel);
+//   3. coarse backward in float64 at block level, rows then columns: P and dS
+//      of the coarse softmax, dQc = dS Kc / sqrt(D); dKc = dS^T Qc / sqrt(D),
+//      dVc = P^T dOc;
+//   4. the inverse routing: for every KV block, the query blocks whose list
+//      holds it, ascending;
+//   5. dQ per query block over its listed KV blocks: S and P = exp(S - lse)
+//      again, dP = dO V^T, dS = P (dP - delta), dQ = dS K / sqrt(D), plus
+//      dQc / (block size) - the gradient through the block mean;
+//   6. dK, dV per KV block over the query blocks that listed it: dV = P^T dO,
+//      dK = dS^T Q / sqrt(D), plus dKc, dVc / (block size).
+// Steps 5 and 6 run bf16 MFMA with float32 accumulation on the operand
+// layouts of the forward kernel (32x32x16 tiles, products computed
+// transposed so that every lane owns one column), recompute P from the saved
+// log-sum-exp instead of storing it, and each write every output row once
+// (no atomics, deterministic).
+#include <math.h>
+
+#include "attn_common.hpp"
+
+namespace vsa {
+namespace {
+
+using namespace attn;
+
+constexpr int kThreads = 256;      // block-level kernels
+constexpr int kAttnThreads = 128;  // MFMA kernels: 2 waves, 32 columns each
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ double wave_sum(double x) {
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+// block-wide reductions over kThreads threads (every thread gets the result)
+__device__ __forceinline__ double block_sum(double x, double* red) {
+    x = wave_sum(x);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    double t = 0.0;
+    for (int w = 0; w < kThreads / 64; ++w) t += red[w];
+    return t;
+}
+__device__ __forceinline__ double block_max(double x, double* red) {
+    for (int o = 32; o > 0; o >>= 1) x = fmax(x, __shfl_xor(x, o));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    double t = -INFINITY;
+    for (int w = 0; w < kThreads / 64; ++w) t = fmax(t, red[w]);
+    return t;
+}
+
+// Sequence owning global KV block g (packed): largest s with cu_kv[s] <= g.
+__device__ __forceinline__ int seq_of_kvblock(const DevProblem& P, int g) {
+    int lo = 0, hi = P.nseq - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (P.cu_kv[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// ---------------------------------------------------------------------------
+// 1. combine backward: grid (query blocks: nQ or total_q, H, B or 1)
+// ---------------------------------------------------------------------------
+template <int D, int MODE>
+__global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
+    DevProblem P, const uint16_t* __restrict__ dout, const uint16_t* __restrict__ out_s,
+    const float* __restrict__ out_c, const uint16_t* __restrict__ gate, int64_t gs0, int64_t gs1, int64_t gs2,
+    const float* __restrict__ lse, float* __restrict__ rs, double* __restrict__ doc, uint16_t* __restrict__ dgate) {
+    constexpr int QD = D / 4;  // d values per thread, 4 threads per token
+    __shared__ float red[kBlock][D + 1];
+    int s, i;
+    const int h = blockIdx.y;
+    if (!P.packed) {
+        i = blockIdx.x;
+        s = blockIdx.z;
+    } else {
+        s = seq_of_qblock(P, blockIdx.x);
+        i = (int)blockIdx.x - clampi(P.cu_q[s], 0, P.total_q);
+    }
+    const SeqView sv = seq_view(P, s, h);
+    if (i < 0 || i >= sv.nq) return;
+    const int size = q_block_size(P, sv, i);
+    const int64_t row0 = sv.qrow_base + (int64_t)kBlock * i;
+    const int64_t qb = sv.qblk_base + i;
+    // token index of the block's first row along the gate's token axis
+    const int64_t tok0 = (int64_t)kBlock * (P.packed ? sv.qblk0 + i : i);
+    const int64_t g0 = (P.packed ? 0 : (int64_t)s * gs0) + (int64_t)h * gs1;
+    const int t = threadIdx.x / 4, d0 = (threadIdx.x % 4) * QD;
+    const float* ocr = out_c + qb * D;
+    float dpart = 0.f, gpart = 0.f;
+    float contrib[QD];
+#pragma unroll
+    for (int e = 0; e < QD; ++e) contrib[e] = 0.f;
+    if (t < size) {
+        const int64_t r = row0 + t;
+        const int64_t goff = g0 + (tok0 + t) * gs2;
+        const float g = MODE == VSA_GATE_TOKEN ? bf16_lo(gate[goff]) : 1.f;
+#pragma unroll
+        for (int c = 0; c < QD / 8; ++c) {
+            const uint4 a = *reinterpret_cast<const uint4*>(dout + r * D + d0 + 8 * c);
+            const uint4 o = *reinterpret_cast<const uint4*>(out_s + r * D + d0 + 8 * c);
+            uint4 gg = make_uint4(0, 0, 0, 0);
+            if (MODE == VSA_GATE_FULL) gg = *reinterpret_cast<const uint4*>(gate + goff + d0 + 8 * c);
+            const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, ow[4] = {o.x, o.y, o.z, o.w};
+            const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
+            uint32_t dg[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int dd = 8 * c + 2 * e;
+                const float a0 = bf16_lo(aw[e]), a1 = bf16_hi(aw[e]);
+                dpart = fmaf(a0, bf16_lo(ow[e]), dpart);
+                dpart = fmaf(a1, bf16_hi(ow[e]), dpart);
+                const float c0 = ocr[d0 + dd], c1 = ocr[d0 + dd + 1];
+                if (MODE == VSA_GATE_FULL) {
+                    contrib[dd] = a0 * bf16_lo(gw[e]);
+                    contrib[dd + 1] = a1 * bf16_hi(gw[e]);
+                    dg[e] = bf16pair(a0 * c0, a1 * c1);
+                } else {
+                    contrib[dd] = a0 * g;
+                    contrib[dd + 1] = a1 * g;
+                    if (MODE == VSA_GATE_TOKEN) gpart = fmaf(a1, c1, fmaf(a0, c0, gpart));
+                }
+            }
+            if (MODE == VSA_GATE_FULL)
+                *reinterpret_cast<uint4*>(dgate + r * D + d0 + 8 * c) = make_uint4(dg[0], dg[1], dg[2], dg[3]);
+        }
+    } else if (MODE == VSA_GATE_FULL && P.packed) {
+#pragma unroll
+        for (int c = 0; c < QD / 8; ++c)
+            *reinterpret_cast<uint4*>(dgate + (row0 + t) * D + d0 + 8 * c) = make_uint4(0, 0, 0, 0);
+    }
+    // the 4 threads of a token are consecutive lanes
+    dpart += __shfl_xor(dpart, 1);
+    dpart += __shfl_xor(dpart, 2);
+    gpart += __shfl_xor(gpart, 1);
+    gpart += __shfl_xor(gpart, 2);
+    if (threadIdx.x % 4 == 0) {
+        const bool valid = t < size;
+        // padding rows: lse = +inf makes every recomputed probability 0
+        rs[qb * kStatRow + t] = valid ? lse[row0 + t] : INFINITY;
+        rs[qb * kStatRow + kBlock + t] = valid ? dpart : 0.f;
+        if (MODE == VSA_GATE_TOKEN && (valid || P.packed))
+            dgate[row0 + t] = (uint16_t)(bf16pair(valid ? gpart : 0.f, 0.f) & 0xffffu);
+    }
+#pragma unroll
+    for (int e = 0; e < QD; ++e) red[t][d0 + e] = contrib[e];
+    __syncthreads();
+    for (int d = threadIdx.x; d < D; d += kThreads) {
+        double acc = 0.0;
+        for (int tt = 0; tt < size; ++tt) acc += (double)red[tt][d];
+        doc[qb * D + d] = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. coarse backward (float64): rows, then columns.  Grid (nQ or max_q /
+// nKV or max_kv, H, sequences).
+// ---------------------------------------------------------------------------
+// Row i: P_j = softmax_j(Qc_i . Kc_j / sqrt(D)), dP_j = dOc_i . Vc_j,
+// dS_j = P_j (dP_j - sum_l P_l dP_l), built in place in the rows of pbuf /
+// dsbuf (row length ld; the workgroup's barriers order its own global
+// accesses), dQc_i = sum_j dS_j Kc_j / sqrt(D).
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_coarse_rows_kernel(DevProblem P, const double* __restrict__ qc,
+                                                                   const double* __restrict__ kc,
+                                                                   const double* __restrict__ vc,
+                                                                   const double* __restrict__ doc,
+                                                                   double* __restrict__ pbuf,
+                                                                   double* __restrict__ dsbuf,
+                                                                   double* __restrict__ dqc, int ld, double scale) {
+    __shared__ double qrow[D], drow[D], red[kThreads / 64], part[2][D];
+    const int s = blockIdx.z, h = blockIdx.y, i = blockIdx.x;
+    const SeqView sv = seq_view(P, s, h);
+    if (i >= sv.nq) return;
+    const int64_t qb = sv.qblk_base + i;
+    double* sl = pbuf + qb * ld;   // scores, then weights, then P
+    double* pl = dsbuf + qb * ld;  // dP, then dS
+    const int nkv = sv.nkv;
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    for (int d = threadIdx.x; d < D; d += kThreads) {
+        qrow[d] = qc[qb * D + d];
+        drow[d] = doc[qb * D + d];
+    }
+    __syncthreads();
+    // one wave per KV block, lanes over d (coalesced rows of Kc and Vc)
+    double mx = -INFINITY;
+    for (int j = wave; j < nkv; j += kThreads / 64) {
+        const double* kr = kc + (sv.kvblk_base + j) * D;
+        const double* vr = vc + (sv.kvblk_base + j) * D;
+        double sc = 0.0, dp = 0.0;
+        for (int d = lane; d < D; d += 64) {
+            sc = fma(qrow[d], kr[d], sc);
+            dp = fma(drow[d], vr[d], dp);
+        }
+        sc = wave_sum(sc);
+        dp = wave_sum(dp);
+        if (lane == 0) {
+            sl[j] = sc;
+            pl[j] = dp;
+        }
+        mx = fmax(mx, sc);
+    }
+    mx = block_max(mx, red);  // its barriers also publish sl / pl
+    double sum = 0.0;
+    for (int j = threadIdx.x; j < nkv; j += kThreads) {
+        const double w = exp((sl[j] - mx) * scale);
+        sl[j] = w;
+        sum += w;
+    }
+    sum = block_sum(sum, red);
+    double dot = 0.0;
+    for (int j = threadIdx.x; j < nkv; j += kThreads) {
+        const double p = sl[j] / sum;
+        sl[j] = p;
+        dot += p * pl[j];
+    }
+    dot = block_sum(dot, red);
+    for (int j = threadIdx.x; j < nkv; j += kThreads) pl[j] = sl[j] * (pl[j] - dot);
+    __syncthreads();
+    // dQc: thread (d, half) sums every other KV block
+    const int d = threadIdx.x % D, half = threadIdx.x / D;
+    if (half < 2) {
+        double acc = 0.0;
+        for (int j = half; j < nkv; j += 2) acc = fma(pl[j], kc[(sv.kvblk_base + j) * D + d], acc);
+        part[half][d] = acc;
+    }
+    __syncthreads();
+    if (threadIdx.x < D) dqc[qb * D + threadIdx.x] = (part[0][threadIdx.x] + part[1][threadIdx.x]) * scale;
+}
+
+// Column j: dKc_j = sum_i dS_ij Qc_i / sqrt(D), dVc_j = sum_i P_ij dOc_i.
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_coarse_cols_kernel(DevProblem P, const double* __restrict__ qc,
+                                                                   const double* __restrict__ doc,
+                                                                   const double* __restrict__ pbuf,
+                                                                   const double* __restrict__ dsbuf,
+                                                                   double* __restrict__ dkc,
+                                                                   double* __restrict__ dvc, int ld, double scale) {
+    __shared__ double part[2][2][D];
+    const int s = blockIdx.z, h = blockIdx.y, j = blockIdx.x;
+    const SeqView sv = seq_view(P, s, h);
+    if (j >= sv.nkv) return;
+    const int d = threadIdx.x % D, half = threadIdx.x / D;
+    if (half < 2) {
+        double ak = 0.0, av = 0.0;
+        for (int i = half; i < sv.nq; i += 2) {
+            const int64_t qb = sv.qblk_base + i;
+            ak = fma(dsbuf[qb * ld + j], qc[qb * D + d], ak);
+            av = fma(pbuf[qb * ld + j], doc[qb * D + d], av);
+        }
+        part[0][half][d] = ak;
+        part[1][half][d] = av;
+    }
+    __syncthreads();
+    if (threadIdx.x < D) {
+        const int64_t kb = sv.kvblk_base + j;
+        dkc[kb * D + threadIdx.x] = (part[0][0][threadIdx.x] + part[0][1][threadIdx.x]) * scale;
+        dvc[kb * D + threadIdx.x] = part[1][0][threadIdx.x] + part[1][1][threadIdx.x];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 4. inverse routing: one wave per KV block, grid (ceil(max KV blocks / 4),
+// H, sequences)
+// ---------------------------------------------------------------------------
+// Whether x is in the ascending list row[0..n).
+__device__ __forceinline__ bool list_has(const int* row, int n, int x) {
+    int lo = 0, hi = n;  // first position with row[pos] >= x
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (row[mid] < x) lo = mid + 1; else hi = mid;
+    }
+    return lo < n && row[lo] == x;
+}
+
+__global__ __launch_bounds__(kThreads) void bwd_k2q_kernel(DevProblem P, const int* __restrict__ idx,
+                                                           const int* __restrict__ num, int* __restrict__ k2q,
+                                                           int* __restrict__ k2q_num, int ldq) {
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int s = blockIdx.z, h = blockIdx.y;
+    const int j = blockIdx.x * (kThreads / 64) + wave;
+    const SeqView sv = seq_view(P, s, h);
+    if (j >= sv.nkv) return;
+    const int key = j + sv.idx_rebase;  // as stored in q2k_idx
+    const int64_t kb = sv.kvblk_base + j;
+    int count = 0;
+    for (int i0 = 0; i0 < sv.nq; i0 += 64) {
+        const int i = i0 + lane;
+        bool member = false;
+        if (i < sv.nq) {
+            const int64_t qb = sv.qblk_base + i;
+            member = list_has(idx + qb * P.idx_row, clampi(num[qb], 0, P.idx_row), key);
+        }
+        const uint64_t mask = __ballot(member);
+        const uint64_t below = mask & ((1ull << lane) - 1ull);
+        if (member) k2q[kb * ldq + count + __popcll(below)] = i;
+        count += __popcll(mask);
+    }
+    if (lane == 0) k2q_num[kb] = count;
+}
+
+// ---------------------------------------------------------------------------
+// shared pieces of the two MFMA kernels
+// ---------------------------------------------------------------------------
+// Row operand of a [64][D] tile: lane (l32, hh) gets T[32 mt + l32][16 ks +
+// 8 hh .. + 7] (A operand of a 32x32x16 product whose rows are the tile's rows).
+template <int CH, int SW>
+__device__ __forceinline__ bf16x8 row_operand(const uint16_t* tile, int mt, int ks, int l32, int hh) {
+    const int row = 32 * mt + l32;
+    return as_bf16x8(*reinterpret_cast<const uint4*>(tile + tile_off<CH>(row, 2 * ks + hh, tile_swz<CH, SW>(row))));
+}
+// Transposed operand of a tile for k-step s4 (16 rows) and 32-row d tile dt:
+// lane (l32, hh) gets T[16 s4 + 4 hh + {0..3, 8..11}][32 dt + l32], the k-slot
+// order of a B operand taken from an accumulator (see acc_to_b).
+template <int CH, int SW>
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int s4, int dt, int hh, int tr_r, int tr_d) {
+    const int d = 32 * dt + tr_d;
+    s16x4 half[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int tok = 16 * s4 + 8 * jj + 4 * hh + tr_r;
+        const int off = tile_off<CH>(tok, d >> 3, tile_swz<CH, SW>(tok)) + (d & 7);
+        half[jj] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)tile + off));
+    }
+    const uint2 h0 = __builtin_bit_cast(uint2, half[0]);
+    const uint2 h1 = __builtin_bit_cast(uint2, half[1]);
+    return as_bf16x8(make_uint4(h0.x, h0.y, h1.x, h1.y));
+}
+// bf16 B operand of k-step s4 from two 32x32 accumulators (rows = the k
+// dimension): k-slots 8 hh .. 8 hh + 7 hold accumulator rows 16 s4 + 4 hh +
+// {0..3, 8..11}, matching tr_operand.
+__device__ __forceinline__ bf16x8 acc_to_b(const f32x16 (&a)[2], int s4) {
+    const f32x16& x = a[s4 >> 1];
+    const int b = 8 * (s4 & 1);
+    return as_bf16x8(make_uint4(bf16pair(x[b + 0], x[b + 1]), bf16pair(x[b + 2], x[b + 3]),
+                                bf16pair(x[b + 4], x[b + 5]), bf16pair(x[b + 6], x[b + 7])));
+}
+// One row of D bf16 values as the B operand of products over d: lane (l32,
+// hh) gets src[16 ks + 8 hh .. + 7] for every k-step (zeros if !valid).
+template <int KS>
+__device__ __forceinline__ void load_b_row(const uint16_t* src, bool valid, int hh, bf16x8 (&f)[KS]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (valid) u = *reinterpret_cast<const uint4*>(src + 16 * ks + 8 * hh);
+        f[ks] = as_bf16x8(u);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 5. dQ: one workgroup (2 waves) per query block; wave w owns query rows
+// 32 w .. 32 w + 31, one per lane column.  K and V of each listed KV block are
+// double-buffered in LDS (K in the dual layout: read by rows for S^T = K Q^T
+// and transposed for dQ^T = K^T dS^T; V by rows for dP^T = V dO^T).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kAttnThreads, 1) void bwd_dq_kernel(
+    DevProblem P, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ rs, const int* __restrict__ idx,
+    const int* __restrict__ num, const double* __restrict__ dqc, uint16_t* __restrict__ dq, float c_log2,
+    float scale) {
+    constexpr int KS = D / 16, DT = D / 32, CH = D / 8;
+    __shared__ __attribute__((aligned(1024))) uint16_t k_tile[2][kBlock * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_tile[2][kBlock * D];
+
+    int s, h, i;
+    SeqView sv;
+    if (!P.packed) {
+        const int N = P.nQ * P.H * P.nseq;
+        const int lin = xcd_remap(blockIdx.x, N);
+        i = lin % P.nQ;
+        const int rest = lin / P.nQ;
+        h = rest % P.H;
+        s = rest / P.H;
+        sv = seq_view(P, s, h);
+    } else {
+        const int N = P.total_q * P.H;
+        const int lin = xcd_remap(blockIdx.x, N);
+        const int g = lin % P.total_q;
+        h = lin / P.total_q;
+        s = seq_of_qblock(P, g);
+        sv = seq_view(P, s, h);
+        i = g - sv.qblk0;
+        if (i < 0 || i >= sv.nq) return;
+    }
+    const int qsize = q_block_size(P, sv, i);
+    const int64_t qrow0 = sv.qrow_base + (int64_t)kBlock * i;
+    const int64_t qb = sv.qblk_base + i;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
+    const int qr = 32 * wave + l32;
+    const bool qvalid = qr < qsize;
+
+    bf16x8 qf[KS], df[KS];
+    load_b_row<KS>(q + (qrow0 + qr) * D, qvalid, hh, qf);
+    load_b_row<KS>(dout + (qrow0 + qr) * D, qvalid, hh, df);
+    const float lse = rs[qb * kStatRow + qr];  // +inf for padding rows
+    const float delta = rs[qb * kStatRow + kBlock + qr];
+
+    f32x16 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
+
+    const int n = __builtin_amdgcn_readfirstlane(clampi(num[qb], 0, P.idx_row));
+    const_int* list = (const_int*)uniform_ptr(idx + qb * P.idx_row);
+    const_int* bs_kv = (const_int*)(P.packed ? uniform_ptr(P.bs_kv + sv.kvblk0) : nullptr);
+    const int rebase = __builtin_amdgcn_readfirstlane(sv.idx_rebase);
+    const int nkv = __builtin_amdgcn_readfirstlane(sv.nkv);
+    auto next_valid = [&](int& t) -> int {
+        for (; t < n; ++t) {
+            const int j = list[t] - rebase;
+            if (j >= 0 && j < nkv) return j;
+        }
+        return -1;
+    };
+    auto kv_size = [&](int j) -> int {
+        return P.packed ? clampi(bs_kv[j], 1, kBlock) : min(kBlock, P.Skv - kBlock * j);
+    };
+    const uint32_t koff0 = (uint32_t)lane_src_offset<CH, kSwzDual>(wave, lane, 0);
+    const uint32_t koff1 = (uint32_t)lane_src_offset<CH, kSwzDual>(wave, lane, 1) - 2048u;
+    const uint32_t voff0 = (uint32_t)lane_src_offset<CH, kSwzRow>(wave, lane, 0);
+    const uint32_t voff1 = (uint32_t)lane_src_offset<CH, kSwzRow>(wave, lane, 1) - 2048u;
+    const uint32_t k_lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&k_tile[0][0] + 1024u * wave);
+    const uint32_t v_lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&v_tile[0][0] + 1024u * wave);
+    constexpr uint32_t kTileBytes = 2u * kBlock * D;
+    const int L16 = lane & 15, g16 = lane >> 4;
+    const int tr_r = tr_token(L16), tr_d = 16 * (g16 & 1) + 4 * tr_dquad(L16);
+
+    // the operands above are in registers before the first direct copy, so
+    // the copies are the only vector-memory operations the waits count
+    __builtin_amdgcn_s_waitcnt(0);
+
+    int t = 0;
+    int j = next_valid(t);
+    int kvsize = j >= 0 ? kv_size(j) : 0;
+    if (j >= 0) {
+        const int64_t r0 = sv.kvrow_base + (int64_t)kBlock * j;
+        load_tile<D, kSwzDual>(k_lds0, k + r0 * D, kvsize, wave, lane, koff0, koff1);
+        load_tile<D, kSwzRow>(v_lds0, v + r0 * D, kvsize, wave, lane, voff0, voff1);
+    }
+    int buf = 0;
+    while (j >= 0) {
+        wait_vmcnt<0>();
+        wg_barrier();  // block j is in LDS; every wave is done with the other buffer
+        ++t;
+        const int jn = next_valid(t);
+        const int kvsize_n = jn >= 0 ? kv_size(jn) : 0;
+        if (jn >= 0) {
+            const int64_t r0 = sv.kvrow_base + (int64_t)kBlock * jn;
+            load_tile<D, kSwzDual>(k_lds0 + kTileBytes * (buf ^ 1), k + r0 * D, kvsize_n, wave, lane, koff0, koff1);
+            load_tile<D, kSwzRow>(v_lds0 + kTileBytes * (buf ^ 1), v + r0 * D, kvsize_n, wave, lane, voff0, voff1);
+        }
+        const uint16_t* kt = k_tile[buf];
+        const uint16_t* vt = v_tile[buf];
+
+        // S^T = K Q^T and dP^T = V dO^T: rows = KV tokens, lane column = query
+        f32x16 sacc[2], pacc[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sacc[mt][e] = pacc[mt][e] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<CH, kSwzDual>(kt, mt, ks, l32, hh),
+                                                                   qf[ks], sacc[mt], 0, 0, 0);
+                pacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<CH, kSwzRow>(vt, mt, ks, l32, hh),
+                                                                   df[ks], pacc[mt], 0, 0, 0);
+            }
+        // dS^T = P^T (dP^T - delta), P^T = exp2(S^T c - lse); element e of tile
+        // mt is KV token 32 mt + 8 (e / 4) + 4 hh + e % 4
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int tok = 32 * mt + 8 * (e >> 2) + 4 * hh + (e & 3);
+                float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][e], c_log2, -lse));
+                if (tok >= kvsize) p = 0.f;
+                sacc[mt][e] = p * (pacc[mt][e] - delta);
+            }
+        // dQ^T += K^T dS^T over 4 k-steps of 16 KV tokens
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            const bf16x8 b = acc_to_b(sacc, s4);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<CH, kSwzDual>(kt, s4, dt, hh, tr_r, tr_d),
+                                                                  b, acc[dt], 0, 0, 0);
+        }
+        j = jn;
+        kvsize = kvsize_n;
+        buf ^= 1;
+    }
+
+    // lane holds dQ[qr][32 dt + 8 (e / 4) + 4 hh + e % 4]
+    uint16_t* orow = dq + (qrow0 + qr) * D;
+    if (qvalid) {
+        const double* cr = dqc + qb * D;
+        const float inv_size = 1.f / (float)qsize;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int d0 = 32 * dt + 8 * jj + 4 * hh;
+                float r[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[e] = fmaf(acc[dt][4 * jj + e], scale, (float)cr[d0 + e] * inv_size);
+                *reinterpret_cast<uint2*>(orow + d0) = make_uint2(bf16pair(r[0], r[1]), bf16pair(r[2], r[3]));
+            }
+    } else if (P.packed) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * jj + 4 * hh) = make_uint2(0, 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 6. dK, dV: one workgroup (2 waves) per KV block; wave w owns KV tokens
+// 32 w .. 32 w + 31, one per lane column, with its K and V rows in registers.
+// Q and dO of each query block that listed this KV block are double-buffered
+// in LDS in the dual layout (read by rows for S = Q K^T and dP = dO V^T,
+// transposed for dV^T = dO^T P and dK^T = Q^T dS), with the block's 64
+// log-sum-exp and delta values next to them.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kAttnThreads, 1) void bwd_dkdv_kernel(
+    DevProblem P, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ rs, const int* __restrict__ k2q,
+    const int* __restrict__ k2q_num, int ldq, const double* __restrict__ dkc, const double* __restrict__ dvc,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float c_log2, float scale) {
+    constexpr int KS = D / 16, DT = D / 32, CH = D / 8;
+    __shared__ __attribute__((aligned(1024))) uint16_t q_tile[2][kBlock * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t o_tile[2][kBlock * D];
+    __shared__ __attribute__((aligned(16))) float stats[2][kStatRow];
+
+    int s, h, j;
+    SeqView sv;
+    if (!P.packed) {
+        const int N = P.nKV * P.H * P.nseq;
+        const int lin = xcd_remap(blockIdx.x, N);
+        j = lin % P.nKV;
+        const int rest = lin / P.nKV;
+        h = rest % P.H;
+        s = rest / P.H;
+        sv = seq_view(P, s, h);
+    } else {
+        const int N = P.total_kv * P.H;
+        const int lin = xcd_remap(blockIdx.x, N);
+        const int g = lin % P.total_kv;
+        h = lin / P.total_kv;
+        s = seq_of_kvblock(P, g);
+        sv = seq_view(P, s, h);
+        j = g - sv.kvblk0;
+        if (j < 0 || j >= sv.nkv) return;
+    }
+    const int kvsize = kv_block_size(P, sv, j);
+    const int64_t kvrow0 = sv.kvrow_base + (int64_t)kBlock * j;
+    const int64_t kb = sv.kvblk_base + j;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
+    const int kr = 32 * wave + l32;
+    const bool kvalid = kr < kvsize;
+
+    bf16x8 kf[KS], vf[KS];
+    load_b_row<KS>(k + (kvrow0 + kr) * D, kvalid, hh, kf);
+    load_b_row<KS>(v + (kvrow0 + kr) * D, kvalid, hh, vf);
+
+    f32x16 dka[DT], dva[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dka[dt][e] = dva[dt][e] = 0.f;
+
+    const int m = __builtin_amdgcn_readfirstlane(clampi(k2q_num[kb], 0, ldq));
+    const_int* list = (const_int*)uniform_ptr(k2q + kb * ldq);
+    const_int* bs_q = (const_int*)(P.packed ? uniform_ptr(P.bs_q + sv.qblk0) : nullptr);
+    const int nq = __builtin_amdgcn_readfirstlane(sv.nq);
+    auto q_size = [&](int i) -> int {
+        return P.packed ? clampi(bs_q[i], 1, kBlock) : min(kBlock, P.Sq - kBlock * i);
+    };
+    const uint32_t off0 = (uint32_t)lane_src_offset<CH, kSwzDual>(wave, lane, 0);
+    const uint32_t off1 = (uint32_t)lane_src_offset<CH, kSwzDual>(wave, lane, 1) - 2048u;
+    const uint32_t q_lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&q_tile[0][0] + 1024u * wave);
+    const uint32_t o_lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&o_tile[0][0] + 1024u * wave);
+    const uint32_t st_lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&stats[0][0]);
+    constexpr uint32_t kTileBytes = 2u * kBlock * D;
+    constexpr uint32_t kStatBytes = 4u * kStatRow;
+    const int L16 = lane & 15, g16 = lane >> 4;
+    const int tr_r = tr_token(L16), tr_d = 16 * (g16 & 1) + 4 * tr_dquad(L16);
+
+    // copies of query block i (local index) into buffer b
+    auto issue = [&](int i, int b) {
+        const int64_t r0 = sv.qrow_base + (int64_t)kBlock * i;
+        const int qs = q_size(i);
+        load_tile<D, kSwzDual>(q_lds0 + kTileBytes * b, q + r0 * D, qs, wave, lane, off0, off1);
+        load_tile<D, kSwzDual>(o_lds0 + kTileBytes * b, dout + r0 * D, qs, wave, lane, off0, off1);
+        // 512 bytes of row statistics: lanes 0..31 of wave 0, 16 bytes each
+        if (wave == 0 && lane < 32)
+            dma_16B(uniform_ptr(rs + (sv.qblk_base + i) * kStatRow), 16u * lane, st_lds0 + kStatBytes * b);
+    };
+    auto entry = [&](int x) -> int { return clampi(list[x], 0, nq - 1); };
+
+    __builtin_amdgcn_s_waitcnt(0);
+    if (m > 0) issue(entry(0), 0);
+    int buf = 0;
+    for (int x = 0; x < m; ++x) {
+        wait_vmcnt<0>();
+        wg_barrier();  // block x is in LDS; every wave is done with the other buffer
+        if (x + 1 < m) issue(entry(x + 1), buf ^ 1);
+        const uint16_t* qt = q_tile[buf];
+        const uint16_t* ot = o_tile[buf];
+        const float* st = stats[buf];
+
+        // S = Q K^T and dP = dO V^T: rows = queries, lane column = KV token
+        f32x16 sacc[2], pacc[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sacc[mt][e] = pacc[mt][e] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<CH, kSwzDual>(qt, mt, ks, l32, hh),
+                                                                   kf[ks], sacc[mt], 0, 0, 0);
+                pacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<CH, kSwzDual>(ot, mt, ks, l32, hh),
+                                                                   vf[ks], pacc[mt], 0, 0, 0);
+            }
+        // P = exp2(S c - lse[row]), dS = P (dP - delta[row]); element e of tile
+        // mt is query row 32 mt + 8 (e / 4) + 4 hh + e % 4 (padding rows have
+        // lse = +inf, so P = 0 there)
+        f32x16 dsacc[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int r0 = 32 * mt + 8 * g + 4 * hh;
+                const float4 l4 = *reinterpret_cast<const float4*>(st + r0);
+                const float4 d4 = *reinterpret_cast<const float4*>(st + kBlock + r0);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][4 * g + e], c_log2, -lv[e]));
+                    if (!kvalid) p = 0.f;
+                    sacc[mt][4 * g + e] = p;
+                    dsacc[mt][4 * g + e] = p * (pacc[mt][4 * g + e] - dl[e]);
+                }
+            }
+        // dV^T += dO^T P and dK^T += Q^T dS over 4 k-steps of 16 queries
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            const bf16x8 pb = acc_to_b(sacc, s4);
+            const bf16x8 db = acc_to_b(dsacc, s4);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<CH, kSwzDual>(ot, s4, dt, hh, tr_r, tr_d),
+                                                                  pb, dva[dt], 0, 0, 0);
+                dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<CH, kSwzDual>(qt, s4, dt, hh, tr_r, tr_d),
+                                                                  db, dka[dt], 0, 0, 0);
+            }
+        }
+        buf ^= 1;
+    }
+
+    // lane holds dK / dV [kr][32 dt + 8 (e / 4) + 4 hh + e % 4]
+    uint16_t* krow = dk + (kvrow0 + kr) * D;
+    uint16_t* vrow = dv + (kvrow0 + kr) * D;
+    if (kvalid) {
+        const double* ckr = dkc + kb * D;
+        const double* cvr = dvc + kb * D;
+        const float inv_size = 1.f / (float)kvsize;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int d0 = 32 * dt + 8 * jj + 4 * hh;
+                float a[4], b[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    a[e] = fmaf(dka[dt][4 * jj + e], scale, (float)ckr[d0 + e] * inv_size);
+                    b[e] = dva[dt][4 * jj + e] + (float)cvr[d0 + e] * inv_size;
+                }
+                *reinterpret_cast<uint2*>(krow + d0) = make_uint2(bf16pair(a[0], a[1]), bf16pair(a[2], a[3]));
+                *reinterpret_cast<uint2*>(vrow + d0) = make_uint2(bf16pair(b[0], b[1]), bf16pair(b[2], b[3]));
+            }
+    } else if (P.packed) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                *reinterpret_cast<uint2*>(krow + 32 * dt + 8 * jj + 4 * hh) = make_uint2(0, 0);
+                *reinterpret_cast<uint2*>(vrow + 32 * dt + 8 * jj + 4 * hh) = make_uint2(0, 0);
+            }
+    }
+}
+
+template <int D>
+hipError_t launch_all(const DevProblem& P, const BwdArgs& A, hipStream_t st) {
+    const int seqs = P.nseq;
+    const int qgrid = P.packed ? P.total_q : P.nQ;
+    const int maxq = P.packed ? P.max_q : P.nQ;
+    const int maxkv = P.packed ? P.max_kv : P.nKV;
+    const double scale = 1.0 / sqrt((double)D);
+    const float c_log2 = (float)(1.4426950408889634 * scale);
+    hipError_t e;
+    // 1. combine backward
+    const dim3 cgrid(qgrid, P.H, P.packed ? 1 : seqs);
+    switch (A.gate_mode) {
+        case VSA_GATE_NONE:
+            hipLaunchKernelGGL((bwd_combine_kernel<D, VSA_GATE_NONE>), cgrid, dim3(kThreads), 0, st, P, A.dout,
+                               A.out_s, A.out_c, A.gate, A.gs0, A.gs1, A.gs2, A.lse, A.rs, A.doc, A.dgate);
+            break;
+        case VSA_GATE_TOKEN:
+            hipLaunchKernelGGL((bwd_combine_kernel<D, VSA_GATE_TOKEN>), cgrid, dim3(kThreads), 0, st, P, A.dout,
+                               A.out_s, A.out_c, A.gate, A.gs0, A.gs1, A.gs2, A.lse, A.rs, A.doc, A.dgate);
+            break;
+        case VSA_GATE_FULL:
+            hipLaunchKernelGGL((bwd_combine_kernel<D, VSA_GATE_FULL>), cgrid, dim3(kThreads), 0, st, P, A.dout,
+                               A.out_s, A.out_c, A.gate, A.gs0, A.gs1, A.gs2, A.lse, A.rs, A.doc, A.dgate);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // 2. block means
+    if ((e = launch_pool(P, A.q, A.k, A.v, A.qc, A.kc, A.vc, st)) != hipSuccess) return e;
+    // 3. coarse backward
+    hipLaunchKernelGGL(bwd_coarse_rows_kernel<D>, dim3(maxq, P.H, seqs), dim3(kThreads), 0, st, P, A.qc, A.kc, A.vc, A.doc, A.pbuf, A.dsbuf, A.dqc,
+                       maxkv, scale);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_coarse_cols_kernel<D>, dim3(maxkv, P.H, seqs), dim3(kThreads), 0, st, P, A.qc, A.doc,
+                       A.pbuf, A.dsbuf, A.dkc, A.dvc, maxkv, scale);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // 4. inverse routing
+    hipLaunchKernelGGL(bwd_k2q_kernel, dim3((maxkv + 3) / 4, P.H, seqs), dim3(kThreads), 0, st, P, A.idx, A.num,
+                       A.k2q, A.k2q_num, maxq);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // 5. dQ, 6. dK / dV
+    const int64_t nq_all = P.packed ? (int64_t)P.total_q * P.H : (int64_t)P.nQ * P.H * P.nseq;
+    const int64_t nkv_all = P.packed ? (int64_t)P.total_kv * P.H : (int64_t)P.nKV * P.H * P.nseq;
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)nq_all), dim3(kAttnThreads), 0, st, P, A.q, A.k, A.v, A.dout,
+                       A.rs, A.idx, A.num, A.dqc, A.dq, c_log2, (float)scale);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)nkv_all), dim3(kAttnThreads), 0, st, P, A.q, A.k, A.v,
+                       A.dout, A.rs, A.k2q, A.k2q_num, maxq, A.dkc, A.dvc, A.dk, A.dv, c_log2, (float)scale);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(const DevProblem& P, const BwdArgs& A, hipStream_t st) {
+    const int64_t nq_all = P.packed ? (int64_t)P.total_q * P.H : (int64_t)P.nQ * P.H * P.nseq;
+    const int64_t nkv_all = P.packed ? (int64_t)P.total_kv * P.H : (int64_t)P.nKV * P.H * P.nseq;
+    if (nq_all <= 0 || nq_all > 0x7fffffff || nkv_all <= 0 || nkv_all > 0x7fffffff) return hipErrorInvalidValue;
+    return P.D == 128 ? launch_all<128>(P, A, st) : launch_all<64>(P, A, st);
+}
+
+}  // namespace vsa

@@ -30,16 +30,12 @@
 //     into one FMA); the running max moves lazily (only when a block raises
 //     it by more than 2^8), so most blocks skip the rescale of the output;
 //     one bf16 rounding per output element.
-#include "attn_layout.hpp"
-#include "vsa_internal.hpp"
+#include "attn_common.hpp"
 
 namespace vsa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+using namespace attn;
 
 constexpr int kAttnThreads = 128;
 // Workgroups resident on one XCD at a time (32 CUs x 4 workgroups).  Query
@@ -50,139 +46,20 @@ constexpr int kAttnThreads = 128;
 // into theirs.  Only the order of the online-softmax updates changes.
 constexpr int kSweep = 128;
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
-__device__ __forceinline__ uint32_t bf16pair(float a, float b) {
-    const f32x2 v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
-// max / sum of x over lanes l and l ^ 32 (v_permlane32_swap: the two halves
-// of the wave trade places, so the pair of results holds both halves)
-__device__ __forceinline__ float max_with_lane_xor32(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_with_lane_xor32(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-// acc + the two bf16 values packed in w (one v_dot2 against (1, 1))
-__device__ __forceinline__ float sum_bf16_pair(uint32_t w, float acc) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3F803F80u), acc,
-                                           false);
-}
-
-// Wait until at most N vector-memory operations of this wave are in flight
-// (loads complete in issue order).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// Workgroup barrier that first waits for this wave's own LDS reads, so that
-// no wave can start overwriting a tile while another's read is in flight.
-__device__ __forceinline__ void wg_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// A pointer every lane holds the same value of, moved to scalar registers.
-template <typename T>
-__device__ __forceinline__ const T* uniform_ptr(const T* p) {
-    const uint64_t v = (uint64_t)p;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return (const T*)(((uint64_t)hi << 32) | lo);
-}
-
-// Read-only, wave-uniform data (the block list, block sizes) is read through
-// the constant address space so the compiler uses scalar loads, which are
-// counted by lgkmcnt and never wait for the direct-to-LDS copies in flight.
-typedef const __attribute__((address_space(4))) int const_int;
-
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4,
-// scalar base + per-lane 32-bit offset): lane l's bytes land at LDS byte
-// lds_base + 16 l.  Written as inline assembly (it has no output register)
-// so that the compiler does not add its own conservative waits for the LDS
-// write before every LDS read; the kernel orders these copies with explicit
-// vmcnt waits and barriers.  M0 (the LDS base of the copy) is saved and
-// restored inside the block.
-__device__ __forceinline__ void dma_16B(const void* sbase, uint32_t voff, uint32_t lds_base) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %2\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(voff), "s"(sbase), "s"(lds_base)
-        : "memory");
-}
-
-// Two direct copies sharing one M0: the immediate offset of the second
-// (2048) is added to both its global and its LDS address, so with voff_b =
-// (wanted source offset) - 2048 it lands 2048 bytes after the first.
-__device__ __forceinline__ void dma_16B_pair(const void* sbase, uint32_t voff_a, uint32_t voff_b,
-                                             uint32_t lds_base) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %4\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %3\n\t"
-        "global_load_lds_dwordx4 %2, %3 offset:2048\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(voff_a), "v"(voff_b), "s"(sbase), "s"(lds_base)
-        : "memory");
-}
-
-// Copy one 64-row KV block starting at `block` into a swizzled tile.  Full
-// blocks: instructions 2m and 2m + 1 of a lane fetch lane_off0 + 4096 m and
-// lane_off1 + 4096 m (passed as lane_off1_m2k = lane_off1 - 2048, see
-// dma_16B_pair) into LDS bytes lds0 + 4096 m and lds0 + 4096 m + 2048.
-// Partial blocks (valid < 64): rows past valid - 1 repeat that row, so every
-// address stays inside the tensor and every LDS value is finite.
-template <int D, bool IS_V>
-__device__ __forceinline__ void load_tile(uint32_t lds0, const uint16_t* block, int valid, int wave,
-                                          int lane, uint32_t lane_off0, uint32_t lane_off1_m2k) {
-    constexpr int CH = D / 8;
-    const char* base = (const char*)uniform_ptr(block);
-    if (valid == kBlock) {
-#pragma unroll
-        for (int m = 0; m < CH / 4; ++m)
-            dma_16B_pair(base + 4096 * m, lane_off0, lane_off1_m2k, lds0 + 4096u * m);
-    } else {
-#pragma unroll
-        for (int n = 0; n < CH / 2; ++n) {
-            const int p = load_chunk_pos(n, wave, lane);
-            const int row = p / CH;
-            const int sw = IS_V ? v_swz<CH>(row) : k_swz<CH>(row);
-            const int c = (p % CH) ^ sw;
-            const int r = min(row, valid - 1);
-            dma_16B(base, (uint32_t)(r * CH * 16 + 16 * c), lds0 + 2048u * n);
-        }
-    }
-}
-
 // Epilogue of the kernel: write the sparse output itself, or fuse the
 // combine with the block's coarse row (no gate, a per-token gate, or a full
 // [.., D] gate).
 enum CombineMode { kSparseOnly = -1, kAddCoarse = 0, kTokenGate = 1, kFullGate = 2 };
 
-// Where the combine's inputs live (unused for kSparseOnly).
+// Where the combine's inputs live (unused for kSparseOnly), and the optional
+// extra outputs a training forward keeps for the backward pass.
 struct CombineArgs {
     const float* out_c;     // block-resolution coarse output
     const uint16_t* gate;   // bf16 gate
     int64_t gs0, gs1, gs2;  // gate element strides: batch, head, token
+    uint16_t* out_s;        // if set (fused modes): the sparse output O / l, bf16
+    float* lse;             // if set: log2 of the softmax denominator of each
+                            // query row in exp2 units of the scaled scores
 };
 
 template <int D, int CMODE>
@@ -292,10 +169,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     };
 
     // per-lane positions inside the tiles
-    const uint32_t koff0 = (uint32_t)lane_src_offset<CH, false>(wave, lane, 0);
-    const uint32_t koff1 = (uint32_t)lane_src_offset<CH, false>(wave, lane, 1) - 2048u;
-    const uint32_t voff0 = (uint32_t)lane_src_offset<CH, true>(wave, lane, 0);
-    const uint32_t voff1 = (uint32_t)lane_src_offset<CH, true>(wave, lane, 1) - 2048u;
+    const uint32_t koff0 = (uint32_t)lane_src_offset<CH, kSwzRow>(wave, lane, 0);
+    const uint32_t koff1 = (uint32_t)lane_src_offset<CH, kSwzRow>(wave, lane, 1) - 2048u;
+    const uint32_t voff0 = (uint32_t)lane_src_offset<CH, kSwzTr>(wave, lane, 0);
+    const uint32_t voff1 = (uint32_t)lane_src_offset<CH, kSwzTr>(wave, lane, 1) - 2048u;
     // this wave's LDS byte base inside each tile
     const uint32_t k_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)k_tile + 1024u * wave);
     const uint32_t v_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)v_tile + 1024u * wave);
@@ -351,7 +228,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
             }
             wg_barrier();  // both waves are done with the K tile
         }
-        if (more) load_tile<D, false>(k_lds, k + r0n * D, kvsize_n, wave, lane, koff0, koff1);
+        if (more) load_tile<D, kSwzRow>(k_lds, k + r0n * D, kvsize_n, wave, lane, koff0, koff1);
 
         if (cur) {
             // ---- online softmax; acc e of tile mt is token 32 mt + 8 (e/4) + 4 hh + e%4
@@ -423,7 +300,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
             }
             wg_barrier();  // both waves are done with the V tile
         }
-        if (more) load_tile<D, true>(v_lds, v + r0n * D, kvsize_n, wave, lane, voff0, voff1);
+        if (more) load_tile<D, kSwzTr>(v_lds, v + r0n * D, kvsize_n, wave, lane, voff0, voff1);
 
         first = false;
         j = jn;
@@ -438,6 +315,27 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     // ---- normalise and store: lane holds O[qr][32 dt + 8 j + 4 hh + 0..3] ----
     const float lt = sum_with_lane_xor32(l);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    // P[t][u] = exp2(s[t][u] c_log2 - lse[t]) for the row's selected tokens
+    if (C.lse && hh == 0 && qr < qsize) C.lse[qrow0 + qr] = m * c_log2 + __log2f(lt);
+    if (CMODE != kSparseOnly && C.out_s && qr < qsize) {
+        uint16_t* srow = C.out_s + (qrow0 + qr) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                uint2 w2;
+                w2.x = bf16pair(o[dt][4 * jj + 0] * inv, o[dt][4 * jj + 1] * inv);
+                w2.y = bf16pair(o[dt][4 * jj + 2] * inv, o[dt][4 * jj + 3] * inv);
+                *reinterpret_cast<uint2*>(srow + 32 * dt + 8 * jj + 4 * hh) = w2;
+            }
+    } else if (CMODE != kSparseOnly && C.out_s && P.packed) {
+        uint16_t* srow = C.out_s + (qrow0 + qr) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                *reinterpret_cast<uint2*>(srow + 32 * dt + 8 * jj + 4 * hh) = make_uint2(0, 0);
+    }
     if (qr < qsize && CMODE == kSparseOnly) {
         uint16_t* orow = out + (qrow0 + qr) * D;
 #pragma unroll
@@ -515,14 +413,15 @@ hipError_t launch_mode(const DevProblem& P, const uint16_t* q, const uint16_t* k
 hipError_t launch_sparse_attn(const DevProblem& P, const uint16_t* q, const uint16_t* k,
                               const uint16_t* v, const int* idx, const int* num, uint16_t* out,
                               hipStream_t st) {
-    return launch_mode<kSparseOnly>(P, q, k, v, idx, num, out, CombineArgs{nullptr, nullptr, 0, 0, 0}, st);
+    return launch_mode<kSparseOnly>(P, q, k, v, idx, num, out,
+                                    CombineArgs{nullptr, nullptr, 0, 0, 0, nullptr, nullptr}, st);
 }
 
 hipError_t launch_sparse_attn_combine(const DevProblem& P, const uint16_t* q, const uint16_t* k,
                                       const uint16_t* v, const int* idx, const int* num, const float* out_c,
                                       const uint16_t* gate, int mode, int64_t gs0, int64_t gs1, int64_t gs2,
-                                      uint16_t* out, hipStream_t st) {
-    const CombineArgs C{out_c, gate, gs0, gs1, gs2};
+                                      uint16_t* out, uint16_t* out_s, float* lse, hipStream_t st) {
+    const CombineArgs C{out_c, gate, gs0, gs1, gs2, out_s, lse};
     switch (mode) {
         case 0: return launch_mode<kAddCoarse>(P, q, k, v, idx, num, out, C, st);
         case 1: return launch_mode<kTokenGate>(P, q, k, v, idx, num, out, C, st);

@@ -145,6 +145,40 @@ Workspace plan_workspace(const vsa::DevProblem& P, void* base) {
     return w;
 }
 
+struct BwdWorkspace {
+    double *qc, *kc, *vc, *doc, *dqc, *dkc, *dvc, *pbuf, *dsbuf;
+    float* rs;
+    int *k2q, *k2q_num;
+    size_t total_bytes;
+};
+
+BwdWorkspace plan_bwd_workspace(const vsa::DevProblem& P, void* base) {
+    BwdWorkspace w{};
+    char* p = (char*)base;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char* r = p ? p + off : nullptr;
+        off += round_up(bytes);
+        return r;
+    };
+    const int64_t maxq = P.packed ? P.max_q : P.nQ, maxkv = P.packed ? P.max_kv : P.nKV;
+    const size_t qd = sizeof(double) * qblocks(P) * P.D, kd = sizeof(double) * kvblocks(P) * P.D;
+    w.qc = (double*)take(qd);
+    w.kc = (double*)take(kd);
+    w.vc = (double*)take(kd);
+    w.doc = (double*)take(qd);
+    w.dqc = (double*)take(qd);
+    w.dkc = (double*)take(kd);
+    w.dvc = (double*)take(kd);
+    w.pbuf = (double*)take(sizeof(double) * qblocks(P) * maxkv);
+    w.dsbuf = (double*)take(sizeof(double) * qblocks(P) * maxkv);
+    w.rs = (float*)take(sizeof(float) * qblocks(P) * vsa::kStatRow);
+    w.k2q = (int*)take(sizeof(int) * kvblocks(P) * maxq);
+    w.k2q_num = (int*)take(sizeof(int) * kvblocks(P));
+    w.total_bytes = off;
+    return w;
+}
+
 bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
     const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
     return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
@@ -376,8 +410,129 @@ int vsa_sparse_attn_combine(const vsa_problem* problem, const vsa_bf16* q, const
     if (gate_mode != VSA_GATE_NONE && overlaps(out, 2 * q_elems(P), gate, 2))
         return fail(VSA_ERR_ALIAS, "gate overlaps out");
     rc = hip_status(vsa::launch_sparse_attn_combine(P, q, k, v, q2k_idx, q2k_num, out_c, gate, gate_mode, gs[0],
-                                                    gs[1], gs[2], out, (hipStream_t)stream),
+                                                    gs[1], gs[2], out, nullptr, nullptr, (hipStream_t)stream),
                     "fused sparse attention launch");
+    return rc ? rc : ok();
+}
+
+int vsa_sparse_attn_combine_train(const vsa_problem* problem, const vsa_bf16* q, const vsa_bf16* k,
+                                  const vsa_bf16* v, const int32_t* q2k_idx, const int32_t* q2k_num,
+                                  const float* out_c, const vsa_bf16* gate, int32_t gate_mode,
+                                  const int64_t* gate_strides_in, vsa_bf16* out, vsa_bf16* out_s, float* lse,
+                                  vsa_stream stream) {
+    vsa::DevProblem P;
+    int rc = make_problem(problem, &P);
+    if (rc) return rc;
+    if ((rc = check_qkv(P, q, k, v))) return rc;
+    if (!q2k_idx || !q2k_num || !out || !out_c || !out_s || !lse)
+        return fail(VSA_ERR_NULL, "q2k_idx, q2k_num, out_c, out, out_s or lse is NULL");
+    if (!aligned16(out) || !aligned16(out_c) || !aligned16(out_s))
+        return fail(VSA_ERR_ALIGN, "out_c, out and out_s must be 16-byte aligned");
+    if ((uintptr_t)lse & 3u) return fail(VSA_ERR_ALIGN, "lse must be 4-byte aligned");
+    if ((rc = check_out_alias(P, out, q, k, v))) return rc;
+    if ((rc = check_out_alias(P, out_s, q, k, v))) return rc;
+    const int64_t ob = 2 * q_elems(P), lb = 4 * (q_elems(P) / P.D);
+    if (overlaps(out, ob, out_s, ob)) return fail(VSA_ERR_ALIAS, "out_s overlaps out");
+    if (overlaps(lse, lb, q, ob) || overlaps(lse, lb, k, 2 * kv_elems(P)) || overlaps(lse, lb, v, 2 * kv_elems(P)) ||
+        overlaps(lse, lb, out, ob) || overlaps(lse, lb, out_s, ob))
+        return fail(VSA_ERR_ALIAS, "lse overlaps an input, out or out_s");
+    int64_t gs[3];
+    if ((rc = gate_strides(P, gate, gate_mode, gate_strides_in, gs))) return rc;
+    if (gate_mode != VSA_GATE_NONE && (overlaps(out, ob, gate, 2) || overlaps(out_s, ob, gate, 2)))
+        return fail(VSA_ERR_ALIAS, "gate overlaps out or out_s");
+    rc = hip_status(vsa::launch_sparse_attn_combine(P, q, k, v, q2k_idx, q2k_num, out_c, gate, gate_mode, gs[0],
+                                                    gs[1], gs[2], out, out_s, lse, (hipStream_t)stream),
+                    "fused sparse attention launch");
+    return rc ? rc : ok();
+}
+
+size_t vsa_backward_workspace_size(const vsa_problem* problem) {
+    vsa::DevProblem P;
+    if (make_problem(problem, &P) != VSA_OK) return 0;
+    return plan_bwd_workspace(P, nullptr).total_bytes;
+}
+
+int vsa_backward(const vsa_problem* problem, const vsa_bf16* q, const vsa_bf16* k, const vsa_bf16* v,
+                 const int32_t* q2k_idx, const int32_t* q2k_num, const float* out_c, const vsa_bf16* gate,
+                 int32_t gate_mode, const int64_t* gate_strides_in, const vsa_bf16* out_s, const float* lse,
+                 const vsa_bf16* dout, vsa_bf16* dq, vsa_bf16* dk, vsa_bf16* dv, vsa_bf16* dgate, void* workspace,
+                 size_t workspace_bytes, vsa_stream stream) {
+    vsa::DevProblem P;
+    int rc = make_problem(problem, &P);
+    if (rc) return rc;
+    if ((rc = check_qkv(P, q, k, v))) return rc;
+    if (!q2k_idx || !q2k_num || !out_c || !out_s || !lse || !dout || !dq || !dk || !dv)
+        return fail(VSA_ERR_NULL, "a required input or output pointer is NULL");
+    if (!aligned16(out_c) || !aligned16(out_s) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+        !aligned16(dv))
+        return fail(VSA_ERR_ALIGN, "out_c, out_s, dout, dq, dk and dv must be 16-byte aligned");
+    if ((uintptr_t)lse & 3u) return fail(VSA_ERR_ALIGN, "lse must be 4-byte aligned");
+    if (((uintptr_t)q2k_idx & 3u) || ((uintptr_t)q2k_num & 3u))
+        return fail(VSA_ERR_ALIGN, "index arrays must be 4-byte aligned");
+    int64_t gs[3];
+    if ((rc = gate_strides(P, gate, gate_mode, gate_strides_in, gs))) return rc;
+    if (gate_mode != VSA_GATE_NONE) {
+        if (!dgate) return fail(VSA_ERR_NULL, "dgate is NULL with gate_mode %d", gate_mode);
+        if (gate_mode == VSA_GATE_FULL ? !aligned16(dgate) : ((uintptr_t)dgate & 1u) != 0)
+            return fail(VSA_ERR_ALIGN, "dgate must be %d-byte aligned", gate_mode == VSA_GATE_FULL ? 16 : 2);
+    }
+    // every output against every input and the other outputs
+    const int64_t qbytes = 2 * q_elems(P), kbytes = 2 * kv_elems(P), rows = q_elems(P) / P.D;
+    const int64_t gbytes = gate_mode == VSA_GATE_FULL ? qbytes : 2 * rows;
+    struct Span {
+        const void* p;
+        int64_t n;
+    };
+    const Span ins[] = {{q, qbytes},        {k, kbytes},       {v, kbytes},
+                        {dout, qbytes},     {out_s, qbytes},   {lse, 4 * rows},
+                        {out_c, 4 * qblocks(P) * P.D},         {gate, gate_mode != VSA_GATE_NONE ? 2 : 0}};
+    const Span outs[] = {{dq, qbytes}, {dk, kbytes}, {dv, kbytes}, {dgate, gate_mode != VSA_GATE_NONE ? gbytes : 0}};
+    for (int a = 0; a < 4; ++a) {
+        if (!outs[a].n) continue;
+        for (const Span& in : ins)
+            if (in.n && overlaps(outs[a].p, outs[a].n, in.p, in.n))
+                return fail(VSA_ERR_ALIAS, "an output of the backward overlaps one of its inputs");
+        for (int b = a + 1; b < 4; ++b)
+            if (outs[b].n && overlaps(outs[a].p, outs[a].n, outs[b].p, outs[b].n))
+                return fail(VSA_ERR_ALIAS, "two outputs of the backward overlap");
+    }
+    if (!workspace) return fail(VSA_ERR_WORKSPACE, "workspace is NULL");
+    if ((uintptr_t)workspace % kAlign) return fail(VSA_ERR_ALIGN, "workspace must be 256-byte aligned");
+    const BwdWorkspace w = plan_bwd_workspace(P, workspace);
+    if (workspace_bytes < w.total_bytes)
+        return fail(VSA_ERR_WORKSPACE, "workspace holds %zu bytes, needs %zu", workspace_bytes, w.total_bytes);
+    vsa::BwdArgs A{};
+    A.q = q;
+    A.k = k;
+    A.v = v;
+    A.dout = dout;
+    A.out_s = out_s;
+    A.gate = gate;
+    A.out_c = out_c;
+    A.lse = lse;
+    A.idx = q2k_idx;
+    A.num = q2k_num;
+    A.gate_mode = gate_mode;
+    A.gs0 = gs[0];
+    A.gs1 = gs[1];
+    A.gs2 = gs[2];
+    A.dq = dq;
+    A.dk = dk;
+    A.dv = dv;
+    A.dgate = dgate;
+    A.qc = w.qc;
+    A.kc = w.kc;
+    A.vc = w.vc;
+    A.doc = w.doc;
+    A.dqc = w.dqc;
+    A.dkc = w.dkc;
+    A.dvc = w.dvc;
+    A.pbuf = w.pbuf;
+    A.dsbuf = w.dsbuf;
+    A.rs = w.rs;
+    A.k2q = w.k2q;
+    A.k2q_num = w.k2q_num;
+    rc = hip_status(vsa::launch_backward(P, A, (hipStream_t)stream), "backward launch");
     return rc ? rc : ok();
 }
 
@@ -428,7 +583,7 @@ static int forward_common(const vsa_problem* pr, const vsa_bf16* q, const vsa_bf
     hipStream_t st = (hipStream_t)stream;
     if ((rc = run_coarse(P, q, k, v, oc, idx, num, w, st))) return rc;
     if ((rc = hip_status(vsa::launch_sparse_attn_combine(P, q, k, v, idx, num, oc, gate, gate_mode, gs[0], gs[1],
-                                                         gs[2], out, st),
+                                                         gs[2], out, nullptr, nullptr, st),
                          "fused sparse attention launch")))
         return rc;
     return ok();

@@ -150,7 +150,7 @@ hipError_t launch_sparse_attn(const DevProblem& P, const uint16_t* q, const uint
 hipError_t launch_sparse_attn_combine(const DevProblem& P, const uint16_t* q, const uint16_t* k,
                                       const uint16_t* v, const int* idx, const int* num, const float* out_c,
                                       const uint16_t* gate, int mode, int64_t gs0, int64_t gs1, int64_t gs2,
-                                      uint16_t* out, hipStream_t st);
+                                      uint16_t* out, uint16_t* out_s, float* lse, hipStream_t st);
 // gather (scatter = false): x [B, Hh, T*H*W, elems] raster -> y [Hh, B * 64 *
 // ntiles, elems] tile order with zero padding; scatter: the inverse.
 hipError_t launch_tile_copy(const TileGrid& g, const uint16_t* src, uint16_t* dst, int B, int Hh, int elems,
@@ -159,5 +159,28 @@ hipError_t launch_combine(const DevProblem& P, const float* out_c, const uint16_
                           int64_t gs0, int64_t gs1, int64_t gs2, uint16_t* out, hipStream_t st);
 
 constexpr int kMaxKvBlocks = 4096;
+
+// Backward pass.  Row statistics: per query block 64 log-sum-exp values
+// (+inf on padding rows) then 64 softmax-backward row terms (0 on padding).
+constexpr int kStatRow = 2 * kBlock;
+
+struct BwdArgs {
+    // inputs
+    const uint16_t *q, *k, *v, *dout, *out_s, *gate;
+    const float *out_c, *lse;
+    const int *idx, *num;
+    int gate_mode;
+    int64_t gs0, gs1, gs2;
+    // outputs
+    uint16_t *dq, *dk, *dv, *dgate;
+    // workspace: float64 block-resolution data ([query blocks][D] for qc, doc,
+    // dqc; [KV blocks][D] for kc, vc, dkc, dvc; [query blocks][ld] for pbuf,
+    // dsbuf with ld = max KV blocks per sequence), row statistics
+    // [query blocks][kStatRow], inverse routing [KV blocks][max query blocks]
+    double *qc, *kc, *vc, *doc, *dqc, *dkc, *dvc, *pbuf, *dsbuf;
+    float* rs;
+    int *k2q, *k2q_num;
+};
+hipError_t launch_backward(const DevProblem& P, const BwdArgs& A, hipStream_t st);
 
 }  // namespace vsa
