@@ -42,10 +42,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="large", choices=["large", "varlen_many", "video"],
-                    help="large (the default line), varlen_many, or video: the large shape as an "
+    ap.add_argument("--workload", default="large", choices=["large", "varlen_many", "video", "train"],
+                    help="large (the default line), varlen_many, video: the large shape as an "
                          "11 x 32 x 44 latent in 4 x 4 x 4 tiles, gathered from and scattered to "
-                         "raster order")
+                         "raster order, or train: the large shape's forward plus backward")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0,
                     help="wall-time budget of the oracle sample (whole heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -202,6 +202,76 @@ def video_bench(args, torch, synth, vsa):
     print(json.dumps(res), flush=True)
 
 
+def train_bench(args, torch, synth, vsa):
+    """Training step on the large shape (B=1, H=56, D=128, S=15488, top-49,
+    per-token gate): coarse/top-k, the training forward (sparse attention
+    with the fused combine, also writing out_s and lse) and the backward
+    (vsa_backward) for a fixed output gradient.  Effective FLOPs: the forward's
+    4 B H nQ k 64^2 D plus 2.5 times that for the backward (dV, dP, dQ, dK and
+    the recomputed scores: five block products where the forward has two)."""
+    dev = torch.device("cuda:0")
+    inp = synth.workload("large")
+    B, H, Sq, Skv, D = inp.shape
+    prob = vsa.dense_problem(B, H, Sq, Skv, D, inp.topk)
+    nq = -(-Sq // 64)
+    kk = min(inp.topk, -(-Skv // 64))
+    fwd_flops = 4.0 * B * H * nq * kk * 64 * 64 * D
+    bwd_flops = 2.5 * fwd_flops
+    q, k, v, gate = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.gate))
+    dout = synth.output_grad(inp.q.shape, 1100).to(dev)
+    cs, isz, ns = vsa.block_shapes(prob)
+    out_c = torch.empty(cs, dtype=torch.float32, device=dev)
+    idx = torch.empty(isz, dtype=torch.int32, device=dev)
+    num = torch.empty(ns, dtype=torch.int32, device=dev)
+    out, out_s = torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty(vsa.lse_shape(prob), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = torch.empty_like(gate)
+    ws = vsa.alloc_workspace(prob, dev)
+    bws = vsa.alloc_backward_workspace(prob, dev)
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        vsa.vsa_coarse_topk(prob, q, k, v, out_c, idx, num, ws)
+        if ev: ev[1].record()
+        vsa.vsa_sparse_attn_combine_train(prob, q, k, v, idx, num, out_c, gate, out, out_s, lse)
+        if ev: ev[2].record()
+        vsa.vsa_backward(prob, q, k, v, idx, num, out_c, gate, out_s, lse, dout, dq, dk, dv, dg, bws)
+        if ev: ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ("coarse", "forward", "backward")
+    avg = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, n in enumerate(names)}
+    ms_per_step = wall * 1e3 / args.steps
+    bwd_tf = bwd_flops / (avg["backward"] * 1e-3) / 1e12
+    res = {
+        "metric": "VSA training step (fwd+bwd) effective TFLOP/s",
+        "value": round((fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"large video-DiT shape B={B} H={H} D={D} S={Sq}, top-{inp.topk}, token gate; "
+                               "coarse + training forward + backward",
+                   "batch": B, "heads": H, "head_dim": D, "seq_len": Sq, "topk": inp.topk, "gate": "token"},
+        "kernels": {"coarse_topk_stage_ms": round(avg["coarse"], 4),
+                    "forward_train_ms": round(avg["forward"], 4),
+                    "forward_train_TFLOPs": round(fwd_flops / (avg["forward"] * 1e-3) / 1e12, 2),
+                    "backward_ms": round(avg["backward"], 4),
+                    "backward_TFLOPs": round(bwd_tf, 2),
+                    "backward_frac_bf16_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -221,6 +291,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload == "video":
         video_bench(args, torch, synth, vsa)
+        return
+    if args.workload == "train":
+        train_bench(args, torch, synth, vsa)
         return
     inp = synth.workload(args.workload)
 

@@ -22,16 +22,22 @@ from tests import numerics as N
 
 pytestmark = pytest.mark.gpu
 
-GRAD_MAX_REL = 2e-2   # max |gpu - ref| / max |ref|
-GRAD_MEAN_REL = 1e-2  # mean |gpu - ref| / mean |ref|
+GRAD_MAX_REL = 1e-2   # max |gpu - ref| / max |ref| (measured 2-5e-3)
+GRAD_MEAN_REL = 5e-3  # mean |gpu - ref| / mean |ref| (measured 1-2.4e-3)
 LSE_ABS = 4e-3        # log2 units: the bf16 rounding of the summed probabilities
+GRAD_FLOOR_MAX = 1e-2
+GRAD_FLOOR_MEAN = 1e-3
 
 
 def check_grad(gpu: np.ndarray, ref: np.ndarray, what: str):
     assert np.isfinite(gpu).all(), f"{what}: non-finite values"
     d = np.abs(gpu - ref)
-    scale_max, scale_mean = float(np.abs(ref).max()), float(np.abs(ref).mean())
-    mx, mean = float(d.max()) / max(scale_max, 1e-30), float(d.mean()) / max(scale_mean, 1e-30)
+    # a gradient that vanishes in exact arithmetic (one key per row: P = 1,
+    # dS = 0) keeps rounding residue; with unit-variance inputs and dout the
+    # scales are floored at GRAD_FLOOR_MAX / GRAD_FLOOR_MEAN
+    scale_max = max(float(np.abs(ref).max()), GRAD_FLOOR_MAX)
+    scale_mean = max(float(np.abs(ref).mean()), GRAD_FLOOR_MEAN)
+    mx, mean = float(d.max()) / scale_max, float(d.mean()) / scale_mean
     G.note(f"  {what}: max-err/max {mx:.2e}, mean-err/mean {mean:.2e} (|ref| max {scale_max:.2e})")
     assert mx <= GRAD_MAX_REL, f"{what}: max error {mx:.3e} of the largest gradient > {GRAD_MAX_REL}"
     assert mean <= GRAD_MEAN_REL, f"{what}: mean error {mean:.3e} of the mean gradient > {GRAD_MEAN_REL}"
@@ -194,3 +200,30 @@ def test_backward_varlen_matches_per_sequence():
         assert (dk[:, okv + skv:okv + 64 * nkv] == 0).all() and (dv[:, okv + skv:okv + 64 * nkv] == 0).all()
         oq += 64 * nq
         okv += 64 * nkv
+
+
+# ---------------------------------------------------------------------------
+# full size: the large shape in the benchmark's launch configuration, whole
+# heads sampled (heads are independent, so a head's gradients need only it)
+# ---------------------------------------------------------------------------
+
+def test_backward_large_shape_sampled_heads():
+    """B=1, H=56, D=128, S=15488 (242 blocks), top-49, token gate: the backward
+    of all heads in one launch sequence, heads 0 and 55 against the oracle
+    (about 30 s of oracle time per head)."""
+    inp = synth.workload("large")
+    B, H, Sq, Skv, D = inp.shape
+    G.note(f"case large backward: H={H} S={Sq} topk={inp.topk}")
+    dout = synth.output_grad(inp.q.shape, 1100)
+    gpu = run_dense_train(inp.q, inp.k, inp.v, inp.gate, dout, inp.topk)
+    for h in (0, H - 1):
+        sl = slice(h, h + 1)
+        ref = BW.vsa_backward(N.f64(inp.q[:, sl]), N.f64(inp.k[:, sl]), N.f64(inp.v[:, sl]), inp.topk,
+                              N.f64(inp.gate[:, sl]), N.f64(dout[:, sl]))
+        G.note(f"  head {h}")
+        G.assert_tie_free(ref)
+        G.assert_indices_equal(gpu["q2k_idx"][:, sl], gpu["q2k_num"][:, sl], ref)
+        dl = float(np.abs(N.f64(gpu["lse"][:, sl]) - ref["lse"]).max())
+        assert dl <= LSE_ABS, f"lse: {dl:.3e}"
+        for name in ("dq", "dk", "dv", "dgate"):
+            check_grad(N.f64(gpu[name][:, sl]), ref[name], name)

@@ -12,9 +12,9 @@
 //      dg[t] = dout[t] * out_c[block] (summed over d for a per-token gate), and
 //      the row statistics (log-sum-exp, delta) of the block in one 512-byte row;
 //   2. the block means again (the forward's pool kernel);
-//   3. coarse backward in float64 at block level, rows then columns: P and dS
-//      of the coarse softmax, dQc = dS Kc / sqrt(D); dKc = dS^T Qc / sqrt(D),
-//      dVc = P^T dOc;
+//   3. coarse backward in float64 at block level: S = Qc Kc^T and dP = dOc
+//      Vc^T, the coarse softmax P and dS = P (dP - rowsum(P dP)), then
+//      dQc = dS Kc / sqrt(D), dKc = dS^T Qc / sqrt(D), dVc = P^T dOc;
 //   4. the inverse routing: for every KV block, the query blocks whose list
 //      holds it, ascending;
 //   5. dQ per query block over its listed KV blocks: S and P = exp(S - lse)
@@ -46,26 +46,6 @@ __device__ __forceinline__ double wave_sum(double x) {
     for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
     return x;
 }
-// block-wide reductions over kThreads threads (every thread gets the result)
-__device__ __forceinline__ double block_sum(double x, double* red) {
-    x = wave_sum(x);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-    __syncthreads();
-    double t = 0.0;
-    for (int w = 0; w < kThreads / 64; ++w) t += red[w];
-    return t;
-}
-__device__ __forceinline__ double block_max(double x, double* red) {
-    for (int o = 32; o > 0; o >>= 1) x = fmax(x, __shfl_xor(x, o));
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-    __syncthreads();
-    double t = -INFINITY;
-    for (int w = 0; w < kThreads / 64; ++w) t = fmax(t, red[w]);
-    return t;
-}
-
 // Sequence owning global KV block g (packed): largest s with cu_kv[s] <= g.
 __device__ __forceinline__ int seq_of_kvblock(const DevProblem& P, int g) {
     int lo = 0, hi = P.nseq - 1;
@@ -171,109 +151,141 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 3. coarse backward (float64): rows, then columns.  Grid (nQ or max_q /
-// nKV or max_kv, H, sequences).
+// 3. coarse backward (float64).  The block-level matrices S = Qc Kc^T and
+// dP = dOc Vc^T come from the forward's tiled score kernel (rows r = (s H +
+// h) max_q + i, row length ld = max_kv); then, per row, P = softmax(S /
+// sqrt(D)) and dS = P (dP - sum_j P_j dP_j) in place; then three tiled
+// products: dQc = dS Kc / sqrt(D), dKc = dS^T Qc / sqrt(D), dVc = P^T dOc.
 // ---------------------------------------------------------------------------
-// Row i: P_j = softmax_j(Qc_i . Kc_j / sqrt(D)), dP_j = dOc_i . Vc_j,
-// dS_j = P_j (dP_j - sum_l P_l dP_l), built in place in the rows of pbuf /
-// dsbuf (row length ld; the workgroup's barriers order its own global
-// accesses), dQc_i = sum_j dS_j Kc_j / sqrt(D).
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_coarse_rows_kernel(DevProblem P, const double* __restrict__ qc,
-                                                                   const double* __restrict__ kc,
-                                                                   const double* __restrict__ vc,
-                                                                   const double* __restrict__ doc,
-                                                                   double* __restrict__ pbuf,
-                                                                   double* __restrict__ dsbuf,
-                                                                   double* __restrict__ dqc, int ld, double scale) {
-    __shared__ double qrow[D], drow[D], red[kThreads / 64], part[2][D];
-    const int s = blockIdx.z, h = blockIdx.y, i = blockIdx.x;
-    const SeqView sv = seq_view(P, s, h);
-    if (i >= sv.nq) return;
-    const int64_t qb = sv.qblk_base + i;
-    double* sl = pbuf + qb * ld;   // scores, then weights, then P
-    double* pl = dsbuf + qb * ld;  // dP, then dS
-    const int nkv = sv.nkv;
+// One wave per row; grid ceil(rows / 4), rows = sequences * H * max_q.
+__global__ __launch_bounds__(kThreads) void bwd_coarse_softmax_kernel(DevProblem P, double* __restrict__ sbuf,
+                                                                      double* __restrict__ dbuf, int ld, int maxq,
+                                                                      double scale) {
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    for (int d = threadIdx.x; d < D; d += kThreads) {
-        qrow[d] = qc[qb * D + d];
-        drow[d] = doc[qb * D + d];
-    }
-    __syncthreads();
-    // one wave per KV block, lanes over d (coalesced rows of Kc and Vc)
+    const int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + wave;
+    if (r >= (int64_t)P.nseq * P.H * maxq) return;
+    const int i = (int)(r % maxq);
+    const int sh = (int)(r / maxq);
+    const SeqView sv = seq_view(P, sh / P.H, sh % P.H);
+    if (i >= sv.nq) return;
+    double* srow = sbuf + r * ld;  // S, then P
+    double* drow = dbuf + r * ld;  // dP, then dS
+    const int n = sv.nkv;
     double mx = -INFINITY;
-    for (int j = wave; j < nkv; j += kThreads / 64) {
-        const double* kr = kc + (sv.kvblk_base + j) * D;
-        const double* vr = vc + (sv.kvblk_base + j) * D;
-        double sc = 0.0, dp = 0.0;
-        for (int d = lane; d < D; d += 64) {
-            sc = fma(qrow[d], kr[d], sc);
-            dp = fma(drow[d], vr[d], dp);
-        }
-        sc = wave_sum(sc);
-        dp = wave_sum(dp);
-        if (lane == 0) {
-            sl[j] = sc;
-            pl[j] = dp;
-        }
-        mx = fmax(mx, sc);
-    }
-    mx = block_max(mx, red);  // its barriers also publish sl / pl
+    for (int j = lane; j < n; j += 64) mx = fmax(mx, srow[j]);
+    for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
     double sum = 0.0;
-    for (int j = threadIdx.x; j < nkv; j += kThreads) {
-        const double w = exp((sl[j] - mx) * scale);
-        sl[j] = w;
+    for (int j = lane; j < n; j += 64) {
+        const double w = exp((srow[j] - mx) * scale);
+        srow[j] = w;
         sum += w;
     }
-    sum = block_sum(sum, red);
+    sum = wave_sum(sum);
+    const double inv = 1.0 / sum;
     double dot = 0.0;
-    for (int j = threadIdx.x; j < nkv; j += kThreads) {
-        const double p = sl[j] / sum;
-        sl[j] = p;
-        dot += p * pl[j];
+    for (int j = lane; j < n; j += 64) {
+        const double p = srow[j] * inv;
+        srow[j] = p;
+        dot = fma(p, drow[j], dot);
     }
-    dot = block_sum(dot, red);
-    for (int j = threadIdx.x; j < nkv; j += kThreads) pl[j] = sl[j] * (pl[j] - dot);
-    __syncthreads();
-    // dQc: thread (d, half) sums every other KV block
-    const int d = threadIdx.x % D, half = threadIdx.x / D;
-    if (half < 2) {
-        double acc = 0.0;
-        for (int j = half; j < nkv; j += 2) acc = fma(pl[j], kc[(sv.kvblk_base + j) * D + d], acc);
-        part[half][d] = acc;
-    }
-    __syncthreads();
-    if (threadIdx.x < D) dqc[qb * D + threadIdx.x] = (part[0][threadIdx.x] + part[1][threadIdx.x]) * scale;
+    dot = wave_sum(dot);
+    for (int j = lane; j < n; j += 64) drow[j] = srow[j] * (drow[j] - dot);
 }
 
-// Column j: dKc_j = sum_i dS_ij Qc_i / sqrt(D), dVc_j = sum_i P_ij dOc_i.
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_coarse_cols_kernel(DevProblem P, const double* __restrict__ qc,
-                                                                   const double* __restrict__ doc,
-                                                                   const double* __restrict__ pbuf,
-                                                                   const double* __restrict__ dsbuf,
-                                                                   double* __restrict__ dkc,
-                                                                   double* __restrict__ dvc, int ld, double scale) {
-    __shared__ double part[2][2][D];
-    const int s = blockIdx.z, h = blockIdx.y, j = blockIdx.x;
+// out[o][d] = alpha sum_k M(o, k) X[k][d] over one sequence and head:
+//   TRANS = false: o = query block, k = KV block, M(o, k) = m[row(o)][k],
+//                  X = a KV-block array, out a query-block array;
+//   TRANS = true:  o = KV block, k = query block, M(o, k) = m[row(k)][o],
+//                  X = a query-block array, out a KV-block array.
+// 64 output rows x D per workgroup, 16-wide k slices of M and X staged in LDS
+// (the next slice prefetched into registers), 4 rows x D / 16 columns per
+// thread.  Grid (ceil(max rows / 64), H, sequences).
+template <int D, bool TRANS>
+__global__ __launch_bounds__(kThreads) void bwd_coarse_mm_kernel(DevProblem P, const double* __restrict__ m,
+                                                                 const double* __restrict__ x,
+                                                                 double* __restrict__ out, int ld, int maxq,
+                                                                 double alpha) {
+    constexpr int kTile = 64, kSlice = 16, kPad = 2;
+    constexpr int CPT = D / 16;  // output columns per thread
+    __shared__ __attribute__((aligned(16))) double mt[kSlice][kTile + kPad];  // [k][o]
+    __shared__ __attribute__((aligned(16))) double xs[kSlice][D];             // [k][d]
+    const int s = blockIdx.z, h = blockIdx.y;
     const SeqView sv = seq_view(P, s, h);
-    if (j >= sv.nkv) return;
-    const int d = threadIdx.x % D, half = threadIdx.x / D;
-    if (half < 2) {
-        double ak = 0.0, av = 0.0;
-        for (int i = half; i < sv.nq; i += 2) {
-            const int64_t qb = sv.qblk_base + i;
-            ak = fma(dsbuf[qb * ld + j], qc[qb * D + d], ak);
-            av = fma(pbuf[qb * ld + j], doc[qb * D + d], av);
+    const int nout = TRANS ? sv.nkv : sv.nq, nk = TRANS ? sv.nq : sv.nkv;
+    const int o0 = blockIdx.x * kTile;
+    if (o0 >= nout) return;
+    const int64_t row0 = ((int64_t)s * P.H + h) * maxq;  // m row of query block 0
+    const int64_t xbase = TRANS ? sv.qblk_base : sv.kvblk_base;
+    const int64_t obase = TRANS ? sv.kvblk_base : sv.qblk_base;
+    const int tid = threadIdx.x;
+    const int ty = tid / 16, tx = tid % 16;
+    double acc[4][CPT];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[r][c] = 0.0;
+    // staging of M: TRANS = false, thread t holds k = 4 (t % 4) .. + 3 of output
+    // row t / 4; TRANS = true, thread t holds outputs 4 (t % 16) .. + 3 of k row t / 16
+    const int ma = TRANS ? tid / 16 : tid / 4;
+    const int mb = TRANS ? 4 * (tid % 16) : 4 * (tid % 4);
+    double mv[4];
+    double2 xv[D / 32];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            int o, k;
+            if (TRANS) { k = k0 + ma; o = o0 + mb + e; } else { o = o0 + ma; k = k0 + mb + e; }
+            const bool ok = o < nout && k < nk;
+            mv[e] = ok ? (TRANS ? m[(row0 + k) * ld + o] : m[(row0 + o) * ld + k]) : 0.0;
         }
-        part[0][half][d] = ak;
-        part[1][half][d] = av;
+#pragma unroll
+        for (int p = 0; p < D / 32; ++p) {
+            const int e = tid + kThreads * p;  // double2 index in the [16][D] slice
+            const int kr = e / (D / 2), dc = 2 * (e % (D / 2));
+            xv[p] = k0 + kr < nk ? *reinterpret_cast<const double2*>(x + (xbase + k0 + kr) * D + dc)
+                                 : make_double2(0.0, 0.0);
+        }
+    };
+    fetch(0);
+    for (int k0 = 0; k0 < nk; k0 += kSlice) {
+        __syncthreads();  // previous slice fully consumed
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (TRANS) mt[ma][mb + e] = mv[e]; else mt[mb + e][ma] = mv[e];
+        }
+#pragma unroll
+        for (int p = 0; p < D / 32; ++p) {
+            const int e = tid + kThreads * p;
+            *reinterpret_cast<double2*>(&xs[e / (D / 2)][2 * (e % (D / 2))]) = xv[p];
+        }
+        __syncthreads();
+        if (k0 + kSlice < nk) fetch(k0 + kSlice);
+#pragma unroll 4
+        for (int kk = 0; kk < kSlice; ++kk) {
+            const double2 w01 = *reinterpret_cast<const double2*>(&mt[kk][4 * ty]);
+            const double2 w23 = *reinterpret_cast<const double2*>(&mt[kk][4 * ty + 2]);
+            const double w[4] = {w01.x, w01.y, w23.x, w23.y};
+            double v[CPT];
+#pragma unroll
+            for (int c = 0; c < CPT; c += 2) {
+                const double2 t2 = *reinterpret_cast<const double2*>(&xs[kk][CPT * tx + c]);
+                v[c] = t2.x;
+                v[c + 1] = t2.y;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) acc[r][c] = fma(w[r], v[c], acc[r][c]);
+        }
     }
-    __syncthreads();
-    if (threadIdx.x < D) {
-        const int64_t kb = sv.kvblk_base + j;
-        dkc[kb * D + threadIdx.x] = (part[0][0][threadIdx.x] + part[0][1][threadIdx.x]) * scale;
-        dvc[kb * D + threadIdx.x] = part[1][0][threadIdx.x] + part[1][1][threadIdx.x];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int o = o0 + 4 * ty + r;
+        if (o >= nout) continue;
+        double* dst = out + (obase + o) * D + CPT * tx;
+#pragma unroll
+        for (int c = 0; c < CPT; c += 2)
+            *reinterpret_cast<double2*>(dst + c) = make_double2(acc[r][c] * alpha, acc[r][c + 1] * alpha);
     }
 }
 
@@ -746,11 +758,20 @@ hipError_t launch_all(const DevProblem& P, const BwdArgs& A, hipStream_t st) {
     // 2. block means
     if ((e = launch_pool(P, A.q, A.k, A.v, A.qc, A.kc, A.vc, st)) != hipSuccess) return e;
     // 3. coarse backward
-    hipLaunchKernelGGL(bwd_coarse_rows_kernel<D>, dim3(maxq, P.H, seqs), dim3(kThreads), 0, st, P, A.qc, A.kc, A.vc, A.doc, A.pbuf, A.dsbuf, A.dqc,
-                       maxkv, scale);
+    if ((e = launch_coarse_scores(P, A.qc, A.kc, A.pbuf, st)) != hipSuccess) return e;
+    if ((e = launch_coarse_scores(P, A.doc, A.vc, A.dsbuf, st)) != hipSuccess) return e;
+    const int64_t crows = (int64_t)seqs * P.H * maxq;
+    hipLaunchKernelGGL(bwd_coarse_softmax_kernel, dim3((unsigned)((crows + 3) / 4)), dim3(kThreads), 0, st, P,
+                       A.pbuf, A.dsbuf, maxkv, maxq, scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_coarse_cols_kernel<D>, dim3(maxkv, P.H, seqs), dim3(kThreads), 0, st, P, A.qc, A.doc,
-                       A.pbuf, A.dsbuf, A.dkc, A.dvc, maxkv, scale);
+    hipLaunchKernelGGL((bwd_coarse_mm_kernel<D, false>), dim3((maxq + 63) / 64, P.H, seqs), dim3(kThreads), 0, st,
+                       P, A.dsbuf, A.kc, A.dqc, maxkv, maxq, scale);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_coarse_mm_kernel<D, true>), dim3((maxkv + 63) / 64, P.H, seqs), dim3(kThreads), 0, st,
+                       P, A.dsbuf, A.qc, A.dkc, maxkv, maxq, scale);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_coarse_mm_kernel<D, true>), dim3((maxkv + 63) / 64, P.H, seqs), dim3(kThreads), 0, st,
+                       P, A.pbuf, A.doc, A.dvc, maxkv, maxq, 1.0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // 4. inverse routing
     hipLaunchKernelGGL(bwd_k2q_kernel, dim3((maxkv + 3) / 4, P.H, seqs), dim3(kThreads), 0, st, P, A.idx, A.num,

@@ -375,6 +375,19 @@ size_t coarse_scratch_doubles(const DevProblem& P) {
     return (size_t)((int64_t)P.nseq * P.H * chunk_rows(P) * ld + rows);
 }
 
+hipError_t launch_coarse_scores(const DevProblem& P, const double* a, const double* b, double* out, hipStream_t st) {
+    const int max_nq = P.packed ? P.max_q : P.nQ;
+    const int ld = P.packed ? P.max_kv : P.nKV;
+    const int tq = (max_nq + kTile - 1) / kTile, tk = (ld + kTile - 1) / kTile;
+    if (P.D == 128)
+        hipLaunchKernelGGL(coarse_scores_kernel<128>, dim3(tq * tk, P.H, P.nseq), dim3(kThreads), 0, st, P, a, b,
+                           out, ld, tk, 0, max_nq);
+    else
+        hipLaunchKernelGGL(coarse_scores_kernel<64>, dim3(tq * tk, P.H, P.nseq), dim3(kThreads), 0, st, P, a, b,
+                           out, ld, tk, 0, max_nq);
+    return hipGetLastError();
+}
+
 hipError_t launch_coarse_topk(const DevProblem& P, const double* qc, const double* kc, const double* vc,
                               float* out_c, int* idx, int* num, double* scratch, hipStream_t st) {
     const int kv_cap = P.packed ? P.max_kv : P.nKV;

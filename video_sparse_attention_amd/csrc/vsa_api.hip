@@ -170,8 +170,9 @@ BwdWorkspace plan_bwd_workspace(const vsa::DevProblem& P, void* base) {
     w.dqc = (double*)take(qd);
     w.dkc = (double*)take(kd);
     w.dvc = (double*)take(kd);
-    w.pbuf = (double*)take(sizeof(double) * qblocks(P) * maxkv);
-    w.dsbuf = (double*)take(sizeof(double) * qblocks(P) * maxkv);
+    const int64_t coarse_rows = (int64_t)P.nseq * P.H * maxq;
+    w.pbuf = (double*)take(sizeof(double) * coarse_rows * maxkv);
+    w.dsbuf = (double*)take(sizeof(double) * coarse_rows * maxkv);
     w.rs = (float*)take(sizeof(float) * qblocks(P) * vsa::kStatRow);
     w.k2q = (int*)take(sizeof(int) * kvblocks(P) * maxq);
     w.k2q_num = (int*)take(sizeof(int) * kvblocks(P));

@@ -144,6 +144,12 @@ hipError_t launch_coarse_topk(const DevProblem& P, const double* qc, const doubl
                               const double* vc, float* out_c, int* idx, int* num, double* scratch,
                               hipStream_t st);
 size_t coarse_scratch_doubles(const DevProblem& P);
+// out[r][j] = a[query block i] . b[KV block j] (float64, raw dot products) for
+// every sequence s and head h, r = (s * H + h) * max_q + i, row length max_kv
+// (max_q / max_kv: nQ / nKV for DENSE); rows and columns past a sequence's
+// blocks are not written.
+hipError_t launch_coarse_scores(const DevProblem& P, const double* a, const double* b, double* out,
+                                hipStream_t st);
 hipError_t launch_sparse_attn(const DevProblem& P, const uint16_t* q, const uint16_t* k,
                               const uint16_t* v, const int* idx, const int* num, uint16_t* out,
                               hipStream_t st);
@@ -174,9 +180,10 @@ struct BwdArgs {
     // outputs
     uint16_t *dq, *dk, *dv, *dgate;
     // workspace: float64 block-resolution data ([query blocks][D] for qc, doc,
-    // dqc; [KV blocks][D] for kc, vc, dkc, dvc; [query blocks][ld] for pbuf,
-    // dsbuf with ld = max KV blocks per sequence), row statistics
-    // [query blocks][kStatRow], inverse routing [KV blocks][max query blocks]
+    // dqc; [KV blocks][D] for kc, vc, dkc, dvc; [sequences * H * max query
+    // blocks][max KV blocks] for pbuf, dsbuf, rows as launch_coarse_scores),
+    // row statistics [query blocks][kStatRow], inverse routing [KV blocks][max
+    // query blocks]
     double *qc, *kc, *vc, *doc, *dqc, *dkc, *dvc, *pbuf, *dsbuf;
     float* rs;
     int *k2q, *k2q_num;
