@@ -81,6 +81,9 @@ typedef const __attribute__((address_space(4))) int const_int;
 // restored inside the block.
 __device__ __forceinline__ void dma_16B(const void* sbase, uint32_t voff, uint32_t lds_base) {
     uint32_t saved;
+    // the LDS base is wave-uniform; readfirstlane keeps it in a scalar register
+    // even when the compiler has placed the value in a vector one
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %3\n\t"
@@ -98,6 +101,7 @@ __device__ __forceinline__ void dma_16B(const void* sbase, uint32_t voff, uint32
 __device__ __forceinline__ void dma_16B_pair(const void* sbase, uint32_t voff_a, uint32_t voff_b,
                                              uint32_t lds_base) {
     uint32_t saved;
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %4\n\t"
@@ -126,14 +130,19 @@ __device__ __forceinline__ void load_tile(uint32_t lds0, const uint16_t* block, 
         for (int m = 0; m < CH / 4; ++m)
             dma_16B_pair(base + 4096 * m, lane_off0, lane_off1_m2k, lds0 + 4096u * m);
     } else {
+        // instruction n covers physical rows row0 + RSTEP n; the swizzles
+        // depend on n only through n & 1 (bit 3 of the row for CH = 16), so a
+        // lane needs row0 and two chunk numbers, and the clamp is
+        // min(row0, valid - 1 - RSTEP n) + RSTEP n with a scalar bound
+        constexpr int RSTEP = 128 / CH;
+        const int p0 = load_chunk_pos(0, wave, lane);
+        const int row0 = p0 / CH;
+        const int c0 = (p0 % CH) ^ tile_swz<CH, SW>(row0);
+        const int c1 = (p0 % CH) ^ tile_swz<CH, SW>(row0 + RSTEP);
 #pragma unroll
         for (int n = 0; n < CH / 2; ++n) {
-            const int p = load_chunk_pos(n, wave, lane);
-            const int row = p / CH;
-            const int sw = tile_swz<CH, SW>(row);
-            const int c = (p % CH) ^ sw;
-            const int r = min(row, valid - 1);
-            dma_16B(base, (uint32_t)(r * CH * 16 + 16 * c), lds0 + 2048u * n);
+            const int r = min(row0, valid - 1 - RSTEP * n) + RSTEP * n;
+            dma_16B(base, (uint32_t)(r * CH * 16 + 16 * ((n & 1) ? c1 : c0)), lds0 + 2048u * n);
         }
     }
 }

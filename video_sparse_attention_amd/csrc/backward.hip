@@ -332,34 +332,45 @@ __global__ __launch_bounds__(kThreads) void bwd_k2q_kernel(DevProblem P, const i
 // ---------------------------------------------------------------------------
 // shared pieces of the two MFMA kernels
 // ---------------------------------------------------------------------------
-// Row operand of a [64][D] tile: lane (l32, hh) gets T[32 mt + l32][16 ks +
-// 8 hh .. + 7] (A operand of a 32x32x16 product whose rows are the tile's rows).
+// LDS operand reads of a [64][D] tile, from per-lane byte offsets computed
+// once per kernel.  Every swizzle depends on the row through its low 4 bits
+// only, so moving by 32 rows (mt) or 16 rows (s4) is a constant that the
+// compiler folds into the instruction's offset field; only the k-step (row
+// operands) or the d tile and 8-row group (transposed operands) need a
+// register each.
+//
+// Row operand: lane (l32, hh) gets T[32 mt + l32][16 ks + 8 hh .. + 7] (A
+// operand of a 32x32x16 product whose rows are the tile's rows).
 template <int CH, int SW>
-__device__ __forceinline__ bf16x8 row_operand(const uint16_t* tile, int mt, int ks, int l32, int hh) {
-    const int row = 32 * mt + l32;
-    return as_bf16x8(*reinterpret_cast<const uint4*>(tile + tile_off<CH>(row, 2 * ks + hh, tile_swz<CH, SW>(row))));
+__device__ __forceinline__ uint32_t row_offset(int l32, int hh, int ks) {
+    return 2u * (uint32_t)tile_off<CH>(l32, 2 * ks + hh, tile_swz<CH, SW>(l32));
 }
-// Transposed operand of a tile for k-step s4 (16 rows) and 32-row d tile dt:
-// lane (l32, hh) gets T[16 s4 + 4 hh + {0..3, 8..11}][32 dt + l32], the k-slot
-// order of a B operand taken from an accumulator (see acc_to_b).
+template <int CH>
+__device__ __forceinline__ bf16x8 row_read(const uint16_t* tile, uint32_t off, int mt) {
+    return as_bf16x8(*reinterpret_cast<const uint4*>((const char*)tile + off + mt * 32 * CH * 16));
+}
+// Transposed operand for k-step s4 (16 rows) and 32-row d tile dt: lane
+// (l32, hh) gets T[16 s4 + 4 hh + {0..3, 8..11}][32 dt + l32], the k-slot
+// order of a B operand taken from an accumulator (see acc_to_b).  Two
+// transpose reads, rows 16 s4 + 8 jj + 4 hh + tr_r.
 template <int CH, int SW>
-__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int s4, int dt, int hh, int tr_r, int tr_d) {
+__device__ __forceinline__ uint32_t tr_offset(int dt, int jj, int hh, int tr_r, int tr_d) {
+    const int tok = 8 * jj + 4 * hh + tr_r;
     const int d = 32 * dt + tr_d;
-    s16x4 half[2];
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        const int tok = 16 * s4 + 8 * jj + 4 * hh + tr_r;
-        const int off = tile_off<CH>(tok, d >> 3, tile_swz<CH, SW>(tok)) + (d & 7);
-        half[jj] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)tile + off));
-    }
-    const uint2 h0 = __builtin_bit_cast(uint2, half[0]);
-    const uint2 h1 = __builtin_bit_cast(uint2, half[1]);
-    return as_bf16x8(make_uint4(h0.x, h0.y, h1.x, h1.y));
+    return 2u * (uint32_t)(tile_off<CH>(tok, d >> 3, tile_swz<CH, SW>(tok)) + (d & 7));
+}
+template <int CH>
+__device__ __forceinline__ bf16x8 tr_read(const uint16_t* tile, uint32_t off0, uint32_t off1, int s4) {
+    typedef __attribute__((address_space(3))) const char lds_char;
+    lds_char* base = (lds_char*)tile + s4 * 16 * CH * 16;
+    const s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off0));
+    const s16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off1));
+    const uint2 a = __builtin_bit_cast(uint2, h0), b = __builtin_bit_cast(uint2, h1);
+    return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
 }
 // bf16 B operand of k-step s4 from two 32x32 accumulators (rows = the k
 // dimension): k-slots 8 hh .. 8 hh + 7 hold accumulator rows 16 s4 + 4 hh +
-// {0..3, 8..11}, matching tr_operand.
+// {0..3, 8..11}, matching tr_read.
 __device__ __forceinline__ bf16x8 acc_to_b(const f32x16 (&a)[2], int s4) {
     const f32x16& x = a[s4 >> 1];
     const int b = 8 * (s4 & 1);
@@ -380,19 +391,24 @@ __device__ __forceinline__ void load_b_row(const uint16_t* src, bool valid, int 
 
 // ---------------------------------------------------------------------------
 // 5. dQ: one workgroup (2 waves) per query block; wave w owns query rows
-// 32 w .. 32 w + 31, one per lane column.  K and V of each listed KV block are
-// double-buffered in LDS (K in the dual layout: read by rows for S^T = K Q^T
-// and transposed for dQ^T = K^T dS^T; V by rows for dP^T = V dO^T).
+// 32 w .. 32 w + 31, one per lane column, with its Q and dO rows in registers
+// as B operands.  One K tile (read by rows for S^T = K Q^T and transposed for
+// dQ^T = K^T dS^T) and one V tile (read by rows for dP^T = V dO^T) in LDS, both
+// in the dual layout, 32 KiB for D = 128, so that four workgroups share a
+// CU.  Per listed KV block t: wait for V_t and K_t; per 32-token half, dP^T
+// (accumulated onto -delta, so it holds dP^T - delta) and S^T, then dS^T =
+// exp2(S^T c - lse) (dP^T - delta) packed to bf16; release V_t and start
+// V_{t+1}; dQ^T += K^T dS^T; release K_t and start K_{t+1}.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kAttnThreads, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(kAttnThreads, 2) void bwd_dq_kernel(
     DevProblem P, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ rs, const int* __restrict__ idx,
     const int* __restrict__ num, const double* __restrict__ dqc, uint16_t* __restrict__ dq, float c_log2,
     float scale) {
     constexpr int KS = D / 16, DT = D / 32, CH = D / 8;
-    __shared__ __attribute__((aligned(1024))) uint16_t k_tile[2][kBlock * D];
-    __shared__ __attribute__((aligned(1024))) uint16_t v_tile[2][kBlock * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t k_tile[kBlock * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_tile[kBlock * D];
 
     int s, h, i;
     SeqView sv;
@@ -448,15 +464,27 @@ __global__ __launch_bounds__(kAttnThreads, 1) void bwd_dq_kernel(
     auto kv_size = [&](int j) -> int {
         return P.packed ? clampi(bs_kv[j], 1, kBlock) : min(kBlock, P.Skv - kBlock * j);
     };
-    const uint32_t koff0 = (uint32_t)lane_src_offset<CH, kSwzDual>(wave, lane, 0);
-    const uint32_t koff1 = (uint32_t)lane_src_offset<CH, kSwzDual>(wave, lane, 1) - 2048u;
-    const uint32_t voff0 = (uint32_t)lane_src_offset<CH, kSwzRow>(wave, lane, 0);
-    const uint32_t voff1 = (uint32_t)lane_src_offset<CH, kSwzRow>(wave, lane, 1) - 2048u;
-    const uint32_t k_lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&k_tile[0][0] + 1024u * wave);
-    const uint32_t v_lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&v_tile[0][0] + 1024u * wave);
-    constexpr uint32_t kTileBytes = 2u * kBlock * D;
+    // both tiles in the dual layout (V is only read by rows, which that layout
+    // serves without conflicts too), so they share every lane offset
+    const uint32_t off0 = (uint32_t)lane_src_offset<CH, kSwzDual>(wave, lane, 0);
+    const uint32_t off1 = (uint32_t)lane_src_offset<CH, kSwzDual>(wave, lane, 1) - 2048u;
+    const uint32_t k_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)k_tile + 1024u * wave);
+    const uint32_t v_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)v_tile + 1024u * wave);
     const int L16 = lane & 15, g16 = lane >> 4;
     const int tr_r = tr_token(L16), tr_d = 16 * (g16 & 1) + 4 * tr_dquad(L16);
+    uint32_t t_row[KS], k_tr[DT][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) t_row[ks] = row_offset<CH, kSwzDual>(l32, hh, ks);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) k_tr[dt][jj] = tr_offset<CH, kSwzDual>(dt, jj, hh, tr_r, tr_d);
+    auto issue_v = [&](int jj, int vs) {
+        load_tile<D, kSwzDual>(v_lds, v + (sv.kvrow_base + (int64_t)kBlock * jj) * D, vs, wave, lane, off0, off1);
+    };
+    auto issue_k = [&](int jj, int vs) {
+        load_tile<D, kSwzDual>(k_lds, k + (sv.kvrow_base + (int64_t)kBlock * jj) * D, vs, wave, lane, off0, off1);
+    };
 
     // the operands above are in registers before the first direct copy, so
     // the copies are the only vector-memory operations the waits count
@@ -466,63 +494,85 @@ __global__ __launch_bounds__(kAttnThreads, 1) void bwd_dq_kernel(
     int j = next_valid(t);
     int kvsize = j >= 0 ? kv_size(j) : 0;
     if (j >= 0) {
-        const int64_t r0 = sv.kvrow_base + (int64_t)kBlock * j;
-        load_tile<D, kSwzDual>(k_lds0, k + r0 * D, kvsize, wave, lane, koff0, koff1);
-        load_tile<D, kSwzRow>(v_lds0, v + r0 * D, kvsize, wave, lane, voff0, voff1);
+        issue_v(j, kvsize);
+        issue_k(j, kvsize);
     }
-    int buf = 0;
     while (j >= 0) {
-        wait_vmcnt<0>();
-        wg_barrier();  // block j is in LDS; every wave is done with the other buffer
         ++t;
         const int jn = next_valid(t);
-        const int kvsize_n = jn >= 0 ? kv_size(jn) : 0;
-        if (jn >= 0) {
-            const int64_t r0 = sv.kvrow_base + (int64_t)kBlock * jn;
-            load_tile<D, kSwzDual>(k_lds0 + kTileBytes * (buf ^ 1), k + r0 * D, kvsize_n, wave, lane, koff0, koff1);
-            load_tile<D, kSwzRow>(v_lds0 + kTileBytes * (buf ^ 1), v + r0 * D, kvsize_n, wave, lane, voff0, voff1);
-        }
-        const uint16_t* kt = k_tile[buf];
-        const uint16_t* vt = v_tile[buf];
-
-        // S^T = K Q^T and dP^T = V dO^T: rows = KV tokens, lane column = query
-        f32x16 sacc[2], pacc[2];
+        const bool more = jn >= 0;
+        const int kvsize_n = more ? kv_size(jn) : 0;
+        wait_vmcnt<0>();  // V_t and K_t landed
+        wg_barrier();
+        // One 32-token half (mt) of the block at a time: dP^T - delta = V dO^T -
+        // delta and S^T = K Q^T (rows = KV tokens 32 mt + 8 (e / 4) + 4 hh +
+        // e % 4, lane column = query), then dS^T = exp2(S^T c - lse) (dP^T -
+        // delta), kept as the bf16 B operands of k-steps 2 mt and 2 mt + 1.
+        bf16x8 dsb[4];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) sacc[mt][e] = pacc[mt][e] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<CH, kSwzDual>(kt, mt, ks, l32, hh),
-                                                                   qf[ks], sacc[mt], 0, 0, 0);
-                pacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<CH, kSwzRow>(vt, mt, ks, l32, hh),
-                                                                   df[ks], pacc[mt], 0, 0, 0);
-            }
-        // dS^T = P^T (dP^T - delta), P^T = exp2(S^T c - lse); element e of tile
-        // mt is KV token 32 mt + 8 (e / 4) + 4 hh + e % 4
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt) {
+            f32x16 pacc, sacc;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int tok = 32 * mt + 8 * (e >> 2) + 4 * hh + (e & 3);
-                float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][e], c_log2, -lse));
-                if (tok >= kvsize) p = 0.f;
-                sacc[mt][e] = p * (pacc[mt][e] - delta);
+                pacc[e] = -delta;
+                sacc[e] = 0.f;
             }
-        // dQ^T += K^T dS^T over 4 k-steps of 16 KV tokens
+            // operands are read one k-step ahead of their MFMAs; the scheduling
+            // barriers keep the compiler from hoisting every read (registers)
+            bf16x8 va = row_read<CH>(v_tile, t_row[0], mt);
+            bf16x8 ka = row_read<CH>(k_tile, t_row[0], mt);
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-            const bf16x8 b = acc_to_b(sacc, s4);
+            for (int ks = 0; ks < KS; ++ks) {
+                bf16x8 vn = va, kn = ka;
+                if (ks + 1 < KS) {
+                    vn = row_read<CH>(v_tile, t_row[ks + 1], mt);
+                    kn = row_read<CH>(k_tile, t_row[ks + 1], mt);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[ks], pacc, 0, 0, 0);
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], sacc, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                va = vn;
+                ka = kn;
+            }
+            if (kvsize < kBlock) {  // tokens past a partial block: S = -inf, P = 0
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<CH, kSwzDual>(kt, s4, dt, hh, tr_r, tr_d),
-                                                                  b, acc[dt], 0, 0, 0);
+                for (int e = 0; e < 16; ++e) {
+                    const int tok = 32 * mt + 8 * (e >> 2) + 4 * hh + (e & 3);
+                    if (tok >= kvsize) sacc[e] = -INFINITY;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sacc[e] = __builtin_amdgcn_exp2f(fmaf(sacc[e], c_log2, -lse)) * pacc[e];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                dsb[2 * mt + hf] = as_bf16x8(make_uint4(
+                    bf16pair(sacc[8 * hf + 0], sacc[8 * hf + 1]), bf16pair(sacc[8 * hf + 2], sacc[8 * hf + 3]),
+                    bf16pair(sacc[8 * hf + 4], sacc[8 * hf + 5]), bf16pair(sacc[8 * hf + 6], sacc[8 * hf + 7])));
         }
+        wg_barrier();  // both waves are done with the V tile
+        if (more) issue_v(jn, kvsize_n);
+        // dQ^T += K^T dS^T over 4 k-steps of 16 KV tokens
+        {
+            bf16x8 ta = tr_read<CH>(k_tile, k_tr[0][0], k_tr[0][1], 0);
+#pragma unroll
+            for (int x = 0; x < 4 * DT; ++x) {
+                const int s4 = x / DT, dt = x % DT;
+                bf16x8 tn = ta;
+                if (x + 1 < 4 * DT) {
+                    const int dn = (x + 1) % DT;
+                    tn = tr_read<CH>(k_tile, k_tr[dn][0], k_tr[dn][1], (x + 1) / DT);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta, dsb[s4], acc[dt], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                ta = tn;
+            }
+        }
+        wg_barrier();  // both waves are done with the K tile
+        if (more) issue_k(jn, kvsize_n);
         j = jn;
         kvsize = kvsize_n;
-        buf ^= 1;
     }
 
     // lane holds dQ[qr][32 dt + 8 (e / 4) + 4 hh + e % 4]
@@ -621,6 +671,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void bwd_dkdv_kernel(
     constexpr uint32_t kStatBytes = 4u * kStatRow;
     const int L16 = lane & 15, g16 = lane >> 4;
     const int tr_r = tr_token(L16), tr_d = 16 * (g16 & 1) + 4 * tr_dquad(L16);
+    // both tiles use the dual layout, so they share the operand offsets
+    uint32_t t_row[KS], t_tr[DT][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) t_row[ks] = row_offset<CH, kSwzDual>(l32, hh, ks);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) t_tr[dt][jj] = tr_offset<CH, kSwzDual>(dt, jj, hh, tr_r, tr_d);
 
     // copies of query block i (local index) into buffer b
     auto issue = [&](int i, int b) {
@@ -655,10 +713,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void bwd_dkdv_kernel(
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<CH, kSwzDual>(qt, mt, ks, l32, hh),
-                                                                   kf[ks], sacc[mt], 0, 0, 0);
-                pacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<CH, kSwzDual>(ot, mt, ks, l32, hh),
-                                                                   vf[ks], pacc[mt], 0, 0, 0);
+                sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<CH>(qt, t_row[ks], mt), kf[ks],
+                                                                   sacc[mt], 0, 0, 0);
+                pacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<CH>(ot, t_row[ks], mt), vf[ks],
+                                                                   pacc[mt], 0, 0, 0);
             }
         // P = exp2(S c - lse[row]), dS = P (dP - delta[row]); element e of tile
         // mt is query row 32 mt + 8 (e / 4) + 4 hh + e % 4 (padding rows have
@@ -687,9 +745,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void bwd_dkdv_kernel(
             const bf16x8 db = acc_to_b(dsacc, s4);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<CH, kSwzDual>(ot, s4, dt, hh, tr_r, tr_d),
+                dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<CH>(ot, t_tr[dt][0], t_tr[dt][1], s4),
                                                                   pb, dva[dt], 0, 0, 0);
-                dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<CH, kSwzDual>(qt, s4, dt, hh, tr_r, tr_d),
+                dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<CH>(qt, t_tr[dt][0], t_tr[dt][1], s4),
                                                                   db, dka[dt], 0, 0, 0);
             }
         }
