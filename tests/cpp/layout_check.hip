@@ -9,6 +9,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <set>
 #include <vector>
 
@@ -72,6 +73,43 @@ static std::vector<int> fill_tile(int valid) {
                 for (int e = 0; e < 8; ++e) tile[lds_elem + e] = val(src_byte / ROWB, (src_byte % ROWB) / 2 + e);
             }
     for (int p = 0; p < 64 * CH; ++p) CHECK(hits[p] == 1, "chunk %d written %d times", p, hits[p]);
+    return tile;
+}
+
+// The four-wave copy (load_tile4): every chunk written once, the fast-path
+// lane offset plus 4096 n equals the per-instruction one, partial blocks clamp
+// inside the valid rows, and the resulting tile equals the two-wave one.
+template <int D, int SW, int ROWS = 64>
+static std::vector<int> fill_tile4(int valid) {
+    constexpr int CH = D / 8;
+    constexpr int ROWB = CH * 16;
+    constexpr int RSTEP = 256 / CH;
+    constexpr int NI = ROWS * CH / 256;
+    std::vector<int> tile(ROWS * D, -1);
+    std::vector<int> hits(ROWS * CH, 0);
+    for (int wave = 0; wave < 4; ++wave)
+        for (int n = 0; n < NI; ++n)
+            for (int lane = 0; lane < 64; ++lane) {
+                const int p = vsa::load_chunk_pos4(n, wave, lane);
+                CHECK(p >= 0 && p < ROWS * CH, "chunk position %d out of range (4 waves)", p);
+                hits[p]++;
+                const int row = p / CH;
+                const int c = (p % CH) ^ vsa::tile_swz<CH, SW>(row);
+                const int fast = vsa::lane_src_offset4<CH, SW>(wave, lane) + 4096 * n;
+                CHECK(fast == row * ROWB + 16 * c, "4-wave fast-path offset D%d SW%d n%d w%d l%d", D, SW, n, wave, lane);
+                // the kernel's partial-block formula
+                const int p0 = vsa::load_chunk_pos4(0, wave, lane);
+                const int row0 = p0 / CH;
+                const int c0 = (p0 % CH) ^ vsa::tile_swz<CH, SW>(row0);
+                const int rk = std::min(row0, valid - 1 - RSTEP * n) + RSTEP * n;
+                CHECK(row0 + RSTEP * n == row && c0 == c, "4-wave partial-path row/chunk");
+                CHECK(rk == std::min(row, valid - 1), "4-wave partial-path clamp");
+                const int src_byte = valid >= ROWS ? fast : rk * ROWB + 16 * c0;
+                CHECK(src_byte / ROWB < valid, "4-wave copy reads past the valid rows");
+                const int lds_elem = (4 * n + wave) * 64 * 8 + 8 * lane;
+                for (int e = 0; e < 8; ++e) tile[lds_elem + e] = val(src_byte / ROWB, (src_byte % ROWB) / 2 + e);
+            }
+    for (int p = 0; p < ROWS * CH; ++p) CHECK(hits[p] == 1, "chunk %d written %d times (4 waves)", p, hits[p]);
     return tile;
 }
 
@@ -195,6 +233,15 @@ static void check_d() {
         const std::vector<int> dual = fill_tile<D, vsa::kSwzDual>(valid);
         check_row_operand<D, vsa::kSwzDual>(dual, valid);
         check_tr_operand<D, vsa::kSwzDual>(dual, valid);
+        const bool same4 = fill_tile4<D, vsa::kSwzDual>(valid) == dual;
+        CHECK(same4, "4-wave copy differs from the 2-wave one (D=%d)", D);
+        // a 32-row tile: the first 32 rows of the 64-row layout (rows clamped
+        // to min(valid, 32) - 1), read by the same row and transposed operands
+        const int v32 = valid < 32 ? valid : 32;
+        const std::vector<int> half = fill_tile4<D, vsa::kSwzDual, 32>(v32);
+        const std::vector<int> ref32 = fill_tile<D, vsa::kSwzDual>(v32);
+        const bool same32 = std::equal(half.begin(), half.end(), ref32.begin());
+        CHECK(same32, "32-row 4-wave copy differs from the first rows of the 64-row layout (D=%d)", D);
     }
     for (int banks : {32, 64}) {
         const int kr = bank_row<D, vsa::kSwzRow>(banks), vt = bank_tr<D, vsa::kSwzTr>(banks);

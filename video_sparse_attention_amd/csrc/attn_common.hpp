@@ -147,5 +147,33 @@ __device__ __forceinline__ void load_tile(uint32_t lds0, const uint16_t* block, 
     }
 }
 
+// The same copy of the first ROWS (64 or 32) rows of a block by four waves
+// (load_chunk_pos4): each wave issues ROWS CH / 256 instructions; instruction
+// n of a block with every row valid fetches lane_off + 4096 n into LDS byte
+// lds0 + 4096 n (lds0 = tile + 1024 wave).  Rows at or past `valid` repeat row
+// valid - 1, as in load_tile.
+template <int D, int SW, int ROWS>
+__device__ __forceinline__ void load_tile4(uint32_t lds0, const uint16_t* block, int valid, int wave, int lane,
+                                           uint32_t lane_off) {
+    constexpr int CH = D / 8;
+    constexpr int NI = ROWS * CH / 256;  // instructions per wave
+    constexpr int RSTEP = 256 / CH;      // rows between a lane's instructions
+    static_assert(NI >= 1 && NI * 256 == ROWS * CH, "tile rows must fill whole instructions");
+    const char* base = (const char*)uniform_ptr(block);
+    if (valid >= ROWS) {
+#pragma unroll
+        for (int n = 0; n < NI; ++n) dma_16B(base + 4096 * n, lane_off, lds0 + 4096u * n);
+    } else {
+        const int p0 = load_chunk_pos4(0, wave, lane);
+        const int row0 = p0 / CH;
+        const int c0 = (p0 % CH) ^ tile_swz<CH, SW>(row0);
+#pragma unroll
+        for (int n = 0; n < NI; ++n) {
+            const int r = min(row0, valid - 1 - RSTEP * n) + RSTEP * n;
+            dma_16B(base, (uint32_t)(r * CH * 16 + 16 * c0), lds0 + 4096u * n);
+        }
+    }
+}
+
 }  // namespace attn
 }  // namespace vsa

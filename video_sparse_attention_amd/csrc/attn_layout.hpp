@@ -69,6 +69,18 @@ __host__ __device__ inline int tile_off(int row, int c, int swz) {
 // (p % CH) ^ swz(p / CH) of row p / CH.
 __host__ __device__ inline int load_chunk_pos(int n, int wave, int lane) { return (2 * n + wave) * 64 + lane; }
 
+// The same for a tile copied by four waves: instruction n of wave w fills LDS
+// chunks p = (4 n + w) * 64 + lane.  Rows per instruction step: 256 / CH, so
+// the swizzle (low 4 row bits) seen by a lane is the same for every n.
+__host__ __device__ inline int load_chunk_pos4(int n, int wave, int lane) { return (4 * n + wave) * 64 + lane; }
+
+template <int CH, int SW>
+__host__ __device__ inline int lane_src_offset4(int wave, int lane) {
+    const int p = load_chunk_pos4(0, wave, lane);
+    const int row = p / CH;
+    return row * CH * 16 + 16 * ((p % CH) ^ tile_swz<CH, SW>(row));
+}
+
 // Byte offset, inside a full 64-row block of the source tensor, of the chunk
 // that copy instruction n (n = 0 or 1) of (wave, lane) fetches; instruction
 // n + 2m fetches the one 4096 m bytes further (rows are 16 * CH bytes).

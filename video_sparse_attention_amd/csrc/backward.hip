@@ -351,7 +351,7 @@ __device__ __forceinline__ bf16x8 row_read(const uint16_t* tile, uint32_t off, i
 }
 // Transposed operand for k-step s4 (16 rows) and 32-row d tile dt: lane
 // (l32, hh) gets T[16 s4 + 4 hh + {0..3, 8..11}][32 dt + l32], the k-slot
-// order of a B operand taken from an accumulator (see acc_to_b).  Two
+// order of a B operand taken from an accumulator (see pack_half).  Two
 // transpose reads, rows 16 s4 + 8 jj + 4 hh + tr_r.
 template <int CH, int SW>
 __device__ __forceinline__ uint32_t tr_offset(int dt, int jj, int hh, int tr_r, int tr_d) {
@@ -367,15 +367,6 @@ __device__ __forceinline__ bf16x8 tr_read(const uint16_t* tile, uint32_t off0, u
     const s16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off1));
     const uint2 a = __builtin_bit_cast(uint2, h0), b = __builtin_bit_cast(uint2, h1);
     return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
-}
-// bf16 B operand of k-step s4 from two 32x32 accumulators (rows = the k
-// dimension): k-slots 8 hh .. 8 hh + 7 hold accumulator rows 16 s4 + 4 hh +
-// {0..3, 8..11}, matching tr_read.
-__device__ __forceinline__ bf16x8 acc_to_b(const f32x16 (&a)[2], int s4) {
-    const f32x16& x = a[s4 >> 1];
-    const int b = 8 * (s4 & 1);
-    return as_bf16x8(make_uint4(bf16pair(x[b + 0], x[b + 1]), bf16pair(x[b + 2], x[b + 3]),
-                                bf16pair(x[b + 4], x[b + 5]), bf16pair(x[b + 6], x[b + 7])));
 }
 // One row of D bf16 values as the B operand of products over d: lane (l32,
 // hh) gets src[16 ks + 8 hh .. + 7] for every k-step (zeros if !valid).
@@ -600,23 +591,45 @@ __global__ __launch_bounds__(kAttnThreads, 2) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 6. dK, dV: one workgroup (2 waves) per KV block; wave w owns KV tokens
-// 32 w .. 32 w + 31, one per lane column, with its K and V rows in registers.
-// Q and dO of each query block that listed this KV block are double-buffered
-// in LDS in the dual layout (read by rows for S = Q K^T and dP = dO V^T,
-// transposed for dV^T = dO^T P and dK^T = Q^T dS), with the block's 64
-// log-sum-exp and delta values next to them.
+// 6. dK, dV: one workgroup (4 waves) per KV block.  Wave w serves KV tokens
+// 32 g .. 32 g + 31 (g = w / 2, one token per lane column) in role r = w % 2:
+// role 0 holds K rows and computes S = Q K^T and P = exp2(S c - lse), role 1
+// holds V rows and computes dP - delta = dO V^T - delta; the two exchange
+// these (float32) through LDS, both form dS = P (dP - delta), and each
+// accumulates dV^T = dO^T P and dK^T = Q^T dS for one half of d (r).  So no
+// product is computed twice, and a wave holds one 32 x D operand and two
+// 32 x D/2 accumulators, which lets two waves share a SIMD.
+// The query blocks that listed this KV block are walked in stages of 32
+// query rows (a block's second half only if it has valid rows there); the Q
+// and dO rows of a stage (dual layout: read by rows for S and dP, transposed
+// for dV^T and dK^T) and its 32 log-sum-exp and delta values are
+// double-buffered in LDS, the copy of stage u + 1 running during stage u:
+// 48.5 KiB for D = 128, two workgroups per CU.
 // ---------------------------------------------------------------------------
+// bf16 B operand of k-step hf (16 rows) of one 32x32 accumulator whose rows
+// are the k dimension: k-slots 8 hh .. 8 hh + 7 hold rows 16 hf + 4 hh +
+// {0..3, 8..11}, matching tr_read.
+__device__ __forceinline__ bf16x8 pack_half(const f32x16& x, int hf) {
+    const int b = 8 * hf;
+    return as_bf16x8(make_uint4(bf16pair(x[b + 0], x[b + 1]), bf16pair(x[b + 2], x[b + 3]),
+                                bf16pair(x[b + 4], x[b + 5]), bf16pair(x[b + 6], x[b + 7])));
+}
+
+constexpr int kDkdvThreads = 256;
+constexpr int kHalf = kBlock / 2;  // query rows per stage
+
 template <int D>
-__global__ __launch_bounds__(kAttnThreads, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kDkdvThreads, 3) void bwd_dkdv_kernel(
     DevProblem P, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ rs, const int* __restrict__ k2q,
     const int* __restrict__ k2q_num, int ldq, const double* __restrict__ dkc, const double* __restrict__ dvc,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float c_log2, float scale) {
-    constexpr int KS = D / 16, DT = D / 32, CH = D / 8;
-    __shared__ __attribute__((aligned(1024))) uint16_t q_tile[2][kBlock * D];
-    __shared__ __attribute__((aligned(1024))) uint16_t o_tile[2][kBlock * D];
-    __shared__ __attribute__((aligned(16))) float stats[2][kStatRow];
+    constexpr int KS = D / 16, DT = D / 32, DH = DT / 2, CH = D / 8;
+    __shared__ __attribute__((aligned(1024))) uint16_t q_tile[2][kHalf * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t o_tile[2][kHalf * D];
+    __shared__ __attribute__((aligned(16))) float stats[2][2 * kHalf];  // [buffer][lse 0..31, delta 32..63]
+    // [token group][role][accumulator element / 4][lane]
+    __shared__ __attribute__((aligned(16))) float4 xch[2][2][4][64];
 
     int s, h, j;
     SeqView sv;
@@ -641,17 +654,21 @@ __global__ __launch_bounds__(kAttnThreads, 1) void bwd_dkdv_kernel(
     const int kvsize = kv_block_size(P, sv, j);
     const int64_t kvrow0 = sv.kvrow_base + (int64_t)kBlock * j;
     const int64_t kb = sv.kvblk_base + j;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
-    const int kr = 32 * wave + l32;
+    // wave, token group and role are wave-uniform: readfirstlane puts them in
+    // scalar registers, so role-dependent code is branched over, not selected
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
+    const int grp = wave >> 1, role = wave & 1;
+    const int kr = 32 * grp + l32;
     const bool kvalid = kr < kvsize;
 
-    bf16x8 kf[KS], vf[KS];
-    load_b_row<KS>(k + (kvrow0 + kr) * D, kvalid, hh, kf);
-    load_b_row<KS>(v + (kvrow0 + kr) * D, kvalid, hh, vf);
+    // role 0: K^T operand of S = Q K^T; role 1: V^T operand of dP = dO V^T
+    bf16x8 bfrag[KS];
+    load_b_row<KS>((role ? v : k) + (kvrow0 + kr) * D, kvalid, hh, bfrag);
 
-    f32x16 dka[DT], dva[DT];
+    f32x16 dka[DH], dva[DH];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DH; ++dt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) dka[dt][e] = dva[dt][e] = 0.f;
 
@@ -662,99 +679,153 @@ __global__ __launch_bounds__(kAttnThreads, 1) void bwd_dkdv_kernel(
     auto q_size = [&](int i) -> int {
         return P.packed ? clampi(bs_q[i], 1, kBlock) : min(kBlock, P.Sq - kBlock * i);
     };
-    const uint32_t off0 = (uint32_t)lane_src_offset<CH, kSwzDual>(wave, lane, 0);
-    const uint32_t off1 = (uint32_t)lane_src_offset<CH, kSwzDual>(wave, lane, 1) - 2048u;
-    const uint32_t q_lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&q_tile[0][0] + 1024u * wave);
-    const uint32_t o_lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&o_tile[0][0] + 1024u * wave);
-    const uint32_t st_lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&stats[0][0]);
-    constexpr uint32_t kTileBytes = 2u * kBlock * D;
-    constexpr uint32_t kStatBytes = 4u * kStatRow;
+    auto entry = [&](int x) -> int { return clampi(list[x], 0, nq - 1); };
+    constexpr uint32_t kTileBytes = 2u * kHalf * D;
+    constexpr uint32_t kStatBytes = 4u * 2 * kHalf;
+    const uint32_t off = (uint32_t)lane_src_offset4<CH, kSwzDual>(wave, lane);
+    const uint32_t q_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&q_tile[0][0] + 1024u * wave);
+    const uint32_t o_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&o_tile[0][0] + 1024u * wave);
+    const uint32_t st_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&stats[0][0]);
+    // statistics copy: lanes 0..7 fetch the stage's 32 lse values, lanes 8..15
+    // its 32 delta values (rows 64 .. 127 of the block's statistics row)
+    const uint32_t st_off = lane < 8 ? 16u * lane : 256u + 16u * (lane - 8);
     const int L16 = lane & 15, g16 = lane >> 4;
     const int tr_r = tr_token(L16), tr_d = 16 * (g16 & 1) + 4 * tr_dquad(L16);
-    // both tiles use the dual layout, so they share the operand offsets
-    uint32_t t_row[KS], t_tr[DT][2];
+    uint32_t t_row[KS], t_tr[DH][2];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) t_row[ks] = row_offset<CH, kSwzDual>(l32, hh, ks);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DH; ++dt)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) t_tr[dt][jj] = tr_offset<CH, kSwzDual>(dt, jj, hh, tr_r, tr_d);
+        for (int jj = 0; jj < 2; ++jj) t_tr[dt][jj] = tr_offset<CH, kSwzDual>(DH * role + dt, jj, hh, tr_r, tr_d);
+    float4* my_xch = &xch[grp][role][0][lane];
+    const float4* other_xch = &xch[grp][role ^ 1][0][lane];
 
-    // copies of query block i (local index) into buffer b
-    auto issue = [&](int i, int b) {
-        const int64_t r0 = sv.qrow_base + (int64_t)kBlock * i;
-        const int qs = q_size(i);
-        load_tile<D, kSwzDual>(q_lds0 + kTileBytes * b, q + r0 * D, qs, wave, lane, off0, off1);
-        load_tile<D, kSwzDual>(o_lds0 + kTileBytes * b, dout + r0 * D, qs, wave, lane, off0, off1);
-        // 512 bytes of row statistics: lanes 0..31 of wave 0, 16 bytes each
-        if (wave == 0 && lane < 32)
-            dma_16B(uniform_ptr(rs + (sv.qblk_base + i) * kStatRow), 16u * lane, st_lds0 + kStatBytes * b);
+    // copies of stage (query block i, half hf) into buffer b
+    auto issue = [&](int i, int hf, int b) {
+        const int64_t r0 = sv.qrow_base + (int64_t)kBlock * i + kHalf * hf;
+        const int valid = min(q_size(i) - kHalf * hf, kHalf);
+        load_tile4<D, kSwzDual, kHalf>(q_lds + kTileBytes * b, q + r0 * D, valid, wave, lane, off);
+        load_tile4<D, kSwzDual, kHalf>(o_lds + kTileBytes * b, dout + r0 * D, valid, wave, lane, off);
+        if (wave == 0 && lane < 16)
+            dma_16B(uniform_ptr(rs + (sv.qblk_base + i) * kStatRow + kHalf * hf), st_off, st_lds + kStatBytes * b);
     };
-    auto entry = [&](int x) -> int { return clampi(list[x], 0, nq - 1); };
 
     __builtin_amdgcn_s_waitcnt(0);
-    if (m > 0) issue(entry(0), 0);
+    int x = 0, hf = 0;
+    int ci = m > 0 ? entry(0) : 0;  // query block of the current stage
+    if (m > 0) issue(ci, 0, 0);
     int buf = 0;
-    for (int x = 0; x < m; ++x) {
+    while (x < m) {
+        // the stage after (x, hf): the block's second half if it has valid rows
+        int nx = x, nhf = 1, ni = ci;
+        if (hf == 1 || q_size(ci) <= kHalf) {
+            nx = x + 1;
+            nhf = 0;
+            ni = nx < m ? entry(nx) : 0;
+        }
         wait_vmcnt<0>();
-        wg_barrier();  // block x is in LDS; every wave is done with the other buffer
-        if (x + 1 < m) issue(entry(x + 1), buf ^ 1);
+        wg_barrier();  // this stage is in LDS; every wave is done with the other buffer
+        if (nx < m) issue(ni, nhf, buf ^ 1);
         const uint16_t* qt = q_tile[buf];
         const uint16_t* ot = o_tile[buf];
         const float* st = stats[buf];
-
-        // S = Q K^T and dP = dO V^T: rows = queries, lane column = KV token
-        f32x16 sacc[2], pacc[2];
+        // role 0: S = Q K^T; role 1: dP = dO V^T; rows = the stage's 32 queries
+        // 8 (e / 4) + 4 hh + e % 4, lane column = KV token
+        f32x16 a;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int e = 0; e < 16; ++e) a[e] = 0.f;
+        {
+            const uint16_t* my_tile = role ? ot : qt;
+            bf16x8 ta = row_read<CH>(my_tile, t_row[0], 0);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) sacc[mt][e] = pacc[mt][e] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<CH>(qt, t_row[ks], mt), kf[ks],
-                                                                   sacc[mt], 0, 0, 0);
-                pacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read<CH>(ot, t_row[ks], mt), vf[ks],
-                                                                   pacc[mt], 0, 0, 0);
-            }
-        // P = exp2(S c - lse[row]), dS = P (dP - delta[row]); element e of tile
-        // mt is query row 32 mt + 8 (e / 4) + 4 hh + e % 4 (padding rows have
-        // lse = +inf, so P = 0 there)
-        f32x16 dsacc[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int r0 = 32 * mt + 8 * g + 4 * hh;
-                const float4 l4 = *reinterpret_cast<const float4*>(st + r0);
-                const float4 d4 = *reinterpret_cast<const float4*>(st + kBlock + r0);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dl[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][4 * g + e], c_log2, -lv[e]));
-                    if (!kvalid) p = 0.f;
-                    sacc[mt][4 * g + e] = p;
-                    dsacc[mt][4 * g + e] = p * (pacc[mt][4 * g + e] - dl[e]);
-                }
-            }
-        // dV^T += dO^T P and dK^T += Q^T dS over 4 k-steps of 16 queries
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-            const bf16x8 pb = acc_to_b(sacc, s4);
-            const bf16x8 db = acc_to_b(dsacc, s4);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<CH>(ot, t_tr[dt][0], t_tr[dt][1], s4),
-                                                                  pb, dva[dt], 0, 0, 0);
-                dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read<CH>(qt, t_tr[dt][0], t_tr[dt][1], s4),
-                                                                  db, dka[dt], 0, 0, 0);
+            for (int ks = 0; ks < KS; ++ks) {
+                bf16x8 tn = ta;
+                if (ks + 1 < KS) tn = row_read<CH>(my_tile, t_row[ks + 1], 0);
+                __builtin_amdgcn_sched_barrier(0);
+                a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta, bfrag[ks], a, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                ta = tn;
             }
         }
+        // role 0: P = exp2(S c - lse[row]) (padding rows have lse = +inf: P = 0;
+        // columns past a partial KV block: P = 0); role 1: dP - delta[row]
+        if (role == 0) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 st4 = *reinterpret_cast<const float4*>(st + 8 * g + 4 * hh);
+                const float sv4[4] = {st4.x, st4.y, st4.z, st4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[4 * g + e] = __builtin_amdgcn_exp2f(fmaf(a[4 * g + e], c_log2, -sv4[e]));
+            }
+            if (kvsize < kBlock && !kvalid) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) a[e] = 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 st4 = *reinterpret_cast<const float4*>(st + kHalf + 8 * g + 4 * hh);
+                const float sv4[4] = {st4.x, st4.y, st4.z, st4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[4 * g + e] -= sv4[e];
+            }
+        }
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+            my_xch[64 * e4] = make_float4(a[4 * e4], a[4 * e4 + 1], a[4 * e4 + 2], a[4 * e4 + 3]);
+        wg_barrier();  // the partner's half is in LDS
+        // P and dS = P (dP - delta), as the bf16 B operands of the stage's two k-steps
+        bf16x8 pb[2], db[2];
+        {
+            f32x16 pm, dm;
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const float4 o4 = other_xch[64 * e4];
+                const float ov[4] = {o4.x, o4.y, o4.z, o4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // P from role 0, dP - delta from role 1, whichever is this wave's
+                    const float mine = a[4 * e4 + e];
+                    pm[4 * e4 + e] = role ? ov[e] : mine;
+                    dm[4 * e4 + e] = mine * ov[e];
+                }
+            }
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                pb[k2] = pack_half(pm, k2);
+                db[k2] = pack_half(dm, k2);
+            }
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS for this wave's half of d, the
+        // transposed operands read one product ahead
+        {
+            bf16x8 ta = tr_read<CH>(ot, t_tr[0][0], t_tr[0][1], 0);
+            bf16x8 tb = tr_read<CH>(qt, t_tr[0][0], t_tr[0][1], 0);
+#pragma unroll
+            for (int y = 0; y < 2 * DH; ++y) {
+                const int k2 = y / DH, dt = y % DH;
+                bf16x8 na = ta, nb = tb;
+                if (y + 1 < 2 * DH) {
+                    const int k2n = (y + 1) / DH, dtn = (y + 1) % DH;
+                    na = tr_read<CH>(ot, t_tr[dtn][0], t_tr[dtn][1], k2n);
+                    nb = tr_read<CH>(qt, t_tr[dtn][0], t_tr[dtn][1], k2n);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta, pb[k2], dva[dt], 0, 0, 0);
+                dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tb, db[k2], dka[dt], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                ta = na;
+                tb = nb;
+            }
+        }
+        x = nx;
+        hf = nhf;
+        ci = ni;
         buf ^= 1;
     }
 
-    // lane holds dK / dV [kr][32 dt + 8 (e / 4) + 4 hh + e % 4]
+    // lane holds dK / dV [kr][32 (DH role + dt) + 8 (e / 4) + 4 hh + e % 4]
     uint16_t* krow = dk + (kvrow0 + kr) * D;
     uint16_t* vrow = dv + (kvrow0 + kr) * D;
     if (kvalid) {
@@ -762,10 +833,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void bwd_dkdv_kernel(
         const double* cvr = dvc + kb * D;
         const float inv_size = 1.f / (float)kvsize;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DH; ++dt)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const int d0 = 32 * dt + 8 * jj + 4 * hh;
+                const int d0 = 32 * (DH * role + dt) + 8 * jj + 4 * hh;
                 float a[4], b[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -777,11 +848,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void bwd_dkdv_kernel(
             }
     } else if (P.packed) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DH; ++dt)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                *reinterpret_cast<uint2*>(krow + 32 * dt + 8 * jj + 4 * hh) = make_uint2(0, 0);
-                *reinterpret_cast<uint2*>(vrow + 32 * dt + 8 * jj + 4 * hh) = make_uint2(0, 0);
+                const int d0 = 32 * (DH * role + dt) + 8 * jj + 4 * hh;
+                *reinterpret_cast<uint2*>(krow + d0) = make_uint2(0, 0);
+                *reinterpret_cast<uint2*>(vrow + d0) = make_uint2(0, 0);
             }
     }
 }
@@ -841,7 +913,7 @@ hipError_t launch_all(const DevProblem& P, const BwdArgs& A, hipStream_t st) {
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)nq_all), dim3(kAttnThreads), 0, st, P, A.q, A.k, A.v, A.dout,
                        A.rs, A.idx, A.num, A.dqc, A.dq, c_log2, (float)scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)nkv_all), dim3(kAttnThreads), 0, st, P, A.q, A.k, A.v,
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)nkv_all), dim3(kDkdvThreads), 0, st, P, A.q, A.k, A.v,
                        A.dout, A.rs, A.k2q, A.k2q_num, maxq, A.dkc, A.dvc, A.dk, A.dv, c_log2, (float)scale);
     return hipGetLastError();
 }
