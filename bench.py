@@ -69,8 +69,11 @@ def copy_calibration():
 
 
 def kernel_hash(path=SPARSE_SRC) -> str:
+    """Hash of the sparse kernel's source and the headers it includes."""
     h = hashlib.sha256()
-    for p in (path, os.path.join(os.path.dirname(path), "attn_layout.hpp")):
+    d = os.path.dirname(path)
+    for p in (path, os.path.join(d, "attn_common.hpp"), os.path.join(d, "attn_layout.hpp"),
+              os.path.join(d, "vsa_internal.hpp")):
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

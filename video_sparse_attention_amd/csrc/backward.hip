@@ -38,6 +38,15 @@ using namespace attn;
 
 constexpr int kThreads = 256;      // block-level kernels
 constexpr int kAttnThreads = 128;  // MFMA kernels: 2 waves, 32 columns each
+// The block lists are walked from a rotated start: work item i begins at
+// entry (i mod kSweep) n / kSweep of its n entries and wraps around, kSweep
+// being about the number of workgroups resident on one XCD (32 CUs times the
+// workgroups per CU).  The lists are ascending, so workgroups running
+// together read nearby entries at the same time and share them in L2,
+// instead of all starting at the front while earlier ones are deep into
+// theirs.  Only the order of the (float32) accumulations changes.
+constexpr int kSweepDq = 128;
+constexpr int kSweepDkdv = 96;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -445,9 +454,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void bwd_dq_kernel(
     const_int* bs_kv = (const_int*)(P.packed ? uniform_ptr(P.bs_kv + sv.kvblk0) : nullptr);
     const int rebase = __builtin_amdgcn_readfirstlane(sv.idx_rebase);
     const int nkv = __builtin_amdgcn_readfirstlane(sv.nkv);
+    const int t0 = n > 0 ? ((i % kSweepDq) * n) / kSweepDq : 0;
     auto next_valid = [&](int& t) -> int {
         for (; t < n; ++t) {
-            const int j = list[t] - rebase;
+            int pos = t0 + t;
+            if (pos >= n) pos -= n;
+            const int j = list[pos] - rebase;
             if (j >= 0 && j < nkv) return j;
         }
         return -1;
@@ -679,7 +691,12 @@ __global__ __launch_bounds__(kDkdvThreads, 3) void bwd_dkdv_kernel(
     auto q_size = [&](int i) -> int {
         return P.packed ? clampi(bs_q[i], 1, kBlock) : min(kBlock, P.Sq - kBlock * i);
     };
-    auto entry = [&](int x) -> int { return clampi(list[x], 0, nq - 1); };
+    const int x0 = m > 0 ? ((j % kSweepDkdv) * m) / kSweepDkdv : 0;
+    auto entry = [&](int x) -> int {
+        int pos = x0 + x;
+        if (pos >= m) pos -= m;
+        return clampi(list[pos], 0, nq - 1);
+    };
     constexpr uint32_t kTileBytes = 2u * kHalf * D;
     constexpr uint32_t kStatBytes = 4u * 2 * kHalf;
     const uint32_t off = (uint32_t)lane_src_offset4<CH, kSwzDual>(wave, lane);
