@@ -13,7 +13,8 @@ without the fused combine is timed for comparison.
 
 Prints one JSON line.  ``value`` is effective TFLOP/s of the whole step with
 the pages' benchmark convention 4*B*H*nQ*k*64*64*D (padded blocks counted as
-full).  ``roofline`` is for the dominant kernel (the sparse attention, MFMA
+full; with ``--block-size 128`` or ``256`` the same count over the 64-token
+sub-blocks of the selected VSA blocks).  ``roofline`` is for the dominant kernel (the sparse attention, MFMA
 bound).  ``cpu_baseline`` times the fp64 oracle on this host's cores on a
 bounded sample of the same workload (whole heads).
 """
@@ -22,6 +23,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -46,6 +48,8 @@ def parse():
                     help="large (the default line), varlen_many, video: the large shape as an "
                          "11 x 32 x 44 latent in 4 x 4 x 4 tiles, gathered from and scattered to "
                          "raster order, or train: the large shape's forward plus backward")
+    ap.add_argument("--block-size", type=int, default=64, choices=[64, 128, 256],
+                    help="VSA block size for the large workload (128 / 256: top-k about 20%% of the blocks)")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0,
                     help="wall-time budget of the oracle sample (whole heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -92,7 +96,23 @@ def measured_traffic(launch_algo_bytes: float):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, budget_s: float):
+def pair_count(idx, num, Sq: int, Skv: int, block: int) -> int:
+    """(64-token query block, 64-token KV block) pairs the sparse attention
+    visits: every selected VSA block of ``block`` tokens stands for its
+    64-token sub-blocks, for each 64-token query block of the VSA query block
+    (for block = 64 this is B*H*nQ*k)."""
+    import numpy as np
+    r = block // 64
+    idx, num = np.asarray(idx, dtype=np.int64), np.asarray(num, dtype=np.int64)
+    nq64, nkv64 = -(-Sq // 64), -(-Skv // 64)
+    nqb = idx.shape[-2]
+    qsub = np.minimum(r, nq64 - r * np.arange(nqb))  # 64-token query blocks per VSA block
+    used = np.arange(idx.shape[-1]) < num[..., None]
+    ksub = np.clip(nkv64 - r * idx, 0, r) * used
+    return int((ksub.sum(axis=-1) * qsub).sum())
+
+
+def cpu_baseline(inp, budget_s: float, block: int = 64):
     """Time the fp64 oracle on whole heads of the workload until the budget is used."""
     import numpy as np
     import torch
@@ -105,21 +125,19 @@ def cpu_baseline(inp, budget_s: float):
         threads = len(os.sched_getaffinity(0))
     to64 = lambda t: t.to(torch.float64).numpy()
     B, H, Sq, Skv, D = inp.shape
-    nq = -(-Sq // 64)
-    nkv = -(-Skv // 64)
-    kk = min(inp.topk, nkv)
-    done, t_total = 0, 0.0
+    done, t_total, pairs = 0, 0.0, 0
     for h in range(H):
         sl = slice(h, h + 1)
         q, k, v = to64(inp.q[:, sl]), to64(inp.k[:, sl]), to64(inp.v[:, sl])
         g = None if inp.gate is None else to64(inp.gate[:, sl])
         t0 = time.perf_counter()
-        oracle.vsa_forward(q, k, v, inp.topk, g)
+        r = oracle.vsa_forward(q, k, v, inp.topk, g, block=block)
         t_total += time.perf_counter() - t0
+        pairs += pair_count(r["q2k_idx"], r["q2k_num"], Sq, Skv, block)
         done += 1
         if t_total >= budget_s:
             break
-    flops = 4.0 * B * done * nq * kk * 64 * 64 * D
+    flops = 4.0 * pairs * 64 * 64 * D
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{done} of {H} heads of the same workload, whole forward per head "
@@ -299,18 +317,24 @@ def main():
         train_bench(args, torch, synth, vsa)
         return
     inp = synth.workload(args.workload)
+    block = args.block_size
+    if block != 64 and args.workload != "large":
+        print("--block-size applies to the large workload only", file=sys.stderr)
+        sys.exit(2)
 
+    flops = None
     if isinstance(inp, synth.DenseInputs):
         B, H, Sq, Skv, D = inp.shape
-        prob = vsa.dense_problem(B, H, Sq, Skv, D, inp.topk)
-        nq = -(-Sq // 64)
-        kk = min(inp.topk, -(-Skv // 64))
-        flops = 4.0 * B * H * nq * kk * 64 * 64 * D
+        nqb = -(-Sq // block)
+        if block != 64:
+            inp.topk = math.ceil(0.20 * -(-Skv // block))  # about 20 % of the VSA blocks
+        prob = vsa.dense_problem(B, H, Sq, Skv, D, inp.topk, block)
         q_tokens = B * H * Sq
-        n_qblocks = B * H * nq
-        cfg = {"workload": f"large video-DiT shape B={B} H={H} D={D} S={Sq} (242 blocks of 64), "
+        n_qblocks = B * H * nqb
+        n_kvblocks = B * H * -(-Skv // block)
+        cfg = {"workload": f"large video-DiT shape B={B} H={H} D={D} S={Sq} ({nqb} blocks of {block}), "
                            f"top-{inp.topk}, per-token-per-head sigmoid gate",
-               "batch": B, "heads": H, "head_dim": D, "seq_len": Sq, "block": 64,
+               "batch": B, "heads": H, "head_dim": D, "seq_len": Sq, "block": block,
                "topk": inp.topk, "gate": "token"}
     else:
         meta = vsa.vsa_build_metadata(inp.seqlens_q, inp.seqlens_kv, inp.topk, device=dev)
@@ -321,6 +345,7 @@ def main():
         flops = 4.0 * H * sum(n * k for n, k in zip(nqs, tk)) * 64 * 64 * D
         q_tokens = H * sum(inp.seqlens_q)
         n_qblocks = H * sum(nqs)
+        n_kvblocks = H * sum(-(-s // 64) for s in inp.seqlens_kv)
         cfg = {"workload": f"{len(nqs)} packed sequences, Q blocks {nqs}, KV = Q + 8 blocks, "
                            f"H={H} D={D}, top-k {tk}, gated",
                "heads": H, "head_dim": D, "block": 64, "topk": tk, "gate": "token"}
@@ -344,6 +369,8 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if flops is None:  # effective flops of the routing the kernels produce (identical every step)
+        flops = 4.0 * pair_count(idx.cpu().numpy(), num.cpu().numpy(), Sq, Skv, block) * 64 * 64 * D
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -387,10 +414,9 @@ def main():
     # algorithmic bytes: the combine reads and writes out once, reads the gate and out_c
     gate_bytes = 0 if gate is None else 2 * q_tokens
     comb_bytes = 2 * 2 * q_tokens * D + gate_bytes + 4 * n_qblocks * D
-    kv_tokens = k.numel() // D
-    coarse_bytes = 2 * (q.numel() + 2 * k.numel()) + 8 * D * (n_qblocks + 2 * (kv_tokens // 64))
+    coarse_bytes = 2 * (q.numel() + 2 * k.numel()) + 8 * D * (n_qblocks + 2 * n_kvblocks)
     sparse_tf = flops / (avg["sparse"] * 1e-3) / 1e12
-    traffic = measured_traffic(None)
+    traffic = measured_traffic(None) if (args.workload == "large" and block == 64) else None
     kname = "sparse_attn_kernel<128, 1>" if gate is not None else "sparse_attn_kernel<128, 0>"
 
     res = {
@@ -432,7 +458,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline and isinstance(inp, synth.DenseInputs):
-        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget_s)
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget_s, block)
     print(json.dumps(res), flush=True)
 
 

@@ -26,24 +26,34 @@
  *   - all arguments are validated on the host before anything is launched; a
  *     negative return value is an error code (VSA_ERR_*), nothing has been
  *     launched in that case, and vsa_last_error() describes it;
- *   - block_size must be 64 and head_dim 64 or 128.
+ *   - head_dim is 64 or 128; block_size (the VSA block: pooling, routing and
+ *     the KV granularity of the sparse attention) is 64, or 128 / 256 for the
+ *     DENSE and BSHD layouts ("[chore] release fastvideo-kernel 0.3.0",
+ *     Block-sparse / VSA attention improvements: 256-token KV blocks;
+ *     "[perf] avoid full-sequence materialization ...", Change: the
+ *     64/128/256 dispatch).  The training forward and the backward take
+ *     64-token blocks in the DENSE or PACKED layout.
  *
  * Layouts:
  *   DENSE   q [B, H, Sq, D], k/v [B, H, Skv, D], out [B, H, Sq, D], each batch
  *           item one sequence; block i of a sequence holds tokens
- *           [64 i, min(64 i + 64, S)).
+ *           [bs i, min(bs i + bs, S)) for block_size bs.
+ *   BSHD    the same with q [B, Sq, H, D], k/v [B, Skv, H, D], out [B, Sq, H, D]
+ *           ("[chore] release fastvideo-kernel 0.3.0", the BSHD-native entry
+ *           that avoids layout round trips); a token gate defaults to
+ *           [B, Sq, H], a full gate to [B, Sq, H, D].
  *   PACKED  block-padded packing of num_seqs sequences: q [H, 64*Nq, D],
  *           k/v [H, 64*Nkv, D] with Nq/Nkv the total block counts; sequence s
  *           owns global query blocks [cu_blocks_q[s], cu_blocks_q[s+1]) and KV
  *           blocks [cu_blocks_kv[s], cu_blocks_kv[s+1]); global block g starts
  *           at slot 64 g and its first block_sizes_*[g] slots are valid tokens
  *           (the rest is padding, never read).
- *   Block-resolution tensors: out_c is float32 [B, H, nQ, D] (DENSE) or
- *   [H, Nq, D] (PACKED); q2k_num is int32 [B, H, nQ] or [H, Nq]; q2k_idx is
- *   int32 [B, H, nQ, kk] with kk = min(topk, nKV) and per-sequence KV block
- *   numbers (DENSE), or [H, Nq, max_topk] with GLOBAL KV block numbers and -1
- *   after the first q2k_num entries (PACKED).  Selected indices are stored in
- *   ascending order.
+ *   Block-resolution tensors: out_c is float32 [B, H, nQ, D] (DENSE, BSHD;
+ *   nQ = ceil(Sq / block_size)) or [H, Nq, D] (PACKED); q2k_num is int32
+ *   [B, H, nQ] or [H, Nq]; q2k_idx is int32 [B, H, nQ, kk] with kk = min(topk,
+ *   nKV) and per-sequence KV block numbers (DENSE, BSHD), or [H, Nq, max_topk]
+ *   with GLOBAL KV block numbers and -1 after the first q2k_num entries
+ *   (PACKED).  Selected indices are stored in ascending order.
  */
 #ifndef VSA_H
 #define VSA_H
@@ -63,7 +73,7 @@ typedef void *vsa_stream;  /* hipStream_t */
 /* status codes */
 #define VSA_OK 0
 #define VSA_ERR_NULL (-1)        /* a required pointer is NULL */
-#define VSA_ERR_UNSUPPORTED (-2) /* block_size != 64, head_dim not 64/128, or a size over a limit */
+#define VSA_ERR_UNSUPPORTED (-2) /* block_size, layout or head_dim not supported, or a size over a limit */
 #define VSA_ERR_TOPK (-3)        /* topk < 1 */
 #define VSA_ERR_SHAPE (-4)       /* empty batch, zero-length sequence, inconsistent block counts */
 #define VSA_ERR_GATE (-5)        /* bad gate mode or strides */
@@ -75,6 +85,7 @@ typedef void *vsa_stream;  /* hipStream_t */
 /* layouts */
 #define VSA_LAYOUT_DENSE 0
 #define VSA_LAYOUT_PACKED 1
+#define VSA_LAYOUT_BSHD 2
 
 /* gate modes: none; one value per (token, head) broadcast over D; full */
 #define VSA_GATE_NONE 0
@@ -82,8 +93,8 @@ typedef void *vsa_stream;  /* hipStream_t */
 #define VSA_GATE_FULL 2
 
 /*
- * A problem description shared by the stage entry points.  For DENSE fill
- * batch, seqlen_q, seqlen_kv and topk; the PACKED fields are ignored.  For
+ * A problem description shared by the stage entry points.  For DENSE and BSHD
+ * fill batch, seqlen_q, seqlen_kv and topk; the PACKED fields are ignored.  For
  * PACKED fill the num_seqs..topk_per_seq block (device arrays as produced by
  * vsa_build_metadata and copied to the device); batch/seqlen/topk are
  * ignored.  The kernels never read outside the arrays whose lengths are given
@@ -92,10 +103,10 @@ typedef void *vsa_stream;  /* hipStream_t */
  * outside a query block's own sequence are skipped.
  */
 typedef struct vsa_problem {
-    int32_t layout;     /* VSA_LAYOUT_DENSE or VSA_LAYOUT_PACKED */
+    int32_t layout;     /* VSA_LAYOUT_DENSE, VSA_LAYOUT_BSHD or VSA_LAYOUT_PACKED */
     int32_t heads;      /* H >= 1 */
     int32_t head_dim;   /* D: 64 or 128 */
-    int32_t block_size; /* must be 64 */
+    int32_t block_size; /* 64; 128 or 256 for DENSE and BSHD */
     /* DENSE */
     int32_t batch;     /* B >= 1 */
     int32_t seqlen_q;  /* Sq >= 1 */
@@ -255,6 +266,19 @@ int vsa_forward(const vsa_bf16 *q, const vsa_bf16 *k, const vsa_bf16 *v, const v
                 int32_t *q2k_num, float *out_c, int32_t batch, int32_t heads, int32_t seqlen_q,
                 int32_t seqlen_kv, int32_t head_dim, int32_t block_size, int32_t topk,
                 void *workspace, size_t workspace_bytes, vsa_stream stream);
+
+/*
+ * vsa_forward_bshd - vsa_forward for [B, S, H, D] tensors (BSHD layout):
+ * q [B,Sq,H,D], k/v [B,Skv,H,D], out [B,Sq,H,D]; everything else, including
+ * block_size 64, 128 or 256, as vsa_forward.  ("[chore] release
+ * fastvideo-kernel 0.3.0", Block-sparse / VSA attention improvements: the
+ * BSHD-native video_sparse_attn_bshd() entry point.)
+ */
+int vsa_forward_bshd(const vsa_bf16 *q, const vsa_bf16 *k, const vsa_bf16 *v, const vsa_bf16 *gate,
+                     int32_t gate_mode, const int64_t *gate_strides, vsa_bf16 *out, int32_t *q2k_idx,
+                     int32_t *q2k_num, float *out_c, int32_t batch, int32_t heads, int32_t seqlen_q,
+                     int32_t seqlen_kv, int32_t head_dim, int32_t block_size, int32_t topk,
+                     void *workspace, size_t workspace_bytes, vsa_stream stream);
 
 /*
  * vsa_forward_varlen - the whole PACKED forward in one launch per stage over

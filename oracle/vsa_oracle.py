@@ -183,13 +183,18 @@ def _f64(x) -> np.ndarray:
 
 
 def vsa_forward(q, k, v, topk: int, gate=None,
-                blocks: Optional[Sequence[Tuple[int, int, int]]] = None) -> Dict[str, np.ndarray]:
+                blocks: Optional[Sequence[Tuple[int, int, int]]] = None,
+                block: int = BLOCK) -> Dict[str, np.ndarray]:
     """VSA forward over a dense ``[B, H, S, D]`` batch (each batch item is one sequence).
 
     ``gate`` is ``None``, ``[B, H, Sq]`` or ``[B, H, Sq, D]``.  With ``blocks``
     (a list of ``(b, h, i)``) the sparse/combine stages run only for those
     query blocks and the other output rows are NaN; the coarse stage and the
-    routing always run for every block.
+    routing always run for every block.  ``block`` is the VSA block size: 64,
+    or 128 / 256 ("[chore] release fastvideo-kernel 0.3.0", Block-sparse / VSA
+    attention improvements: 256-token KV blocks; "[perf] avoid full-sequence
+    materialization ...", Change: the 64/128/256 dispatch) - pooling, routing
+    and the sparse attention all work on blocks of that many tokens.
 
     Returns ``out``, ``out_s`` (``[B,H,Sq,D]``), ``out_c`` (``[B,H,nQ,D]``),
     ``q2k_idx`` (``[B,H,nQ,min(topk,nKV)]``, int32, ascending), ``q2k_num``
@@ -199,7 +204,7 @@ def vsa_forward(q, k, v, topk: int, gate=None,
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, Sq, D = q.shape
     Skv = k.shape[2]
-    qs, ks = block_sizes(Sq), block_sizes(Skv)
+    qs, ks = block_sizes(Sq, block), block_sizes(Skv, block)
     nq, nkv = len(qs), len(ks)
     kk = min(topk, nkv)
     out_c = np.empty((B, H, nq, D))
@@ -209,7 +214,7 @@ def vsa_forward(q, k, v, topk: int, gate=None,
     maxdot = np.empty((B, H))
     for b in range(B):
         for h in range(H):
-            qc, kc, vc = pool(q[b, h], qs), pool(k[b, h], ks), pool(v[b, h], ks)
+            qc, kc, vc = pool(q[b, h], qs, block), pool(k[b, h], ks, block), pool(v[b, h], ks, block)
             dots, out_c[b, h] = coarse(qc, kc, vc)
             maxdot[b, h] = np.abs(dots).max()
             for i in range(nq):
@@ -222,8 +227,8 @@ def vsa_forward(q, k, v, topk: int, gate=None,
     out_s = np.full((B, H, Sq, D), fill)
     out = np.full((B, H, Sq, D), fill)
     for b, h, i in want:
-        lo, n = BLOCK * i, qs[i]
-        rows = sparse_block(q[b, h, lo:lo + n], k[b, h], v[b, h], ks, idx[b, h, i])
+        lo, n = block * i, qs[i]
+        rows = sparse_block(q[b, h, lo:lo + n], k[b, h], v[b, h], ks, idx[b, h, i], block)
         out_s[b, h, lo:lo + n] = rows
         g = None if gate is None else gate[b, h, lo:lo + n]
         out[b, h, lo:lo + n] = combine(out_c[b, h, i], rows, g)

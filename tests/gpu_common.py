@@ -20,14 +20,28 @@ def note(msg: str) -> None:
     sys.stdout.flush()
 
 
-def run_dense_stages(inp, dev=DEV, idx_override=None):
+def to_bshd(t):
+    """[B, H, S(, D)] -> contiguous [B, S, H(, D)] (None stays None)."""
+    if t is None:
+        return None
+    return t.transpose(1, 2).contiguous()
+
+
+def from_bshd(t):
+    return t.transpose(1, 2).contiguous()
+
+
+def run_dense_stages(inp, dev=DEV, idx_override=None, block_size=64, bshd=False):
     """Stage calls on a dense workload: returns dict with out, out_s, out_c,
     q2k_idx, q2k_num (CPU tensors).  With ``idx_override`` (numpy idx, num) the
-    sparse stage runs on those indices instead of the GPU's own."""
+    sparse stage runs on those indices instead of the GPU's own.  With
+    ``bshd`` the inputs are handed over as [B, S, H, D] tensors (vsa problem
+    of layout BSHD) and the token outputs are returned as [B, H, S, D]."""
     B, H, Sq, Skv, D = inp.shape
-    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
-    gate = None if inp.gate is None else inp.gate.to(dev)
-    prob = vsa.dense_problem(B, H, Sq, Skv, D, inp.topk)
+    conv = to_bshd if bshd else (lambda t: t)
+    q, k, v = (conv(t).to(dev) for t in (inp.q, inp.k, inp.v))
+    gate = None if inp.gate is None else conv(inp.gate).to(dev)
+    prob = vsa.dense_problem(B, H, Sq, Skv, D, inp.topk, block_size, bshd)
     cs, isz, ns = vsa.block_shapes(prob)
     out_c = torch.empty(cs, dtype=torch.float32, device=dev)
     idx = torch.empty(isz, dtype=torch.int32, device=dev)
@@ -46,8 +60,9 @@ def run_dense_stages(inp, dev=DEV, idx_override=None):
     out_f = torch.empty_like(q)
     vsa.vsa_sparse_attn_combine(prob, q, k, v, sidx, snum, out_c, gate, out_f)
     torch.cuda.synchronize()
-    return dict(out=out.cpu(), out_s=out_s.cpu(), out_c=out_c.cpu(), q2k_idx=idx.cpu(),
-                q2k_num=num.cpu(), out_fused=out_f.cpu())
+    back = from_bshd if bshd else (lambda t: t)
+    return dict(out=back(out.cpu()), out_s=back(out_s.cpu()), out_c=out_c.cpu(), q2k_idx=idx.cpu(),
+                q2k_num=num.cpu(), out_fused=back(out_f.cpu()))
 
 
 def run_varlen_stages(inp, dev=DEV, idx_override=None):
@@ -78,9 +93,9 @@ def run_varlen_stages(inp, dev=DEV, idx_override=None):
                 q2k_num=num.cpu(), meta=meta, out_fused=out_f.cpu())
 
 
-def oracle_dense(inp, blocks=None):
+def oracle_dense(inp, blocks=None, block=64):
     g = None if inp.gate is None else f64(inp.gate)
-    return oracle.vsa_forward(f64(inp.q), f64(inp.k), f64(inp.v), inp.topk, g, blocks=blocks)
+    return oracle.vsa_forward(f64(inp.q), f64(inp.k), f64(inp.v), inp.topk, g, blocks=blocks, block=block)
 
 
 def oracle_varlen(inp, blocks=None):

@@ -547,6 +547,52 @@ def pin_lse_reproduces_sparse_output(seed=20):
                 assert np.allclose(p @ v[b, h, toks], ref["out_s"][b, h, rows], rtol=1e-11, atol=1e-12)
 
 
+def pin_large_blocks_dense_equivalence(seed=21):
+    """VSA blocks of 128 and 256 tokens with top-k = every block: out_s is
+    textbook attention over the whole sequence and out_c attention over the
+    means of 128 / 256 consecutive tokens (torch's avg_pool1d)."""
+    rng = _rng(seed)
+    for block, (B, H, S, D) in ((128, (1, 2, 512, 32)), (256, (2, 1, 512, 16))):
+        q, k, v = (rng.standard_normal((B, H, S, D)) for _ in range(3))
+        r = O.vsa_forward(q, k, v, topk=10 ** 6, block=block)
+        assert r["q2k_idx"].shape == (B, H, S // block, S // block)
+        assert np.allclose(r["out_s"], _sdpa(q, k, v), atol=1e-12, rtol=0)
+
+        def ap(x):
+            t = torch.from_numpy(x).reshape(B * H, S, D).transpose(1, 2)
+            return torch.nn.functional.avg_pool1d(t, block).transpose(1, 2).reshape(B, H, -1, D).numpy()
+        assert np.allclose(r["out_c"], _sdpa(ap(q), ap(k), ap(v)), atol=1e-12, rtol=0)
+
+
+def pin_large_blocks_by_duplication(seed=22):
+    """A 128-token VSA block made of two copies of the same 64 tokens has the
+    mean of those 64 tokens, and softmax over doubled keys equals softmax over
+    the keys once: VSA with 128-token blocks on such a sequence equals VSA with
+    64-token blocks on the undoubled one, token for token (routing, coarse
+    output, sparse output).  The ragged last block of 20 tokens is doubled too
+    (a 40-token last VSA block): every key then appears exactly twice, so the
+    softmax weights are those of the undoubled sequence."""
+    rng = _rng(seed)
+    B, H, L, D = 1, 2, 64 * 5 + 20, 16
+    base = [rng.standard_normal((B, H, L, D)) for _ in range(3)]
+    sizes = O.block_sizes(L, 64)
+
+    def double(x):  # every 64-token block (and the ragged one) twice in a row
+        parts = []
+        for i, n in enumerate(sizes):
+            blk = x[:, :, 64 * i: 64 * i + n]
+            parts += [blk, blk]
+        return np.concatenate(parts, axis=2)
+    q2, k2, v2 = (double(x) for x in base)
+    for topk in (2, 3):
+        small = O.vsa_forward(*base, topk=topk, block=64)
+        big = O.vsa_forward(q2, k2, v2, topk=topk, block=128)
+        assert np.array_equal(big["q2k_idx"], small["q2k_idx"])
+        assert np.allclose(big["out_c"], small["out_c"], rtol=1e-12, atol=1e-13)
+        out_small = double(small["out"])
+        assert np.allclose(big["out"], out_small, rtol=1e-11, atol=1e-12)
+
+
 ALL_PINS = [
     pin_block_sizes, pin_pool_partial_block, pin_two_token_closed_form,
     pin_coarse_and_routing_closed_form, pin_combine_closed_form, pin_topk_bruteforce,
@@ -558,4 +604,5 @@ ALL_PINS = [
     pin_video_forward_1d_equals_dense, pin_video_forward_tile_equivariance,
     pin_backward_forward_matches_oracle, pin_backward_gradcheck, pin_backward_dense_equivalence,
     pin_lse_dense_equivalence, pin_lse_reproduces_sparse_output,
+    pin_large_blocks_dense_equivalence, pin_large_blocks_by_duplication,
 ]

@@ -124,12 +124,23 @@ def dense(B=1, H=2, Sq=1000, Skv=1000, D=128, topk=3, bs=64):
 FAKE = 0x7f0000000000  # 256-aligned, never dereferenced
 
 
+def bshd(B=1, H=2, Sq=1000, Skv=1000, D=128, topk=3, bs=64):
+    return VsaProblem(layout=2, heads=H, head_dim=D, block_size=bs, batch=B, seqlen_q=Sq,
+                      seqlen_kv=Skv, topk=topk)
+
+
 def packed(num_seqs=2, nq=5, nkv=6, mq=3, mkv=4, mk=2, H=2, D=64, ptrs=True):
     p = [FAKE + 4096 * i for i in range(5)] if ptrs else [None] * 5
     return VsaProblem(layout=1, heads=H, head_dim=D, block_size=64, num_seqs=num_seqs,
                       total_q_blocks=nq, total_kv_blocks=nkv, max_q_blocks=mq, max_kv_blocks=mkv,
                       max_topk=mk, cu_blocks_q=p[0], cu_blocks_kv=p[1], block_sizes_q=p[2],
                       block_sizes_kv=p[3], topk_per_seq=p[4])
+
+
+def packed_bs(bs):
+    p = packed()
+    p.block_size = bs
+    return p
 
 
 def test_workspace_is_block_resolution(lib):
@@ -193,7 +204,20 @@ E = _abi
     (lambda L: coarse(L, dense(), wsb=100), E.VSA_ERR_WORKSPACE),
     (lambda L: coarse(L, dense(), ws=ctypes.c_void_p(FAKE + 64)), E.VSA_ERR_ALIGN),
     (lambda L: coarse(L, dense(), k=ctypes.c_void_p(FAKE + 2)), E.VSA_ERR_ALIGN),
-    (lambda L: coarse(L, dense(bs=128)), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: coarse(L, dense(bs=96)), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: coarse(L, dense(bs=512)), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: coarse(L, packed_bs(128)), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: coarse(L, dense(bs=128, Skv=128 * 4097)), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: train_fwd(L, dense(bs=128)), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: train_fwd(L, bshd()), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: bwd(L, dense(bs=256)), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: bwd(L, bshd()), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: L.vsa_forward_bshd(A, B_, C_, None, 0, None, O_, None, None, None, 1, 2, 1000, 1000, 128, 32, 3, W_,
+                                  1 << 40, None), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: L.vsa_forward_bshd(A, B_, C_, None, 0, None, A, None, None, None, 1, 2, 1000, 1000, 128, 128, 3, W_,
+                                  1 << 40, None), E.VSA_ERR_ALIAS),
+    (lambda L: L.vsa_forward_bshd(A, B_, C_, G_, 1, None, O_, None, None, None, 1, 2, 1000, 1000, 128, 256, 3, W_,
+                                  10, None), E.VSA_ERR_WORKSPACE),
     (lambda L: coarse(L, dense(D=96)), E.VSA_ERR_UNSUPPORTED),
     (lambda L: coarse(L, dense(topk=0)), E.VSA_ERR_TOPK),
     (lambda L: coarse(L, dense(B=0)), E.VSA_ERR_SHAPE),

@@ -1,0 +1,117 @@
+"""GPU parity of the 128- and 256-token VSA blocks and of the [B, S, H, D]
+(BSHD) entry against the fp64 oracle (which takes the block size as a
+parameter and works on [B, H, S, D]; BSHD inputs are the same tensors
+transposed), on seeded inputs with ragged tails, plus the full-size large
+shape at both block sizes on sampled query blocks."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import video_sparse_attention_amd as vsa
+from tests import gpu_common as G
+from tests import numerics as N
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(B, H, Sq, Skv, D, topk, gate, seed):
+    inp = synth.dense_inputs(B, H, Sq, D, topk, seed=seed, gated=gate == "token", S_kv=Skv)
+    if gate == "full":
+        inp.gate = synth.full_gate((B, H, Sq, D), seed + 1)
+    return inp
+
+
+def _check_all(inp, gpu, ref):
+    G.assert_tie_free(ref)
+    G.assert_indices_equal(gpu["q2k_idx"], gpu["q2k_num"], ref)
+    N.check_out_c(N.f64(gpu["out_c"]), ref["out_c"])
+    rel = N.check_sparse(N.f64(gpu["out_s"]), ref["out_s"])
+    mx, mean = N.check_out(N.f64(gpu["out"]), ref["out"])
+    N.check_out(N.f64(gpu["out_fused"]), ref["out"], "out (fused combine)")
+    N.check_fused(N.f64(gpu["out_fused"]), N.f64(gpu["out"]), N.f64(gpu["out_s"]))
+    G.note(f"  out max-abs {mx:.2e} mean-abs {mean:.2e}; sparse rel-rms {rel:.2e}")
+
+
+@pytest.mark.parametrize("block,B,H,Sq,Skv,D,topk,gate", [
+    (128, 1, 2, 128 * 5 + 37, 128 * 5 + 37, 128, 2, "token"),  # ragged 37-token tail (one 64-sub-block)
+    (128, 2, 2, 700, 900, 64, 3, None),                        # Sq != Skv, tails of 60 and 4 tokens
+    (128, 1, 1, 128 * 6 + 64, 128 * 6 + 64, 128, 3, "full"),   # last VSA block = one full 64-sub-block
+    (256, 1, 3, 256 * 4 + 100, 256 * 4 + 100, 128, 2, "full"), # 100-token tail: sub-blocks 64 + 36
+    (256, 1, 1, 256 * 3, 256 * 6 - 7, 64, 100, "token"),       # top-k above the VSA block count
+    (256, 2, 1, 256 * 5 + 200, 256 * 5 + 200, 64, 1, None),    # top-1, 200-token tail (4 sub-blocks, last 8)
+    (128, 1, 2, 1, 1, 128, 1, None),                           # single token
+])
+def test_large_vsa_blocks(block, B, H, Sq, Skv, D, topk, gate):
+    inp = _inputs(B, H, Sq, Skv, D, topk, gate, seed=3000 + block + Sq + Skv + D)
+    G.note(f"case block={block} B={B} H={H} Sq={Sq} Skv={Skv} D={D} topk={topk} gate={gate}")
+    ref = G.oracle_dense(inp, block=block)
+    gpu = G.run_dense_stages(inp, block_size=block)
+    _check_all(inp, gpu, ref)
+    # the one-call forward launches the same kernels: identical bits
+    q, k, v = (t.to(G.DEV) for t in (inp.q, inp.k, inp.v))
+    g = None if inp.gate is None else inp.gate.to(G.DEV)
+    out, oc, idx, num = vsa.vsa_forward(q, k, v, topk, g, block_size=block, return_aux=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), gpu["out_fused"])
+    assert torch.equal(oc.cpu(), gpu["out_c"])
+    assert torch.equal(idx.cpu(), gpu["q2k_idx"])
+    assert torch.equal(num.cpu(), gpu["q2k_num"])
+
+
+@pytest.mark.parametrize("block", [64, 128, 256])
+@pytest.mark.parametrize("gate", ["token", "full", None])
+def test_bshd_matches_dense_bits(block, gate):
+    """BSHD tensors are the dense ones with strided rows: the same kernels in
+    the same order give the same bits, and both match the oracle."""
+    B, H, Sq, Skv, D = 2, 3, 64 * 9 + 17, 64 * 11 + 50, 128
+    inp = _inputs(B, H, Sq, Skv, D, 3, gate, seed=4000 + block)
+    G.note(f"case bshd block={block} gate={gate} B={B} H={H} Sq={Sq} Skv={Skv}")
+    ref = G.oracle_dense(inp, block=block)
+    dense = G.run_dense_stages(inp, block_size=block)
+    bshd = G.run_dense_stages(inp, block_size=block, bshd=True)
+    _check_all(inp, bshd, ref)
+    for key in ("out", "out_s", "out_c", "q2k_idx", "q2k_num", "out_fused"):
+        assert torch.equal(bshd[key], dense[key]), key
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bshd_forward_entry(D):
+    """vsa_forward_bshd (one call) on [B, S, H, D], with the gate given as a
+    [B, S, H] tensor and as a transposed view of a [B, H, S] one."""
+    B, H, Sq, Skv = 1, 4, 64 * 7 + 9, 64 * 7 + 9
+    inp = _inputs(B, H, Sq, Skv, D, 2, "token", seed=4100 + D)
+    G.note(f"case bshd forward D={D}")
+    ref = G.oracle_dense(inp)
+    G.assert_tie_free(ref)
+    q, k, v = (G.to_bshd(t).to(G.DEV) for t in (inp.q, inp.k, inp.v))
+    g_bsh = G.to_bshd(inp.gate).to(G.DEV)
+    g_view = inp.gate.to(G.DEV).transpose(1, 2)  # [B, S, H] view of [B, H, S] storage
+    assert not g_view.is_contiguous()
+    outs = []
+    for g in (g_bsh, g_view):
+        out, oc, idx, num = vsa.vsa_forward(q, k, v, 2, g, bshd=True, return_aux=True)
+        torch.cuda.synchronize()
+        G.assert_indices_equal(idx.cpu(), num.cpu(), ref)
+        N.check_out_c(N.f64(oc), ref["out_c"])
+        N.check_out(N.f64(G.from_bshd(out.cpu())), ref["out"])
+        outs.append(out.cpu())
+    assert torch.equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("block,topk", [(128, 25), (256, 13)])
+def test_large_shape_large_blocks(block, topk):
+    """The large video-DiT shape (B=1, H=56, S=15488, D=128, gated) with VSA
+    blocks of 128 (121 blocks) and 256 tokens (61 blocks, the last 128 tokens),
+    top-k about 20 % of the blocks: every index and coarse row, sampled token
+    outputs."""
+    inp = synth.dense_inputs(1, 56, 15488, 128, topk, seed=5000 + block, gated=True)
+    B, H, Sq, Skv, D = inp.shape
+    nq = -(-Sq // block)
+    rng = np.random.default_rng(block)
+    picks = rng.choice(H * nq, 24, replace=False)
+    blocks = [(0, int(p) // nq, int(p) % nq) for p in picks] + [(0, H - 1, nq - 1), (0, 0, 0)]
+    G.note(f"case large block={block} topk={topk}, {len(blocks)} sampled VSA blocks")
+    gpu = G.run_dense_stages(inp, block_size=block)
+    ref = G.oracle_dense(inp, blocks=blocks, block=block)
+    _check_all(inp, gpu, ref)

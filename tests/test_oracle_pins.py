@@ -184,6 +184,26 @@ def _lse_max_only(q, k, idx, block=64):
     return out
 
 
+_orig_block_sizes = O.block_sizes
+_orig_pool = O.pool
+_orig_sparse_block = O.sparse_block
+
+
+def _block_sizes_always_64(seqlen, block=64):
+    # the block parameter ignored when splitting a sequence
+    return _orig_block_sizes(seqlen, 64)
+
+
+def _pool_stride_64(x, sizes, block=64):
+    # blocks of `block` tokens averaged, but located 64 rows apart
+    return _orig_pool(x, sizes, 64)
+
+
+def _sparse_stride_64(q_rows, k, v, kv_sizes, idx, block=64):
+    # selected KV blocks located 64 rows apart whatever the block size
+    return _orig_sparse_block(q_rows, k, v, kv_sizes, idx, 64)
+
+
 MISTAKES = {
     "sparse_scale_dropped": ("sparse_block", _sparse_no_scale),
     "pool_divides_by_64": ("pool", _pool_div64),
@@ -205,6 +225,9 @@ MISTAKES = {
     "lse_natural_log": ("backward.sparse_row_lse2", _lse_natural_log),
     "lse_unscaled": ("backward.sparse_row_lse2", _lse_unscaled),
     "lse_max_only": ("backward.sparse_row_lse2", _lse_max_only),
+    "block_sizes_ignore_block": ("block_sizes", _block_sizes_always_64),
+    "pool_blocks_64_apart": ("pool", _pool_stride_64),
+    "sparse_blocks_64_apart": ("sparse_block", _sparse_stride_64),
 }
 
 

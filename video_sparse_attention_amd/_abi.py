@@ -19,6 +19,7 @@ VSA_ERR_HIP = -9
 
 VSA_LAYOUT_DENSE = 0
 VSA_LAYOUT_PACKED = 1
+VSA_LAYOUT_BSHD = 2
 VSA_GATE_NONE = 0
 VSA_GATE_TOKEN = 1
 VSA_GATE_FULL = 2
@@ -64,6 +65,8 @@ SIGNATURES = {
                            vp, vp, vp, vp, vp, sz, vp]),
     "vsa_forward": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
                           i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]),
+    "vsa_forward_bshd": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
+                               i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]),
     "vsa_forward_varlen": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
                                  vp, vp, vp, vp, vp,
                                  i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]),

@@ -15,7 +15,7 @@ from typing import List, Optional, Sequence
 import torch
 
 from . import _abi
-from ._abi import (VSA_GATE_FULL, VSA_GATE_NONE, VSA_GATE_TOKEN, VSA_LAYOUT_DENSE,
+from ._abi import (VSA_GATE_FULL, VSA_GATE_NONE, VSA_GATE_TOKEN, VSA_LAYOUT_BSHD, VSA_LAYOUT_DENSE,
                    VSA_LAYOUT_PACKED, VsaError, VsaMetaSizes, VsaProblem)
 
 BLOCK = 64
@@ -45,8 +45,10 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None, contiguous=True, grad_o
                            "use video_sparse_attn for training")
 
 
-def _gate_args(gate: Optional[torch.Tensor], token_shape, full_shape):
-    """(mode, strides array or None) for a gate tensor, strict on shape."""
+def _gate_args(gate: Optional[torch.Tensor], token_shape, full_shape, bshd: bool = False):
+    """(mode, strides array or None) for a gate tensor, strict on shape; the
+    C ABI takes element strides in (batch, head, token) order, so a BSHD gate's
+    (batch, token, head) strides are reordered."""
     if gate is None:
         return VSA_GATE_NONE, None
     _need(gate, "gate", torch.bfloat16, contiguous=False)
@@ -63,6 +65,8 @@ def _gate_args(gate: Optional[torch.Tensor], token_shape, full_shape):
         raise ValueError(f"gate has shape {shp}, expected {tuple(token_shape)} or {tuple(full_shape)}")
     if len(st) == 2:  # packed: [H, slots(, D)] -> (unused, head, slot)
         st = [0] + st
+    elif bshd:  # [B, S, H(, D)] -> (batch, head, token)
+        st = [st[0], st[2], st[1]]
     return mode, (ctypes.c_int64 * 3)(*st)
 
 
@@ -128,9 +132,11 @@ def vsa_build_metadata(seqlens_q: Sequence[int], seqlens_kv: Optional[Sequence[i
 
 
 def dense_problem(batch: int, heads: int, seqlen_q: int, seqlen_kv: int, head_dim: int,
-                  topk: int) -> VsaProblem:
-    return VsaProblem(layout=VSA_LAYOUT_DENSE, heads=heads, head_dim=head_dim, block_size=BLOCK,
-                      batch=batch, seqlen_q=seqlen_q, seqlen_kv=seqlen_kv, topk=topk)
+                  topk: int, block_size: int = BLOCK, bshd: bool = False) -> VsaProblem:
+    """A DENSE ([B,H,S,D]) or, with ``bshd``, BSHD ([B,S,H,D]) problem;
+    ``block_size`` 64, 128 or 256."""
+    return VsaProblem(layout=VSA_LAYOUT_BSHD if bshd else VSA_LAYOUT_DENSE, heads=heads, head_dim=head_dim,
+                      block_size=block_size, batch=batch, seqlen_q=seqlen_q, seqlen_kv=seqlen_kv, topk=topk)
 
 
 def vsa_workspace_size(problem: VsaProblem) -> int:
@@ -149,9 +155,9 @@ def alloc_workspace(problem: VsaProblem, device) -> torch.Tensor:
 
 def block_shapes(problem: VsaProblem):
     """(out_c shape, q2k_idx shape, q2k_num shape) of a problem."""
-    if problem.layout == VSA_LAYOUT_DENSE:
-        nq = -(-problem.seqlen_q // BLOCK)
-        nkv = -(-problem.seqlen_kv // BLOCK)
+    if problem.layout in (VSA_LAYOUT_DENSE, VSA_LAYOUT_BSHD):
+        nq = -(-problem.seqlen_q // problem.block_size)
+        nkv = -(-problem.seqlen_kv // problem.block_size)
         kk = min(problem.topk, nkv)
         b, h, d = problem.batch, problem.heads, problem.head_dim
         return (b, h, nq, d), (b, h, nq, kk), (b, h, nq)
@@ -165,6 +171,9 @@ def token_shapes(problem: VsaProblem):
     if problem.layout == VSA_LAYOUT_DENSE:
         b = problem.batch
         return (b, h, problem.seqlen_q, d), (b, h, problem.seqlen_kv, d)
+    if problem.layout == VSA_LAYOUT_BSHD:
+        b = problem.batch
+        return (b, problem.seqlen_q, h, d), (b, problem.seqlen_kv, h, d)
     return (h, BLOCK * problem.total_q_blocks, d), (h, BLOCK * problem.total_kv_blocks, d)
 
 
@@ -196,7 +205,7 @@ def vsa_sparse_attn_from_indices(problem: VsaProblem, q, k, v, q2k_idx, q2k_num,
     _, isz, ns = block_shapes(problem)
     if tuple(q2k_idx.shape[:-1]) != tuple(isz[:-1]):
         raise ValueError(f"q2k_idx has shape {tuple(q2k_idx.shape)}, expected {isz[:-1]} + (k,)")
-    if problem.layout == VSA_LAYOUT_DENSE and q2k_idx.shape[-1] != isz[-1]:
+    if problem.layout != VSA_LAYOUT_PACKED and q2k_idx.shape[-1] != isz[-1]:
         raise ValueError(f"q2k_idx rows must hold min(topk, nKV) = {isz[-1]} entries")
     _need(q2k_idx, "q2k_idx", torch.int32)
     _need(q2k_num, "q2k_num", torch.int32, ns)
@@ -214,7 +223,7 @@ def vsa_sparse_attn_combine(problem: VsaProblem, q, k, v, q2k_idx, q2k_num, out_
     cs, isz, ns = block_shapes(problem)
     if tuple(q2k_idx.shape[:-1]) != tuple(isz[:-1]):
         raise ValueError(f"q2k_idx has shape {tuple(q2k_idx.shape)}, expected {isz[:-1]} + (k,)")
-    if problem.layout == VSA_LAYOUT_DENSE and q2k_idx.shape[-1] != isz[-1]:
+    if problem.layout != VSA_LAYOUT_PACKED and q2k_idx.shape[-1] != isz[-1]:
         raise ValueError(f"q2k_idx rows must hold min(topk, nKV) = {isz[-1]} entries")
     _need(q2k_idx, "q2k_idx", torch.int32)
     _need(q2k_num, "q2k_num", torch.int32, ns)
@@ -228,7 +237,7 @@ def vsa_sparse_attn_combine(problem: VsaProblem, q, k, v, q2k_idx, q2k_num, out_
 
 def _gate_shapes(problem):
     qs = token_shapes(problem)[0]
-    return qs[:-1], qs
+    return qs[:-1], qs, problem.layout == VSA_LAYOUT_BSHD
 
 
 def vsa_combine(problem: VsaProblem, out_c, gate, out) -> None:
@@ -375,21 +384,28 @@ def video_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: i
 # ---------------------------------------------------------------------------
 
 def vsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int,
-                gate: Optional[torch.Tensor] = None, *, out: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None, return_aux: bool = False):
-    """VSA forward on dense ``[B, H, S, D]`` bf16 tensors (vsa_forward).
+                gate: Optional[torch.Tensor] = None, *, block_size: int = BLOCK, bshd: bool = False,
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                return_aux: bool = False):
+    """VSA forward on dense ``[B, H, S, D]`` bf16 tensors (vsa_forward), or on
+    ``[B, S, H, D]`` tensors with ``bshd`` (vsa_forward_bshd).
 
-    ``gate``: None, ``[B, H, Sq]`` or ``[B, H, Sq, D]`` bf16 (any strides, e.g. a
-    transposed ``[B, S, H]`` view).  With ``return_aux`` also returns
+    ``gate``: None, ``[B, H, Sq]`` or ``[B, H, Sq, D]`` bf16 (``[B, Sq, H]`` or
+    ``[B, Sq, H, D]`` with ``bshd``; any strides, e.g. a transposed view).
+    ``block_size``: 64, 128 or 256.  With ``return_aux`` also returns
     ``(out_c, q2k_idx, q2k_num)``.
     """
     if q.dim() != 4:
-        raise ValueError("q must be [B, H, S, D]")
-    B, H, Sq, D = q.shape
-    Skv = k.shape[2] if k.dim() == 4 else -1
-    problem = dense_problem(B, H, Sq, Skv, D, topk)
+        raise ValueError("q must be [B, H, S, D] ([B, S, H, D] with bshd)")
+    if bshd:
+        B, Sq, H, D = q.shape
+        Skv = k.shape[1] if k.dim() == 4 else -1
+    else:
+        B, H, Sq, D = q.shape
+        Skv = k.shape[2] if k.dim() == 4 else -1
+    problem = dense_problem(B, H, Sq, Skv, D, topk, block_size, bshd)
     _check_qkv(problem, q, k, v)
-    mode, st = _gate_args(gate, (B, H, Sq), (B, H, Sq, D))
+    mode, st = _gate_args(gate, *_gate_shapes(problem))
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", torch.bfloat16, q.shape)
@@ -402,10 +418,11 @@ def vsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int,
                torch.empty(isz, dtype=torch.int32, device=q.device),
                torch.empty(ns, dtype=torch.int32, device=q.device))
     oc, idx, num = aux if aux else (None, None, None)
-    _abi.check(_abi.load().vsa_forward(
+    fn = _abi.load().vsa_forward_bshd if bshd else _abi.load().vsa_forward
+    _abi.check(fn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(gate), mode, st, _ptr(out), _ptr(idx), _ptr(num),
-        _ptr(oc), B, H, Sq, Skv, D, BLOCK, topk, _ptr(workspace), workspace.numel(),
-        _stream(q.device)), "vsa_forward")
+        _ptr(oc), B, H, Sq, Skv, D, block_size, topk, _ptr(workspace), workspace.numel(),
+        _stream(q.device)), "vsa_forward_bshd" if bshd else "vsa_forward")
     return (out, *aux) if return_aux else out
 
 

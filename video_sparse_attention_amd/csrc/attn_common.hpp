@@ -114,18 +114,20 @@ __device__ __forceinline__ void dma_16B_pair(const void* sbase, uint32_t voff_a,
         : "memory");
 }
 
-// Copy one 64-row KV block starting at `block` into a swizzled tile.  Full
-// blocks: instructions 2m and 2m + 1 of a lane fetch lane_off0 + 4096 m and
-// lane_off1 + 4096 m (passed as lane_off1_m2k = lane_off1 - 2048, see
-// dma_16B_pair) into LDS bytes lds0 + 4096 m and lds0 + 4096 m + 2048.
-// Partial blocks (valid < 64): rows past valid - 1 repeat that row, so every
-// address stays inside the tensor and every LDS value is finite.
+// Copy one 64-row KV block starting at `block` (rows `pitch` bytes apart)
+// into a swizzled tile.  Full blocks of contiguous rows: instructions 2m and
+// 2m + 1 of a lane fetch lane_off0 + 4096 m and lane_off1 + 4096 m (passed as
+// lane_off1_m2k = lane_off1 - 2048, see dma_16B_pair) into LDS bytes
+// lds0 + 4096 m and lds0 + 4096 m + 2048.  Otherwise one copy per instruction
+// with the row clamped: rows past valid - 1 repeat that row, so every address
+// stays inside the tensor and every LDS value is finite.
 template <int D, int SW>
 __device__ __forceinline__ void load_tile(uint32_t lds0, const uint16_t* block, int valid, int wave,
-                                          int lane, uint32_t lane_off0, uint32_t lane_off1_m2k) {
+                                          int lane, uint32_t lane_off0, uint32_t lane_off1_m2k,
+                                          uint32_t pitch = 2u * D) {
     constexpr int CH = D / 8;
     const char* base = (const char*)uniform_ptr(block);
-    if (valid == kBlock) {
+    if (valid == kBlock && pitch == 2u * D) {
 #pragma unroll
         for (int m = 0; m < CH / 4; ++m)
             dma_16B_pair(base + 4096 * m, lane_off0, lane_off1_m2k, lds0 + 4096u * m);
@@ -142,7 +144,7 @@ __device__ __forceinline__ void load_tile(uint32_t lds0, const uint16_t* block, 
 #pragma unroll
         for (int n = 0; n < CH / 2; ++n) {
             const int r = min(row0, valid - 1 - RSTEP * n) + RSTEP * n;
-            dma_16B(base, (uint32_t)(r * CH * 16 + 16 * ((n & 1) ? c1 : c0)), lds0 + 2048u * n);
+            dma_16B(base, (uint32_t)r * pitch + 16u * ((n & 1) ? c1 : c0), lds0 + 2048u * n);
         }
     }
 }

@@ -33,22 +33,24 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DevProblem P, con
     constexpr int TG = kCombThreads / CH;  // token groups
     constexpr int TPT = kBlock / TG;       // tokens per thread
 
-    int64_t row0, cb;   // first token row of the block, block index in out_c
+    int64_t off0, st, cb;  // element offset of the block's first row, row stride, row of out_c
     int size;
-    int64_t g_base;     // gate element offset of token 0 of the block
+    int64_t g_base;        // gate element offset of token 0 of the block
     if (!P.packed) {
-        const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+        const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;  // 64-token block
         if (blk >= P.nQ) return;
         const int64_t sh = (int64_t)b * P.H + h;
         size = min(kBlock, P.Sq - kBlock * blk);
-        row0 = sh * P.Sq + (int64_t)kBlock * blk;
-        cb = sh * P.nQ + blk;
+        st = P.q_st;
+        off0 = (int64_t)b * P.q_sb + (int64_t)h * P.q_sh + (int64_t)kBlock * blk * st;
+        cb = sh * P.nQB + blk / P.ratio;  // out_c is at VSA-block resolution
         g_base = (int64_t)b * gs0 + (int64_t)h * gs1 + (int64_t)kBlock * blk * gs2;
     } else {
         const int g = blockIdx.x, h = blockIdx.y;
         if (g >= P.total_q) return;
         size = clampi(P.bs_q[g], 1, kBlock);
-        row0 = ((int64_t)h * P.total_q + g) * kBlock;
+        st = D;
+        off0 = ((int64_t)h * P.total_q + g) * kBlock * D;
         cb = (int64_t)h * P.total_q + g;
         g_base = (int64_t)h * gs1 + (int64_t)kBlock * g * gs2;
     }
@@ -65,7 +67,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DevProblem P, con
     for (int r = 0; r < TPT; ++r) {
         const int t = tg + TG * r;
         if (t < size) {
-            w[r] = *reinterpret_cast<const uint4*>(out + (row0 + t) * D + 8 * c);
+            w[r] = *reinterpret_cast<const uint4*>(out + off0 + t * st + 8 * c);
             if (MODE == 1) gt[r] = __uint_as_float((uint32_t)gate[g_base + (int64_t)t * gs2] << 16);
             if (MODE == 2) gf[r] = *reinterpret_cast<const uint4*>(gate + g_base + (int64_t)t * gs2 + 8 * c);
         }
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DevProblem P, con
             }
             res[e] = pack2(a, b);
         }
-        *reinterpret_cast<uint4*>(out + (row0 + t) * D + 8 * c) = make_uint4(res[0], res[1], res[2], res[3]);
+        *reinterpret_cast<uint4*>(out + off0 + t * st + 8 * c) = make_uint4(res[0], res[1], res[2], res[3]);
     }
 }
 

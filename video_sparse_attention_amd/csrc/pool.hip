@@ -3,12 +3,13 @@
 // coarse/sparse combine", Problem and Notes).
 //
 // HBM-bound streaming kernel.  Thread (block, c) owns the 16-byte chunk c
-// (8 consecutive d) of one 64-token block and walks the block's valid tokens
+// (8 consecutive d) of one block (64 tokens; 64 * ratio tokens for the VSA
+// blocks of 128 or 256 tokens of the dense layouts) and walks its valid tokens
 // with independent 16-byte loads (8 in flight per thread), accumulating the
 // 8 sums in float64 registers: no LDS and no cross-thread reduction.  The
 // CH = D/8 threads of a block read each token row as one contiguous
 // 16*CH-byte segment, so every load instruction of a wave is fully
-// coalesced.  Sums of at most 64 bf16 values in float64 are exact for any
+// coalesced.  Sums of at most 256 bf16 values in float64 are exact for any
 // realistic data, so the result does not depend on the order of the
 // additions; the mean is an IEEE division by the block's valid-token count.
 #include "vsa_internal.hpp"
@@ -37,24 +38,27 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(DevProblem P, const 
     const int blk = blockIdx.x * BPG + threadIdx.x / CH;
     const int c = threadIdx.x % CH;
 
-    int64_t row0, out_row;
+    int64_t off0, st, out_row;  // element offset of the block's first row, row stride
     int size;
     if (!P.packed) {
-        const int nb = which == 0 ? P.nQ : P.nKV;
+        const int nb = which == 0 ? P.nQB : P.nKVB;
         if (blk >= nb) return;
         const int S = which == 0 ? P.Sq : P.Skv;
-        size = min(kBlock, S - kBlock * blk);
-        const int64_t sh = (int64_t)b * P.H + h;
-        row0 = sh * S + (int64_t)kBlock * blk;
-        out_row = sh * nb + blk;
+        const int bt = kBlock * P.ratio;  // tokens per block
+        size = min(bt, S - bt * blk);
+        st = which == 0 ? P.q_st : P.kv_st;
+        off0 = (which == 0 ? (int64_t)b * P.q_sb + (int64_t)h * P.q_sh : (int64_t)b * P.kv_sb + (int64_t)h * P.kv_sh) +
+               (int64_t)bt * blk * st;
+        out_row = ((int64_t)b * P.H + h) * nb + blk;
     } else {
         const int nb = which == 0 ? P.total_q : P.total_kv;
         if (blk >= nb) return;
         size = clampi(which == 0 ? P.bs_q[blk] : P.bs_kv[blk], 1, kBlock);
-        row0 = ((int64_t)h * nb + blk) * kBlock;
+        st = D;
+        off0 = ((int64_t)h * nb + blk) * kBlock * D;
         out_row = (int64_t)h * nb + blk;
     }
-    const uint16_t* src = (which == 0 ? q : (which == 1 ? k : v)) + row0 * D + 8 * c;
+    const uint16_t* src = (which == 0 ? q : (which == 1 ? k : v)) + off0 + 8 * c;
     double* dst = which == 0 ? qc : (which == 1 ? kc : vc);
 
     double acc[8];
@@ -65,7 +69,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(DevProblem P, const 
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int t = t0 + u;
-            w[u] = t < size ? *reinterpret_cast<const uint4*>(src + (int64_t)t * D) : make_uint4(0, 0, 0, 0);
+            w[u] = t < size ? *reinterpret_cast<const uint4*>(src + (int64_t)t * st) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -86,7 +90,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(DevProblem P, const 
 hipError_t launch_pool(const DevProblem& P, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        double* qc, double* kc, double* vc, hipStream_t st) {
     const int bpg = kPoolThreads / (P.D / 8);
-    const int nb = P.packed ? max(P.total_q, P.total_kv) : max(P.nQ, P.nKV);
+    const int nb = P.packed ? max(P.total_q, P.total_kv) : max(P.nQB, P.nKVB);
     const dim3 grid((nb + bpg - 1) / bpg, P.H, P.packed ? 3 : 3 * P.nseq);
     if (P.D == 128)
         hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(kPoolThreads), 0, st, P, q, k, v, qc, kc, vc);

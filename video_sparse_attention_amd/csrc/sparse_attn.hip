@@ -100,7 +100,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
         if (i < 0 || i >= sv.nq) return;  // block outside every sequence
     }
     const int qsize = q_block_size(P, sv, i);
-    const int64_t qrow0 = sv.qrow_base + (int64_t)kBlock * i;
+    const int64_t qrow0 = sv.qrow_base + (int64_t)kBlock * i;    // row index (lse)
+    const int64_t qoff0 = sv.q_off + (int64_t)kBlock * i * sv.q_st;  // element offset of row 0
+    // VSA blocks of 64 * ratio tokens (dense layouts): the routing and out_c
+    // are per VSA block; a selected VSA block J stands for the 64-token KV
+    // blocks J ratio .. J ratio + ratio - 1
+    const int lr = P.ratio >> 1;  // log2(ratio) for ratio 1, 2, 4
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -114,7 +119,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         uint4 u = make_uint4(0, 0, 0, 0);
-        if (qr < qsize) u = *reinterpret_cast<const uint4*>(q + (qrow0 + qr) * D + 16 * ks + 8 * hh);
+        if (qr < qsize) u = *reinterpret_cast<const uint4*>(q + qoff0 + qr * sv.q_st + 16 * ks + 8 * hh);
         qf[ks] = as_bf16x8(u);
     }
 
@@ -126,8 +131,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     float m = -INFINITY;  // running (lazy) max of raw scores for this lane's query
     float l = 0.f;        // this lane's share of the running sum
 
-    const int64_t qb = sv.qblk_base + i;
-    const int n = __builtin_amdgcn_readfirstlane(clampi(num[qb], 0, P.idx_row));
+    // VSA block of this query block in the block-resolution arrays
+    const int64_t qb = P.packed ? sv.qblk_base + i : ((int64_t)s * P.H + h) * P.nQB + (i >> lr);
+    const int nsel = __builtin_amdgcn_readfirstlane(clampi(num[qb], 0, P.idx_row));
+    const int n = nsel << lr;  // 64-token KV blocks to visit
     const_int* list = (const_int*)uniform_ptr(idx + qb * P.idx_row);
     const_int* bs_kv = (const_int*)(P.packed ? uniform_ptr(P.bs_kv + sv.kvblk0) : nullptr);
     const int rebase = __builtin_amdgcn_readfirstlane(sv.idx_rebase);
@@ -139,12 +146,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     // vmcnt waits count.
     __builtin_amdgcn_s_waitcnt(0);
 
-    // the walk visits list positions (t0 + t) mod n for t = 0 .. n-1
-    const int t0 = n > 0 ? ((i % kSweep) * n) / kSweep : 0;
+    // the walk visits positions (t0 + t) mod n for t = 0 .. n-1 of the list
+    // expanded to 64-token blocks
+    const int t0 = n > 0 ? (((i >> lr) % kSweep) * n) / kSweep : 0;
     auto entry = [&](int t) -> int {
         int pos = t0 + t;
         if (pos >= n) pos -= n;
-        return list[pos];
+        const int J = list[pos >> lr];
+        // no sequence has 2^28 VSA blocks: such an entry (or a negative one)
+        // is out of range, and is kept from wrapping into range by the shift
+        if (lr > 0 && (unsigned)J >= (1u << 28)) return -1;
+        return (J << lr) + (pos & ((1 << lr) - 1));
     };
     // The entry of walk step pre_t is loaded one step ahead, so the scalar
     // load's latency is hidden behind a whole block of work.
@@ -173,6 +185,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     const uint32_t koff1 = (uint32_t)lane_src_offset<CH, kSwzRow>(wave, lane, 1) - 2048u;
     const uint32_t voff0 = (uint32_t)lane_src_offset<CH, kSwzTr>(wave, lane, 0);
     const uint32_t voff1 = (uint32_t)lane_src_offset<CH, kSwzTr>(wave, lane, 1) - 2048u;
+    const uint32_t pitch = __builtin_amdgcn_readfirstlane((uint32_t)(2 * sv.kv_st));  // bytes between KV rows
     // this wave's LDS byte base inside each tile
     const uint32_t k_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)k_tile + 1024u * wave);
     const uint32_t v_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)v_tile + 1024u * wave);
@@ -191,7 +204,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     while (j >= 0 || first) {
         const bool cur = j >= 0;
         const bool more = jn >= 0;
-        const int64_t r0n = more ? sv.kvrow_base + (int64_t)kBlock * jn : 0;
+        const int64_t off_n = more ? sv.kv_off + (int64_t)kBlock * jn * sv.kv_st : 0;
 
         // ---- S^T = K Q^T ----------------------------------------------------
         f32x16 sacc[2];
@@ -228,7 +241,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
             }
             wg_barrier();  // both waves are done with the K tile
         }
-        if (more) load_tile<D, kSwzRow>(k_lds, k + r0n * D, kvsize_n, wave, lane, koff0, koff1);
+        if (more) load_tile<D, kSwzRow>(k_lds, k + off_n, kvsize_n, wave, lane, koff0, koff1, pitch);
 
         if (cur) {
             // ---- online softmax; acc e of tile mt is token 32 mt + 8 (e/4) + 4 hh + e%4
@@ -300,7 +313,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
             }
             wg_barrier();  // both waves are done with the V tile
         }
-        if (more) load_tile<D, kSwzTr>(v_lds, v + r0n * D, kvsize_n, wave, lane, voff0, voff1);
+        if (more) load_tile<D, kSwzTr>(v_lds, v + off_n, kvsize_n, wave, lane, voff0, voff1, pitch);
 
         first = false;
         j = jn;
@@ -318,7 +331,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     // P[t][u] = exp2(s[t][u] c_log2 - lse[t]) for the row's selected tokens
     if (C.lse && hh == 0 && qr < qsize) C.lse[qrow0 + qr] = m * c_log2 + __log2f(lt);
     if (CMODE != kSparseOnly && C.out_s && qr < qsize) {
-        uint16_t* srow = C.out_s + (qrow0 + qr) * D;
+        uint16_t* srow = C.out_s + qoff0 + qr * sv.q_st;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -329,7 +342,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
                 *reinterpret_cast<uint2*>(srow + 32 * dt + 8 * jj + 4 * hh) = w2;
             }
     } else if (CMODE != kSparseOnly && C.out_s && P.packed) {
-        uint16_t* srow = C.out_s + (qrow0 + qr) * D;
+        uint16_t* srow = C.out_s + qoff0 + qr * sv.q_st;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -337,7 +350,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
                 *reinterpret_cast<uint2*>(srow + 32 * dt + 8 * jj + 4 * hh) = make_uint2(0, 0);
     }
     if (qr < qsize && CMODE == kSparseOnly) {
-        uint16_t* orow = out + (qrow0 + qr) * D;
+        uint16_t* orow = out + qoff0 + qr * sv.q_st;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -350,7 +363,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     } else if (qr < qsize) {
         // fused combine: out = out_c[block] * gate + O / l in float32 (FMA),
         // one rounding to bf16
-        uint16_t* orow = out + (qrow0 + qr) * D;
+        uint16_t* orow = out + qoff0 + qr * sv.q_st;
         const float* ocr = C.out_c + qb * D;
         // token index of this row along the gate's token axis
         const int64_t tok = (int64_t)kBlock * (P.packed ? sv.qblk0 + i : i) + qr;
@@ -384,7 +397,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
                 *reinterpret_cast<uint2*>(orow + d0) = w2;
             }
     } else if (P.packed) {
-        uint16_t* orow = out + (qrow0 + qr) * D;
+        uint16_t* orow = out + qoff0 + qr * sv.q_st;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll

@@ -38,8 +38,10 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // Validate a problem and build its kernel-side view.
 int make_problem(const vsa_problem* pr, vsa::DevProblem* P) {
     if (!pr) return fail(VSA_ERR_NULL, "problem is NULL");
-    if (pr->block_size != VSA_BLOCK)
-        return fail(VSA_ERR_UNSUPPORTED, "block_size %d unsupported (only 64)", pr->block_size);
+    const bool dense = pr->layout == VSA_LAYOUT_DENSE || pr->layout == VSA_LAYOUT_BSHD;
+    if (pr->block_size != VSA_BLOCK && !(dense && (pr->block_size == 128 || pr->block_size == 256)))
+        return fail(VSA_ERR_UNSUPPORTED, "block_size %d unsupported (64; 128 or 256 for the dense layouts)",
+                    pr->block_size);
     if (pr->head_dim != 64 && pr->head_dim != 128)
         return fail(VSA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", pr->head_dim);
     if (pr->heads < 1) return fail(VSA_ERR_SHAPE, "heads must be >= 1 (got %d)", pr->heads);
@@ -47,7 +49,8 @@ int make_problem(const vsa_problem* pr, vsa::DevProblem* P) {
     *P = vsa::DevProblem{};
     P->H = pr->heads;
     P->D = pr->head_dim;
-    if (pr->layout == VSA_LAYOUT_DENSE) {
+    P->ratio = 1;
+    if (dense) {
         if (pr->batch < 1) return fail(VSA_ERR_SHAPE, "empty batch (batch=%d)", pr->batch);
         if (3LL * pr->batch > kGridYZMax) return fail(VSA_ERR_UNSUPPORTED, "batch too large");
         if (pr->seqlen_q < 1 || pr->seqlen_kv < 1)
@@ -57,14 +60,26 @@ int make_problem(const vsa_problem* pr, vsa::DevProblem* P) {
         P->nseq = pr->batch;
         P->Sq = pr->seqlen_q;
         P->Skv = pr->seqlen_kv;
+        P->ratio = pr->block_size / VSA_BLOCK;
         P->nQ = (pr->seqlen_q + VSA_BLOCK - 1) / VSA_BLOCK;
         P->nKV = (pr->seqlen_kv + VSA_BLOCK - 1) / VSA_BLOCK;
-        if (P->nKV > vsa::kMaxKvBlocks)
-            return fail(VSA_ERR_UNSUPPORTED, "%d KV blocks per sequence exceeds %d", P->nKV, vsa::kMaxKvBlocks);
-        P->kk = std::min(pr->topk, P->nKV);
+        P->nQB = (pr->seqlen_q + pr->block_size - 1) / pr->block_size;
+        P->nKVB = (pr->seqlen_kv + pr->block_size - 1) / pr->block_size;
+        if (P->nKVB > vsa::kMaxKvBlocks)
+            return fail(VSA_ERR_UNSUPPORTED, "%d KV blocks per sequence exceeds %d", P->nKVB, vsa::kMaxKvBlocks);
+        P->kk = std::min(pr->topk, P->nKVB);
         P->idx_row = P->kk;
         if ((int64_t)P->nQ * P->H * P->nseq > 0x7fffffffLL)
             return fail(VSA_ERR_UNSUPPORTED, "too many query blocks in one launch");
+        const int64_t H = P->H, D = P->D, Sq = P->Sq, Skv = P->Skv;
+        if (pr->layout == VSA_LAYOUT_DENSE) {  // [B, H, S, D]
+            P->q_sb = H * Sq * D, P->q_sh = Sq * D, P->q_st = D;
+            P->kv_sb = H * Skv * D, P->kv_sh = Skv * D, P->kv_st = D;
+        } else {  // [B, S, H, D]
+            P->bshd = 1;
+            P->q_sb = Sq * H * D, P->q_sh = D, P->q_st = H * D;
+            P->kv_sb = Skv * H * D, P->kv_sh = D, P->kv_st = H * D;
+        }
     } else if (pr->layout == VSA_LAYOUT_PACKED) {
         if (pr->num_seqs < 1) return fail(VSA_ERR_SHAPE, "empty batch (num_seqs=%d)", pr->num_seqs);
         if (pr->num_seqs > kGridYZMax) return fail(VSA_ERR_UNSUPPORTED, "num_seqs > %lld", (long long)kGridYZMax);
@@ -96,6 +111,9 @@ int make_problem(const vsa_problem* pr, vsa::DevProblem* P) {
         P->max_kv = pr->max_kv_blocks;
         P->max_topk = pr->max_topk;
         P->idx_row = pr->max_topk;
+        P->q_st = P->kv_st = P->D;  // rows of the packed layout are contiguous
+        P->q_sh = (int64_t)pr->total_q_blocks * VSA_BLOCK * P->D;
+        P->kv_sh = (int64_t)pr->total_kv_blocks * VSA_BLOCK * P->D;
     } else {
         return fail(VSA_ERR_UNSUPPORTED, "unknown layout %d", pr->layout);
     }
@@ -109,11 +127,12 @@ int64_t q_elems(const vsa::DevProblem& P) {
 int64_t kv_elems(const vsa::DevProblem& P) {
     return P.packed ? (int64_t)P.H * P.total_kv * VSA_BLOCK * P.D : (int64_t)P.nseq * P.H * P.Skv * P.D;
 }
+// block-resolution array lengths (VSA blocks)
 int64_t qblocks(const vsa::DevProblem& P) {
-    return P.packed ? (int64_t)P.H * P.total_q : (int64_t)P.nseq * P.H * P.nQ;
+    return P.packed ? (int64_t)P.H * P.total_q : (int64_t)P.nseq * P.H * P.nQB;
 }
 int64_t kvblocks(const vsa::DevProblem& P) {
-    return P.packed ? (int64_t)P.H * P.total_kv : (int64_t)P.nseq * P.H * P.nKV;
+    return P.packed ? (int64_t)P.H * P.total_kv : (int64_t)P.nseq * P.H * P.nKVB;
 }
 
 struct Workspace {
@@ -136,7 +155,7 @@ Workspace plan_workspace(const vsa::DevProblem& P, void* base) {
     w.qc = (double*)take(sizeof(double) * qblocks(P) * P.D);
     w.kc = (double*)take(sizeof(double) * kvblocks(P) * P.D);
     w.vc = (double*)take(sizeof(double) * kvblocks(P) * P.D);
-    w.coarse = (double*)take(sizeof(double) * vsa::coarse_scratch_doubles(P));
+    w.coarse = (double*)take(sizeof(double) * vsa::coarse_scratch_doubles(vsa::coarse_view(P)));
     w.coarse_bytes = off;
     w.out_c = (float*)take(sizeof(float) * qblocks(P) * P.D);
     w.idx = (int*)take(sizeof(int) * qblocks(P) * P.idx_row);
@@ -217,10 +236,14 @@ int gate_strides(const vsa::DevProblem& P, const uint16_t* gate, int mode, const
         }
         if (!P.packed && P.Sq > 1 && out[2] == 0) return fail(VSA_ERR_GATE, "gate token stride is 0");
         if (P.H > 1 && out[1] == 0) return fail(VSA_ERR_GATE, "gate head stride is 0");
-    } else if (!P.packed) {
+    } else if (!P.packed && !P.bshd) {  // [B, H, Sq(, D)]
         out[2] = dmul;
         out[1] = (int64_t)P.Sq * dmul;
         out[0] = (int64_t)P.H * P.Sq * dmul;
+    } else if (!P.packed) {  // [B, Sq, H(, D)]
+        out[2] = (int64_t)P.H * dmul;
+        out[1] = dmul;
+        out[0] = (int64_t)P.Sq * P.H * dmul;
     } else {
         out[2] = dmul;
         out[1] = (int64_t)P.total_q * VSA_BLOCK * dmul;
@@ -240,7 +263,7 @@ int run_coarse(const vsa::DevProblem& P, const uint16_t* q, const uint16_t* k, c
                float* out_c, int* idx, int* num, const Workspace& w, hipStream_t st) {
     int rc = hip_status(vsa::launch_pool(P, q, k, v, w.qc, w.kc, w.vc, st), "pool launch");
     if (rc) return rc;
-    return hip_status(vsa::launch_coarse_topk(P, w.qc, w.kc, w.vc, out_c, idx, num, w.coarse, st),
+    return hip_status(vsa::launch_coarse_topk(vsa::coarse_view(P), w.qc, w.kc, w.vc, out_c, idx, num, w.coarse, st),
                       "coarse/top-k launch");
 }
 
@@ -424,6 +447,8 @@ int vsa_sparse_attn_combine_train(const vsa_problem* problem, const vsa_bf16* q,
     vsa::DevProblem P;
     int rc = make_problem(problem, &P);
     if (rc) return rc;
+    if (P.bshd || P.ratio != 1)
+        return fail(VSA_ERR_UNSUPPORTED, "the training forward takes [B,H,S,D] or packed tensors with 64-token blocks");
     if ((rc = check_qkv(P, q, k, v))) return rc;
     if (!q2k_idx || !q2k_num || !out || !out_c || !out_s || !lse)
         return fail(VSA_ERR_NULL, "q2k_idx, q2k_num, out_c, out, out_s or lse is NULL");
@@ -450,6 +475,7 @@ int vsa_sparse_attn_combine_train(const vsa_problem* problem, const vsa_bf16* q,
 size_t vsa_backward_workspace_size(const vsa_problem* problem) {
     vsa::DevProblem P;
     if (make_problem(problem, &P) != VSA_OK) return 0;
+    if (P.bshd || P.ratio != 1) return 0;
     return plan_bwd_workspace(P, nullptr).total_bytes;
 }
 
@@ -461,6 +487,8 @@ int vsa_backward(const vsa_problem* problem, const vsa_bf16* q, const vsa_bf16* 
     vsa::DevProblem P;
     int rc = make_problem(problem, &P);
     if (rc) return rc;
+    if (P.bshd || P.ratio != 1)
+        return fail(VSA_ERR_UNSUPPORTED, "the backward takes [B,H,S,D] or packed tensors with 64-token blocks");
     if ((rc = check_qkv(P, q, k, v))) return rc;
     if (!q2k_idx || !q2k_num || !out_c || !out_s || !lse || !dout || !dq || !dk || !dv)
         return fail(VSA_ERR_NULL, "a required input or output pointer is NULL");
@@ -597,6 +625,24 @@ int vsa_forward(const vsa_bf16* q, const vsa_bf16* k, const vsa_bf16* v, const v
                 size_t workspace_bytes, vsa_stream stream) {
     vsa_problem pr{};
     pr.layout = VSA_LAYOUT_DENSE;
+    pr.heads = heads;
+    pr.head_dim = head_dim;
+    pr.block_size = block_size;
+    pr.batch = batch;
+    pr.seqlen_q = seqlen_q;
+    pr.seqlen_kv = seqlen_kv;
+    pr.topk = topk;
+    return forward_common(&pr, q, k, v, gate, gate_mode, gate_strides, out, q2k_idx, q2k_num, out_c, workspace,
+                          workspace_bytes, stream);
+}
+
+int vsa_forward_bshd(const vsa_bf16* q, const vsa_bf16* k, const vsa_bf16* v, const vsa_bf16* gate,
+                     int32_t gate_mode, const int64_t* gate_strides, vsa_bf16* out, int32_t* q2k_idx,
+                     int32_t* q2k_num, float* out_c, int32_t batch, int32_t heads, int32_t seqlen_q,
+                     int32_t seqlen_kv, int32_t head_dim, int32_t block_size, int32_t topk, void* workspace,
+                     size_t workspace_bytes, vsa_stream stream) {
+    vsa_problem pr{};
+    pr.layout = VSA_LAYOUT_BSHD;
     pr.heads = heads;
     pr.head_dim = head_dim;
     pr.block_size = block_size;

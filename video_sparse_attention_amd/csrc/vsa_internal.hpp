@@ -12,12 +12,21 @@ namespace vsa {
 constexpr int kBlock = 64;
 
 // Kernel-side view of a problem (passed by value to every kernel).
+// Token rows of q/out and k/v are addressed through element strides (d is
+// contiguous): [B,H,S,D] and [B,S,H,D] are both "dense" (one sequence per
+// batch item), the packed layout is [H,slots,D].  The attention kernels work
+// on 64-token blocks; the coarse branch and the routing on VSA blocks of
+// 64 * ratio tokens (ratio 1, 2 or 4; 1 for the packed layout).
 struct DevProblem {
-    int packed;  // 0 dense [B,H,S,D], 1 block-padded packed [H,slots,D]
+    int packed;  // 0 dense ([B,H,S,D] or [B,S,H,D]), 1 block-padded packed [H,slots,D]
+    int bshd;    // dense tensors are [B,S,H,D]
     int H, D;
     int nseq;  // B (dense) or num_seqs (packed)
     // dense
-    int Sq, Skv, nQ, nKV, kk;  // kk = min(topk, nKV)
+    int Sq, Skv, nQ, nKV;  // lengths and 64-token block counts
+    int ratio;             // VSA block = 64 * ratio tokens
+    int nQB, nKVB;         // VSA blocks per sequence (= nQ, nKV when ratio is 1)
+    int kk;                // min(topk, nKVB): row length of q2k_idx (dense)
     // packed
     const int* cu_q;
     const int* cu_kv;
@@ -26,6 +35,9 @@ struct DevProblem {
     const int* topk_s;
     int total_q, total_kv, max_q, max_kv, max_topk;
     int idx_row;  // row length of q2k_idx: kk (dense) or max_topk (packed)
+    // element strides of token rows: sequence (batch item), head, token
+    int64_t q_sb, q_sh, q_st;
+    int64_t kv_sb, kv_sh, kv_st;
 };
 
 // One sequence on one head: where its blocks live.
@@ -34,8 +46,10 @@ struct SeqView {
     int qblk0, kvblk0;    // first global block index (packed) or 0 (dense)
     int64_t qblk_base;    // index of block 0 in block-resolution q arrays
     int64_t kvblk_base;   // index of block 0 in block-resolution kv arrays
-    int64_t qrow_base;    // row (token slot) of block 0 in q/out
-    int64_t kvrow_base;   // row of block 0 in k/v
+    int64_t qrow_base;    // row (token slot) of block 0 in [.., S] row-indexed arrays (lse)
+    int64_t kvrow_base;   // the same for k/v
+    int64_t q_off, kv_off;  // element offset of token row 0 in q/out and in k/v
+    int64_t q_st, kv_st;    // element stride between consecutive token rows
     int idx_rebase;       // added to local KV block numbers when stored
 };
 
@@ -54,6 +68,10 @@ __device__ __forceinline__ SeqView seq_view(const DevProblem& P, int s, int h) {
         v.kvblk_base = sh * P.nKV;
         v.qrow_base = sh * P.Sq;
         v.kvrow_base = sh * P.Skv;
+        v.q_off = (int64_t)s * P.q_sb + (int64_t)h * P.q_sh;
+        v.kv_off = (int64_t)s * P.kv_sb + (int64_t)h * P.kv_sh;
+        v.q_st = P.q_st;
+        v.kv_st = P.kv_st;
         v.idx_rebase = 0;
     } else {
         int q0 = clampi(P.cu_q[s], 0, P.total_q);
@@ -69,6 +87,10 @@ __device__ __forceinline__ SeqView seq_view(const DevProblem& P, int s, int h) {
         v.kvblk_base = (int64_t)h * P.total_kv + k0;
         v.qrow_base = ((int64_t)h * P.total_q + q0) * kBlock;
         v.kvrow_base = ((int64_t)h * P.total_kv + k0) * kBlock;
+        v.q_off = v.qrow_base * P.D;
+        v.kv_off = v.kvrow_base * P.D;
+        v.q_st = P.D;
+        v.kv_st = P.D;
         v.idx_rebase = k0;
     }
     return v;
@@ -137,8 +159,17 @@ __host__ __device__ inline int64_t tile_token_raster(const TileGrid& g, int b, i
 // ---------------------------------------------------------------------------
 // launchers (one per kernel family; each returns hipError_t of the launch)
 // ---------------------------------------------------------------------------
+// Block means over VSA blocks of 64 * P.ratio tokens (dense) or over the
+// packed layout's 64-token blocks.
 hipError_t launch_pool(const DevProblem& P, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        double* qc, double* kc, double* vc, hipStream_t st);
+// The problem as the coarse branch sees it: VSA blocks as its blocks.
+inline DevProblem coarse_view(const DevProblem& P) {
+    DevProblem C = P;
+    C.nQ = P.nQB;
+    C.nKV = P.nKVB;
+    return C;
+}
 // scratch: coarse_scratch_doubles(P) doubles (block-level scores and row sums)
 hipError_t launch_coarse_topk(const DevProblem& P, const double* qc, const double* kc,
                               const double* vc, float* out_c, int* idx, int* num, double* scratch,
