@@ -8,8 +8,9 @@ into its epilogue, issued through the C ABI stage entry points exactly as
 vsa_forward issues them, on PyTorch's current HIP stream with inputs resident
 in HBM.  HIP events between the stages give each kernel's average duration
 over the timed steps.  Outside the timed steps the stand-alone combine kernel
-is timed with L2 and MALL flushed (its HBM rate) and the sparse kernel
-without the fused combine is timed for comparison.
+is timed with L2 and MALL flushed (its HBM rate; median of 20 launches, each
+after reading a 1 GiB buffer) and the sparse kernel without the fused combine
+is timed for comparison.
 
 Prints one JSON line.  ``value`` is effective TFLOP/s of the whole step with
 the pages' benchmark convention 4*B*H*nQ*k*64*64*D (padded blocks counted as
@@ -388,18 +389,26 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
 
     # Outside the timed steps: the stand-alone combine kernel (the pages'
-    # separate combine) with L2 and MALL flushed before each launch by
-    # writing a 1 GiB buffer, and the sparse kernel without the fused combine.
+    # separate combine) with L2 and MALL flushed before each launch, and the
+    # sparse kernel without the fused combine.  The flush reads a 1 GiB
+    # buffer: afterwards neither cache holds any of the combine's data and no
+    # dirty line of earlier writes is left to be written back during the
+    # timed launch.  The same launch after a flush that WRITES 1 GiB is also
+    # reported: there the MALL's write-back of 256 MB of the flush buffer's
+    # dirty lines lands inside the combine's window.
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    comb_ms, unf_ms = [], []
-    for _ in range(5):
-        flush.fill_(1.0)
+    comb_ms, comb_dirty_ms, unf_ms = [], [], []
+    for rep in range(40):
+        if rep % 2 == 0:
+            flush.sum()
+        else:
+            flush.fill_(1.0)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         vsa.vsa_combine(prob, out_c, gate, out)
         e1.record()
         torch.cuda.synchronize()
-        comb_ms.append(e0.elapsed_time(e1))
+        (comb_ms if rep % 2 == 0 else comb_dirty_ms).append(e0.elapsed_time(e1))
     for _ in range(5):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -409,6 +418,7 @@ def main():
         unf_ms.append(e0.elapsed_time(e1))
     del flush
     comb = sorted(comb_ms)[len(comb_ms) // 2]
+    comb_dirty = sorted(comb_dirty_ms)[len(comb_dirty_ms) // 2]
     unf = sorted(unf_ms)[len(unf_ms) // 2]
 
     # algorithmic bytes: the combine reads and writes out once, reads the gate and out_c
@@ -453,6 +463,8 @@ def main():
             "combine_standalone_cold_ms": round(comb, 4),
             "combine_standalone_GBps": round(comb_bytes / (comb * 1e-3) / 1e9, 1),
             "combine_standalone_frac_hbm": round(comb_bytes / (comb * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "combine_after_write_flush_ms": round(comb_dirty, 4),
+            "combine_after_write_flush_GBps": round(comb_bytes / (comb_dirty * 1e-3) / 1e9, 1),
             "combine_bytes": comb_bytes,
         },
         "cpu_baseline": None,
