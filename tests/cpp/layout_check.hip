@@ -76,41 +76,52 @@ static std::vector<int> fill_tile(int valid) {
     return tile;
 }
 
-// The four-wave copy (load_tile4): every chunk written once, the fast-path
-// lane offset plus 4096 n equals the per-instruction one, partial blocks clamp
-// inside the valid rows, and the resulting tile equals the two-wave one.
-template <int D, int SW, int ROWS = 64>
-static std::vector<int> fill_tile4(int valid) {
+// The NW-wave copy (load_tile_n, NW = 4 or 8): every chunk written once, the
+// fast-path lane offset plus 1024 NW n equals the per-instruction one, partial
+// or strided blocks (rows PITCH bytes apart) clamp inside the valid rows and
+// read inside each row, and the resulting tile equals the two-wave one.
+template <int D, int SW, int ROWS = 64, int NW = 4>
+static std::vector<int> fill_tileN(int valid, int pitch = D * 2) {
     constexpr int CH = D / 8;
     constexpr int ROWB = CH * 16;
-    constexpr int RSTEP = 256 / CH;
-    constexpr int NI = ROWS * CH / 256;
+    constexpr int RSTEP = 64 * NW / CH;
+    constexpr int NI = ROWS * CH / (64 * NW);
+    static_assert(NI >= 1 && NI * 64 * NW == ROWS * CH, "whole instructions");
     std::vector<int> tile(ROWS * D, -1);
     std::vector<int> hits(ROWS * CH, 0);
-    for (int wave = 0; wave < 4; ++wave)
+    for (int wave = 0; wave < NW; ++wave)
         for (int n = 0; n < NI; ++n)
             for (int lane = 0; lane < 64; ++lane) {
-                const int p = vsa::load_chunk_pos4(n, wave, lane);
-                CHECK(p >= 0 && p < ROWS * CH, "chunk position %d out of range (4 waves)", p);
+                const int p = vsa::load_chunk_posN<NW>(n, wave, lane);
+                CHECK(p >= 0 && p < ROWS * CH, "chunk position %d out of range (%d waves)", p, NW);
                 hits[p]++;
                 const int row = p / CH;
                 const int c = (p % CH) ^ vsa::tile_swz<CH, SW>(row);
-                const int fast = vsa::lane_src_offset4<CH, SW>(wave, lane) + 4096 * n;
-                CHECK(fast == row * ROWB + 16 * c, "4-wave fast-path offset D%d SW%d n%d w%d l%d", D, SW, n, wave, lane);
+                const int fast = vsa::lane_src_offsetN<CH, SW, NW>(wave, lane) + 1024 * NW * n;
+                CHECK(fast == row * ROWB + 16 * c, "%d-wave fast-path offset D%d SW%d n%d w%d l%d", NW, D, SW, n,
+                      wave, lane);
                 // the kernel's partial-block formula
-                const int p0 = vsa::load_chunk_pos4(0, wave, lane);
+                const int p0 = vsa::load_chunk_posN<NW>(0, wave, lane);
                 const int row0 = p0 / CH;
                 const int c0 = (p0 % CH) ^ vsa::tile_swz<CH, SW>(row0);
                 const int rk = std::min(row0, valid - 1 - RSTEP * n) + RSTEP * n;
-                CHECK(row0 + RSTEP * n == row && c0 == c, "4-wave partial-path row/chunk");
-                CHECK(rk == std::min(row, valid - 1), "4-wave partial-path clamp");
-                const int src_byte = valid >= ROWS ? fast : rk * ROWB + 16 * c0;
-                CHECK(src_byte / ROWB < valid, "4-wave copy reads past the valid rows");
-                const int lds_elem = (4 * n + wave) * 64 * 8 + 8 * lane;
-                for (int e = 0; e < 8; ++e) tile[lds_elem + e] = val(src_byte / ROWB, (src_byte % ROWB) / 2 + e);
+                CHECK(row0 + RSTEP * n == row && c0 == c, "%d-wave partial-path row/chunk", NW);
+                CHECK(rk == std::min(row, valid - 1), "%d-wave partial-path clamp", NW);
+                // byte offset in the source block of rows `pitch` bytes apart
+                const bool fast_path = valid >= ROWS && pitch == ROWB;
+                const long src = fast_path ? fast : (long)rk * pitch + 16 * c0;
+                CHECK(src / pitch < valid && src % pitch + 16 <= ROWB, "%d-wave copy reads outside the valid rows", NW);
+                const int srow = (int)(src / pitch), sbyte = (int)(src % pitch);
+                const int lds_elem = (NW * n + wave) * 64 * 8 + 8 * lane;
+                for (int e = 0; e < 8; ++e) tile[lds_elem + e] = val(srow, sbyte / 2 + e);
             }
-    for (int p = 0; p < ROWS * CH; ++p) CHECK(hits[p] == 1, "chunk %d written %d times (4 waves)", p, hits[p]);
+    for (int p = 0; p < ROWS * CH; ++p) CHECK(hits[p] == 1, "chunk %d written %d times (%d waves)", p, hits[p], NW);
     return tile;
+}
+
+template <int D, int SW, int ROWS = 64>
+static std::vector<int> fill_tile4(int valid) {
+    return fill_tileN<D, SW, ROWS, 4>(valid);
 }
 
 // Row operand (the A operand of S^T = K Q^T, or of S = Q K^T / dP = dO V^T in
@@ -242,6 +253,17 @@ static void check_d() {
         const std::vector<int> ref32 = fill_tile<D, vsa::kSwzDual>(v32);
         const bool same32 = std::equal(half.begin(), half.end(), ref32.begin());
         CHECK(same32, "32-row 4-wave copy differs from the first rows of the 64-row layout (D=%d)", D);
+        // the forward's K (row) and V (transposed) tiles copied by the 4 or 8
+        // waves of a workgroup that serves 2 or 4 query blocks, with rows
+        // contiguous or 2*D*H bytes apart ([B,S,H,D] with H = 3)
+        for (int pitch : {2 * D, 2 * D * 3}) {
+            const std::vector<int> k2 = fill_tile<D, vsa::kSwzRow>(valid);
+            const std::vector<int> v2 = fill_tile<D, vsa::kSwzTr>(valid);
+            CHECK((fill_tileN<D, vsa::kSwzRow, 64, 4>(valid, pitch) == k2), "4-wave K tile (D=%d pitch %d)", D, pitch);
+            CHECK((fill_tileN<D, vsa::kSwzTr, 64, 4>(valid, pitch) == v2), "4-wave V tile (D=%d pitch %d)", D, pitch);
+            CHECK((fill_tileN<D, vsa::kSwzRow, 64, 8>(valid, pitch) == k2), "8-wave K tile (D=%d pitch %d)", D, pitch);
+            CHECK((fill_tileN<D, vsa::kSwzTr, 64, 8>(valid, pitch) == v2), "8-wave V tile (D=%d pitch %d)", D, pitch);
+        }
     }
     for (int banks : {32, 64}) {
         const int kr = bank_row<D, vsa::kSwzRow>(banks), vt = bank_tr<D, vsa::kSwzTr>(banks);

@@ -149,32 +149,41 @@ __device__ __forceinline__ void load_tile(uint32_t lds0, const uint16_t* block, 
     }
 }
 
-// The same copy of the first ROWS (64 or 32) rows of a block by four waves
-// (load_chunk_pos4): each wave issues ROWS CH / 256 instructions; instruction
-// n of a block with every row valid fetches lane_off + 4096 n into LDS byte
-// lds0 + 4096 n (lds0 = tile + 1024 wave).  Rows at or past `valid` repeat row
-// valid - 1, as in load_tile.
-template <int D, int SW, int ROWS>
-__device__ __forceinline__ void load_tile4(uint32_t lds0, const uint16_t* block, int valid, int wave, int lane,
-                                           uint32_t lane_off) {
+// The same copy of the first ROWS (64 or 32) rows of a block by NW = 4 or 8
+// waves (load_chunk_posN): each wave issues ROWS CH / (64 NW) instructions;
+// instruction n of a block of contiguous rows with every row valid fetches
+// lane_off + 1024 NW n into LDS byte lds0 + 1024 NW n (lds0 = tile + 1024
+// wave).  Otherwise (a partial block, or rows `pitch` bytes apart) row
+// row0 + RSTEP n is fetched with the row clamped: rows at or past `valid`
+// repeat row valid - 1, as in load_tile.
+template <int D, int SW, int ROWS, int NW>
+__device__ __forceinline__ void load_tile_n(uint32_t lds0, const uint16_t* block, int valid, int wave, int lane,
+                                            uint32_t lane_off, uint32_t pitch = 2u * D) {
     constexpr int CH = D / 8;
-    constexpr int NI = ROWS * CH / 256;  // instructions per wave
-    constexpr int RSTEP = 256 / CH;      // rows between a lane's instructions
-    static_assert(NI >= 1 && NI * 256 == ROWS * CH, "tile rows must fill whole instructions");
+    constexpr int NI = ROWS * CH / (64 * NW);  // instructions per wave
+    constexpr int RSTEP = 64 * NW / CH;        // rows between a lane's instructions
+    static_assert(NI >= 1 && NI * 64 * NW == ROWS * CH, "tile rows must fill whole instructions");
+    static_assert(RSTEP % 16 == 0, "the swizzle must not change between a lane's instructions");
     const char* base = (const char*)uniform_ptr(block);
-    if (valid >= ROWS) {
+    if (valid >= ROWS && pitch == 2u * D) {
 #pragma unroll
-        for (int n = 0; n < NI; ++n) dma_16B(base + 4096 * n, lane_off, lds0 + 4096u * n);
+        for (int n = 0; n < NI; ++n) dma_16B(base + 1024 * NW * n, lane_off, lds0 + 1024u * NW * n);
     } else {
-        const int p0 = load_chunk_pos4(0, wave, lane);
+        const int p0 = load_chunk_posN<NW>(0, wave, lane);
         const int row0 = p0 / CH;
         const int c0 = (p0 % CH) ^ tile_swz<CH, SW>(row0);
 #pragma unroll
         for (int n = 0; n < NI; ++n) {
             const int r = min(row0, valid - 1 - RSTEP * n) + RSTEP * n;
-            dma_16B(base, (uint32_t)(r * CH * 16 + 16 * c0), lds0 + 4096u * n);
+            dma_16B(base, (uint32_t)r * pitch + 16u * c0, lds0 + 1024u * NW * n);
         }
     }
+}
+
+template <int D, int SW, int ROWS>
+__device__ __forceinline__ void load_tile4(uint32_t lds0, const uint16_t* block, int valid, int wave, int lane,
+                                           uint32_t lane_off) {
+    load_tile_n<D, SW, ROWS, 4>(lds0, block, valid, wave, lane, lane_off);
 }
 
 }  // namespace attn

@@ -69,16 +69,28 @@ __host__ __device__ inline int tile_off(int row, int c, int swz) {
 // (p % CH) ^ swz(p / CH) of row p / CH.
 __host__ __device__ inline int load_chunk_pos(int n, int wave, int lane) { return (2 * n + wave) * 64 + lane; }
 
-// The same for a tile copied by four waves: instruction n of wave w fills LDS
-// chunks p = (4 n + w) * 64 + lane.  Rows per instruction step: 256 / CH, so
-// the swizzle (low 4 row bits) seen by a lane is the same for every n.
-__host__ __device__ inline int load_chunk_pos4(int n, int wave, int lane) { return (4 * n + wave) * 64 + lane; }
+// The same for a tile copied by NW = 4 or 8 waves: instruction n of wave w
+// fills LDS chunks p = (NW n + w) * 64 + lane.  Rows per instruction step:
+// 64 NW / CH (16, 32 or 64), so the swizzle (low 4 row bits) seen by a lane
+// is the same for every n.
+template <int NW>
+__host__ __device__ inline int load_chunk_posN(int n, int wave, int lane) {
+    return (NW * n + wave) * 64 + lane;
+}
+__host__ __device__ inline int load_chunk_pos4(int n, int wave, int lane) { return load_chunk_posN<4>(n, wave, lane); }
 
-template <int CH, int SW>
-__host__ __device__ inline int lane_src_offset4(int wave, int lane) {
-    const int p = load_chunk_pos4(0, wave, lane);
+// Byte offset, inside a block of contiguous rows, of the chunk that copy
+// instruction 0 of (wave, lane) fetches; instruction n fetches the one
+// 1024 NW n bytes further.
+template <int CH, int SW, int NW>
+__host__ __device__ inline int lane_src_offsetN(int wave, int lane) {
+    const int p = load_chunk_posN<NW>(0, wave, lane);
     const int row = p / CH;
     return row * CH * 16 + 16 * ((p % CH) ^ tile_swz<CH, SW>(row));
+}
+template <int CH, int SW>
+__host__ __device__ inline int lane_src_offset4(int wave, int lane) {
+    return lane_src_offsetN<CH, SW, 4>(wave, lane);
 }
 
 // Byte offset, inside a full 64-row block of the source tensor, of the chunk

@@ -7,6 +7,12 @@
 // Work decomposition (gfx950, 64-wide waves, bf16 MFMA 32x32x16):
 //   * one workgroup = 2 waves = one 64-token query block of one head; wave w
 //     owns query rows 32w .. 32w+31 and keeps its Q fragment in registers;
+//   * with VSA blocks of 128 or 256 tokens (dense layouts) the 64-token query
+//     blocks of one VSA block share its block list: one workgroup of 4 waves
+//     serves two of them, copies each selected KV tile into LDS once (each
+//     wave issues a quarter of the copy) and both wave pairs read it, which
+//     halves the L2 -> LDS traffic (sharing among all four blocks of a
+//     256-token VSA block in one 8-wave workgroup measured slower);
 //   * scores are computed transposed, S^T = K Q^T, so the accumulator layout
 //     of v_mfma_f32_32x32x16_bf16 gives every lane ONE query column and 32
 //     of its KV tokens: the running max and sum of the online softmax stay
@@ -37,7 +43,7 @@ namespace {
 
 using namespace attn;
 
-constexpr int kAttnThreads = 128;
+constexpr int kAttnThreads = 128;  // per 64-token query block
 // Workgroups resident on one XCD at a time (32 CUs x 4 workgroups).  Query
 // block i starts its walk over its block list at entry (i mod kSweep) * n /
 // kSweep and wraps around, so the workgroups running together on an XCD read
@@ -62,15 +68,20 @@ struct CombineArgs {
                             // query row in exp2 units of the scaled scores
 };
 
-template <int D, int CMODE>
-__global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
+// R = 64-token query blocks per workgroup: 1, or 2 for dense problems with
+// 128- or 256-token VSA blocks (blocks 2J and 2J + 1 then lie in one VSA
+// block and share its list).  Two waves per SIMD.
+template <int D, int CMODE, int R>
+__global__ __launch_bounds__(kAttnThreads * R, 2) void sparse_attn_kernel(
     DevProblem P, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int* __restrict__ idx, const int* __restrict__ num,
     uint16_t* __restrict__ out, float c_log2, CombineArgs C) {
+    static_assert(R == 1 || R == 2, "1 or 2 query blocks per workgroup");
     constexpr int KS = D / 16;      // MFMA k-steps over d for S^T
     constexpr int DT = D / 32;      // 32-row d tiles of O^T
     constexpr int CH = D / 8;       // 16-byte chunks per token row
-    constexpr int LOADS = CH / 2;   // direct-load instructions per wave per tile
+    constexpr int NW = 2 * R;       // waves sharing (and copying) each tile
+    constexpr int LOADS = CH / NW;  // direct-load instructions per wave per tile
     // The running max is only moved when a block's max exceeds it by more than
     // kLazy (in log2 units): probabilities then stay <= 2^kLazy, far from any
     // float32/bf16 range limit, and most blocks skip the rescale entirely.
@@ -78,10 +89,26 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     __shared__ __attribute__((aligned(1024))) uint16_t k_tile[kBlock * D];
     __shared__ __attribute__((aligned(1024))) uint16_t v_tile[kBlock * D];
 
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;  // 0 .. 2R-1
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+
     // ---- which query block -------------------------------------------------
     int s, h, i;
     SeqView sv;
-    if (!P.packed) {
+    if (R > 1) {  // dense, 64-token query blocks 2J and 2J + 1 of one VSA block
+        const int nJ = (P.nQ + 1) / 2;
+        const int N = nJ * P.H * P.nseq;
+        const int lin = xcd_remap(blockIdx.x, N);
+        const int J = lin % nJ;
+        const int rest = lin / nJ;
+        h = rest % P.H;
+        s = rest / P.H;
+        sv = seq_view(P, s, h);
+        i = 2 * J + (wave >> 1);  // this wave pair's query block (may be past the end)
+    } else if (!P.packed) {
         const int N = P.nQ * P.H * P.nseq;
         const int lin = xcd_remap(blockIdx.x, N);
         i = lin % P.nQ;
@@ -99,7 +126,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
         i = g - sv.qblk0;
         if (i < 0 || i >= sv.nq) return;  // block outside every sequence
     }
-    const int qsize = q_block_size(P, sv, i);
+    // a query block past the end of the sequence (last VSA block) has no rows;
+    // its waves still take part in the shared copies and barriers
+    const int qsize = (R > 1 && i >= P.nQ) ? 0 : q_block_size(P, sv, i);
     const int64_t qrow0 = sv.qrow_base + (int64_t)kBlock * i;    // row index (lse)
     const int64_t qoff0 = sv.q_off + (int64_t)kBlock * i * sv.q_st;  // element offset of row 0
     // VSA blocks of 64 * ratio tokens (dense layouts): the routing and out_c
@@ -107,14 +136,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     // blocks J ratio .. J ratio + ratio - 1
     const int lr = P.ratio >> 1;  // log2(ratio) for ratio 1, 2, 4
 
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int l32 = lane & 31;
-    const int hh = lane >> 5;
-
     // ---- Q operand: B of S^T, column = query row, k-slots = 8 d values ----
-    const int qr = 32 * wave + l32;
+    const int qr = 32 * (wave & 1) + l32;
     bf16x8 qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -180,11 +203,18 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
         return P.packed ? clampi(bs_kv[j], 1, kBlock) : min(kBlock, P.Skv - kBlock * j);
     };
 
-    // per-lane positions inside the tiles
-    const uint32_t koff0 = (uint32_t)lane_src_offset<CH, kSwzRow>(wave, lane, 0);
-    const uint32_t koff1 = (uint32_t)lane_src_offset<CH, kSwzRow>(wave, lane, 1) - 2048u;
-    const uint32_t voff0 = (uint32_t)lane_src_offset<CH, kSwzTr>(wave, lane, 0);
-    const uint32_t voff1 = (uint32_t)lane_src_offset<CH, kSwzTr>(wave, lane, 1) - 2048u;
+    // per-lane positions inside the tiles (copies by 2 waves: two offsets,
+    // see load_tile; by 4 or 8 waves: one, see load_tile_n)
+    uint32_t koff0, koff1 = 0, voff0, voff1 = 0;
+    if constexpr (R == 1) {
+        koff0 = (uint32_t)lane_src_offset<CH, kSwzRow>(wave, lane, 0);
+        koff1 = (uint32_t)lane_src_offset<CH, kSwzRow>(wave, lane, 1) - 2048u;
+        voff0 = (uint32_t)lane_src_offset<CH, kSwzTr>(wave, lane, 0);
+        voff1 = (uint32_t)lane_src_offset<CH, kSwzTr>(wave, lane, 1) - 2048u;
+    } else {
+        koff0 = (uint32_t)lane_src_offsetN<CH, kSwzRow, NW>(wave, lane);
+        voff0 = (uint32_t)lane_src_offsetN<CH, kSwzTr, NW>(wave, lane);
+    }
     const uint32_t pitch = __builtin_amdgcn_readfirstlane((uint32_t)(2 * sv.kv_st));  // bytes between KV rows
     // this wave's LDS byte base inside each tile
     const uint32_t k_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)k_tile + 1024u * wave);
@@ -241,7 +271,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
             }
             wg_barrier();  // both waves are done with the K tile
         }
-        if (more) load_tile<D, kSwzRow>(k_lds, k + off_n, kvsize_n, wave, lane, koff0, koff1, pitch);
+        if (more) {
+            if constexpr (R == 1) load_tile<D, kSwzRow>(k_lds, k + off_n, kvsize_n, wave, lane, koff0, koff1, pitch);
+            else load_tile_n<D, kSwzRow, kBlock, NW>(k_lds, k + off_n, kvsize_n, wave, lane, koff0, pitch);
+        }
 
         if (cur) {
             // ---- online softmax; acc e of tile mt is token 32 mt + 8 (e/4) + 4 hh + e%4
@@ -313,7 +346,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
             }
             wg_barrier();  // both waves are done with the V tile
         }
-        if (more) load_tile<D, kSwzTr>(v_lds, v + off_n, kvsize_n, wave, lane, voff0, voff1, pitch);
+        if (more) {
+            if constexpr (R == 1) load_tile<D, kSwzTr>(v_lds, v + off_n, kvsize_n, wave, lane, voff0, voff1, pitch);
+            else load_tile_n<D, kSwzTr, kBlock, NW>(v_lds, v + off_n, kvsize_n, wave, lane, voff0, pitch);
+        }
 
         first = false;
         j = jn;
@@ -406,19 +442,33 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     }
 }
 
+template <int D, int CMODE, int R>
+hipError_t launch_r(const DevProblem& P, unsigned grid, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    const int* idx, const int* num, uint16_t* out, float c, const CombineArgs& C, hipStream_t st) {
+    hipLaunchKernelGGL((sparse_attn_kernel<D, CMODE, R>), dim3(grid), dim3(kAttnThreads * R), 0, st, P, q, k, v, idx,
+                       num, out, c, C);
+    return hipGetLastError();
+}
+
+template <int D, int CMODE>
+hipError_t launch_d(const DevProblem& P, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int* idx,
+                    const int* num, uint16_t* out, float c, const CombineArgs& C, hipStream_t st) {
+    // dense problems with 128/256-token VSA blocks: one workgroup per pair of
+    // 64-token query blocks
+    const bool pairs = !P.packed && P.ratio >= 2;
+    const int64_t N = P.packed ? (int64_t)P.total_q * P.H
+                               : (int64_t)(pairs ? (P.nQ + 1) / 2 : P.nQ) * P.H * P.nseq;
+    if (N <= 0 || N > 0x7fffffff) return hipErrorInvalidValue;
+    if (pairs) return launch_r<D, CMODE, 2>(P, (unsigned)N, q, k, v, idx, num, out, c, C, st);
+    return launch_r<D, CMODE, 1>(P, (unsigned)N, q, k, v, idx, num, out, c, C, st);
+}
+
 template <int CMODE>
 hipError_t launch_mode(const DevProblem& P, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const int* idx, const int* num, uint16_t* out, const CombineArgs& C, hipStream_t st) {
-    const int64_t N = P.packed ? (int64_t)P.total_q * P.H : (int64_t)P.nQ * P.H * P.nseq;
-    if (N <= 0 || N > 0x7fffffff) return hipErrorInvalidValue;
     const float c = (float)(1.4426950408889634 / sqrt((double)P.D));
-    if (P.D == 128)
-        hipLaunchKernelGGL((sparse_attn_kernel<128, CMODE>), dim3((unsigned)N), dim3(kAttnThreads), 0, st, P, q,
-                           k, v, idx, num, out, c, C);
-    else
-        hipLaunchKernelGGL((sparse_attn_kernel<64, CMODE>), dim3((unsigned)N), dim3(kAttnThreads), 0, st, P, q,
-                           k, v, idx, num, out, c, C);
-    return hipGetLastError();
+    if (P.D == 128) return launch_d<128, CMODE>(P, q, k, v, idx, num, out, c, C, st);
+    return launch_d<64, CMODE>(P, q, k, v, idx, num, out, c, C, st);
 }
 
 }  // namespace
