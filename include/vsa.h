@@ -309,13 +309,16 @@ int vsa_forward_varlen(const vsa_bf16 *q, const vsa_bf16 *k, const vsa_bf16 *v,
  * attention improvements: block-sparse attention forward and backward.)
  * The backward is the gradient of the forward with the routing (q2k_idx)
  * held fixed: the top-k choice is piecewise constant and carries none.
+ * Both take every problem the forward takes: DENSE and BSHD tensors with
+ * VSA blocks of 64, 128 or 256 tokens, PACKED with 64.
  */
 
 /*
  * vsa_sparse_attn_combine_train - vsa_sparse_attn_combine that also writes
  * out_s, the bf16 normalised block-sparse attention output on its own (query
  * layout, padding slots of PACKED written with 0), and lse, float32, one per
- * query row ([B, H, Sq] DENSE, [H, 64*Nq] PACKED, padding slots not written):
+ * query row ([B, H, Sq] for DENSE and for BSHD, [H, 64*Nq] PACKED, padding
+ * slots not written):
  * log2 of the softmax denominator of the row in units where the row's
  * probabilities are exp2(s * log2(e) / sqrt(D) - lse) for raw scores s = q.k
  * (-inf for a row whose list holds no valid block).  Arguments, checks and
@@ -332,11 +335,11 @@ int vsa_sparse_attn_combine_train(const vsa_problem *problem, const vsa_bf16 *q,
 /*
  * vsa_backward_workspace_size - bytes of device workspace vsa_backward needs:
  * float64 block means of Q, K, V and their gradients, the coarse output
- * gradient, two float64 block-level matrices (query blocks x the most KV
- * blocks of a sequence: the coarse softmax and its score gradient), 128 float32
- * row statistics per query block and the inverse routing (KV blocks x the
- * most query blocks of a sequence, int32).  Returns 0 when the problem is
- * invalid.
+ * gradient (one row per VSA block), two float64 block-level matrices (VSA
+ * query blocks x the most VSA KV blocks of a sequence: the coarse softmax and
+ * its score gradient), 128 float32 row statistics per 64-token query block
+ * and the inverse routing (64-token KV blocks x the most 64-token query
+ * blocks of a sequence, int32).  Returns 0 when the problem is invalid.
  */
 size_t vsa_backward_workspace_size(const vsa_problem *problem);
 
@@ -351,9 +354,11 @@ size_t vsa_backward_workspace_size(const vsa_problem *problem);
  * padding slots are not read).
  * Outputs (bf16, written in full, PACKED padding slots with 0): dq in the
  * query layout, dk and dv in the KV layout, and for a gate dgate, contiguous
- * in the query layout whatever gate_strides were: [B, H, Sq] / [H, 64*Nq]
- * for VSA_GATE_TOKEN, the same with a trailing D for VSA_GATE_FULL (NULL and
- * unused for VSA_GATE_NONE).
+ * in the query layout whatever gate_strides were: [B, H, Sq] (BSHD:
+ * [B, Sq, H]) / [H, 64*Nq] for VSA_GATE_TOKEN, the same with a trailing D for
+ * VSA_GATE_FULL (NULL and unused for VSA_GATE_NONE).  With VSA blocks of 128
+ * or 256 tokens the gradients through the block means spread dQc, dKc, dVc
+ * over the valid tokens of each VSA block.
  * Arithmetic: the coarse branch and the gradients through the block means
  * in float64; the block-sparse part as bf16 matrix products with float32
  * accumulation (probabilities recomputed from lse, rounded to bf16 as

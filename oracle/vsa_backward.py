@@ -96,19 +96,20 @@ def sparse_row_lse2(q, k, idx, block: int = O.BLOCK) -> np.ndarray:
     return out
 
 
-def vsa_backward(q, k, v, topk: int, gate, dout) -> Dict[str, np.ndarray]:
+def vsa_backward(q, k, v, topk: int, gate, dout, block: int = O.BLOCK) -> Dict[str, np.ndarray]:
     """Gradients of ``sum(out * dout)`` with respect to q, k, v and the gate
     (float64 numpy in, float64 numpy out), plus the forward's routing and
-    outputs for reference."""
-    fwd = O.vsa_forward(q, k, v, topk, gate)
+    outputs for reference.  ``block`` is the VSA block size (64, 128 or 256),
+    as in ``vsa_oracle.vsa_forward``."""
+    fwd = O.vsa_forward(q, k, v, topk, gate, block=block)
     t = lambda x: torch.tensor(np.asarray(x, dtype=np.float64), dtype=torch.float64, requires_grad=True)
     tq, tk, tv = t(q), t(k), t(v)
     tg = None if gate is None else t(gate)
-    out, out_c, out_s = forward_torch(tq, tk, tv, tg, fwd["q2k_idx"])
+    out, out_c, out_s = forward_torch(tq, tk, tv, tg, fwd["q2k_idx"], block)
     out.backward(torch.tensor(np.asarray(dout, dtype=np.float64)))
     res = dict(dq=tq.grad.numpy(), dk=tk.grad.numpy(), dv=tv.grad.numpy(),
                dgate=None if tg is None else tg.grad.numpy(),
                out=out.detach().numpy(), out_c=out_c.detach().numpy(), out_s=out_s.detach().numpy(),
                q2k_idx=fwd["q2k_idx"], q2k_num=fwd["q2k_num"], gap=fwd["gap"],
-               max_abs_dot=fwd["max_abs_dot"], lse=sparse_row_lse2(q, k, fwd["q2k_idx"]))
+               max_abs_dot=fwd["max_abs_dot"], lse=sparse_row_lse2(q, k, fwd["q2k_idx"], block))
     return res

@@ -514,6 +514,49 @@ def pin_backward_dense_equivalence(seed=18):
         assert np.allclose(a.grad.numpy(), b_.grad.numpy(), rtol=1e-10, atol=1e-12)
 
 
+def pin_backward_large_blocks(seed=23):
+    """VSA blocks of 128 tokens: the restatement reproduces the oracle's
+    forward (ragged last block, token gate); its gradients match finite
+    differences; with every block selected they are those of torch's dense
+    attention on the tokens and on the 128-token means (avg_pool1d), and the
+    row log-sum-exp is scipy's over the dense scores."""
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(seed)
+    B, H, S, D = 1, 2, 128 * 2 + 37, 8
+    q, k, v = (rng.standard_normal((B, H, S, D)) for _ in range(3))
+    gate = rng.uniform(0, 1, (B, H, S))
+    ref = O.vsa_forward(q, k, v, 2, gate, block=128)
+    out, out_c, out_s = BW.forward_torch(_t64(q), _t64(k), _t64(v), _t64(gate), ref["q2k_idx"], 128)
+    assert np.allclose(out.detach().numpy(), ref["out"], rtol=1e-12, atol=1e-13)
+    assert np.allclose(out_c.detach().numpy(), ref["out_c"], rtol=1e-12, atol=1e-13)
+
+    Sg, Dg = 128 + 6, 3
+    qg, kg, vg = (rng.standard_normal((1, 1, Sg, Dg)) for _ in range(3))
+    gg = rng.uniform(0.2, 0.8, (1, 1, Sg))
+    idx = O.vsa_forward(qg, kg, vg, 1, gg, block=128)["q2k_idx"]
+    w = _t64(rng.standard_normal((1, 1, Sg, Dg)))
+    f = lambda a, b_, c, g: (BW.forward_torch(a, b_, c, g, idx, 128)[0] * w).sum()
+    assert torch.autograd.gradcheck(f, (_t64(qg, True), _t64(kg, True), _t64(vg, True), _t64(gg, True)),
+                                    eps=1e-6, atol=1e-7, rtol=1e-5)
+
+    S3 = 128 * 3
+    q, k, v = (rng.standard_normal((B, H, S3, D)) for _ in range(3))
+    w, wc = rng.standard_normal((B, H, S3, D)), rng.standard_normal((B, H, 3, D))
+    idx = O.vsa_forward(q, k, v, 3, block=128)["q2k_idx"]
+    tq, tk, tv = _t64(q, True), _t64(k, True), _t64(v, True)
+    _, out_c, out_s = BW.forward_torch(tq, tk, tv, None, idx, 128)
+    ((out_s * _t64(w)).sum() + (out_c * _t64(wc)).sum()).backward()
+    rq, rk, rv = _t64(q, True), _t64(k, True), _t64(v, True)
+    ref_s = torch.nn.functional.scaled_dot_product_attention(rq, rk, rv)
+    pool = lambda x: torch.nn.functional.avg_pool1d(x.reshape(B * H, S3, D).transpose(1, 2), 128).transpose(1, 2).reshape(B, H, 3, D)
+    ref_c = torch.nn.functional.scaled_dot_product_attention(pool(rq), pool(rk), pool(rv))
+    ((ref_s * _t64(w)).sum() + (ref_c * _t64(wc)).sum()).backward()
+    for a, b_ in ((tq, rq), (tk, rk), (tv, rv)):
+        assert np.allclose(a.grad.numpy(), b_.grad.numpy(), rtol=1e-10, atol=1e-12)
+    dense = logsumexp(np.einsum("bhsd,bhtd->bhst", q, k) / math.sqrt(D), axis=-1) / math.log(2.0)
+    assert np.allclose(BW.sparse_row_lse2(q, k, idx, 128), dense, rtol=1e-13, atol=1e-12)
+
+
 def pin_lse_dense_equivalence(seed=19):
     """Every block selected: the row log-sum-exp is scipy's logsumexp of the
     dense scaled scores, in base 2."""
@@ -605,4 +648,5 @@ ALL_PINS = [
     pin_backward_forward_matches_oracle, pin_backward_gradcheck, pin_backward_dense_equivalence,
     pin_lse_dense_equivalence, pin_lse_reproduces_sparse_output,
     pin_large_blocks_dense_equivalence, pin_large_blocks_by_duplication,
+    pin_backward_large_blocks,
 ]

@@ -208,10 +208,11 @@ E = _abi
     (lambda L: coarse(L, dense(bs=512)), E.VSA_ERR_UNSUPPORTED),
     (lambda L: coarse(L, packed_bs(128)), E.VSA_ERR_UNSUPPORTED),
     (lambda L: coarse(L, dense(bs=128, Skv=128 * 4097)), E.VSA_ERR_UNSUPPORTED),
-    (lambda L: train_fwd(L, dense(bs=128)), E.VSA_ERR_UNSUPPORTED),
-    (lambda L: train_fwd(L, bshd()), E.VSA_ERR_UNSUPPORTED),
-    (lambda L: bwd(L, dense(bs=256)), E.VSA_ERR_UNSUPPORTED),
-    (lambda L: bwd(L, bshd()), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: train_fwd(L, dense(bs=128), lse=None), E.VSA_ERR_NULL),
+    (lambda L: train_fwd(L, bshd(), out_s=O_), E.VSA_ERR_ALIAS),
+    (lambda L: bwd(L, dense(bs=256), wsb=4096), E.VSA_ERR_WORKSPACE),
+    (lambda L: bwd(L, bshd(bs=128), dk=DO_), E.VSA_ERR_ALIAS),
+    (lambda L: bwd(L, packed_bs(128)), E.VSA_ERR_UNSUPPORTED),
     (lambda L: L.vsa_forward_bshd(A, B_, C_, None, 0, None, O_, None, None, None, 1, 2, 1000, 1000, 128, 32, 3, W_,
                                   1 << 40, None), E.VSA_ERR_UNSUPPORTED),
     (lambda L: L.vsa_forward_bshd(A, B_, C_, None, 0, None, A, None, None, None, 1, 2, 1000, 1000, 128, 128, 3, W_,
@@ -345,6 +346,17 @@ def test_backward_workspace(lib):
         assert floor <= ws <= floor + 13 * 256, (S, ws, floor)
     assert lib.vsa_backward_workspace_size(ctypes.byref(packed())) > 0
     assert lib.vsa_backward_workspace_size(ctypes.byref(dense(bs=32))) == 0
+    # VSA blocks of 128 / 256 tokens: the coarse data per VSA block, the row
+    # statistics and the inverse lists per 64-token block; BSHD the same
+    for bs in (128, 256):
+        S = 64 * 242
+        nb64, nbv = S // 64, -(-S // bs)
+        qb64, qbv = 56 * nb64, 56 * nbv
+        floor = 8 * qbv * 128 * 7 + 2 * 8 * qbv * nbv + 4 * qb64 * 128 + 4 * qb64 * nb64 + 4 * qb64
+        for p in (dense(B=1, H=56, Sq=S, Skv=S, D=128, topk=32, bs=bs),
+                  bshd(B=1, H=56, Sq=S, Skv=S, D=128, topk=32, bs=bs)):
+            ws = lib.vsa_backward_workspace_size(ctypes.byref(p))
+            assert floor <= ws <= floor + 13 * 256, (bs, ws, floor)
 
 
 def test_layout_maps_on_cpu(tmp_path):

@@ -43,14 +43,17 @@ def check_grad(gpu: np.ndarray, ref: np.ndarray, what: str):
     assert mean <= GRAD_MEAN_REL, f"{what}: mean error {mean:.3e} of the mean gradient > {GRAD_MEAN_REL}"
 
 
-def run_dense_train(q, k, v, gate, dout, topk, dev=G.DEV):
+def run_dense_train(q, k, v, gate, dout, topk, dev=G.DEV, block_size=64, bshd=False):
     """Coarse/top-k, the training forward, the plain fused forward and the
-    backward on dense [B, H, S, D] CPU bf16 tensors; returns CPU results."""
+    backward on dense [B, H, S, D] CPU bf16 tensors; returns CPU results in
+    [B, H, S(, D)].  With ``bshd`` the tensors go to the library as
+    [B, S, H, D] (gate [B, S, H(, D)]) and come back transposed."""
     B, H, Sq, D = q.shape
     Skv = k.shape[2]
-    q, k, v, dout = (t.to(dev) for t in (q, k, v, dout))
-    gate = None if gate is None else gate.to(dev)
-    prob = vsa.dense_problem(B, H, Sq, Skv, D, topk)
+    conv = G.to_bshd if bshd else (lambda t: t)
+    q, k, v, dout = (conv(t).to(dev) for t in (q, k, v, dout))
+    gate = None if gate is None else conv(gate).to(dev)
+    prob = vsa.dense_problem(B, H, Sq, Skv, D, topk, block_size, bshd)
     cs, isz, ns = vsa.block_shapes(prob)
     out_c = torch.empty(cs, dtype=torch.float32, device=dev)
     idx = torch.empty(isz, dtype=torch.int32, device=dev)
@@ -66,17 +69,19 @@ def run_dense_train(q, k, v, gate, dout, topk, dev=G.DEV):
     dg = None if gate is None else torch.empty(gate.shape, dtype=torch.bfloat16, device=dev)
     vsa.vsa_backward(prob, q, k, v, idx, num, out_c, gate, out_s, lse, dout, dq, dk, dv, dg)
     torch.cuda.synchronize()
-    cpu = lambda t: None if t is None else t.cpu()
-    return dict(out=cpu(out), out_plain=cpu(out_plain), out_s=cpu(out_s), lse=cpu(lse), q2k_idx=cpu(idx),
-                q2k_num=cpu(num), dq=cpu(dq), dk=cpu(dk), dv=cpu(dv), dgate=cpu(dg))
+    back = G.from_bshd if bshd else (lambda t: t)
+    cpu = lambda t: None if t is None else back(t.cpu())
+    return dict(out=cpu(out), out_plain=cpu(out_plain), out_s=cpu(out_s), lse=lse.cpu(), q2k_idx=idx.cpu(),
+                q2k_num=num.cpu(), dq=cpu(dq), dk=cpu(dk), dv=cpu(dv), dgate=cpu(dg), out_c=out_c.cpu())
 
 
-def check_dense_case(q, k, v, gate, topk, seed, tag):
-    G.note(f"case {tag}: q {tuple(q.shape)} kv {tuple(k.shape)} topk={topk} "
+def check_dense_case(q, k, v, gate, topk, seed, tag, block_size=64, bshd=False):
+    G.note(f"case {tag}: q {tuple(q.shape)} kv {tuple(k.shape)} topk={topk} block={block_size} bshd={bshd} "
            f"gate={'none' if gate is None else tuple(gate.shape)}")
     dout = synth.output_grad(q.shape, seed)
-    gpu = run_dense_train(q, k, v, gate, dout, topk)
-    ref = BW.vsa_backward(N.f64(q), N.f64(k), N.f64(v), topk, None if gate is None else N.f64(gate), N.f64(dout))
+    gpu = run_dense_train(q, k, v, gate, dout, topk, block_size=block_size, bshd=bshd)
+    ref = BW.vsa_backward(N.f64(q), N.f64(k), N.f64(v), topk, None if gate is None else N.f64(gate), N.f64(dout),
+                          block=block_size)
     G.assert_tie_free(ref)
     G.assert_indices_equal(gpu["q2k_idx"], gpu["q2k_num"], ref)
     assert torch.equal(gpu["out"], gpu["out_plain"]), "training forward changed the output bits"
@@ -200,6 +205,53 @@ def test_backward_varlen_matches_per_sequence():
         assert (dk[:, okv + skv:okv + 64 * nkv] == 0).all() and (dv[:, okv + skv:okv + 64 * nkv] == 0).all()
         oq += 64 * nq
         okv += 64 * nkv
+
+
+# ---------------------------------------------------------------------------
+# VSA blocks of 128 / 256 tokens and [B, S, H, D] tensors
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("block,B,H,Sq,Skv,D,topk,gate", [
+    (128, 1, 2, 128 * 3 + 37, 128 * 3 + 37, 128, 2, "token"),  # ragged 37-token last VSA block
+    (128, 2, 1, 128 * 2 + 70, 128 * 4 + 9, 64, 2, "full"),     # Sq != Skv, full gate, D = 64
+    (256, 1, 2, 256 * 2 + 100, 256 * 2 + 100, 128, 1, "token"),  # top-1, 100-token tail (2 sub-blocks)
+    (256, 1, 1, 256 * 3, 256 * 3 - 30, 64, 3, None),           # every VSA block selected
+])
+def test_backward_large_vsa_blocks(block, B, H, Sq, Skv, D, topk, gate):
+    inp = synth.dense_inputs(B, H, Sq, D, topk, seed=2500 + block + Sq, gated=gate == "token", S_kv=Skv)
+    g = inp.gate if gate == "token" else (synth.full_gate((B, H, Sq, D), 2501 + Sq) if gate == "full" else None)
+    check_dense_case(inp.q, inp.k, inp.v, g, topk, 2502 + Sq, f"block {block}", block_size=block)
+
+
+@pytest.mark.parametrize("block,gate", [(64, "token"), (128, "full"), (256, None)])
+def test_backward_bshd_matches_dense_bits(block, gate):
+    """[B, S, H, D] tensors through the training forward and the backward give
+    the bits of the [B, H, S, D] path (the same kernels, strided rows), and
+    both match the oracle."""
+    B, H, Sq, Skv, D = 2, 3, 64 * 5 + 17, 64 * 6 + 40, 128
+    inp = synth.dense_inputs(B, H, Sq, D, 2, seed=2600 + block, gated=gate == "token", S_kv=Skv)
+    g = inp.gate if gate == "token" else (synth.full_gate((B, H, Sq, D), 2601) if gate == "full" else None)
+    gpu_b, _ = check_dense_case(inp.q, inp.k, inp.v, g, 2, 2602, f"bshd block {block}", block_size=block, bshd=True)
+    dout = synth.output_grad(inp.q.shape, 2602)
+    gpu_d = run_dense_train(inp.q, inp.k, inp.v, g, dout, 2, block_size=block)
+    for key in ("out", "out_s", "lse", "q2k_idx", "q2k_num", "dq", "dk", "dv", "out_c") + (("dgate",) if g is not None else ()):
+        assert torch.equal(gpu_b[key], gpu_d[key]), key
+
+
+def test_autograd_large_blocks_bshd():
+    """video_sparse_attn with 128-token VSA blocks on [B, S, H, D] tensors:
+    the autograd gradients are the entry points' bits."""
+    B, H, S, D = 1, 2, 128 * 3 + 20, 64
+    inp = synth.dense_inputs(B, H, S, D, 2, seed=2700, gated=True)
+    dout = synth.output_grad(inp.q.shape, 2701)
+    ref = run_dense_train(inp.q, inp.k, inp.v, inp.gate, dout, 2, block_size=128, bshd=True)
+    q, k, v, g = (G.to_bshd(t).to(G.DEV).requires_grad_(True) for t in (inp.q, inp.k, inp.v, inp.gate))
+    out = vsa.video_sparse_attn(q, k, v, 2, g, block_size=128, bshd=True)
+    out.backward(G.to_bshd(dout).to(G.DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(G.from_bshd(out.detach().cpu()), ref["out"])
+    for t, name in ((q, "dq"), (k, "dk"), (v, "dv"), (g, "dgate")):
+        assert torch.equal(G.from_bshd(t.grad.cpu()), ref[name]), name
 
 
 # ---------------------------------------------------------------------------

@@ -204,6 +204,11 @@ def _sparse_stride_64(q_rows, k, v, kv_sizes, idx, block=64):
     return _orig_sparse_block(q_rows, k, v, kv_sizes, idx, 64)
 
 
+def _bw_blocks_64(q, k, v, gate, idx, block=64):
+    # the restatement ignores the VSA block size (pools and attends 64-token blocks)
+    return _forward_torch_ok(q, k, v, gate, idx, 64)
+
+
 MISTAKES = {
     "sparse_scale_dropped": ("sparse_block", _sparse_no_scale),
     "pool_divides_by_64": ("pool", _pool_div64),
@@ -228,6 +233,7 @@ MISTAKES = {
     "block_sizes_ignore_block": ("block_sizes", _block_sizes_always_64),
     "pool_blocks_64_apart": ("pool", _pool_stride_64),
     "sparse_blocks_64_apart": ("sparse_block", _sparse_stride_64),
+    "backward_ignores_block_size": ("backward.forward_torch", _bw_blocks_64),
 }
 
 

@@ -255,6 +255,10 @@ def vsa_combine(problem: VsaProblem, out_c, gate, out) -> None:
 # ---------------------------------------------------------------------------
 
 def lse_shape(problem: VsaProblem):
+    """[B, H, Sq] for both dense layouts (also for [B, S, H, D] tensors),
+    [H, slots] packed."""
+    if problem.layout in (VSA_LAYOUT_DENSE, VSA_LAYOUT_BSHD):
+        return (problem.batch, problem.heads, problem.seqlen_q)
     return token_shapes(problem)[0][:-1]
 
 
@@ -299,7 +303,8 @@ def vsa_backward(problem: VsaProblem, q, k, v, q2k_idx, q2k_num, out_c, gate, ou
                  dq, dk, dv, dgate=None, workspace=None) -> None:
     """Gradients of ``sum(out * dout)`` of the forward with these inputs and
     routing (vsa_backward): writes ``dq``, ``dk``, ``dv`` and, with a gate,
-    ``dgate`` (contiguous, the gate's shape)."""
+    ``dgate`` (contiguous, the gate's shape: [B, H, Sq(, D)], or [B, Sq, H(, D)]
+    for a BSHD problem)."""
     _check_qkv(problem, q, k, v)
     cs, isz, ns = block_shapes(problem)
     if tuple(q2k_idx.shape[:-1]) != tuple(isz[:-1]):
@@ -332,9 +337,14 @@ class _VideoSparseAttn(torch.autograd.Function):
     backward = vsa_backward (the routing is held fixed)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, gate, topk):
-        B, H, Sq, D = q.shape
-        problem = dense_problem(B, H, Sq, k.shape[2], D, topk)
+    def forward(ctx, q, k, v, gate, topk, block_size, bshd):
+        if bshd:
+            B, Sq, H, D = q.shape
+            Skv = k.shape[1]
+        else:
+            B, H, Sq, D = q.shape
+            Skv = k.shape[2]
+        problem = dense_problem(B, H, Sq, Skv, D, topk, block_size, bshd)
         q, k, v = q.detach(), k.detach(), v.detach()
         g = None if gate is None else gate.detach()
         cs, isz, ns = block_shapes(problem)
@@ -347,7 +357,7 @@ class _VideoSparseAttn(torch.autograd.Function):
         out_s = torch.empty_like(q)
         lse = torch.empty(lse_shape(problem), dtype=torch.float32, device=dev)
         vsa_sparse_attn_combine_train(problem, q, k, v, idx, num, out_c, g, out, out_s, lse)
-        ctx.topk = topk
+        ctx.problem = problem
         ctx.has_gate = g is not None
         ctx.save_for_backward(q, k, v, *( [g] if g is not None else []), idx, num, out_c, out_s, lse)
         ctx.mark_non_differentiable(idx, num)
@@ -359,23 +369,24 @@ class _VideoSparseAttn(torch.autograd.Function):
         q, k, v = saved[:3]
         g = saved[3] if ctx.has_gate else None
         idx, num, out_c, out_s, lse = saved[4 if ctx.has_gate else 3:]
-        B, H, Sq, D = q.shape
-        problem = dense_problem(B, H, Sq, k.shape[2], D, ctx.topk)
         dout = dout.contiguous()
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         dg = None if g is None else torch.empty(g.shape, dtype=torch.bfloat16, device=q.device)
-        vsa_backward(problem, q, k, v, idx, num, out_c, g, out_s, lse, dout, dq, dk, dv, dg)
-        return dq, dk, dv, dg, None
+        vsa_backward(ctx.problem, q, k, v, idx, num, out_c, g, out_s, lse, dout, dq, dk, dv, dg)
+        return dq, dk, dv, dg, None, None, None
 
 
 def video_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int,
-                      gate: Optional[torch.Tensor] = None, return_routing: bool = False):
-    """Differentiable VSA on dense ``[B, H, S, D]`` bf16 tensors: the forward of
-    ``vsa_forward`` and, through autograd, the gradients of q, k, v and the
-    gate (``[B, H, Sq]`` or ``[B, H, Sq, D]``) from vsa_backward."""
+                      gate: Optional[torch.Tensor] = None, return_routing: bool = False, *,
+                      block_size: int = BLOCK, bshd: bool = False):
+    """Differentiable VSA on dense ``[B, H, S, D]`` bf16 tensors (``[B, S, H, D]``
+    with ``bshd``): the forward of ``vsa_forward`` and, through autograd, the
+    gradients of q, k, v and the gate (``[B, H, Sq]`` or ``[B, H, Sq, D]``;
+    ``[B, Sq, H(, D)]`` with ``bshd``) from vsa_backward.  ``block_size``: the
+    VSA block, 64, 128 or 256 tokens."""
     if q.dim() != 4:
-        raise ValueError("q must be [B, H, S, D]")
-    out, idx, num = _VideoSparseAttn.apply(q, k, v, gate, topk)
+        raise ValueError("q must be [B, H, S, D] ([B, S, H, D] with bshd)")
+    out, idx, num = _VideoSparseAttn.apply(q, k, v, gate, topk, block_size, bshd)
     return (out, idx, num) if return_routing else out
 
 

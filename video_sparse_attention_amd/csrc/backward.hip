@@ -66,7 +66,8 @@ __device__ __forceinline__ int seq_of_kvblock(const DevProblem& P, int g) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. combine backward: grid (query blocks: nQ or total_q, H, B or 1)
+// 1. combine backward: grid (VSA blocks: nQB or total_q, H, B or 1); the
+// workgroup walks the VSA block's 64-token query blocks in order
 // ---------------------------------------------------------------------------
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
@@ -75,88 +76,97 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
     const float* __restrict__ lse, float* __restrict__ rs, double* __restrict__ doc, uint16_t* __restrict__ dgate) {
     constexpr int QD = D / 4;  // d values per thread, 4 threads per token
     __shared__ float red[kBlock][D + 1];
-    int s, i;
+    int s, I;
     const int h = blockIdx.y;
     if (!P.packed) {
-        i = blockIdx.x;
+        I = blockIdx.x;
         s = blockIdx.z;
     } else {
         s = seq_of_qblock(P, blockIdx.x);
-        i = (int)blockIdx.x - clampi(P.cu_q[s], 0, P.total_q);
+        I = (int)blockIdx.x - clampi(P.cu_q[s], 0, P.total_q);
     }
     const SeqView sv = seq_view(P, s, h);
-    if (i < 0 || i >= sv.nq) return;
-    const int size = q_block_size(P, sv, i);
-    const int64_t row0 = sv.qrow_base + (int64_t)kBlock * i;
-    const int64_t qb = sv.qblk_base + i;
-    // token index of the block's first row along the gate's token axis
-    const int64_t tok0 = (int64_t)kBlock * (P.packed ? sv.qblk0 + i : i);
+    const int R = P.packed ? 1 : P.ratio;  // 64-token query blocks per VSA block
+    if (I < 0 || R * I >= sv.nq) return;
+    // row of the VSA block in the block-resolution arrays (out_c, dOc)
+    const int64_t cb = P.packed ? sv.qblk_base + I : ((int64_t)s * P.H + h) * P.nQB + I;
     const int64_t g0 = (P.packed ? 0 : (int64_t)s * gs0) + (int64_t)h * gs1;
     const int t = threadIdx.x / 4, d0 = (threadIdx.x % 4) * QD;
-    const float* ocr = out_c + qb * D;
-    float dpart = 0.f, gpart = 0.f;
-    float contrib[QD];
+    const float* ocr = out_c + cb * D;
+    double dsum = 0.0;  // thread d < D: dOc[d] summed over the VSA block's tokens
+    for (int r = 0; r < R; ++r) {
+        const int i = R * I + r;
+        if (i >= sv.nq) break;  // the same for every thread
+        const int size = q_block_size(P, sv, i);
+        const int64_t row0 = sv.qrow_base + (int64_t)kBlock * i;  // row of token 0 in [.., S] arrays (lse)
+        const int64_t qb = sv.qblk_base + i;                       // 64-token block (statistics)
+        // token index of the block's first row along the gate's token axis
+        const int64_t tok0 = (int64_t)kBlock * (P.packed ? sv.qblk0 + i : i);
+        // element offset of token t of this block in dout / out_s / a full dgate
+        const int64_t qo = sv.q_off + ((int64_t)kBlock * i + t) * sv.q_st;
+        float dpart = 0.f, gpart = 0.f;
+        float contrib[QD];
 #pragma unroll
-    for (int e = 0; e < QD; ++e) contrib[e] = 0.f;
-    if (t < size) {
-        const int64_t r = row0 + t;
-        const int64_t goff = g0 + (tok0 + t) * gs2;
-        const float g = MODE == VSA_GATE_TOKEN ? bf16_lo(gate[goff]) : 1.f;
+        for (int e = 0; e < QD; ++e) contrib[e] = 0.f;
+        if (t < size) {
+            const int64_t goff = g0 + (tok0 + t) * gs2;
+            const float g = MODE == VSA_GATE_TOKEN ? bf16_lo(gate[goff]) : 1.f;
 #pragma unroll
-        for (int c = 0; c < QD / 8; ++c) {
-            const uint4 a = *reinterpret_cast<const uint4*>(dout + r * D + d0 + 8 * c);
-            const uint4 o = *reinterpret_cast<const uint4*>(out_s + r * D + d0 + 8 * c);
-            uint4 gg = make_uint4(0, 0, 0, 0);
-            if (MODE == VSA_GATE_FULL) gg = *reinterpret_cast<const uint4*>(gate + goff + d0 + 8 * c);
-            const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, ow[4] = {o.x, o.y, o.z, o.w};
-            const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
-            uint32_t dg[4];
+            for (int c = 0; c < QD / 8; ++c) {
+                const uint4 a = *reinterpret_cast<const uint4*>(dout + qo + d0 + 8 * c);
+                const uint4 o = *reinterpret_cast<const uint4*>(out_s + qo + d0 + 8 * c);
+                uint4 gg = make_uint4(0, 0, 0, 0);
+                if (MODE == VSA_GATE_FULL) gg = *reinterpret_cast<const uint4*>(gate + goff + d0 + 8 * c);
+                const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, ow[4] = {o.x, o.y, o.z, o.w};
+                const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
+                uint32_t dg[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int dd = 8 * c + 2 * e;
-                const float a0 = bf16_lo(aw[e]), a1 = bf16_hi(aw[e]);
-                dpart = fmaf(a0, bf16_lo(ow[e]), dpart);
-                dpart = fmaf(a1, bf16_hi(ow[e]), dpart);
-                const float c0 = ocr[d0 + dd], c1 = ocr[d0 + dd + 1];
-                if (MODE == VSA_GATE_FULL) {
-                    contrib[dd] = a0 * bf16_lo(gw[e]);
-                    contrib[dd + 1] = a1 * bf16_hi(gw[e]);
-                    dg[e] = bf16pair(a0 * c0, a1 * c1);
-                } else {
-                    contrib[dd] = a0 * g;
-                    contrib[dd + 1] = a1 * g;
-                    if (MODE == VSA_GATE_TOKEN) gpart = fmaf(a1, c1, fmaf(a0, c0, gpart));
+                for (int e = 0; e < 4; ++e) {
+                    const int dd = 8 * c + 2 * e;
+                    const float a0 = bf16_lo(aw[e]), a1 = bf16_hi(aw[e]);
+                    dpart = fmaf(a0, bf16_lo(ow[e]), dpart);
+                    dpart = fmaf(a1, bf16_hi(ow[e]), dpart);
+                    const float c0 = ocr[d0 + dd], c1 = ocr[d0 + dd + 1];
+                    if (MODE == VSA_GATE_FULL) {
+                        contrib[dd] = a0 * bf16_lo(gw[e]);
+                        contrib[dd + 1] = a1 * bf16_hi(gw[e]);
+                        dg[e] = bf16pair(a0 * c0, a1 * c1);
+                    } else {
+                        contrib[dd] = a0 * g;
+                        contrib[dd + 1] = a1 * g;
+                        if (MODE == VSA_GATE_TOKEN) gpart = fmaf(a1, c1, fmaf(a0, c0, gpart));
+                    }
                 }
+                if (MODE == VSA_GATE_FULL)
+                    *reinterpret_cast<uint4*>(dgate + qo + d0 + 8 * c) = make_uint4(dg[0], dg[1], dg[2], dg[3]);
             }
-            if (MODE == VSA_GATE_FULL)
-                *reinterpret_cast<uint4*>(dgate + r * D + d0 + 8 * c) = make_uint4(dg[0], dg[1], dg[2], dg[3]);
+        } else if (MODE == VSA_GATE_FULL && P.packed) {
+#pragma unroll
+            for (int c = 0; c < QD / 8; ++c)
+                *reinterpret_cast<uint4*>(dgate + qo + d0 + 8 * c) = make_uint4(0, 0, 0, 0);
         }
-    } else if (MODE == VSA_GATE_FULL && P.packed) {
+        // the 4 threads of a token are consecutive lanes
+        dpart += __shfl_xor(dpart, 1);
+        dpart += __shfl_xor(dpart, 2);
+        gpart += __shfl_xor(gpart, 1);
+        gpart += __shfl_xor(gpart, 2);
+        if (threadIdx.x % 4 == 0) {
+            const bool valid = t < size;
+            // padding rows: lse = +inf makes every recomputed probability 0
+            rs[qb * kStatRow + t] = valid ? lse[row0 + t] : INFINITY;
+            rs[qb * kStatRow + kBlock + t] = valid ? dpart : 0.f;
+            // a token gate's gradient in the query layout: element offset / D
+            if (MODE == VSA_GATE_TOKEN && (valid || P.packed))
+                dgate[qo / D] = (uint16_t)(bf16pair(valid ? gpart : 0.f, 0.f) & 0xffffu);
+        }
 #pragma unroll
-        for (int c = 0; c < QD / 8; ++c)
-            *reinterpret_cast<uint4*>(dgate + (row0 + t) * D + d0 + 8 * c) = make_uint4(0, 0, 0, 0);
+        for (int e = 0; e < QD; ++e) red[t][d0 + e] = contrib[e];
+        __syncthreads();
+        for (int d = threadIdx.x; d < D; d += kThreads)
+            for (int tt = 0; tt < size; ++tt) dsum += (double)red[tt][d];
+        __syncthreads();  // red is rewritten by the next 64-token block
     }
-    // the 4 threads of a token are consecutive lanes
-    dpart += __shfl_xor(dpart, 1);
-    dpart += __shfl_xor(dpart, 2);
-    gpart += __shfl_xor(gpart, 1);
-    gpart += __shfl_xor(gpart, 2);
-    if (threadIdx.x % 4 == 0) {
-        const bool valid = t < size;
-        // padding rows: lse = +inf makes every recomputed probability 0
-        rs[qb * kStatRow + t] = valid ? lse[row0 + t] : INFINITY;
-        rs[qb * kStatRow + kBlock + t] = valid ? dpart : 0.f;
-        if (MODE == VSA_GATE_TOKEN && (valid || P.packed))
-            dgate[row0 + t] = (uint16_t)(bf16pair(valid ? gpart : 0.f, 0.f) & 0xffffu);
-    }
-#pragma unroll
-    for (int e = 0; e < QD; ++e) red[t][d0 + e] = contrib[e];
-    __syncthreads();
-    for (int d = threadIdx.x; d < D; d += kThreads) {
-        double acc = 0.0;
-        for (int tt = 0; tt < size; ++tt) acc += (double)red[tt][d];
-        doc[qb * D + d] = acc;
-    }
+    for (int d = threadIdx.x; d < D; d += kThreads) doc[cb * D + d] = dsum;
 }
 
 // ---------------------------------------------------------------------------
@@ -320,14 +330,17 @@ __global__ __launch_bounds__(kThreads) void bwd_k2q_kernel(DevProblem P, const i
     const int j = blockIdx.x * (kThreads / 64) + wave;
     const SeqView sv = seq_view(P, s, h);
     if (j >= sv.nkv) return;
-    const int key = j + sv.idx_rebase;  // as stored in q2k_idx
+    // lists hold VSA blocks of 64 * ratio tokens (dense; 64 when packed)
+    const int lr = P.ratio >> 1;
+    const int key = (j >> lr) + sv.idx_rebase;  // as stored in q2k_idx
     const int64_t kb = sv.kvblk_base + j;
+    const int64_t vbase = P.packed ? sv.qblk_base : ((int64_t)s * P.H + h) * P.nQB;
     int count = 0;
     for (int i0 = 0; i0 < sv.nq; i0 += 64) {
         const int i = i0 + lane;
         bool member = false;
         if (i < sv.nq) {
-            const int64_t qb = sv.qblk_base + i;
+            const int64_t qb = vbase + (i >> lr);  // the list of i's VSA block
             member = list_has(idx + qb * P.idx_row, clampi(num[qb], 0, P.idx_row), key);
         }
         const uint64_t mask = __ballot(member);
@@ -431,15 +444,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void bwd_dq_kernel(
         if (i < 0 || i >= sv.nq) return;
     }
     const int qsize = q_block_size(P, sv, i);
-    const int64_t qrow0 = sv.qrow_base + (int64_t)kBlock * i;
-    const int64_t qb = sv.qblk_base + i;
+    const int64_t qoff0 = sv.q_off + (int64_t)kBlock * i * sv.q_st;  // element offset of the block's row 0
+    const int64_t qb = sv.qblk_base + i;                              // 64-token block (statistics)
+    // VSA blocks of 64 * ratio tokens (dense): the list, out_c and dQc are
+    // per VSA block; a listed VSA block J stands for 64-token KV blocks
+    // J ratio .. J ratio + ratio - 1
+    const int lr = P.ratio >> 1;
+    const int64_t qbv = P.packed ? qb : ((int64_t)s * P.H + h) * P.nQB + (i >> lr);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
     const int qr = 32 * wave + l32;
     const bool qvalid = qr < qsize;
 
     bf16x8 qf[KS], df[KS];
-    load_b_row<KS>(q + (qrow0 + qr) * D, qvalid, hh, qf);
-    load_b_row<KS>(dout + (qrow0 + qr) * D, qvalid, hh, df);
+    load_b_row<KS>(q + qoff0 + qr * sv.q_st, qvalid, hh, qf);
+    load_b_row<KS>(dout + qoff0 + qr * sv.q_st, qvalid, hh, df);
     const float lse = rs[qb * kStatRow + qr];  // +inf for padding rows
     const float delta = rs[qb * kStatRow + kBlock + qr];
 
@@ -449,8 +467,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void bwd_dq_kernel(
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
 
-    const int n = __builtin_amdgcn_readfirstlane(clampi(num[qb], 0, P.idx_row));
-    const_int* list = (const_int*)uniform_ptr(idx + qb * P.idx_row);
+    const int nsel = __builtin_amdgcn_readfirstlane(clampi(num[qbv], 0, P.idx_row));
+    const int n = nsel << lr;  // 64-token KV blocks to visit
+    const_int* list = (const_int*)uniform_ptr(idx + qbv * P.idx_row);
     const_int* bs_kv = (const_int*)(P.packed ? uniform_ptr(P.bs_kv + sv.kvblk0) : nullptr);
     const int rebase = __builtin_amdgcn_readfirstlane(sv.idx_rebase);
     const int nkv = __builtin_amdgcn_readfirstlane(sv.nkv);
@@ -459,7 +478,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void bwd_dq_kernel(
         for (; t < n; ++t) {
             int pos = t0 + t;
             if (pos >= n) pos -= n;
-            const int j = list[pos] - rebase;
+            const int J = list[pos >> lr];
+            // no sequence has 2^28 VSA blocks: such an entry (or a negative
+            // one) is out of range, and is kept from wrapping by the shift
+            if (lr > 0 && (unsigned)J >= (1u << 28)) continue;
+            const int j = (J << lr) + (pos & ((1 << lr) - 1)) - rebase;
             if (j >= 0 && j < nkv) return j;
         }
         return -1;
@@ -482,11 +505,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void bwd_dq_kernel(
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) k_tr[dt][jj] = tr_offset<CH, kSwzDual>(dt, jj, hh, tr_r, tr_d);
+    const uint32_t pitch = __builtin_amdgcn_readfirstlane((uint32_t)(2 * sv.kv_st));  // bytes between KV rows
     auto issue_v = [&](int jj, int vs) {
-        load_tile<D, kSwzDual>(v_lds, v + (sv.kvrow_base + (int64_t)kBlock * jj) * D, vs, wave, lane, off0, off1);
+        load_tile<D, kSwzDual>(v_lds, v + sv.kv_off + (int64_t)kBlock * jj * sv.kv_st, vs, wave, lane, off0, off1,
+                               pitch);
     };
     auto issue_k = [&](int jj, int vs) {
-        load_tile<D, kSwzDual>(k_lds, k + (sv.kvrow_base + (int64_t)kBlock * jj) * D, vs, wave, lane, off0, off1);
+        load_tile<D, kSwzDual>(k_lds, k + sv.kv_off + (int64_t)kBlock * jj * sv.kv_st, vs, wave, lane, off0, off1,
+                               pitch);
     };
 
     // the operands above are in registers before the first direct copy, so
@@ -579,10 +605,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void bwd_dq_kernel(
     }
 
     // lane holds dQ[qr][32 dt + 8 (e / 4) + 4 hh + e % 4]
-    uint16_t* orow = dq + (qrow0 + qr) * D;
+    uint16_t* orow = dq + qoff0 + qr * sv.q_st;
     if (qvalid) {
-        const double* cr = dqc + qb * D;
-        const float inv_size = 1.f / (float)qsize;
+        // the gradient through the block mean: dQc over the VSA block's valid tokens
+        const double* cr = dqc + qbv * D;
+        const int vsize = P.packed ? qsize : min(kBlock << lr, P.Sq - (kBlock << lr) * (i >> lr));
+        const float inv_size = 1.f / (float)vsize;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -664,8 +692,11 @@ __global__ __launch_bounds__(kDkdvThreads, 3) void bwd_dkdv_kernel(
         if (j < 0 || j >= sv.nkv) return;
     }
     const int kvsize = kv_block_size(P, sv, j);
-    const int64_t kvrow0 = sv.kvrow_base + (int64_t)kBlock * j;
-    const int64_t kb = sv.kvblk_base + j;
+    const int64_t kvoff0 = sv.kv_off + (int64_t)kBlock * j * sv.kv_st;  // element offset of the block's row 0
+    const int64_t kb = sv.kvblk_base + j;                               // 64-token block (inverse lists)
+    // dKc / dVc are per VSA block of 64 * ratio tokens (dense)
+    const int lr = P.ratio >> 1;
+    const int64_t kbv = P.packed ? kb : ((int64_t)s * P.H + h) * P.nKVB + (j >> lr);
     // wave, token group and role are wave-uniform: readfirstlane puts them in
     // scalar registers, so role-dependent code is branched over, not selected
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -676,7 +707,7 @@ __global__ __launch_bounds__(kDkdvThreads, 3) void bwd_dkdv_kernel(
 
     // role 0: K^T operand of S = Q K^T; role 1: V^T operand of dP = dO V^T
     bf16x8 bfrag[KS];
-    load_b_row<KS>((role ? v : k) + (kvrow0 + kr) * D, kvalid, hh, bfrag);
+    load_b_row<KS>((role ? v : k) + kvoff0 + kr * sv.kv_st, kvalid, hh, bfrag);
 
     f32x16 dka[DH], dva[DH];
 #pragma unroll
@@ -719,11 +750,12 @@ __global__ __launch_bounds__(kDkdvThreads, 3) void bwd_dkdv_kernel(
     const float4* other_xch = &xch[grp][role ^ 1][0][lane];
 
     // copies of stage (query block i, half hf) into buffer b
+    const uint32_t qpitch = __builtin_amdgcn_readfirstlane((uint32_t)(2 * sv.q_st));  // bytes between query rows
     auto issue = [&](int i, int hf, int b) {
-        const int64_t r0 = sv.qrow_base + (int64_t)kBlock * i + kHalf * hf;
+        const int64_t o0 = sv.q_off + ((int64_t)kBlock * i + kHalf * hf) * sv.q_st;
         const int valid = min(q_size(i) - kHalf * hf, kHalf);
-        load_tile4<D, kSwzDual, kHalf>(q_lds + kTileBytes * b, q + r0 * D, valid, wave, lane, off);
-        load_tile4<D, kSwzDual, kHalf>(o_lds + kTileBytes * b, dout + r0 * D, valid, wave, lane, off);
+        load_tile_n<D, kSwzDual, kHalf, 4>(q_lds + kTileBytes * b, q + o0, valid, wave, lane, off, qpitch);
+        load_tile_n<D, kSwzDual, kHalf, 4>(o_lds + kTileBytes * b, dout + o0, valid, wave, lane, off, qpitch);
         if (wave == 0 && lane < 16)
             dma_16B(uniform_ptr(rs + (sv.qblk_base + i) * kStatRow + kHalf * hf), st_off, st_lds + kStatBytes * b);
     };
@@ -843,12 +875,14 @@ __global__ __launch_bounds__(kDkdvThreads, 3) void bwd_dkdv_kernel(
     }
 
     // lane holds dK / dV [kr][32 (DH role + dt) + 8 (e / 4) + 4 hh + e % 4]
-    uint16_t* krow = dk + (kvrow0 + kr) * D;
-    uint16_t* vrow = dv + (kvrow0 + kr) * D;
+    uint16_t* krow = dk + kvoff0 + kr * sv.kv_st;
+    uint16_t* vrow = dv + kvoff0 + kr * sv.kv_st;
     if (kvalid) {
-        const double* ckr = dkc + kb * D;
-        const double* cvr = dvc + kb * D;
-        const float inv_size = 1.f / (float)kvsize;
+        // the gradient through the block means, over the VSA block's valid tokens
+        const double* ckr = dkc + kbv * D;
+        const double* cvr = dvc + kbv * D;
+        const int vsize = P.packed ? kvsize : min(kBlock << lr, P.Skv - (kBlock << lr) * (j >> lr));
+        const float inv_size = 1.f / (float)vsize;
 #pragma unroll
         for (int dt = 0; dt < DH; ++dt)
 #pragma unroll
@@ -878,9 +912,14 @@ __global__ __launch_bounds__(kDkdvThreads, 3) void bwd_dkdv_kernel(
 template <int D>
 hipError_t launch_all(const DevProblem& P, const BwdArgs& A, hipStream_t st) {
     const int seqs = P.nseq;
-    const int qgrid = P.packed ? P.total_q : P.nQ;
-    const int maxq = P.packed ? P.max_q : P.nQ;
-    const int maxkv = P.packed ? P.max_kv : P.nKV;
+    // the coarse branch works on VSA blocks (64 * ratio tokens, dense), the
+    // attention kernels and the inverse lists on 64-token blocks
+    const DevProblem CP = coarse_view(P);
+    const int qgrid = P.packed ? P.total_q : P.nQB;
+    const int maxq = P.packed ? P.max_q : P.nQB;
+    const int maxkv = P.packed ? P.max_kv : P.nKVB;
+    const int maxq64 = P.packed ? P.max_q : P.nQ;
+    const int maxkv64 = P.packed ? P.max_kv : P.nKV;
     const double scale = 1.0 / sqrt((double)D);
     const float c_log2 = (float)(1.4426950408889634 * scale);
     hipError_t e;
@@ -905,24 +944,24 @@ hipError_t launch_all(const DevProblem& P, const BwdArgs& A, hipStream_t st) {
     // 2. block means
     if ((e = launch_pool(P, A.q, A.k, A.v, A.qc, A.kc, A.vc, st)) != hipSuccess) return e;
     // 3. coarse backward
-    if ((e = launch_coarse_scores(P, A.qc, A.kc, A.pbuf, st)) != hipSuccess) return e;
-    if ((e = launch_coarse_scores(P, A.doc, A.vc, A.dsbuf, st)) != hipSuccess) return e;
+    if ((e = launch_coarse_scores(CP, A.qc, A.kc, A.pbuf, st)) != hipSuccess) return e;
+    if ((e = launch_coarse_scores(CP, A.doc, A.vc, A.dsbuf, st)) != hipSuccess) return e;
     const int64_t crows = (int64_t)seqs * P.H * maxq;
-    hipLaunchKernelGGL(bwd_coarse_softmax_kernel, dim3((unsigned)((crows + 3) / 4)), dim3(kThreads), 0, st, P,
+    hipLaunchKernelGGL(bwd_coarse_softmax_kernel, dim3((unsigned)((crows + 3) / 4)), dim3(kThreads), 0, st, CP,
                        A.pbuf, A.dsbuf, maxkv, maxq, scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_coarse_mm_kernel<D, false>), dim3((maxq + 63) / 64, P.H, seqs), dim3(kThreads), 0, st,
-                       P, A.dsbuf, A.kc, A.dqc, maxkv, maxq, scale);
+                       CP, A.dsbuf, A.kc, A.dqc, maxkv, maxq, scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_coarse_mm_kernel<D, true>), dim3((maxkv + 63) / 64, P.H, seqs), dim3(kThreads), 0, st,
-                       P, A.dsbuf, A.qc, A.dkc, maxkv, maxq, scale);
+                       CP, A.dsbuf, A.qc, A.dkc, maxkv, maxq, scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_coarse_mm_kernel<D, true>), dim3((maxkv + 63) / 64, P.H, seqs), dim3(kThreads), 0, st,
-                       P, A.pbuf, A.doc, A.dvc, maxkv, maxq, 1.0);
+                       CP, A.pbuf, A.doc, A.dvc, maxkv, maxq, 1.0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // 4. inverse routing
-    hipLaunchKernelGGL(bwd_k2q_kernel, dim3((maxkv + 3) / 4, P.H, seqs), dim3(kThreads), 0, st, P, A.idx, A.num,
-                       A.k2q, A.k2q_num, maxq);
+    // 4. inverse routing (64-token blocks)
+    hipLaunchKernelGGL(bwd_k2q_kernel, dim3((maxkv64 + 3) / 4, P.H, seqs), dim3(kThreads), 0, st, P, A.idx, A.num,
+                       A.k2q, A.k2q_num, maxq64);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // 5. dQ, 6. dK / dV
     const int64_t nq_all = P.packed ? (int64_t)P.total_q * P.H : (int64_t)P.nQ * P.H * P.nseq;
@@ -931,7 +970,7 @@ hipError_t launch_all(const DevProblem& P, const BwdArgs& A, hipStream_t st) {
                        A.rs, A.idx, A.num, A.dqc, A.dq, c_log2, (float)scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)nkv_all), dim3(kDkdvThreads), 0, st, P, A.q, A.k, A.v,
-                       A.dout, A.rs, A.k2q, A.k2q_num, maxq, A.dkc, A.dvc, A.dk, A.dv, c_log2, (float)scale);
+                       A.dout, A.rs, A.k2q, A.k2q_num, maxq64, A.dkc, A.dvc, A.dk, A.dv, c_log2, (float)scale);
     return hipGetLastError();
 }
 

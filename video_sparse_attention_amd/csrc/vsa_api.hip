@@ -127,6 +127,13 @@ int64_t q_elems(const vsa::DevProblem& P) {
 int64_t kv_elems(const vsa::DevProblem& P) {
     return P.packed ? (int64_t)P.H * P.total_kv * VSA_BLOCK * P.D : (int64_t)P.nseq * P.H * P.Skv * P.D;
 }
+// 64-token block counts (the attention kernels' granularity)
+int64_t qblocks64(const vsa::DevProblem& P) {
+    return P.packed ? (int64_t)P.H * P.total_q : (int64_t)P.nseq * P.H * P.nQ;
+}
+int64_t kvblocks64(const vsa::DevProblem& P) {
+    return P.packed ? (int64_t)P.H * P.total_kv : (int64_t)P.nseq * P.H * P.nKV;
+}
 // block-resolution array lengths (VSA blocks)
 int64_t qblocks(const vsa::DevProblem& P) {
     return P.packed ? (int64_t)P.H * P.total_q : (int64_t)P.nseq * P.H * P.nQB;
@@ -180,7 +187,9 @@ BwdWorkspace plan_bwd_workspace(const vsa::DevProblem& P, void* base) {
         off += round_up(bytes);
         return r;
     };
-    const int64_t maxq = P.packed ? P.max_q : P.nQ, maxkv = P.packed ? P.max_kv : P.nKV;
+    // coarse matrices per VSA block; statistics and inverse lists per 64-token block
+    const int64_t maxq = P.packed ? P.max_q : P.nQB, maxkv = P.packed ? P.max_kv : P.nKVB;
+    const int64_t maxq64 = P.packed ? P.max_q : P.nQ;
     const size_t qd = sizeof(double) * qblocks(P) * P.D, kd = sizeof(double) * kvblocks(P) * P.D;
     w.qc = (double*)take(qd);
     w.kc = (double*)take(kd);
@@ -192,9 +201,9 @@ BwdWorkspace plan_bwd_workspace(const vsa::DevProblem& P, void* base) {
     const int64_t coarse_rows = (int64_t)P.nseq * P.H * maxq;
     w.pbuf = (double*)take(sizeof(double) * coarse_rows * maxkv);
     w.dsbuf = (double*)take(sizeof(double) * coarse_rows * maxkv);
-    w.rs = (float*)take(sizeof(float) * qblocks(P) * vsa::kStatRow);
-    w.k2q = (int*)take(sizeof(int) * kvblocks(P) * maxq);
-    w.k2q_num = (int*)take(sizeof(int) * kvblocks(P));
+    w.rs = (float*)take(sizeof(float) * qblocks64(P) * vsa::kStatRow);
+    w.k2q = (int*)take(sizeof(int) * kvblocks64(P) * maxq64);
+    w.k2q_num = (int*)take(sizeof(int) * kvblocks64(P));
     w.total_bytes = off;
     return w;
 }
@@ -447,8 +456,6 @@ int vsa_sparse_attn_combine_train(const vsa_problem* problem, const vsa_bf16* q,
     vsa::DevProblem P;
     int rc = make_problem(problem, &P);
     if (rc) return rc;
-    if (P.bshd || P.ratio != 1)
-        return fail(VSA_ERR_UNSUPPORTED, "the training forward takes [B,H,S,D] or packed tensors with 64-token blocks");
     if ((rc = check_qkv(P, q, k, v))) return rc;
     if (!q2k_idx || !q2k_num || !out || !out_c || !out_s || !lse)
         return fail(VSA_ERR_NULL, "q2k_idx, q2k_num, out_c, out, out_s or lse is NULL");
@@ -475,7 +482,6 @@ int vsa_sparse_attn_combine_train(const vsa_problem* problem, const vsa_bf16* q,
 size_t vsa_backward_workspace_size(const vsa_problem* problem) {
     vsa::DevProblem P;
     if (make_problem(problem, &P) != VSA_OK) return 0;
-    if (P.bshd || P.ratio != 1) return 0;
     return plan_bwd_workspace(P, nullptr).total_bytes;
 }
 
@@ -487,8 +493,6 @@ int vsa_backward(const vsa_problem* problem, const vsa_bf16* q, const vsa_bf16* 
     vsa::DevProblem P;
     int rc = make_problem(problem, &P);
     if (rc) return rc;
-    if (P.bshd || P.ratio != 1)
-        return fail(VSA_ERR_UNSUPPORTED, "the backward takes [B,H,S,D] or packed tensors with 64-token blocks");
     if ((rc = check_qkv(P, q, k, v))) return rc;
     if (!q2k_idx || !q2k_num || !out_c || !out_s || !lse || !dout || !dq || !dk || !dv)
         return fail(VSA_ERR_NULL, "a required input or output pointer is NULL");
