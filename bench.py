@@ -427,7 +427,9 @@ def main():
     coarse_bytes = 2 * (q.numel() + 2 * k.numel()) + 8 * D * (n_qblocks + 2 * n_kvblocks)
     sparse_tf = flops / (avg["sparse"] * 1e-3) / 1e12
     traffic = measured_traffic(None) if (args.workload == "large" and block == 64) else None
-    kname = "sparse_attn_kernel<128, 1>" if gate is not None else "sparse_attn_kernel<128, 0>"
+    kname = "sparse_attn_kernel<128, 1, 1>" if gate is not None else "sparse_attn_kernel<128, 0, 1>"
+    if block != 64:
+        kname = kname.replace(", 1>", ", 2>")  # one workgroup per pair of 64-token query blocks
 
     res = {
         "metric": METRIC,
