@@ -2,16 +2,19 @@
 // block means; "[perf] avoid full-sequence materialization in VSA
 // coarse/sparse combine", Problem and Notes).
 //
-// HBM-bound streaming kernel.  Thread (block, c) owns the 16-byte chunk c
-// (8 consecutive d) of one block (64 tokens; 64 * ratio tokens for the VSA
-// blocks of 128 or 256 tokens of the dense layouts) and walks its valid tokens
-// with independent 16-byte loads (8 in flight per thread), accumulating the
-// 8 sums in float64 registers: no LDS and no cross-thread reduction.  The
-// CH = D/8 threads of a block read each token row as one contiguous
-// 16*CH-byte segment, so every load instruction of a wave is fully
-// coalesced.  Sums of at most 256 bf16 values in float64 are exact for any
-// realistic data, so the result does not depend on the order of the
-// additions; the mean is an IEEE division by the block's valid-token count.
+// HBM-bound streaming kernel.  Thread (block, slice s, c) owns the 16-byte
+// chunk c (8 consecutive d) of tokens s, s + 4, s + 8, ... of one block (64
+// tokens; 64 * ratio tokens for the VSA blocks of 128 or 256 tokens of the
+// dense layouts) and walks them with independent 16-byte loads (8 in flight
+// per thread), accumulating 8 sums in float64 registers; the 4 slices of a
+// chunk then add their sums with lane shuffles (no LDS).  The 4 CH threads of
+// a block (CH = D/8) read 4 consecutive token rows per load instruction, 4
+// contiguous 16*CH-byte segments, so every instruction of a wave is fully
+// coalesced, and splitting a block over 4 slices gives the launch enough
+// short workgroups to fill the chip evenly.  Sums of at most 256 bf16 values
+// in float64 are exact for any realistic data, so the result does not depend
+// on the order of the additions; the mean is an IEEE division by the block's
+// valid-token count.
 #include "vsa_internal.hpp"
 
 namespace vsa {
@@ -19,6 +22,7 @@ namespace {
 
 constexpr int kPoolThreads = 256;
 constexpr int kUnroll = 8;
+constexpr int kSlices = 4;  // threads sharing one (block, chunk)
 
 __device__ __forceinline__ double bf16_lo(uint32_t w) { return (double)__uint_as_float(w << 16); }
 __device__ __forceinline__ double bf16_hi(uint32_t w) { return (double)__uint_as_float(w & 0xffff0000u); }
@@ -30,13 +34,15 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(DevProblem P, const 
                                                             double* __restrict__ qc,
                                                             double* __restrict__ kc,
                                                             double* __restrict__ vc) {
-    constexpr int CH = D / 8;                  // threads per block
-    constexpr int BPG = kPoolThreads / CH;     // blocks per workgroup
-    const int which = blockIdx.z % 3;          // 0 q, 1 k, 2 v
-    const int b = blockIdx.z / 3;              // batch item (dense) or 0 (packed)
+    constexpr int CH = D / 8;                        // 16-byte chunks per token row
+    constexpr int TPB = CH * kSlices;                // threads per block (64 or 32: within a wave)
+    constexpr int BPG = kPoolThreads / TPB;          // blocks per workgroup
+    const int which = blockIdx.z % 3;                // 0 q, 1 k, 2 v
+    const int b = blockIdx.z / 3;                    // batch item (dense) or 0 (packed)
     const int h = blockIdx.y;
-    const int blk = blockIdx.x * BPG + threadIdx.x / CH;
+    const int blk = blockIdx.x * BPG + threadIdx.x / TPB;
     const int c = threadIdx.x % CH;
+    const int sl = (threadIdx.x % TPB) / CH;         // token slice
 
     int64_t off0, st, out_row;  // element offset of the block's first row, row stride
     int size;
@@ -64,11 +70,11 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(DevProblem P, const 
     double acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-    for (int t0 = 0; t0 < size; t0 += kUnroll) {
+    for (int t0 = sl; t0 < size; t0 += kSlices * kUnroll) {
         uint4 w[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int t = t0 + u;
+            const int t = t0 + kSlices * u;
             w[u] = t < size ? *reinterpret_cast<const uint4*>(src + (int64_t)t * st) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
@@ -79,6 +85,13 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(DevProblem P, const 
             acc[6] += bf16_lo(w[u].w); acc[7] += bf16_hi(w[u].w);
         }
     }
+    // the slices of a chunk are lanes CH apart inside one wave
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        acc[e] += __shfl_xor(acc[e], CH);
+        acc[e] += __shfl_xor(acc[e], 2 * CH);
+    }
+    if (sl != 0) return;
     const double cnt = (double)size;
     double2* o = reinterpret_cast<double2*>(dst + out_row * D + 8 * c);
 #pragma unroll
@@ -89,7 +102,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(DevProblem P, const 
 
 hipError_t launch_pool(const DevProblem& P, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        double* qc, double* kc, double* vc, hipStream_t st) {
-    const int bpg = kPoolThreads / (P.D / 8);
+    const int bpg = kPoolThreads / (P.D / 8 * kSlices);
     const int nb = P.packed ? max(P.total_q, P.total_kv) : max(P.nQB, P.nKVB);
     const dim3 grid((nb + bpg - 1) / bpg, P.H, P.packed ? 3 : 3 * P.nseq);
     if (P.D == 128)
