@@ -231,19 +231,26 @@ __global__ __launch_bounds__(kThreads) void coarse_select_kernel(DevProblem P, d
 }
 
 // ---------------------------------------------------------------------------
-// 3. out_c = W Vc / sum(W)
+// 3. out_c = W Vc / sum(W); a workgroup computes 64 rows x D / 2 columns,
+// so that a head's few row tiles spread over twice as many CUs (a 4-way
+// split, which stages every W slice four times, measured no faster)
 // ---------------------------------------------------------------------------
+constexpr int kOutSplit = 2;  // column ranges per row tile
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void coarse_out_kernel(DevProblem P, const double* __restrict__ sc, int ld,
                                                               const double* __restrict__ lsum,
                                                               const double* __restrict__ vc,
                                                               float* __restrict__ out_c, int c0, int C) {
-    constexpr int CPT = D / 16;  // output columns per thread
+    constexpr int DC = D / kOutSplit;  // columns per workgroup
+    constexpr int CPT = DC / 16;       // output columns per thread
+    static_assert(CPT >= 2 && CPT % 2 == 0, "double2 reads of the Vc slice");
     __shared__ __attribute__((aligned(16))) double wt[kSlice][kTile + kPad];  // [kv][row]
-    __shared__ __attribute__((aligned(16))) double vs[kSlice][D];             // [kv][d]
+    __shared__ __attribute__((aligned(16))) double vs[kSlice][DC];            // [kv][d - cbase]
     const int s = blockIdx.z, h = blockIdx.y;
     const SeqView sv = seq_view(P, s, h);
-    const int i0 = c0 + blockIdx.x * kTile;
+    const int cbase = (blockIdx.x % kOutSplit) * DC;
+    const int i0 = c0 + (blockIdx.x / kOutSplit) * kTile;
     const int iend = min(sv.nq, c0 + C);
     if (i0 >= iend) return;
     const int64_t srow0 = ((int64_t)s * P.H + h) * C - c0;  // scratch row of local block 0
@@ -262,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void coarse_out_kernel(DevProblem P, cons
         for (int c = 0; c < CPT; ++c) acc[r][c] = 0.0;
     // the next slice is loaded into registers while the current one is used
     double wv[4];
-    double2 vv[D / 32];  // Vc slice: 16 rows of D values, one double2 per thread per pass
+    double2 vv[DC / 32];  // Vc slice: 16 rows of DC values, one double2 per thread per pass
     auto fetch = [&](int j0) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -270,11 +277,12 @@ __global__ __launch_bounds__(kThreads) void coarse_out_kernel(DevProblem P, cons
             wv[e] = (w_ok && j < nkv) ? wrow[j] : 0.0;
         }
 #pragma unroll
-        for (int p = 0; p < D / 32; ++p) {
-            const int e = tid + kThreads * p;  // double2 index in the [16][D] slice
-            const int jr = e / (D / 2), dc = 2 * (e % (D / 2));
-            vv[p] = j0 + jr < nkv ? *reinterpret_cast<const double2*>(vc + (sv.kvblk_base + j0 + jr) * D + dc)
-                                  : make_double2(0.0, 0.0);
+        for (int p = 0; p < DC / 32; ++p) {
+            const int e = tid + kThreads * p;  // double2 index in the [16][DC] slice
+            const int jr = e / (DC / 2), dc = 2 * (e % (DC / 2));
+            vv[p] = j0 + jr < nkv
+                        ? *reinterpret_cast<const double2*>(vc + (sv.kvblk_base + j0 + jr) * D + cbase + dc)
+                        : make_double2(0.0, 0.0);
         }
     };
     fetch(0);
@@ -283,9 +291,9 @@ __global__ __launch_bounds__(kThreads) void coarse_out_kernel(DevProblem P, cons
 #pragma unroll
         for (int e = 0; e < 4; ++e) wt[sj + e][sr] = wv[e];
 #pragma unroll
-        for (int p = 0; p < D / 32; ++p) {
+        for (int p = 0; p < DC / 32; ++p) {
             const int e = tid + kThreads * p;
-            *reinterpret_cast<double2*>(&vs[e / (D / 2)][2 * (e % (D / 2))]) = vv[p];
+            *reinterpret_cast<double2*>(&vs[e / (DC / 2)][2 * (e % (DC / 2))]) = vv[p];
         }
         __syncthreads();
         if (j0 + kSlice < nkv) fetch(j0 + kSlice);
@@ -313,11 +321,10 @@ __global__ __launch_bounds__(kThreads) void coarse_out_kernel(DevProblem P, cons
         if (i >= iend) continue;
         const int64_t qb = sv.qblk_base + i;
         const double l = lsum[qb];
-        float* o = out_c + qb * D + CPT * tx;
+        float* o = out_c + qb * D + cbase + CPT * tx;
 #pragma unroll
-        for (int c = 0; c < CPT; c += 4)
-            *reinterpret_cast<float4*>(o + c) = make_float4((float)(acc[r][c] / l), (float)(acc[r][c + 1] / l),
-                                                           (float)(acc[r][c + 2] / l), (float)(acc[r][c + 3] / l));
+        for (int c = 0; c < CPT; c += 2)
+            *reinterpret_cast<float2*>(o + c) = make_float2((float)(acc[r][c] / l), (float)(acc[r][c + 1] / l));
     }
 }
 
@@ -346,8 +353,8 @@ hipError_t launch_d(const DevProblem& P, const double* qc, const double* kc, con
                                scale, c0, C);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(coarse_out_kernel<D>, dim3(tq, P.H, P.nseq), dim3(kThreads), 0, st, P, sc, ld, lsum, vc,
-                           out_c, c0, C);
+        hipLaunchKernelGGL(coarse_out_kernel<D>, dim3(tq * kOutSplit, P.H, P.nseq), dim3(kThreads), 0, st, P,
+                           sc, ld, lsum, vc, out_c, c0, C);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
