@@ -1,0 +1,91 @@
+"""Seeded random sweep of the forward against the fp64 oracle (shapes,
+head dims, VSA block sizes, both dense layouts, every gate mode, top-k up to
+past the block count), and capture of the forward in a HIP graph replayed
+against eager runs."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import video_sparse_attention_amd as vsa
+from tests import gpu_common as G
+from tests import numerics as N
+
+pytestmark = pytest.mark.gpu
+
+
+def sweep_configs(n=24, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        block = int(rng.choice([64, 128, 256]))
+        Sq = int(rng.integers(1, 9 * 64))
+        Skv = Sq if rng.random() < 0.5 else int(rng.integers(1, 9 * 64))
+        nkvb = -(-Skv // block)
+        out.append(dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)), Sq=Sq, Skv=Skv,
+                        D=int(rng.choice([64, 128])), block=block, bshd=bool(rng.random() < 0.5),
+                        gate=str(rng.choice(["none", "token", "full"])),
+                        topk=int(rng.integers(1, nkvb + 2)), seed=9000 + c))
+    return out
+
+
+def sweep_inputs(cfg):
+    inp = synth.dense_inputs(cfg["B"], cfg["H"], cfg["Sq"], cfg["D"], cfg["topk"], seed=cfg["seed"],
+                             gated=cfg["gate"] == "token", S_kv=cfg["Skv"])
+    if cfg["gate"] == "full":
+        inp.gate = synth.full_gate((cfg["B"], cfg["H"], cfg["Sq"], cfg["D"]), cfg["seed"] + 1)
+    return inp
+
+
+@pytest.mark.parametrize("cfg", sweep_configs(), ids=lambda c: f"s{c['seed']}")
+def test_random_forward(cfg):
+    G.note(f"case {cfg}")
+    inp = sweep_inputs(cfg)
+    ref = G.oracle_dense(inp, block=cfg["block"])
+    G.assert_tie_free(ref)
+    conv = G.to_bshd if cfg["bshd"] else (lambda t: t)
+    q, k, v = (conv(t).to(G.DEV) for t in (inp.q, inp.k, inp.v))
+    g = None if inp.gate is None else conv(inp.gate).to(G.DEV)
+    out, oc, idx, num = vsa.vsa_forward(q, k, v, cfg["topk"], g, block_size=cfg["block"], bshd=cfg["bshd"],
+                                        return_aux=True)
+    torch.cuda.synchronize()
+    out = G.from_bshd(out.cpu()) if cfg["bshd"] else out.cpu()
+    G.assert_indices_equal(idx.cpu(), num.cpu(), ref)
+    N.check_out_c(N.f64(oc), ref["out_c"])
+    mx, mean = N.check_out(N.f64(out), ref["out"])
+    G.note(f"  out max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
+@pytest.mark.parametrize("block,bshd", [(64, False), (128, True)])
+def test_forward_graph_replay(block, bshd):
+    """vsa_forward captured once in a graph on preallocated buffers; between
+    replays new inputs are copied in and the forward runs eagerly on its own
+    buffers; every replay equals the eager result bit for bit."""
+    B, H, S, D, topk = 1, 4, 64 * 9 + 13, 128, 3
+    conv = G.to_bshd if bshd else (lambda t: t)
+    first = synth.dense_inputs(B, H, S, D, topk, seed=9500, gated=True)
+    q, k, v, g = (conv(t).to(G.DEV) for t in (first.q, first.k, first.v, first.gate))
+    prob = vsa.dense_problem(B, H, S, S, D, topk, block, bshd)
+    ws_g, ws_e = vsa.alloc_workspace(prob, G.DEV), vsa.alloc_workspace(prob, G.DEV)
+    out_g, out_e = torch.empty_like(q), torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # a warm-up call outside the capture
+        vsa.vsa_forward(q, k, v, topk, g, block_size=block, bshd=bshd, out=out_g, workspace=ws_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        vsa.vsa_forward(q, k, v, topk, g, block_size=block, bshd=bshd, out=out_g, workspace=ws_g)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        nxt = synth.dense_inputs(B, H, S, D, topk, seed=9501 + rep, gated=True)
+        for dst, src in ((q, nxt.q), (k, nxt.k), (v, nxt.v), (g, nxt.gate)):
+            dst.copy_(conv(src).to(G.DEV))
+        vsa.vsa_forward(q, k, v, topk, g, block_size=block, bshd=bshd, out=out_e, workspace=ws_e)
+        torch.cuda.synchronize()
+        out_g.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {rep} differs from the eager forward"
+    G.note(f"  {4} replays equal to the eager forward (block {block}, bshd {bshd})")
