@@ -89,3 +89,57 @@ def test_forward_graph_replay(block, bshd):
         torch.cuda.synchronize()
         assert torch.equal(out_g, out_e), f"replay {rep} differs from the eager forward"
     G.note(f"  {4} replays equal to the eager forward (block {block}, bshd {bshd})")
+
+
+def varlen_configs(n=8, seed=78):
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        ns = int(rng.integers(1, 6))
+        lq = [int(x) for x in rng.integers(1, 6 * 64, ns)]
+        lkv = lq if rng.random() < 0.5 else [int(x) for x in rng.integers(1, 6 * 64, ns)]
+        topk = [int(rng.integers(1, -(-s // 64) + 2)) for s in lkv]
+        out.append(dict(lq=lq, lkv=lkv, topk=topk, H=int(rng.integers(1, 4)), D=int(rng.choice([64, 128])),
+                        gated=bool(rng.random() < 0.5), seed=9600 + c))
+    return out
+
+
+@pytest.mark.parametrize("cfg", varlen_configs(), ids=lambda c: f"v{c['seed']}")
+def test_random_varlen(cfg):
+    """Packed sequences of random lengths (Q and KV lengths equal or not,
+    per-sequence top-k up to past the sequence's block count): every stage
+    against the oracle's separate varlen path."""
+    G.note(f"case {cfg}")
+    inp = synth.varlen_inputs(cfg["lq"], cfg["lkv"], cfg["H"], cfg["D"], cfg["topk"], cfg["seed"], cfg["gated"])
+    ref = G.oracle_varlen(inp)
+    G.assert_tie_free(ref)
+    gpu = G.run_varlen_stages(inp)
+    G.assert_indices_equal(gpu["q2k_idx"], gpu["q2k_num"], ref)
+    N.check_out_c(N.f64(gpu["out_c"]), ref["out_c"])
+    N.check_sparse(N.f64(gpu["out_s"]), ref["out_s"])
+    mx, mean = N.check_out(N.f64(gpu["out_fused"]), ref["out"], "out (fused combine)")
+    G.note(f"  out max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
+def backward_configs(n=10, seed=79):
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        block = int(rng.choice([64, 128, 256]))
+        Sq = int(rng.integers(1, 6 * 64))
+        Skv = Sq if rng.random() < 0.5 else int(rng.integers(1, 6 * 64))
+        out.append(dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 3)), Sq=Sq, Skv=Skv,
+                        D=int(rng.choice([64, 128])), block=block, bshd=bool(rng.random() < 0.5),
+                        gate=str(rng.choice(["none", "token", "full"])),
+                        topk=int(rng.integers(1, -(-Skv // block) + 2)), seed=9700 + c))
+    return out
+
+
+@pytest.mark.parametrize("cfg", backward_configs(), ids=lambda c: f"b{c['seed']}")
+def test_random_backward(cfg):
+    """The training forward and the backward on random configurations
+    against the backward oracle (tolerances of tests/test_gpu_backward.py)."""
+    from tests.test_gpu_backward import check_dense_case
+    inp = sweep_inputs(cfg)
+    check_dense_case(inp.q, inp.k, inp.v, inp.gate, cfg["topk"], cfg["seed"] + 5, f"sweep {cfg}",
+                     block_size=cfg["block"], bshd=cfg["bshd"])
