@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=10.0,
                     help="wall-time budget of the oracle sample (whole heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--oracle-stages", action="store_true",
+                    help="time the fp64 oracle per stage on every workload (host only) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy kernel (reference for the HBM "
                          "byte counters) three times and exit")
@@ -144,6 +146,70 @@ def cpu_baseline(inp, budget_s: float, block: int = 64):
             "sample": f"{done} of {H} heads of the same workload, whole forward per head "
                       f"(pool, coarse, top-k, sparse, combine) in fp64 NumPy; "
                       f"{t_total:.1f} s; rate scaled by the same effective-FLOP formula"}
+
+
+def _oracle_stage_seconds(oracle, q, k, v, gate, topk):
+    """Wall seconds of the oracle's stages on one head of one sequence
+    ([S, D] float64 arrays): pool + coarse + top-k, sparse, combine."""
+    qs, ks = oracle.block_sizes(q.shape[0]), oracle.block_sizes(k.shape[0])
+    t0 = time.perf_counter()
+    qc, kc, vc = oracle.pool(q, qs), oracle.pool(k, ks), oracle.pool(v, ks)
+    dots, out_c = oracle.coarse(qc, kc, vc)
+    sel = [oracle.select_topk(dots[i], topk)[0] for i in range(len(qs))]
+    t1 = time.perf_counter()
+    rows = [oracle.sparse_block(q[64 * i: 64 * i + n], k, v, ks, sel[i]) for i, n in enumerate(qs)]
+    t2 = time.perf_counter()
+    for i, n in enumerate(qs):
+        oracle.combine(out_c[i], rows[i], None if gate is None else gate[64 * i: 64 * i + n])
+    t3 = time.perf_counter()
+    return t1 - t0, t2 - t1, t3 - t2
+
+
+def oracle_stages(budget_s: float):
+    """Per-stage wall time of the fp64 oracle on the host cores for every
+    workload: whole workloads for the three small ones (also with one BLAS
+    thread), a bounded sample of heads (and sequences) for the large ones,
+    scaled to the whole workload and labelled so."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import oracle
+    import synth
+    f64 = lambda t: t.float().double().numpy()
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    lines = []
+    for name in ("tiny", "dense_equiv", "varlen_small", "large", "varlen_many"):
+        inp = synth.workload(name)
+        units = []  # (q, k, v, gate, topk) per (sequence, head)
+        if isinstance(inp, synth.DenseInputs):
+            B, H = inp.shape[0], inp.shape[1]
+            for b in range(B):
+                for h in range(H):
+                    g = None if inp.gate is None else f64(inp.gate[b, h])
+                    units.append((inp.q[b, h], inp.k[b, h], inp.v[b, h], g, inp.topk))
+        else:
+            for h in range(inp.heads):
+                for s, per in enumerate(inp.per_seq):
+                    g = None if per["gate"] is None else f64(per["gate"][h])
+                    units.append((per["q"][h], per["k"][h], per["v"][h], g, inp.topk[s]))
+        small = name in ("tiny", "dense_equiv", "varlen_small")
+        for nthreads in ((threads, 1) if small else (threads,)):
+            with threadpool_limits(nthreads):
+                tot = np.zeros(3)
+                done = 0
+                for (q, k, v, g, topk) in units:
+                    tot += _oracle_stage_seconds(oracle, f64(q), f64(k), f64(v), g, topk)
+                    done += 1
+                    if not small and tot.sum() >= budget_s:
+                        break
+            scale = len(units) / done
+            lines.append({"workload": name, "threads": nthreads, "units": len(units), "timed_units": done,
+                          "extrapolated": done < len(units),
+                          "seconds": {"pool_coarse_topk": round(tot[0] * scale, 4),
+                                      "sparse": round(tot[1] * scale, 4),
+                                      "combine": round(tot[2] * scale, 4)}})
+            print(json.dumps(lines[-1]), flush=True)
+    return lines
 
 
 def video_bench(args, torch, synth, vsa):
@@ -302,6 +368,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.oracle_stages:
+        oracle_stages(args.cpu_budget_s)
         return
 
     import torch
