@@ -633,18 +633,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void bwd_dq_kernel(
 // ---------------------------------------------------------------------------
 // 6. dK, dV: one workgroup (4 waves) per KV block.  Wave w serves KV tokens
 // 32 g .. 32 g + 31 (g = w / 2, one token per lane column) in role r = w % 2:
-// role 0 holds K rows and computes S = Q K^T and P = exp2(S c - lse), role 1
-// holds V rows and computes dP - delta = dO V^T - delta; the two exchange
-// these (float32) through LDS, both form dS = P (dP - delta), and each
-// accumulates dV^T = dO^T P and dK^T = Q^T dS for one half of d (r).  So no
-// product is computed twice, and a wave holds one 32 x D operand and two
-// 32 x D/2 accumulators, which lets two waves share a SIMD.
+// role 0 holds the K rows, computes S = Q K^T and P = exp2(S c - lse) and
+// accumulates dV^T = dO^T P; role 1 holds the V rows, computes dP - delta =
+// dO V^T - delta, takes P from role 0 (float32, through LDS) to form dS =
+// P (dP - delta) and accumulates dK^T = Q^T dS.  So no product is computed
+// twice, P is the only value exchanged and it flows one way, and a wave
+// holds one 32 x D operand and one 32 x D accumulator, which lets three
+// waves share a SIMD.
 // The query blocks that listed this KV block are walked in stages of 32
 // query rows (a block's second half only if it has valid rows there); the Q
 // and dO rows of a stage (dual layout: read by rows for S and dP, transposed
 // for dV^T and dK^T) and its 32 log-sum-exp and delta values are
 // double-buffered in LDS, the copy of stage u + 1 running during stage u:
-// 48.5 KiB for D = 128, two workgroups per CU.
+// 40.5 KiB for D = 128.
 // ---------------------------------------------------------------------------
 // bf16 B operand of k-step hf (16 rows) of one 32x32 accumulator whose rows
 // are the k dimension: k-slots 8 hh .. 8 hh + 7 hold rows 16 hf + 4 hh +
@@ -664,12 +665,12 @@ __global__ __launch_bounds__(kDkdvThreads, 3) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ dout, const float* __restrict__ rs, const int* __restrict__ k2q,
     const int* __restrict__ k2q_num, int ldq, const double* __restrict__ dkc, const double* __restrict__ dvc,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float c_log2, float scale) {
-    constexpr int KS = D / 16, DT = D / 32, DH = DT / 2, CH = D / 8;
+    constexpr int KS = D / 16, DT = D / 32, CH = D / 8;
     __shared__ __attribute__((aligned(1024))) uint16_t q_tile[2][kHalf * D];
     __shared__ __attribute__((aligned(1024))) uint16_t o_tile[2][kHalf * D];
     __shared__ __attribute__((aligned(16))) float stats[2][2 * kHalf];  // [buffer][lse 0..31, delta 32..63]
-    // [token group][role][accumulator element / 4][lane]
-    __shared__ __attribute__((aligned(16))) float4 xch[2][2][4][64];
+    // P of the stage from role 0: [token group][accumulator element / 4][lane]
+    __shared__ __attribute__((aligned(16))) float4 xch[2][4][64];
 
     int s, h, j;
     SeqView sv;
@@ -709,11 +710,12 @@ __global__ __launch_bounds__(kDkdvThreads, 3) void bwd_dkdv_kernel(
     bf16x8 bfrag[KS];
     load_b_row<KS>((role ? v : k) + kvoff0 + kr * sv.kv_st, kvalid, hh, bfrag);
 
-    f32x16 dka[DH], dva[DH];
+    // role 0: dV^T, role 1: dK^T (unscaled), 32 x D each
+    f32x16 acc[DT];
 #pragma unroll
-    for (int dt = 0; dt < DH; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) dka[dt][e] = dva[dt][e] = 0.f;
+        for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
 
     const int m = __builtin_amdgcn_readfirstlane(clampi(k2q_num[kb], 0, ldq));
     const_int* list = (const_int*)uniform_ptr(k2q + kb * ldq);
@@ -739,15 +741,14 @@ __global__ __launch_bounds__(kDkdvThreads, 3) void bwd_dkdv_kernel(
     const uint32_t st_off = lane < 8 ? 16u * lane : 256u + 16u * (lane - 8);
     const int L16 = lane & 15, g16 = lane >> 4;
     const int tr_r = tr_token(L16), tr_d = 16 * (g16 & 1) + 4 * tr_dquad(L16);
-    uint32_t t_row[KS], t_tr[DH][2];
+    uint32_t t_row[KS], t_tr[DT][2];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) t_row[ks] = row_offset<CH, kSwzDual>(l32, hh, ks);
 #pragma unroll
-    for (int dt = 0; dt < DH; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) t_tr[dt][jj] = tr_offset<CH, kSwzDual>(DH * role + dt, jj, hh, tr_r, tr_d);
-    float4* my_xch = &xch[grp][role][0][lane];
-    const float4* other_xch = &xch[grp][role ^ 1][0][lane];
+        for (int jj = 0; jj < 2; ++jj) t_tr[dt][jj] = tr_offset<CH, kSwzDual>(dt, jj, hh, tr_r, tr_d);
+    float4* p_xch = &xch[grp][0][lane];
 
     // copies of stage (query block i, half hf) into buffer b
     const uint32_t qpitch = __builtin_amdgcn_readfirstlane((uint32_t)(2 * sv.q_st));  // bytes between query rows
@@ -820,52 +821,48 @@ __global__ __launch_bounds__(kDkdvThreads, 3) void bwd_dkdv_kernel(
                 for (int e = 0; e < 4; ++e) a[4 * g + e] -= sv4[e];
             }
         }
+        if (role == 0) {
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4)
-            my_xch[64 * e4] = make_float4(a[4 * e4], a[4 * e4 + 1], a[4 * e4 + 2], a[4 * e4 + 3]);
-        wg_barrier();  // the partner's half is in LDS
-        // P and dS = P (dP - delta), as the bf16 B operands of the stage's two k-steps
-        bf16x8 pb[2], db[2];
-        {
-            f32x16 pm, dm;
+            for (int e4 = 0; e4 < 4; ++e4)
+                p_xch[64 * e4] = make_float4(a[4 * e4], a[4 * e4 + 1], a[4 * e4 + 2], a[4 * e4 + 3]);
+        }
+        wg_barrier();  // P of this stage is in LDS
+        // the bf16 B operands of the stage's two k-steps: P (role 0) or
+        // dS = P (dP - delta) (role 1)
+        bf16x8 opb[2];
+        if (role == 0) {
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) opb[k2] = pack_half(a, k2);
+        } else {
+            f32x16 dm;
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4) {
-                const float4 o4 = other_xch[64 * e4];
-                const float ov[4] = {o4.x, o4.y, o4.z, o4.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    // P from role 0, dP - delta from role 1, whichever is this wave's
-                    const float mine = a[4 * e4 + e];
-                    pm[4 * e4 + e] = role ? ov[e] : mine;
-                    dm[4 * e4 + e] = mine * ov[e];
-                }
+                const float4 p4 = p_xch[64 * e4];
+                dm[4 * e4 + 0] = p4.x * a[4 * e4 + 0];
+                dm[4 * e4 + 1] = p4.y * a[4 * e4 + 1];
+                dm[4 * e4 + 2] = p4.z * a[4 * e4 + 2];
+                dm[4 * e4 + 3] = p4.w * a[4 * e4 + 3];
             }
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-                pb[k2] = pack_half(pm, k2);
-                db[k2] = pack_half(dm, k2);
-            }
+            for (int k2 = 0; k2 < 2; ++k2) opb[k2] = pack_half(dm, k2);
         }
-        // dV^T += dO^T P and dK^T += Q^T dS for this wave's half of d, the
-        // transposed operands read one product ahead
+        // role 0: dV^T += dO^T P; role 1: dK^T += Q^T dS, over all of d; the
+        // transposed operand read one product ahead
         {
-            bf16x8 ta = tr_read<CH>(ot, t_tr[0][0], t_tr[0][1], 0);
-            bf16x8 tb = tr_read<CH>(qt, t_tr[0][0], t_tr[0][1], 0);
+            const uint16_t* tt = role ? qt : ot;
+            bf16x8 ta = tr_read<CH>(tt, t_tr[0][0], t_tr[0][1], 0);
 #pragma unroll
-            for (int y = 0; y < 2 * DH; ++y) {
-                const int k2 = y / DH, dt = y % DH;
-                bf16x8 na = ta, nb = tb;
-                if (y + 1 < 2 * DH) {
-                    const int k2n = (y + 1) / DH, dtn = (y + 1) % DH;
-                    na = tr_read<CH>(ot, t_tr[dtn][0], t_tr[dtn][1], k2n);
-                    nb = tr_read<CH>(qt, t_tr[dtn][0], t_tr[dtn][1], k2n);
+            for (int y = 0; y < 2 * DT; ++y) {
+                const int k2 = y / DT, dt = y % DT;
+                bf16x8 na = ta;
+                if (y + 1 < 2 * DT) {
+                    const int k2n = (y + 1) / DT, dtn = (y + 1) % DT;
+                    na = tr_read<CH>(tt, t_tr[dtn][0], t_tr[dtn][1], k2n);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta, pb[k2], dva[dt], 0, 0, 0);
-                dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tb, db[k2], dka[dt], 0, 0, 0);
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta, opb[k2], acc[dt], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
                 ta = na;
-                tb = nb;
             }
         }
         x = nx;
@@ -874,38 +871,30 @@ __global__ __launch_bounds__(kDkdvThreads, 3) void bwd_dkdv_kernel(
         buf ^= 1;
     }
 
-    // lane holds dK / dV [kr][32 (DH role + dt) + 8 (e / 4) + 4 hh + e % 4]
-    uint16_t* krow = dk + kvoff0 + kr * sv.kv_st;
-    uint16_t* vrow = dv + kvoff0 + kr * sv.kv_st;
+    // lane holds dV (role 0) / dK (role 1) [kr][32 dt + 8 (e / 4) + 4 hh + e % 4]
+    uint16_t* row = (role ? dk : dv) + kvoff0 + kr * sv.kv_st;
     if (kvalid) {
         // the gradient through the block means, over the VSA block's valid tokens
-        const double* ckr = dkc + kbv * D;
-        const double* cvr = dvc + kbv * D;
+        const double* cr = (role ? dkc : dvc) + kbv * D;
         const int vsize = P.packed ? kvsize : min(kBlock << lr, P.Skv - (kBlock << lr) * (j >> lr));
         const float inv_size = 1.f / (float)vsize;
+        const float mul = role ? scale : 1.f;  // dK = Q^T dS / sqrt(D)
 #pragma unroll
-        for (int dt = 0; dt < DH; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const int d0 = 32 * (DH * role + dt) + 8 * jj + 4 * hh;
-                float a[4], b[4];
+                const int d0 = 32 * dt + 8 * jj + 4 * hh;
+                float r[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    a[e] = fmaf(dka[dt][4 * jj + e], scale, (float)ckr[d0 + e] * inv_size);
-                    b[e] = dva[dt][4 * jj + e] + (float)cvr[d0 + e] * inv_size;
-                }
-                *reinterpret_cast<uint2*>(krow + d0) = make_uint2(bf16pair(a[0], a[1]), bf16pair(a[2], a[3]));
-                *reinterpret_cast<uint2*>(vrow + d0) = make_uint2(bf16pair(b[0], b[1]), bf16pair(b[2], b[3]));
+                for (int e = 0; e < 4; ++e) r[e] = fmaf(acc[dt][4 * jj + e], mul, (float)cr[d0 + e] * inv_size);
+                *reinterpret_cast<uint2*>(row + d0) = make_uint2(bf16pair(r[0], r[1]), bf16pair(r[2], r[3]));
             }
     } else if (P.packed) {
 #pragma unroll
-        for (int dt = 0; dt < DH; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int d0 = 32 * (DH * role + dt) + 8 * jj + 4 * hh;
-                *reinterpret_cast<uint2*>(krow + d0) = make_uint2(0, 0);
-                *reinterpret_cast<uint2*>(vrow + d0) = make_uint2(0, 0);
-            }
+            for (int jj = 0; jj < 4; ++jj)
+                *reinterpret_cast<uint2*>(row + 32 * dt + 8 * jj + 4 * hh) = make_uint2(0, 0);
     }
 }
 
