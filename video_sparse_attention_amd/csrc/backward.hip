@@ -216,22 +216,29 @@ __global__ __launch_bounds__(kThreads) void bwd_coarse_softmax_kernel(DevProblem
 //                  X = a KV-block array, out a query-block array;
 //   TRANS = true:  o = KV block, k = query block, M(o, k) = m[row(k)][o],
 //                  X = a query-block array, out a KV-block array.
-// 64 output rows x D per workgroup, 16-wide k slices of M and X staged in LDS
-// (the next slice prefetched into registers), 4 rows x D / 16 columns per
-// thread.  Grid (ceil(max rows / 64), H, sequences).
+// 64 output rows x D / 2 columns per workgroup (the two column halves of a
+// row tile in consecutive workgroups, so that a head's few row tiles spread
+// over twice as many CUs), 16-wide k slices of M and X staged in LDS (the
+// next slice prefetched into registers), 4 rows x D / 32 columns per thread.
+// Grid (2 ceil(max rows / 64), H, sequences).
+constexpr int kMmSplit = 2;
+
 template <int D, bool TRANS>
 __global__ __launch_bounds__(kThreads) void bwd_coarse_mm_kernel(DevProblem P, const double* __restrict__ m,
                                                                  const double* __restrict__ x,
                                                                  double* __restrict__ out, int ld, int maxq,
                                                                  double alpha) {
     constexpr int kTile = 64, kSlice = 16, kPad = 2;
-    constexpr int CPT = D / 16;  // output columns per thread
+    constexpr int DC = D / kMmSplit;  // columns per workgroup
+    constexpr int CPT = DC / 16;      // output columns per thread
+    static_assert(CPT >= 2 && CPT % 2 == 0, "double2 column pairs");
     __shared__ __attribute__((aligned(16))) double mt[kSlice][kTile + kPad];  // [k][o]
-    __shared__ __attribute__((aligned(16))) double xs[kSlice][D];             // [k][d]
+    __shared__ __attribute__((aligned(16))) double xs[kSlice][DC];            // [k][d - cbase]
     const int s = blockIdx.z, h = blockIdx.y;
     const SeqView sv = seq_view(P, s, h);
     const int nout = TRANS ? sv.nkv : sv.nq, nk = TRANS ? sv.nq : sv.nkv;
-    const int o0 = blockIdx.x * kTile;
+    const int cbase = (blockIdx.x % kMmSplit) * DC;
+    const int o0 = (blockIdx.x / kMmSplit) * kTile;
     if (o0 >= nout) return;
     const int64_t row0 = ((int64_t)s * P.H + h) * maxq;  // m row of query block 0
     const int64_t xbase = TRANS ? sv.qblk_base : sv.kvblk_base;
@@ -248,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void bwd_coarse_mm_kernel(DevProblem P, c
     const int ma = TRANS ? tid / 16 : tid / 4;
     const int mb = TRANS ? 4 * (tid % 16) : 4 * (tid % 4);
     double mv[4];
-    double2 xv[D / 32];
+    double2 xv[DC / 32];
     auto fetch = [&](int k0) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -258,10 +265,10 @@ __global__ __launch_bounds__(kThreads) void bwd_coarse_mm_kernel(DevProblem P, c
             mv[e] = ok ? (TRANS ? m[(row0 + k) * ld + o] : m[(row0 + o) * ld + k]) : 0.0;
         }
 #pragma unroll
-        for (int p = 0; p < D / 32; ++p) {
-            const int e = tid + kThreads * p;  // double2 index in the [16][D] slice
-            const int kr = e / (D / 2), dc = 2 * (e % (D / 2));
-            xv[p] = k0 + kr < nk ? *reinterpret_cast<const double2*>(x + (xbase + k0 + kr) * D + dc)
+        for (int p = 0; p < DC / 32; ++p) {
+            const int e = tid + kThreads * p;  // double2 index in the [16][DC] slice
+            const int kr = e / (DC / 2), dc = 2 * (e % (DC / 2));
+            xv[p] = k0 + kr < nk ? *reinterpret_cast<const double2*>(x + (xbase + k0 + kr) * D + cbase + dc)
                                  : make_double2(0.0, 0.0);
         }
     };
@@ -273,9 +280,9 @@ __global__ __launch_bounds__(kThreads) void bwd_coarse_mm_kernel(DevProblem P, c
             if (TRANS) mt[ma][mb + e] = mv[e]; else mt[mb + e][ma] = mv[e];
         }
 #pragma unroll
-        for (int p = 0; p < D / 32; ++p) {
+        for (int p = 0; p < DC / 32; ++p) {
             const int e = tid + kThreads * p;
-            *reinterpret_cast<double2*>(&xs[e / (D / 2)][2 * (e % (D / 2))]) = xv[p];
+            *reinterpret_cast<double2*>(&xs[e / (DC / 2)][2 * (e % (DC / 2))]) = xv[p];
         }
         __syncthreads();
         if (k0 + kSlice < nk) fetch(k0 + kSlice);
@@ -301,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void bwd_coarse_mm_kernel(DevProblem P, c
     for (int r = 0; r < 4; ++r) {
         const int o = o0 + 4 * ty + r;
         if (o >= nout) continue;
-        double* dst = out + (obase + o) * D + CPT * tx;
+        double* dst = out + (obase + o) * D + cbase + CPT * tx;
 #pragma unroll
         for (int c = 0; c < CPT; c += 2)
             *reinterpret_cast<double2*>(dst + c) = make_double2(acc[r][c] * alpha, acc[r][c + 1] * alpha);
@@ -939,13 +946,16 @@ hipError_t launch_all(const DevProblem& P, const BwdArgs& A, hipStream_t st) {
     hipLaunchKernelGGL(bwd_coarse_softmax_kernel, dim3((unsigned)((crows + 3) / 4)), dim3(kThreads), 0, st, CP,
                        A.pbuf, A.dsbuf, maxkv, maxq, scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_coarse_mm_kernel<D, false>), dim3((maxq + 63) / 64, P.H, seqs), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((bwd_coarse_mm_kernel<D, false>), dim3(kMmSplit * ((maxq + 63) / 64), P.H, seqs),
+                       dim3(kThreads), 0, st,
                        CP, A.dsbuf, A.kc, A.dqc, maxkv, maxq, scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_coarse_mm_kernel<D, true>), dim3((maxkv + 63) / 64, P.H, seqs), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((bwd_coarse_mm_kernel<D, true>), dim3(kMmSplit * ((maxkv + 63) / 64), P.H, seqs),
+                       dim3(kThreads), 0, st,
                        CP, A.dsbuf, A.qc, A.dkc, maxkv, maxq, scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_coarse_mm_kernel<D, true>), dim3((maxkv + 63) / 64, P.H, seqs), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((bwd_coarse_mm_kernel<D, true>), dim3(kMmSplit * ((maxkv + 63) / 64), P.H, seqs),
+                       dim3(kThreads), 0, st,
                        CP, A.pbuf, A.doc, A.dvc, maxkv, maxq, 1.0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // 4. inverse routing (64-token blocks)
