@@ -240,10 +240,10 @@ def vsa_forward(q, k, v, topk: int, gate=None,
 # Varlen: block-padded packed q [H, 64*sum nQ, D], k/v [H, 64*sum nKV, D]
 # ---------------------------------------------------------------------------
 
-def varlen_metadata(seqlens_q: Sequence[int], seqlens_kv: Sequence[int]):
+def varlen_metadata(seqlens_q: Sequence[int], seqlens_kv: Sequence[int], block: int = BLOCK):
     """Per-sequence block counts, cumulative block offsets and per-block sizes."""
-    qsz = [block_sizes(s) for s in seqlens_q]
-    ksz = [block_sizes(s) for s in seqlens_kv]
+    qsz = [block_sizes(s, block) for s in seqlens_q]
+    ksz = [block_sizes(s, block) for s in seqlens_kv]
     cu_q = np.concatenate([[0], np.cumsum([len(x) for x in qsz])]).astype(np.int64)
     cu_kv = np.concatenate([[0], np.cumsum([len(x) for x in ksz])]).astype(np.int64)
     return qsz, ksz, cu_q, cu_kv
@@ -251,7 +251,8 @@ def varlen_metadata(seqlens_q: Sequence[int], seqlens_kv: Sequence[int]):
 
 def vsa_forward_varlen(q, k, v, seqlens_q: Sequence[int], seqlens_kv: Sequence[int],
                        topk: Sequence[int], gate=None,
-                       blocks: Optional[Sequence[Tuple[int, int]]] = None) -> Dict[str, np.ndarray]:
+                       blocks: Optional[Sequence[Tuple[int, int]]] = None,
+                       block: int = BLOCK) -> Dict[str, np.ndarray]:
     """VSA forward over block-padded packed sequences, in one pass over the packed arrays.
 
     Sequence ``s`` occupies query blocks ``[cu_q[s], cu_q[s+1])`` and KV blocks
@@ -267,19 +268,25 @@ def vsa_forward_varlen(q, k, v, seqlens_q: Sequence[int], seqlens_kv: Sequence[i
     Returns ``out``, ``out_s`` (``[H, slots_q, D]``), ``out_c``
     (``[H, nQ_total, D]``), ``q2k_idx`` (``[H, nQ_total, max_k]`` int32, -1 past
     ``q2k_num``), ``q2k_num``, ``gap``, ``max_abs_dot`` (``[H, num_seqs]``).
+    With ``block`` = 128 or 256 every VSA block occupies that many slots
+    (reading of the 256-token variable-block-size variants of "[chore]
+    release fastvideo-kernel 0.3.0", Block-sparse / VSA attention
+    improvements, with the packing of "[kernel] Add varlen support ...").
     """
-    qsz, ksz, _, _ = varlen_metadata(seqlens_q, seqlens_kv)
-    return forward_packed_blocks(q, k, v, qsz, ksz, topk, gate, blocks)
+    qsz, ksz, _, _ = varlen_metadata(seqlens_q, seqlens_kv, block)
+    return forward_packed_blocks(q, k, v, qsz, ksz, topk, gate, blocks, block)
 
 
 def forward_packed_blocks(q, k, v, qsz: Sequence[Sequence[int]], ksz: Sequence[Sequence[int]],
                           topk: Sequence[int], gate=None,
-                          blocks: Optional[Sequence[Tuple[int, int]]] = None) -> Dict[str, np.ndarray]:
+                          blocks: Optional[Sequence[Tuple[int, int]]] = None,
+                          block: int = BLOCK) -> Dict[str, np.ndarray]:
     """The packed forward of ``vsa_forward_varlen`` for arbitrary per-block
     valid-token counts: sequence ``s`` has query blocks of ``qsz[s]`` valid
     tokens and KV blocks of ``ksz[s]`` valid tokens, each block at the start
     of its own 64 slots (the layout the pages' ``variable_block_sizes``
-    describe; a partial block need not be the last one)."""
+    describe; a partial block need not be the last one).  ``block``: slots
+    per block, the VSA block size."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     H, _, D = q.shape
     cu_q = np.concatenate([[0], np.cumsum([len(x) for x in qsz])]).astype(np.int64)
@@ -295,13 +302,13 @@ def forward_packed_blocks(q, k, v, qsz: Sequence[Sequence[int]], ksz: Sequence[S
     maxdot = np.empty((H, ns))
     seq_of = np.empty(nq_tot, dtype=np.int64)
     for s in range(ns):
-        q0, k0 = BLOCK * cu_q[s], BLOCK * cu_kv[s]
-        qspan, kspan = BLOCK * len(qsz[s]), BLOCK * len(ksz[s])
+        q0, k0 = block * cu_q[s], block * cu_kv[s]
+        qspan, kspan = block * len(qsz[s]), block * len(ksz[s])
         seq_of[cu_q[s]:cu_q[s + 1]] = s
         for h in range(H):
-            qc = pool(q[h, q0:q0 + qspan], qsz[s])
-            kc = pool(k[h, k0:k0 + kspan], ksz[s])
-            vc = pool(v[h, k0:k0 + kspan], ksz[s])
+            qc = pool(q[h, q0:q0 + qspan], qsz[s], block)
+            kc = pool(k[h, k0:k0 + kspan], ksz[s], block)
+            vc = pool(v[h, k0:k0 + kspan], ksz[s], block)
             dots, oc = coarse(qc, kc, vc)
             maxdot[h, s] = np.abs(dots).max()
             for i in range(len(qsz[s])):
@@ -319,11 +326,11 @@ def forward_packed_blocks(q, k, v, qsz: Sequence[Sequence[int]], ksz: Sequence[S
     out_s = np.zeros_like(q) if blocks is None else np.full(q.shape, np.nan)
     out = np.zeros_like(q) if blocks is None else np.full(q.shape, np.nan)
     for h, g in want:
-        lo, n = BLOCK * g, qsz_g[g]
+        lo, n = block * g, qsz_g[g]
         sel = idx[h, g, :num[h, g]]
-        rows = sparse_block(q[h, lo:lo + n], k[h], v[h], ksz_g, sel)
-        out_s[h, lo:lo + BLOCK] = 0.0
-        out[h, lo:lo + BLOCK] = 0.0
+        rows = sparse_block(q[h, lo:lo + n], k[h], v[h], ksz_g, sel, block)
+        out_s[h, lo:lo + block] = 0.0
+        out[h, lo:lo + block] = 0.0
         out_s[h, lo:lo + n] = rows
         gr = None if gate is None else gate[h, lo:lo + n]
         out[h, lo:lo + n] = combine(out_c[h, g], rows, gr)

@@ -288,13 +288,13 @@ def pin_gate_special_values(seed=9):
 # varlen: packed equals per-sequence
 # ---------------------------------------------------------------------------
 
-def _pack(seqs, key, H, D, lens):
-    n = [-(-s // 64) for s in lens]
-    out = np.zeros((H, 64 * sum(n)) + ((D,) if key != "gate" else ()))
+def _pack(seqs, key, H, D, lens, block=64):
+    n = [-(-s // block) for s in lens]
+    out = np.zeros((H, block * sum(n)) + ((D,) if key != "gate" else ()))
     o = 0
     for s, x in enumerate(seqs):
         out[:, o:o + lens[s]] = x[key]
-        o += 64 * n[s]
+        o += block * n[s]
     return out
 
 
@@ -330,6 +330,49 @@ def pin_varlen_matches_per_sequence(seed=10):
         oq += 64 * nq
         nq_acc += nq
         nkv_acc += nkv
+
+
+def pin_varlen_large_blocks_matches_per_sequence(seed=24):
+    """Packed sequences with VSA blocks of 128 and 256 tokens (each block
+    128 / 256 slots): the separate packed path equals the dense path run on
+    each sequence alone with the same block size, bit for bit, including
+    rebased indices, partial blocks and zero padding slots; a single
+    sequence packed alone equals the dense forward."""
+    rng = _rng(seed)
+    H, D = 2, 32
+    for block in (128, 256):
+        lens_q = [3 * block, block + 37, 1, 2 * block - 5]
+        lens_kv = [2 * block + 9, block + 37, 70, 3 * block]
+        topk = [2, 1, 3, 2]
+        seqs = []
+        for sq, skv in zip(lens_q, lens_kv):
+            seqs.append(dict(q=rng.standard_normal((H, sq, D)), k=rng.standard_normal((H, skv, D)),
+                             v=rng.standard_normal((H, skv, D)),
+                             gate=1 / (1 + np.exp(-rng.standard_normal((H, sq))))))
+        qp, kp, vp = (_pack(seqs, x, H, D, lens_q if x == "q" else lens_kv, block) for x in "qkv")
+        gp = _pack(seqs, "gate", H, D, lens_q, block)
+        r = O.vsa_forward_varlen(qp, kp, vp, lens_q, lens_kv, topk, gp, block=block)
+        oq = nq_acc = nkv_acc = 0
+        for s, x in enumerate(seqs):
+            ref = O.vsa_forward(x["q"][None], x["k"][None], x["v"][None], topk[s], x["gate"][None], block=block)
+            nq, nkv = -(-lens_q[s] // block), -(-lens_kv[s] // block)
+            kk = min(topk[s], nkv)
+            assert np.array_equal(r["out"][:, oq:oq + lens_q[s]], ref["out"][0]), (block, s)
+            assert np.array_equal(r["out_c"][:, nq_acc:nq_acc + nq], ref["out_c"][0]), (block, s)
+            got = r["q2k_idx"][:, nq_acc:nq_acc + nq]
+            assert np.array_equal(got[..., :kk], ref["q2k_idx"][0] + nkv_acc), (block, s)
+            assert (got[..., kk:] == -1).all()
+            pad = slice(oq + lens_q[s], oq + block * nq)
+            assert (r["out"][:, pad] == 0).all() and (r["out_s"][:, pad] == 0).all()
+            oq += block * nq
+            nq_acc += nq
+            nkv_acc += nkv
+    q, k, v, g = _rand_dense(seed + 1, B=1, H=2, nq=9, nkv=9, tail=11)
+    d = O.vsa_forward(q, k, v, 2, g, block=256)
+    r = O.vsa_forward_varlen(q[0], k[0], v[0], [q.shape[2]], [k.shape[2]], [2], g[0], block=256)
+    n = q.shape[2]
+    assert np.array_equal(r["out"][:, :n], d["out"][0])
+    assert np.array_equal(r["q2k_idx"], d["q2k_idx"][0])
 
 
 def pin_single_sequence_varlen_equals_dense(seed=11):
@@ -648,5 +691,5 @@ ALL_PINS = [
     pin_backward_forward_matches_oracle, pin_backward_gradcheck, pin_backward_dense_equivalence,
     pin_lse_dense_equivalence, pin_lse_reproduces_sparse_output,
     pin_large_blocks_dense_equivalence, pin_large_blocks_by_duplication,
-    pin_backward_large_blocks,
+    pin_backward_large_blocks, pin_varlen_large_blocks_matches_per_sequence,
 ]

@@ -204,6 +204,16 @@ def _sparse_stride_64(q_rows, k, v, kv_sizes, idx, block=64):
     return _orig_sparse_block(q_rows, k, v, kv_sizes, idx, 64)
 
 
+_orig_packed = O.forward_packed_blocks
+
+
+def _packed_slots_64(q, k, v, qsz, ksz, topk, gate=None, blocks=None, block=64):
+    # packed VSA blocks located 64 slots apart whatever their size; the sizes
+    # are cut to 64 so that the slip runs instead of raising
+    cut = lambda sz: [[min(n, 64) for n in x] for x in sz]
+    return _orig_packed(q, k, v, cut(qsz), cut(ksz), topk, gate, blocks, 64)
+
+
 def _bw_blocks_64(q, k, v, gate, idx, block=64):
     # the restatement ignores the VSA block size (pools and attends 64-token blocks)
     return _forward_torch_ok(q, k, v, gate, idx, 64)
@@ -234,6 +244,7 @@ MISTAKES = {
     "pool_blocks_64_apart": ("pool", _pool_stride_64),
     "sparse_blocks_64_apart": ("sparse_block", _sparse_stride_64),
     "backward_ignores_block_size": ("backward.forward_torch", _bw_blocks_64),
+    "packed_blocks_64_slots_apart": ("forward_packed_blocks", _packed_slots_64),
 }
 
 
