@@ -27,12 +27,11 @@
  *     negative return value is an error code (VSA_ERR_*), nothing has been
  *     launched in that case, and vsa_last_error() describes it;
  *   - head_dim is 64 or 128; block_size (the VSA block: pooling, routing and
- *     the KV granularity of the sparse attention) is 64, or 128 / 256 for the
- *     DENSE and BSHD layouts ("[chore] release fastvideo-kernel 0.3.0",
- *     Block-sparse / VSA attention improvements: 256-token KV blocks;
- *     "[perf] avoid full-sequence materialization ...", Change: the
- *     64/128/256 dispatch).  The training forward and the backward take
- *     64-token blocks in the DENSE or PACKED layout.
+ *     the KV granularity of the sparse attention) is 64, 128 or 256 in every
+ *     layout ("[chore] release fastvideo-kernel 0.3.0", Block-sparse / VSA
+ *     attention improvements: 256-token KV blocks and the variable-block-size
+ *     variants; "[perf] avoid full-sequence materialization ...", Change: the
+ *     64/128/256 dispatch).
  *
  * Layouts:
  *   DENSE   q [B, H, Sq, D], k/v [B, H, Skv, D], out [B, H, Sq, D], each batch
@@ -42,11 +41,12 @@
  *           ("[chore] release fastvideo-kernel 0.3.0", the BSHD-native entry
  *           that avoids layout round trips); a token gate defaults to
  *           [B, Sq, H], a full gate to [B, Sq, H, D].
- *   PACKED  block-padded packing of num_seqs sequences: q [H, 64*Nq, D],
- *           k/v [H, 64*Nkv, D] with Nq/Nkv the total block counts; sequence s
- *           owns global query blocks [cu_blocks_q[s], cu_blocks_q[s+1]) and KV
- *           blocks [cu_blocks_kv[s], cu_blocks_kv[s+1]); global block g starts
- *           at slot 64 g and its first block_sizes_*[g] slots are valid tokens
+ *   PACKED  block-padded packing of num_seqs sequences: q [H, bs*Nq, D],
+ *           k/v [H, bs*Nkv, D] with bs = block_size and Nq/Nkv the total
+ *           block counts; sequence s owns global query blocks
+ *           [cu_blocks_q[s], cu_blocks_q[s+1]) and KV blocks
+ *           [cu_blocks_kv[s], cu_blocks_kv[s+1]); global block g starts at
+ *           slot bs g and its first block_sizes_*[g] slots are valid tokens
  *           (the rest is padding, never read).
  *   Block-resolution tensors: out_c is float32 [B, H, nQ, D] (DENSE, BSHD;
  *   nQ = ceil(Sq / block_size)) or [H, Nq, D] (PACKED); q2k_num is int32
@@ -99,14 +99,14 @@ typedef void *vsa_stream;  /* hipStream_t */
  * vsa_build_metadata and copied to the device); batch/seqlen/topk are
  * ignored.  The kernels never read outside the arrays whose lengths are given
  * here, whatever values the device arrays hold: block sizes are clamped to
- * [1, 64], per-sequence top-k to [1, min(max_topk, KV blocks)], and indices
- * outside a query block's own sequence are skipped.
+ * [1, block_size], per-sequence top-k to [1, min(max_topk, KV blocks)], and
+ * indices outside a query block's own sequence are skipped.
  */
 typedef struct vsa_problem {
     int32_t layout;     /* VSA_LAYOUT_DENSE, VSA_LAYOUT_BSHD or VSA_LAYOUT_PACKED */
     int32_t heads;      /* H >= 1 */
     int32_t head_dim;   /* D: 64 or 128 */
-    int32_t block_size; /* 64; 128 or 256 for DENSE and BSHD */
+    int32_t block_size; /* 64, 128 or 256 */
     /* DENSE */
     int32_t batch;     /* B >= 1 */
     int32_t seqlen_q;  /* Sq >= 1 */
@@ -121,8 +121,8 @@ typedef struct vsa_problem {
     int32_t max_topk;        /* row length of q2k_idx, >= every per-sequence top-k */
     const int32_t *cu_blocks_q;    /* device, [num_seqs + 1] */
     const int32_t *cu_blocks_kv;   /* device, [num_seqs + 1] */
-    const int32_t *block_sizes_q;  /* device, [Nq], 1..64 */
-    const int32_t *block_sizes_kv; /* device, [Nkv], 1..64 */
+    const int32_t *block_sizes_q;  /* device, [Nq], 1..block_size */
+    const int32_t *block_sizes_kv; /* device, [Nkv], 1..block_size */
     const int32_t *topk_per_seq;   /* device, [num_seqs] */
 } vsa_problem;
 
@@ -134,8 +134,8 @@ typedef struct vsa_meta_sizes {
     int32_t max_q_blocks;
     int32_t max_kv_blocks;
     int32_t max_topk; /* max over sequences of min(topk, KV blocks) */
-    int64_t q_slots;  /* 64 * total_q_blocks: rows per head of packed q/out */
-    int64_t kv_slots; /* 64 * total_kv_blocks */
+    int64_t q_slots;  /* block_size * total_q_blocks: rows per head of packed q/out */
+    int64_t kv_slots; /* block_size * total_kv_blocks */
 } vsa_meta_sizes;
 
 /*
@@ -146,17 +146,20 @@ typedef struct vsa_meta_sizes {
  * into fastvideo_kernel": build_vsa_metadata, variable block sizes.)
  *
  * seqlens_q/seqlens_kv/topk are host arrays of num_seqs entries
- * (seqlens_kv NULL means equal to seqlens_q).  `sizes` is always filled.
+ * (seqlens_kv NULL means equal to seqlens_q); block_size (64, 128 or 256)
+ * is the VSA block, the slots each block occupies.  `sizes` is always
+ * filled.
  * The five output arrays are host arrays the caller allocates from `sizes`
  * (pass all NULL to size them first): cu_blocks_q/kv [num_seqs + 1],
  * block_sizes_q [total_q_blocks], block_sizes_kv [total_kv_blocks],
  * topk_clamped [num_seqs] = min(topk[s], KV blocks of s).
  * Errors: VSA_ERR_NULL (seqlens_q, topk or sizes NULL; some but not all
- * outputs NULL), VSA_ERR_SHAPE (num_seqs < 1, a length < 1, totals beyond
- * 2^31 slots), VSA_ERR_TOPK (a topk < 1).  No device memory is touched.
+ * outputs NULL), VSA_ERR_UNSUPPORTED (block_size), VSA_ERR_SHAPE
+ * (num_seqs < 1, a length < 1, totals beyond 2^31 slots), VSA_ERR_TOPK (a
+ * topk < 1).  No device memory is touched.
  */
 int vsa_build_metadata(int32_t num_seqs, const int32_t *seqlens_q, const int32_t *seqlens_kv,
-                       const int32_t *topk, vsa_meta_sizes *sizes, int32_t *cu_blocks_q,
+                       const int32_t *topk, int32_t block_size, vsa_meta_sizes *sizes, int32_t *cu_blocks_q,
                        int32_t *cu_blocks_kv, int32_t *block_sizes_q, int32_t *block_sizes_kv,
                        int32_t *topk_clamped);
 
@@ -286,9 +289,10 @@ int vsa_forward_bshd(const vsa_bf16 *q, const vsa_bf16 *k, const vsa_bf16 *v, co
  * Summary / How it works; "[chore] release fastvideo-kernel 0.3.0",
  * varlen block-sparse attention with Q/KV length mismatch).
  *
- * q [H, 64*Nq, D], k/v [H, 64*Nkv, D], out [H, 64*Nq, D] (padding slots of out
- * are written with 0).  The device metadata arrays and sizes are those of
- * vsa_build_metadata (topk_per_seq = its topk_clamped).  q2k_idx holds global
+ * q [H, bs*Nq, D], k/v [H, bs*Nkv, D], out [H, bs*Nq, D] with bs =
+ * block_size (padding slots of out are written with 0).  The device metadata
+ * arrays and sizes are those of vsa_build_metadata for the same block_size
+ * (topk_per_seq = its topk_clamped).  q2k_idx holds global
  * KV block numbers.  Optional outputs and workspace as for vsa_forward.
  */
 int vsa_forward_varlen(const vsa_bf16 *q, const vsa_bf16 *k, const vsa_bf16 *v,
@@ -309,15 +313,15 @@ int vsa_forward_varlen(const vsa_bf16 *q, const vsa_bf16 *k, const vsa_bf16 *v,
  * attention improvements: block-sparse attention forward and backward.)
  * The backward is the gradient of the forward with the routing (q2k_idx)
  * held fixed: the top-k choice is piecewise constant and carries none.
- * Both take every problem the forward takes: DENSE and BSHD tensors with
- * VSA blocks of 64, 128 or 256 tokens, PACKED with 64.
+ * Both take every problem the forward takes: every layout, VSA blocks of
+ * 64, 128 or 256 tokens.
  */
 
 /*
  * vsa_sparse_attn_combine_train - vsa_sparse_attn_combine that also writes
  * out_s, the bf16 normalised block-sparse attention output on its own (query
  * layout, padding slots of PACKED written with 0), and lse, float32, one per
- * query row ([B, H, Sq] for DENSE and for BSHD, [H, 64*Nq] PACKED, padding
+ * query row ([B, H, Sq] for DENSE and for BSHD, [H, bs*Nq] PACKED, padding
  * slots not written):
  * log2 of the softmax denominator of the row in units where the row's
  * probabilities are exp2(s * log2(e) / sqrt(D) - lse) for raw scores s = q.k
@@ -355,7 +359,7 @@ size_t vsa_backward_workspace_size(const vsa_problem *problem);
  * Outputs (bf16, written in full, PACKED padding slots with 0): dq in the
  * query layout, dk and dv in the KV layout, and for a gate dgate, contiguous
  * in the query layout whatever gate_strides were: [B, H, Sq] (BSHD:
- * [B, Sq, H]) / [H, 64*Nq] for VSA_GATE_TOKEN, the same with a trailing D for
+ * [B, Sq, H]) / [H, bs*Nq] for VSA_GATE_TOKEN, the same with a trailing D for
  * VSA_GATE_FULL (NULL and unused for VSA_GATE_NONE).  With VSA blocks of 128
  * or 256 tokens the gradients through the block means spread dQc, dKc, dVc
  * over the valid tokens of each VSA block.

@@ -59,15 +59,16 @@ class DenseInputs:
 
 @dataclass
 class VarlenInputs:
-    q: torch.Tensor  # [H, 64*sum(nQ), D] bf16, block-padded, zero padding
-    k: torch.Tensor  # [H, 64*sum(nKV), D]
+    q: torch.Tensor  # [H, block*sum(nQ), D] bf16, block-padded, zero padding
+    k: torch.Tensor  # [H, block*sum(nKV), D]
     v: torch.Tensor
-    gate: Optional[torch.Tensor]  # [H, 64*sum(nQ)] or None
+    gate: Optional[torch.Tensor]  # [H, block*sum(nQ)] or None
     seqlens_q: List[int]
     seqlens_kv: List[int]
     topk: List[int]  # requested per-sequence top-k (before any clamping)
     name: str = ""
     per_seq: List[Dict[str, torch.Tensor]] = field(default_factory=list)
+    block: int = BLOCK  # slots per block (the VSA block size)
 
     @property
     def heads(self) -> int:
@@ -101,15 +102,15 @@ def dense_inputs(B: int, H: int, S: int, D: int, topk: int, seed: int,
 
 def varlen_inputs(seqlens_q: List[int], seqlens_kv: Optional[List[int]], H: int,
                   D: int, topk: List[int], seed: int, gated: bool = False,
-                  name: str = "") -> VarlenInputs:
+                  name: str = "", block: int = BLOCK) -> VarlenInputs:
     seqlens_kv = list(seqlens_q) if seqlens_kv is None else list(seqlens_kv)
     assert len(seqlens_q) == len(seqlens_kv) == len(topk)
-    nq = [_ceil_div(s, BLOCK) for s in seqlens_q]
-    nkv = [_ceil_div(s, BLOCK) for s in seqlens_kv]
-    q = torch.zeros(H, BLOCK * sum(nq), D, dtype=torch.bfloat16)
-    k = torch.zeros(H, BLOCK * sum(nkv), D, dtype=torch.bfloat16)
+    nq = [_ceil_div(s, block) for s in seqlens_q]
+    nkv = [_ceil_div(s, block) for s in seqlens_kv]
+    q = torch.zeros(H, block * sum(nq), D, dtype=torch.bfloat16)
+    k = torch.zeros(H, block * sum(nkv), D, dtype=torch.bfloat16)
     v = torch.zeros_like(k)
-    gate = torch.zeros(H, BLOCK * sum(nq), dtype=torch.bfloat16) if gated else None
+    gate = torch.zeros(H, block * sum(nq), dtype=torch.bfloat16) if gated else None
     gen = torch.Generator().manual_seed(seed)
     per_seq = []
     oq = okv = 0
@@ -124,10 +125,10 @@ def varlen_inputs(seqlens_q: List[int], seqlens_kv: Optional[List[int]], H: int,
         if gated:
             gate[:, oq:oq + sq] = gs
         per_seq.append({"q": qs, "k": ks, "v": vs, "gate": gs})
-        oq += BLOCK * nq[s]
-        okv += BLOCK * nkv[s]
+        oq += block * nq[s]
+        okv += block * nkv[s]
     return VarlenInputs(q, k, v, gate, list(seqlens_q), seqlens_kv, list(topk),
-                        name, per_seq)
+                        name, per_seq, block)
 
 
 def output_grad(shape, seed: int) -> torch.Tensor:

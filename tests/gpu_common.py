@@ -66,7 +66,7 @@ def run_dense_stages(inp, dev=DEV, idx_override=None, block_size=64, bshd=False)
 
 
 def run_varlen_stages(inp, dev=DEV, idx_override=None):
-    meta = vsa.vsa_build_metadata(inp.seqlens_q, inp.seqlens_kv, inp.topk, device=dev)
+    meta = vsa.vsa_build_metadata(inp.seqlens_q, inp.seqlens_kv, inp.topk, device=dev, block_size=inp.block)
     H, D = inp.heads, inp.head_dim
     prob = meta.problem(H, D)
     q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
@@ -101,7 +101,7 @@ def oracle_dense(inp, blocks=None, block=64):
 def oracle_varlen(inp, blocks=None):
     g = None if inp.gate is None else f64(inp.gate)
     return oracle.vsa_forward_varlen(f64(inp.q), f64(inp.k), f64(inp.v), inp.seqlens_q,
-                                     inp.seqlens_kv, inp.topk, g, blocks=blocks)
+                                     inp.seqlens_kv, inp.topk, g, blocks=blocks, block=inp.block)
 
 
 def assert_tie_free(ref):

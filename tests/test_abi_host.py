@@ -58,33 +58,34 @@ def test_status_strings(lib):
 # metadata
 # ---------------------------------------------------------------------------
 
-def _meta(lib, sq, skv, topk):
+def _meta(lib, sq, skv, topk, block=64):
     n = len(sq)
     arr = lambda xs: (ctypes.c_int32 * max(len(xs), 1))(*xs)
     sizes = VsaMetaSizes()
-    rc = lib.vsa_build_metadata(n, arr(sq), None if skv is None else arr(skv), arr(topk),
+    rc = lib.vsa_build_metadata(n, arr(sq), None if skv is None else arr(skv), arr(topk), block,
                                 ctypes.byref(sizes), None, None, None, None, None)
     if rc:
         return rc, sizes, None
     bufs = [(ctypes.c_int32 * (n + 1))(), (ctypes.c_int32 * (n + 1))(),
             (ctypes.c_int32 * sizes.total_q_blocks)(), (ctypes.c_int32 * sizes.total_kv_blocks)(),
             (ctypes.c_int32 * n)()]
-    rc = lib.vsa_build_metadata(n, arr(sq), None if skv is None else arr(skv), arr(topk),
+    rc = lib.vsa_build_metadata(n, arr(sq), None if skv is None else arr(skv), arr(topk), block,
                                 ctypes.byref(sizes), *bufs)
     return rc, sizes, [list(b) for b in bufs]
 
 
+@pytest.mark.parametrize("block", [64, 128, 256])
 @pytest.mark.parametrize("sq,skv,topk", [
     ([320, 576, 872], None, [2, 3, 4]),
     ([64 * n for n in range(32, 145, 16)], [64 * (n + 8) for n in range(32, 145, 16)],
      [8, 12, 15, 18, 21, 24, 28, 31]),
     ([1, 65, 130], [200, 1, 64], [5, 1, 1]),
 ])
-def test_metadata_matches_oracle(lib, sq, skv, topk):
-    rc, sizes, (cu_q, cu_kv, bs_q, bs_kv, tk) = _meta(lib, sq, skv, topk)
+def test_metadata_matches_oracle(lib, sq, skv, topk, block):
+    rc, sizes, (cu_q, cu_kv, bs_q, bs_kv, tk) = _meta(lib, sq, skv, topk, block)
     assert rc == 0
     skv_ = sq if skv is None else skv
-    qsz, ksz, ocu_q, ocu_kv = oracle.varlen_metadata(sq, skv_)
+    qsz, ksz, ocu_q, ocu_kv = oracle.varlen_metadata(sq, skv_, block)
     assert cu_q == list(ocu_q) and cu_kv == list(ocu_kv)
     assert bs_q == [n for x in qsz for n in x] and bs_kv == [n for x in ksz for n in x]
     assert tk == [min(t, len(k)) for t, k in zip(topk, ksz)]
@@ -92,7 +93,7 @@ def test_metadata_matches_oracle(lib, sq, skv, topk):
     assert sizes.max_q_blocks == max(len(x) for x in qsz)
     assert sizes.max_kv_blocks == max(len(x) for x in ksz)
     assert sizes.max_topk == max(tk)
-    assert sizes.q_slots == 64 * ocu_q[-1] and sizes.kv_slots == 64 * ocu_kv[-1]
+    assert sizes.q_slots == block * ocu_q[-1] and sizes.kv_slots == block * ocu_kv[-1]
 
 
 def test_metadata_errors(lib):
@@ -100,16 +101,25 @@ def test_metadata_errors(lib):
     assert _meta(lib, [64, 0], None, [1, 1])[0] == _abi.VSA_ERR_SHAPE   # zero-length sequence
     assert _meta(lib, [64], [0], [1])[0] == _abi.VSA_ERR_SHAPE
     assert _meta(lib, [64, 64], None, [1, 0])[0] == _abi.VSA_ERR_TOPK   # topk < 1
+    for bad in (32, 96, 512):
+        assert _meta(lib, [64], None, [1], bad)[0] == _abi.VSA_ERR_UNSUPPORTED
     sizes = VsaMetaSizes()
     one = (ctypes.c_int32 * 1)(64)
-    assert lib.vsa_build_metadata(1, None, None, one, ctypes.byref(sizes),
+    assert lib.vsa_build_metadata(1, None, None, one, 64, ctypes.byref(sizes),
                                   None, None, None, None, None) == _abi.VSA_ERR_NULL
-    assert lib.vsa_build_metadata(1, one, None, one, None, None, None, None, None, None) == _abi.VSA_ERR_NULL
+    assert lib.vsa_build_metadata(1, one, None, one, 64, None, None, None, None, None, None) == _abi.VSA_ERR_NULL
     buf = (ctypes.c_int32 * 2)()
-    assert lib.vsa_build_metadata(1, one, None, one, ctypes.byref(sizes), buf, None, None, None,
+    assert lib.vsa_build_metadata(1, one, None, one, 64, ctypes.byref(sizes), buf, None, None, None,
                                   None) == _abi.VSA_ERR_NULL  # some outputs but not all
-    assert lib.vsa_build_metadata(1, (ctypes.c_int32 * 1)(2 ** 31 - 1), None, one, ctypes.byref(sizes),
+    assert lib.vsa_build_metadata(1, (ctypes.c_int32 * 1)(2 ** 31 - 1), None, one, 64, ctypes.byref(sizes),
                                   None, None, None, None, None) == _abi.VSA_ERR_SHAPE
+    # 2^31 - 255 tokens fit in 64-slot blocks, not in 256-slot ones (2^31 slots)
+    sz = VsaMetaSizes()
+    L = (ctypes.c_int32 * 1)(2 ** 31 - 255)
+    assert lib.vsa_build_metadata(1, L, None, one, 64, ctypes.byref(sz), None, None, None, None, None) == 0
+    assert sz.q_slots == 2 ** 31 - 192
+    assert lib.vsa_build_metadata(1, L, None, one, 256, ctypes.byref(sz), None, None, None, None,
+                                  None) == _abi.VSA_ERR_SHAPE
 
 
 # ---------------------------------------------------------------------------
@@ -206,13 +216,15 @@ E = _abi
     (lambda L: coarse(L, dense(), k=ctypes.c_void_p(FAKE + 2)), E.VSA_ERR_ALIGN),
     (lambda L: coarse(L, dense(bs=96)), E.VSA_ERR_UNSUPPORTED),
     (lambda L: coarse(L, dense(bs=512)), E.VSA_ERR_UNSUPPORTED),
-    (lambda L: coarse(L, packed_bs(128)), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: coarse(L, packed_bs(96)), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: coarse(L, packed_bs(128), wsb=100), E.VSA_ERR_WORKSPACE),
     (lambda L: coarse(L, dense(bs=128, Skv=128 * 4097)), E.VSA_ERR_UNSUPPORTED),
     (lambda L: train_fwd(L, dense(bs=128), lse=None), E.VSA_ERR_NULL),
     (lambda L: train_fwd(L, bshd(), out_s=O_), E.VSA_ERR_ALIAS),
     (lambda L: bwd(L, dense(bs=256), wsb=4096), E.VSA_ERR_WORKSPACE),
     (lambda L: bwd(L, bshd(bs=128), dk=DO_), E.VSA_ERR_ALIAS),
-    (lambda L: bwd(L, packed_bs(128)), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: bwd(L, packed_bs(32)), E.VSA_ERR_UNSUPPORTED),
+    (lambda L: bwd(L, packed_bs(256), wsb=4096), E.VSA_ERR_WORKSPACE),
     (lambda L: L.vsa_forward_bshd(A, B_, C_, None, 0, None, O_, None, None, None, 1, 2, 1000, 1000, 128, 32, 3, W_,
                                   1 << 40, None), E.VSA_ERR_UNSUPPORTED),
     (lambda L: L.vsa_forward_bshd(A, B_, C_, None, 0, None, A, None, None, None, 1, 2, 1000, 1000, 128, 128, 3, W_,
@@ -357,6 +369,15 @@ def test_backward_workspace(lib):
                   bshd(B=1, H=56, Sq=S, Skv=S, D=128, topk=32, bs=bs)):
             ws = lib.vsa_backward_workspace_size(ctypes.byref(p))
             assert floor <= ws <= floor + 13 * 256, (bs, ws, floor)
+    # packed with VSA blocks of 128 / 256 tokens: Nq = 5, Nkv = 6 VSA blocks,
+    # at most 3 / 4 per sequence, H = 2, D = 64
+    for bs in (64, 128, 256):
+        r = bs // 64
+        nq, nkv, mq, mkv, H, D = 5, 6, 3, 4, 2, 64
+        floor = (8 * H * (3 * nq + 4 * nkv) * D + 2 * 8 * 2 * H * mq * mkv
+                 + 4 * H * nq * r * 128 + 4 * H * nkv * r * mq * r + 4 * H * nkv * r)
+        ws = lib.vsa_backward_workspace_size(ctypes.byref(packed_bs(bs)))
+        assert floor <= ws <= floor + 13 * 256, (bs, ws, floor)
 
 
 def test_layout_maps_on_cpu(tmp_path):

@@ -157,15 +157,19 @@ def test_autograd_wrapper_matches_entry_points():
 # packed sequences: every sequence against its own dense oracle
 # ---------------------------------------------------------------------------
 
-def test_backward_varlen_matches_per_sequence():
+@pytest.mark.parametrize("block", [64, 128, 256])
+def test_backward_varlen_matches_per_sequence(block):
+    """With VSA blocks of 128 / 256 slots the packed blocks hold empty 64-token
+    blocks (135 tokens at 256: 64 + 64 + 7 + 0; 129 KV tokens: 64 + 64 + 1 + 0;
+    320 KV tokens: a second VSA block of 64 + 0 + 0 + 0)."""
     seqlens_q = [64 * 2 + 7, 64 * 4, 30]
     seqlens_kv = [64 * 3 + 50, 64 * 2 + 1, 64 * 5]
     topk = [2, 1, 3]
     H, D = 2, 128
-    inp = synth.varlen_inputs(seqlens_q, seqlens_kv, H, D, topk, seed=2060, gated=True)
-    G.note(f"case varlen: seqlens_q={seqlens_q} seqlens_kv={seqlens_kv} topk={topk}")
+    inp = synth.varlen_inputs(seqlens_q, seqlens_kv, H, D, topk, seed=2060 + block, gated=True, block=block)
+    G.note(f"case varlen block={block}: seqlens_q={seqlens_q} seqlens_kv={seqlens_kv} topk={topk}")
     dev = G.DEV
-    meta = vsa.vsa_build_metadata(seqlens_q, seqlens_kv, topk, device=dev)
+    meta = vsa.vsa_build_metadata(seqlens_q, seqlens_kv, topk, device=dev, block_size=block)
     prob = meta.problem(H, D)
     q, k, v, gate = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.gate))
     dout_cpu = synth.output_grad(inp.q.shape, 2061)
@@ -190,7 +194,7 @@ def test_backward_varlen_matches_per_sequence():
         per = inp.per_seq[s]
         g64 = lambda t: N.f64(t)[None]
         ref = BW.vsa_backward(g64(per["q"]), g64(per["k"]), g64(per["v"]), topk[s], g64(per["gate"]),
-                              N.f64(dout_cpu[:, oq:oq + sq])[None])
+                              N.f64(dout_cpu[:, oq:oq + sq])[None], block=block)
         G.assert_tie_free(ref)
         G.note(f"  sequence {s}")
         check_grad(N.f64(dq[:, oq:oq + sq]), ref["dq"][0], "dq")
@@ -199,12 +203,12 @@ def test_backward_varlen_matches_per_sequence():
         check_grad(N.f64(dg[:, oq:oq + sq]), ref["dgate"][0], "dgate")
         dl = float(np.abs(N.f64(lse[:, oq:oq + sq]) - ref["lse"][0]).max())
         assert dl <= LSE_ABS, f"lse of sequence {s}: {dl:.3e}"
-        nq, nkv = -(-sq // 64), -(-skv // 64)
+        nq, nkv = -(-sq // block), -(-skv // block)
         # padding slots of every gradient are written with 0
-        assert (dq[:, oq + sq:oq + 64 * nq] == 0).all() and (dg[:, oq + sq:oq + 64 * nq] == 0).all()
-        assert (dk[:, okv + skv:okv + 64 * nkv] == 0).all() and (dv[:, okv + skv:okv + 64 * nkv] == 0).all()
-        oq += 64 * nq
-        okv += 64 * nkv
+        assert (dq[:, oq + sq:oq + block * nq] == 0).all() and (dg[:, oq + sq:oq + block * nq] == 0).all()
+        assert (dk[:, okv + skv:okv + block * nkv] == 0).all() and (dv[:, okv + skv:okv + block * nkv] == 0).all()
+        oq += block * nq
+        okv += block * nkv
 
 
 # ---------------------------------------------------------------------------

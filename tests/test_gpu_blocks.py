@@ -2,7 +2,8 @@
 (BSHD) entry against the fp64 oracle (which takes the block size as a
 parameter and works on [B, H, S, D]; BSHD inputs are the same tensors
 transposed), on seeded inputs with ragged tails, plus the full-size large
-shape at both block sizes on sampled query blocks."""
+shape at both block sizes on sampled query blocks, and packed sequences with
+VSA blocks of 128 / 256 slots."""
 import numpy as np
 import pytest
 import torch
@@ -115,3 +116,70 @@ def test_large_shape_large_blocks(block, topk):
     gpu = G.run_dense_stages(inp, block_size=block)
     ref = G.oracle_dense(inp, blocks=blocks, block=block)
     _check_all(inp, gpu, ref)
+
+
+# ---------------------------------------------------------------------------
+# packed sequences with VSA blocks of 128 / 256 slots
+# ---------------------------------------------------------------------------
+
+# lengths giving VSA blocks whose trailing 64-token blocks are empty (at 256:
+# 37 tokens = 37 + 0 + 0 + 0, 300 = 256 + (44 + 0 + 0 + 0), 129 = 64 + 64 + 1 + 0)
+_LENS_Q = [3 * 256 + 37, 300, 1, 129, 2 * 256]
+_LENS_KV = [2 * 256 + 9, 300, 70, 256 * 3 - 5, 129]
+_TOPK = [2, 1, 3, 2, 5]
+
+
+@pytest.mark.parametrize("block", [128, 256])
+@pytest.mark.parametrize("gate", ["token", "full", None])
+def test_varlen_large_blocks(block, gate):
+    inp = synth.varlen_inputs(_LENS_Q, _LENS_KV, 3, 128, _TOPK, seed=6000 + block, gated=gate == "token",
+                              block=block)
+    if gate == "full":
+        inp.gate = synth.full_gate(tuple(inp.q.shape), 6001 + block)
+    G.note(f"case varlen block={block} gate={gate} lens_q={_LENS_Q} lens_kv={_LENS_KV}")
+    ref = G.oracle_varlen(inp)
+    gpu = G.run_varlen_stages(inp)
+    _check_all(inp, gpu, ref)
+    # padding slots (including whole empty 64-token blocks) hold 0
+    o = 0
+    for sq in inp.seqlens_q:
+        nb = -(-sq // block)
+        for key in ("out", "out_s", "out_fused"):
+            assert (gpu[key][:, o + sq:o + block * nb] == 0).all(), key
+        o += block * nb
+    # the one-call packed forward launches the same kernels: identical bits
+    dev = G.DEV
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    g = None if inp.gate is None else inp.gate.to(dev)
+    out, oc, idx, num = vsa.vsa_forward_varlen(q, k, v, gpu["meta"], g, return_aux=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), gpu["out_fused"])
+    assert torch.equal(oc.cpu(), gpu["out_c"])
+    assert torch.equal(idx.cpu(), gpu["q2k_idx"])
+    assert torch.equal(num.cpu(), gpu["q2k_num"])
+
+
+@pytest.mark.parametrize("block", [128, 256])
+def test_varlen_large_blocks_equals_per_sequence(block):
+    """One packed launch with 128- / 256-slot blocks gives the bits of one
+    dense launch per sequence with the same VSA block size (indices rebased)."""
+    D = 64
+    inp = synth.varlen_inputs(_LENS_Q, _LENS_KV, 2, D, _TOPK, seed=6100 + block, gated=True, block=block)
+    G.note(f"case varlen = per sequence, block={block}")
+    packed = G.run_varlen_stages(inp)
+    oq = bq = bkv = 0
+    for s, seq in enumerate(inp.per_seq):
+        d = synth.DenseInputs(seq["q"][None], seq["k"][None], seq["v"][None], seq["gate"][None], _TOPK[s])
+        one = G.run_dense_stages(d, block_size=block)
+        nq, nkv = -(-_LENS_Q[s] // block), -(-_LENS_KV[s] // block)
+        kk = min(_TOPK[s], nkv)
+        sl = slice(oq, oq + _LENS_Q[s])
+        for key in ("out", "out_s", "out_fused"):
+            assert torch.equal(packed[key][:, sl], one[key][0]), (s, key)
+        assert torch.equal(packed["out_c"][:, bq:bq + nq], one["out_c"][0]), s
+        pi = packed["q2k_idx"][:, bq:bq + nq]
+        assert torch.equal(pi[..., :kk], one["q2k_idx"][0] + bkv), s
+        assert (pi[..., kk:] == -1).all()
+        oq += block * nq
+        bq += nq
+        bkv += nkv

@@ -53,7 +53,7 @@ P_PROBLEM = ctypes.POINTER(VsaProblem)
 
 # name -> (restype, argtypes); the exported symbols of include/vsa.h
 SIGNATURES = {
-    "vsa_build_metadata": (i32, [i32, vp, vp, vp, ctypes.POINTER(VsaMetaSizes), vp, vp, vp, vp, vp]),
+    "vsa_build_metadata": (i32, [i32, vp, vp, vp, i32, ctypes.POINTER(VsaMetaSizes), vp, vp, vp, vp, vp]),
     "vsa_workspace_size": (sz, [P_PROBLEM]),
     "vsa_coarse_topk": (i32, [P_PROBLEM, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
     "vsa_sparse_attn_from_indices": (i32, [P_PROBLEM, vp, vp, vp, vp, vp, vp, vp]),

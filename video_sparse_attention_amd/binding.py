@@ -85,6 +85,7 @@ class VarlenMeta:
     block_sizes_kv: torch.Tensor
     topk: torch.Tensor             # host int32 [num_seqs], clamped
     device_arrays: Optional[dict] = None
+    block_size: int = BLOCK        # VSA block: slots per block
 
     def to(self, device) -> "VarlenMeta":
         names = ("cu_blocks_q", "cu_blocks_kv", "block_sizes_q", "block_sizes_kv", "topk")
@@ -97,7 +98,7 @@ class VarlenMeta:
         d = self.device_arrays
         s = self.sizes
         return VsaProblem(
-            layout=VSA_LAYOUT_PACKED, heads=heads, head_dim=head_dim, block_size=BLOCK,
+            layout=VSA_LAYOUT_PACKED, heads=heads, head_dim=head_dim, block_size=self.block_size,
             num_seqs=s.num_seqs, total_q_blocks=s.total_q_blocks,
             total_kv_blocks=s.total_kv_blocks, max_q_blocks=s.max_q_blocks,
             max_kv_blocks=s.max_kv_blocks, max_topk=s.max_topk,
@@ -107,8 +108,9 @@ class VarlenMeta:
 
 
 def vsa_build_metadata(seqlens_q: Sequence[int], seqlens_kv: Optional[Sequence[int]] = None,
-                       topk: Sequence[int] = (), device=None) -> VarlenMeta:
-    """Host block metadata for packed sequences (vsa_build_metadata)."""
+                       topk: Sequence[int] = (), device=None, block_size: int = BLOCK) -> VarlenMeta:
+    """Host block metadata for packed sequences (vsa_build_metadata), VSA
+    blocks of ``block_size`` (64, 128 or 256) tokens and slots."""
     lib = _abi.load()
     n = len(seqlens_q)
     sq = (ctypes.c_int32 * max(n, 1))(*seqlens_q)
@@ -117,17 +119,17 @@ def vsa_build_metadata(seqlens_q: Sequence[int], seqlens_kv: Optional[Sequence[i
         raise ValueError("topk needs one entry per sequence")
     tk = (ctypes.c_int32 * max(n, 1))(*topk)
     sizes = VsaMetaSizes()
-    _abi.check(lib.vsa_build_metadata(n, sq, skv, tk, ctypes.byref(sizes),
+    _abi.check(lib.vsa_build_metadata(n, sq, skv, tk, block_size, ctypes.byref(sizes),
                                       None, None, None, None, None), "vsa_build_metadata")
     cu_q = torch.zeros(n + 1, dtype=torch.int32)
     cu_kv = torch.zeros(n + 1, dtype=torch.int32)
     bs_q = torch.zeros(sizes.total_q_blocks, dtype=torch.int32)
     bs_kv = torch.zeros(sizes.total_kv_blocks, dtype=torch.int32)
     tkc = torch.zeros(n, dtype=torch.int32)
-    _abi.check(lib.vsa_build_metadata(n, sq, skv, tk, ctypes.byref(sizes), _ptr(cu_q), _ptr(cu_kv),
-                                      _ptr(bs_q), _ptr(bs_kv), _ptr(tkc)), "vsa_build_metadata")
+    _abi.check(lib.vsa_build_metadata(n, sq, skv, tk, block_size, ctypes.byref(sizes), _ptr(cu_q),
+                                      _ptr(cu_kv), _ptr(bs_q), _ptr(bs_kv), _ptr(tkc)), "vsa_build_metadata")
     meta = VarlenMeta(sizes, list(seqlens_q), list(seqlens_q if seqlens_kv is None else seqlens_kv),
-                      cu_q, cu_kv, bs_q, bs_kv, tkc)
+                      cu_q, cu_kv, bs_q, bs_kv, tkc, block_size=block_size)
     return meta.to(device) if device is not None else meta
 
 
@@ -174,7 +176,8 @@ def token_shapes(problem: VsaProblem):
     if problem.layout == VSA_LAYOUT_BSHD:
         b = problem.batch
         return (b, problem.seqlen_q, h, d), (b, problem.seqlen_kv, h, d)
-    return (h, BLOCK * problem.total_q_blocks, d), (h, BLOCK * problem.total_kv_blocks, d)
+    bs = problem.block_size
+    return (h, bs * problem.total_q_blocks, d), (h, bs * problem.total_kv_blocks, d)
 
 
 # ---------------------------------------------------------------------------
@@ -442,9 +445,9 @@ def vsa_forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, meta: 
                        workspace: Optional[torch.Tensor] = None, return_aux: bool = False):
     """VSA forward over block-padded packed sequences (vsa_forward_varlen).
 
-    ``q`` is ``[H, 64*Nq, D]``, ``k``/``v`` ``[H, 64*Nkv, D]``; ``meta`` from
-    ``vsa_build_metadata(..., device=q.device)``.  ``gate``: None,
-    ``[H, 64*Nq]`` or ``[H, 64*Nq, D]``.
+    ``q`` is ``[H, bs*Nq, D]``, ``k``/``v`` ``[H, bs*Nkv, D]`` with bs the
+    metadata's block size; ``meta`` from ``vsa_build_metadata(...,
+    device=q.device)``.  ``gate``: None, ``[H, bs*Nq]`` or ``[H, bs*Nq, D]``.
     """
     if q.dim() != 3:
         raise ValueError("packed q must be [H, slots, D]")
@@ -472,7 +475,7 @@ def vsa_forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, meta: 
         _ptr(q), _ptr(k), _ptr(v), _ptr(gate), mode, st, _ptr(out), _ptr(idx), _ptr(num), _ptr(oc),
         _ptr(d["cu_blocks_q"]), _ptr(d["cu_blocks_kv"]), _ptr(d["block_sizes_q"]),
         _ptr(d["block_sizes_kv"]), _ptr(d["topk"]), s.num_seqs, s.total_q_blocks,
-        s.total_kv_blocks, s.max_q_blocks, s.max_kv_blocks, s.max_topk, H, D, BLOCK,
+        s.total_kv_blocks, s.max_q_blocks, s.max_kv_blocks, s.max_topk, H, D, meta.block_size,
         _ptr(workspace), workspace.numel(), _stream(q.device)), "vsa_forward_varlen")
     return (out, *aux) if return_aux else out
 

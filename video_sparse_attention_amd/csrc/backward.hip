@@ -86,10 +86,10 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
         I = (int)blockIdx.x - clampi(P.cu_q[s], 0, P.total_q);
     }
     const SeqView sv = seq_view(P, s, h);
-    const int R = P.packed ? 1 : P.ratio;  // 64-token query blocks per VSA block
+    const int R = P.ratio;  // 64-token query blocks per VSA block
     if (I < 0 || R * I >= sv.nq) return;
     // row of the VSA block in the block-resolution arrays (out_c, dOc)
-    const int64_t cb = P.packed ? sv.qblk_base + I : ((int64_t)s * P.H + h) * P.nQB + I;
+    const int64_t cb = sv.qvsa_base + I;
     const int64_t g0 = (P.packed ? 0 : (int64_t)s * gs0) + (int64_t)h * gs1;
     const int t = threadIdx.x / 4, d0 = (threadIdx.x % 4) * QD;
     const float* ocr = out_c + cb * D;
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void bwd_combine_kernel(
         const int64_t row0 = sv.qrow_base + (int64_t)kBlock * i;  // row of token 0 in [.., S] arrays (lse)
         const int64_t qb = sv.qblk_base + i;                       // 64-token block (statistics)
         // token index of the block's first row along the gate's token axis
-        const int64_t tok0 = (int64_t)kBlock * (P.packed ? sv.qblk0 + i : i);
+        const int64_t tok0 = (int64_t)kBlock * (P.packed ? sv.qblk0 * R + i : i);
         // element offset of token t of this block in dout / out_s / a full dgate
         const int64_t qo = sv.q_off + ((int64_t)kBlock * i + t) * sv.q_st;
         float dpart = 0.f, gpart = 0.f;
@@ -337,17 +337,19 @@ __global__ __launch_bounds__(kThreads) void bwd_k2q_kernel(DevProblem P, const i
     const int j = blockIdx.x * (kThreads / 64) + wave;
     const SeqView sv = seq_view(P, s, h);
     if (j >= sv.nkv) return;
-    // lists hold VSA blocks of 64 * ratio tokens (dense; 64 when packed)
+    // lists hold VSA blocks of 64 * ratio tokens
     const int lr = P.ratio >> 1;
     const int key = (j >> lr) + sv.idx_rebase;  // as stored in q2k_idx
     const int64_t kb = sv.kvblk_base + j;
-    const int64_t vbase = P.packed ? sv.qblk_base : ((int64_t)s * P.H + h) * P.nQB;
+    // an empty 64-token block of a packed VSA block (KV or query side) takes
+    // part in no product
+    const bool kv_empty = P.packed && lr > 0 && kv_block_size(P, sv, j) == 0;
     int count = 0;
-    for (int i0 = 0; i0 < sv.nq; i0 += 64) {
+    for (int i0 = 0; i0 < sv.nq && !kv_empty; i0 += 64) {
         const int i = i0 + lane;
         bool member = false;
-        if (i < sv.nq) {
-            const int64_t qb = vbase + (i >> lr);  // the list of i's VSA block
+        if (i < sv.nq && (!P.packed || lr == 0 || q_block_size(P, sv, i) > 0)) {
+            const int64_t qb = sv.qvsa_base + (i >> lr);  // the list of i's VSA block
             member = list_has(idx + qb * P.idx_row, clampi(num[qb], 0, P.idx_row), key);
         }
         const uint64_t mask = __ballot(member);
@@ -441,23 +443,24 @@ __global__ __launch_bounds__(kAttnThreads, 2) void bwd_dq_kernel(
         s = rest / P.H;
         sv = seq_view(P, s, h);
     } else {
-        const int N = P.total_q * P.H;
+        const int lr = P.ratio >> 1;
+        const int N = (P.total_q << lr) * P.H;
         const int lin = xcd_remap(blockIdx.x, N);
-        const int g = lin % P.total_q;
-        h = lin / P.total_q;
-        s = seq_of_qblock(P, g);
+        const int g = lin % (P.total_q << lr);
+        h = lin / (P.total_q << lr);
+        s = seq_of_qblock(P, g >> lr);
         sv = seq_view(P, s, h);
-        i = g - sv.qblk0;
+        i = g - (sv.qblk0 << lr);
         if (i < 0 || i >= sv.nq) return;
     }
-    const int qsize = q_block_size(P, sv, i);
+    const int qsize = q_block_size(P, sv, i);  // 0: an empty block of a packed VSA block
     const int64_t qoff0 = sv.q_off + (int64_t)kBlock * i * sv.q_st;  // element offset of the block's row 0
     const int64_t qb = sv.qblk_base + i;                              // 64-token block (statistics)
-    // VSA blocks of 64 * ratio tokens (dense): the list, out_c and dQc are
-    // per VSA block; a listed VSA block J stands for 64-token KV blocks
+    // VSA blocks of 64 * ratio tokens: the list, out_c and dQc are per VSA
+    // block; a listed VSA block J stands for 64-token KV blocks
     // J ratio .. J ratio + ratio - 1
     const int lr = P.ratio >> 1;
-    const int64_t qbv = P.packed ? qb : ((int64_t)s * P.H + h) * P.nQB + (i >> lr);
+    const int64_t qbv = sv.qvsa_base + (i >> lr);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
     const int qr = 32 * wave + l32;
     const bool qvalid = qr < qsize;
@@ -474,28 +477,30 @@ __global__ __launch_bounds__(kAttnThreads, 2) void bwd_dq_kernel(
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
 
-    const int nsel = __builtin_amdgcn_readfirstlane(clampi(num[qbv], 0, P.idx_row));
+    const int nsel = __builtin_amdgcn_readfirstlane(qsize > 0 ? clampi(num[qbv], 0, P.idx_row) : 0);
     const int n = nsel << lr;  // 64-token KV blocks to visit
     const_int* list = (const_int*)uniform_ptr(idx + qbv * P.idx_row);
     const_int* bs_kv = (const_int*)(P.packed ? uniform_ptr(P.bs_kv + sv.kvblk0) : nullptr);
     const int rebase = __builtin_amdgcn_readfirstlane(sv.idx_rebase);
     const int nkv = __builtin_amdgcn_readfirstlane(sv.nkv);
     const int t0 = n > 0 ? ((i % kSweepDq) * n) / kSweepDq : 0;
+    // valid tokens of local KV block j (packed: 0 for an empty 64-token block
+    // of a VSA block)
+    auto kv_size = [&](int j) -> int {
+        return P.packed ? packed_sub_size(bs_kv[j >> lr], j & ((1 << lr) - 1)) : min(kBlock, P.Skv - kBlock * j);
+    };
     auto next_valid = [&](int& t) -> int {
         for (; t < n; ++t) {
             int pos = t0 + t;
             if (pos >= n) pos -= n;
-            const int J = list[pos >> lr];
+            const int J = list[pos >> lr] - rebase;
             // no sequence has 2^28 VSA blocks: such an entry (or a negative
             // one) is out of range, and is kept from wrapping by the shift
-            if (lr > 0 && (unsigned)J >= (1u << 28)) continue;
-            const int j = (J << lr) + (pos & ((1 << lr) - 1)) - rebase;
-            if (j >= 0 && j < nkv) return j;
+            if ((unsigned)J >= (1u << 28)) continue;
+            const int j = (J << lr) + (pos & ((1 << lr) - 1));
+            if (j < nkv && (lr == 0 || !P.packed || kv_size(j) > 0)) return j;
         }
         return -1;
-    };
-    auto kv_size = [&](int j) -> int {
-        return P.packed ? clampi(bs_kv[j], 1, kBlock) : min(kBlock, P.Skv - kBlock * j);
     };
     // both tiles in the dual layout (V is only read by rows, which that layout
     // serves without conflicts too), so they share every lane offset
@@ -616,7 +621,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void bwd_dq_kernel(
     if (qvalid) {
         // the gradient through the block mean: dQc over the VSA block's valid tokens
         const double* cr = dqc + qbv * D;
-        const int vsize = P.packed ? qsize : min(kBlock << lr, P.Sq - (kBlock << lr) * (i >> lr));
+        const int vsize = P.packed ? clampi(P.bs_q[sv.qblk0 + (i >> lr)], 1, kBlock << lr)
+                                   : min(kBlock << lr, P.Sq - (kBlock << lr) * (i >> lr));
         const float inv_size = 1.f / (float)vsize;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -690,21 +696,22 @@ __global__ __launch_bounds__(kDkdvThreads, 3) void bwd_dkdv_kernel(
         s = rest / P.H;
         sv = seq_view(P, s, h);
     } else {
-        const int N = P.total_kv * P.H;
+        const int lr = P.ratio >> 1;
+        const int N = (P.total_kv << lr) * P.H;
         const int lin = xcd_remap(blockIdx.x, N);
-        const int g = lin % P.total_kv;
-        h = lin / P.total_kv;
-        s = seq_of_kvblock(P, g);
+        const int g = lin % (P.total_kv << lr);
+        h = lin / (P.total_kv << lr);
+        s = seq_of_kvblock(P, g >> lr);
         sv = seq_view(P, s, h);
-        j = g - sv.kvblk0;
+        j = g - (sv.kvblk0 << lr);
         if (j < 0 || j >= sv.nkv) return;
     }
-    const int kvsize = kv_block_size(P, sv, j);
+    const int kvsize = kv_block_size(P, sv, j);  // 0: an empty block of a packed VSA block (no list)
     const int64_t kvoff0 = sv.kv_off + (int64_t)kBlock * j * sv.kv_st;  // element offset of the block's row 0
     const int64_t kb = sv.kvblk_base + j;                               // 64-token block (inverse lists)
-    // dKc / dVc are per VSA block of 64 * ratio tokens (dense)
+    // dKc / dVc are per VSA block of 64 * ratio tokens
     const int lr = P.ratio >> 1;
-    const int64_t kbv = P.packed ? kb : ((int64_t)s * P.H + h) * P.nKVB + (j >> lr);
+    const int64_t kbv = sv.kvvsa_base + (j >> lr);
     // wave, token group and role are wave-uniform: readfirstlane puts them in
     // scalar registers, so role-dependent code is branched over, not selected
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -728,8 +735,9 @@ __global__ __launch_bounds__(kDkdvThreads, 3) void bwd_dkdv_kernel(
     const_int* list = (const_int*)uniform_ptr(k2q + kb * ldq);
     const_int* bs_q = (const_int*)(P.packed ? uniform_ptr(P.bs_q + sv.qblk0) : nullptr);
     const int nq = __builtin_amdgcn_readfirstlane(sv.nq);
+    // valid rows of local query block i (the lists hold no empty block)
     auto q_size = [&](int i) -> int {
-        return P.packed ? clampi(bs_q[i], 1, kBlock) : min(kBlock, P.Sq - kBlock * i);
+        return P.packed ? packed_sub_size(bs_q[i >> lr], i & ((1 << lr) - 1)) : min(kBlock, P.Sq - kBlock * i);
     };
     const int x0 = m > 0 ? ((j % kSweepDkdv) * m) / kSweepDkdv : 0;
     auto entry = [&](int x) -> int {
@@ -883,7 +891,8 @@ __global__ __launch_bounds__(kDkdvThreads, 3) void bwd_dkdv_kernel(
     if (kvalid) {
         // the gradient through the block means, over the VSA block's valid tokens
         const double* cr = (role ? dkc : dvc) + kbv * D;
-        const int vsize = P.packed ? kvsize : min(kBlock << lr, P.Skv - (kBlock << lr) * (j >> lr));
+        const int vsize = P.packed ? clampi(P.bs_kv[sv.kvblk0 + (j >> lr)], 1, kBlock << lr)
+                                   : min(kBlock << lr, P.Skv - (kBlock << lr) * (j >> lr));
         const float inv_size = 1.f / (float)vsize;
         const float mul = role ? scale : 1.f;  // dK = Q^T dS / sqrt(D)
 #pragma unroll
@@ -908,14 +917,14 @@ __global__ __launch_bounds__(kDkdvThreads, 3) void bwd_dkdv_kernel(
 template <int D>
 hipError_t launch_all(const DevProblem& P, const BwdArgs& A, hipStream_t st) {
     const int seqs = P.nseq;
-    // the coarse branch works on VSA blocks (64 * ratio tokens, dense), the
+    // the coarse branch works on VSA blocks (64 * ratio tokens), the
     // attention kernels and the inverse lists on 64-token blocks
     const DevProblem CP = coarse_view(P);
     const int qgrid = P.packed ? P.total_q : P.nQB;
     const int maxq = P.packed ? P.max_q : P.nQB;
     const int maxkv = P.packed ? P.max_kv : P.nKVB;
-    const int maxq64 = P.packed ? P.max_q : P.nQ;
-    const int maxkv64 = P.packed ? P.max_kv : P.nKV;
+    const int maxq64 = P.packed ? P.max_q * P.ratio : P.nQ;
+    const int maxkv64 = P.packed ? P.max_kv * P.ratio : P.nKV;
     const double scale = 1.0 / sqrt((double)D);
     const float c_log2 = (float)(1.4426950408889634 * scale);
     hipError_t e;
@@ -963,8 +972,8 @@ hipError_t launch_all(const DevProblem& P, const BwdArgs& A, hipStream_t st) {
                        A.k2q, A.k2q_num, maxq64);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // 5. dQ, 6. dK / dV
-    const int64_t nq_all = P.packed ? (int64_t)P.total_q * P.H : (int64_t)P.nQ * P.H * P.nseq;
-    const int64_t nkv_all = P.packed ? (int64_t)P.total_kv * P.H : (int64_t)P.nKV * P.H * P.nseq;
+    const int64_t nq_all = P.packed ? (int64_t)P.total_q * P.ratio * P.H : (int64_t)P.nQ * P.H * P.nseq;
+    const int64_t nkv_all = P.packed ? (int64_t)P.total_kv * P.ratio * P.H : (int64_t)P.nKV * P.H * P.nseq;
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)nq_all), dim3(kAttnThreads), 0, st, P, A.q, A.k, A.v, A.dout,
                        A.rs, A.idx, A.num, A.dqc, A.dq, c_log2, (float)scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -976,8 +985,8 @@ hipError_t launch_all(const DevProblem& P, const BwdArgs& A, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_backward(const DevProblem& P, const BwdArgs& A, hipStream_t st) {
-    const int64_t nq_all = P.packed ? (int64_t)P.total_q * P.H : (int64_t)P.nQ * P.H * P.nseq;
-    const int64_t nkv_all = P.packed ? (int64_t)P.total_kv * P.H : (int64_t)P.nKV * P.H * P.nseq;
+    const int64_t nq_all = P.packed ? (int64_t)P.total_q * P.ratio * P.H : (int64_t)P.nQ * P.H * P.nseq;
+    const int64_t nkv_all = P.packed ? (int64_t)P.total_kv * P.ratio * P.H : (int64_t)P.nKV * P.H * P.nseq;
     if (nq_all <= 0 || nq_all > 0x7fffffff || nkv_all <= 0 || nkv_all > 0x7fffffff) return hipErrorInvalidValue;
     return P.D == 128 ? launch_all<128>(P, A, st) : launch_all<64>(P, A, st);
 }

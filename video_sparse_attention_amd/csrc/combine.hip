@@ -45,14 +45,15 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DevProblem P, con
         off0 = (int64_t)b * P.q_sb + (int64_t)h * P.q_sh + (int64_t)kBlock * blk * st;
         cb = sh * P.nQB + blk / P.ratio;  // out_c is at VSA-block resolution
         g_base = (int64_t)b * gs0 + (int64_t)h * gs1 + (int64_t)kBlock * blk * gs2;
-    } else {
-        const int g = blockIdx.x, h = blockIdx.y;
-        if (g >= P.total_q) return;
-        size = clampi(P.bs_q[g], 1, kBlock);
+    } else {  // 64-token block blk of the packed slots, in VSA block blk / ratio
+        const int blk = blockIdx.x, h = blockIdx.y;
+        const int lr = P.ratio >> 1;
+        if (blk >= (P.total_q << lr)) return;
+        size = packed_sub_size(P.bs_q[blk >> lr], blk & ((1 << lr) - 1));
         st = D;
-        off0 = ((int64_t)h * P.total_q + g) * kBlock * D;
-        cb = (int64_t)h * P.total_q + g;
-        g_base = (int64_t)h * gs1 + (int64_t)kBlock * g * gs2;
+        off0 = ((int64_t)h * (P.total_q << lr) + blk) * kBlock * D;
+        cb = (int64_t)h * P.total_q + (blk >> lr);
+        g_base = (int64_t)h * gs1 + (int64_t)kBlock * blk * gs2;
     }
     const int c = threadIdx.x % CH;
     const int tg = threadIdx.x / CH;
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DevProblem P, con
 template <int D>
 hipError_t launch_d(const DevProblem& P, const float* out_c, const uint16_t* gate, int mode,
                     int64_t gs0, int64_t gs1, int64_t gs2, uint16_t* out, hipStream_t st) {
-    dim3 grid = P.packed ? dim3(P.total_q, P.H, 1) : dim3(P.nQ, P.H, P.nseq);
+    dim3 grid = P.packed ? dim3(P.total_q * P.ratio, P.H, 1) : dim3(P.nQ, P.H, P.nseq);
     dim3 block(kCombThreads);
     if (mode == 0)
         hipLaunchKernelGGL((combine_kernel<D, 0>), grid, block, 0, st, P, out_c, gate, gs0, gs1, gs2, out);

@@ -3,9 +3,8 @@
 // coarse/sparse combine", Problem and Notes).
 //
 // HBM-bound streaming kernel.  Thread (block, slice s, c) owns the 16-byte
-// chunk c (8 consecutive d) of tokens s, s + 4, s + 8, ... of one block (64
-// tokens; 64 * ratio tokens for the VSA blocks of 128 or 256 tokens of the
-// dense layouts) and walks them with independent 16-byte loads (8 in flight
+// chunk c (8 consecutive d) of tokens s, s + 4, s + 8, ... of one VSA block
+// (64 * ratio tokens, ratio 1, 2 or 4) and walks them with independent 16-byte loads (8 in flight
 // per thread), accumulating 8 sums in float64 registers; the 4 slices of a
 // chunk then add their sums with lane shuffles (no LDS).  The 4 CH threads of
 // a block (CH = D/8) read 4 consecutive token rows per load instruction, 4
@@ -59,9 +58,10 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(DevProblem P, const 
     } else {
         const int nb = which == 0 ? P.total_q : P.total_kv;
         if (blk >= nb) return;
-        size = clampi(which == 0 ? P.bs_q[blk] : P.bs_kv[blk], 1, kBlock);
+        const int bt = kBlock * P.ratio;  // slots per block
+        size = clampi(which == 0 ? P.bs_q[blk] : P.bs_kv[blk], 1, bt);
         st = D;
-        off0 = ((int64_t)h * nb + blk) * kBlock * D;
+        off0 = ((int64_t)h * nb + blk) * bt * D;
         out_row = (int64_t)h * nb + blk;
     }
     const uint16_t* src = (which == 0 ? q : (which == 1 ? k : v)) + off0 + 8 * c;

@@ -7,8 +7,8 @@
 // Work decomposition (gfx950, 64-wide waves, bf16 MFMA 32x32x16):
 //   * one workgroup = 2 waves = one 64-token query block of one head; wave w
 //     owns query rows 32w .. 32w+31 and keeps its Q fragment in registers;
-//   * with VSA blocks of 128 or 256 tokens (dense layouts) the 64-token query
-//     blocks of one VSA block share its block list: one workgroup of 4 waves
+//   * with VSA blocks of 128 or 256 tokens the 64-token query blocks of one
+//     VSA block share its block list: one workgroup of 4 waves
 //     serves two of them, copies each selected KV tile into LDS once (each
 //     wave issues a quarter of the copy) and both wave pairs read it, which
 //     halves the L2 -> LDS traffic (sharing among all four blocks of a
@@ -68,9 +68,9 @@ struct CombineArgs {
                             // query row in exp2 units of the scaled scores
 };
 
-// R = 64-token query blocks per workgroup: 1, or 2 for dense problems with
-// 128- or 256-token VSA blocks (blocks 2J and 2J + 1 then lie in one VSA
-// block and share its list).  Two waves per SIMD.
+// R = 64-token query blocks per workgroup: 1, or 2 for problems with 128- or
+// 256-token VSA blocks (blocks 2J and 2J + 1 then lie in one VSA block and
+// share its list).  Two waves per SIMD.
 template <int D, int CMODE, int R>
 __global__ __launch_bounds__(kAttnThreads * R, 2) void sparse_attn_kernel(
     DevProblem P, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -95,10 +95,15 @@ __global__ __launch_bounds__(kAttnThreads * R, 2) void sparse_attn_kernel(
     const int l32 = lane & 31;
     const int hh = lane >> 5;
 
+    // VSA blocks of 64 * ratio tokens: the routing and out_c are per VSA
+    // block; a selected VSA block J stands for the 64-token KV blocks
+    // J ratio .. J ratio + ratio - 1
+    const int lr = P.ratio >> 1;  // log2(ratio) for ratio 1, 2, 4
+
     // ---- which query block -------------------------------------------------
     int s, h, i;
     SeqView sv;
-    if (R > 1) {  // dense, 64-token query blocks 2J and 2J + 1 of one VSA block
+    if (R > 1 && !P.packed) {  // 64-token query blocks 2J and 2J + 1 of one VSA block
         const int nJ = (P.nQ + 1) / 2;
         const int N = nJ * P.H * P.nseq;
         const int lin = xcd_remap(blockIdx.x, N);
@@ -108,6 +113,16 @@ __global__ __launch_bounds__(kAttnThreads * R, 2) void sparse_attn_kernel(
         s = rest / P.H;
         sv = seq_view(P, s, h);
         i = 2 * J + (wave >> 1);  // this wave pair's query block (may be past the end)
+    } else if (R > 1) {  // packed: every VSA block holds ratio / 2 pairs
+        const int npair = P.total_q << (lr - 1);
+        const int N = npair * P.H;
+        const int lin = xcd_remap(blockIdx.x, N);
+        const int gJ = lin % npair;
+        h = lin / npair;
+        s = seq_of_qblock(P, gJ >> (lr - 1));
+        sv = seq_view(P, s, h);
+        i = 2 * gJ + (wave >> 1) - (sv.qblk0 << lr);
+        if (i < 0 || i >= sv.nq) return;  // block outside every sequence (both pairs alike)
     } else if (!P.packed) {
         const int N = P.nQ * P.H * P.nseq;
         const int lin = xcd_remap(blockIdx.x, N);
@@ -117,24 +132,24 @@ __global__ __launch_bounds__(kAttnThreads * R, 2) void sparse_attn_kernel(
         s = rest / P.H;
         sv = seq_view(P, s, h);
     } else {
-        const int N = P.total_q * P.H;
+        const int N = (P.total_q << lr) * P.H;
         const int lin = xcd_remap(blockIdx.x, N);
-        const int g = lin % P.total_q;
-        h = lin / P.total_q;
-        s = seq_of_qblock(P, g);
+        const int g = lin % (P.total_q << lr);
+        h = lin / (P.total_q << lr);
+        s = seq_of_qblock(P, g >> lr);
         sv = seq_view(P, s, h);
-        i = g - sv.qblk0;
+        i = g - (sv.qblk0 << lr);
         if (i < 0 || i >= sv.nq) return;  // block outside every sequence
     }
-    // a query block past the end of the sequence (last VSA block) has no rows;
-    // its waves still take part in the shared copies and barriers
-    const int qsize = (R > 1 && i >= P.nQ) ? 0 : q_block_size(P, sv, i);
+    // a query block past the end of a dense sequence (last VSA block) or an
+    // empty one of a packed VSA block has no rows; its waves still take part
+    // in the shared copies and barriers
+    const int qsize = (R > 1 && i >= sv.nq) ? 0 : q_block_size(P, sv, i);
+    // the first query block of the workgroup is the fullest: when it is empty
+    // (packed) no block list is walked
+    const int lead_size = R > 1 ? q_block_size(P, sv, i & ~1) : qsize;
     const int64_t qrow0 = sv.qrow_base + (int64_t)kBlock * i;    // row index (lse)
     const int64_t qoff0 = sv.q_off + (int64_t)kBlock * i * sv.q_st;  // element offset of row 0
-    // VSA blocks of 64 * ratio tokens (dense layouts): the routing and out_c
-    // are per VSA block; a selected VSA block J stands for the 64-token KV
-    // blocks J ratio .. J ratio + ratio - 1
-    const int lr = P.ratio >> 1;  // log2(ratio) for ratio 1, 2, 4
 
     // ---- Q operand: B of S^T, column = query row, k-slots = 8 d values ----
     const int qr = 32 * (wave & 1) + l32;
@@ -155,8 +170,8 @@ __global__ __launch_bounds__(kAttnThreads * R, 2) void sparse_attn_kernel(
     float l = 0.f;        // this lane's share of the running sum
 
     // VSA block of this query block in the block-resolution arrays
-    const int64_t qb = P.packed ? sv.qblk_base + i : ((int64_t)s * P.H + h) * P.nQB + (i >> lr);
-    const int nsel = __builtin_amdgcn_readfirstlane(clampi(num[qb], 0, P.idx_row));
+    const int64_t qb = sv.qvsa_base + (i >> lr);
+    const int nsel = __builtin_amdgcn_readfirstlane(lead_size > 0 ? clampi(num[qb], 0, P.idx_row) : 0);
     const int n = nsel << lr;  // 64-token KV blocks to visit
     const_int* list = (const_int*)uniform_ptr(idx + qb * P.idx_row);
     const_int* bs_kv = (const_int*)(P.packed ? uniform_ptr(P.bs_kv + sv.kvblk0) : nullptr);
@@ -170,37 +185,37 @@ __global__ __launch_bounds__(kAttnThreads * R, 2) void sparse_attn_kernel(
     __builtin_amdgcn_s_waitcnt(0);
 
     // the walk visits positions (t0 + t) mod n for t = 0 .. n-1 of the list
-    // expanded to 64-token blocks
+    // expanded to 64-token blocks; entries are local 64-token KV blocks
     const int t0 = n > 0 ? (((i >> lr) % kSweep) * n) / kSweep : 0;
     auto entry = [&](int t) -> int {
         int pos = t0 + t;
         if (pos >= n) pos -= n;
-        const int J = list[pos >> lr];
+        const int J = list[pos >> lr] - rebase;
         // no sequence has 2^28 VSA blocks: such an entry (or a negative one)
         // is out of range, and is kept from wrapping into range by the shift
-        if (lr > 0 && (unsigned)J >= (1u << 28)) return -1;
+        if ((unsigned)J >= (1u << 28)) return -1;
         return (J << lr) + (pos & ((1 << lr) - 1));
     };
     // The entry of walk step pre_t is loaded one step ahead, so the scalar
     // load's latency is hidden behind a whole block of work.
     int pre_t = 0;
     int pre = n > 0 ? entry(0) : 0;
-    // next valid entry at or after walk step t (-1: none)
+    // valid tokens of local KV block j (packed: 0 for an empty 64-token
+    // block of a VSA block)
+    auto kv_size = [&](int j) -> int {
+        return P.packed ? packed_sub_size(bs_kv[j >> lr], j & ((1 << lr) - 1)) : min(kBlock, P.Skv - kBlock * j);
+    };
+    // next valid, non-empty entry at or after walk step t (-1: none)
     auto next_valid = [&](int& t) -> int {
         for (; t < n; ++t) {
-            const int raw = t == pre_t ? pre : entry(t);
+            const int j = t == pre_t ? pre : entry(t);
             if (t + 1 < n) {
                 pre = entry(t + 1);
                 pre_t = t + 1;
             }
-            const int j = raw - rebase;
-            if (j >= 0 && j < nkv) return j;
+            if (j >= 0 && j < nkv && (lr == 0 || !P.packed || kv_size(j) > 0)) return j;
         }
         return -1;
-    };
-    // valid tokens of local KV block j
-    auto kv_size = [&](int j) -> int {
-        return P.packed ? clampi(bs_kv[j], 1, kBlock) : min(kBlock, P.Skv - kBlock * j);
     };
 
     // per-lane positions inside the tiles (copies by 2 waves: two offsets,
@@ -402,7 +417,7 @@ __global__ __launch_bounds__(kAttnThreads * R, 2) void sparse_attn_kernel(
         uint16_t* orow = out + qoff0 + qr * sv.q_st;
         const float* ocr = C.out_c + qb * D;
         // token index of this row along the gate's token axis
-        const int64_t tok = (int64_t)kBlock * (P.packed ? sv.qblk0 + i : i) + qr;
+        const int64_t tok = (int64_t)kBlock * (P.packed ? (sv.qblk0 << lr) + i : i) + qr;
         const int64_t goff = (P.packed ? 0 : (int64_t)s * C.gs0) + (int64_t)h * C.gs1 + tok * C.gs2;
         float g = 1.f;
         if (CMODE == kTokenGate) g = __uint_as_float((uint32_t)C.gate[goff] << 16);
@@ -453,10 +468,10 @@ hipError_t launch_r(const DevProblem& P, unsigned grid, const uint16_t* q, const
 template <int D, int CMODE>
 hipError_t launch_d(const DevProblem& P, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int* idx,
                     const int* num, uint16_t* out, float c, const CombineArgs& C, hipStream_t st) {
-    // dense problems with 128/256-token VSA blocks: one workgroup per pair of
-    // 64-token query blocks
-    const bool pairs = !P.packed && P.ratio >= 2;
-    const int64_t N = P.packed ? (int64_t)P.total_q * P.H
+    // 128/256-token VSA blocks: one workgroup per pair of 64-token query
+    // blocks
+    const bool pairs = P.ratio >= 2;
+    const int64_t N = P.packed ? (int64_t)P.total_q * P.ratio / (pairs ? 2 : 1) * P.H
                                : (int64_t)(pairs ? (P.nQ + 1) / 2 : P.nQ) * P.H * P.nseq;
     if (N <= 0 || N > 0x7fffffff) return hipErrorInvalidValue;
     if (pairs) return launch_r<D, CMODE, 2>(P, (unsigned)N, q, k, v, idx, num, out, c, C, st);

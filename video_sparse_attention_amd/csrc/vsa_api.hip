@@ -39,9 +39,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int make_problem(const vsa_problem* pr, vsa::DevProblem* P) {
     if (!pr) return fail(VSA_ERR_NULL, "problem is NULL");
     const bool dense = pr->layout == VSA_LAYOUT_DENSE || pr->layout == VSA_LAYOUT_BSHD;
-    if (pr->block_size != VSA_BLOCK && !(dense && (pr->block_size == 128 || pr->block_size == 256)))
-        return fail(VSA_ERR_UNSUPPORTED, "block_size %d unsupported (64; 128 or 256 for the dense layouts)",
-                    pr->block_size);
+    if (pr->block_size != VSA_BLOCK && pr->block_size != 128 && pr->block_size != 256)
+        return fail(VSA_ERR_UNSUPPORTED, "block_size %d unsupported (64, 128 or 256)", pr->block_size);
     if (pr->head_dim != 64 && pr->head_dim != 128)
         return fail(VSA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", pr->head_dim);
     if (pr->heads < 1) return fail(VSA_ERR_SHAPE, "heads must be >= 1 (got %d)", pr->heads);
@@ -49,7 +48,7 @@ int make_problem(const vsa_problem* pr, vsa::DevProblem* P) {
     *P = vsa::DevProblem{};
     P->H = pr->heads;
     P->D = pr->head_dim;
-    P->ratio = 1;
+    P->ratio = pr->block_size / VSA_BLOCK;
     if (dense) {
         if (pr->batch < 1) return fail(VSA_ERR_SHAPE, "empty batch (batch=%d)", pr->batch);
         if (3LL * pr->batch > kGridYZMax) return fail(VSA_ERR_UNSUPPORTED, "batch too large");
@@ -60,11 +59,11 @@ int make_problem(const vsa_problem* pr, vsa::DevProblem* P) {
         P->nseq = pr->batch;
         P->Sq = pr->seqlen_q;
         P->Skv = pr->seqlen_kv;
-        P->ratio = pr->block_size / VSA_BLOCK;
-        P->nQ = (pr->seqlen_q + VSA_BLOCK - 1) / VSA_BLOCK;
-        P->nKV = (pr->seqlen_kv + VSA_BLOCK - 1) / VSA_BLOCK;
-        P->nQB = (pr->seqlen_q + pr->block_size - 1) / pr->block_size;
-        P->nKVB = (pr->seqlen_kv + pr->block_size - 1) / pr->block_size;
+        const int64_t sq = pr->seqlen_q, skv = pr->seqlen_kv, bs = pr->block_size;
+        P->nQ = (int)((sq + VSA_BLOCK - 1) / VSA_BLOCK);
+        P->nKV = (int)((skv + VSA_BLOCK - 1) / VSA_BLOCK);
+        P->nQB = (int)((sq + bs - 1) / bs);
+        P->nKVB = (int)((skv + bs - 1) / bs);
         if (P->nKVB > vsa::kMaxKvBlocks)
             return fail(VSA_ERR_UNSUPPORTED, "%d KV blocks per sequence exceeds %d", P->nKVB, vsa::kMaxKvBlocks);
         P->kk = std::min(pr->topk, P->nKVB);
@@ -96,8 +95,10 @@ int make_problem(const vsa_problem* pr, vsa::DevProblem* P) {
             return fail(VSA_ERR_UNSUPPORTED, "%d KV blocks per sequence exceeds %d", pr->max_kv_blocks,
                         vsa::kMaxKvBlocks);
         if (pr->max_topk < 1) return fail(VSA_ERR_TOPK, "max_topk must be >= 1 (got %d)", pr->max_topk);
-        if ((int64_t)pr->total_q_blocks * pr->heads > 0x7fffffffLL)
+        if ((int64_t)pr->total_q_blocks * pr->heads * P->ratio > 0x7fffffffLL)
             return fail(VSA_ERR_UNSUPPORTED, "too many query blocks in one launch");
+        if ((int64_t)std::max(pr->total_q_blocks, pr->total_kv_blocks) * pr->block_size > 0x7fffffffLL)
+            return fail(VSA_ERR_SHAPE, "packed length exceeds 2^31 slots");
         P->packed = 1;
         P->nseq = pr->num_seqs;
         P->cu_q = pr->cu_blocks_q;
@@ -112,8 +113,8 @@ int make_problem(const vsa_problem* pr, vsa::DevProblem* P) {
         P->max_topk = pr->max_topk;
         P->idx_row = pr->max_topk;
         P->q_st = P->kv_st = P->D;  // rows of the packed layout are contiguous
-        P->q_sh = (int64_t)pr->total_q_blocks * VSA_BLOCK * P->D;
-        P->kv_sh = (int64_t)pr->total_kv_blocks * VSA_BLOCK * P->D;
+        P->q_sh = (int64_t)pr->total_q_blocks * pr->block_size * P->D;
+        P->kv_sh = (int64_t)pr->total_kv_blocks * pr->block_size * P->D;
     } else {
         return fail(VSA_ERR_UNSUPPORTED, "unknown layout %d", pr->layout);
     }
@@ -122,17 +123,17 @@ int make_problem(const vsa_problem* pr, vsa::DevProblem* P) {
 
 // element counts of the token-resolution tensors
 int64_t q_elems(const vsa::DevProblem& P) {
-    return P.packed ? (int64_t)P.H * P.total_q * VSA_BLOCK * P.D : (int64_t)P.nseq * P.H * P.Sq * P.D;
+    return P.packed ? (int64_t)P.H * P.total_q * P.ratio * VSA_BLOCK * P.D : (int64_t)P.nseq * P.H * P.Sq * P.D;
 }
 int64_t kv_elems(const vsa::DevProblem& P) {
-    return P.packed ? (int64_t)P.H * P.total_kv * VSA_BLOCK * P.D : (int64_t)P.nseq * P.H * P.Skv * P.D;
+    return P.packed ? (int64_t)P.H * P.total_kv * P.ratio * VSA_BLOCK * P.D : (int64_t)P.nseq * P.H * P.Skv * P.D;
 }
 // 64-token block counts (the attention kernels' granularity)
 int64_t qblocks64(const vsa::DevProblem& P) {
-    return P.packed ? (int64_t)P.H * P.total_q : (int64_t)P.nseq * P.H * P.nQ;
+    return P.packed ? (int64_t)P.H * P.total_q * P.ratio : (int64_t)P.nseq * P.H * P.nQ;
 }
 int64_t kvblocks64(const vsa::DevProblem& P) {
-    return P.packed ? (int64_t)P.H * P.total_kv : (int64_t)P.nseq * P.H * P.nKV;
+    return P.packed ? (int64_t)P.H * P.total_kv * P.ratio : (int64_t)P.nseq * P.H * P.nKV;
 }
 // block-resolution array lengths (VSA blocks)
 int64_t qblocks(const vsa::DevProblem& P) {
@@ -189,7 +190,7 @@ BwdWorkspace plan_bwd_workspace(const vsa::DevProblem& P, void* base) {
     };
     // coarse matrices per VSA block; statistics and inverse lists per 64-token block
     const int64_t maxq = P.packed ? P.max_q : P.nQB, maxkv = P.packed ? P.max_kv : P.nKVB;
-    const int64_t maxq64 = P.packed ? P.max_q : P.nQ;
+    const int64_t maxq64 = P.packed ? (int64_t)P.max_q * P.ratio : P.nQ;
     const size_t qd = sizeof(double) * qblocks(P) * P.D, kd = sizeof(double) * kvblocks(P) * P.D;
     w.qc = (double*)take(qd);
     w.kc = (double*)take(kd);
@@ -255,7 +256,7 @@ int gate_strides(const vsa::DevProblem& P, const uint16_t* gate, int mode, const
         out[0] = (int64_t)P.Sq * P.H * dmul;
     } else {
         out[2] = dmul;
-        out[1] = (int64_t)P.total_q * VSA_BLOCK * dmul;
+        out[1] = (int64_t)P.total_q * P.ratio * VSA_BLOCK * dmul;
         out[0] = 0;
     }
     if (mode == VSA_GATE_FULL) {
@@ -335,11 +336,14 @@ const char* vsa_last_error(void) { return g_err.c_str(); }
 const char* vsa_version(void) { return "libvsa 0.1.0 gfx950"; }
 
 int vsa_build_metadata(int32_t num_seqs, const int32_t* seqlens_q, const int32_t* seqlens_kv,
-                       const int32_t* topk, vsa_meta_sizes* sizes, int32_t* cu_blocks_q,
+                       const int32_t* topk, int32_t block_size, vsa_meta_sizes* sizes, int32_t* cu_blocks_q,
                        int32_t* cu_blocks_kv, int32_t* block_sizes_q, int32_t* block_sizes_kv,
                        int32_t* topk_clamped) {
     if (!sizes) return fail(VSA_ERR_NULL, "sizes is NULL");
     *sizes = vsa_meta_sizes{};
+    if (block_size != VSA_BLOCK && block_size != 128 && block_size != 256)
+        return fail(VSA_ERR_UNSUPPORTED, "block_size %d unsupported (64, 128 or 256)", block_size);
+    const int bs = block_size;
     if (num_seqs < 1) return fail(VSA_ERR_SHAPE, "empty batch (num_seqs=%d)", num_seqs);
     if (!seqlens_q || !topk) return fail(VSA_ERR_NULL, "seqlens_q or topk is NULL");
     const int nout = !!cu_blocks_q + !!cu_blocks_kv + !!block_sizes_q + !!block_sizes_kv + !!topk_clamped;
@@ -351,15 +355,15 @@ int vsa_build_metadata(int32_t num_seqs, const int32_t* seqlens_q, const int32_t
         if (seqlens_q[s] < 1 || seqlens_kv[s] < 1)
             return fail(VSA_ERR_SHAPE, "sequence %d has zero length (q=%d, kv=%d)", s, seqlens_q[s], seqlens_kv[s]);
         if (topk[s] < 1) return fail(VSA_ERR_TOPK, "sequence %d: topk must be >= 1 (got %d)", s, topk[s]);
-        const int32_t nq = (seqlens_q[s] + VSA_BLOCK - 1) / VSA_BLOCK;
-        const int32_t nkv = (seqlens_kv[s] + VSA_BLOCK - 1) / VSA_BLOCK;
+        const int32_t nq = (int32_t)(((int64_t)seqlens_q[s] + bs - 1) / bs);
+        const int32_t nkv = (int32_t)(((int64_t)seqlens_kv[s] + bs - 1) / bs);
         tq += nq;
         tkv += nkv;
         mq = std::max(mq, nq);
         mkv = std::max(mkv, nkv);
         mk = std::max(mk, std::min(topk[s], nkv));
     }
-    if (tq * VSA_BLOCK > 0x7fffffffLL || tkv * VSA_BLOCK > 0x7fffffffLL)
+    if (tq * bs > 0x7fffffffLL || tkv * bs > 0x7fffffffLL)
         return fail(VSA_ERR_SHAPE, "packed length exceeds 2^31 slots");
     sizes->num_seqs = num_seqs;
     sizes->total_q_blocks = (int32_t)tq;
@@ -367,17 +371,17 @@ int vsa_build_metadata(int32_t num_seqs, const int32_t* seqlens_q, const int32_t
     sizes->max_q_blocks = mq;
     sizes->max_kv_blocks = mkv;
     sizes->max_topk = mk;
-    sizes->q_slots = tq * VSA_BLOCK;
-    sizes->kv_slots = tkv * VSA_BLOCK;
+    sizes->q_slots = tq * bs;
+    sizes->kv_slots = tkv * bs;
     if (nout == 0) return ok();
     int32_t oq = 0, okv = 0;
     for (int s = 0; s < num_seqs; ++s) {
-        const int32_t nq = (seqlens_q[s] + VSA_BLOCK - 1) / VSA_BLOCK;
-        const int32_t nkv = (seqlens_kv[s] + VSA_BLOCK - 1) / VSA_BLOCK;
+        const int32_t nq = (seqlens_q[s] + bs - 1) / bs;
+        const int32_t nkv = (seqlens_kv[s] + bs - 1) / bs;
         cu_blocks_q[s] = oq;
         cu_blocks_kv[s] = okv;
-        for (int i = 0; i < nq; ++i) block_sizes_q[oq + i] = std::min(VSA_BLOCK, seqlens_q[s] - VSA_BLOCK * i);
-        for (int j = 0; j < nkv; ++j) block_sizes_kv[okv + j] = std::min(VSA_BLOCK, seqlens_kv[s] - VSA_BLOCK * j);
+        for (int i = 0; i < nq; ++i) block_sizes_q[oq + i] = std::min(bs, seqlens_q[s] - bs * i);
+        for (int j = 0; j < nkv; ++j) block_sizes_kv[okv + j] = std::min(bs, seqlens_kv[s] - bs * j);
         topk_clamped[s] = std::min(topk[s], nkv);
         oq += nq;
         okv += nkv;

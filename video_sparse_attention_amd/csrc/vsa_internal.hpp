@@ -16,7 +16,8 @@ constexpr int kBlock = 64;
 // contiguous): [B,H,S,D] and [B,S,H,D] are both "dense" (one sequence per
 // batch item), the packed layout is [H,slots,D].  The attention kernels work
 // on 64-token blocks; the coarse branch and the routing on VSA blocks of
-// 64 * ratio tokens (ratio 1, 2 or 4; 1 for the packed layout).
+// 64 * ratio tokens (ratio 1, 2 or 4).  Packed metadata (cu_*, bs_*,
+// total_*, max_*) counts VSA blocks, each occupying 64 * ratio slots.
 struct DevProblem {
     int packed;  // 0 dense ([B,H,S,D] or [B,S,H,D]), 1 block-padded packed [H,slots,D]
     int bshd;    // dense tensors are [B,S,H,D]
@@ -24,13 +25,13 @@ struct DevProblem {
     int nseq;  // B (dense) or num_seqs (packed)
     // dense
     int Sq, Skv, nQ, nKV;  // lengths and 64-token block counts
-    int ratio;             // VSA block = 64 * ratio tokens
+    int ratio;             // VSA block = 64 * ratio tokens (1 in the coarse view)
     int nQB, nKVB;         // VSA blocks per sequence (= nQ, nKV when ratio is 1)
     int kk;                // min(topk, nKVB): row length of q2k_idx (dense)
     // packed
     const int* cu_q;
     const int* cu_kv;
-    const int* bs_q;
+    const int* bs_q;  // valid tokens per VSA block
     const int* bs_kv;
     const int* topk_s;
     int total_q, total_kv, max_q, max_kv, max_topk;
@@ -40,17 +41,21 @@ struct DevProblem {
     int64_t kv_sb, kv_sh, kv_st;
 };
 
-// One sequence on one head: where its blocks live.
+// One sequence on one head: where its blocks live.  "Blocks" are 64-token
+// blocks (the attention kernels' tiles); in the coarse view (ratio 1) they
+// are the VSA blocks.
 struct SeqView {
-    int nq, nkv, k;       // query blocks, KV blocks, top-k (clamped)
-    int qblk0, kvblk0;    // first global block index (packed) or 0 (dense)
-    int64_t qblk_base;    // index of block 0 in block-resolution q arrays
-    int64_t kvblk_base;   // index of block 0 in block-resolution kv arrays
+    int nq, nkv, k;       // query blocks, KV blocks, top-k (clamped, in VSA blocks)
+    int qblk0, kvblk0;    // first global VSA block (packed: index into bs_q / bs_kv) or 0 (dense)
+    int64_t qblk_base;    // index of block 0 in 64-token-block arrays (row statistics)
+    int64_t kvblk_base;   // the same for k/v
+    int64_t qvsa_base;    // index of VSA block 0 in VSA-block arrays (out_c, q2k_idx, q2k_num)
+    int64_t kvvsa_base;   // the same for k/v
     int64_t qrow_base;    // row (token slot) of block 0 in [.., S] row-indexed arrays (lse)
     int64_t kvrow_base;   // the same for k/v
     int64_t q_off, kv_off;  // element offset of token row 0 in q/out and in k/v
     int64_t q_st, kv_st;    // element stride between consecutive token rows
-    int idx_rebase;       // added to local KV block numbers when stored
+    int idx_rebase;       // added to local VSA block numbers when stored in q2k_idx
 };
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
@@ -66,6 +71,8 @@ __device__ __forceinline__ SeqView seq_view(const DevProblem& P, int s, int h) {
         const int64_t sh = (int64_t)s * P.H + h;
         v.qblk_base = sh * P.nQ;
         v.kvblk_base = sh * P.nKV;
+        v.qvsa_base = sh * P.nQB;
+        v.kvvsa_base = sh * P.nKVB;
         v.qrow_base = sh * P.Sq;
         v.kvrow_base = sh * P.Skv;
         v.q_off = (int64_t)s * P.q_sb + (int64_t)h * P.q_sh;
@@ -78,15 +85,19 @@ __device__ __forceinline__ SeqView seq_view(const DevProblem& P, int s, int h) {
         int q1 = clampi(P.cu_q[s + 1], q0, P.total_q);
         int k0 = clampi(P.cu_kv[s], 0, P.total_kv);
         int k1 = clampi(P.cu_kv[s + 1], k0, P.total_kv);
-        v.nq = min(q1 - q0, P.max_q);
-        v.nkv = min(k1 - k0, P.max_kv);
-        v.k = clampi(P.topk_s[s], 1, min(P.max_topk, max(v.nkv, 1)));
+        const int lr = P.ratio >> 1;  // log2(ratio): 64-token blocks per VSA block
+        const int nkvb = min(k1 - k0, P.max_kv);
+        v.nq = min(q1 - q0, P.max_q) << lr;
+        v.nkv = nkvb << lr;
+        v.k = clampi(P.topk_s[s], 1, min(P.max_topk, max(nkvb, 1)));
         v.qblk0 = q0;
         v.kvblk0 = k0;
-        v.qblk_base = (int64_t)h * P.total_q + q0;
-        v.kvblk_base = (int64_t)h * P.total_kv + k0;
-        v.qrow_base = ((int64_t)h * P.total_q + q0) * kBlock;
-        v.kvrow_base = ((int64_t)h * P.total_kv + k0) * kBlock;
+        v.qvsa_base = (int64_t)h * P.total_q + q0;
+        v.kvvsa_base = (int64_t)h * P.total_kv + k0;
+        v.qblk_base = v.qvsa_base << lr;
+        v.kvblk_base = v.kvvsa_base << lr;
+        v.qrow_base = v.qblk_base * kBlock;
+        v.kvrow_base = v.kvblk_base * kBlock;
         v.q_off = v.qrow_base * P.D;
         v.kv_off = v.kvrow_base * P.D;
         v.q_st = P.D;
@@ -96,17 +107,25 @@ __device__ __forceinline__ SeqView seq_view(const DevProblem& P, int s, int h) {
     return v;
 }
 
+// Valid tokens of 64-token block r of a packed VSA block holding `size`
+// tokens: the first block keeps at least one token (sizes are clamped to
+// [1, 64 ratio]), later ones may be empty.
+__device__ __forceinline__ int packed_sub_size(int size, int r) {
+    return clampi(size - kBlock * r, r == 0 ? 1 : 0, kBlock);
+}
 // Valid tokens of local query / KV block i of sequence view v.
 __device__ __forceinline__ int q_block_size(const DevProblem& P, const SeqView& v, int i) {
     if (!P.packed) return min(kBlock, P.Sq - kBlock * i);
-    return clampi(P.bs_q[v.qblk0 + i], 1, kBlock);
+    const int lr = P.ratio >> 1;
+    return packed_sub_size(P.bs_q[v.qblk0 + (i >> lr)], i & ((1 << lr) - 1));
 }
 __device__ __forceinline__ int kv_block_size(const DevProblem& P, const SeqView& v, int j) {
     if (!P.packed) return min(kBlock, P.Skv - kBlock * j);
-    return clampi(P.bs_kv[v.kvblk0 + j], 1, kBlock);
+    const int lr = P.ratio >> 1;
+    return packed_sub_size(P.bs_kv[v.kvblk0 + (j >> lr)], j & ((1 << lr) - 1));
 }
 
-// Sequence owning global query block g (packed): largest s with cu_q[s] <= g.
+// Sequence owning global query VSA block g (packed): largest s with cu_q[s] <= g.
 __device__ __forceinline__ int seq_of_qblock(const DevProblem& P, int g) {
     int lo = 0, hi = P.nseq - 1;
     while (lo < hi) {
@@ -159,8 +178,7 @@ __host__ __device__ inline int64_t tile_token_raster(const TileGrid& g, int b, i
 // ---------------------------------------------------------------------------
 // launchers (one per kernel family; each returns hipError_t of the launch)
 // ---------------------------------------------------------------------------
-// Block means over VSA blocks of 64 * P.ratio tokens (dense) or over the
-// packed layout's 64-token blocks.
+// Block means over VSA blocks of 64 * P.ratio tokens.
 hipError_t launch_pool(const DevProblem& P, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        double* qc, double* kc, double* vc, hipStream_t st);
 // The problem as the coarse branch sees it: VSA blocks as its blocks.
@@ -168,6 +186,7 @@ inline DevProblem coarse_view(const DevProblem& P) {
     DevProblem C = P;
     C.nQ = P.nQB;
     C.nKV = P.nKVB;
+    C.ratio = 1;
     return C;
 }
 // scratch: coarse_scratch_doubles(P) doubles (block-level scores and row sums)
