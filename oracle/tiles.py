@@ -14,7 +14,7 @@ notes):
 
 * the latent is a ``T x H x W`` grid of tokens flattened in raster order
   (``w`` fastest, then ``h``, then ``t``);
-* it is cut into tiles of ``tt x th x tw`` tokens (``tt * th * tw <= 64``;
+* it is cut into tiles of ``tt x th x tw`` tokens (``tt * th * tw <= 256``;
   64 = 4 x 4 x 4 is the default), the last tile along an axis being shorter
   when the extent is not a multiple of the tile;
 * tiles are ordered in raster order of their tile coordinates, and the
@@ -23,7 +23,12 @@ notes):
   ``p`` of that tiled order, ``reverse_tile_partition_indices`` is its inverse
   permutation, ``variable_block_sizes[b]`` the number of tokens of tile ``b``
   and ``non_pad_index[p]`` the slot of position ``p`` when every tile is
-  padded to 64 slots (slot ``64 b + u`` for the ``u``-th token of tile ``b``).
+  padded to its VSA block of ``bs`` slots (slot ``bs b + u`` for the ``u``-th
+  token of tile ``b``).  ``bs`` is 64 for tiles of at most 64 tokens and 128
+  or 256 for the larger tiles of the 128/256-token variants ("[chore] release
+  fastvideo-kernel 0.3.0", Block-sparse / VSA attention improvements): the
+  smallest of 64, 128, 256 that holds the tile (reading: the tile is the VSA
+  block, e.g. 4 x 8 x 8 = 256 tokens in a 256-slot block).
 
 Each function below spells that out with explicit loops.
 """
@@ -38,12 +43,23 @@ from .vsa_oracle import BLOCK, forward_packed_blocks
 DEFAULT_TILE = (4, 4, 4)
 
 
+def tile_block(tile: Tuple[int, int, int]) -> int:
+    """Slots of the VSA block that holds one tile: the smallest of 64, 128
+    and 256 that is at least the tile's token count."""
+    n = tile[0] * tile[1] * tile[2]
+    for bs in (BLOCK, 2 * BLOCK, 4 * BLOCK):
+        if n <= bs:
+            return bs
+    raise ValueError("a tile holds at most 256 tokens")
+
+
 def tile_partition(T: int, H: int, W: int, tile: Tuple[int, int, int] = DEFAULT_TILE) -> Dict[str, np.ndarray]:
     """Tile order, its inverse, tile sizes and padded positions (loops over
     tiles, then over the tokens of each tile)."""
     tt, th, tw = tile
-    if min(T, H, W) < 1 or min(tt, th, tw) < 1 or tt * th * tw > BLOCK:
-        raise ValueError("grid and tile extents must be >= 1 and a tile at most 64 tokens")
+    if min(T, H, W) < 1 or min(tt, th, tw) < 1 or tt * th * tw > 4 * BLOCK:
+        raise ValueError("grid and tile extents must be >= 1 and a tile at most 256 tokens")
+    bs = tile_block(tile)
     n_t, n_h, n_w = -(-T // tt), -(-H // th), -(-W // tw)
     fwd, nonpad, sizes = [], [], []
     for bt in range(n_t):
@@ -58,7 +74,7 @@ def tile_partition(T: int, H: int, W: int, tile: Tuple[int, int, int] = DEFAULT_
                     for lh in range(eh):
                         for lw in range(ew):
                             fwd.append(((bt * tt + lt) * H + (bh * th + lh)) * W + (bw * tw + lw))
-                            nonpad.append(BLOCK * b + u)
+                            nonpad.append(bs * b + u)
                             u += 1
                 sizes.append(u)
     rev = [0] * len(fwd)
@@ -71,12 +87,13 @@ def tile_partition(T: int, H: int, W: int, tile: Tuple[int, int, int] = DEFAULT_
 
 
 def tile_gather(x: np.ndarray, grid: Tuple[int, int, int], tile=DEFAULT_TILE) -> np.ndarray:
-    """``x`` ``[..., T*H*W, D]`` in raster order -> ``[..., 64 * n_tiles, D]``
-    in tile order, each tile padded to 64 slots with zeros."""
+    """``x`` ``[..., T*H*W, D]`` in raster order -> ``[..., bs * n_tiles, D]``
+    in tile order, each tile padded to its ``bs = tile_block(tile)`` slots with
+    zeros."""
     meta = tile_partition(*grid, tile)
     fwd, nonpad = meta["tile_partition_indices"], meta["non_pad_index"]
     n_tiles = len(meta["variable_block_sizes"])
-    y = np.zeros(x.shape[:-2] + (BLOCK * n_tiles, x.shape[-1]), dtype=x.dtype)
+    y = np.zeros(x.shape[:-2] + (tile_block(tile) * n_tiles, x.shape[-1]), dtype=x.dtype)
     for p in range(len(fwd)):
         y[..., nonpad[p], :] = x[..., fwd[p], :]
     return y
@@ -109,7 +126,9 @@ def vsa_forward_video(q, k, v, grid: Tuple[int, int, int], topk: int, gate=None,
     sizes = [int(x) for x in meta["variable_block_sizes"]]
     n_tiles = len(sizes)
 
-    def pack(x):  # [B, Hh, S, ...] raster -> [Hh, B * 64 * n_tiles, ...]
+    bs = tile_block(tile)
+
+    def pack(x):  # [B, Hh, S, ...] raster -> [Hh, B * bs * n_tiles, ...]
         if x.ndim == 3:
             g = tile_gather(x[..., None], grid, tile)[..., 0]
         else:
@@ -118,8 +137,8 @@ def vsa_forward_video(q, k, v, grid: Tuple[int, int, int], topk: int, gate=None,
 
     gq, gk, gv = pack(q), pack(k), pack(v)
     gg = None if gate is None else pack(np.asarray(gate, dtype=np.float64))
-    res = forward_packed_blocks(gq, gk, gv, [sizes] * B, [sizes] * B, [topk] * B, gg, blocks)
-    slots = BLOCK * n_tiles
+    res = forward_packed_blocks(gq, gk, gv, [sizes] * B, [sizes] * B, [topk] * B, gg, blocks, bs)
+    slots = bs * n_tiles
     out = res["out"]
     out_raster = np.stack([tile_scatter(out[:, b * slots:(b + 1) * slots], grid, tile) for b in range(B)])
     res["out_raster"] = out_raster

@@ -411,13 +411,21 @@ def pin_magnitudes(seed=12):
 
 TILE_CASES = [((4, 4, 4), (4, 4, 4)), ((5, 6, 7), (4, 4, 4)), ((3, 9, 2), (4, 4, 4)),
               ((8, 4, 12), (4, 4, 4)), ((6, 10, 5), (2, 4, 8)), ((1, 1, 130), (1, 1, 64)),
-              ((9, 1, 1), (8, 1, 1))]
+              ((9, 1, 1), (8, 1, 1)),
+              # tiles of the 128/256-token variants (blocks of 128 and 256 slots)
+              ((9, 10, 11), (4, 4, 8)), ((5, 9, 17), (4, 8, 8)), ((3, 7, 7), (3, 5, 7)),
+              ((1, 1, 300), (1, 1, 256))]
+
+
+def _slots_per_tile(vol):
+    # 64 slots up to 64 tokens, else the next power of two (128 or 256)
+    return 64 * 2 ** max(0, math.ceil(math.log2(vol / 64)))
 
 
 def pin_tile_partition_by_sorting():
     """Tile order from an independent construction: tile number of every
     token from its coordinates, then a stable sort by (tile, t, h, w); sizes by
-    counting; padded slot = 64 * tile + rank inside the tile."""
+    counting; padded slot = (slots per tile) * tile + rank inside the tile."""
     for (T, H, W), (tt, th, tw) in TILE_CASES:
         m = TL.tile_partition(T, H, W, (tt, th, tw))
         t, h, w = np.unravel_index(np.arange(T * H * W), (T, H, W))
@@ -430,7 +438,7 @@ def pin_tile_partition_by_sorting():
         first = np.concatenate([[0], np.cumsum(sizes)[:-1]])
         tiles_in_order = tile_of[fwd]
         rank = np.arange(len(fwd)) - first[tiles_in_order]
-        assert np.array_equal(m["non_pad_index"], 64 * tiles_in_order + rank)
+        assert np.array_equal(m["non_pad_index"], _slots_per_tile(tt * th * tw) * tiles_in_order + rank)
         assert np.array_equal(m["reverse_tile_partition_indices"][fwd], np.arange(len(fwd)))
         assert sizes.sum() == T * H * W and sizes.max() <= tt * th * tw
 
@@ -447,11 +455,20 @@ def pin_tile_closed_forms():
     assert np.array_equal(m["tile_partition_indices"], np.arange(200))
     assert list(m["variable_block_sizes"]) == O.block_sizes(200)
     assert np.array_equal(m["non_pad_index"], np.arange(200))
+    # the same with 256-token tiles: 256-slot blocks, still the identity
+    m = TL.tile_partition(1, 1, 700, (1, 1, 256))
+    assert np.array_equal(m["tile_partition_indices"], np.arange(700))
+    assert list(m["variable_block_sizes"]) == [256, 256, 188]
+    assert np.array_equal(m["non_pad_index"], np.arange(700))
+    # a full 4 x 8 x 8 grid is one tile of 256 tokens in raster order
+    m = TL.tile_partition(4, 8, 8, (4, 8, 8))
+    assert list(m["variable_block_sizes"]) == [256]
+    assert np.array_equal(m["tile_partition_indices"], np.arange(256))
 
 
 def pin_tile_gather_scatter_roundtrip(seed=13):
     rng = np.random.default_rng(seed)
-    for (T, H, W), tile in TILE_CASES[:5]:
+    for (T, H, W), tile in TILE_CASES[:5] + TILE_CASES[7:10]:
         x = rng.standard_normal((2, T * H * W, 3))
         y = TL.tile_gather(x, (T, H, W), tile)
         m = TL.tile_partition(T, H, W, tile)
@@ -462,18 +479,20 @@ def pin_tile_gather_scatter_roundtrip(seed=13):
 
 
 def pin_video_forward_1d_equals_dense(seed=14):
-    """A 1 x 1 x S grid in 1 x 1 x 64 tiles is the dense forward on the raster
-    sequence (same blocks, same order)."""
+    """A 1 x 1 x S grid in 1 x 1 x b tiles is the dense forward with VSA blocks
+    of b tokens on the raster sequence (same blocks, same order), b = 64, 128,
+    256."""
     rng = np.random.default_rng(seed)
-    S, D = 64 * 5 + 23, 16
-    q, k, v = (rng.standard_normal((2, 3, S, D)) for _ in range(3))
-    gate = rng.uniform(0, 1, (2, 3, S))
-    dense = O.vsa_forward(q, k, v, 3, gate)
-    vid = TL.vsa_forward_video(q, k, v, (1, 1, S), 3, gate, tile=(1, 1, 64))
-    assert np.allclose(vid["out_raster"], dense["out"], rtol=1e-12, atol=1e-13)
-    nq = len(O.block_sizes(S))
-    idx = vid["q2k_idx"].reshape(3, 2, nq, 3) - (np.arange(2) * nq)[None, :, None, None]
-    assert np.array_equal(idx.transpose(1, 0, 2, 3), dense["q2k_idx"])
+    for b, S in ((64, 64 * 5 + 23), (128, 128 * 4 + 23), (256, 256 * 3 + 100)):
+        D = 16
+        q, k, v = (rng.standard_normal((2, 3, S, D)) for _ in range(3))
+        gate = rng.uniform(0, 1, (2, 3, S))
+        dense = O.vsa_forward(q, k, v, 3, gate, block=b)
+        vid = TL.vsa_forward_video(q, k, v, (1, 1, S), 3, gate, tile=(1, 1, b))
+        assert np.allclose(vid["out_raster"], dense["out"], rtol=1e-12, atol=1e-13), b
+        nq = len(O.block_sizes(S, b))
+        idx = vid["q2k_idx"].reshape(3, 2, nq, 3) - (np.arange(2) * nq)[None, :, None, None]
+        assert np.array_equal(idx.transpose(1, 0, 2, 3), dense["q2k_idx"]), b
 
 
 def pin_video_forward_tile_equivariance(seed=15):

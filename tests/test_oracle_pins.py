@@ -141,6 +141,17 @@ def _tiles_reverse_is_forward(T, H, W, tile=(4, 4, 4)):
     return m
 
 
+def _tiles_64_slots(T, H, W, tile=(4, 4, 4)):
+    # every tile padded to 64 slots whatever its size (overlapping slots for
+    # tiles of more than 64 tokens)
+    m = _tile_partition_ok(T, H, W, tile)
+    sizes = m["variable_block_sizes"]
+    first = np.concatenate([[0], np.cumsum(sizes)[:-1]])
+    tile_of = np.repeat(np.arange(len(sizes)), sizes)
+    m["non_pad_index"] = 64 * tile_of + (np.arange(len(tile_of)) - first[tile_of])
+    return m
+
+
 _forward_torch_ok = BW.forward_torch
 _lse_ok = BW.sparse_row_lse2
 
@@ -235,6 +246,7 @@ MISTAKES = {
     "tiles_local_order_w_slowest": ("tiles.tile_partition", _tiles_local_order_w_slowest),
     "tiles_not_padded": ("tiles.tile_partition", _tiles_unpadded),
     "tiles_reverse_is_forward": ("tiles.tile_partition", _tiles_reverse_is_forward),
+    "tiles_always_64_slots": ("tiles.tile_partition", _tiles_64_slots),
     "backward_gate_on_sparse": ("backward.forward_torch", _bw_gate_on_sparse),
     "backward_value_detached": ("backward.forward_torch", _bw_value_detached),
     "lse_natural_log": ("backward.sparse_row_lse2", _lse_natural_log),
