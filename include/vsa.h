@@ -388,11 +388,14 @@ int vsa_backward(const vsa_problem *problem, const vsa_bf16 *q, const vsa_bf16 *
  *
  * A latent is a T x H x W grid of tokens flattened in raster order (w
  * fastest).  It is cut into tiles of tile_t x tile_h x tile_w tokens (at most
- * 64; 4 x 4 x 4 is the usual choice), the last tile along an axis shorter when
- * the extent is not a multiple; tiles are ordered in raster order of their
- * tile coordinates and the tokens of a tile in raster order.  Each tile is
- * one VSA block of the PACKED layout: 64 slots, its first tile-size slots
- * valid.
+ * 256; 4 x 4 x 4 is the usual choice, 4 x 4 x 8 and 4 x 8 x 8 those of the
+ * 128/256-token variants of "[chore] release fastvideo-kernel 0.3.0"), the
+ * last tile along an axis shorter when the extent is not a multiple; tiles
+ * are ordered in raster order of their tile coordinates and the tokens of a
+ * tile in raster order.  Each tile is one VSA block of the PACKED layout:
+ * bs = 64 slots for tiles of at most 64 tokens, else 128 or 256 (the
+ * smallest that holds the tile), its first tile-size slots valid; the
+ * block_size of the forward problem is bs.
  */
 
 /*
@@ -401,9 +404,9 @@ int vsa_backward(const vsa_problem *problem, const vsa_bf16 *q, const vsa_bf16 *
  *   tile_sizes [num_tiles]                      valid tokens of each tile
  *   tile_partition_indices [T*H*W]              raster index of tiled position p
  *   reverse_tile_partition_indices [T*H*W]      tiled position of raster index r
- *   non_pad_index [T*H*W]                       slot 64*tile + rank of position p
+ *   non_pad_index [T*H*W]                       slot bs*tile + rank of position p
  * Errors: VSA_ERR_NULL (num_tiles NULL), VSA_ERR_SHAPE (an extent < 1, a tile
- * of more than 64 tokens, more than 2^31 - 1 tokens or slots).
+ * of more than 256 tokens, more than 2^31 - 1 tokens or slots).
  */
 int vsa_tile_partition(int32_t T, int32_t H, int32_t W, int32_t tile_t, int32_t tile_h, int32_t tile_w,
                        int32_t *num_tiles, int32_t *tile_sizes, int64_t *tile_partition_indices,
@@ -413,7 +416,8 @@ int vsa_tile_partition(int32_t T, int32_t H, int32_t W, int32_t tile_t, int32_t 
  * vsa_build_tile_metadata - the PACKED-layout metadata (same outputs and
  * conventions as vsa_build_metadata) of num_videos videos of one grid packed
  * one after another, queries and keys/values on the same tiles, top-k
- * clamped to the tile count.  Errors as vsa_build_metadata and
+ * clamped to the tile count; the slot counts in `sizes` are for blocks of bs
+ * slots (the forward's block_size).  Errors as vsa_build_metadata and
  * vsa_tile_partition; VSA_ERR_UNSUPPORTED beyond 4096 tiles per video.
  */
 int vsa_build_tile_metadata(int32_t num_videos, int32_t T, int32_t H, int32_t W, int32_t tile_t,
@@ -423,8 +427,8 @@ int vsa_build_tile_metadata(int32_t num_videos, int32_t T, int32_t H, int32_t W,
 
 /*
  * vsa_tile_gather - x [batch, heads, T*H*W, elems] (raster order, contiguous,
- * bf16) -> y [heads, batch * 64 * num_tiles, elems] in tile order, video b at
- * slots [b * 64 * num_tiles, (b + 1) * 64 * num_tiles), padding slots written
+ * bf16) -> y [heads, batch * bs * num_tiles, elems] in tile order, video b at
+ * slots [b * bs * num_tiles, (b + 1) * bs * num_tiles), padding slots written
  * with 0: the PACKED input of vsa_forward_varlen for the metadata of
  * vsa_build_tile_metadata (elems = head_dim for q/k/v, 1 for a per-token
  * gate, head_dim for a full gate).

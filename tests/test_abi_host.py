@@ -400,7 +400,10 @@ def test_layout_maps_on_cpu(tmp_path):
 
 TILE_CASES = [((4, 4, 4), (4, 4, 4)), ((5, 6, 7), (4, 4, 4)), ((3, 9, 2), (4, 4, 4)),
               ((8, 4, 12), (4, 4, 4)), ((6, 10, 5), (2, 4, 8)), ((1, 1, 130), (1, 1, 64)),
-              ((9, 1, 1), (8, 1, 1)), ((13, 17, 11), (4, 4, 4))]
+              ((9, 1, 1), (8, 1, 1)), ((13, 17, 11), (4, 4, 4)),
+              # 128/256-token tiles (blocks of 128 and 256 slots)
+              ((9, 10, 11), (4, 4, 8)), ((5, 9, 17), (4, 8, 8)), ((3, 7, 7), (3, 5, 7)),
+              ((1, 1, 300), (1, 1, 256)), ((8, 16, 24), (4, 8, 8))]
 
 
 @pytest.mark.parametrize("grid,tile", TILE_CASES)
@@ -413,13 +416,16 @@ def test_tile_partition_matches_oracle(lib, grid, tile):
         assert np.array_equal(got[key].numpy(), want[key]), key
 
 
-@pytest.mark.parametrize("grid,tile", TILE_CASES[:4])
+@pytest.mark.parametrize("grid,tile", TILE_CASES[:4] + TILE_CASES[8:])
 def test_tile_metadata_is_packed_layout(lib, grid, tile):
     import oracle.tiles as TL
     import video_sparse_attention_amd as vsa
     m = vsa.vsa_build_tile_metadata(3, grid, 7, tile)
     sizes = TL.tile_partition(*grid, tile)["variable_block_sizes"]
     n = len(sizes)
+    bs = TL.tile_block(tile)
+    assert m.block_size == bs == vsa.tile_block(tile)
+    assert m.sizes.q_slots == m.sizes.kv_slots == 3 * n * bs
     assert m.sizes.num_seqs == 3 and m.sizes.total_q_blocks == 3 * n == m.sizes.total_kv_blocks
     assert m.cu_blocks_q.tolist() == [0, n, 2 * n, 3 * n] == m.cu_blocks_kv.tolist()
     assert np.array_equal(m.block_sizes_q.numpy(), np.tile(sizes, 3))
@@ -432,7 +438,9 @@ def test_tile_errors(lib):
     E = _abi
     assert lib.vsa_tile_partition(4, 4, 4, 4, 4, 4, None, None, None, None, None) == E.VSA_ERR_NULL
     assert lib.vsa_tile_partition(0, 4, 4, 4, 4, 4, ctypes.byref(nt), None, None, None, None) == E.VSA_ERR_SHAPE
-    assert lib.vsa_tile_partition(4, 4, 4, 8, 4, 4, ctypes.byref(nt), None, None, None, None) == E.VSA_ERR_SHAPE
+    assert lib.vsa_tile_partition(4, 4, 4, 8, 8, 8, ctypes.byref(nt), None, None, None, None) == E.VSA_ERR_SHAPE
+    assert lib.vsa_tile_partition(4, 4, 4, 1, 1, 257, ctypes.byref(nt), None, None, None, None) == E.VSA_ERR_SHAPE
+    assert lib.vsa_tile_partition(4, 4, 4, 4, 8, 8, ctypes.byref(nt), None, None, None, None) == 0
     assert lib.vsa_tile_partition(4, 4, 4, 4, 0, 4, ctypes.byref(nt), None, None, None, None) == E.VSA_ERR_SHAPE
     sizes = _abi.VsaMetaSizes()
     assert lib.vsa_build_tile_metadata(0, 4, 4, 4, 4, 4, 4, 1, ctypes.byref(sizes),
@@ -451,7 +459,7 @@ def test_tile_errors(lib):
     assert g(A, ctypes.c_void_p(FAKE + 4096), 1, 2, 4, 4, 4, 4, 4, 4, 128, None) == E.VSA_ERR_ALIAS
     assert g(A, O_, 0, 2, 4, 4, 4, 4, 4, 4, 128, None) == E.VSA_ERR_SHAPE
     assert g(A, O_, 1, 2, 4, 4, 4, 4, 4, 4, 0, None) == E.VSA_ERR_SHAPE
-    assert g(A, O_, 1, 2, 4, 4, 4, 3, 5, 5, 128, None) == E.VSA_ERR_SHAPE
+    assert g(A, O_, 1, 2, 4, 4, 4, 3, 10, 9, 128, None) == E.VSA_ERR_SHAPE  # 270-token tile
     assert lib.vsa_tile_scatter(A, ctypes.c_void_p(FAKE + 2), 1, 2, 4, 4, 4, 4, 4, 4, 1, None) == E.VSA_ERR_ALIAS
     assert lib.vsa_tile_scatter(A, ctypes.c_void_p(FAKE + (3 << 32) + 1), 1, 2, 4, 4, 4, 4, 4, 4, 1,
                                 None) == E.VSA_ERR_ALIGN

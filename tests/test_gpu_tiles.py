@@ -22,6 +22,9 @@ def _bits(t):
 @pytest.mark.parametrize("grid,tile,E", [
     ((5, 6, 7), (4, 4, 4), 128), ((3, 9, 2), (4, 4, 4), 64), ((6, 10, 5), (2, 4, 8), 16),
     ((5, 6, 7), (4, 4, 4), 1), ((4, 5, 3), (4, 4, 4), 3), ((1, 1, 130), (1, 1, 64), 8),
+    # tiles of 128 / 256 tokens in blocks of 128 / 256 slots
+    ((9, 10, 11), (4, 4, 8), 128), ((5, 9, 17), (4, 8, 8), 64), ((3, 7, 7), (3, 5, 7), 1),
+    ((1, 1, 300), (1, 1, 256), 8),
 ])
 def test_tile_gather_scatter_bit_exact(grid, tile, E):
     G.note(f"case tile copy grid={grid} tile={tile} E={E}")
@@ -51,6 +54,9 @@ def _video_inputs(B, Hh, grid, D, seed, gated=True):
     ((5, 6, 7), (4, 4, 4), 64, 3),        # partial tiles along every axis
     ((8, 8, 12), (4, 4, 4), 128, 4),      # full tiles only
     ((6, 10, 5), (2, 4, 8), 128, 5),      # a non-cubic tile
+    ((9, 10, 11), (4, 4, 8), 128, 3),     # 128-token tiles, partial along every axis
+    ((8, 16, 20), (4, 8, 8), 64, 4),      # 256-token tiles, partial along w
+    ((5, 9, 17), (4, 8, 8), 128, 2),      # 256-token tiles, partial along every axis
 ])
 def test_video_forward_matches_oracle(grid, tile, D, topk):
     B, Hh = 2, 3
@@ -67,13 +73,15 @@ def test_video_forward_matches_oracle(grid, tile, D, topk):
     G.note(f"  out max-abs {mx:.2e} mean-abs {mean:.2e}")
 
 
-def test_video_1d_equals_dense():
-    """A 1 x 1 x S grid in 1 x 1 x 64 tiles is the dense forward, bit for bit."""
-    S, D = 64 * 6 + 19, 128
-    q, k, v, gate = _video_inputs(2, 3, (1, 1, S), D, seed=77)
+@pytest.mark.parametrize("bs", [64, 128, 256])
+def test_video_1d_equals_dense(bs):
+    """A 1 x 1 x S grid in 1 x 1 x bs tiles is the dense forward with VSA
+    blocks of bs tokens, bit for bit."""
+    S, D = bs * 6 + 19, 128
+    q, k, v, gate = _video_inputs(2, 3, (1, 1, S), D, seed=77 + bs)
     dev = [t.to(G.DEV) for t in (q, k, v, gate)]
-    a = vsa.vsa_forward_video(*dev[:3], (1, 1, S), 4, dev[3], (1, 1, 64))
-    b = vsa.vsa_forward(*dev[:3], 4, dev[3])
+    a = vsa.vsa_forward_video(*dev[:3], (1, 1, S), 4, dev[3], (1, 1, bs))
+    b = vsa.vsa_forward(*dev[:3], 4, dev[3], block_size=bs)
     torch.cuda.synchronize()
     assert torch.equal(a.cpu(), b.cpu())
 

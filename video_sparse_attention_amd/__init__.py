@@ -15,6 +15,7 @@ from .binding import (  # noqa: E402,F401
     dense_problem,
     token_shapes,
     DEFAULT_TILE,
+    tile_block,
     tile_gather,
     tile_partition,
     tile_scatter,
@@ -38,7 +39,7 @@ from .binding import (  # noqa: E402,F401
 
 __all__ = [
     "BLOCK", "VarlenMeta", "VsaError", "alloc_workspace", "block_shapes", "dense_problem",
-    "token_shapes", "DEFAULT_TILE", "tile_gather", "tile_partition", "tile_scatter",
+    "token_shapes", "DEFAULT_TILE", "tile_block", "tile_gather", "tile_partition", "tile_scatter",
     "vsa_build_tile_metadata", "vsa_forward_video", "vsa_build_metadata", "vsa_coarse_topk", "vsa_combine", "vsa_forward",
     "vsa_forward_varlen", "vsa_sparse_attn_combine", "vsa_sparse_attn_from_indices", "vsa_workspace_size",
     "alloc_backward_workspace", "lse_shape", "video_sparse_attn", "vsa_backward",

@@ -524,7 +524,7 @@ def vsa_build_tile_metadata(num_videos: int, grid, topk: int, tile=DEFAULT_TILE,
                                            _ptr(cu_kv), _ptr(bs_q), _ptr(bs_kv), _ptr(tkc)),
                "vsa_build_tile_metadata")
     S = T * H * W
-    meta = VarlenMeta(sizes, [S] * n, [S] * n, cu_q, cu_kv, bs_q, bs_kv, tkc)
+    meta = VarlenMeta(sizes, [S] * n, [S] * n, cu_q, cu_kv, bs_q, bs_kv, tkc, block_size=tile_block(tile))
     return meta.to(device) if device is not None else meta
 
 
@@ -532,9 +532,16 @@ def _tile_count(grid, tile) -> int:
     return -(-grid[0] // tile[0]) * -(-grid[1] // tile[1]) * -(-grid[2] // tile[2])
 
 
+def tile_block(tile) -> int:
+    """Slots per tile (the VSA block size of the tiled forward): 64 for
+    tiles of at most 64 tokens, else 128 or 256."""
+    n = tile[0] * tile[1] * tile[2]
+    return BLOCK if n <= BLOCK else (2 * BLOCK if n <= 2 * BLOCK else 4 * BLOCK)
+
+
 def tile_gather(x: torch.Tensor, grid, tile=DEFAULT_TILE, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """``x`` ``[B, heads, T*H*W(, E)]`` raster -> ``[heads, B * 64 * n_tiles(, E)]``
-    tile order with zero padding (vsa_tile_gather)."""
+    """``x`` ``[B, heads, T*H*W(, E)]`` raster -> ``[heads, B * bs * n_tiles(, E)]``
+    tile order with zero padding, bs = tile_block(tile) (vsa_tile_gather)."""
     T, H, W = grid
     squeeze = x.dim() == 3
     if x.dim() not in (3, 4) or x.shape[2] != T * H * W:
@@ -542,7 +549,7 @@ def tile_gather(x: torch.Tensor, grid, tile=DEFAULT_TILE, out: Optional[torch.Te
     _need(x, "x", torch.bfloat16)
     B, Hh = x.shape[0], x.shape[1]
     E = 1 if squeeze else x.shape[3]
-    slots = BLOCK * _tile_count(grid, tile)
+    slots = tile_block(tile) * _tile_count(grid, tile)
     shape = (Hh, B * slots) if squeeze else (Hh, B * slots, E)
     if out is None:
         out = torch.empty(shape, dtype=torch.bfloat16, device=x.device)
@@ -554,10 +561,10 @@ def tile_gather(x: torch.Tensor, grid, tile=DEFAULT_TILE, out: Optional[torch.Te
 
 def tile_scatter(y: torch.Tensor, grid, batch: int, tile=DEFAULT_TILE,
                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Inverse of ``tile_gather``: ``[heads, B * 64 * n_tiles(, E)]`` ->
+    """Inverse of ``tile_gather``: ``[heads, B * bs * n_tiles(, E)]`` ->
     ``[B, heads, T*H*W(, E)]`` (vsa_tile_scatter)."""
     T, H, W = grid
-    slots = BLOCK * _tile_count(grid, tile)
+    slots = tile_block(tile) * _tile_count(grid, tile)
     squeeze = y.dim() == 2
     if y.dim() not in (2, 3) or y.shape[1] != batch * slots:
         raise ValueError(f"y must be [heads, {batch * slots}(, E)], got {tuple(y.shape)}")

@@ -17,7 +17,7 @@ namespace {
 constexpr int kCopyThreads = 256;
 
 // One workgroup per (tile, video, head): the tile's geometry is worked out
-// once, then the 64 slots x copy units of the tile are spread over the
+// once, then the blk slots x copy units of the tile are spread over the
 // threads (32-bit index arithmetic only).
 template <bool VEC>
 __global__ __launch_bounds__(kCopyThreads) void tile_copy_kernel(TileGrid G, const uint16_t* __restrict__ src,
@@ -29,11 +29,11 @@ __global__ __launch_bounds__(kCopyThreads) void tile_copy_kernel(TileGrid G, con
     const int b = bh % B, h = bh / B;
     int et, eh, ew;
     const int size = tile_extents(G, tile, et, eh, ew);
-    const int64_t P = (int64_t)kBlock * G.ntiles;
+    const int64_t P = (int64_t)G.blk * G.ntiles;
     const int64_t S = (int64_t)G.T * G.H * G.W;
-    const int64_t tiled0 = ((int64_t)h * B + b) * P + (int64_t)kBlock * tile;  // row of slot 0
+    const int64_t tiled0 = ((int64_t)h * B + b) * P + (int64_t)G.blk * tile;  // row of slot 0
     const int64_t raster0 = ((int64_t)b * Hh + h) * S;
-    for (int i = threadIdx.x; i < kBlock * cpr; i += kCopyThreads) {
+    for (int i = threadIdx.x; i < G.blk * cpr; i += kCopyThreads) {
         const int u = i / cpr, c = i - u * cpr;
         const int64_t tiled = tiled0 + u;
         if (u >= size) {

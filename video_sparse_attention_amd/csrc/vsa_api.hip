@@ -279,12 +279,12 @@ int run_coarse(const vsa::DevProblem& P, const uint16_t* q, const uint16_t* k, c
 
 int check_tiles(int32_t T, int32_t H, int32_t W, int32_t tt, int32_t th, int32_t tw, vsa::TileGrid* g) {
     if (T < 1 || H < 1 || W < 1) return fail(VSA_ERR_SHAPE, "grid extents must be >= 1 (got %d x %d x %d)", T, H, W);
-    if (tt < 1 || th < 1 || tw < 1 || (int64_t)tt * th * tw > VSA_BLOCK)
+    if (tt < 1 || th < 1 || tw < 1 || (int64_t)tt * th * tw > 4 * VSA_BLOCK)
         return fail(VSA_ERR_SHAPE, "tile %d x %d x %d: extents must be >= 1 and the tile at most %d tokens", tt, th,
-                    tw, VSA_BLOCK);
+                    tw, 4 * VSA_BLOCK);
     if ((int64_t)T * H * W > 0x7fffffffLL) return fail(VSA_ERR_SHAPE, "grid exceeds 2^31 - 1 tokens");
     *g = vsa::make_tile_grid(T, H, W, tt, th, tw);
-    if ((int64_t)g->ntiles * VSA_BLOCK > 0x7fffffffLL) return fail(VSA_ERR_SHAPE, "padded length exceeds 2^31 slots");
+    if ((int64_t)g->ntiles * g->blk > 0x7fffffffLL) return fail(VSA_ERR_SHAPE, "padded length exceeds 2^31 slots");
     return VSA_OK;
 }
 
@@ -295,7 +295,7 @@ int tile_copy(const vsa_bf16* src, vsa_bf16* dst, int32_t batch, int32_t heads, 
     if (rc) return rc;
     if (batch < 1 || heads < 1 || elems < 1)
         return fail(VSA_ERR_SHAPE, "batch, heads and elems must be >= 1 (got %d, %d, %d)", batch, heads, elems);
-    if ((int64_t)batch * g.ntiles * VSA_BLOCK > 0x7fffffffLL)
+    if ((int64_t)batch * g.ntiles * g.blk > 0x7fffffffLL)
         return fail(VSA_ERR_SHAPE, "packed length exceeds 2^31 slots");
     if (!src || !dst) return fail(VSA_ERR_NULL, "source or destination is NULL");
     const bool vec = elems % 8 == 0;
@@ -303,7 +303,7 @@ int tile_copy(const vsa_bf16* src, vsa_bf16* dst, int32_t batch, int32_t heads, 
     if (((uintptr_t)src & mask) || ((uintptr_t)dst & mask))
         return fail(VSA_ERR_ALIGN, "tensors must be %d-byte aligned", vec ? 16 : 2);
     const int64_t raster_bytes = 2LL * batch * heads * ((int64_t)T * H * W) * elems;
-    const int64_t tiled_bytes = 2LL * batch * heads * ((int64_t)g.ntiles * VSA_BLOCK) * elems;
+    const int64_t tiled_bytes = 2LL * batch * heads * ((int64_t)g.ntiles * g.blk) * elems;
     const int64_t sb = scatter ? tiled_bytes : raster_bytes, db = scatter ? raster_bytes : tiled_bytes;
     if (overlaps(src, sb, dst, db)) return fail(VSA_ERR_ALIAS, "source and destination overlap");
     rc = hip_status(vsa::launch_tile_copy(g, src, dst, batch, heads, elems, scatter, (hipStream_t)stream),
@@ -708,7 +708,7 @@ int vsa_tile_partition(int32_t T, int32_t H, int32_t W, int32_t tile_t, int32_t 
             const int64_t r = vsa::tile_token_raster(g, b, u, eh, ew);
             if (tile_partition_indices) tile_partition_indices[p] = r;
             if (reverse_tile_partition_indices) reverse_tile_partition_indices[r] = p;
-            if (non_pad_index) non_pad_index[p] = (int64_t)VSA_BLOCK * b + u;
+            if (non_pad_index) non_pad_index[p] = (int64_t)g.blk * b + u;
         }
     }
     return ok();
@@ -730,7 +730,7 @@ int vsa_build_tile_metadata(int32_t num_videos, int32_t T, int32_t H, int32_t W,
     const int nout = !!cu_blocks_q + !!cu_blocks_kv + !!block_sizes_q + !!block_sizes_kv + !!topk_clamped;
     if (nout != 0 && nout != 5) return fail(VSA_ERR_NULL, "pass all five output arrays or none");
     const int64_t total = (int64_t)num_videos * g.ntiles;
-    if (total * VSA_BLOCK > 0x7fffffffLL) return fail(VSA_ERR_SHAPE, "packed length exceeds 2^31 slots");
+    if (total * g.blk > 0x7fffffffLL) return fail(VSA_ERR_SHAPE, "packed length exceeds 2^31 slots");
     const int32_t kk = std::min(topk, g.ntiles);
     sizes->num_seqs = num_videos;
     sizes->total_q_blocks = (int32_t)total;
@@ -738,8 +738,8 @@ int vsa_build_tile_metadata(int32_t num_videos, int32_t T, int32_t H, int32_t W,
     sizes->max_q_blocks = g.ntiles;
     sizes->max_kv_blocks = g.ntiles;
     sizes->max_topk = kk;
-    sizes->q_slots = total * VSA_BLOCK;
-    sizes->kv_slots = total * VSA_BLOCK;
+    sizes->q_slots = total * g.blk;
+    sizes->kv_slots = total * g.blk;
     if (nout == 0) return ok();
     for (int s = 0; s <= num_videos; ++s) cu_blocks_q[s] = cu_blocks_kv[s] = s * g.ntiles;
     for (int s = 0; s < num_videos; ++s) {

@@ -137,15 +137,19 @@ __device__ __forceinline__ int seq_of_qblock(const DevProblem& P, int g) {
 
 // ---------------------------------------------------------------------------
 // 3-D tile partition of a T x H x W token grid (raster order, w fastest) into
-// tiles of tt x th x tw tokens: tiles in raster order of their tile
-// coordinates (edge tiles shorter), tokens in raster order inside a tile.
-// ("[kernel] Extract VSA utility functions into fastvideo_kernel", Summary.)
+// tiles of tt x th x tw tokens (at most 256): tiles in raster order of their
+// tile coordinates (edge tiles shorter), tokens in raster order inside a
+// tile; each tile is one VSA block of blk slots, the smallest of 64, 128 and
+// 256 that holds it.  ("[kernel] Extract VSA utility functions into
+// fastvideo_kernel", Summary; the 128/256-token variants of "[chore] release
+// fastvideo-kernel 0.3.0".)
 // ---------------------------------------------------------------------------
 struct TileGrid {
     int T, H, W;     // token grid
     int tt, th, tw;  // tile extents
     int nt, nh, nw;  // tiles along each axis
     int ntiles;
+    int blk;         // slots per tile (VSA block size)
 };
 
 __host__ __device__ inline TileGrid make_tile_grid(int T, int H, int W, int tt, int th, int tw) {
@@ -156,6 +160,8 @@ __host__ __device__ inline TileGrid make_tile_grid(int T, int H, int W, int tt, 
     g.nh = (H + th - 1) / th;
     g.nw = (W + tw - 1) / tw;
     g.ntiles = g.nt * g.nh * g.nw;
+    const int vol = tt * th * tw;
+    g.blk = vol <= kBlock ? kBlock : (vol <= 2 * kBlock ? 2 * kBlock : 4 * kBlock);
     return g;
 }
 
@@ -207,7 +213,7 @@ hipError_t launch_sparse_attn_combine(const DevProblem& P, const uint16_t* q, co
                                       const uint16_t* v, const int* idx, const int* num, const float* out_c,
                                       const uint16_t* gate, int mode, int64_t gs0, int64_t gs1, int64_t gs2,
                                       uint16_t* out, uint16_t* out_s, float* lse, hipStream_t st);
-// gather (scatter = false): x [B, Hh, T*H*W, elems] raster -> y [Hh, B * 64 *
+// gather (scatter = false): x [B, Hh, T*H*W, elems] raster -> y [Hh, B * blk *
 // ntiles, elems] tile order with zero padding; scatter: the inverse.
 hipError_t launch_tile_copy(const TileGrid& g, const uint16_t* src, uint16_t* dst, int B, int Hh, int elems,
                             bool scatter, hipStream_t st);
