@@ -189,6 +189,14 @@ def test_backward_varlen_matches_per_sequence(block):
     vsa.vsa_backward(prob, q, k, v, idx, num, out_c, gate, out_s, lse, dout, dq, dk, dv, dg)
     torch.cuda.synchronize()
     dq, dk, dv, dg, lse = (t.cpu() for t in (dq, dk, dv, dg, lse))
+    # the autograd wrapper over the same packed problem: the same bits
+    qa, ka, va, ga = (t.clone().requires_grad_(True) for t in (q, k, v, gate))
+    outa = vsa.video_sparse_attn_varlen(qa, ka, va, meta, ga)
+    outa.backward(dout)
+    torch.cuda.synchronize()
+    assert torch.equal(outa.detach().cpu(), out.cpu())
+    for t, want, name in ((qa, dq, "dq"), (ka, dk, "dk"), (va, dv, "dv"), (ga, dg, "dgate")):
+        assert torch.equal(t.grad.cpu(), want), f"autograd {name}"
     oq = okv = 0
     for s, (sq, skv) in enumerate(zip(seqlens_q, seqlens_kv)):
         per = inp.per_seq[s]

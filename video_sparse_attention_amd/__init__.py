@@ -32,6 +32,7 @@ from .binding import (  # noqa: E402,F401
     alloc_backward_workspace,
     lse_shape,
     video_sparse_attn,
+    video_sparse_attn_varlen,
     vsa_backward,
     vsa_backward_workspace_size,
     vsa_sparse_attn_combine_train,
@@ -42,6 +43,6 @@ __all__ = [
     "token_shapes", "DEFAULT_TILE", "tile_block", "tile_gather", "tile_partition", "tile_scatter",
     "vsa_build_tile_metadata", "vsa_forward_video", "vsa_build_metadata", "vsa_coarse_topk", "vsa_combine", "vsa_forward",
     "vsa_forward_varlen", "vsa_sparse_attn_combine", "vsa_sparse_attn_from_indices", "vsa_workspace_size",
-    "alloc_backward_workspace", "lse_shape", "video_sparse_attn", "vsa_backward",
+    "alloc_backward_workspace", "lse_shape", "video_sparse_attn", "video_sparse_attn_varlen", "vsa_backward",
     "vsa_backward_workspace_size", "vsa_sparse_attn_combine_train",
 ]

@@ -340,14 +340,8 @@ class _VideoSparseAttn(torch.autograd.Function):
     backward = vsa_backward (the routing is held fixed)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, gate, topk, block_size, bshd):
-        if bshd:
-            B, Sq, H, D = q.shape
-            Skv = k.shape[1]
-        else:
-            B, H, Sq, D = q.shape
-            Skv = k.shape[2]
-        problem = dense_problem(B, H, Sq, Skv, D, topk, block_size, bshd)
+    def forward(ctx, q, k, v, gate, problem, keep):
+        # keep: the packed metadata whose device arrays the problem points to
         q, k, v = q.detach(), k.detach(), v.detach()
         g = None if gate is None else gate.detach()
         cs, isz, ns = block_shapes(problem)
@@ -361,6 +355,7 @@ class _VideoSparseAttn(torch.autograd.Function):
         lse = torch.empty(lse_shape(problem), dtype=torch.float32, device=dev)
         vsa_sparse_attn_combine_train(problem, q, k, v, idx, num, out_c, g, out, out_s, lse)
         ctx.problem = problem
+        ctx.keep = keep
         ctx.has_gate = g is not None
         ctx.save_for_backward(q, k, v, *( [g] if g is not None else []), idx, num, out_c, out_s, lse)
         ctx.mark_non_differentiable(idx, num)
@@ -376,7 +371,7 @@ class _VideoSparseAttn(torch.autograd.Function):
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         dg = None if g is None else torch.empty(g.shape, dtype=torch.bfloat16, device=q.device)
         vsa_backward(ctx.problem, q, k, v, idx, num, out_c, g, out_s, lse, dout, dq, dk, dv, dg)
-        return dq, dk, dv, dg, None, None, None
+        return dq, dk, dv, dg, None, None
 
 
 def video_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int,
@@ -387,9 +382,35 @@ def video_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: i
     gradients of q, k, v and the gate (``[B, H, Sq]`` or ``[B, H, Sq, D]``;
     ``[B, Sq, H(, D)]`` with ``bshd``) from vsa_backward.  ``block_size``: the
     VSA block, 64, 128 or 256 tokens."""
-    if q.dim() != 4:
-        raise ValueError("q must be [B, H, S, D] ([B, S, H, D] with bshd)")
-    out, idx, num = _VideoSparseAttn.apply(q, k, v, gate, topk, block_size, bshd)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, S, D] ([B, S, H, D] with bshd)")
+    if bshd:
+        B, Sq, H, D = q.shape
+        Skv = k.shape[1]
+    else:
+        B, H, Sq, D = q.shape
+        Skv = k.shape[2]
+    problem = dense_problem(B, H, Sq, Skv, D, topk, block_size, bshd)
+    out, idx, num = _VideoSparseAttn.apply(q, k, v, gate, problem, None)
+    return (out, idx, num) if return_routing else out
+
+
+def video_sparse_attn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, meta: VarlenMeta,
+                             gate: Optional[torch.Tensor] = None, return_routing: bool = False):
+    """Differentiable VSA over block-padded packed sequences (``q``
+    ``[H, bs*Nq, D]``, ``k``/``v`` ``[H, bs*Nkv, D]``, ``meta`` from
+    ``vsa_build_metadata`` with the same block size): the forward of
+    ``vsa_forward_varlen`` and, through autograd, the gradients of q, k, v and
+    the gate (``[H, bs*Nq]`` or ``[H, bs*Nq, D]``) from vsa_backward, padding
+    slots 0.  With ``return_routing`` also returns ``q2k_idx`` (global KV
+    block numbers) and ``q2k_num``."""
+    if q.dim() != 3:
+        raise ValueError("packed q must be [H, slots, D]")
+    H, _, D = q.shape
+    if meta.device_arrays is None:
+        meta.to(q.device)
+    problem = meta.problem(H, D)
+    out, idx, num = _VideoSparseAttn.apply(q, k, v, gate, problem, meta)
     return (out, idx, num) if return_routing else out
 
 
