@@ -388,8 +388,8 @@ def main():
         return
     inp = synth.workload(args.workload)
     block = args.block_size
-    if block != 64 and args.workload != "large":
-        print("--block-size applies to the large workload only", file=sys.stderr)
+    if block != 64 and args.workload not in ("large", "varlen_many"):
+        print("--block-size applies to the large and varlen_many workloads only", file=sys.stderr)
         sys.exit(2)
 
     flops = None
@@ -407,18 +407,27 @@ def main():
                "batch": B, "heads": H, "head_dim": D, "seq_len": Sq, "block": block,
                "topk": inp.topk, "gate": "token"}
     else:
-        meta = vsa.vsa_build_metadata(inp.seqlens_q, inp.seqlens_kv, inp.topk, device=dev)
+        if block != 64:  # the same sequences in VSA blocks of 128 / 256 slots, top-k about 20 % of them
+            w = synth.WORKLOADS[args.workload]
+            tk_b = [math.ceil(0.20 * -(-s // block)) for s in w["seqlens_kv"]]
+            inp = synth.varlen_inputs(w["seqlens_q"], w["seqlens_kv"], w["H"], w["D"], tk_b, w["seed"], w["gated"],
+                                      name=args.workload, block=block)
+        meta = vsa.vsa_build_metadata(inp.seqlens_q, inp.seqlens_kv, inp.topk, device=dev, block_size=block)
         H, D = inp.heads, inp.head_dim
         prob = meta.problem(H, D)
         tk = meta.topk.tolist()
-        nqs = [-(-s // 64) for s in inp.seqlens_q]
-        flops = 4.0 * H * sum(n * k for n, k in zip(nqs, tk)) * 64 * 64 * D
+        nqs = [-(-s // block) for s in inp.seqlens_q]
+        # every sequence is a whole number of VSA blocks here: each selected
+        # block stands for block / 64 full 64-token KV blocks, for each of the
+        # block / 64 query blocks of a VSA query block
+        r = block // 64
+        flops = 4.0 * H * sum(n * k * r * r for n, k in zip(nqs, tk)) * 64 * 64 * D
         q_tokens = H * sum(inp.seqlens_q)
         n_qblocks = H * sum(nqs)
-        n_kvblocks = H * sum(-(-s // 64) for s in inp.seqlens_kv)
-        cfg = {"workload": f"{len(nqs)} packed sequences, Q blocks {nqs}, KV = Q + 8 blocks, "
-                           f"H={H} D={D}, top-k {tk}, gated",
-               "heads": H, "head_dim": D, "block": 64, "topk": tk, "gate": "token"}
+        n_kvblocks = H * sum(-(-s // block) for s in inp.seqlens_kv)
+        cfg = {"workload": f"{len(nqs)} packed sequences, Q blocks {nqs} of {block} tokens, "
+                           f"KV = Q + {512 // block} blocks, H={H} D={D}, top-k {tk}, gated",
+               "heads": H, "head_dim": D, "block": block, "topk": tk, "gate": "token"}
 
     q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
     gate = None if inp.gate is None else inp.gate.to(dev)
