@@ -1,6 +1,7 @@
 """Seeded random sweep of the forward against the fp64 oracle (shapes,
 head dims, VSA block sizes, both dense layouts, every gate mode, top-k up to
-past the block count), and capture of the forward in a HIP graph replayed
+past the block count), packed batches (VSA blocks of 64, 128 and 256 slots;
+forward and backward), and capture of the forward in a HIP graph replayed
 against eager runs."""
 import numpy as np
 import pytest
@@ -143,3 +144,71 @@ def test_random_backward(cfg):
     inp = sweep_inputs(cfg)
     check_dense_case(inp.q, inp.k, inp.v, inp.gate, cfg["topk"], cfg["seed"] + 5, f"sweep {cfg}",
                      block_size=cfg["block"], bshd=cfg["bshd"])
+
+
+def varlen_block_configs(n=8, seed=80, base=9800):
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        block = int(rng.choice([128, 256]))
+        ns = int(rng.integers(1, 5))
+        lq = [int(x) for x in rng.integers(1, 4 * block, ns)]
+        lkv = lq if rng.random() < 0.5 else [int(x) for x in rng.integers(1, 4 * block, ns)]
+        topk = [int(rng.integers(1, -(-s // block) + 2)) for s in lkv]
+        out.append(dict(lq=lq, lkv=lkv, topk=topk, H=int(rng.integers(1, 3)), D=int(rng.choice([64, 128])),
+                        gated=bool(rng.random() < 0.5), block=block, seed=base + c))
+    return out
+
+
+@pytest.mark.parametrize("cfg", varlen_block_configs(), ids=lambda c: f"vb{c['seed']}")
+def test_random_varlen_large_blocks(cfg):
+    """Packed sequences of random lengths in VSA blocks of 128 / 256 slots
+    (trailing 64-token blocks of a VSA block often empty): every stage against
+    the oracle's separate varlen path."""
+    G.note(f"case {cfg}")
+    inp = synth.varlen_inputs(cfg["lq"], cfg["lkv"], cfg["H"], cfg["D"], cfg["topk"], cfg["seed"], cfg["gated"],
+                              block=cfg["block"])
+    ref = G.oracle_varlen(inp)
+    G.assert_tie_free(ref)
+    gpu = G.run_varlen_stages(inp)
+    G.assert_indices_equal(gpu["q2k_idx"], gpu["q2k_num"], ref)
+    N.check_out_c(N.f64(gpu["out_c"]), ref["out_c"])
+    N.check_sparse(N.f64(gpu["out_s"]), ref["out_s"])
+    mx, mean = N.check_out(N.f64(gpu["out_fused"]), ref["out"], "out (fused combine)")
+    G.note(f"  out max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
+@pytest.mark.parametrize("cfg", varlen_block_configs(n=6, seed=81, base=9900), ids=lambda c: f"vbb{c['seed']}")
+def test_random_varlen_backward(cfg):
+    """The packed training forward and backward (autograd wrapper) with VSA
+    blocks of 128 / 256 slots: each sequence's gradients against the backward
+    oracle run on that sequence alone; padding slots of every gradient 0."""
+    from oracle import vsa_backward as BW
+    from tests.test_gpu_backward import check_grad
+    G.note(f"case {cfg}")
+    inp = synth.varlen_inputs(cfg["lq"], cfg["lkv"], cfg["H"], cfg["D"], cfg["topk"], cfg["seed"], True,
+                              block=cfg["block"])
+    bs = cfg["block"]
+    dev = G.DEV
+    meta = vsa.vsa_build_metadata(cfg["lq"], cfg["lkv"], cfg["topk"], device=dev, block_size=bs)
+    dout = synth.output_grad(inp.q.shape, cfg["seed"] + 7)
+    q, k, v, g = (t.to(dev).requires_grad_(True) for t in (inp.q, inp.k, inp.v, inp.gate))
+    vsa.video_sparse_attn_varlen(q, k, v, meta, g).backward(dout.to(dev))
+    torch.cuda.synchronize()
+    dq, dk, dv, dg = (t.grad.cpu() for t in (q, k, v, g))
+    oq = okv = 0
+    for s, (sq, skv) in enumerate(zip(cfg["lq"], cfg["lkv"])):
+        per = inp.per_seq[s]
+        one = lambda t: N.f64(t)[None]
+        ref = BW.vsa_backward(one(per["q"]), one(per["k"]), one(per["v"]), cfg["topk"][s], one(per["gate"]),
+                              N.f64(dout[:, oq:oq + sq])[None], block=bs)
+        G.assert_tie_free(ref)
+        check_grad(N.f64(dq[:, oq:oq + sq]), ref["dq"][0], f"dq[{s}]")
+        check_grad(N.f64(dk[:, okv:okv + skv]), ref["dk"][0], f"dk[{s}]")
+        check_grad(N.f64(dv[:, okv:okv + skv]), ref["dv"][0], f"dv[{s}]")
+        check_grad(N.f64(dg[:, oq:oq + sq]), ref["dgate"][0], f"dgate[{s}]")
+        nq, nkv = -(-sq // bs), -(-skv // bs)
+        assert (dq[:, oq + sq:oq + bs * nq] == 0).all() and (dg[:, oq + sq:oq + bs * nq] == 0).all()
+        assert (dk[:, okv + skv:okv + bs * nkv] == 0).all() and (dv[:, okv + skv:okv + bs * nkv] == 0).all()
+        oq += bs * nq
+        okv += bs * nkv
