@@ -407,11 +407,8 @@ def main():
                "batch": B, "heads": H, "head_dim": D, "seq_len": Sq, "block": block,
                "topk": inp.topk, "gate": "token"}
     else:
-        if block != 64:  # the same sequences in VSA blocks of 128 / 256 slots, top-k about 20 % of them
-            w = synth.WORKLOADS[args.workload]
-            tk_b = [math.ceil(0.20 * -(-s // block)) for s in w["seqlens_kv"]]
-            inp = synth.varlen_inputs(w["seqlens_q"], w["seqlens_kv"], w["H"], w["D"], tk_b, w["seed"], w["gated"],
-                                      name=args.workload, block=block)
+        if block != 64:  # the same sequences in VSA blocks of 128 / 256 slots, top-k 20 % of them
+            inp = synth.workload(args.workload, block=block)
         meta = vsa.vsa_build_metadata(inp.seqlens_q, inp.seqlens_kv, inp.topk, device=dev, block_size=block)
         H, D = inp.heads, inp.head_dim
         prob = meta.problem(H, D)

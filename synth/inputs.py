@@ -163,7 +163,7 @@ WORKLOADS = {
                         seed=1002),
     # 3: three packed sequences of 5, 9 and 14 blocks, the last ending in a
     #    40-token partial block; top-k = ceil(0.25 * KV blocks)
-    "varlen_small": dict(kind="varlen", H=16, D=128, gated=False, seed=1003,
+    "varlen_small": dict(kind="varlen", H=16, D=128, gated=False, seed=1003, topk_frac=0.25,
                          seqlens_q=[5 * 64, 9 * 64, 13 * 64 + 40],
                          seqlens_kv=[5 * 64, 9 * 64, 13 * 64 + 40],
                          topk=[_frac_topk(n, 0.25) for n in (5, 9, 14)]),
@@ -172,20 +172,27 @@ WORKLOADS = {
                   gated=True, seed=1004),
     # 5: eight packed sequences, Q blocks 32..144 step 16, KV = Q + 8 blocks,
     #    top-k = ceil(0.20 * KV blocks), gated
-    "varlen_many": dict(kind="varlen", H=24, D=128, gated=True, seed=1005,
+    "varlen_many": dict(kind="varlen", H=24, D=128, gated=True, seed=1005, topk_frac=0.20,
                         seqlens_q=[64 * n for n in _VARLEN_MANY_Q_BLOCKS],
                         seqlens_kv=[64 * (n + 8) for n in _VARLEN_MANY_Q_BLOCKS],
                         topk=[_frac_topk(n + 8, 0.20) for n in _VARLEN_MANY_Q_BLOCKS]),
 }
 
 
-def workload(name: str, heads: Optional[int] = None):
-    """Build a named workload; ``heads`` optionally overrides H (same seed/recipe)."""
+def workload(name: str, heads: Optional[int] = None, block: int = BLOCK):
+    """Build a named workload; ``heads`` optionally overrides H (same seed/recipe).
+    ``block`` (packed workloads): the same sequences in VSA blocks of 128 or
+    256 slots, the per-sequence top-k the same fraction of the VSA blocks."""
     cfg = dict(WORKLOADS[name])
     if heads is not None:
         cfg["H"] = heads
     if cfg["kind"] == "dense":
+        if block != BLOCK:
+            raise ValueError("dense workloads take the block size at the problem, not here")
         return dense_inputs(cfg["B"], cfg["H"], cfg["S"], cfg["D"], cfg["topk"],
                             cfg["seed"], cfg["gated"], name=name)
+    topk = cfg["topk"]
+    if block != BLOCK:
+        topk = [_frac_topk(_ceil_div(s, block), cfg["topk_frac"]) for s in cfg["seqlens_kv"]]
     return varlen_inputs(cfg["seqlens_q"], cfg["seqlens_kv"], cfg["H"], cfg["D"],
-                         cfg["topk"], cfg["seed"], cfg["gated"], name=name)
+                         topk, cfg["seed"], cfg["gated"], name=name, block=block)

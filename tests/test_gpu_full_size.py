@@ -35,14 +35,17 @@ def test_large_video_dit_shape():
     G.note(f"  out max-abs {mx:.2e} mean-abs {mean:.2e}; sparse rel-rms {rel:.2e}")
 
 
-def test_varlen_many_sequences():
-    """8 packed sequences, Q blocks 32..144, KV = Q + 8 blocks, H=24, gated."""
-    inp = synth.workload("varlen_many")
-    nq_tot = sum(-(-s // 64) for s in inp.seqlens_q)
-    rng = np.random.default_rng(5)
+@pytest.mark.parametrize("block", [64, 128, 256])
+def test_varlen_many_sequences(block):
+    """8 packed sequences, Q blocks 32..144, KV = Q + 8 blocks (of 64 tokens),
+    H=24, gated; also in VSA blocks of 128 and 256 slots with top-k 20 % of
+    those (the benchmark's --block-size runs)."""
+    inp = synth.workload("varlen_many", block=block)
+    nq_tot = sum(-(-s // block) for s in inp.seqlens_q)
+    rng = np.random.default_rng(5 + block)
     picks = rng.choice(inp.heads * nq_tot, N_SAMPLE, replace=False)
     blocks = [(int(p) // nq_tot, int(p) % nq_tot) for p in picks] + [(inp.heads - 1, nq_tot - 1)]
-    G.note(f"case varlen_many: lens={inp.seqlens_q} topk={inp.topk}")
+    G.note(f"case varlen_many block={block}: lens={inp.seqlens_q} topk={inp.topk}")
     gpu = G.run_varlen_stages(inp)
     ref = G.oracle_varlen(inp, blocks=blocks)
     G.assert_tie_free(ref)
