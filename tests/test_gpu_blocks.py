@@ -183,3 +183,32 @@ def test_varlen_large_blocks_equals_per_sequence(block):
         oq += block * nq
         bq += nq
         bkv += nkv
+
+
+def test_varlen_large_blocks_caller_lists():
+    """The packed sparse stage (VSA blocks of 256 slots) on caller-made lists in
+    any order: entries of another sequence, negative and out-of-range entries
+    are skipped; the rest is attention over the listed blocks' valid tokens
+    (their trailing empty 64-token blocks included in the skip)."""
+    import oracle
+    bs, H, D = 256, 2, 128
+    lq, lkv = [300, 200], [600, 130]  # Q VSA blocks 2 + 1, KV VSA blocks 3 + 1 (global 0..2, 3)
+    inp = synth.varlen_inputs(lq, lkv, H, D, [3, 3], seed=6200, gated=False, block=bs)
+    rows = [[2, 3, 0], [-5, 1, 99], [3, 0, 50]]    # per global query block
+    valid = [[2, 0], [1], [0]]                       # local KV blocks that count
+    idx = np.array([rows] * H, dtype=np.int32)      # [H, Nq, max_topk = 3]
+    num = np.full((H, 3), 3, dtype=np.int32)
+    G.note("case packed caller lists, 256-slot blocks")
+    gpu = G.run_varlen_stages(inp, idx_override=(idx, num))
+    out_s = N.f64(gpu["out_s"])
+    owner = [(0, 0), (0, 1), (1, 0)]  # (sequence, local query block) of each global query block
+    q_off = [0, bs * 2]
+    for h in range(H):
+        for g, (s, i) in enumerate(owner):
+            per = inp.per_seq[s]
+            q, k, v = (N.f64(per[x])[h] for x in ("q", "k", "v"))
+            n = oracle.block_sizes(lq[s], bs)[i]
+            want = oracle.sparse_block(q[bs * i:bs * i + n], k, v, oracle.block_sizes(lkv[s], bs), valid[g], bs)
+            lo = q_off[s] + bs * i
+            N.check_sparse(out_s[h, lo:lo + n], want, f"caller list h{h} block {g}")
+            assert (out_s[h, lo + n:lo + bs] == 0).all()
