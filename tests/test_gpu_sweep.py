@@ -92,6 +92,46 @@ def test_forward_graph_replay(block, bshd):
     G.note(f"  {4} replays equal to the eager forward (block {block}, bshd {bshd})")
 
 
+@pytest.mark.parametrize("block", [64, 256])
+def test_varlen_graph_replay(block):
+    """vsa_forward_varlen (packed, VSA blocks of 64 or 256 slots) captured once
+    in a graph on preallocated buffers; between replays new inputs are copied
+    in and the forward runs eagerly on its own buffers; every replay equals the
+    eager result bit for bit, padding slots included."""
+    lq, lkv, H, D, topk = [300, 77, 530], [260, 400, 530], 2, 128, [2, 3, 2]
+
+    def make(seed):
+        return synth.varlen_inputs(lq, lkv, H, D, topk, seed=seed, gated=True, block=block)
+
+    first = make(9550)
+    q, k, v, g = (t.to(G.DEV) for t in (first.q, first.k, first.v, first.gate))
+    meta = vsa.vsa_build_metadata(lq, lkv, topk, device=G.DEV, block_size=block)
+    prob = meta.problem(H, D)
+    ws_g, ws_e = vsa.alloc_workspace(prob, G.DEV), vsa.alloc_workspace(prob, G.DEV)
+    out_g, out_e = torch.empty_like(q), torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # a warm-up call outside the capture
+        vsa.vsa_forward_varlen(q, k, v, meta, g, out=out_g, workspace=ws_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        vsa.vsa_forward_varlen(q, k, v, meta, g, out=out_g, workspace=ws_g)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        nxt = make(9551 + rep)
+        for dst, src in ((q, nxt.q), (k, nxt.k), (v, nxt.v), (g, nxt.gate)):
+            dst.copy_(src.to(G.DEV))
+        vsa.vsa_forward_varlen(q, k, v, meta, g, out=out_e, workspace=ws_e)
+        torch.cuda.synchronize()
+        out_g.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {rep} differs from the eager forward"
+    G.note(f"  4 replays equal to the eager packed forward (block {block})")
+
+
 def varlen_configs(n=8, seed=78):
     rng = np.random.default_rng(seed)
     out = []
