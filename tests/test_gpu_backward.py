@@ -291,3 +291,53 @@ def test_backward_large_shape_sampled_heads():
         assert dl <= LSE_ABS, f"lse: {dl:.3e}"
         for name in ("dq", "dk", "dv", "dgate"):
             check_grad(N.f64(gpu[name][:, sl]), ref[name], name)
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture of the backward
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("block", [64, 256])
+def test_backward_graph_replay(block):
+    """vsa_backward captured once in a graph on preallocated buffers; between
+    replays a new output gradient is copied in and the backward runs eagerly
+    on its own outputs; every replay equals the eager result bit for bit."""
+    B, H, S, D, topk = 1, 2, 64 * 7 + 29, 128, 2
+    inp = synth.dense_inputs(B, H, S, D, topk, seed=2900 + block, gated=True)
+    dev = G.DEV
+    q, k, v, g = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.gate))
+    prob = vsa.dense_problem(B, H, S, S, D, topk, block)
+    cs, isz, ns = vsa.block_shapes(prob)
+    out_c = torch.empty(cs, dtype=torch.float32, device=dev)
+    idx = torch.empty(isz, dtype=torch.int32, device=dev)
+    num = torch.empty(ns, dtype=torch.int32, device=dev)
+    vsa.vsa_coarse_topk(prob, q, k, v, out_c, idx, num, vsa.alloc_workspace(prob, dev))
+    out, out_s = torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty(vsa.lse_shape(prob), dtype=torch.float32, device=dev)
+    vsa.vsa_sparse_attn_combine_train(prob, q, k, v, idx, num, out_c, g, out, out_s, lse)
+    dout = synth.output_grad(q.shape, 2950).to(dev)
+    grads_g = [torch.empty_like(t) for t in (q, k, v, g)]
+    grads_e = [torch.empty_like(t) for t in (q, k, v, g)]
+    ws_g, ws_e = vsa.alloc_backward_workspace(prob, dev), vsa.alloc_backward_workspace(prob, dev)
+    run = lambda gr, ws: vsa.vsa_backward(prob, q, k, v, idx, num, out_c, g, out_s, lse, dout, *gr, ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # a warm-up call outside the capture
+        run(grads_g, ws_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(grads_g, ws_g)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        dout.copy_(synth.output_grad(q.shape, 2951 + rep).to(dev))
+        run(grads_e, ws_e)
+        torch.cuda.synchronize()
+        for t in grads_g:
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b, name in zip(grads_g, grads_e, ("dq", "dk", "dv", "dgate")):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager backward"
+    G.note(f"  4 backward replays equal to the eager backward (block {block})")
