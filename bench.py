@@ -45,10 +45,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="large", choices=["large", "varlen_many", "video", "train"],
+    ap.add_argument("--workload", default="large",
+                    choices=["large", "varlen_many", "video", "train", "pages_bench_49k"],
                     help="large (the default line), varlen_many, video: the large shape as an "
                          "11 x 32 x 44 latent in 4 x 4 x 4 tiles, gathered from and scattered to "
-                         "raster order, or train: the large shape's forward plus backward")
+                         "raster order, train: the large shape's forward plus backward, or "
+                         "pages_bench_49k: B=1 H=16 D=128 S=49152, top-64 of 768 blocks, ungated")
     ap.add_argument("--block-size", type=int, default=64, choices=[64, 128, 256],
                     help="VSA block size for the large workload (128 / 256: top-k about 20%% of the blocks)")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0,
@@ -402,10 +404,12 @@ def main():
         q_tokens = B * H * Sq
         n_qblocks = B * H * nqb
         n_kvblocks = B * H * -(-Skv // block)
-        cfg = {"workload": f"large video-DiT shape B={B} H={H} D={D} S={Sq} ({nqb} blocks of {block}), "
-                           f"top-{inp.topk}, per-token-per-head sigmoid gate",
+        gated = inp.gate is not None
+        what = "large video-DiT shape" if args.workload == "large" else "the pages' benchmark-command shape"
+        cfg = {"workload": f"{what} B={B} H={H} D={D} S={Sq} ({nqb} blocks of {block}), "
+                           f"top-{inp.topk}, " + ("per-token-per-head sigmoid gate" if gated else "ungated"),
                "batch": B, "heads": H, "head_dim": D, "seq_len": Sq, "block": block,
-               "topk": inp.topk, "gate": "token"}
+               "topk": inp.topk, "gate": "token" if gated else "none"}
     else:
         if block != 64:  # the same sequences in VSA blocks of 128 / 256 slots, top-k 20 % of them
             inp = synth.workload(args.workload, block=block)

@@ -170,7 +170,7 @@ int vsa_build_metadata(int32_t num_seqs, const int32_t *seqlens_q, const int32_t
  * full-sequence materialization in VSA coarse/sparse combine", Change):
  * pooled Q/K/V in float64, the float64 block-level score matrix of a chunk of
  * query blocks (the coarse stage runs chunk by chunk so that this matrix
- * stays below max(32 MiB, 1/8 of the bytes of q)) and, for the two forward
+ * stays below max(128 MiB, 1/8 of the bytes of q)) and, for the two forward
  * calls, the float32 coarse output and the routing indices when the caller
  * does not ask for them.  Returns 0 when the problem is invalid.
  */

@@ -170,6 +170,9 @@ WORKLOADS = {
     # 4: the large video-DiT shape, 242 blocks, top-k = ceil(0.20 * 242) = 49, gated
     "large": dict(kind="dense", B=1, H=56, S=15488, D=128, topk=_frac_topk(242, 0.20),
                   gated=True, seed=1004),
+    # the shape of the pages' listed benchmark command (batch 1, 16 heads,
+    # head_dim 128, 49152 query tokens, top-64 of 768 blocks), ungated
+    "pages_bench_49k": dict(kind="dense", B=1, H=16, S=49152, D=128, topk=64, gated=False, seed=1006),
     # 5: eight packed sequences, Q blocks 32..144 step 16, KV = Q + 8 blocks,
     #    top-k = ceil(0.20 * KV blocks), gated
     "varlen_many": dict(kind="varlen", H=24, D=128, gated=True, seed=1005, topk_frac=0.20,

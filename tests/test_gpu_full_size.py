@@ -35,6 +35,28 @@ def test_large_video_dit_shape():
     G.note(f"  out max-abs {mx:.2e} mean-abs {mean:.2e}; sparse rel-rms {rel:.2e}")
 
 
+def test_pages_benchmark_shape():
+    """B=1, H=16, D=128, S=49152 (768 blocks), top-64, ungated: the shape of
+    the pages' listed benchmark command (bench.py --workload pages_bench_49k);
+    its block-level score matrix exceeds the coarse stage's bound, so the
+    coarse stage runs in chunks of query blocks."""
+    inp = synth.workload("pages_bench_49k")
+    B, H, Sq, Skv, D = inp.shape
+    nq = Sq // 64
+    rng = np.random.default_rng(6)
+    picks = rng.choice(H * nq, N_SAMPLE, replace=False)
+    blocks = [(0, int(p) // nq, int(p) % nq) for p in picks] + [(0, H - 1, nq - 1), (0, 0, 0)]
+    G.note(f"case pages bench shape: H={H} S={Sq} topk={inp.topk}, {len(blocks)} sampled blocks")
+    gpu = G.run_dense_stages(inp)
+    ref = G.oracle_dense(inp, blocks=blocks)
+    G.assert_tie_free(ref)
+    G.assert_indices_equal(gpu["q2k_idx"], gpu["q2k_num"], ref)
+    N.check_out_c(N.f64(gpu["out_c"]), ref["out_c"])
+    N.check_sparse(N.f64(gpu["out_s"]), ref["out_s"])
+    mx, mean = N.check_out(N.f64(gpu["out_fused"]), ref["out"], "out (fused combine)")
+    G.note(f"  out max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
 @pytest.mark.parametrize("block", [64, 128, 256])
 def test_varlen_many_sequences(block):
     """8 packed sequences, Q blocks 32..144, KV = Q + 8 blocks (of 64 tokens),
@@ -72,16 +94,16 @@ def test_large_sparse_on_oracle_indices():
 
 
 def test_coarse_in_chunks():
-    """2100 x 2100 query/KV blocks on one head: the float64 score matrix (35 MB)
-    exceeds the coarse stage's workspace bound, so it runs in two chunks of
-    query blocks; every index row, every coarse row and sampled outputs are
-    compared with the oracle."""
-    S = 64 * 2100
-    inp = synth.dense_inputs(1, 1, S, 64, 7, seed=2100, gated=True)
+    """3000 x 3000 query/KV blocks on two heads: the float64 score matrix
+    (144 MB) exceeds the coarse stage's workspace bound (128 MiB), so it runs
+    in two chunks of query blocks; every index row, every coarse row and
+    sampled outputs are compared with the oracle."""
+    S = 64 * 3000
+    inp = synth.dense_inputs(1, 2, S, 64, 7, seed=2100, gated=True)
     nq = S // 64
     rng = np.random.default_rng(7)
-    blocks = [(0, 0, int(i)) for i in rng.choice(nq, 16, replace=False)] + [(0, 0, 1996), (0, 0, 1997),
-                                                                             (0, 0, nq - 1)]
+    blocks = [(0, int(i) % 2, int(i) // 2) for i in rng.choice(2 * nq, 16, replace=False)]
+    blocks += [(0, 0, 2795), (0, 1, 2796), (0, 1, nq - 1)]
     G.note(f"case chunked coarse: S={S} D=64 topk=7, {len(blocks)} sampled blocks")
     gpu = G.run_dense_stages(inp)
     ref = G.oracle_dense(inp, blocks=blocks)

@@ -362,13 +362,15 @@ hipError_t launch_d(const DevProblem& P, const double* qc, const double* kc, con
 }
 
 // Query blocks per chunk: all of them unless the chunk's score matrix would
-// exceed max(32 MiB, 1/8 of the bytes of the bf16 query tensor).
+// exceed max(128 MiB, 1/8 of the bytes of the bf16 query tensor).  Few large
+// chunks keep the products' grids wide (a chunk of a few hundred rows of a
+// 16-head problem leaves half the chip idle in the output product).
 int chunk_rows(const DevProblem& P) {
     const int max_nq = P.packed ? P.max_q : P.nQ;
     const int64_t ld = P.packed ? P.max_kv : P.nKV;
     const int64_t q_bytes = P.packed ? (int64_t)P.H * P.total_q * kBlock * P.D * 2
                                      : (int64_t)P.nseq * P.H * P.Sq * P.D * 2;
-    const int64_t cap = q_bytes / 8 > ((int64_t)32 << 20) ? q_bytes / 8 : ((int64_t)32 << 20);
+    const int64_t cap = q_bytes / 8 > ((int64_t)128 << 20) ? q_bytes / 8 : ((int64_t)128 << 20);
     const int64_t per_row = (int64_t)P.nseq * P.H * ld * 8;
     const int64_t c = cap / (per_row > 0 ? per_row : 1);
     return (int)(c >= max_nq ? max_nq : (c < 1 ? 1 : c));
