@@ -68,6 +68,8 @@ extern "C" {
 typedef uint16_t vsa_bf16; /* bfloat16 bit pattern */
 typedef void *vsa_stream;  /* hipStream_t */
 
+/* tokens per attention tile; VSA blocks (the unit of pooling, routing and
+   out_c) are VSA_BLOCK, 2 VSA_BLOCK or 4 VSA_BLOCK tokens (block_size) */
 #define VSA_BLOCK 64
 
 /* status codes */
@@ -111,7 +113,7 @@ typedef struct vsa_problem {
     int32_t batch;     /* B >= 1 */
     int32_t seqlen_q;  /* Sq >= 1 */
     int32_t seqlen_kv; /* Skv >= 1 */
-    int32_t topk;      /* >= 1, clamped to ceil(Skv/64) */
+    int32_t topk;      /* >= 1, clamped to ceil(Skv/block_size) */
     /* PACKED */
     int32_t num_seqs;        /* >= 1 */
     int32_t total_q_blocks;  /* Nq = cu_blocks_q[num_seqs] */

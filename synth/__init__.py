@@ -15,4 +15,8 @@ from .inputs import (  # noqa: F401
     bf16_to_f64,
     full_gate,
     output_grad,
+    tied_dense_inputs,
+    tied_varlen_inputs,
+    TIED_Q_UNIT,
+    TIED_K_UNIT,
 )

@@ -199,3 +199,86 @@ def workload(name: str, heads: Optional[int] = None, block: int = BLOCK):
         topk = [_frac_topk(_ceil_div(s, block), cfg["topk_frac"]) for s in cfg["seqlens_kv"]]
     return varlen_inputs(cfg["seqlens_q"], cfg["seqlens_kv"], cfg["H"], cfg["D"],
                          topk, cfg["seed"], cfg["gated"], name=name, block=block)
+
+
+# ---------------------------------------------------------------------------
+# Inputs with exact ties among the block-level scores.
+#
+# Every value is a small integer (uniform in {-2, ..., 2}) times a power of
+# two (1/4 for queries, 1 for keys, 1/8 for values), which bf16 holds
+# exactly.  KV blocks (VSA blocks of ``block`` tokens) are copies of a few
+# seeded integer patterns, and some are all zero, so that many KV blocks of a
+# sequence have bitwise-equal contents: every query block then sees exactly
+# equal scores for them, and a top-k boundary inside such a group has several
+# correct answers unless a tie rule decides.  With whole blocks (or partial
+# blocks of a power-of-two size) the block means are multiples of a power of
+# two and every dot product of means is exact in float64 in any summation
+# order.  Only layout and random draws happen here.
+# ---------------------------------------------------------------------------
+
+TIED_Q_UNIT, TIED_K_UNIT, TIED_V_UNIT = 0.25, 1.0, 0.125
+
+
+def _int_values(gen: torch.Generator, shape, unit: float = 1.0) -> torch.Tensor:
+    return (torch.randint(-2, 3, tuple(shape), generator=gen).to(torch.float32) * unit).to(torch.bfloat16)
+
+
+def _tied_kv(gen: torch.Generator, H: int, S_kv: int, D: int, block: int, n_patterns: int,
+             zero_frac: float) -> torch.Tensor:
+    """[H, S_kv, D]: VSA block j of head h is pattern[h, c(h, j)] or zero."""
+    nb = _ceil_div(S_kv, block)
+    pats = _int_values(gen, (H, n_patterns, block, D), TIED_K_UNIT)
+    choice = torch.randint(0, n_patterns, (H, nb), generator=gen)
+    zero = torch.rand(H, nb, generator=gen) < zero_frac
+    out = torch.zeros(H, nb * block, D, dtype=torch.bfloat16)
+    for h in range(H):
+        for j in range(nb):
+            if not bool(zero[h, j]):
+                out[h, j * block:(j + 1) * block] = pats[h, int(choice[h, j])]
+    return out[:, :S_kv].contiguous()
+
+
+def tied_dense_inputs(B: int, H: int, S: int, D: int, topk: int, seed: int, gated: bool = False,
+                      S_kv: Optional[int] = None, block: int = BLOCK, n_patterns: int = 3,
+                      zero_frac: float = 0.2, name: str = "tied") -> DenseInputs:
+    """Dense ``[B, H, S, D]`` inputs whose KV blocks repeat (see above).  Keys
+    and values share the block pattern choice, so equal key blocks also carry
+    equal values."""
+    S_kv = S if S_kv is None else S_kv
+    gen = torch.Generator().manual_seed(seed)
+    q = _int_values(gen, (B, H, S, D), TIED_Q_UNIT)
+    k = torch.stack([_tied_kv(gen, H, S_kv, D, block, n_patterns, zero_frac) for _ in range(B)])
+    v = _int_values(gen, (B, H, S_kv, D), TIED_V_UNIT)
+    gate = _bf16_gate(gen, (B, H, S)) if gated else None
+    return DenseInputs(q, k, v, gate, topk, name)
+
+
+def tied_varlen_inputs(seqlens_q: List[int], seqlens_kv: Optional[List[int]], H: int, D: int,
+                       topk: List[int], seed: int, gated: bool = False, block: int = BLOCK,
+                       n_patterns: int = 3, zero_frac: float = 0.2, name: str = "tied_varlen") -> VarlenInputs:
+    """Packed inputs (block-aligned, zero padding) whose sequences' KV blocks
+    repeat as in ``tied_dense_inputs``."""
+    seqlens_kv = list(seqlens_q) if seqlens_kv is None else list(seqlens_kv)
+    nq = [_ceil_div(s, block) for s in seqlens_q]
+    nkv = [_ceil_div(s, block) for s in seqlens_kv]
+    q = torch.zeros(H, block * sum(nq), D, dtype=torch.bfloat16)
+    k = torch.zeros(H, block * sum(nkv), D, dtype=torch.bfloat16)
+    v = torch.zeros_like(k)
+    gate = torch.zeros(H, block * sum(nq), dtype=torch.bfloat16) if gated else None
+    gen = torch.Generator().manual_seed(seed)
+    per_seq = []
+    oq = okv = 0
+    for s, (sq, skv) in enumerate(zip(seqlens_q, seqlens_kv)):
+        qs = _int_values(gen, (H, sq, D), TIED_Q_UNIT)
+        ks = _tied_kv(gen, H, skv, D, block, n_patterns, zero_frac)
+        vs = _int_values(gen, (H, skv, D), TIED_V_UNIT)
+        gs = _bf16_gate(gen, (H, sq)) if gated else None
+        q[:, oq:oq + sq] = qs
+        k[:, okv:okv + skv] = ks
+        v[:, okv:okv + skv] = vs
+        if gated:
+            gate[:, oq:oq + sq] = gs
+        per_seq.append({"q": qs, "k": ks, "v": vs, "gate": gs})
+        oq += block * nq[s]
+        okv += block * nkv[s]
+    return VarlenInputs(q, k, v, gate, list(seqlens_q), seqlens_kv, list(topk), name, per_seq, block)

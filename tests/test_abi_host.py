@@ -433,6 +433,19 @@ def test_tile_metadata_is_packed_layout(lib, grid, tile):
     assert m.topk.tolist() == [min(7, n)] * 3 and m.sizes.max_topk == min(7, n)
 
 
+def test_video_forward_reuses_device_tile_metadata(lib):
+    """The video forward keeps one device copy of the tile metadata per
+    (videos, grid, top-k, tile, device): a second forward of the same shape
+    builds and copies nothing."""
+    import video_sparse_attention_amd.binding as BD
+    a = BD._cached_tile_metadata(2, (5, 8, 8), 3, (4, 4, 4), "cpu")
+    b = BD._cached_tile_metadata(2, (5, 8, 8), 3, (4, 4, 4), "cpu")
+    c = BD._cached_tile_metadata(2, (5, 8, 8), 4, (4, 4, 4), "cpu")
+    assert a is b and c is not a
+    assert a.cu_blocks_q.data_ptr() == b.cu_blocks_q.data_ptr()
+    assert c.topk.tolist() == [4, 4] and a.topk.tolist() == [3, 3]
+
+
 def test_tile_errors(lib):
     nt = ctypes.c_int32(0)
     E = _abi

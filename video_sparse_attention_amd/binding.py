@@ -601,6 +601,22 @@ def tile_scatter(y: torch.Tensor, grid, batch: int, tile=DEFAULT_TILE,
     return out
 
 
+# Device copies of the tile metadata, one per (videos, grid, top-k, tile,
+# device): built and copied to the device on the first forward of a shape,
+# so later forwards of that shape issue no host -> device copy.
+_TILE_META_CACHE: dict = {}
+
+
+def _cached_tile_metadata(num_videos: int, grid, topk: int, tile, device) -> VarlenMeta:
+    key = (int(num_videos), tuple(int(x) for x in grid), int(topk), tuple(int(x) for x in tile),
+           torch.device(device))
+    meta = _TILE_META_CACHE.get(key)
+    if meta is None:
+        meta = vsa_build_tile_metadata(num_videos, grid, topk, tile, device=device)
+        _TILE_META_CACHE[key] = meta
+    return meta
+
+
 def vsa_forward_video(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid, topk: int,
                       gate: Optional[torch.Tensor] = None, tile=DEFAULT_TILE, *, return_aux: bool = False):
     """VSA forward of ``B`` videos of one ``grid = (T, H, W)`` given in raster
@@ -616,7 +632,7 @@ def vsa_forward_video(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid, t
     for name, t in (("k", k), ("v", v)):
         if tuple(t.shape) != tuple(q.shape):
             raise ValueError(f"{name} must have the shape of q {tuple(q.shape)}, got {tuple(t.shape)}")
-    meta = vsa_build_tile_metadata(B, grid, topk, tile, device=q.device)
+    meta = _cached_tile_metadata(B, grid, topk, tile, q.device)
     gq, gk, gv = (tile_gather(t, grid, tile) for t in (q, k, v))
     gg = None if gate is None else tile_gather(gate, grid, tile)
     res = vsa_forward_varlen(gq, gk, gv, meta, gg, return_aux=return_aux)
