@@ -273,6 +273,30 @@ int vsa_forward(const vsa_bf16 *q, const vsa_bf16 *k, const vsa_bf16 *v, const v
                 void *workspace, size_t workspace_bytes, vsa_stream stream);
 
 /*
+ * vsa_forward_noalloc - vsa_forward without a caller-provided workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The workspace is a
+ * file-scope device array of vsa_noalloc_scratch_bytes() bytes (96 MiB),
+ * which every GPU the library runs on holds from the library's first use on
+ * it until the process ends; its device address is taken once per device, on
+ * the first call with that device current.  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine).
+ *
+ * Arguments, outputs and errors as for vsa_forward (DENSE [B,H,S,D] tensors);
+ * VSA_ERR_WORKSPACE when the problem's vsa_workspace_size() exceeds the array
+ * (checked before any device call).  All calls on one GPU share that GPU's
+ * array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller.  Nothing in the array
+ * needs clearing between calls.
+ */
+size_t vsa_noalloc_scratch_bytes(void);
+int vsa_forward_noalloc(const vsa_bf16 *q, const vsa_bf16 *k, const vsa_bf16 *v, const vsa_bf16 *gate,
+                        int32_t gate_mode, const int64_t *gate_strides, vsa_bf16 *out, int32_t *q2k_idx,
+                        int32_t *q2k_num, float *out_c, int32_t batch, int32_t heads, int32_t seqlen_q,
+                        int32_t seqlen_kv, int32_t head_dim, int32_t block_size, int32_t topk,
+                        vsa_stream stream);
+
+/*
  * vsa_forward_bshd - vsa_forward for [B, S, H, D] tensors (BSHD layout):
  * q [B,Sq,H,D], k/v [B,Skv,H,D], out [B,Sq,H,D]; everything else, including
  * block_size 64, 128 or 256, as vsa_forward.  ("[chore] release

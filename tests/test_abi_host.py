@@ -433,6 +433,23 @@ def test_tile_metadata_is_packed_layout(lib, grid, tile):
     assert m.topk.tolist() == [min(7, n)] * 3 and m.sizes.max_topk == min(7, n)
 
 
+def test_noalloc_rejects_problems_past_its_scratch(lib):
+    """vsa_forward_noalloc checks the problem's workspace against its fixed
+    per-device scratch array before any device call (so this runs without a
+    GPU); NULL tensors never get that far."""
+    assert lib.vsa_noalloc_scratch_bytes() == 96 << 20
+    E = _abi
+    # 56 heads x 4096 blocks: far more than 96 MiB of block-level workspace
+    rc = lib.vsa_forward_noalloc(None, None, None, None, 0, None, None, None, None, None,
+                                 1, 56, 64 * 4096, 64 * 4096, 128, 64, 49, None)
+    assert rc == E.VSA_ERR_WORKSPACE
+    assert "scratch" in lib.vsa_last_error().decode()
+    # invalid problems are rejected as by vsa_forward
+    rc = lib.vsa_forward_noalloc(None, None, None, None, 0, None, None, None, None, None,
+                                 1, 2, 64, 64, 128, 32, 1, None)
+    assert rc == E.VSA_ERR_UNSUPPORTED
+
+
 def test_video_forward_reuses_device_tile_metadata(lib):
     """The video forward keeps one device copy of the tile metadata per
     (videos, grid, top-k, tile, device): a second forward of the same shape

@@ -25,6 +25,8 @@ from .binding import (  # noqa: E402,F401
     vsa_coarse_topk,
     vsa_combine,
     vsa_forward,
+    vsa_forward_noalloc,
+    vsa_noalloc_scratch_bytes,
     vsa_forward_varlen,
     vsa_sparse_attn_combine,
     vsa_sparse_attn_from_indices,
@@ -42,7 +44,7 @@ __all__ = [
     "BLOCK", "VarlenMeta", "VsaError", "alloc_workspace", "block_shapes", "dense_problem",
     "token_shapes", "DEFAULT_TILE", "tile_block", "tile_gather", "tile_partition", "tile_scatter",
     "vsa_build_tile_metadata", "vsa_forward_video", "vsa_build_metadata", "vsa_coarse_topk", "vsa_combine", "vsa_forward",
-    "vsa_forward_varlen", "vsa_sparse_attn_combine", "vsa_sparse_attn_from_indices", "vsa_workspace_size",
+    "vsa_forward_noalloc", "vsa_noalloc_scratch_bytes", "vsa_forward_varlen", "vsa_sparse_attn_combine", "vsa_sparse_attn_from_indices", "vsa_workspace_size",
     "alloc_backward_workspace", "lse_shape", "video_sparse_attn", "video_sparse_attn_varlen", "vsa_backward",
     "vsa_backward_workspace_size", "vsa_sparse_attn_combine_train",
 ]

@@ -65,6 +65,9 @@ SIGNATURES = {
                            vp, vp, vp, vp, vp, sz, vp]),
     "vsa_forward": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
                           i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]),
+    "vsa_forward_noalloc": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
+                                  i32, i32, i32, i32, i32, i32, i32, vp]),
+    "vsa_noalloc_scratch_bytes": (sz, []),
     "vsa_forward_bshd": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
                                i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]),
     "vsa_forward_varlen": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,

@@ -461,6 +461,42 @@ def vsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int,
     return (out, *aux) if return_aux else out
 
 
+def vsa_forward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int,
+                        gate: Optional[torch.Tensor] = None, *, block_size: int = BLOCK,
+                        out: Optional[torch.Tensor] = None, return_aux: bool = False):
+    """vsa_forward on dense ``[B, H, S, D]`` tensors through the entry point
+    that allocates nothing (vsa_forward_noalloc): its workspace is the
+    library's per-device scratch array (vsa_noalloc_scratch_bytes), shared by
+    every call on that GPU.  Outputs as for ``vsa_forward`` (``out`` and the
+    aux outputs are the caller's tensors)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, S, D]")
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2] if k.dim() == 4 else -1
+    problem = dense_problem(B, H, Sq, Skv, D, topk, block_size)
+    _check_qkv(problem, q, k, v)
+    mode, st = _gate_args(gate, *_gate_shapes(problem))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, q.shape)
+    aux = None
+    if return_aux:
+        cs, isz, ns = block_shapes(problem)
+        aux = (torch.empty(cs, dtype=torch.float32, device=q.device),
+               torch.empty(isz, dtype=torch.int32, device=q.device),
+               torch.empty(ns, dtype=torch.int32, device=q.device))
+    oc, idx, num = aux if aux else (None, None, None)
+    _abi.check(_abi.load().vsa_forward_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), mode, st, _ptr(out), _ptr(idx), _ptr(num),
+        _ptr(oc), B, H, Sq, Skv, D, block_size, topk, _stream(q.device)), "vsa_forward_noalloc")
+    return (out, *aux) if return_aux else out
+
+
+def vsa_noalloc_scratch_bytes() -> int:
+    """Bytes of the per-device scratch array of vsa_forward_noalloc."""
+    return int(_abi.load().vsa_noalloc_scratch_bytes())
+
+
 def vsa_forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, meta: VarlenMeta,
                        gate: Optional[torch.Tensor] = None, *, out: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None, return_aux: bool = False):

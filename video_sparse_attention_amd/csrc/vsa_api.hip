@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "vsa_internal.hpp"
@@ -311,6 +312,43 @@ int tile_copy(const vsa_bf16* src, vsa_bf16* dst, int32_t batch, int32_t heads, 
     return rc ? rc : ok();
 }
 
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// vsa_forward_noalloc: vsa_forward with its workspace in a file-scope device
+// array instead of a caller-provided buffer, for callers that cannot allocate
+// device memory (HIP graph capture, tight serving loops).  Every GPU the
+// library runs on holds its own copy of the array (kNoAllocScratchBytes) from
+// the module's load until the process ends.  In host code `scratch` names a
+// host-side stand-in, not a device address: the array's device address is
+// taken once per device with hipGetSymbolAddress, with that device current,
+// and only that address is handed to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = (size_t)96 << 20;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};  // device address of `scratch` per device, set once
+
+// The current device's address of `scratch` (taken on the first call on that
+// device).  Returns VSA_OK or an error code with the detail set.
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(VSA_ERR_HIP, "hipGetDevice failed");
+    if (dev >= kMaxDevices) return fail(VSA_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(VSA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return VSA_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -642,6 +680,39 @@ int vsa_forward(const vsa_bf16* q, const vsa_bf16* k, const vsa_bf16* v, const v
     pr.topk = topk;
     return forward_common(&pr, q, k, v, gate, gate_mode, gate_strides, out, q2k_idx, q2k_num, out_c, workspace,
                           workspace_bytes, stream);
+}
+
+size_t vsa_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+int vsa_forward_noalloc(const vsa_bf16* q, const vsa_bf16* k, const vsa_bf16* v, const vsa_bf16* gate,
+                        int32_t gate_mode, const int64_t* gate_strides, vsa_bf16* out, int32_t* q2k_idx,
+                        int32_t* q2k_num, float* out_c, int32_t batch, int32_t heads, int32_t seqlen_q,
+                        int32_t seqlen_kv, int32_t head_dim, int32_t block_size, int32_t topk,
+                        vsa_stream stream) {
+    vsa_problem pr{};
+    pr.layout = VSA_LAYOUT_DENSE;
+    pr.heads = heads;
+    pr.head_dim = head_dim;
+    pr.block_size = block_size;
+    pr.batch = batch;
+    pr.seqlen_q = seqlen_q;
+    pr.seqlen_kv = seqlen_kv;
+    pr.topk = topk;
+    // the size check comes first: a problem past the array is rejected
+    // before any device is touched
+    vsa::DevProblem P;
+    int rc = make_problem(&pr, &P);
+    if (rc) return rc;
+    const size_t need = plan_workspace(P, nullptr).total_bytes;
+    if (need > kNoAllocScratchBytes)
+        return fail(VSA_ERR_WORKSPACE, "problem needs %zu bytes of scratch, vsa_forward_noalloc has %zu", need,
+                    kNoAllocScratchBytes);
+    void* ws = nullptr;
+    if ((rc = scratch_address(&ws))) return rc;
+    // the forward writes every scratch value before reading it (pooled
+    // blocks, scores, routing), so nothing needs clearing between calls
+    return forward_common(&pr, q, k, v, gate, gate_mode, gate_strides, out, q2k_idx, q2k_num, out_c, ws,
+                          kNoAllocScratchBytes, stream);
 }
 
 int vsa_forward_bshd(const vsa_bf16* q, const vsa_bf16* k, const vsa_bf16* v, const vsa_bf16* gate,
