@@ -58,6 +58,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--oracle-stages", action="store_true",
                     help="time the fp64 oracle per stage on every workload (host only) and exit")
+    ap.add_argument("--combine-only", choices=["read", "write", "stream"], default=None,
+                    help="time only the stand-alone combine kernel on the large workload, 40 launches, "
+                         "each after a flush of L2 and MALL that reads (or writes) a 1 GiB buffer, or "
+                         "(stream) back to back over four output buffers in turn, and exit (one mode per "
+                         "process, so that a kernel trace of the run holds that mode's launches only)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy kernel (reference for the HBM "
                          "byte counters) three times and exit")
@@ -75,6 +80,64 @@ def copy_calibration():
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read_per_launch": 4 * n,
                       "copy_calibration_bytes_written_per_launch": 4 * n}), flush=True)
+
+
+def combine_only(mode: str, launches: int = 40):
+    """The stand-alone combine on the large workload, each launch after a
+    flush of L2 and MALL: reading a 1 GiB buffer (no dirty line is left) or
+    writing it (the MALL's write-back of the flush buffer then lands in the
+    combine's window); or back to back over four outputs in turn ("stream").
+    Prints the median duration and HBM rate."""
+    import torch
+
+    import synth
+    import video_sparse_attention_amd as vsa
+    dev = torch.device("cuda:0")
+    inp = synth.workload("large")
+    B, H, Sq, Skv, D = inp.shape
+    prob = vsa.dense_problem(B, H, Sq, Skv, D, inp.topk)
+    q, k, v, gate = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.gate))
+    cs, isz, ns = vsa.block_shapes(prob)
+    out_c = torch.empty(cs, dtype=torch.float32, device=dev)
+    idx = torch.empty(isz, dtype=torch.int32, device=dev)
+    num = torch.empty(ns, dtype=torch.int32, device=dev)
+    ws = vsa.alloc_workspace(prob, dev)
+    vsa.vsa_coarse_topk(prob, q, k, v, out_c, idx, num, ws)
+    out = torch.empty_like(q)
+    vsa.vsa_sparse_attn_from_indices(prob, q, k, v, idx, num, out)
+    times = []
+    if mode == "stream":
+        # four 222 MB outputs in turn (888 MB, above the 256 MB MALL): in the
+        # steady state every launch's reads miss the caches and its writes
+        # evict the dirty lines of earlier launches, so the write-backs fall
+        # inside the launches
+        outs = [out] + [out.clone() for _ in range(3)]
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(launches)]
+        for i in range(launches):
+            evs[i][0].record()
+            vsa.vsa_combine(prob, out_c, gate, outs[i % 4])
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        times = [a.elapsed_time(b) for a, b in evs[8:]]
+    else:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        for _ in range(launches):
+            if mode == "read":
+                flush.sum()
+            else:
+                flush.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            vsa.vsa_combine(prob, out_c, gate, out)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+    med = sorted(times)[len(times) // 2]
+    nbytes = 2 * 2 * B * H * Sq * D + 2 * B * H * Sq + 4 * B * H * (-(-Sq // 64)) * D
+    print(json.dumps({"combine_flush": mode, "launches": launches, "median_ms": round(med, 4),
+                      "bytes": nbytes, "GBps": round(nbytes / (med * 1e-3) / 1e9, 1),
+                      "frac_hbm": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}), flush=True)
 
 
 def kernel_hash(path=SPARSE_SRC) -> str:
@@ -370,6 +433,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.combine_only:
+        combine_only(args.combine_only)
         return
     if args.oracle_stages:
         oracle_stages(args.cpu_budget_s)

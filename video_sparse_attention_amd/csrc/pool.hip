@@ -4,8 +4,10 @@
 //
 // HBM-bound streaming kernel.  Thread (block, slice s, c) owns the 16-byte
 // chunk c (8 consecutive d) of tokens s, s + 4, s + 8, ... of one VSA block
-// (64 * ratio tokens, ratio 1, 2 or 4) and walks them with independent 16-byte loads (8 in flight
-// per thread), accumulating 8 sums in float64 registers; the 4 slices of a
+// (64 * ratio tokens, ratio 1, 2 or 4) and walks them with independent,
+// non-temporal 16-byte loads (16 in flight per thread: a whole 64-token block
+// in one round; both measured 7 % faster than 8 cached loads), accumulating 8
+// sums in float64 registers; the 4 slices of a
 // chunk then add their sums with lane shuffles (no LDS).  The 4 CH threads of
 // a block (CH = D/8) read 4 consecutive token rows per load instruction, 4
 // contiguous 16*CH-byte segments, so every instruction of a wave is fully
@@ -20,7 +22,8 @@ namespace vsa {
 namespace {
 
 constexpr int kPoolThreads = 256;
-constexpr int kUnroll = 8;
+constexpr int kUnroll = 16;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kSlices = 4;  // threads sharing one (block, chunk)
 
 __device__ __forceinline__ double bf16_lo(uint32_t w) { return (double)__uint_as_float(w << 16); }
@@ -75,7 +78,9 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(DevProblem P, const 
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int t = t0 + kSlices * u;
-            w[u] = t < size ? *reinterpret_cast<const uint4*>(src + (int64_t)t * st) : make_uint4(0, 0, 0, 0);
+            u32x4 x = {0, 0, 0, 0};
+            if (t < size) x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)t * st));
+            w[u] = make_uint4(x[0], x[1], x[2], x[3]);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
