@@ -4,7 +4,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libvsa.so")
+# VSA_LIBRARY names another build of the same library (the host-sanitizer
+# build of the CPU tests); by default the in-tree libvsa.so is loaded.
+LIB_PATH = os.environ.get("VSA_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "lib", "libvsa.so")
 
 VSA_OK = 0
 VSA_ERR_NULL = -1

@@ -52,13 +52,18 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
+def build(verbose: bool = False, extra_flags=None, build_dir: str = BUILD, lib_path: str = LIB,
+          link_cmd=None) -> str:
+    """Compile every HIP source with ``HIPCC_FLAGS + extra_flags`` into
+    ``build_dir`` and link ``lib_path``.  ``link_cmd`` (a list ending where the
+    object files go) replaces hipcc's own shared-library link, e.g. for an
+    instrumented host build that links a sanitizer runtime."""
     hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
-    os.makedirs(LIBDIR, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
+    os.makedirs(os.path.dirname(lib_path), exist_ok=True)
     flags = HIPCC_FLAGS + list(extra_flags or [])
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in srcs]
+    objs = [os.path.join(build_dir, os.path.basename(s) + ".o") for s in srcs]
 
     def compile_one(pair):
         src, obj = pair
@@ -66,9 +71,12 @@ def build(verbose: bool = False, extra_flags=None) -> str:
 
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         logs = list(ex.map(compile_one, zip(srcs, objs)))
-    tmp = LIB + ".tmp"
-    logs.append(_run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]))
-    os.replace(tmp, LIB)
+    tmp = lib_path + ".tmp"
+    if link_cmd is None:
+        logs.append(_run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]))
+    else:
+        logs.append(_run([*link_cmd, "-o", tmp, *objs]))
+    os.replace(tmp, lib_path)
     if verbose:
         for l in logs:
             if l.strip():
