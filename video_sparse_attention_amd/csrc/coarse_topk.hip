@@ -150,32 +150,43 @@ __global__ __launch_bounds__(kThreads) void coarse_select_kernel(DevProblem P, d
     const int64_t qb = sv.qblk_base + i;
     double* row = sc + srow * ld;
     int* orow = idx_out + qb * P.idx_row;
-    const int nkv = min(sv.nkv, 64 * KPL);
-    const int k = sv.k;
+    // wave-uniform, so the bisection state below lives in scalar registers
+    const int nkv = __builtin_amdgcn_readfirstlane(min(sv.nkv, 64 * KPL));
+    const int k = __builtin_amdgcn_readfirstlane(sv.k);  // 1 <= k <= nkv
 
-    uint64_t key[KPL];  // 0 marks "no block": below the key of any double
+    // Key 0 marks "no block".  Every valid key is non-zero (a double maps to
+    // 0 only from the all-ones NaN pattern), so once the high half of the
+    // threshold is known to be >= 1 - it is, since k <= nkv - the comparisons
+    // below never count, select or tie-break an empty slot, and need no
+    // bounds test.
+    uint64_t key[KPL];
 #pragma unroll
     for (int e = 0; e < KPL; ++e) {
         const int j = 64 * e + lane;
         key[e] = j < nkv ? order_key(row[j]) : 0ull;
     }
+    // lane groups past nkv hold only zeros; the wide variants skip them (the
+    // narrowest one compares them, which costs less than the branches)
+    const int groups = (nkv + 63) / 64;
+    auto live = [&](int e) { return KPL == 4 || e < groups; };
     // T = the k-th largest key.  First the k-th largest of the high 32 bits
     // (Th) by bitwise bisection on 32-bit compares; the low 32 bits only need
     // a second bisection when the candidates sharing Th are more than the
     // number still to be chosen.
     uint32_t Th = 0;
+#pragma unroll 8
     for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = Th | (1u << bit);
         int cnt = 0;
 #pragma unroll
         for (int e = 0; e < KPL; ++e)
-            if (64 * e < nkv) cnt += __popcll(__ballot((uint32_t)(key[e] >> 32) >= cand));
-        if (cnt >= k) Th = cand;
+            if (live(e)) cnt += __popcll(__ballot((uint32_t)(key[e] >> 32) >= cand));
+        Th = cnt >= k ? cand : Th;
     }
     int gt_hi = 0, eq_hi = 0;
 #pragma unroll
     for (int e = 0; e < KPL; ++e)
-        if (64 * e < nkv) {
+        if (live(e)) {
             const uint32_t hi = (uint32_t)(key[e] >> 32);
             gt_hi += __popcll(__ballot(hi > Th));
             eq_hi += __popcll(__ballot(hi == Th));
@@ -188,9 +199,9 @@ __global__ __launch_bounds__(kThreads) void coarse_select_kernel(DevProblem P, d
             int cnt = 0;
 #pragma unroll
             for (int e = 0; e < KPL; ++e)
-                if (64 * e < nkv)
-                    cnt += __popcll(__ballot((uint32_t)(key[e] >> 32) == Th && (uint32_t)key[e] >= cand));
-            if (cnt >= need_hi) Tl = cand;
+                if (live(e))
+                    cnt += __popcll(__ballot(((uint32_t)(key[e] >> 32) == Th) & ((uint32_t)key[e] >= cand)));
+            Tl = cnt >= need_hi ? cand : Tl;
         }
     }
     // (when every candidate is chosen, T = Th:0 selects all of them below)
@@ -198,12 +209,12 @@ __global__ __launch_bounds__(kThreads) void coarse_select_kernel(DevProblem P, d
     int n_gt = 0;
 #pragma unroll
     for (int e = 0; e < KPL; ++e)
-        if (64 * e < nkv) n_gt += __popcll(__ballot(key[e] > T));
+        if (live(e)) n_gt += __popcll(__ballot(key[e] > T));
     const int need_eq = k - n_gt;
     int n_sel = 0, n_eq = 0;
 #pragma unroll
     for (int e = 0; e < KPL; ++e) {
-        if (64 * e >= nkv) break;
+        if (e >= groups) break;
         const int j = 64 * e + lane;
         const bool eq = key[e] == T;
         const uint64_t eq_mask = __ballot(eq);
