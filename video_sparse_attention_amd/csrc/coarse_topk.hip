@@ -39,6 +39,13 @@ __device__ __forceinline__ uint64_t order_key(double s) {
     return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
+// Column position inside a 64-wide LDS row for the 4-column register tiles
+// below: thread tx reads its columns 4 tx, 4 tx + 1 at 2 tx and 4 tx + 2,
+// 4 tx + 3 at 32 + 2 tx, so the 16 threads of a row of the thread grid read
+// 256 contiguous bytes per double2 access (no bank conflicts); column pairs
+// 2m, 2m + 1 stay adjacent.
+__device__ __forceinline__ int quad_col(int c) { return ((c >> 1) & 1) * 32 + (c >> 2) * 2 + (c & 1); }
+
 __device__ __forceinline__ int prefix_popc(uint64_t mask) {
     const int l = __lane_id();
     const uint64_t below = l == 0 ? 0ull : (mask & ((~0ull) >> (64 - l)));
@@ -100,15 +107,16 @@ __global__ __launch_bounds__(kThreads) void coarse_scores_kernel(DevProblem P, c
     for (int d0 = 0; d0 < D; d0 += kSlice) {
         __syncthreads();  // previous slice fully consumed
         qt[sd + 0][sr] = qa.x; qt[sd + 1][sr] = qa.y; qt[sd + 2][sr] = qb.x; qt[sd + 3][sr] = qb.y;
-        kt[sd + 0][sr] = ka.x; kt[sd + 1][sr] = ka.y; kt[sd + 2][sr] = kb.x; kt[sd + 3][sr] = kb.y;
+        const int kcol = quad_col(sr);
+        kt[sd + 0][kcol] = ka.x; kt[sd + 1][kcol] = ka.y; kt[sd + 2][kcol] = kb.x; kt[sd + 3][kcol] = kb.y;
         __syncthreads();
         if (d0 + kSlice < D) fetch(d0 + kSlice);
 #pragma unroll
         for (int d = 0; d < kSlice; ++d) {
             const double2 q01 = *reinterpret_cast<const double2*>(&qt[d][4 * ty]);
             const double2 q23 = *reinterpret_cast<const double2*>(&qt[d][4 * ty + 2]);
-            const double2 k01 = *reinterpret_cast<const double2*>(&kt[d][4 * tx]);
-            const double2 k23 = *reinterpret_cast<const double2*>(&kt[d][4 * tx + 2]);
+            const double2 k01 = *reinterpret_cast<const double2*>(&kt[d][2 * tx]);
+            const double2 k23 = *reinterpret_cast<const double2*>(&kt[d][32 + 2 * tx]);
             const double qv[4] = {q01.x, q01.y, q23.x, q23.y};
             const double kv[4] = {k01.x, k01.y, k23.x, k23.y};
 #pragma unroll
@@ -304,7 +312,8 @@ __global__ __launch_bounds__(kThreads) void coarse_out_kernel(DevProblem P, cons
 #pragma unroll
         for (int p = 0; p < DC / 32; ++p) {
             const int e = tid + kThreads * p;
-            *reinterpret_cast<double2*>(&vs[e / (DC / 2)][2 * (e % (DC / 2))]) = vv[p];
+            const int col = 2 * (e % (DC / 2));
+            *reinterpret_cast<double2*>(&vs[e / (DC / 2)][CPT == 4 ? quad_col(col) : col]) = vv[p];
         }
         __syncthreads();
         if (j0 + kSlice < nkv) fetch(j0 + kSlice);
@@ -316,7 +325,8 @@ __global__ __launch_bounds__(kThreads) void coarse_out_kernel(DevProblem P, cons
             double v[CPT];
 #pragma unroll
             for (int c = 0; c < CPT; c += 2) {
-                const double2 t2 = *reinterpret_cast<const double2*>(&vs[jj][CPT * tx + c]);
+                const int col = CPT == 4 ? quad_col(CPT * tx + c) : CPT * tx + c;
+                const double2 t2 = *reinterpret_cast<const double2*>(&vs[jj][col]);
                 v[c] = t2.x;
                 v[c + 1] = t2.y;
             }
