@@ -23,6 +23,8 @@
 //   3. output: out_c = W Vc / sum(W) per row, 64 rows x D columns per
 //      workgroup, 16-row slices of W and Vc staged in LDS, rounded once to
 //      float32.
+#include "attn_layout.hpp"
+#include "pool_common.hpp"
 #include "vsa_internal.hpp"
 
 namespace vsa {
@@ -64,17 +66,36 @@ __device__ __forceinline__ double wave_sum(double x) {
 // ---------------------------------------------------------------------------
 // 1. block-level scores
 // ---------------------------------------------------------------------------
-template <int D>
+// One-dimensional grid: workgroups [0, n_tiles) are the score tiles over
+// (tile, head, sequence), tiles fastest, renumbered so that the tiles of a
+// head run on one XCD; with POOLV, workgroups from n_tiles on pool V (full
+// problem PP, grid columns x heads x batch items) into vc.
+static_assert(kThreads == pool::kPoolThreads, "the pool body runs on a score kernel's workgroup");
+template <int D, bool POOLV>
 __global__ __launch_bounds__(kThreads) void coarse_scores_kernel(DevProblem P, const double* __restrict__ qc,
                                                                  const double* __restrict__ kc,
                                                                  double* __restrict__ sc, int ld,
-                                                                 int tiles_kv, int c0, int C) {
+                                                                 int tiles_kv, int c0, int C, int n_tiles,
+                                                                 DevProblem PP, const uint16_t* __restrict__ v,
+                                                                 double* __restrict__ vc) {
     __shared__ __attribute__((aligned(16))) double qt[kSlice][kTile + kPad];  // [d][row]
     __shared__ __attribute__((aligned(16))) double kt[kSlice][kTile + kPad];  // [d][col]
-    const int s = blockIdx.z, h = blockIdx.y;
+    if constexpr (POOLV) {
+        if ((int)blockIdx.x >= n_tiles) {
+            const int g = blockIdx.x - n_tiles;
+            const int cols = pool::pool_columns(PP);
+            pool::pool_group<D>(PP, nullptr, nullptr, v, nullptr, nullptr, vc, 2, g / cols / PP.H, (g / cols) % PP.H,
+                                g % cols);
+            return;
+        }
+    }
+    const int per_head = ((C + kTile - 1) / kTile) * tiles_kv;
+    const int lin = xcd_remap(blockIdx.x, n_tiles);
+    const int tile = lin % per_head;
+    const int h = (lin / per_head) % P.H, s = lin / per_head / P.H;
     const SeqView sv = seq_view(P, s, h);
-    const int i0 = c0 + (blockIdx.x / tiles_kv) * kTile;  // local query block of tile row 0
-    const int j0 = (blockIdx.x % tiles_kv) * kTile;
+    const int i0 = c0 + (tile / tiles_kv) * kTile;  // local query block of tile row 0
+    const int j0 = (tile % tiles_kv) * kTile;
     const int iend = min(sv.nq, c0 + C);
     if (i0 >= iend || j0 >= sv.nkv) return;
     const int64_t srow0 = ((int64_t)s * P.H + h) * C - c0;  // scratch row of local block 0
@@ -350,17 +371,27 @@ __global__ __launch_bounds__(kThreads) void coarse_out_kernel(DevProblem P, cons
 }
 
 template <int D>
-hipError_t launch_d(const DevProblem& P, const double* qc, const double* kc, const double* vc, float* out_c,
-                    int* idx, int* num, double* sc, double* lsum, int C, hipStream_t st) {
+hipError_t launch_d(const DevProblem& P, const double* qc, const double* kc, double* vc, float* out_c,
+                    int* idx, int* num, double* sc, double* lsum, int C, hipStream_t st, const DevProblem* PP,
+                    const uint16_t* v) {
     const int max_nq = P.packed ? P.max_q : P.nQ;
     const int ld = P.packed ? P.max_kv : P.nKV;
     const int tq = (C + kTile - 1) / kTile, tk = (ld + kTile - 1) / kTile;
+    if ((int64_t)tq * tk * P.H * P.nseq > 0x7fffffff) return hipErrorInvalidValue;
     const int64_t rows = (int64_t)P.nseq * P.H * C;
     const dim3 sgrid((unsigned)((rows + kThreads / 64 - 1) / (kThreads / 64)));
     const double scale = 1.0 / sqrt((double)D);
     for (int c0 = 0; c0 < max_nq; c0 += C) {
-        hipLaunchKernelGGL(coarse_scores_kernel<D>, dim3(tq * tk, P.H, P.nseq), dim3(kThreads), 0, st, P, qc, kc,
-                           sc, ld, tk, c0, C);
+        const int n_tiles = tq * tk * P.H * P.nseq;
+        if (PP && c0 == 0) {  // the first launch also pools V
+            const int64_t n_pool = (int64_t)pool::pool_columns(*PP) * PP->H * (PP->packed ? 1 : PP->nseq);
+            if (n_tiles + n_pool > 0x7fffffff) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((coarse_scores_kernel<D, true>), dim3((unsigned)(n_tiles + n_pool)), dim3(kThreads), 0,
+                               st, P, qc, kc, sc, ld, tk, c0, C, n_tiles, *PP, v, vc);
+        } else {
+            hipLaunchKernelGGL((coarse_scores_kernel<D, false>), dim3((unsigned)n_tiles), dim3(kThreads), 0, st, P,
+                               qc, kc, sc, ld, tk, c0, C, n_tiles, P, nullptr, nullptr);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (ld <= 4 * 64)
@@ -409,24 +440,28 @@ hipError_t launch_coarse_scores(const DevProblem& P, const double* a, const doub
     const int max_nq = P.packed ? P.max_q : P.nQ;
     const int ld = P.packed ? P.max_kv : P.nKV;
     const int tq = (max_nq + kTile - 1) / kTile, tk = (ld + kTile - 1) / kTile;
+    if ((int64_t)tq * tk * P.H * P.nseq > 0x7fffffff) return hipErrorInvalidValue;
+    const int n_tiles = tq * tk * P.H * P.nseq;
     if (P.D == 128)
-        hipLaunchKernelGGL(coarse_scores_kernel<128>, dim3(tq * tk, P.H, P.nseq), dim3(kThreads), 0, st, P, a, b,
-                           out, ld, tk, 0, max_nq);
+        hipLaunchKernelGGL((coarse_scores_kernel<128, false>), dim3((unsigned)n_tiles), dim3(kThreads), 0, st, P, a,
+                           b, out, ld, tk, 0, max_nq, n_tiles, P, nullptr, nullptr);
     else
-        hipLaunchKernelGGL(coarse_scores_kernel<64>, dim3(tq * tk, P.H, P.nseq), dim3(kThreads), 0, st, P, a, b,
-                           out, ld, tk, 0, max_nq);
+        hipLaunchKernelGGL((coarse_scores_kernel<64, false>), dim3((unsigned)n_tiles), dim3(kThreads), 0, st, P, a,
+                           b, out, ld, tk, 0, max_nq, n_tiles, P, nullptr, nullptr);
     return hipGetLastError();
 }
 
-hipError_t launch_coarse_topk(const DevProblem& P, const double* qc, const double* kc, const double* vc,
-                              float* out_c, int* idx, int* num, double* scratch, hipStream_t st) {
+hipError_t launch_coarse_topk(const DevProblem& P, const double* qc, const double* kc, double* vc,
+                              float* out_c, int* idx, int* num, double* scratch, hipStream_t st,
+                              const DevProblem* pool_p, const uint16_t* v) {
+    if ((pool_p == nullptr) != (v == nullptr) || (pool_p && pool_p->D != P.D)) return hipErrorInvalidValue;
     const int kv_cap = P.packed ? P.max_kv : P.nKV;
     if (kv_cap < 1 || kv_cap > kMaxKvBlocks) return hipErrorInvalidValue;
     const int C = chunk_rows(P);
     double* sc = scratch;
     double* lsum = scratch + (int64_t)P.nseq * P.H * C * kv_cap;
-    if (P.D == 128) return launch_d<128>(P, qc, kc, vc, out_c, idx, num, sc, lsum, C, st);
-    return launch_d<64>(P, qc, kc, vc, out_c, idx, num, sc, lsum, C, st);
+    if (P.D == 128) return launch_d<128>(P, qc, kc, vc, out_c, idx, num, sc, lsum, C, st, pool_p, v);
+    return launch_d<64>(P, qc, kc, vc, out_c, idx, num, sc, lsum, C, st, pool_p, v);
 }
 
 }  // namespace vsa

@@ -272,9 +272,12 @@ int gate_strides(const vsa::DevProblem& P, const uint16_t* gate, int mode, const
 
 int run_coarse(const vsa::DevProblem& P, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                float* out_c, int* idx, int* num, const Workspace& w, hipStream_t st) {
-    int rc = hip_status(vsa::launch_pool(P, q, k, v, w.qc, w.kc, w.vc, st), "pool launch");
+    // Q and K are pooled first; V is pooled by workgroups of the first score
+    // launch, which needs only Q and K and leaves the memory system idle
+    int rc = hip_status(vsa::launch_pool_qk(P, q, k, w.qc, w.kc, st), "pool launch");
     if (rc) return rc;
-    return hip_status(vsa::launch_coarse_topk(vsa::coarse_view(P), w.qc, w.kc, w.vc, out_c, idx, num, w.coarse, st),
+    return hip_status(vsa::launch_coarse_topk(vsa::coarse_view(P), w.qc, w.kc, w.vc, out_c, idx, num, w.coarse, st,
+                                              &P, v),
                       "coarse/top-k launch");
 }
 

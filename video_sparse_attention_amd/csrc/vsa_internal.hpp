@@ -187,6 +187,9 @@ __host__ __device__ inline int64_t tile_token_raster(const TileGrid& g, int b, i
 // Block means over VSA blocks of 64 * P.ratio tokens.
 hipError_t launch_pool(const DevProblem& P, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        double* qc, double* kc, double* vc, hipStream_t st);
+// The same for Q and K only (V is then pooled by launch_coarse_topk).
+hipError_t launch_pool_qk(const DevProblem& P, const uint16_t* q, const uint16_t* k, double* qc, double* kc,
+                          hipStream_t st);
 // The problem as the coarse branch sees it: VSA blocks as its blocks.
 inline DevProblem coarse_view(const DevProblem& P) {
     DevProblem C = P;
@@ -195,10 +198,13 @@ inline DevProblem coarse_view(const DevProblem& P) {
     C.ratio = 1;
     return C;
 }
-// scratch: coarse_scratch_doubles(P) doubles (block-level scores and row sums)
+// scratch: coarse_scratch_doubles(P) doubles (block-level scores and row sums).
+// With pool_p and v set, V has not been pooled yet: the first score launch
+// also pools it (pool_p = the full problem, v its bf16 tensor) into vc, in
+// workgroups of its own that run beside the score tiles.
 hipError_t launch_coarse_topk(const DevProblem& P, const double* qc, const double* kc,
-                              const double* vc, float* out_c, int* idx, int* num, double* scratch,
-                              hipStream_t st);
+                              double* vc, float* out_c, int* idx, int* num, double* scratch,
+                              hipStream_t st, const DevProblem* pool_p = nullptr, const uint16_t* v = nullptr);
 size_t coarse_scratch_doubles(const DevProblem& P);
 // out[r][j] = a[query block i] . b[KV block j] (float64, raw dot products) for
 // every sequence s and head h, r = (s * H + h) * max_q + i, row length max_kv
