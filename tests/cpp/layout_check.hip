@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "attn_layout.hpp"
+#include "vsa_internal.hpp"
 
 static int failures = 0;
 #define CHECK(cond, ...)                  \
@@ -277,9 +278,36 @@ static void check_d() {
     }
 }
 
+// Column order of the float64 block-level products' LDS rows: a permutation
+// of 0..63 that keeps column pairs adjacent and puts the two double2 reads of
+// the 16 threads of a thread-grid row on 64 distinct banks each.
+static void check_quad_col() {
+    std::vector<int> seen(64, 0);
+    for (int c = 0; c < 64; ++c) {
+        const int q = vsa::quad_col(c);
+        CHECK(q >= 0 && q < 64, "quad_col(%d)=%d", c, q);
+        if (q >= 0 && q < 64) seen[q]++;
+        if (c % 2 == 1) CHECK(q == vsa::quad_col(c - 1) + 1, "quad_col splits the pair %d", c - 1);
+    }
+    for (int q = 0; q < 64; ++q) CHECK(seen[q] == 1, "quad_col misses %d", q);
+    for (int half = 0; half < 2; ++half) {
+        std::vector<int> addr, bytes;
+        for (int tx = 0; tx < 16; ++tx) {
+            addr.push_back(8 * vsa::quad_col(4 * tx + 2 * half));
+            bytes.push_back(16);
+        }
+        CHECK(bank_ways(addr, bytes, 64) == 1, "quad_col reads conflict (pair %d)", half);
+        // the plain order (columns 4 tx + 2 half) has two-way conflicts
+        std::vector<int> plain;
+        for (int tx = 0; tx < 16; ++tx) plain.push_back(8 * (4 * tx + 2 * half));
+        CHECK(bank_ways(plain, bytes, 64) == 2, "plain order expected two-way (pair %d)", half);
+    }
+}
+
 int main() {
     check_d<128>();
     check_d<64>();
+    check_quad_col();
     const int Ns[] = {1, 2, 7, 8, 9, 15, 16, 17, 63, 64, 65, 242, 1000, 13552, 16896, 100003};
     for (int N : Ns) {
         std::vector<char> hit(N, 0);

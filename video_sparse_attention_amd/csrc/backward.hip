@@ -282,7 +282,8 @@ __global__ __launch_bounds__(kThreads) void bwd_coarse_mm_kernel(DevProblem P, c
 #pragma unroll
         for (int p = 0; p < DC / 32; ++p) {
             const int e = tid + kThreads * p;
-            *reinterpret_cast<double2*>(&xs[e / (DC / 2)][2 * (e % (DC / 2))]) = xv[p];
+            const int col = 2 * (e % (DC / 2));
+            *reinterpret_cast<double2*>(&xs[e / (DC / 2)][CPT == 4 ? quad_col(col) : col]) = xv[p];
         }
         __syncthreads();
         if (k0 + kSlice < nk) fetch(k0 + kSlice);
@@ -294,7 +295,8 @@ __global__ __launch_bounds__(kThreads) void bwd_coarse_mm_kernel(DevProblem P, c
             double v[CPT];
 #pragma unroll
             for (int c = 0; c < CPT; c += 2) {
-                const double2 t2 = *reinterpret_cast<const double2*>(&xs[kk][CPT * tx + c]);
+                const int col = CPT == 4 ? quad_col(CPT * tx + c) : CPT * tx + c;
+                const double2 t2 = *reinterpret_cast<const double2*>(&xs[kk][col]);
                 v[c] = t2.x;
                 v[c + 1] = t2.y;
             }

@@ -41,13 +41,6 @@ __device__ __forceinline__ uint64_t order_key(double s) {
     return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
-// Column position inside a 64-wide LDS row for the 4-column register tiles
-// below: thread tx reads its columns 4 tx, 4 tx + 1 at 2 tx and 4 tx + 2,
-// 4 tx + 3 at 32 + 2 tx, so the 16 threads of a row of the thread grid read
-// 256 contiguous bytes per double2 access (no bank conflicts); column pairs
-// 2m, 2m + 1 stay adjacent.
-__device__ __forceinline__ int quad_col(int c) { return ((c >> 1) & 1) * 32 + (c >> 2) * 2 + (c & 1); }
-
 __device__ __forceinline__ int prefix_popc(uint64_t mask) {
     const int l = __lane_id();
     const uint64_t below = l == 0 ? 0ull : (mask & ((~0ull) >> (64 - l)));
