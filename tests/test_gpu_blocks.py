@@ -42,6 +42,7 @@ def _check_all(inp, gpu, ref):
     (256, 1, 1, 256 * 3, 256 * 6 - 7, 64, 100, "token"),       # top-k above the VSA block count
     (256, 2, 1, 256 * 5 + 200, 256 * 5 + 200, 64, 1, None),    # top-1, 200-token tail (4 sub-blocks, last 8)
     (128, 1, 2, 1, 1, 128, 1, None),                           # single token
+    (256, 1, 1, 256 + 30, 256 * 4095 + 100, 64, 40, "token"),  # the maximum: 4096 VSA blocks of 256
 ])
 def test_large_vsa_blocks(block, B, H, Sq, Skv, D, topk, gate):
     inp = _inputs(B, H, Sq, Skv, D, topk, gate, seed=3000 + block + Sq + Skv + D)
