@@ -104,6 +104,45 @@ def test_dense_edge_cases(B, H, Sq, Skv, D, topk, gate):
     N.check_out(N.f64(out), ref["out"])
 
 
+@pytest.mark.parametrize("scale", [4.0, 16.0])
+def test_sharp_softmax(scale):
+    """Q and K scaled up so that every softmax is nearly one-hot and the
+    running maximum jumps by far more than the lazy-rescale threshold from
+    block to block (and the coarse scores spread over a wide range)."""
+    inp = synth.dense_inputs(1, 2, 64 * 20 + 5, 128, 5, seed=2100 + int(scale), gated=True)
+    inp.q = (inp.q.float() * scale).to(torch.bfloat16)
+    inp.k = (inp.k.float() * scale).to(torch.bfloat16)
+    G.note(f"case sharp softmax scale={scale}")
+    ref = G.oracle_dense(inp)
+    G.assert_tie_free(ref)
+    q, k, v, g = (t.to(G.DEV) for t in (inp.q, inp.k, inp.v, inp.gate))
+    out, oc, idx, num = vsa.vsa_forward(q, k, v, inp.topk, g, return_aux=True)
+    torch.cuda.synchronize()
+    G.assert_indices_equal(idx.cpu(), num.cpu(), ref)
+    N.check_out_c(N.f64(oc), ref["out_c"])
+    N.check_out(N.f64(out), ref["out"])
+    assert torch.isfinite(out.float()).all()
+
+
+def test_zero_inputs():
+    """All-zero Q, K, V: every coarse score ties, so the routing is the first
+    k blocks of every row (the lower-index rule); every softmax is uniform
+    over zeros and the output is exactly zero."""
+    B, H, S, D, topk = 1, 2, 64 * 9 + 20, 64, 4
+    q = torch.zeros(B, H, S, D, dtype=torch.bfloat16)
+    gen = torch.Generator().manual_seed(5)
+    gate = torch.sigmoid(torch.randn(B, H, S, generator=gen)).to(torch.bfloat16)
+    ref = oracle.vsa_forward(N.f64(q), N.f64(q), N.f64(q), topk, N.f64(gate))
+    nq = -(-S // 64)
+    assert np.array_equal(ref["q2k_idx"], np.broadcast_to(np.arange(topk), (B, H, nq, topk)))
+    qd, gd = q.to(G.DEV), gate.to(G.DEV)
+    out, oc, idx, num = vsa.vsa_forward(qd, qd, qd, topk, gd, return_aux=True)
+    torch.cuda.synchronize()
+    G.assert_indices_equal(idx.cpu(), num.cpu(), ref)
+    assert torch.count_nonzero(oc).item() == 0
+    assert torch.count_nonzero(out).item() == 0
+
+
 def test_sparse_on_oracle_indices():
     """The sparse stage fed the oracle's routing reproduces the oracle's out_s."""
     for name in ("tiny", "dense_equiv"):
