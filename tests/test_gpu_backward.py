@@ -29,7 +29,7 @@ GRAD_FLOOR_MAX = 1e-2
 GRAD_FLOOR_MEAN = 1e-3
 
 
-def check_grad(gpu: np.ndarray, ref: np.ndarray, what: str):
+def check_grad(gpu: np.ndarray, ref: np.ndarray, what: str, max_rel=None, mean_rel=None):
     assert np.isfinite(gpu).all(), f"{what}: non-finite values"
     d = np.abs(gpu - ref)
     # a gradient that vanishes in exact arithmetic (one key per row: P = 1,
@@ -39,8 +39,10 @@ def check_grad(gpu: np.ndarray, ref: np.ndarray, what: str):
     scale_mean = max(float(np.abs(ref).mean()), GRAD_FLOOR_MEAN)
     mx, mean = float(d.max()) / scale_max, float(d.mean()) / scale_mean
     G.note(f"  {what}: max-err/max {mx:.2e}, mean-err/mean {mean:.2e} (|ref| max {scale_max:.2e})")
-    assert mx <= GRAD_MAX_REL, f"{what}: max error {mx:.3e} of the largest gradient > {GRAD_MAX_REL}"
-    assert mean <= GRAD_MEAN_REL, f"{what}: mean error {mean:.3e} of the mean gradient > {GRAD_MEAN_REL}"
+    max_rel = GRAD_MAX_REL if max_rel is None else max_rel
+    mean_rel = GRAD_MEAN_REL if mean_rel is None else mean_rel
+    assert mx <= max_rel, f"{what}: max error {mx:.3e} of the largest gradient > {max_rel}"
+    assert mean <= mean_rel, f"{what}: mean error {mean:.3e} of the mean gradient > {mean_rel}"
 
 
 def run_dense_train(q, k, v, gate, dout, topk, dev=G.DEV, block_size=64, bshd=False):
@@ -75,7 +77,8 @@ def run_dense_train(q, k, v, gate, dout, topk, dev=G.DEV, block_size=64, bshd=Fa
                 q2k_num=num.cpu(), dq=cpu(dq), dk=cpu(dk), dv=cpu(dv), dgate=cpu(dg), out_c=out_c.cpu())
 
 
-def check_dense_case(q, k, v, gate, topk, seed, tag, block_size=64, bshd=False):
+def check_dense_case(q, k, v, gate, topk, seed, tag, block_size=64, bshd=False, max_rel=None, mean_rel=None,
+                     lse_abs=LSE_ABS):
     G.note(f"case {tag}: q {tuple(q.shape)} kv {tuple(k.shape)} topk={topk} block={block_size} bshd={bshd} "
            f"gate={'none' if gate is None else tuple(gate.shape)}")
     dout = synth.output_grad(q.shape, seed)
@@ -89,11 +92,11 @@ def check_dense_case(q, k, v, gate, topk, seed, tag, block_size=64, bshd=False):
     N.check_sparse(N.f64(gpu["out_s"]), ref["out_s"])
     dl = float(np.abs(N.f64(gpu["lse"]) - ref["lse"]).max())
     G.note(f"  lse max-abs {dl:.2e}")
-    assert dl <= LSE_ABS, f"lse: max-abs {dl:.3e} > {LSE_ABS}"
+    assert dl <= lse_abs, f"lse: max-abs {dl:.3e} > {lse_abs}"
     for name in ("dq", "dk", "dv"):
-        check_grad(N.f64(gpu[name]), ref[name], name)
+        check_grad(N.f64(gpu[name]), ref[name], name, max_rel, mean_rel)
     if gate is not None:
-        check_grad(N.f64(gpu["dgate"]), ref["dgate"], "dgate")
+        check_grad(N.f64(gpu["dgate"]), ref["dgate"], "dgate", max_rel, mean_rel)
     return gpu, ref
 
 
@@ -127,6 +130,25 @@ def test_backward_degenerate_lengths(Sq, Skv):
     """One-token queries, a single (partial) KV block, exact block multiples."""
     inp = synth.dense_inputs(1, 2, Sq, 64, 2, seed=2030 + Sq, S_kv=Skv, gated=True)
     check_dense_case(inp.q, inp.k, inp.v, inp.gate, 2, 2031 + Sq + Skv, f"Sq={Sq} Skv={Skv}")
+
+
+@pytest.mark.parametrize("scale", [1.5, 3.0, 8.0])
+def test_backward_sharp_softmax(scale):
+    """Q and K scaled up: nearly one-hot probabilities, large log-sum-exp
+    values and a running maximum that moves far past the lazy-rescale
+    threshold; the recomputed probabilities and dS must still match.  The
+    error relative to the largest gradient keeps the usual bound; the mean
+    bound is wider here (measured 2.5e-3, 5.9e-3 and 1.4e-2 for dq at the
+    three scales): as the softmax sharpens, dq and dk concentrate on a few
+    large entries, so their mean shrinks against the largest one, while the
+    bf16 rounding of dS and of the output that delta = sum(dout * out_s) is
+    formed from scales with the largest entries.  (The pages' backward test
+    uses a 5 % relative tolerance.)"""
+    inp = synth.dense_inputs(1, 2, 64 * 6 + 9, 128, 3, seed=2040 + int(scale), gated=True)
+    q = (inp.q.float() * scale).to(torch.bfloat16)
+    k = (inp.k.float() * scale).to(torch.bfloat16)
+    check_dense_case(q, k, inp.v, inp.gate, 3, 2041 + int(scale), f"sharp softmax x{scale}",
+                     mean_rel=3e-2)
 
 
 def test_backward_is_deterministic():
