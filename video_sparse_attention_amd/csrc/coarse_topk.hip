@@ -12,7 +12,9 @@
 //      Qc Kc^T (raw dot products, no scale) of the chunk's query blocks is
 //      written to a workspace matrix with one row per query block; 64 x 64
 //      output tiles per workgroup, 16-wide d slices of Qc and Kc staged
-//      transposed in LDS, 4 x 4 outputs per thread;
+//      transposed in LDS, 4 x 4 outputs per thread.  The first of these
+//      launches also pools V, in workgroups of its own (the pool kernel has
+//      pooled Q and K before it);
 //   2. select: one wave per query block row.  The row's order-preserving
 //      64-bit keys sit in registers (up to 64 per lane), the k-th largest is
 //      found by bisection with wave-wide ballot counts (32 rounds on the high
