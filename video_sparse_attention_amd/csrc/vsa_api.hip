@@ -273,7 +273,8 @@ int gate_strides(const vsa::DevProblem& P, const uint16_t* gate, int mode, const
 int run_coarse(const vsa::DevProblem& P, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                float* out_c, int* idx, int* num, const Workspace& w, hipStream_t st) {
     // Q and K are pooled first; V is pooled by workgroups of the first score
-    // launch, which needs only Q and K and leaves the memory system idle
+    // launch, which needs only Q and K and, being latency-bound, leaves most
+    // of the HBM bandwidth to them
     int rc = hip_status(vsa::launch_pool_qk(P, q, k, w.qc, w.kc, st), "pool launch");
     if (rc) return rc;
     return hip_status(vsa::launch_coarse_topk(vsa::coarse_view(P), w.qc, w.kc, w.vc, out_c, idx, num, w.coarse, st,
