@@ -278,36 +278,37 @@ static void check_d() {
     }
 }
 
-// Column order of the float64 block-level products' LDS rows: a permutation
-// of 0..63 that keeps column pairs adjacent and puts the two double2 reads of
-// the 16 threads of a thread-grid row on 64 distinct banks each.
-static void check_quad_col() {
-    std::vector<int> seen(64, 0);
-    for (int c = 0; c < 64; ++c) {
-        const int q = vsa::quad_col(c);
-        CHECK(q >= 0 && q < 64, "quad_col(%d)=%d", c, q);
-        if (q >= 0 && q < 64) seen[q]++;
-        if (c % 2 == 1) CHECK(q == vsa::quad_col(c - 1) + 1, "quad_col splits the pair %d", c - 1);
-    }
-    for (int q = 0; q < 64; ++q) CHECK(seen[q] == 1, "quad_col misses %d", q);
-    for (int half = 0; half < 2; ++half) {
-        std::vector<int> addr, bytes;
-        for (int tx = 0; tx < 16; ++tx) {
-            addr.push_back(8 * vsa::quad_col(4 * tx + 2 * half));
-            bytes.push_back(16);
+// Operand reads of the float64 MFMA block-level products (v_mfma_f64_16x16x4):
+// lane (m = lane % 16, g = lane / 16) reads element m of staged row g, rows
+// `pitch` doubles apart (64 or 32 values plus 16 of padding).  Each half-wave
+// of a ds_read_b64 (32 lanes, two rows) must touch 64 distinct banks; without
+// the padding the two rows of a half-wave share their banks.
+static void check_f64_mfma_operands() {
+    const int rows[] = {64, 32};
+    for (int len : rows) {
+        for (int pad : {16, 0}) {
+            const int pitch = len + pad;
+            int worst = 0;
+            for (int col0 = 0; col0 + 16 <= len; col0 += 16)
+                for (int half = 0; half < 2; ++half) {
+                    std::vector<int> addr, bytes;
+                    for (int l = 32 * half; l < 32 * half + 32; ++l) {
+                        addr.push_back(8 * ((l / 16) * pitch + col0 + l % 16));
+                        bytes.push_back(8);
+                    }
+                    const int w = bank_ways(addr, bytes, 64);
+                    worst = w > worst ? w : worst;
+                }
+            if (pad) CHECK(worst == 1, "f64 MFMA operand reads conflict (row %d, pitch %d)", len, pitch);
+            else CHECK(worst == 2, "unpadded rows expected two-way (row %d)", len);
         }
-        CHECK(bank_ways(addr, bytes, 64) == 1, "quad_col reads conflict (pair %d)", half);
-        // the plain order (columns 4 tx + 2 half) has two-way conflicts
-        std::vector<int> plain;
-        for (int tx = 0; tx < 16; ++tx) plain.push_back(8 * (4 * tx + 2 * half));
-        CHECK(bank_ways(plain, bytes, 64) == 2, "plain order expected two-way (pair %d)", half);
     }
 }
 
 int main() {
     check_d<128>();
     check_d<64>();
-    check_quad_col();
+    check_f64_mfma_operands();
     const int Ns[] = {1, 2, 7, 8, 9, 15, 16, 17, 63, 64, 65, 242, 1000, 13552, 16896, 100003};
     for (int N : Ns) {
         std::vector<char> hit(N, 0);

@@ -219,21 +219,26 @@ __global__ __launch_bounds__(kThreads) void bwd_coarse_softmax_kernel(DevProblem
 // 64 output rows x D / 2 columns per workgroup (the two column halves of a
 // row tile in consecutive workgroups, so that a head's few row tiles spread
 // over twice as many CUs), 16-wide k slices of M and X staged in LDS (the
-// next slice prefetched into registers), 4 rows x D / 32 columns per thread.
-// Grid (2 ceil(max rows / 64), H, sequences).
+// next slice prefetched into registers), products by float64 MFMA
+// (v_mfma_f64_16x16x4): each wave computes 16 or 32 output rows by 32
+// columns.  Grid (2 ceil(max rows / 64), H, sequences).
 constexpr int kMmSplit = 2;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 template <int D, bool TRANS>
 __global__ __launch_bounds__(kThreads) void bwd_coarse_mm_kernel(DevProblem P, const double* __restrict__ m,
                                                                  const double* __restrict__ x,
                                                                  double* __restrict__ out, int ld, int maxq,
                                                                  double alpha) {
-    constexpr int kTile = 64, kSlice = 16, kPad = 2;
-    constexpr int DC = D / kMmSplit;  // columns per workgroup
-    constexpr int CPT = DC / 16;      // output columns per thread
-    static_assert(CPT >= 2 && CPT % 2 == 0, "double2 column pairs");
+    // LDS rows 16 doubles longer than their 64 or 32 values (32 banks modulo
+    // 64): the four 16-lane groups of an operand read fall on disjoint banks
+    constexpr int kTile = 64, kSlice = 16, kPad = 16;
+    constexpr int DC = D / kMmSplit;     // columns per workgroup
+    constexpr int NT = 2;                // 16-column products per wave
+    constexpr int MT = DC == 64 ? 2 : 1; // 16-row products per wave
+    static_assert(DC == 32 || DC == 64, "64 or 32 columns per workgroup");
     __shared__ __attribute__((aligned(16))) double mt[kSlice][kTile + kPad];  // [k][o]
-    __shared__ __attribute__((aligned(16))) double xs[kSlice][DC];            // [k][d - cbase]
+    __shared__ __attribute__((aligned(16))) double xs[kSlice][DC + kPad];     // [k][d - cbase]
     const int s = blockIdx.z, h = blockIdx.y;
     const SeqView sv = seq_view(P, s, h);
     const int nout = TRANS ? sv.nkv : sv.nq, nk = TRANS ? sv.nq : sv.nkv;
@@ -244,12 +249,17 @@ __global__ __launch_bounds__(kThreads) void bwd_coarse_mm_kernel(DevProblem P, c
     const int64_t xbase = TRANS ? sv.qblk_base : sv.kvblk_base;
     const int64_t obase = TRANS ? sv.kvblk_base : sv.qblk_base;
     const int tid = threadIdx.x;
-    const int ty = tid / 16, tx = tid % 16;
-    double acc[4][CPT];
+    // wave w computes outputs wr .. wr + 16 MT - 1, columns wc .. wc + 31 of
+    // the tile: lane (i = lane % 16, g = lane / 16) supplies M(row i, k g) and
+    // X[k g][col i] of each 4-wide k step
+    const int wave = tid / 64, lane = tid % 64, lm = lane & 15, lg = lane >> 4;
+    const int wr = MT == 2 ? 32 * (wave >> 1) : 16 * wave;
+    const int wc = MT == 2 ? 32 * (wave & 1) : 0;
+    f64x4 acc[MT][NT];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int a = 0; a < MT; ++a)
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) acc[r][c] = 0.0;
+        for (int b = 0; b < NT; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
     // staging of M: TRANS = false, thread t holds k = 4 (t % 4) .. + 3 of output
     // row t / 4; TRANS = true, thread t holds outputs 4 (t % 16) .. + 3 of k row t / 16
     const int ma = TRANS ? tid / 16 : tid / 4;
@@ -282,39 +292,35 @@ __global__ __launch_bounds__(kThreads) void bwd_coarse_mm_kernel(DevProblem P, c
 #pragma unroll
         for (int p = 0; p < DC / 32; ++p) {
             const int e = tid + kThreads * p;
-            const int col = 2 * (e % (DC / 2));
-            *reinterpret_cast<double2*>(&xs[e / (DC / 2)][CPT == 4 ? quad_col(col) : col]) = xv[p];
+            *reinterpret_cast<double2*>(&xs[e / (DC / 2)][2 * (e % (DC / 2))]) = xv[p];
         }
         __syncthreads();
         if (k0 + kSlice < nk) fetch(k0 + kSlice);
-#pragma unroll 4
-        for (int kk = 0; kk < kSlice; ++kk) {
-            const double2 w01 = *reinterpret_cast<const double2*>(&mt[kk][4 * ty]);
-            const double2 w23 = *reinterpret_cast<const double2*>(&mt[kk][4 * ty + 2]);
-            const double w[4] = {w01.x, w01.y, w23.x, w23.y};
-            double v[CPT];
 #pragma unroll
-            for (int c = 0; c < CPT; c += 2) {
-                const int col = CPT == 4 ? quad_col(CPT * tx + c) : CPT * tx + c;
-                const double2 t2 = *reinterpret_cast<const double2*>(&xs[kk][col]);
-                v[c] = t2.x;
-                v[c + 1] = t2.y;
-            }
+        for (int k4 = 0; k4 < kSlice; k4 += 4) {
+            const int kk = k4 + lg;
+            double a[MT], b[NT];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int i = 0; i < MT; ++i) a[i] = mt[kk][wr + 16 * i + lm];
 #pragma unroll
-                for (int c = 0; c < CPT; ++c) acc[r][c] = fma(w[r], v[c], acc[r][c]);
+            for (int j = 0; j < NT; ++j) b[j] = xs[kk][wc + 16 * j + lm];
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < NT; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
         }
     }
+    // accumulator e of product (i, j): output wr + 16 i + 4 e + g, column wc + 16 j + m
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int o = o0 + 4 * ty + r;
-        if (o >= nout) continue;
-        double* dst = out + (obase + o) * D + cbase + CPT * tx;
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int c = 0; c < CPT; c += 2)
-            *reinterpret_cast<double2*>(dst + c) = make_double2(acc[r][c] * alpha, acc[r][c + 1] * alpha);
-    }
+        for (int e = 0; e < 4; ++e) {
+            const int o = o0 + wr + 16 * i + 4 * e + lg;
+            if (o >= nout) continue;
+            double* dst = out + (obase + o) * D + cbase + wc + lm;
+#pragma unroll
+            for (int j = 0; j < NT; ++j) dst[16 * j] = acc[i][j][e] * alpha;
+        }
 }
 
 // ---------------------------------------------------------------------------

@@ -12,9 +12,11 @@
 //      Qc Kc^T (raw dot products, no scale) of the chunk's query blocks is
 //      written to a workspace matrix with one row per query block; 64 x 64
 //      output tiles per workgroup, 16-wide d slices of Qc and Kc staged
-//      transposed in LDS, 4 x 4 outputs per thread.  The first of these
-//      launches also pools V, in workgroups of its own (the pool kernel has
-//      pooled Q and K before it);
+//      transposed in LDS, each wave's 32 x 32 quarter computed by float64
+//      MFMA (v_mfma_f64_16x16x4, the same float64 FMAs as the vector unit at
+//      a quarter of its LDS reads).  The first of these launches also pools
+//      V, in workgroups of its own (the pool kernel has pooled Q and K before
+//      it);
 //   2. select: one wave per query block row.  The row's order-preserving
 //      64-bit keys sit in registers (up to 64 per lane), the k-th largest is
 //      found by bisection with wave-wide ballot counts (32 rounds on the high
@@ -22,9 +24,9 @@
 //      threshold go to the lowest indices, and the indices are emitted in
 //      ascending order with ballot prefix counts.  The row is then replaced
 //      by its softmax weights exp((s - max) / sqrt(D)) and their sum is kept;
-//   3. output: out_c = W Vc / sum(W) per row, 64 rows x D columns per
-//      workgroup, 16-row slices of W and Vc staged in LDS, rounded once to
-//      float32.
+//   3. output: out_c = W Vc / sum(W) per row, 64 rows x D / 2 columns per
+//      workgroup, 16-row slices of W and Vc staged in LDS, float64 MFMA as
+//      in 1, rounded once to float32.
 #include "attn_layout.hpp"
 #include "pool_common.hpp"
 #include "vsa_internal.hpp"
@@ -35,7 +37,11 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTile = 64;   // query rows (and KV columns) per workgroup tile
 constexpr int kSlice = 16;  // d (or KV) values per LDS slice
-constexpr int kPad = 2;     // keeps each transposed LDS row 16-byte aligned
+// LDS rows of the staged slices are kPad = 16 doubles longer than their 64 or
+// 32 values (80 or 48 doubles, 32 banks modulo 64), so the four 16-lane
+// groups of an MFMA operand read (one row each) fall on disjoint banks
+constexpr int kPad = 16;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint64_t order_key(double s) {
     // -0.0 and +0.0 compare equal as doubles; fold them before the bit map.
@@ -102,11 +108,16 @@ __global__ __launch_bounds__(kThreads) void coarse_scores_kernel(DevProblem P, c
     const double* qrow = qc + (sv.qblk_base + i0 + (q_ok ? sr : 0)) * D + sd;
     const double* krow = kc + (sv.kvblk_base + j0 + (k_ok ? sr : 0)) * D + sd;
 
-    double acc[4][4];
+    // wave w computes the 32 x 32 quarter (rows 32 (w / 2), columns 32 (w % 2))
+    // of the tile as 2 x 2 products v_mfma_f64_16x16x4: lane (m = lane % 16,
+    // g = lane / 16) supplies Qc[row m][d g] and Kc[col m][d g] of each 4-wide d step
+    const int wave = tid / 64, lane = tid % 64, lm = lane & 15, lg = lane >> 4;
+    const int wr = 32 * (wave >> 1), wc = 32 * (wave & 1);
+    f64x4 acc[2][2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] = 0.0;
+        for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
     // the next slice is loaded into registers while the current one is used
     double2 qa = make_double2(0.0, 0.0), qb = qa, ka = qa, kb = qa;
     auto fetch = [&](int d0) {
@@ -123,33 +134,36 @@ __global__ __launch_bounds__(kThreads) void coarse_scores_kernel(DevProblem P, c
     for (int d0 = 0; d0 < D; d0 += kSlice) {
         __syncthreads();  // previous slice fully consumed
         qt[sd + 0][sr] = qa.x; qt[sd + 1][sr] = qa.y; qt[sd + 2][sr] = qb.x; qt[sd + 3][sr] = qb.y;
-        const int kcol = quad_col(sr);
-        kt[sd + 0][kcol] = ka.x; kt[sd + 1][kcol] = ka.y; kt[sd + 2][kcol] = kb.x; kt[sd + 3][kcol] = kb.y;
+        kt[sd + 0][sr] = ka.x; kt[sd + 1][sr] = ka.y; kt[sd + 2][sr] = kb.x; kt[sd + 3][sr] = kb.y;
         __syncthreads();
         if (d0 + kSlice < D) fetch(d0 + kSlice);
 #pragma unroll
-        for (int d = 0; d < kSlice; ++d) {
-            const double2 q01 = *reinterpret_cast<const double2*>(&qt[d][4 * ty]);
-            const double2 q23 = *reinterpret_cast<const double2*>(&qt[d][4 * ty + 2]);
-            const double2 k01 = *reinterpret_cast<const double2*>(&kt[d][2 * tx]);
-            const double2 k23 = *reinterpret_cast<const double2*>(&kt[d][32 + 2 * tx]);
-            const double qv[4] = {q01.x, q01.y, q23.x, q23.y};
-            const double kv[4] = {k01.x, k01.y, k23.x, k23.y};
+        for (int d4 = 0; d4 < kSlice; d4 += 4) {
+            const int d = d4 + lg;
+            double a[2], b[2];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int x = 0; x < 2; ++x) {
+                a[x] = qt[d][wr + 16 * x + lm];
+                b[x] = kt[d][wc + 16 * x + lm];
+            }
 #pragma unroll
-                for (int c = 0; c < 4; ++c) acc[r][c] = fma(qv[r], kv[c], acc[r][c]);
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
         }
     }
+    // accumulator e of product (x, y): row wr + 16 x + 4 e + g, column wc + 16 y + m
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 4 * ty + r;
-        if (i >= iend) continue;
-        double* out = sc + (srow0 + i) * ld + j0 + 4 * tx;
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            if (j0 + 4 * tx + c < sv.nkv) out[c] = acc[r][c];
-    }
+        for (int e = 0; e < 4; ++e) {
+            const int i = i0 + wr + 16 * x + 4 * e + lg;
+            if (i >= iend) continue;
+            double* out = sc + (srow0 + i) * ld + j0 + wc + lm;
+#pragma unroll
+            for (int y = 0; y < 2; ++y)
+                if (j0 + wc + 16 * y + lm < sv.nkv) out[16 * y] = acc[x][y][e];
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -277,11 +291,12 @@ __global__ __launch_bounds__(kThreads) void coarse_out_kernel(DevProblem P, cons
                                                               const double* __restrict__ lsum,
                                                               const double* __restrict__ vc,
                                                               float* __restrict__ out_c, int c0, int C) {
-    constexpr int DC = D / kOutSplit;  // columns per workgroup
-    constexpr int CPT = DC / 16;       // output columns per thread
-    static_assert(CPT >= 2 && CPT % 2 == 0, "double2 reads of the Vc slice");
+    constexpr int DC = D / kOutSplit;        // columns per workgroup
+    constexpr int NT = 2;                    // 16-column products per wave
+    constexpr int MT = DC == 64 ? 2 : 1;     // 16-row products per wave
+    static_assert(DC == 32 || DC == 64, "64 or 32 columns per workgroup");
     __shared__ __attribute__((aligned(16))) double wt[kSlice][kTile + kPad];  // [kv][row]
-    __shared__ __attribute__((aligned(16))) double vs[kSlice][DC];            // [kv][d - cbase]
+    __shared__ __attribute__((aligned(16))) double vs[kSlice][DC + kPad];     // [kv][d - cbase]
     const int s = blockIdx.z, h = blockIdx.y;
     const SeqView sv = seq_view(P, s, h);
     const int cbase = (blockIdx.x % kOutSplit) * DC;
@@ -291,17 +306,22 @@ __global__ __launch_bounds__(kThreads) void coarse_out_kernel(DevProblem P, cons
     const int64_t srow0 = ((int64_t)s * P.H + h) * C - c0;  // scratch row of local block 0
     const int nkv = sv.nkv;
     const int tid = threadIdx.x;
-    const int ty = tid / 16, tx = tid % 16;
     // staging of W: thread t copies 4 consecutive KV entries of row t / 4
     const int sr = tid / 4, sj = 4 * (tid % 4);
     const bool w_ok = i0 + sr < iend;
     const double* wrow = sc + (srow0 + i0 + (w_ok ? sr : 0)) * ld;
+    // wave w computes rows wr .. wr + 16 MT - 1 and columns wc .. wc + 31 of the
+    // tile as MT x 2 products v_mfma_f64_16x16x4: lane (m = lane % 16, g =
+    // lane / 16) supplies W[row m][kv g] and Vc[kv g][col m] of each 4-wide KV step
+    const int wave = tid / 64, lane = tid % 64, lm = lane & 15, lg = lane >> 4;
+    const int wr = MT == 2 ? 32 * (wave >> 1) : 16 * wave;
+    const int wc = MT == 2 ? 32 * (wave & 1) : 0;
 
-    double acc[4][CPT];
+    f64x4 acc[MT][NT];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int a = 0; a < MT; ++a)
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) acc[r][c] = 0.0;
+        for (int b = 0; b < NT; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
     // the next slice is loaded into registers while the current one is used
     double wv[4];
     double2 vv[DC / 32];  // Vc slice: 16 rows of DC values, one double2 per thread per pass
@@ -328,41 +348,37 @@ __global__ __launch_bounds__(kThreads) void coarse_out_kernel(DevProblem P, cons
 #pragma unroll
         for (int p = 0; p < DC / 32; ++p) {
             const int e = tid + kThreads * p;
-            const int col = 2 * (e % (DC / 2));
-            *reinterpret_cast<double2*>(&vs[e / (DC / 2)][CPT == 4 ? quad_col(col) : col]) = vv[p];
+            *reinterpret_cast<double2*>(&vs[e / (DC / 2)][2 * (e % (DC / 2))]) = vv[p];
         }
         __syncthreads();
         if (j0 + kSlice < nkv) fetch(j0 + kSlice);
-#pragma unroll 4
-        for (int jj = 0; jj < kSlice; ++jj) {
-            const double2 w01 = *reinterpret_cast<const double2*>(&wt[jj][4 * ty]);
-            const double2 w23 = *reinterpret_cast<const double2*>(&wt[jj][4 * ty + 2]);
-            const double w[4] = {w01.x, w01.y, w23.x, w23.y};
-            double v[CPT];
 #pragma unroll
-            for (int c = 0; c < CPT; c += 2) {
-                const int col = CPT == 4 ? quad_col(CPT * tx + c) : CPT * tx + c;
-                const double2 t2 = *reinterpret_cast<const double2*>(&vs[jj][col]);
-                v[c] = t2.x;
-                v[c + 1] = t2.y;
-            }
+        for (int j4 = 0; j4 < kSlice; j4 += 4) {
+            const int j = j4 + lg;
+            double a[MT], b[NT];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int x = 0; x < MT; ++x) a[x] = wt[j][wr + 16 * x + lm];
 #pragma unroll
-                for (int c = 0; c < CPT; ++c) acc[r][c] = fma(w[r], v[c], acc[r][c]);
+            for (int y = 0; y < NT; ++y) b[y] = vs[j][wc + 16 * y + lm];
+#pragma unroll
+            for (int x = 0; x < MT; ++x)
+#pragma unroll
+                for (int y = 0; y < NT; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
         }
     }
+    // accumulator e of product (x, y): row wr + 16 x + 4 e + g, column wc + 16 y + m
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 4 * ty + r;
-        if (i >= iend) continue;
-        const int64_t qb = sv.qblk_base + i;
-        const double l = lsum[qb];
-        float* o = out_c + qb * D + cbase + CPT * tx;
+    for (int x = 0; x < MT; ++x)
 #pragma unroll
-        for (int c = 0; c < CPT; c += 2)
-            *reinterpret_cast<float2*>(o + c) = make_float2((float)(acc[r][c] / l), (float)(acc[r][c + 1] / l));
-    }
+        for (int e = 0; e < 4; ++e) {
+            const int i = i0 + wr + 16 * x + 4 * e + lg;
+            if (i >= iend) continue;
+            const int64_t qb = sv.qblk_base + i;
+            const double l = lsum[qb];
+            float* o = out_c + qb * D + cbase + wc + lm;
+#pragma unroll
+            for (int y = 0; y < NT; ++y) o[16 * y] = (float)(acc[x][y][e] / l);
+        }
 }
 
 template <int D>

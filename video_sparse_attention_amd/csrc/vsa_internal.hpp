@@ -60,14 +60,6 @@ struct SeqView {
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
-// Column position inside a 64-wide float64 LDS row for the 4-column register
-// tiles of the float64 block-level products: thread tx reads its columns
-// 4 tx, 4 tx + 1 at 2 tx and 4 tx + 2, 4 tx + 3 at 32 + 2 tx, so the 16
-// threads of a row of the thread grid read 256 contiguous bytes per double2
-// access (no bank conflicts); column pairs 2m, 2m + 1 stay adjacent.  A
-// permutation of 0 .. 63.
-__host__ __device__ inline int quad_col(int c) { return ((c >> 1) & 1) * 32 + (c >> 2) * 2 + (c & 1); }
-
 __device__ __forceinline__ SeqView seq_view(const DevProblem& P, int s, int h) {
     SeqView v;
     if (!P.packed) {
