@@ -101,7 +101,6 @@ __global__ __launch_bounds__(kThreads) void coarse_scores_kernel(DevProblem P, c
     if (i0 >= iend || j0 >= sv.nkv) return;
     const int64_t srow0 = ((int64_t)s * P.H + h) * C - c0;  // scratch row of local block 0
     const int tid = threadIdx.x;
-    const int ty = tid / 16, tx = tid % 16;
     // staging: thread t copies 4 consecutive d of row t / 4
     const int sr = tid / 4, sd = 4 * (tid % 4);
     const bool q_ok = i0 + sr < iend, k_ok = j0 + sr < sv.nkv;

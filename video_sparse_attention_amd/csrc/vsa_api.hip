@@ -215,7 +215,7 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
     return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
 }
 
-int check_qkv(const vsa::DevProblem& P, const void* q, const void* k, const void* v) {
+int check_qkv(const vsa::DevProblem&, const void* q, const void* k, const void* v) {
     if (!q || !k || !v) return fail(VSA_ERR_NULL, "q, k or v is NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(VSA_ERR_ALIGN, "q, k and v must be 16-byte aligned");
     return VSA_OK;
