@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -493,3 +494,22 @@ def test_tile_errors(lib):
     assert lib.vsa_tile_scatter(A, ctypes.c_void_p(FAKE + 2), 1, 2, 4, 4, 4, 4, 4, 4, 1, None) == E.VSA_ERR_ALIAS
     assert lib.vsa_tile_scatter(A, ctypes.c_void_p(FAKE + (3 << 32) + 1), 1, 2, 4, 4, 4, 4, 4, 4, 1,
                                 None) == E.VSA_ERR_ALIGN
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """With no libvsa.so at the configured path, the first entry point raises
+    ImportError naming the missing library: there is no CPU or PyTorch
+    fallback on the product path."""
+    code = (
+        "import video_sparse_attention_amd as vsa\n"
+        "p = vsa.dense_problem(1, 1, 64, 64, 64, 1)\n"
+        "try:\n"
+        "    vsa.vsa_workspace_size(p)\n"
+        "except ImportError as e:\n"
+        "    print('IMPORT-ERROR:', e)\n"
+        "else:\n"
+        "    print('NO-ERROR')\n")
+    env = dict(os.environ, VSA_LIBRARY=str(tmp_path / "absent" / "libvsa.so"))
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-3000:]
+    assert "IMPORT-ERROR:" in r.stdout and "libvsa.so not found" in r.stdout, r.stdout + r.stderr[-2000:]
