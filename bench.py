@@ -359,7 +359,8 @@ def train_bench(args, torch, synth, vsa):
     """Training step on the large shape (B=1, H=56, D=128, S=15488, top-49,
     per-token gate): coarse/top-k, the training forward (sparse attention
     with the fused combine, also writing out_s and lse) and the backward
-    (vsa_backward) for a fixed output gradient.  Effective FLOPs: the forward's
+    (vsa_backward_pooled: the block means of q, k and v come from the coarse
+    stage's workspace, as in the autograd wrapper) for a fixed output gradient.  Effective FLOPs: the forward's
     4 B H nQ k 64^2 D plus 2.5 times that for the backward (dV, dP, dQ, dK and
     the recomputed scores: five block products where the forward has two)."""
     dev = torch.device("cuda:0")
@@ -389,7 +390,8 @@ def train_bench(args, torch, synth, vsa):
         if ev: ev[1].record()
         vsa.vsa_sparse_attn_combine_train(prob, q, k, v, idx, num, out_c, gate, out, out_s, lse)
         if ev: ev[2].record()
-        vsa.vsa_backward(prob, q, k, v, idx, num, out_c, gate, out_s, lse, dout, dq, dk, dv, dg, bws)
+        vsa.vsa_backward(prob, q, k, v, idx, num, out_c, gate, out_s, lse, dout, dq, dk, dv, dg, bws,
+                         forward_workspace=ws)
         if ev: ev[3].record()
 
     for _ in range(args.warmup):

@@ -407,6 +407,30 @@ int vsa_backward(const vsa_problem *problem, const vsa_bf16 *q, const vsa_bf16 *
                  void *workspace, size_t workspace_bytes, vsa_stream stream);
 
 /*
+ * vsa_backward_pooled - vsa_backward that reads the float64 block means of
+ * q, k and v from the forward instead of pooling q, k and v again (one pass
+ * over the three tensors fewer; the gradients are bit-identical to
+ * vsa_backward's).
+ *
+ * forward_workspace: the workspace (at least its first vsa_workspace_size
+ * bytes, 256-byte aligned) of the vsa_coarse_topk or vsa_forward call that
+ * produced q2k_idx, q2k_num and out_c for these q, k, v and this problem,
+ * unchanged since; the library reads its block means and writes nothing to
+ * it.  Not the scratch of vsa_forward_noalloc, which the next call reuses.
+ * Every other argument as vsa_backward.
+ * Errors as vsa_backward, plus VSA_ERR_WORKSPACE (forward_workspace NULL or
+ * smaller than the forward's block means need), VSA_ERR_ALIGN (not 256-byte
+ * aligned) and VSA_ERR_ALIAS (an output or the backward workspace overlapping
+ * the forward's block means).
+ */
+int vsa_backward_pooled(const vsa_problem *problem, const vsa_bf16 *q, const vsa_bf16 *k, const vsa_bf16 *v,
+                        const int32_t *q2k_idx, const int32_t *q2k_num, const float *out_c, const vsa_bf16 *gate,
+                        int32_t gate_mode, const int64_t *gate_strides, const vsa_bf16 *out_s, const float *lse,
+                        const vsa_bf16 *dout, vsa_bf16 *dq, vsa_bf16 *dk, vsa_bf16 *dv, vsa_bf16 *dgate,
+                        const void *forward_workspace, size_t forward_workspace_bytes, void *workspace,
+                        size_t workspace_bytes, vsa_stream stream);
+
+/*
  * 3-D tile partition of video latents ("[kernel] Extract VSA utility
  * functions into fastvideo_kernel", Summary, Design decisions and review
  * thread: tile partition indices and their inverse, variable block sizes with

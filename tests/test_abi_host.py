@@ -292,8 +292,9 @@ def _fk(n):
     return ctypes.c_void_p(FAKE + (n << 32))
 
 
-# distinct fake buffers, 4 GiB apart: q, k, v, out_c, ws, gate/idx, out_s, lse, dout, dq, dk, dv, dgate
-OS_, LSE_, DO_, DQ_, DK_, DV_, DG_ = (_fk(n) for n in range(6, 13))
+# distinct fake buffers, 4 GiB apart: q, k, v, out_c, ws, gate/idx, out_s, lse, dout, dq, dk, dv, dgate,
+# and a forward workspace
+OS_, LSE_, DO_, DQ_, DK_, DV_, DG_, FW_ = (_fk(n) for n in range(6, 14))
 
 
 def train_fwd(lib, p, q=A, k=B_, v=C_, idx=G_, num=G_, oc=W_, gate=None, mode=0, st=None, out=O_, out_s=OS_,
@@ -308,7 +309,20 @@ def bwd(lib, p, q=A, k=B_, v=C_, idx=G_, num=G_, oc=O_, gate=None, mode=0, st=No
                             dgate, ws, wsb, None)
 
 
+def bwdp(lib, p, fws=FW_, fwsb=1 << 40, ws=W_, wsb=1 << 40, dq=DQ_, dout=DO_):
+    return lib.vsa_backward_pooled(ctypes.byref(p), A, B_, C_, G_, G_, O_, None, 0, None, OS_, LSE_, dout, dq, DK_,
+                                   DV_, DG_, fws, fwsb, ws, wsb, None)
+
+
 @pytest.mark.parametrize("call,code", [
+    (lambda L: bwdp(L, dense(), fws=None), E.VSA_ERR_WORKSPACE),
+    (lambda L: bwdp(L, dense(), fwsb=4096), E.VSA_ERR_WORKSPACE),
+    (lambda L: bwdp(L, dense(), fws=ctypes.c_void_p(FAKE + (13 << 32) + 16)), E.VSA_ERR_ALIGN),
+    (lambda L: bwdp(L, dense(), dq=FW_), E.VSA_ERR_ALIAS),
+    (lambda L: bwdp(L, dense(), ws=FW_), E.VSA_ERR_ALIAS),
+    (lambda L: bwdp(L, dense(), dout=None), E.VSA_ERR_NULL),
+    (lambda L: bwdp(L, dense(), ws=None), E.VSA_ERR_WORKSPACE),
+    (lambda L: bwdp(L, dense(topk=0)), E.VSA_ERR_TOPK),
     (lambda L: train_fwd(L, dense(), out_s=None), E.VSA_ERR_NULL),
     (lambda L: train_fwd(L, dense(), lse=None), E.VSA_ERR_NULL),
     (lambda L: train_fwd(L, dense(), out_s=ctypes.c_void_p(FAKE + (6 << 32) + 8)), E.VSA_ERR_ALIGN),
@@ -513,3 +527,17 @@ def test_missing_library_fails_loudly(tmp_path):
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-3000:]
     assert "IMPORT-ERROR:" in r.stdout and "libvsa.so not found" in r.stdout, r.stdout + r.stderr[-2000:]
+
+
+def test_packed_problem_keeps_its_metadata_arrays_alive():
+    """A packed problem holds raw addresses of its metadata's arrays; built
+    from a temporary VarlenMeta it must keep those arrays alive itself."""
+    import gc
+    import video_sparse_attention_amd as vsa
+    p = vsa.vsa_build_metadata([100, 300, 5], topk=[1, 2, 1], device="cpu").problem(2, 64)
+    gc.collect()
+    d = p._device_arrays
+    assert p.cu_blocks_q == d["cu_blocks_q"].data_ptr() and p.cu_blocks_kv == d["cu_blocks_kv"].data_ptr()
+    assert p.block_sizes_q == d["block_sizes_q"].data_ptr() and p.topk_per_seq == d["topk"].data_ptr()
+    assert d["cu_blocks_q"].tolist() == [0, 2, 7, 8]
+    assert d["block_sizes_q"].tolist() == [64, 36, 64, 64, 64, 64, 44, 5]

@@ -363,3 +363,60 @@ def test_backward_graph_replay(block):
         for a, b, name in zip(grads_g, grads_e, ("dq", "dk", "dv", "dgate")):
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager backward"
     G.note(f"  4 backward replays equal to the eager backward (block {block})")
+
+
+# ---------------------------------------------------------------------------
+# vsa_backward_pooled: the block means come from the forward's workspace
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("case", ["dense64", "bshd128", "packed256", "chunked"])
+def test_backward_pooled_matches_vsa_backward(case):
+    """vsa_backward_pooled reads the float64 block means of q, k and v from
+    the workspace of the vsa_coarse_topk call that made the routing instead of
+    pooling the three tensors; its gradients must be bitwise those of
+    vsa_backward (the same pooling arithmetic ran in the forward).  The
+    chunked case runs the coarse stage in two chunks of query blocks (3000
+    blocks on two heads), so the forward's block means must be complete
+    although its score matrix only ever holds one chunk."""
+    dev = G.DEV
+    if case == "packed256":
+        seqlens = [300, 130, 520]
+        topk = [1, 1, 2]
+        inp = synth.varlen_inputs(seqlens, None, 2, 128, topk, seed=2300, gated=True, block=256)
+        # the problem points into meta's device arrays: meta must outlive every call
+        meta = vsa.vsa_build_metadata(seqlens, None, topk, device=dev, block_size=256)
+        prob = meta.problem(2, 128)
+        q, k, v, gate = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.gate))
+    else:
+        if case == "dense64":
+            B, H, Sq, Skv, D, topk, bs, bshd, mode = 2, 2, 64 * 3 + 20, 64 * 4 + 5, 128, 2, 64, False, "token"
+        elif case == "bshd128":
+            B, H, Sq, Skv, D, topk, bs, bshd, mode = 1, 3, 128 * 2 + 70, 128 * 3 + 9, 64, 2, 128, True, "full"
+        else:
+            B, H, Sq, Skv, D, topk, bs, bshd, mode = 1, 2, 64 * 3000, 64 * 3000, 64, 7, 64, False, "token"
+        inp = synth.dense_inputs(B, H, Sq, D, topk, seed=2301, gated=True, S_kv=Skv)
+        conv = G.to_bshd if bshd else (lambda t: t)
+        q, k, v = (conv(t).to(dev) for t in (inp.q, inp.k, inp.v))
+        gate = conv(inp.gate if mode == "token" else inp.gate[..., None].expand(*inp.q.shape).contiguous()).to(dev)
+        prob = vsa.dense_problem(B, H, Sq, Skv, D, topk, bs, bshd)
+    G.note(f"case pooled backward: {case}")
+    cs, isz, ns = vsa.block_shapes(prob)
+    out_c = torch.empty(cs, dtype=torch.float32, device=dev)
+    idx = torch.empty(isz, dtype=torch.int32, device=dev)
+    num = torch.empty(ns, dtype=torch.int32, device=dev)
+    ws = vsa.alloc_workspace(prob, dev)
+    vsa.vsa_coarse_topk(prob, q, k, v, out_c, idx, num, ws)
+    out, out_s = torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty(vsa.lse_shape(prob), dtype=torch.float32, device=dev)
+    vsa.vsa_sparse_attn_combine_train(prob, q, k, v, idx, num, out_c, gate, out, out_s, lse)
+    dout = synth.output_grad(tuple(q.shape), 2302).to(dev)
+    grads = {}
+    for name, fw in (("plain", None), ("pooled", ws)):
+        nan = float("nan")
+        dq, dk, dv, dg = (torch.full_like(t, nan) for t in (q, k, v, gate))
+        vsa.vsa_backward(prob, q, k, v, idx, num, out_c, gate, out_s, lse, dout, dq, dk, dv, dg,
+                         forward_workspace=fw)
+        torch.cuda.synchronize()
+        grads[name] = [t.cpu() for t in (dq, dk, dv, dg)]
+    for what, a, b in zip(("dq", "dk", "dv", "dgate"), grads["plain"], grads["pooled"]):
+        assert torch.isfinite(a.float()).all(), f"{case}: {what} has non-finite values"
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{case}: {what} differs"

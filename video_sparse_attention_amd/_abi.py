@@ -66,6 +66,8 @@ SIGNATURES = {
     "vsa_backward_workspace_size": (sz, [P_PROBLEM]),
     "vsa_backward": (i32, [P_PROBLEM, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                            vp, vp, vp, vp, vp, sz, vp]),
+    "vsa_backward_pooled": (i32, [P_PROBLEM, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
+                                  vp, vp, vp, vp, vp, sz, vp, sz, vp]),
     "vsa_forward": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
                           i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]),
     "vsa_forward_noalloc": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,

@@ -97,7 +97,7 @@ class VarlenMeta:
             raise RuntimeError("call .to(device) before building a packed problem")
         d = self.device_arrays
         s = self.sizes
-        return VsaProblem(
+        p = VsaProblem(
             layout=VSA_LAYOUT_PACKED, heads=heads, head_dim=head_dim, block_size=self.block_size,
             num_seqs=s.num_seqs, total_q_blocks=s.total_q_blocks,
             total_kv_blocks=s.total_kv_blocks, max_q_blocks=s.max_q_blocks,
@@ -105,6 +105,10 @@ class VarlenMeta:
             cu_blocks_q=d["cu_blocks_q"].data_ptr(), cu_blocks_kv=d["cu_blocks_kv"].data_ptr(),
             block_sizes_q=d["block_sizes_q"].data_ptr(),
             block_sizes_kv=d["block_sizes_kv"].data_ptr(), topk_per_seq=d["topk"].data_ptr())
+        # the problem carries raw device addresses of these arrays: it keeps
+        # them alive itself, so a problem outliving its VarlenMeta stays valid
+        p._device_arrays = d
+        return p
 
 
 def vsa_build_metadata(seqlens_q: Sequence[int], seqlens_kv: Optional[Sequence[int]] = None,
@@ -303,11 +307,14 @@ def alloc_backward_workspace(problem: VsaProblem, device) -> torch.Tensor:
 
 
 def vsa_backward(problem: VsaProblem, q, k, v, q2k_idx, q2k_num, out_c, gate, out_s, lse, dout,
-                 dq, dk, dv, dgate=None, workspace=None) -> None:
+                 dq, dk, dv, dgate=None, workspace=None, forward_workspace=None) -> None:
     """Gradients of ``sum(out * dout)`` of the forward with these inputs and
     routing (vsa_backward): writes ``dq``, ``dk``, ``dv`` and, with a gate,
     ``dgate`` (contiguous, the gate's shape: [B, H, Sq(, D)], or [B, Sq, H(, D)]
-    for a BSHD problem)."""
+    for a BSHD problem).  ``forward_workspace``: the workspace of the
+    ``vsa_coarse_topk`` call that produced the routing, unchanged since; its
+    block means of q, k and v are then reused (vsa_backward_pooled) instead of
+    pooling the three tensors again."""
     _check_qkv(problem, q, k, v)
     cs, isz, ns = block_shapes(problem)
     if tuple(q2k_idx.shape[:-1]) != tuple(isz[:-1]):
@@ -328,16 +335,26 @@ def vsa_backward(problem: VsaProblem, q, k, v, q2k_idx, q2k_num, out_c, gate, ou
     if workspace is None:
         workspace = alloc_backward_workspace(problem, q.device)
     _need(workspace, "workspace", torch.uint8)
-    _abi.check(_abi.load().vsa_backward(
+    dg = _ptr(dgate if mode != VSA_GATE_NONE else None)
+    if forward_workspace is None:
+        _abi.check(_abi.load().vsa_backward(
+            ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(q2k_idx), _ptr(q2k_num), _ptr(out_c),
+            _ptr(gate), mode, st, _ptr(out_s), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), dg,
+            _ptr(workspace), workspace.numel(), _stream(q.device)), "vsa_backward")
+        return
+    _need(forward_workspace, "forward_workspace", torch.uint8)
+    _abi.check(_abi.load().vsa_backward_pooled(
         ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(q2k_idx), _ptr(q2k_num), _ptr(out_c),
-        _ptr(gate), mode, st, _ptr(out_s), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-        _ptr(dgate if mode != VSA_GATE_NONE else None), _ptr(workspace), workspace.numel(),
-        _stream(q.device)), "vsa_backward")
+        _ptr(gate), mode, st, _ptr(out_s), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), dg,
+        _ptr(forward_workspace), forward_workspace.numel(), _ptr(workspace), workspace.numel(),
+        _stream(q.device)), "vsa_backward_pooled")
 
 
 class _VideoSparseAttn(torch.autograd.Function):
     """Autograd wrapper: forward = vsa_coarse_topk + vsa_sparse_attn_combine_train,
-    backward = vsa_backward (the routing is held fixed)."""
+    backward = vsa_backward_pooled (the routing is held fixed; the forward's
+    workspace is kept for the backward, which reuses its block means of q, k
+    and v)."""
 
     @staticmethod
     def forward(ctx, q, k, v, gate, problem, keep):
@@ -349,7 +366,8 @@ class _VideoSparseAttn(torch.autograd.Function):
         out_c = torch.empty(cs, dtype=torch.float32, device=dev)
         idx = torch.empty(isz, dtype=torch.int32, device=dev)
         num = torch.empty(ns, dtype=torch.int32, device=dev)
-        vsa_coarse_topk(problem, q, k, v, out_c, idx, num, alloc_workspace(problem, dev))
+        ws = alloc_workspace(problem, dev)
+        vsa_coarse_topk(problem, q, k, v, out_c, idx, num, ws)
         out = torch.empty_like(q)
         out_s = torch.empty_like(q)
         lse = torch.empty(lse_shape(problem), dtype=torch.float32, device=dev)
@@ -357,7 +375,7 @@ class _VideoSparseAttn(torch.autograd.Function):
         ctx.problem = problem
         ctx.keep = keep
         ctx.has_gate = g is not None
-        ctx.save_for_backward(q, k, v, *( [g] if g is not None else []), idx, num, out_c, out_s, lse)
+        ctx.save_for_backward(q, k, v, *( [g] if g is not None else []), idx, num, out_c, out_s, lse, ws)
         ctx.mark_non_differentiable(idx, num)
         return out, idx, num
 
@@ -366,11 +384,12 @@ class _VideoSparseAttn(torch.autograd.Function):
         saved = list(ctx.saved_tensors)
         q, k, v = saved[:3]
         g = saved[3] if ctx.has_gate else None
-        idx, num, out_c, out_s, lse = saved[4 if ctx.has_gate else 3:]
+        idx, num, out_c, out_s, lse, ws = saved[4 if ctx.has_gate else 3:]
         dout = dout.contiguous()
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         dg = None if g is None else torch.empty(g.shape, dtype=torch.bfloat16, device=q.device)
-        vsa_backward(ctx.problem, q, k, v, idx, num, out_c, g, out_s, lse, dout, dq, dk, dv, dg)
+        vsa_backward(ctx.problem, q, k, v, idx, num, out_c, g, out_s, lse, dout, dq, dk, dv, dg,
+                     forward_workspace=ws)
         return dq, dk, dv, dg, None, None
 
 

@@ -954,8 +954,8 @@ hipError_t launch_all(const DevProblem& P, const BwdArgs& A, hipStream_t st) {
         default: return hipErrorInvalidValue;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // 2. block means
-    if ((e = launch_pool(P, A.q, A.k, A.v, A.qc, A.kc, A.vc, st)) != hipSuccess) return e;
+    // 2. block means (unless the caller passed the forward's)
+    if (!A.pooled && (e = launch_pool(P, A.q, A.k, A.v, A.qc, A.kc, A.vc, st)) != hipSuccess) return e;
     // 3. coarse backward
     if ((e = launch_coarse_scores(CP, A.qc, A.kc, A.pbuf, st)) != hipSuccess) return e;
     if ((e = launch_coarse_scores(CP, A.doc, A.vc, A.dsbuf, st)) != hipSuccess) return e;

@@ -531,11 +531,16 @@ size_t vsa_backward_workspace_size(const vsa_problem* problem) {
     return plan_bwd_workspace(P, nullptr).total_bytes;
 }
 
-int vsa_backward(const vsa_problem* problem, const vsa_bf16* q, const vsa_bf16* k, const vsa_bf16* v,
-                 const int32_t* q2k_idx, const int32_t* q2k_num, const float* out_c, const vsa_bf16* gate,
-                 int32_t gate_mode, const int64_t* gate_strides_in, const vsa_bf16* out_s, const float* lse,
-                 const vsa_bf16* dout, vsa_bf16* dq, vsa_bf16* dk, vsa_bf16* dv, vsa_bf16* dgate, void* workspace,
-                 size_t workspace_bytes, vsa_stream stream) {
+// The backward; with forward_workspace (the workspace of the forward call that
+// produced the routing) the block means of q, k and v are read from it
+// instead of being pooled again.
+static int backward_common(const vsa_problem* problem, const vsa_bf16* q, const vsa_bf16* k, const vsa_bf16* v,
+                           const int32_t* q2k_idx, const int32_t* q2k_num, const float* out_c,
+                           const vsa_bf16* gate, int32_t gate_mode, const int64_t* gate_strides_in,
+                           const vsa_bf16* out_s, const float* lse, const vsa_bf16* dout, vsa_bf16* dq,
+                           vsa_bf16* dk, vsa_bf16* dv, vsa_bf16* dgate, void* workspace, size_t workspace_bytes,
+                           const void* forward_workspace, size_t forward_workspace_bytes, bool use_forward,
+                           vsa_stream stream) {
     vsa::DevProblem P;
     int rc = make_problem(problem, &P);
     if (rc) return rc;
@@ -580,6 +585,23 @@ int vsa_backward(const vsa_problem* problem, const vsa_bf16* q, const vsa_bf16* 
     const BwdWorkspace w = plan_bwd_workspace(P, workspace);
     if (workspace_bytes < w.total_bytes)
         return fail(VSA_ERR_WORKSPACE, "workspace holds %zu bytes, needs %zu", workspace_bytes, w.total_bytes);
+    // the forward's block means: Qc, Kc, Vc at the start of its workspace
+    Workspace fw{};
+    if (use_forward) {
+        if (!forward_workspace) return fail(VSA_ERR_WORKSPACE, "forward workspace is NULL");
+        if ((uintptr_t)forward_workspace % kAlign)
+            return fail(VSA_ERR_ALIGN, "forward workspace must be 256-byte aligned");
+        fw = plan_workspace(P, const_cast<void*>(forward_workspace));
+        if (forward_workspace_bytes < fw.coarse_bytes)
+            return fail(VSA_ERR_WORKSPACE, "forward workspace holds %zu bytes, needs %zu", forward_workspace_bytes,
+                        fw.coarse_bytes);
+        const int64_t pooled_bytes = (const char*)fw.coarse - (const char*)forward_workspace;
+        for (const Span& o : outs)
+            if (o.n && overlaps(o.p, o.n, forward_workspace, pooled_bytes))
+                return fail(VSA_ERR_ALIAS, "an output of the backward overlaps the forward workspace");
+        if (overlaps(workspace, (int64_t)w.total_bytes, forward_workspace, pooled_bytes))
+            return fail(VSA_ERR_ALIAS, "the backward workspace overlaps the forward workspace");
+    }
     vsa::BwdArgs A{};
     A.q = q;
     A.k = k;
@@ -599,9 +621,10 @@ int vsa_backward(const vsa_problem* problem, const vsa_bf16* q, const vsa_bf16* 
     A.dk = dk;
     A.dv = dv;
     A.dgate = dgate;
-    A.qc = w.qc;
-    A.kc = w.kc;
-    A.vc = w.vc;
+    A.qc = use_forward ? fw.qc : w.qc;
+    A.kc = use_forward ? fw.kc : w.kc;
+    A.vc = use_forward ? fw.vc : w.vc;
+    A.pooled = use_forward;
     A.doc = w.doc;
     A.dqc = w.dqc;
     A.dkc = w.dkc;
@@ -613,6 +636,26 @@ int vsa_backward(const vsa_problem* problem, const vsa_bf16* q, const vsa_bf16* 
     A.k2q_num = w.k2q_num;
     rc = hip_status(vsa::launch_backward(P, A, (hipStream_t)stream), "backward launch");
     return rc ? rc : ok();
+}
+
+int vsa_backward(const vsa_problem* problem, const vsa_bf16* q, const vsa_bf16* k, const vsa_bf16* v,
+                 const int32_t* q2k_idx, const int32_t* q2k_num, const float* out_c, const vsa_bf16* gate,
+                 int32_t gate_mode, const int64_t* gate_strides_in, const vsa_bf16* out_s, const float* lse,
+                 const vsa_bf16* dout, vsa_bf16* dq, vsa_bf16* dk, vsa_bf16* dv, vsa_bf16* dgate, void* workspace,
+                 size_t workspace_bytes, vsa_stream stream) {
+    return backward_common(problem, q, k, v, q2k_idx, q2k_num, out_c, gate, gate_mode, gate_strides_in, out_s, lse,
+                           dout, dq, dk, dv, dgate, workspace, workspace_bytes, nullptr, 0, false, stream);
+}
+
+int vsa_backward_pooled(const vsa_problem* problem, const vsa_bf16* q, const vsa_bf16* k, const vsa_bf16* v,
+                        const int32_t* q2k_idx, const int32_t* q2k_num, const float* out_c, const vsa_bf16* gate,
+                        int32_t gate_mode, const int64_t* gate_strides_in, const vsa_bf16* out_s, const float* lse,
+                        const vsa_bf16* dout, vsa_bf16* dq, vsa_bf16* dk, vsa_bf16* dv, vsa_bf16* dgate,
+                        const void* forward_workspace, size_t forward_workspace_bytes, void* workspace,
+                        size_t workspace_bytes, vsa_stream stream) {
+    return backward_common(problem, q, k, v, q2k_idx, q2k_num, out_c, gate, gate_mode, gate_strides_in, out_s, lse,
+                           dout, dq, dk, dv, dgate, workspace, workspace_bytes, forward_workspace,
+                           forward_workspace_bytes, true, stream);
 }
 
 int vsa_combine(const vsa_problem* problem, const float* out_c, const vsa_bf16* gate, int32_t gate_mode,

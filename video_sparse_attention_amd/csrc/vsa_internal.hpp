@@ -249,6 +249,9 @@ struct BwdArgs {
     double *qc, *kc, *vc, *doc, *dqc, *dkc, *dvc, *pbuf, *dsbuf;
     float* rs;
     int *k2q, *k2q_num;
+    // qc, kc and vc already hold the block means of q, k and v (those the
+    // forward computed): the pool launch is skipped
+    bool pooled;
 };
 hipError_t launch_backward(const DevProblem& P, const BwdArgs& A, hipStream_t st);
 
