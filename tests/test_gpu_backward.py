@@ -319,11 +319,13 @@ def test_backward_large_shape_sampled_heads():
 # HIP graph capture of the backward
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("block", [64, 256])
-def test_backward_graph_replay(block):
-    """vsa_backward captured once in a graph on preallocated buffers; between
-    replays a new output gradient is copied in and the backward runs eagerly
-    on its own outputs; every replay equals the eager result bit for bit."""
+@pytest.mark.parametrize("block,pooled", [(64, False), (256, False), (64, True), (256, True)])
+def test_backward_graph_replay(block, pooled):
+    """vsa_backward (or, pooled, vsa_backward_pooled reading the forward
+    workspace's block means) captured once in a graph on preallocated
+    buffers; between replays a new output gradient is copied in and the
+    backward runs eagerly on its own outputs; every replay equals the eager
+    result bit for bit."""
     B, H, S, D, topk = 1, 2, 64 * 7 + 29, 128, 2
     inp = synth.dense_inputs(B, H, S, D, topk, seed=2900 + block, gated=True)
     dev = G.DEV
@@ -333,7 +335,8 @@ def test_backward_graph_replay(block):
     out_c = torch.empty(cs, dtype=torch.float32, device=dev)
     idx = torch.empty(isz, dtype=torch.int32, device=dev)
     num = torch.empty(ns, dtype=torch.int32, device=dev)
-    vsa.vsa_coarse_topk(prob, q, k, v, out_c, idx, num, vsa.alloc_workspace(prob, dev))
+    fws = vsa.alloc_workspace(prob, dev)
+    vsa.vsa_coarse_topk(prob, q, k, v, out_c, idx, num, fws)
     out, out_s = torch.empty_like(q), torch.empty_like(q)
     lse = torch.empty(vsa.lse_shape(prob), dtype=torch.float32, device=dev)
     vsa.vsa_sparse_attn_combine_train(prob, q, k, v, idx, num, out_c, g, out, out_s, lse)
@@ -341,7 +344,8 @@ def test_backward_graph_replay(block):
     grads_g = [torch.empty_like(t) for t in (q, k, v, g)]
     grads_e = [torch.empty_like(t) for t in (q, k, v, g)]
     ws_g, ws_e = vsa.alloc_backward_workspace(prob, dev), vsa.alloc_backward_workspace(prob, dev)
-    run = lambda gr, ws: vsa.vsa_backward(prob, q, k, v, idx, num, out_c, g, out_s, lse, dout, *gr, ws)
+    run = lambda gr, ws: vsa.vsa_backward(prob, q, k, v, idx, num, out_c, g, out_s, lse, dout, *gr, ws,
+                                          forward_workspace=fws if pooled else None)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):  # a warm-up call outside the capture
@@ -362,7 +366,7 @@ def test_backward_graph_replay(block):
         torch.cuda.synchronize()
         for a, b, name in zip(grads_g, grads_e, ("dq", "dk", "dv", "dgate")):
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager backward"
-    G.note(f"  4 backward replays equal to the eager backward (block {block})")
+    G.note(f"  4 backward replays equal to the eager backward (block {block}, pooled {pooled})")
 
 
 # ---------------------------------------------------------------------------
