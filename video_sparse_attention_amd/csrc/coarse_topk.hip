@@ -19,8 +19,9 @@
 //      it);
 //   2. select: one wave per query block row.  The row's order-preserving
 //      64-bit keys sit in registers (up to 64 per lane), the k-th largest is
-//      found by bisection with wave-wide ballot counts (32 rounds on the high
-//      halves, 32 more on the low halves only when needed), ties at the
+//      found by bisection with wave-wide ballot counts (up to 32 rounds on
+//      the high halves, stopping as soon as exactly k keys lie at or above the
+//      candidate; up to 32 more on the low halves only when needed), ties at the
 //      threshold go to the lowest indices, and the indices are emitted in
 //      ascending order with ballot prefix counts.  The row is then replaced
 //      by its softmax weights exp((s - max) / sqrt(D)) and their sum is kept;
@@ -219,6 +220,10 @@ __global__ __launch_bounds__(kThreads) void coarse_select_kernel(DevProblem P, d
         for (int e = 0; e < KPL; ++e)
             if (live(e)) cnt += __popcll(__ballot((uint32_t)(key[e] >> 32) >= cand));
         Th = cnt >= k ? cand : Th;
+        // exactly k keys have their high half >= cand: they are the
+        // selection (the steps below then find no tie to break), so the
+        // remaining bits need not be resolved
+        if (cnt == k) break;
     }
     int gt_hi = 0, eq_hi = 0;
 #pragma unroll
@@ -239,6 +244,7 @@ __global__ __launch_bounds__(kThreads) void coarse_select_kernel(DevProblem P, d
                 if (live(e))
                     cnt += __popcll(__ballot(((uint32_t)(key[e] >> 32) == Th) & ((uint32_t)key[e] >= cand)));
             Tl = cnt >= need_hi ? cand : Tl;
+            if (cnt == need_hi) break;  // the same within the high-half group
         }
     }
     // (when every candidate is chosen, T = Th:0 selects all of them below)
