@@ -80,6 +80,8 @@ def test_deterministic():
     (1, 1, 128, 64 * 300, 128, 20, None),    # 300 KV blocks: 16 keys per lane in the top-k
     (1, 1, 200, 64 * 1100 - 5, 64, 7, None), # 1100 KV blocks: 64 keys per lane, 4 rows per group
     (1, 1, 64 * 3 + 17, 64 * 4095 + 5, 64, 300, "token"),  # the maximum, 4096 KV blocks, 5-token tail
+    (1, 2, 64 * 70 + 9, 64 * 600 + 3, 128, 9, "token"),  # D = 128, 601 KV blocks: the 4-way output split,
+                                                          # a 7-row last row tile and a 3-token KV tail
 ])
 def test_dense_edge_cases(B, H, Sq, Skv, D, topk, gate):
     inp = synth.dense_inputs(B, H, Sq, D, topk, seed=2000 + Sq + Skv + D + topk,

@@ -285,18 +285,20 @@ __global__ __launch_bounds__(kThreads) void coarse_select_kernel(DevProblem P, d
 }
 
 // ---------------------------------------------------------------------------
-// 3. out_c = W Vc / sum(W); a workgroup computes 64 rows x D / 2 columns,
-// so that a head's few row tiles spread over twice as many CUs (a 4-way
-// split, which stages every W slice four times, measured no faster)
+// 3. out_c = W Vc / sum(W); a workgroup computes 64 rows x D / SPLIT
+// columns, so that a head's few row tiles spread over SPLIT times as many
+// CUs: SPLIT = 2, or 4 for D = 128 and rows of at least kLongRow KV blocks
+// (every W slice is then staged four times, which pays only when the rows
+// are long: 4 % faster at 768 KV blocks, 1 % slower at 242)
 // ---------------------------------------------------------------------------
-constexpr int kOutSplit = 2;  // column ranges per row tile
+constexpr int kLongRow = 512;
 
-template <int D>
+template <int D, int SPLIT>
 __global__ __launch_bounds__(kThreads) void coarse_out_kernel(DevProblem P, const double* __restrict__ sc, int ld,
                                                               const double* __restrict__ lsum,
                                                               const double* __restrict__ vc,
                                                               float* __restrict__ out_c, int c0, int C) {
-    constexpr int DC = D / kOutSplit;        // columns per workgroup
+    constexpr int DC = D / SPLIT;            // columns per workgroup
     constexpr int NT = 2;                    // 16-column products per wave
     constexpr int MT = DC == 64 ? 2 : 1;     // 16-row products per wave
     static_assert(DC == 32 || DC == 64, "64 or 32 columns per workgroup");
@@ -304,8 +306,8 @@ __global__ __launch_bounds__(kThreads) void coarse_out_kernel(DevProblem P, cons
     __shared__ __attribute__((aligned(16))) double vs[kSlice][DC + kPad];     // [kv][d - cbase]
     const int s = blockIdx.z, h = blockIdx.y;
     const SeqView sv = seq_view(P, s, h);
-    const int cbase = (blockIdx.x % kOutSplit) * DC;
-    const int i0 = c0 + (blockIdx.x / kOutSplit) * kTile;
+    const int cbase = (blockIdx.x % SPLIT) * DC;
+    const int i0 = c0 + (blockIdx.x / SPLIT) * kTile;
     const int iend = min(sv.nq, c0 + C);
     if (i0 >= iend) return;
     const int64_t srow0 = ((int64_t)s * P.H + h) * C - c0;  // scratch row of local block 0
@@ -421,8 +423,16 @@ hipError_t launch_d(const DevProblem& P, const double* qc, const double* kc, dou
                                scale, c0, C);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(coarse_out_kernel<D>, dim3(tq * kOutSplit, P.H, P.nseq), dim3(kThreads), 0, st, P,
-                           sc, ld, lsum, vc, out_c, c0, C);
+        bool split4 = false;
+        if constexpr (D == 128) split4 = ld >= kLongRow;
+        if constexpr (D == 128) {
+            if (split4)
+                hipLaunchKernelGGL((coarse_out_kernel<D, 4>), dim3(tq * 4, P.H, P.nseq), dim3(kThreads), 0, st, P,
+                                   sc, ld, lsum, vc, out_c, c0, C);
+        }
+        if (!split4)
+            hipLaunchKernelGGL((coarse_out_kernel<D, 2>), dim3(tq * 2, P.H, P.nseq), dim3(kThreads), 0, st, P, sc,
+                               ld, lsum, vc, out_c, c0, C);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
